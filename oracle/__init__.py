@@ -1,0 +1,26 @@
+"""CPU oracle for packed attention over a rollout DAG.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute anything in this package; only the test-suite, the smoke check and the
+benchmark's CPU-baseline leg use it.  It shares no code, tables or helpers with
+the HIP library: it rebuilds positions and visibility from the raw node and
+mount tables itself, in plain Python/NumPy, in float64 unless a caller asks for
+float32.
+
+What it computes (the plain definition that the packed method reaches up to
+rounding order):
+
+* ``dag``       -- node validation, start positions (Octopus Eq. 2), active
+                   mounts with their transitive closure, visible sets, the
+                   root-to-leaf trajectories with mounted spans spliced in, and
+                   each node's owning leaf (Octopus Eq. 6).
+* ``rope``      -- the rotary phase of Octopus Eq. 1.
+* ``attention`` -- four independent evaluations of attention over the DAG:
+                   brute force (explicit loops), flat per-trajectory dense causal
+                   attention (the reference), a dense packed mask, and per-row /
+                   per-key evaluations for sampling large inputs.
+
+Parity unpinned: the RoPE pairing convention (first half / second half of the
+head dimension) and the frequency base (10000) are a textbook choice the pages
+do not fix; both sides take them as parameters.
+"""

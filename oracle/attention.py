@@ -1,0 +1,301 @@
+"""Attention over a rollout DAG, four independent ways.
+
+What is computed (Octopus Sec. 3.3 Eq. 4 and HARTS Sec. 4.2 Eq. 21-22): every
+compact query token t = (u, i) attends, with softmax weights, to the keys of
+its visible set V(u, i) -- the node's ancestors, its active mounted spans and
+its own tokens up to i -- after rotating q and k at their Eq. 2 positions:
+
+    s_tj = scale * <R(pos_t) q_t,h , R(pos_j) k_j,g>,   g = h // (Hq / Hkv)
+    O_t,h = sum_{j in V(t)} softmax_j(s_tj) v_j,g,      lse_t,h = log sum_j exp s_tj
+
+The backward pass is the standard softmax-attention backward chained through
+R^T; a key shared by several readers (ancestors, mounted spans) receives the
+sum of every reader's contribution (Octopus Sec. 3.4 Eq. 8, HARTS Sec. 3.4).
+
+* :func:`attn_flat` -- the reference: expand every root-to-leaf trajectory with
+  its mounted spans spliced in, run dense causal attention on it (positions
+  from Eq. 2, not from the sequence index), keep each node's outputs from its
+  owning trajectory, and scatter-add the expanded gradients to compact tokens.
+  The upstream gradient of a compact token lives on its owner trajectory only
+  (Octopus Eq. 6), unless per-trajectory gradients are passed explicitly.
+* :func:`attn_brute` -- explicit loops over (query, head, visible key).
+* :func:`attn_packed_mask` -- one dense token-by-token mask over the packed tokens.
+* :func:`attn_rows` / :func:`attn_key_grads` -- selected outputs and selected
+  key gradients, for sampling inputs too large for the other three.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+from .dag import Dag
+from .rope import rotate, rotate_transpose
+
+
+@dataclass
+class AttnParams:
+    hq: int
+    hkv: int
+    scale: Optional[float] = None      # None -> 1/sqrt(d)
+    rope_base: float = 10000.0         # 0 -> no rotation
+
+    def scale_for(self, d: int) -> float:
+        return (1.0 / np.sqrt(d)) if self.scale is None else float(self.scale)
+
+    def group(self, h: int) -> int:
+        return h // (self.hq // self.hkv)
+
+
+def _np(x):
+    if hasattr(x, "detach"):
+        x = x.detach().cpu()
+        if str(x.dtype) == "torch.bfloat16":
+            x = x.float()
+        x = x.numpy()
+    return np.asarray(x)
+
+
+def _softmax_rows(s: np.ndarray):
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    z = e.sum(axis=-1, keepdims=True)
+    return e / z, (m + np.log(z))[..., 0]
+
+
+# ---------------------------------------------------------------------------
+# flat per-trajectory reference
+# ---------------------------------------------------------------------------
+
+def attn_flat(spec, q, k, v, do, p: AttnParams, transitive: bool = True,
+              dtype=np.float64, traj_do: Optional[Dict[int, np.ndarray]] = None,
+              block: int = 1024, with_grad: bool = True):
+    """Returns (o, lse, dq, dk, dv) over compact tokens (token-major, float64 arrays).
+
+    ``traj_do`` maps a leaf to the upstream gradient of its trajectory's rows
+    ([len(trajectory), Hq, d]); without it each compact token's ``do`` is placed
+    on its owner trajectory and zero elsewhere.
+    """
+    g = Dag(spec, transitive)
+    q, k, v = _np(q), _np(k), _np(v)
+    do = None if do is None else _np(do)
+    U, hq, d = q.shape
+    scale = p.scale_for(d)
+    pos = g.token_positions()
+    qr = rotate(q, pos, p.rope_base).astype(dtype)
+    kr = rotate(k, pos, p.rope_base).astype(dtype)
+    vv = np.asarray(v, np.float64).astype(dtype)
+    node_of, _ = g.token_node()
+    owner = g.owner()
+    o = np.zeros((U, hq, d))
+    lse = np.zeros((U, hq))
+    dq_r = np.zeros((U, hq, d))
+    dk_r = np.zeros((U, p.hkv, d))
+    dv = np.zeros((U, p.hkv, d))
+    for leaf in g.leaves_dfs():
+        seq, own = g.trajectory(leaf)
+        L = len(seq)
+        if L == 0:
+            continue
+        mine = own & (np.asarray([owner[node_of[t]] for t in seq]) == leaf)
+        Q, K, V = qr[seq], kr[seq], vv[seq]
+        if traj_do is not None:
+            dO = np.asarray(traj_do.get(leaf, np.zeros((L, hq, d))), np.float64).astype(dtype)
+        elif do is not None:
+            dO = np.zeros((L, hq, d), dtype)
+            dO[mine] = do[seq[mine]]
+        else:
+            dO = None
+        dQ = np.zeros((L, hq, d), dtype)
+        dK = np.zeros((L, p.hkv, d), dtype)
+        dV = np.zeros((L, p.hkv, d), dtype)
+        for h in range(hq):
+            gg = p.group(h)
+            for r0 in range(0, L, block):
+                r1 = min(L, r0 + block)
+                s = scale * (Q[r0:r1, h] @ K[:r1, gg].T)
+                causal = np.arange(r1)[None, :] > np.arange(r0, r1)[:, None]
+                s = np.where(causal, -np.inf, s)
+                P, l = _softmax_rows(s)
+                O = P @ V[:r1, gg]
+                rows = np.nonzero(mine[r0:r1])[0]
+                o[seq[r0 + rows], h] = O[rows]
+                lse[seq[r0 + rows], h] = l[rows]
+                if with_grad and dO is not None:
+                    g_o = dO[r0:r1, h]
+                    dP = g_o @ V[:r1, gg].T
+                    D = (g_o * O).sum(axis=1, keepdims=True)
+                    dS = P * (dP - D)
+                    dQ[r0:r1, h] += scale * (dS @ K[:r1, gg])
+                    dK[:r1, gg] += scale * (dS.T @ Q[r0:r1, h])
+                    dV[:r1, gg] += P.T @ g_o
+        if with_grad and dO is not None:
+            np.add.at(dq_r, seq, dQ.astype(np.float64))
+            np.add.at(dk_r, seq, dK.astype(np.float64))
+            np.add.at(dv, seq, dV.astype(np.float64))
+    if not with_grad or (do is None and traj_do is None):
+        return o, lse, None, None, None
+    dq = rotate_transpose(dq_r, pos, p.rope_base)
+    dk = rotate_transpose(dk_r, pos, p.rope_base)
+    return o, lse, dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# brute force: explicit loops, float64, tiny inputs only
+# ---------------------------------------------------------------------------
+
+def attn_brute(spec, q, k, v, do, p: AttnParams, transitive: bool = True):
+    g = Dag(spec, transitive)
+    q, k, v, do = (np.asarray(_np(x), np.float64) for x in (q, k, v, do))
+    U, hq, d = q.shape
+    scale = p.scale_for(d)
+    pos = g.token_positions()
+    qr, kr = rotate(q, pos, p.rope_base), rotate(k, pos, p.rope_base)
+    node_of, off = g.token_node()
+    o = np.zeros_like(q)
+    lse = np.zeros((U, hq))
+    dqr = np.zeros_like(q)
+    dkr = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for t in range(U):
+        keys = g.visible_tokens(int(node_of[t]), int(off[t]))
+        for h in range(hq):
+            gg = p.group(h)
+            s = np.array([scale * float(np.dot(qr[t, h], kr[j, gg])) for j in keys])
+            m = max(s)
+            w = [np.exp(x - m) for x in s]
+            z = sum(w)
+            pr = [x / z for x in w]
+            lse[t, h] = m + np.log(z)
+            for a, j in enumerate(keys):
+                o[t, h] += pr[a] * v[j, gg]
+            dp = [float(np.dot(do[t, h], v[j, gg])) for j in keys]
+            D = float(np.dot(do[t, h], o[t, h]))
+            for a, j in enumerate(keys):
+                ds = pr[a] * (dp[a] - D)
+                dqr[t, h] += scale * ds * kr[j, gg]
+                dkr[j, gg] += scale * ds * qr[t, h]
+                dv[j, gg] += pr[a] * do[t, h]
+    return (o, lse, rotate_transpose(dqr, pos, p.rope_base),
+            rotate_transpose(dkr, pos, p.rope_base), dv)
+
+
+# ---------------------------------------------------------------------------
+# dense packed mask over compact tokens, float64
+# ---------------------------------------------------------------------------
+
+def visibility_mask(spec, transitive: bool = True) -> np.ndarray:
+    g = Dag(spec, transitive)
+    node_of, off = g.token_node()
+    M = np.zeros((g.n_tokens, g.n_tokens), bool)
+    for t in range(g.n_tokens):
+        M[t, g.visible_tokens(int(node_of[t]), int(off[t]))] = True
+    return M
+
+
+def attn_packed_mask(spec, q, k, v, do, p: AttnParams, transitive: bool = True):
+    g = Dag(spec, transitive)
+    q, k, v, do = (np.asarray(_np(x), np.float64) for x in (q, k, v, do))
+    U, hq, d = q.shape
+    scale = p.scale_for(d)
+    pos = g.token_positions()
+    qr, kr = rotate(q, pos, p.rope_base), rotate(k, pos, p.rope_base)
+    M = visibility_mask(spec, transitive)
+    o = np.zeros_like(q)
+    lse = np.zeros((U, hq))
+    dqr = np.zeros_like(q)
+    dkr = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for h in range(hq):
+        gg = p.group(h)
+        s = np.where(M, scale * (qr[:, h] @ kr[:, gg].T), -np.inf)
+        P, l = _softmax_rows(s)
+        o[:, h] = P @ v[:, gg]
+        lse[:, h] = l
+        dP = do[:, h] @ v[:, gg].T
+        D = (do[:, h] * o[:, h]).sum(axis=1, keepdims=True)
+        dS = P * (dP - D)
+        dqr[:, h] = scale * (dS @ kr[:, gg])
+        dkr[:, gg] += scale * (dS.T @ qr[:, h])
+        dv[:, gg] += P.T @ do[:, h]
+    return (o, lse, rotate_transpose(dqr, pos, p.rope_base),
+            rotate_transpose(dkr, pos, p.rope_base), dv)
+
+
+# ---------------------------------------------------------------------------
+# sampled evaluation for large inputs
+# ---------------------------------------------------------------------------
+
+class RowSampler:
+    """Per-token evaluation of outputs and key gradients straight from V(t)."""
+
+    def __init__(self, spec, p: AttnParams, transitive: bool = True):
+        self.g = Dag(spec, transitive)
+        self.p = p
+        self.pos = self.g.token_positions()
+        self.node_of, self.off = self.g.token_node()
+
+    def _fwd_one(self, t, q, k, v):
+        g, p = self.g, self.p
+        keys = g.visible_tokens(int(self.node_of[t]), int(self.off[t]))
+        d = q.shape[-1]
+        scale = p.scale_for(d)
+        qt = rotate(np.asarray(q[t:t + 1], np.float64), self.pos[t:t + 1], p.rope_base)[0]
+        kk = rotate(np.asarray(k[keys], np.float64), self.pos[keys], p.rope_base)
+        vv = np.asarray(v[keys], np.float64)
+        out = []
+        for h in range(p.hq):
+            gg = p.group(h)
+            s = scale * (kk[:, gg] @ qt[h])
+            P, l = _softmax_rows(s[None, :])
+            out.append((keys, P[0], float(l[0]), P[0] @ vv[:, gg], kk[:, gg], qt[h]))
+        return out
+
+    def rows(self, tokens: Sequence[int], q, k, v):
+        """(o [n,Hq,d], lse [n,Hq]) for the given compact tokens."""
+        q, k, v = _np(q), _np(k), _np(v)
+        d = q.shape[-1]
+        o = np.zeros((len(tokens), self.p.hq, d))
+        lse = np.zeros((len(tokens), self.p.hq))
+        for a, t in enumerate(tokens):
+            for h, (_, _, l, oh, _, _) in enumerate(self._fwd_one(int(t), q, k, v)):
+                o[a, h] = oh
+                lse[a, h] = l
+        return o, lse
+
+    def readers(self, j: int) -> np.ndarray:
+        """Every compact query token whose visible set contains key token j."""
+        g = self.g
+        u, jo = int(self.node_of[j]), int(self.off[j])
+        out = [np.arange(g.offset[u] + jo, g.offset[u] + g.length[u])]
+        for w in range(g.n):
+            if w == u or g.length[w] == 0:
+                continue
+            if any(b <= jo < e for b, e in g.visible_ranges(w).get(u, [])):
+                out.append(np.arange(g.offset[w], g.offset[w] + g.length[w]))
+        return np.concatenate(out)
+
+    def key_grads(self, keys: Sequence[int], q, k, v, do):
+        """(dk [n,Hkv,d], dv [n,Hkv,d]) for the given key tokens, summed over all readers."""
+        q, k, v, do = _np(q), _np(k), _np(v), _np(do)
+        p = self.p
+        d = q.shape[-1]
+        scale = p.scale_for(d)
+        dk = np.zeros((len(keys), p.hkv, d))
+        dv = np.zeros((len(keys), p.hkv, d))
+        for a, j in enumerate(keys):
+            j = int(j)
+            for t in self.readers(j):
+                t = int(t)
+                for h, (kt, P, _, oh, kk, qh) in enumerate(self._fwd_one(t, q, k, v)):
+                    gg = p.group(h)
+                    g_o = np.asarray(do[t, h], np.float64)
+                    idx = int(np.searchsorted(kt, j))
+                    dp_all = np.asarray(v[kt, gg], np.float64) @ g_o
+                    D = float(g_o @ oh)
+                    ds = P[idx] * (dp_all[idx] - D)
+                    dk[a, gg] += scale * ds * qh
+                    dv[a, gg] += P[idx] * g_o
+            dk[a] = rotate_transpose(dk[a][None], self.pos[j:j + 1], p.rope_base)[0]
+        return dk, dv

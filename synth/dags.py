@@ -1,0 +1,291 @@
+"""Rollout-DAG topologies for the five workloads and for property tests.
+
+A DAG is given as two tables (the same ones the C library's ``dag_build``
+takes):
+
+* nodes: ``parent`` (-1 for a root, otherwise an index smaller than the node's
+  own), ``length`` (own tokens, >= 0) and the node's slice of the mount table
+  ``[mount_first, mount_first + mount_count)``;
+* mounts: ``src`` node and ``[begin, end)`` in the source's own token offsets.
+
+A node is a maximal run of tokens; a read_thread mount takes effect at the
+first token of the node that lists it (Octopus, Sec. 3.3 "Node Splitting and
+Prefix Deduplication": nodes split at every fork, rewind or read_thread
+boundary).  Only shapes are drawn here; positions and visibility are the
+method's business and are computed elsewhere.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import List, Tuple
+
+import numpy as np
+
+
+@dataclass
+class DagSpec:
+    parent: np.ndarray
+    length: np.ndarray
+    mount_first: np.ndarray
+    mount_count: np.ndarray
+    mount_src: np.ndarray
+    mount_begin: np.ndarray
+    mount_end: np.ndarray
+    name: str = ""
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def n_nodes(self) -> int:
+        return int(self.parent.shape[0])
+
+    @property
+    def n_mounts(self) -> int:
+        return int(self.mount_src.shape[0])
+
+    @property
+    def n_tokens(self) -> int:
+        return int(self.length.sum())
+
+    def mounts_of(self, u: int) -> List[Tuple[int, int, int]]:
+        f, c = int(self.mount_first[u]), int(self.mount_count[u])
+        return [(int(self.mount_src[i]), int(self.mount_begin[i]), int(self.mount_end[i]))
+                for i in range(f, f + c)]
+
+    def node_table(self) -> np.ndarray:
+        """[n, 4] int32 rows (parent, length, mount_first, mount_count)."""
+        return np.stack([self.parent, self.length, self.mount_first, self.mount_count],
+                        axis=1).astype(np.int32)
+
+    def mount_table(self) -> np.ndarray:
+        """[m, 3] int32 rows (src, begin, end)."""
+        if self.n_mounts == 0:
+            return np.zeros((0, 3), np.int32)
+        return np.stack([self.mount_src, self.mount_begin, self.mount_end], axis=1).astype(np.int32)
+
+
+class DagBuilder:
+    """Collects nodes and per-node mounts, then emits a :class:`DagSpec`."""
+
+    def __init__(self) -> None:
+        self.parent: List[int] = []
+        self.length: List[int] = []
+        self.mounts: List[List[Tuple[int, int, int]]] = []
+
+    def node(self, parent: int, length: int) -> int:
+        self.parent.append(int(parent))
+        self.length.append(int(length))
+        self.mounts.append([])
+        return len(self.parent) - 1
+
+    def mount(self, reader: int, src: int, begin: int, end: int) -> None:
+        self.mounts[reader].append((int(src), int(begin), int(end)))
+
+    def build(self, name: str = "", **meta) -> DagSpec:
+        n = len(self.parent)
+        first = np.zeros(n, np.int32)
+        count = np.zeros(n, np.int32)
+        src, beg, end = [], [], []
+        for u in range(n):
+            first[u] = len(src)
+            count[u] = len(self.mounts[u])
+            for s, b, e in self.mounts[u]:
+                src.append(s)
+                beg.append(b)
+                end.append(e)
+        return DagSpec(np.asarray(self.parent, np.int32), np.asarray(self.length, np.int32),
+                       first, count, np.asarray(src, np.int32), np.asarray(beg, np.int32),
+                       np.asarray(end, np.int32), name=name, meta=dict(meta))
+
+
+# ---------------------------------------------------------------------------
+# Workload 1: tiny fp32 tree.  Root of 64 tokens forks three 32-token branches
+# b0, b1, b2; b2 reads b1's last 16 tokens.  ``mount_at`` is b2's own offset
+# where the read happens (it splits b2 into a pre-mount and a post-mount node).
+# ---------------------------------------------------------------------------
+
+def config1_variant(mount_at: int = 16, span: Tuple[int, int] | None = (16, 32),
+                    split: bool = True) -> DagSpec:
+    """Tiny tree; ``span=None`` drops the read, ``span=(b, b)`` is a zero-length read.
+
+    With ``split`` b2 is cut at ``mount_at`` into a pre-read and a post-read node
+    even when there is no read (so that variants with and without a read have the
+    same nodes).
+    """
+    g = DagBuilder()
+    root = g.node(-1, 64)
+    g.node(root, 32)                       # b0
+    b1 = g.node(root, 32)                  # b1
+    if mount_at == 0 or not split:
+        b2 = g.node(root, 32)
+        if span is not None:
+            g.mount(b2, b1, span[0], span[1])
+    else:
+        pre = g.node(root, mount_at)
+        post = g.node(pre, 32 - mount_at)
+        if span is not None:
+            g.mount(post, b1, span[0], span[1])
+    return g.build(name=f"tiny(mount_at={mount_at},span={span})")
+
+
+def config1() -> DagSpec:
+    return config1_variant(16, (16, 32))
+
+
+# ---------------------------------------------------------------------------
+# Workload 2: 8 trees, 4096-token root, fan-out 4 at depths 0 and 1,
+# non-root segments uniform in [1024, 4096], no mounts.
+# ---------------------------------------------------------------------------
+
+def config2(seed: int = 1002, n_trees: int = 8) -> DagSpec:
+    rng = np.random.default_rng(np.random.SeedSequence(seed))
+    g = DagBuilder()
+    for _ in range(n_trees):
+        root = g.node(-1, 4096)
+        kids = [g.node(root, int(rng.integers(1024, 4097))) for _ in range(4)]
+        for c in kids:
+            for _ in range(4):
+                g.node(c, int(rng.integers(1024, 4097)))
+    return g.build(name="trees8_fanout4_depth2")
+
+
+# ---------------------------------------------------------------------------
+# Workload 3: 16 full trees with random depth, fan-out and segment lengths;
+# every node except the first one of its depth level (BFS order) reads one or
+# two earlier same-depth nodes' tail spans (a sibling when it has an earlier
+# one, otherwise a cousin), at a uniform point of its own segment.
+# ---------------------------------------------------------------------------
+
+# Structure seed chosen by tests/golden/select_workload3_seed.py (first seed >= 1003 whose
+# mean unique tokens per tree is in [192K, 320K] and whose flat expansion ratio is in
+# [5.3, 5.9] with reads counted as direct mounts); the script records its findings in
+# tests/golden/workload3_seed.json.  The workload's reads are direct (not transitive).
+CONFIG3_SEED = 1097
+CONFIG3_TRANSITIVE = False
+
+
+def _tree3(rng, g: DagBuilder, seg_lo: int, seg_hi: int, depth_hi: int, fan_lo: int,
+           fan_hi: int, span_lo: int, span_hi: int) -> None:
+    depth = int(rng.integers(1, depth_hi + 1))
+    # BFS over segments; each segment is (depth, parent segment, length)
+    segs = [(0, -1, int(rng.integers(seg_lo, seg_hi + 1)))]
+    children: List[List[int]] = [[]]
+    head = 0
+    while head < len(segs):
+        d, _, _ = segs[head]
+        if d < depth:
+            f = int(rng.integers(fan_lo, fan_hi + 1))
+            for _ in range(f):
+                segs.append((d + 1, head, int(rng.integers(seg_lo, seg_hi + 1))))
+                children.append([])
+                children[head].append(len(segs) - 1)
+        head += 1
+    # reads: source choices, span lengths and read points
+    first_at_depth = {}
+    reads = {}
+    for i, (d, p, ln) in enumerate(segs):
+        if d not in first_at_depth:
+            first_at_depth[d] = i
+            continue
+        n_reads = int(rng.integers(1, 3))
+        sib = [j for j in (children[p] if p >= 0 else []) if j < i]
+        same_depth = [j for j in range(first_at_depth[d], i) if segs[j][0] == d]
+        pool = sib if sib else same_depth
+        rs = []
+        for _ in range(n_reads):
+            src = pool[int(rng.integers(0, len(pool)))]
+            want = int(rng.integers(span_lo, span_hi + 1))
+            rs.append((src, want))
+        at = int(rng.integers(0, ln))
+        reads[i] = (at, rs)
+    # emit nodes: a reading segment splits into pre (own [0, at)) and post (own [at, ln))
+    pre_node, post_node, pre_len = {}, {}, {}
+    for i, (d, p, ln) in enumerate(segs):
+        par = post_node[p] if p >= 0 else -1
+        if i in reads:
+            at, _ = reads[i]
+            a = g.node(par, at)
+            b = g.node(a, ln - at)
+            pre_node[i], post_node[i], pre_len[i] = a, b, at
+        else:
+            a = g.node(par, ln)
+            pre_node[i], post_node[i], pre_len[i] = a, a, ln
+    for i, (at, rs) in reads.items():
+        for src, want in rs:
+            ln = segs[src][2]
+            b = max(0, ln - want)                       # the source's last `want` own tokens
+            cut = pre_len[src]
+            if pre_node[src] != post_node[src] and b < cut:
+                g.mount(post_node[i], pre_node[src], b, cut)
+                g.mount(post_node[i], post_node[src], 0, ln - cut)
+            elif pre_node[src] != post_node[src]:
+                g.mount(post_node[i], post_node[src], b - cut, ln - cut)
+            else:
+                g.mount(post_node[i], post_node[src], b, ln)
+
+
+def config3_structure(seed: int, n_trees: int = 16, seg=(512, 4096), depth_hi: int = 4,
+                      fan=(2, 6), span=(256, 2048)) -> DagSpec:
+    rng = np.random.default_rng(np.random.SeedSequence(seed))
+    g = DagBuilder()
+    for _ in range(n_trees):
+        _tree3(rng, g, seg[0], seg[1], depth_hi, fan[0], fan[1], span[0], span[1])
+    return g.build(name=f"trees16_mounts(seed={seed})", seed=seed, transitive=CONFIG3_TRANSITIVE)
+
+
+def config3(seed: int | None = None, **kw) -> DagSpec:
+    s = CONFIG3_SEED if seed is None else seed
+    if s is None:
+        raise RuntimeError("workload-3 seed not selected yet")
+    return config3_structure(s, **kw)
+
+
+# ---------------------------------------------------------------------------
+# Workload 4: commander-worker episodes.  An 8192-token commander prefix forks 8
+# workers of 32768 own tokens; worker w reads at own offset 16384 + 2048 w the
+# last 8192 tokens of the pre-read part of workers w+1 and w-1 (mod 8).
+# ---------------------------------------------------------------------------
+
+def config4(n_episodes: int = 4, commander: int = 8192, workers: int = 8, budget: int = 32768,
+            span: int = 8192, first_read: int = 16384, read_step: int = 2048) -> DagSpec:
+    g = DagBuilder()
+    for _ in range(n_episodes):
+        root = g.node(-1, commander)
+        at = [first_read + read_step * w for w in range(workers)]
+        pre = [g.node(root, at[w]) for w in range(workers)]
+        post = [g.node(pre[w], budget - at[w]) for w in range(workers)]
+        for w in range(workers):
+            for s in ((w + 1) % workers, (w - 1) % workers):
+                g.mount(post[w], pre[s], at[s] - span, at[s])
+    return g.build(name="commander_workers", transitive=True)
+
+
+# ---------------------------------------------------------------------------
+# Small random DAGs for property tests: random forest, random reads onto
+# earlier non-ancestor nodes (so the combined graph stays acyclic).
+# ---------------------------------------------------------------------------
+
+def random_tiny_dag(rng: np.random.Generator, n_nodes: int = 8, max_len: int = 9,
+                    p_mount: float = 0.5, max_mounts: int = 2, zero_len_p: float = 0.1,
+                    n_roots: int = 1) -> DagSpec:
+    g = DagBuilder()
+    anc: List[set] = []
+    for u in range(n_nodes):
+        if u < n_roots:
+            par = -1
+        else:
+            par = int(rng.integers(0, u))
+        ln = 0 if rng.random() < zero_len_p else int(rng.integers(1, max_len + 1))
+        g.node(par, ln)
+        anc.append(set() if par < 0 else (anc[par] | {par}))
+    for u in range(n_nodes):
+        if rng.random() >= p_mount:
+            continue
+        cands = [s for s in range(u) if s not in anc[u] and g.length[s] > 0]
+        if not cands:
+            continue
+        for _ in range(int(rng.integers(1, max_mounts + 1))):
+            s = cands[int(rng.integers(0, len(cands)))]
+            b = int(rng.integers(0, g.length[s]))
+            e = int(rng.integers(b, g.length[s] + 1))
+            g.mount(u, s, b, e)
+    return g.build(name="random_tiny")
