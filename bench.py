@@ -1,0 +1,255 @@
+#!/usr/bin/env python3
+"""Throughput of packed DAG attention, forward + backward, on one MI355X.
+
+Workload (the metric's configuration): 16 synthetic rollout trees, random
+fan-out 2..6, depth 1..4, segments of 512..4096 tokens, every reader branch
+reading 1-2 earlier same-depth branches' tail spans of 256..2048 tokens
+(direct reads); bf16, 16 query / 4 KV heads, head_dim 128, 64-token pages.
+Inputs are seeded and generated on the GPU, resident in HBM before timing.
+
+Printed JSON (one line on stdout; progress goes to stderr):
+  value       counted TFLOP/s = 3.5 * 4 * d * Hq * P / time per step, P = visible
+              (query, key) pairs over unique query tokens (forward 2 products,
+              backward 5)
+  roofline    the dominant kernel's counted FLOPs per launch over its mean launch
+              time (HIP events on the launch stream), against the 2.5 PFLOP/s
+              dense bf16 MFMA peak
+  x_vs_flat   the same kernels on the flat per-trajectory expansion (each
+              trajectory one causal chain, mounted spans copied in), timed in the
+              same process, divided by the packed time
+  cpu_baseline  the CPU oracle (float32 NumPy) on one trajectory of the workload
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "DAG-attn fwd+bwd TFLOP/s (unique tokens), % bf16 MFMA peak, x vs flat expand"
+PEAK_BF16_TFLOPS = 2500.0
+HQ, HKV, D = 16, 4, 128
+
+
+def log(msg: str) -> None:
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+def gen(shape, seed, stream, dev):
+    import synth
+    import torch
+    return synth.normal(shape, seed, stream, dev, torch.bfloat16)
+
+
+def run_steps(dpa, plan, p, tensors, ws, n):
+    q, k, v, o, lse, do, dq, dk, dv = tensors
+    for _ in range(n):
+        dpa.attn_fwd(plan, p, q, k, v, o=o, lse=lse, ws=ws)
+        dpa.attn_bwd(plan, p, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, ws=ws)
+
+
+def alloc(dpa, plan, p, seed, dev):
+    import torch
+    C = plan.rows
+    q, k, v = gen((C, HQ, D), seed, 1, dev), gen((C, HKV, D), seed, 2, dev), gen((C, HKV, D), seed, 3, dev)
+    do = gen((C, HQ, D), seed, 4, dev)
+    o, dq = torch.empty_like(q), torch.empty_like(q)
+    lse = torch.empty((C, HQ), dtype=torch.float32, device=dev)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    fw, bw = dpa.workspace_bytes(plan, p)
+    ws = torch.empty(max(fw, bw), dtype=torch.uint8, device=dev)
+    return (q, k, v, o, lse, do, dq, dk, dv), ws
+
+
+def flat_time(dpa, spec, plan, p, dev, steps, max_rows=3_000_000):
+    """Seconds per fwd+bwd of the flat expansion, run in chunks of whole trajectories."""
+    import numpy as np
+    import torch
+
+    import synth
+    parent = np.asarray(spec.parent)
+    has_child = np.zeros(len(parent), bool)
+    has_child[parent[parent >= 0]] = True
+    lengths = []
+    for u in np.nonzero(~has_child)[0]:
+        L = int(spec.length[u]) + sum(hi - lo for _, lo, hi in plan.node_ranges(int(u)))
+        if L:
+            lengths.append(L)
+    chunks, cur, rows = [], [], 0
+    for L in lengths:
+        if cur and rows + L > max_rows:
+            chunks.append(cur)
+            cur, rows = [], 0
+        cur.append(L)
+        rows += L
+    if cur:
+        chunks.append(cur)
+    total, pairs = 0.0, 0
+    for i, ch in enumerate(chunks):
+        g = synth.DagBuilder()
+        for L in ch:
+            g.node(-1, L)
+        fplan = dpa.Plan(g.build(name="flat"))
+        pairs += fplan.info["visible_pairs"]
+        tensors, ws = alloc(dpa, fplan, p, 4242 + i, dev)
+        fplan.upload()
+        run_steps(dpa, fplan, p, tensors, ws, 1)          # warm-up (first touch, code objects)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_steps(dpa, fplan, p, tensors, ws, steps)
+        torch.cuda.synchronize()
+        total += (time.perf_counter() - t0) / steps
+        del tensors, ws, fplan
+        torch.cuda.empty_cache()
+        log(f"flat chunk {i + 1}/{len(chunks)}: {len(ch)} trajectories, {sum(ch)} rows")
+    return total, pairs, sum(lengths), len(lengths)
+
+
+def cpu_baseline(spec, plan, budget_s=15.0):
+    """The oracle (float32) on one causal trajectory of the workload, sized to ~budget_s."""
+    import numpy as np
+
+    import synth
+    from oracle.attention import AttnParams, attn_flat
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the process's CPU set
+        cores = len(os.sched_getaffinity(0))
+
+    def run(L):
+        g = synth.DagBuilder()
+        g.node(-1, L)
+        s = g.build()
+        q, k, v, do = synth.attn_inputs(L, HQ, HKV, D, seed=77)
+        t0 = time.perf_counter()
+        attn_flat(s, q.numpy(), k.numpy(), v.numpy(), do.numpy(), AttnParams(HQ, HKV), dtype=np.float32)
+        return time.perf_counter() - t0
+
+    L0 = 1024
+    t0 = run(L0)
+    # trajectory lengths of the workload; take the longest one that fits the budget
+    parent = np.asarray(spec.parent)
+    has_child = np.zeros(len(parent), bool)
+    has_child[parent[parent >= 0]] = True
+    lens = sorted(int(spec.length[u]) + sum(hi - lo for _, lo, hi in plan.node_ranges(int(u)))
+                  for u in np.nonzero(~has_child)[0])
+    fit = [L for L in lens if t0 * (L / L0) ** 2 <= budget_s] or [lens[0]]
+    L = fit[-1]
+    t = run(L)
+    pairs = L * (L + 1) // 2
+    flops = 3.5 * 4 * D * HQ * pairs
+    return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"one trajectory of the workload as a causal chain of {L} tokens, fwd+bwd, "
+                      f"float32 NumPy, {t:.1f} s"}
+
+
+def traffic_record(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if it matches the source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "kernels.hip")
+    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    ent = rec.get("kernels", {}).get(kernel)
+    if not ent or rec.get("kernels_hip_sha256_16") != h:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--flat-steps", type=int, default=1)
+    ap.add_argument("--no-flat", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus "
+              f"{args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import dag_packed_attention_amd as dpa
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    spec = synth.config3()
+    plan = dpa.Plan(spec)
+    info = plan.info
+    log(f"plan: {spec.n_nodes} nodes, {info['tokens']} tokens, {info['rows']} rows, P={info['visible_pairs']}, "
+        f"built in {time.perf_counter() - t0:.1f} s")
+    p = dpa.AttnParams(HQ, HKV, D, "bf16")
+    tensors, ws = alloc(dpa, plan, p, 1003, dev)
+    plan.upload()
+    run_steps(dpa, plan, p, tensors, ws, args.warmup)
+    torch.cuda.synchronize()
+    log(f"warm-up done ({args.warmup} steps)")
+    plan.timing_enable(True, capacity=8 * (args.steps + 1))
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run_steps(dpa, plan, p, tensors, ws, args.steps)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / args.steps
+    kt = plan.timing_read()
+    plan.timing_enable(False)
+    log(f"timed {args.steps} steps: {dt * 1e3:.1f} ms/step; per-kernel ms/launch: "
+        + ", ".join(f"{k}={ms / max(n, 1):.2f}" for k, (ms, n) in kt.items()))
+
+    P = info["visible_pairs"]
+    f_fwd = 4.0 * D * HQ * P
+    counted = 3.5 * f_fwd
+    value = counted / dt / 1e12
+    # counted FLOPs per kernel: forward S and PV; dK/dV kernel S, dP, dV, dK; dQ kernel dQ
+    per_kernel = {"fwd": f_fwd, "dkdv": 2.0 * f_fwd, "dq": 0.5 * f_fwd}
+    dom = max(per_kernel, key=lambda k: kt[k][0])
+    ms = kt[dom][0] / max(kt[dom][1], 1)
+    achieved = per_kernel[dom] / (ms * 1e-3) / 1e12
+    roof = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_record(dom),
+            "ms_per_launch": {k: round(v[0] / max(v[1], 1), 3) for k, v in kt.items()}}
+
+    out = {"metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(dt * 1e3, 2), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+           "tflops_strict_3x": round(3.0 * f_fwd / dt / 1e12, 2),
+           "config": {"workload": "16 rollout trees, fan-out 2-6, depth 1-4, segments 512-4096, "
+                                  "1-2 direct sibling/cousin tail reads of 256-2048 tokens per reader",
+                      "seed": int(spec.meta["seed"]), "unique_tokens": info["tokens"], "rows": info["rows"],
+                      "visible_pairs": P, "flat_rows": info["flat_rows"], "flat_pairs": info["flat_pairs"],
+                      "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "page": 64},
+           "roofline": roof}
+
+    del tensors, ws
+    torch.cuda.empty_cache()
+    if not args.no_flat:
+        t_flat, fpairs, frows, ntraj = flat_time(dpa, spec, plan, p, dev, args.flat_steps)
+        out["x_vs_flat"] = round(t_flat / dt, 3)
+        out["flat"] = {"ms_per_step": round(t_flat * 1e3, 1), "rows": frows, "pairs": fpairs,
+                       "trajectories": ntraj, "pairs_ratio": round(fpairs / P, 3)}
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(spec, plan)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,304 @@
+"""Packed attention over a rollout DAG on AMD MI355X -- Python binding of libdag_attn.
+
+This module only marshals arguments to the C ABI declared in
+``include/dag_attn.h``; every step of the computation runs in the library
+(host compactor in C++, HIP kernels on the GPU).  PyTorch provides device
+memory and the stream.  If the library cannot be loaded (or built in place),
+importing this package fails.
+
+Names follow the C ABI: :class:`Plan` wraps ``dag_build`` and the plan
+queries, :func:`attn_fwd` / :func:`attn_bwd` wrap ``dag_attn_fwd`` /
+``dag_attn_bwd``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdag_attn.so")
+
+DAG_OK = 0
+STATUS = {0: "OK", 1: "INVALID", 2: "NOT_TOPO", 3: "MOUNT_CYCLE", 4: "MOUNT_RANGE",
+          5: "SELF_ANCESTOR_MOUNT", 6: "OVERFLOW", 7: "WORKSPACE", 8: "UNSUPPORTED", 9: "DEVICE"}
+DTYPE_BF16, DTYPE_FP32 = 0, 1
+
+
+class DagNode(ctypes.Structure):
+    _fields_ = [("parent", ctypes.c_int32), ("length", ctypes.c_int32),
+                ("mount_first", ctypes.c_int32), ("mount_count", ctypes.c_int32)]
+
+
+class DagMount(ctypes.Structure):
+    _fields_ = [("src_node", ctypes.c_int32), ("begin", ctypes.c_int32), ("end", ctypes.c_int32)]
+
+
+class DagBuildOpts(ctypes.Structure):
+    _fields_ = [("page_size", ctypes.c_int32), ("q_block", ctypes.c_int32),
+                ("transitive", ctypes.c_int32), ("page_shuffle", ctypes.c_int32)]
+
+
+class DagPlanInfo(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("rows", "tokens", "pages", "query_pages", "visible_pairs",
+                                             "flat_rows", "flat_pairs", "n_trajectories", "fwd_tiles",
+                                             "bwd_entries")] + \
+               [("max_position", ctypes.c_int32), ("transitive", ctypes.c_int32)]
+
+
+class DagAttnParams(ctypes.Structure):
+    _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("rope_base", ctypes.c_float)]
+
+
+class DagError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+        self.code = STATUS.get(status, str(status))
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        from . import build_lib
+        build_lib.build()
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "dag_build": ([ctypes.POINTER(DagNode), I32, ctypes.POINTER(DagMount), I32,
+                       ctypes.POINTER(DagBuildOpts), ctypes.POINTER(P)], I32),
+        "dag_plan_destroy": ([P], None),
+        "dag_plan_info_get": ([P, ctypes.POINTER(DagPlanInfo)], I32),
+        "dag_plan_rows": ([P, P, P], I32),
+        "dag_plan_starts": ([P, P], I32),
+        "dag_plan_node_ranges": ([P, I32, P, I32, ctypes.POINTER(I32)], I32),
+        "dag_plan_upload": ([P, P], I32),
+        "dag_attn_workspace": ([P, ctypes.POINTER(DagAttnParams), ctypes.POINTER(SZ),
+                                ctypes.POINTER(SZ)], I32),
+        "dag_attn_fwd": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, SZ, P], I32),
+        "dag_attn_bwd": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "dag_attn_timing_enable": ([P, I32, I32], I32),
+        "dag_attn_timing_read": ([P, P, P], I32),
+        "dag_last_error": ([], ctypes.c_char_p),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+_lib = _load()
+
+
+def _check(status: int) -> None:
+    if status != DAG_OK:
+        raise DagError(status, _lib.dag_last_error().decode())
+
+
+def last_error() -> str:
+    return _lib.dag_last_error().decode()
+
+
+# ---------------------------------------------------------------------------
+# plans
+# ---------------------------------------------------------------------------
+
+class Plan:
+    """An immutable compiled DAG (``dag_build``).  ``spec`` has the node and mount
+    tables as attributes ``parent, length, mount_first, mount_count, mount_src,
+    mount_begin, mount_end``."""
+
+    def __init__(self, spec, transitive: Optional[bool] = None, page_shuffle: int = 0):
+        if transitive is None:
+            transitive = bool(getattr(spec, "meta", {}).get("transitive", True))
+        n = len(spec.parent)
+        nodes = (DagNode * max(n, 1))()
+        for u in range(n):
+            nodes[u] = DagNode(int(spec.parent[u]), int(spec.length[u]), int(spec.mount_first[u]),
+                               int(spec.mount_count[u]))
+        m = len(spec.mount_src)
+        mounts = (DagMount * max(m, 1))()
+        for i in range(m):
+            mounts[i] = DagMount(int(spec.mount_src[i]), int(spec.mount_begin[i]), int(spec.mount_end[i]))
+        opts = DagBuildOpts(64, 64, 1 if transitive else 0, int(page_shuffle))
+        self._h = ctypes.c_void_p()
+        _check(_lib.dag_build(nodes, n, mounts, m, ctypes.byref(opts), ctypes.byref(self._h)))
+        info = DagPlanInfo()
+        _check(_lib.dag_plan_info_get(self._h, ctypes.byref(info)))
+        self.info = {f: getattr(info, f) for f, _ in DagPlanInfo._fields_}
+        self.n_nodes = n
+        self._rows = None
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value and _lib is not None:
+            _lib.dag_plan_destroy(h)
+            self._h = None
+
+    @property
+    def rows(self) -> int:
+        return int(self.info["rows"])
+
+    @property
+    def tokens(self) -> int:
+        return int(self.info["tokens"])
+
+    def row_maps(self) -> Tuple[np.ndarray, np.ndarray]:
+        """(row_of_token [U], pos_of_row [C]) as int32 arrays."""
+        if self._rows is None:
+            rot = np.zeros(max(self.tokens, 1), np.int32)
+            por = np.zeros(max(self.rows, 1), np.int32)
+            _check(_lib.dag_plan_rows(self._h, rot.ctypes.data, por.ctypes.data))
+            self._rows = (rot[: self.tokens], por[: self.rows])
+        return self._rows
+
+    def starts(self) -> np.ndarray:
+        out = np.zeros(self.n_nodes, np.int32)
+        _check(_lib.dag_plan_starts(self._h, out.ctypes.data))
+        return out
+
+    def node_ranges(self, u: int):
+        """[(src, lo, hi), ...]: non-self visibility of node u in kernel visiting order."""
+        n = ctypes.c_int32(0)
+        _check(_lib.dag_plan_node_ranges(self._h, int(u), None, 0, ctypes.byref(n)))
+        buf = np.zeros(max(3 * n.value, 3), np.int32)
+        _check(_lib.dag_plan_node_ranges(self._h, int(u), buf.ctypes.data, n.value, ctypes.byref(n)))
+        return [tuple(int(x) for x in buf[3 * i: 3 * i + 3]) for i in range(n.value)]
+
+    def upload(self, stream=None) -> None:
+        _check(_lib.dag_plan_upload(self._h, _stream_ptr(stream)))
+
+    KERNELS = ("prologue_fwd", "fwd", "prologue_bwd", "dkdv", "dq")
+
+    def timing_enable(self, enable: bool = True, capacity: int = 256) -> None:
+        """Record HIP events around each kernel the library launches for this plan."""
+        _check(_lib.dag_attn_timing_enable(self._h, 1 if enable else 0, int(capacity)))
+
+    def timing_read(self):
+        """{kernel: (total ms, launches)} since the last read (waits for the events)."""
+        ms = np.zeros(len(self.KERNELS), np.float64)
+        cnt = np.zeros(len(self.KERNELS), np.int64)
+        _check(_lib.dag_attn_timing_read(self._h, ms.ctypes.data, cnt.ctypes.data))
+        return {k: (float(ms[i]), int(cnt[i])) for i, k in enumerate(self.KERNELS)}
+
+
+# ---------------------------------------------------------------------------
+# attention
+# ---------------------------------------------------------------------------
+
+@dataclass
+class AttnParams:
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    dtype: str = "bf16"          # "bf16" or "fp32"
+    scale: float = 0.0           # 0 -> 1/sqrt(head_dim)
+    rope_base: float = 10000.0   # 0 -> no rotation
+
+    def c(self) -> DagAttnParams:
+        dt = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}[self.dtype]
+        return DagAttnParams(self.n_q_heads, self.n_kv_heads, self.head_dim, dt, float(self.scale),
+                             float(self.rope_base))
+
+    @property
+    def torch_dtype(self):
+        import torch
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+
+def _stream_ptr(stream) -> ctypes.c_void_p:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def workspace_bytes(plan: Plan, p: AttnParams) -> Tuple[int, int]:
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    cp = p.c()
+    _check(_lib.dag_attn_workspace(plan._h, ctypes.byref(cp), ctypes.byref(f), ctypes.byref(b)))
+    return int(f.value), int(b.value)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check_tensor(name, t, rows, heads, d, dtype, device):
+    if t.dtype != dtype or tuple(t.shape) != (rows, heads, d) or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name}: expected contiguous {dtype} [{rows}, {heads}, {d}] on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def attn_fwd(plan: Plan, p: AttnParams, q, k, v, o=None, lse=None, ws=None, stream=None):
+    """``dag_attn_fwd``: q [C,Hq,D], k/v [C,Hkv,D] in row layout -> (o [C,Hq,D], lse [C,Hq] fp32)."""
+    import torch
+    C, dt, dev = plan.rows, p.torch_dtype, q.device
+    _check_tensor("q", q, C, p.n_q_heads, p.head_dim, dt, dev)
+    _check_tensor("k", k, C, p.n_kv_heads, p.head_dim, dt, dev)
+    _check_tensor("v", v, C, p.n_kv_heads, p.head_dim, dt, dev)
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((C, p.n_q_heads), dtype=torch.float32, device=dev)
+    need, _ = workspace_bytes(plan, p)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    cp = p.c()
+    _check(_lib.dag_attn_fwd(plan._h, ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                             _ptr(ws), ws.numel(), _stream_ptr(stream)))
+    return o, lse
+
+
+def attn_bwd(plan: Plan, p: AttnParams, q, k, v, o, lse, dO, dq=None, dk=None, dv=None, ws=None,
+             stream=None):
+    """``dag_attn_bwd``: returns (dq [C,Hq,D], dk [C,Hkv,D], dv [C,Hkv,D])."""
+    import torch
+    C, dt, dev = plan.rows, p.torch_dtype, q.device
+    for name, t, h in (("q", q, p.n_q_heads), ("k", k, p.n_kv_heads), ("v", v, p.n_kv_heads),
+                       ("o", o, p.n_q_heads), ("dO", dO, p.n_q_heads)):
+        _check_tensor(name, t, C, h, p.head_dim, dt, dev)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    _, need = workspace_bytes(plan, p)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    cp = p.c()
+    _check(_lib.dag_attn_bwd(plan._h, ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                             _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                             _stream_ptr(stream)))
+    return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# layout helpers (token-major <-> row layout); pure data movement
+# ---------------------------------------------------------------------------
+
+def to_rows(plan: Plan, x_tok, fill: float = 0.0):
+    """Scatter token-major [U, H, D] into the plan's row layout [C, H, D] (padding = fill)."""
+    import torch
+    rot, _ = plan.row_maps()
+    out = torch.full((plan.rows,) + tuple(x_tok.shape[1:]), fill, dtype=x_tok.dtype, device=x_tok.device)
+    if plan.tokens:
+        out[torch.as_tensor(rot, dtype=torch.long, device=x_tok.device)] = x_tok
+    return out
+
+
+def from_rows(plan: Plan, x_rows):
+    """Gather the plan's row layout [C, ...] back to token-major [U, ...]."""
+    import torch
+    rot, _ = plan.row_maps()
+    return x_rows[torch.as_tensor(rot, dtype=torch.long, device=x_rows.device)]
+
+
+__all__ = ["Plan", "AttnParams", "DagError", "attn_fwd", "attn_bwd", "workspace_bytes", "to_rows",
+           "from_rows", "last_error", "LIB_PATH"]

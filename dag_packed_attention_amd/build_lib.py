@@ -1,0 +1,57 @@
+"""Build libdag_attn.so in-tree for gfx950.
+
+    python dag_packed_attention_amd/build_lib.py      (or call build())
+
+The host compactor (plan.cpp) is plain C++ and is compiled with g++; the ABI
+glue and the kernels are compiled with hipcc for gfx950.  Packed-fp32 code
+generation is switched off for the device code.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libdag_attn.so")
+ARCH = os.environ.get("DAG_ATTN_ARCH", "gfx950")
+
+HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             f"-I{os.path.join(ROOT, 'include')}"]
+CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{os.path.join(ROOT, 'include')}"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"build step failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    return r
+
+
+def build(verbose: bool = False) -> str:
+    obj_dir = os.path.join(HERE, "_build")
+    os.makedirs(obj_dir, exist_ok=True)
+    steps = [
+        ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "plan.cpp"), "-o", os.path.join(obj_dir, "plan.o")],
+        [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "abi.cpp"), "-o", os.path.join(obj_dir, "abi.o")],
+        [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "kernels.hip"), "-o", os.path.join(obj_dir, "kernels.o")],
+    ]
+    with ThreadPoolExecutor(len(steps)) as ex:
+        for r in ex.map(_run, steps):
+            if verbose and r.stderr:
+                sys.stderr.write(r.stderr)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp,
+          *(os.path.join(obj_dir, f) for f in ("plan.o", "abi.o", "kernels.o"))])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,496 @@
+// C ABI of libdag_attn: plan management, workspace sizing and kernel launches.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "launch.hpp"
+#include "plan.hpp"
+
+struct dag_plan {
+  dagattn::Plan p;
+};
+
+namespace dagattn {
+
+struct DeviceTables {
+  int device = -1;
+  void* block = nullptr;
+  int32_t* pos_of_row = nullptr;
+  Tile* tiles = nullptr;
+  QPage* qpages = nullptr;
+  int32_t* fwd_order = nullptr;
+  KEntry* kentries = nullptr;
+  int32_t* kv_off = nullptr;
+  int32_t* bwd_order = nullptr;
+  int32_t* page_table = nullptr;
+  int32_t* page_nrows = nullptr;
+};
+
+struct Timing {
+  std::vector<hipEvent_t> ev;     // 2 * capacity events
+  std::vector<int> kernel;        // kernel id of each recorded pair
+  int used = 0;
+};
+
+}  // namespace dagattn
+
+using namespace dagattn;
+
+namespace {
+
+thread_local std::string g_err;
+
+dag_status set_err(dag_status code, const std::string& msg) {
+  g_err = msg;
+  return code;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// A bump allocator over the caller's workspace.
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base((char*)b) {}
+  template <typename T> T* take(size_t count) {
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += align256(count * sizeof(T));
+    return p;
+  }
+};
+
+bool mfma_path(const dag_attn_params* p) {
+  return p->dtype == DAG_DTYPE_BF16 && p->head_dim == 128 && p->n_q_heads == 4 * p->n_kv_heads;
+}
+
+dag_status check_params(const dag_attn_params* p) {
+  if (!p) return set_err(DAG_E_INVALID, "null params");
+  if (p->n_q_heads <= 0 || p->n_kv_heads <= 0 || p->n_q_heads % p->n_kv_heads)
+    return set_err(DAG_E_UNSUPPORTED, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (p->head_dim < 2 || p->head_dim > 128 || (p->head_dim & 1))
+    return set_err(DAG_E_UNSUPPORTED, "head_dim must be even and in [2, 128]");
+  if (p->dtype != DAG_DTYPE_BF16 && p->dtype != DAG_DTYPE_FP32)
+    return set_err(DAG_E_UNSUPPORTED, "dtype must be DAG_DTYPE_BF16 or DAG_DTYPE_FP32");
+  if (!(p->rope_base >= 0.f) || std::isinf(p->rope_base) || (p->rope_base > 0.f && p->rope_base <= 1.f))
+    return set_err(DAG_E_INVALID, "rope_base must be 0 (off) or > 1");
+  if (!std::isfinite(p->scale)) return set_err(DAG_E_INVALID, "scale must be finite");
+  return DAG_OK;
+}
+
+LaunchShape shape_of(const Plan& P, const dag_attn_params* p) {
+  LaunchShape s;
+  s.C = P.info.rows;
+  s.pages = P.info.pages;
+  s.Hq = p->n_q_heads;
+  s.Hkv = p->n_kv_heads;
+  s.D = p->head_dim;
+  s.scale = p->scale != 0.f ? p->scale : (float)(1.0 / std::sqrt((double)p->head_dim));
+  s.log2_base = p->rope_base > 0.f ? std::log2((double)p->rope_base) : 0.0;
+  return s;
+}
+
+// Workspace regions.  The same function sizes and carves them.
+struct FwdWs {
+  float2* cs;
+  void* qn;
+  void* kn;
+  void* vt;
+};
+struct BwdWs {
+  float2* cs;
+  void* qn;
+  void* kn;
+  void* qt;
+  void* kt;
+  void* dOt;
+  float2* ld;
+};
+
+size_t carve_fwd(const LaunchShape& s, bool mfma, void* base, FwdWs* w) {
+  Carve c(base);
+  const size_t C = (size_t)s.C;
+  w->cs = s.log2_base > 0 ? c.take<float2>(C * (s.D / 2)) : nullptr;
+  if (mfma) {
+    w->qn = c.take<bf16_t>(C * s.Hq * s.D);
+    w->kn = c.take<bf16_t>(C * s.Hkv * s.D);
+    w->vt = c.take<bf16_t>(C * s.Hkv * s.D);
+  } else {
+    w->qn = c.take<float>(C * s.Hq * s.D);
+    w->kn = c.take<float>(C * s.Hkv * s.D);
+    w->vt = nullptr;
+  }
+  return c.off;
+}
+
+size_t carve_bwd(const LaunchShape& s, bool mfma, void* base, BwdWs* w) {
+  Carve c(base);
+  const size_t C = (size_t)s.C;
+  w->cs = s.log2_base > 0 ? c.take<float2>(C * (s.D / 2)) : nullptr;
+  w->ld = c.take<float2>(C * s.Hq);
+  if (mfma) {
+    w->qn = c.take<bf16_t>(C * s.Hq * s.D);
+    w->qt = c.take<bf16_t>(C * s.Hq * s.D);
+    w->dOt = c.take<bf16_t>(C * s.Hq * s.D);
+    w->kn = c.take<bf16_t>(C * s.Hkv * s.D);
+    w->kt = c.take<bf16_t>(C * s.Hkv * s.D);
+  } else {
+    w->qn = c.take<float>(C * s.Hq * s.D);
+    w->kn = c.take<float>(C * s.Hkv * s.D);
+    w->qt = w->dOt = w->kt = nullptr;
+  }
+  return c.off;
+}
+
+template <typename T> T* dev_take(char* block, size_t& off, size_t count) {
+  T* p = (T*)(block + off);
+  off += align256(count * sizeof(T));
+  return p;
+}
+
+dag_status ensure_uploaded(Plan& P, hipStream_t st) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return set_err(DAG_E_DEVICE, "hipGetDevice failed");
+  if (P.dev) {
+    if (P.dev->device != dev)
+      return set_err(DAG_E_DEVICE, "plan was uploaded to device " + std::to_string(P.dev->device) +
+                                       ", current device is " + std::to_string(dev));
+    return DAG_OK;
+  }
+  size_t bytes = 0;
+  bytes += align256(P.pos_of_row.size() * 4) + align256(P.tiles.size() * sizeof(Tile)) +
+           align256(P.qpages.size() * sizeof(QPage)) + align256(P.fwd_order.size() * 4) +
+           align256(P.kentries.size() * sizeof(KEntry)) + align256(P.kv_off.size() * 4) +
+           align256(P.bwd_order.size() * 4) + align256(P.page_table.size() * 4) +
+           align256(P.page_nrows.size() * 4) + 256;
+  DeviceTables* D = new (std::nothrow) DeviceTables();
+  if (!D) return set_err(DAG_E_DEVICE, "out of host memory");
+  D->device = dev;
+  if (hipMalloc(&D->block, bytes) != hipSuccess) {
+    delete D;
+    (void)hipGetLastError();
+    return set_err(DAG_E_DEVICE, "hipMalloc of " + std::to_string(bytes) + " plan bytes failed");
+  }
+  char* b = (char*)D->block;
+  size_t off = 0;
+  D->pos_of_row = dev_take<int32_t>(b, off, P.pos_of_row.size());
+  D->tiles = dev_take<Tile>(b, off, P.tiles.size());
+  D->qpages = dev_take<QPage>(b, off, P.qpages.size());
+  D->fwd_order = dev_take<int32_t>(b, off, P.fwd_order.size());
+  D->kentries = dev_take<KEntry>(b, off, P.kentries.size());
+  D->kv_off = dev_take<int32_t>(b, off, P.kv_off.size());
+  D->bwd_order = dev_take<int32_t>(b, off, P.bwd_order.size());
+  D->page_table = dev_take<int32_t>(b, off, P.page_table.size());
+  D->page_nrows = dev_take<int32_t>(b, off, P.page_nrows.size());
+  auto put = [&](void* dst, const void* src, size_t n) {
+    return n == 0 || hipMemcpyAsync(dst, src, n, hipMemcpyHostToDevice, st) == hipSuccess;
+  };
+  bool ok = put(D->pos_of_row, P.pos_of_row.data(), P.pos_of_row.size() * 4) &&
+            put(D->tiles, P.tiles.data(), P.tiles.size() * sizeof(Tile)) &&
+            put(D->qpages, P.qpages.data(), P.qpages.size() * sizeof(QPage)) &&
+            put(D->fwd_order, P.fwd_order.data(), P.fwd_order.size() * 4) &&
+            put(D->kentries, P.kentries.data(), P.kentries.size() * sizeof(KEntry)) &&
+            put(D->kv_off, P.kv_off.data(), P.kv_off.size() * 4) &&
+            put(D->bwd_order, P.bwd_order.data(), P.bwd_order.size() * 4) &&
+            put(D->page_table, P.page_table.data(), P.page_table.size() * 4) &&
+            put(D->page_nrows, P.page_nrows.data(), P.page_nrows.size() * 4);
+  // the host vectors are pageable: finish the copies before returning
+  ok = ok && hipStreamSynchronize(st) == hipSuccess;
+  if (!ok) {
+    (void)hipFree(D->block);
+    delete D;
+    (void)hipGetLastError();
+    return set_err(DAG_E_DEVICE, "plan upload failed");
+  }
+  P.dev = D;
+  return DAG_OK;
+}
+
+// Event pair around one kernel launch while timing is enabled.
+struct Span {
+  Timing* t;
+  int slot = -1;
+  hipStream_t st;
+  Span(Plan& P, int kernel, hipStream_t s) : t(P.timing), st(s) {
+    if (t && t->used < (int)t->kernel.size()) {
+      slot = t->used++;
+      t->kernel[slot] = kernel;
+      (void)hipEventRecord(t->ev[2 * slot], st);
+    }
+  }
+  ~Span() {
+    if (slot >= 0) (void)hipEventRecord(t->ev[2 * slot + 1], st);
+  }
+};
+
+void destroy_timing(Plan& P) {
+  if (!P.timing) return;
+  for (hipEvent_t e : P.timing->ev) (void)hipEventDestroy(e);
+  delete P.timing;
+  P.timing = nullptr;
+}
+
+dag_status launched(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_err(DAG_E_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+  return DAG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dag_last_error(void) { return g_err.c_str(); }
+
+dag_status dag_build(const dag_node* nodes, int32_t n_nodes, const dag_mount* mounts, int32_t n_mounts,
+                     const dag_build_opts* opts, dag_plan** out) {
+  if (!out) return set_err(DAG_E_INVALID, "null output pointer");
+  *out = nullptr;
+  dag_plan* plan = new (std::nothrow) dag_plan();
+  if (!plan) return set_err(DAG_E_INVALID, "out of host memory");
+  std::string err;
+  dag_status st;
+  try {
+    st = build_plan(nodes, n_nodes, mounts, n_mounts, opts, &plan->p, &err);
+  } catch (const std::bad_alloc&) {
+    st = DAG_E_OVERFLOW;
+    err = "out of host memory while building the plan";
+  }
+  if (st != DAG_OK) {
+    delete plan;
+    return set_err(st, err);
+  }
+  *out = plan;
+  g_err.clear();
+  return DAG_OK;
+}
+
+void dag_plan_destroy(dag_plan* plan) {
+  if (!plan) return;
+  destroy_timing(plan->p);
+  if (plan->p.dev) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != plan->p.dev->device) (void)hipSetDevice(plan->p.dev->device);
+    (void)hipFree(plan->p.dev->block);
+    if (cur >= 0 && cur != plan->p.dev->device) (void)hipSetDevice(cur);
+    delete plan->p.dev;
+  }
+  delete plan;
+}
+
+dag_status dag_plan_info_get(const dag_plan* plan, dag_plan_info* out) {
+  if (!plan || !out) return set_err(DAG_E_INVALID, "null argument");
+  *out = plan->p.info;
+  return DAG_OK;
+}
+
+dag_status dag_plan_rows(const dag_plan* plan, int32_t* row_of_token, int32_t* pos_of_row) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  if (row_of_token && !plan->p.row_of_token.empty())
+    std::memcpy(row_of_token, plan->p.row_of_token.data(), plan->p.row_of_token.size() * 4);
+  if (pos_of_row && !plan->p.pos_of_row.empty())
+    std::memcpy(pos_of_row, plan->p.pos_of_row.data(), plan->p.pos_of_row.size() * 4);
+  return DAG_OK;
+}
+
+dag_status dag_plan_starts(const dag_plan* plan, int32_t* start) {
+  if (!plan || !start) return set_err(DAG_E_INVALID, "null argument");
+  std::memcpy(start, plan->p.start.data(), plan->p.start.size() * 4);
+  return DAG_OK;
+}
+
+dag_status dag_plan_node_ranges(const dag_plan* plan, int32_t u, int32_t* out, int32_t cap, int32_t* n) {
+  if (!plan || !n) return set_err(DAG_E_INVALID, "null argument");
+  const Plan& P = plan->p;
+  if (u < 0 || u >= P.n_nodes) return set_err(DAG_E_INVALID, "node index out of range");
+  const int64_t b = P.range_off[u], e = P.range_off[u + 1];
+  *n = (int32_t)(e - b);
+  for (int64_t i = b; i < e && i - b < cap && out; ++i)
+    for (int j = 0; j < 3; ++j) out[3 * (i - b) + j] = P.ranges[3 * i + j];
+  return DAG_OK;
+}
+
+dag_status dag_attn_timing_enable(dag_plan* plan, int32_t enable, int32_t capacity) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  destroy_timing(plan->p);
+  if (!enable) return DAG_OK;
+  if (capacity <= 0 || capacity > (1 << 20)) return set_err(DAG_E_INVALID, "capacity out of range");
+  Timing* t = new (std::nothrow) Timing();
+  if (!t) return set_err(DAG_E_DEVICE, "out of host memory");
+  t->ev.assign(2 * (size_t)capacity, nullptr);
+  t->kernel.assign(capacity, -1);
+  for (auto& e : t->ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      plan->p.timing = t;
+      destroy_timing(plan->p);
+      return set_err(DAG_E_DEVICE, "hipEventCreate failed");
+    }
+  plan->p.timing = t;
+  return DAG_OK;
+}
+
+dag_status dag_attn_timing_read(dag_plan* plan, double* ms, int64_t* counts) {
+  if (!plan || !ms || !counts) return set_err(DAG_E_INVALID, "null argument");
+  for (int k = 0; k < DAG_K_COUNT; ++k) {
+    ms[k] = 0;
+    counts[k] = 0;
+  }
+  Timing* t = plan->p.timing;
+  if (!t) return set_err(DAG_E_INVALID, "timing is not enabled");
+  for (int i = 0; i < t->used; ++i) {
+    float e = 0.f;
+    if (hipEventSynchronize(t->ev[2 * i + 1]) != hipSuccess ||
+        hipEventElapsedTime(&e, t->ev[2 * i], t->ev[2 * i + 1]) != hipSuccess)
+      return set_err(DAG_E_DEVICE, "reading timing events failed");
+    ms[t->kernel[i]] += e;
+    counts[t->kernel[i]] += 1;
+  }
+  t->used = 0;
+  return DAG_OK;
+}
+
+dag_status dag_plan_upload(dag_plan* plan, void* hip_stream) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  return ensure_uploaded(plan->p, (hipStream_t)hip_stream);
+}
+
+dag_status dag_attn_workspace(const dag_plan* plan, const dag_attn_params* p, size_t* fwd_bytes,
+                              size_t* bwd_bytes) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  dag_status st = check_params(p);
+  if (st != DAG_OK) return st;
+  const LaunchShape s = shape_of(plan->p, p);
+  FwdWs fw;
+  BwdWs bw;
+  if (fwd_bytes) *fwd_bytes = carve_fwd(s, mfma_path(p), nullptr, &fw);
+  if (bwd_bytes) *bwd_bytes = carve_bwd(s, mfma_path(p), nullptr, &bw);
+  return DAG_OK;
+}
+
+dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k, const void* v,
+                        void* o, float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  dag_status st = check_params(p);
+  if (st != DAG_OK) return st;
+  Plan& P = plan->p;
+  if (P.info.rows == 0) return DAG_OK;
+  if (!q || !k || !v || !o || !lse) return set_err(DAG_E_INVALID, "null tensor pointer");
+  const LaunchShape s = shape_of(P, p);
+  const bool mfma = mfma_path(p);
+  FwdWs w;
+  const size_t need = carve_fwd(s, mfma, nullptr, &w);
+  if (!ws || ws_bytes < need)
+    return set_err(DAG_E_WORKSPACE, "forward workspace needs " + std::to_string(need) + " bytes");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if ((st = ensure_uploaded(P, stream)) != DAG_OK) return st;
+  carve_fwd(s, mfma, ws, &w);
+  const DeviceTables& D = *P.dev;
+  const int64_t n_qp = (int64_t)P.qpages.size();
+  {
+    Span sp(P, DAG_K_PROLOGUE_FWD, stream);
+    if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
+    if (mfma) {
+      launch_relayout<bf16_t, bf16_t>(s, (const bf16_t*)q, w.cs, D.page_nrows, (bf16_t*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<bf16_t, bf16_t>(s, (const bf16_t*)k, w.cs, D.page_nrows, (bf16_t*)w.kn, nullptr, s.Hkv, stream);
+      launch_relayout<bf16_t, bf16_t>(s, (const bf16_t*)v, nullptr, D.page_nrows, nullptr, (bf16_t*)w.vt, s.Hkv,
+                                      stream);
+    } else if (p->dtype == DAG_DTYPE_BF16) {
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, D.page_nrows, (float*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv, stream);
+    } else {
+      launch_relayout<float, float>(s, (const float*)q, w.cs, D.page_nrows, (float*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<float, float>(s, (const float*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv, stream);
+    }
+  }
+  {
+    Span sp(P, DAG_K_FWD, stream);
+    if (mfma)
+      launch_fwd_mfma(s, n_qp, (const bf16_t*)w.qn, (const bf16_t*)w.kn, (const bf16_t*)w.vt, D.qpages, D.fwd_order,
+                      D.tiles, (bf16_t*)o, lse, stream);
+    else if (p->dtype == DAG_DTYPE_BF16)
+      launch_fwd_simple<bf16_t>(s, n_qp, (const float*)w.qn, (const float*)w.kn, (const bf16_t*)v, D.qpages,
+                                D.fwd_order, D.tiles, (bf16_t*)o, lse, stream);
+    else
+      launch_fwd_simple<float>(s, n_qp, (const float*)w.qn, (const float*)w.kn, (const float*)v, D.qpages,
+                               D.fwd_order, D.tiles, (float*)o, lse, stream);
+  }
+  return launched("dag_attn_fwd");
+}
+
+dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k, const void* v,
+                        const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
+                        size_t ws_bytes, void* hip_stream) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  dag_status st = check_params(p);
+  if (st != DAG_OK) return st;
+  Plan& P = plan->p;
+  if (P.info.rows == 0) return DAG_OK;
+  if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv)
+    return set_err(DAG_E_INVALID, "null tensor pointer");
+  const LaunchShape s = shape_of(P, p);
+  const bool mfma = mfma_path(p);
+  BwdWs w;
+  const size_t need = carve_bwd(s, mfma, nullptr, &w);
+  if (!ws || ws_bytes < need)
+    return set_err(DAG_E_WORKSPACE, "backward workspace needs " + std::to_string(need) + " bytes");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if ((st = ensure_uploaded(P, stream)) != DAG_OK) return st;
+  carve_bwd(s, mfma, ws, &w);
+  const DeviceTables& D = *P.dev;
+  const int64_t n_qp = (int64_t)P.qpages.size(), n_kvp = (int64_t)P.bwd_order.size();
+  if (mfma) {
+    const bf16_t *q16 = (const bf16_t*)q, *k16 = (const bf16_t*)k, *v16 = (const bf16_t*)v;
+    const bf16_t *o16 = (const bf16_t*)o, *d16 = (const bf16_t*)dO;
+    {
+      Span sp(P, DAG_K_PROLOGUE_BWD, stream);
+      if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
+      launch_rowdot<bf16_t>(s, o16, d16, lse, D.page_nrows, w.ld, stream);
+      launch_relayout<bf16_t, bf16_t>(s, q16, w.cs, D.page_nrows, (bf16_t*)w.qn, (bf16_t*)w.qt, s.Hq, stream);
+      launch_relayout<bf16_t, bf16_t>(s, k16, w.cs, D.page_nrows, (bf16_t*)w.kn, (bf16_t*)w.kt, s.Hkv, stream);
+      launch_relayout<bf16_t, bf16_t>(s, d16, nullptr, D.page_nrows, nullptr, (bf16_t*)w.dOt, s.Hq, stream);
+    }
+    {
+      Span sp(P, DAG_K_DKDV, stream);
+      launch_dkdv_mfma(s, n_kvp, (const bf16_t*)w.qn, (const bf16_t*)w.qt, (const bf16_t*)w.kn, v16, d16,
+                       (const bf16_t*)w.dOt, w.ld, w.cs, D.bwd_order, D.kv_off, D.kentries, D.page_table,
+                       D.page_nrows, (bf16_t*)dk, (bf16_t*)dv, stream);
+    }
+    {
+      Span sp(P, DAG_K_DQ, stream);
+      launch_dq_mfma(s, n_qp, (const bf16_t*)w.qn, (const bf16_t*)w.kn, (const bf16_t*)w.kt, v16, d16, w.ld, w.cs,
+                     D.qpages, D.fwd_order, D.tiles, (bf16_t*)dq, stream);
+    }
+  } else if (p->dtype == DAG_DTYPE_BF16) {
+    {
+      Span sp(P, DAG_K_PROLOGUE_BWD, stream);
+      if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
+      launch_rowdot<bf16_t>(s, (const bf16_t*)o, (const bf16_t*)dO, lse, D.page_nrows, w.ld, stream);
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, D.page_nrows, (float*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv, stream);
+    }
+    Span sp(P, DAG_K_DKDV, stream);
+    launch_bwd_simple<bf16_t>(s, n_qp, n_kvp, (const float*)w.qn, (const float*)w.kn, (const bf16_t*)v,
+                              (const bf16_t*)dO, w.ld, w.cs, D.qpages, D.fwd_order, D.tiles, D.bwd_order, D.kv_off,
+                              D.kentries, D.page_table, D.page_nrows, (bf16_t*)dq, (bf16_t*)dk, (bf16_t*)dv, stream);
+  } else {
+    {
+      Span sp(P, DAG_K_PROLOGUE_BWD, stream);
+      if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
+      launch_rowdot<float>(s, (const float*)o, (const float*)dO, lse, D.page_nrows, w.ld, stream);
+      launch_relayout<float, float>(s, (const float*)q, w.cs, D.page_nrows, (float*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<float, float>(s, (const float*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv, stream);
+    }
+    Span sp(P, DAG_K_DKDV, stream);
+    launch_bwd_simple<float>(s, n_qp, n_kvp, (const float*)w.qn, (const float*)w.kn, (const float*)v,
+                             (const float*)dO, w.ld, w.cs, D.qpages, D.fwd_order, D.tiles, D.bwd_order, D.kv_off,
+                             D.kentries, D.page_table, D.page_nrows, (float*)dq, (float*)dk, (float*)dv, stream);
+  }
+  return launched("dag_attn_bwd");
+}
+
+}  // extern "C"

@@ -1,0 +1,828 @@
+// HIP kernels for packed attention over a rollout DAG, written for gfx950.
+//
+// Data layout in HBM (C compact rows = pages * 64):
+//   user tensors   q, o, dO, dq  [C][Hq][D]     k, v, dk, dv  [C][Hkv][D]    lse [C][Hq] fp32
+//   workspace      cs  [C][D/2]  float2        cos/sin of the Eq. 1 rotation per row
+//                  xn  [page][H][64][D]        rotated, page-major ("natural")
+//                  xt  [page][H][D][64]        rotated, page-major, transposed, rows of every
+//                                              16-group stored with bits 2 and 3 of the row
+//                                              index swapped (the order in which an MFMA
+//                                              accumulator lane holds them, see below)
+//                  ld  [page][Hq][64] float2   (lse * log2 e, rowsum(dO * O)) for the backward
+//
+// MFMA path (bf16, D = 128, Hq = 4 Hkv).  A work-group serves one 64-row block
+// and one KV head; its four waves are the four query heads of that GQA group,
+// so every K/V tile staged in LDS is read by four heads.  Products are taken
+// in the transposed orientation S^T = K Q^T and O^T = V^T P^T with
+// v_mfma_f32_32x32x16_bf16: a 32x32 accumulator lane then holds one query
+// row (column n = lane % 32) and 16 keys, so the online-softmax state is
+// per lane and only the max crosses lanes (lane ^ 32).  Accumulator element r
+// of lane l is row m = 8 (r / 4) + 4 (l / 32) + r % 4.  Feeding it straight
+// back as the B operand of the next product makes the contraction index of
+// the two operands follow that same order, hence the bit-swapped rows of the
+// transposed layouts.
+//
+// The backward is two kernels.  dK/dV: one work-group per KV page and KV head
+// walks the page's reader list (every query block that sees the page, in a
+// fixed order), keeps dK and dV in registers, sums the four heads through LDS
+// in a fixed order and writes once: deterministic, no atomics.  dQ: one
+// work-group per query block, like the forward.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "launch.hpp"
+#include "plan.hpp"
+
+namespace dagattn {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+__device__ __forceinline__ bf16_t f2bf(float x) {
+  __bf16 b = (__bf16)x;
+  return *reinterpret_cast<bf16_t*>(&b);
+}
+template <typename T> __device__ __forceinline__ float ld_f(const T* p);
+template <> __device__ __forceinline__ float ld_f<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld_f<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+template <typename T> __device__ __forceinline__ void st_f(T* p, float x);
+template <> __device__ __forceinline__ void st_f<float>(float* p, float x) { *p = x; }
+template <> __device__ __forceinline__ void st_f<bf16_t>(bf16_t* p, float x) { *p = f2bf(x); }
+
+// position of row r inside its transposed 16-group (bits 2 and 3 swapped)
+__device__ __forceinline__ int tperm(int r) {
+  return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
+}
+
+// ---------------------------------------------------------------------------
+// prologue
+// ---------------------------------------------------------------------------
+
+// cos/sin of the rotary angle pos * base^(-2i/D) for every row and frequency,
+// formed in double precision and rounded to float.
+__global__ void cs_kernel(const int32_t* __restrict__ pos_of_row, float2* __restrict__ cs,
+                          int64_t C, int half, double log2_base, int D) {
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= C * half) return;
+  const int64_t row = idx / half;
+  const int i = (int)(idx % half);
+  const int p = pos_of_row[row];
+  float2 r = make_float2(1.f, 0.f);
+  if (p >= 0) {
+    const double theta = exp2(-2.0 * (double)i / (double)D * log2_base);
+    double s, c;
+    sincos((double)p * theta, &s, &c);
+    r = make_float2((float)c, (float)s);
+  }
+  cs[idx] = r;
+}
+
+// Rotate (optional) and relayout one page x head of a [C][H][D] tensor into
+// page-major natural and/or transposed layouts.  Padding rows become zeros.
+// One block of 256 threads per (page, head); D <= 128.
+template <typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void relayout_kernel(
+    const Tin* __restrict__ x, const float2* __restrict__ cs, const int32_t* __restrict__ page_nrows,
+    Tout* __restrict__ out_n, Tout* __restrict__ out_t, int H, int D) {
+  extern __shared__ float tile[];  // [64][D + 1]
+  const int page = blockIdx.x / H, h = blockIdx.x % H;
+  const int nrows = page_nrows[page];
+  const int half = D / 2, ld = D + 1;
+  for (int idx = threadIdx.x; idx < 64 * half; idx += blockDim.x) {
+    const int r = idx / half, i = idx % half;
+    float a = 0.f, b = 0.f;
+    if (r < nrows) {
+      const int64_t row = (int64_t)page * 64 + r;
+      const Tin* src = x + (row * H + h) * D;
+      a = ld_f(src + i);
+      b = ld_f(src + i + half);
+      if (cs) {
+        const float2 t = cs[row * half + i];
+        const float a2 = a * t.x - b * t.y;
+        b = b * t.x + a * t.y;
+        a = a2;
+      }
+    }
+    tile[r * ld + i] = a;
+    tile[r * ld + i + half] = b;
+  }
+  __syncthreads();
+  const int64_t base = ((int64_t)page * H + h) * 64 * D;
+  if (out_n)
+    for (int idx = threadIdx.x; idx < 64 * D; idx += blockDim.x) {
+      const int r = idx / D, d = idx % D;
+      st_f(out_n + base + idx, tile[r * ld + d]);
+    }
+  if (out_t)
+    for (int idx = threadIdx.x; idx < 64 * D; idx += blockDim.x) {
+      const int d = idx / 64, p = idx % 64;
+      const int r = tperm(p);
+      st_f(out_t + base + (int64_t)d * 64 + p, tile[r * ld + d]);
+    }
+}
+
+// ld[page][h][r] = (lse * log2 e, sum_d dO * O) for the backward; zero on padding rows.
+template <typename T>
+__global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ dO,
+                              const float* __restrict__ lse, const int32_t* __restrict__ page_nrows,
+                              float2* __restrict__ ldout, int64_t n_pages, int Hq, int D) {
+  const int64_t idx = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;  // one wave per (row, h)
+  const int lane = threadIdx.x % 64;
+  if (idx >= n_pages * 64 * Hq) return;
+  const int64_t row = idx / Hq;
+  const int h = (int)(idx % Hq);
+  const int64_t page = row / 64;
+  const int r = (int)(row % 64);
+  float acc = 0.f;
+  const bool valid = r < page_nrows[page];
+  if (valid)
+    for (int d = lane; d < D; d += 64) acc += ld_f(o + (row * Hq + h) * D + d) * ld_f(dO + (row * Hq + h) * D + d);
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) {
+    float2 v = make_float2(0.f, 0.f);
+    if (valid) v = make_float2(lse[row * Hq + h] * kLog2e, acc);
+    ldout[(page * Hq + h) * 64 + r] = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernels: bf16, D = 128, four query heads per KV head
+// ---------------------------------------------------------------------------
+
+constexpr int kD = 128;
+constexpr int kKStride = kD + 8;   // LDS row stride (bf16) of a [64][128] tile: +16 B against bank conflicts
+constexpr int kTStride = 64 + 8;   // LDS row stride (bf16) of a [128][64] tile
+// dK/dV work-group LDS: the K and V tiles, later overlaid by the [64][129] fp32 head sum
+constexpr int kSmemDkdv = (2 * 64 * kKStride * 2 > 64 * (kD + 1) * 4) ? 2 * 64 * kKStride * 2 : 64 * (kD + 1) * 4;
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+__device__ __forceinline__ bf16x8 ld8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)s[base + e];
+  return r;
+}
+// key (or row) index within a 32-block held by accumulator element r of a lane in half `hi`
+__device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
+
+// Copy a contiguous [64][128] bf16 tile into LDS with row stride kKStride.
+__device__ __forceinline__ void stage_rows(bf16_t* lds, const bf16_t* g, int64_t g_row_stride) {
+  for (int c = threadIdx.x; c < 64 * 16; c += 256) {
+    const int r = c >> 4, col = (c & 15) * 8;
+    *reinterpret_cast<uint4*>(lds + r * kKStride + col) =
+        *reinterpret_cast<const uint4*>(g + (int64_t)r * g_row_stride + col);
+  }
+}
+// Copy a contiguous [128][64] bf16 tile into LDS with row stride kTStride.
+__device__ __forceinline__ void stage_cols(bf16_t* lds, const bf16_t* g) {
+  for (int c = threadIdx.x; c < 128 * 8; c += 256) {
+    const int r = c >> 3, col = (c & 7) * 8;
+    *reinterpret_cast<uint4*>(lds + r * kTStride + col) =
+        *reinterpret_cast<const uint4*>(g + (int64_t)r * 64 + col);
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
+    const bf16_t* __restrict__ qn, const bf16_t* __restrict__ kn, const bf16_t* __restrict__ vt,
+    const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
+    bf16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, float sl2) {
+  __shared__ bf16_t lk[64 * kKStride];
+  __shared__ bf16_t lv[kD * kTStride];
+  const int item = blockIdx.x;
+  const QPage qp = qpages[order[item / Hkv]];
+  const int g = item % Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int h = g * 4 + wave;
+
+  bf16x8 qf[2][8];
+  const bf16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qf[nb][ks] = ld8(qb + (nb * 32 + l32) * kD + ks * 16 + hi * 8);
+
+  f32x16 oacc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) oacc[a][b] = zero16();
+  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+
+  for (int t = 0; t < qp.tile_count; ++t) {
+    const Tile tl = tiles[qp.tile_begin + t];
+    const int lo = tl.lohi & 0xff, hi_t = (tl.lohi >> 8) & 0xff;
+    const bool diag = (t == qp.tile_count - 1);
+    __syncthreads();
+    stage_rows(lk, kn + ((int64_t)tl.page * Hkv + g) * 64 * kD, kD);
+    stage_cols(lv, vt + ((int64_t)tl.page * Hkv + g) * kD * 64);
+    __syncthreads();
+
+    f32x16 s[2][2];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      s[mb][0] = zero16();
+      s[mb][1] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 a = ld8(lk + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
+        s[mb][0] = mfma(a, qf[0][ks], s[mb][0]);
+        s[mb][1] = mfma(a, qf[1][ks], s[mb][1]);
+      }
+    }
+    bf16x8 pf[4][2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int row = nb * 32 + l32;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = mb * 32 + acc_row(r, hi);
+          const bool ok = key >= lo && key < hi_t && (!diag || key <= row);
+          const float x = ok ? s[mb][nb][r] * sl2 : -INFINITY;
+          s[mb][nb][r] = x;
+          mx = fmaxf(mx, x);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrow[nb], mx);
+      const float alpha = __builtin_amdgcn_exp2f(mrow[nb] - mnew);
+      mrow[nb] = mnew;
+      float sum = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(s[mb][nb][r] - mnew);
+          s[mb][nb][r] = p;
+          sum += p;
+        }
+      lrow[nb] = lrow[nb] * alpha + sum;
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[a][nb][r] *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        pf[2 * mb][nb] = pack8(s[mb][nb], 0);
+        pf[2 * mb + 1][nb] = pack8(s[mb][nb], 8);
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 va = ld8(lv + (a * 32 + l32) * kTStride + ks * 16 + hi * 8);
+        oacc[a][0] = mfma(va, pf[ks][0], oacc[a][0]);
+        oacc[a][1] = mfma(va, pf[ks][1], oacc[a][1]);
+      }
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int row = nb * 32 + l32;
+    const float l = lrow[nb] + __shfl_xor(lrow[nb], 32);
+    const bool valid = row < qp.nrows;
+    const float inv = valid ? 1.f / l : 0.f;
+    const int64_t grow = (int64_t)qp.phys * 64 + row;
+    bf16_t* orow = o + (grow * Hq + h) * kD;
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = a * 32 + 8 * j + 4 * hi;
+        uint2 w;
+        w.x = (uint32_t)f2bf(oacc[a][nb][4 * j] * inv) | ((uint32_t)f2bf(oacc[a][nb][4 * j + 1] * inv) << 16);
+        w.y = (uint32_t)f2bf(oacc[a][nb][4 * j + 2] * inv) | ((uint32_t)f2bf(oacc[a][nb][4 * j + 3] * inv) << 16);
+        *reinterpret_cast<uint2*>(orow + d) = w;
+      }
+    if (hi == 0) lse[grow * Hq + h] = valid ? (mrow[nb] + __log2f(l)) * kLn2 : 0.f;
+  }
+}
+
+// dQ for one query block (64 rows) x one KV head; waves = the four query heads.
+__global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
+    const bf16_t* __restrict__ qn, const bf16_t* __restrict__ kn, const bf16_t* __restrict__ kt,
+    const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO, const float2* __restrict__ ldd,
+    const float2* __restrict__ cs, const QPage* __restrict__ qpages, const int32_t* __restrict__ order,
+    const Tile* __restrict__ tiles, bf16_t* __restrict__ dq, int Hq, int Hkv, float sl2, float scale) {
+  __shared__ bf16_t lk[64 * kKStride];
+  __shared__ bf16_t lvv[64 * kKStride];
+  __shared__ bf16_t lkt[kD * kTStride];
+  const int item = blockIdx.x;
+  const QPage qp = qpages[order[item / Hkv]];
+  const int g = item % Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int h = g * 4 + wave;
+
+  bf16x8 qf[2][8], df[2][8];
+  const bf16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
+  float lse2[2], Dv[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int row = nb * 32 + l32;
+    const bf16_t* drow = dO + (((int64_t)qp.phys * 64 + row) * Hq + h) * kD;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      qf[nb][ks] = ld8(qb + row * kD + ks * 16 + hi * 8);
+      df[nb][ks] = ld8(drow + ks * 16 + hi * 8);
+    }
+    const float2 t = ldd[((int64_t)qp.phys * Hq + h) * 64 + row];
+    lse2[nb] = t.x;
+    Dv[nb] = t.y;
+  }
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
+
+  for (int t = 0; t < qp.tile_count; ++t) {
+    const Tile tl = tiles[qp.tile_begin + t];
+    const int lo = tl.lohi & 0xff, hi_t = (tl.lohi >> 8) & 0xff;
+    const bool diag = (t == qp.tile_count - 1);
+    __syncthreads();
+    stage_rows(lk, kn + ((int64_t)tl.page * Hkv + g) * 64 * kD, kD);
+    stage_rows(lvv, v + ((int64_t)tl.page * 64 * Hkv + g) * kD, (int64_t)Hkv * kD);
+    stage_cols(lkt, kt + ((int64_t)tl.page * Hkv + g) * kD * 64);
+    __syncthreads();
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 s[2], dp[2];
+      s[0] = s[1] = dp[0] = dp[1] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const bf16x8 a = ld8(lk + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
+        const bf16x8 b = ld8(lvv + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
+        s[0] = mfma(a, qf[0][ks], s[0]);
+        s[1] = mfma(a, qf[1][ks], s[1]);
+        dp[0] = mfma(b, df[0][ks], dp[0]);
+        dp[1] = mfma(b, df[1][ks], dp[1]);
+      }
+      bf16x8 dsf[2][2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int row = nb * 32 + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = mb * 32 + acc_row(r, hi);
+          const bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < qp.nrows;
+          const float p = ok ? __builtin_amdgcn_exp2f(s[nb][r] * sl2 - lse2[nb]) : 0.f;
+          s[nb][r] = ok ? p * (dp[nb][r] - Dv[nb]) : 0.f;  // padding rows may hold NaN
+        }
+        dsf[0][nb] = pack8(s[nb], 0);
+        dsf[1][nb] = pack8(s[nb], 8);
+      }
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const bf16x8 ka = ld8(lkt + (a * 32 + l32) * kTStride + (mb * 2 + kk) * 16 + hi * 8);
+          acc[a][0] = mfma(ka, dsf[kk][0], acc[a][0]);
+          acc[a][1] = mfma(ka, dsf[kk][1], acc[a][1]);
+        }
+    }
+  }
+
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int row = nb * 32 + l32;
+    const bool valid = row < qp.nrows;
+    const int64_t grow = (int64_t)qp.phys * 64 + row;
+    bf16_t* out = dq + (grow * Hq + h) * kD;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = a * 32 + 8 * j + 4 * hi + i;  // d < 64 pairs with d + 64 (block a + 2)
+          const float g1 = acc[a][nb][4 * j + i] * scale, g2 = acc[a + 2][nb][4 * j + i] * scale;
+          float r1 = 0.f, r2 = 0.f;
+          if (valid) {
+            const float2 c = cs ? cs[grow * (kD / 2) + d] : make_float2(1.f, 0.f);
+            r1 = g1 * c.x + g2 * c.y;
+            r2 = g2 * c.x - g1 * c.y;
+          }
+          out[d] = f2bf(r1);
+          out[d + 64] = f2bf(r2);
+        }
+  }
+}
+
+// dK, dV for one KV page x one KV head.  Waves = the four query heads; each
+// wave walks the page's reader list and keeps its own dK/dV in registers; the
+// four are then summed through LDS in head order.
+__global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
+    const bf16_t* __restrict__ qn, const bf16_t* __restrict__ qt, const bf16_t* __restrict__ kn,
+    const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO, const bf16_t* __restrict__ dOt,
+    const float2* __restrict__ ldd, const float2* __restrict__ cs, const int32_t* __restrict__ order,
+    const int32_t* __restrict__ kv_off, const KEntry* __restrict__ ents,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ page_nrows,
+    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int Hq, int Hkv, float sl2, float scale) {
+  // K/V tiles during the walk; the same bytes hold the head reduction afterwards
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemDkdv];
+  bf16_t* lk = reinterpret_cast<bf16_t*>(smem);
+  bf16_t* lvv = lk + 64 * kKStride;
+  float* red = reinterpret_cast<float*>(smem);
+  const int item = blockIdx.x;
+  const int page = order[item / Hkv];
+  const int g = item % Hkv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int h = g * 4 + wave;
+  const int krows = page_nrows[page];
+
+  stage_rows(lk, kn + ((int64_t)page * Hkv + g) * 64 * kD, kD);
+  stage_rows(lvv, v + ((int64_t)page * 64 * Hkv + g) * kD, (int64_t)Hkv * kD);
+  __syncthreads();
+
+  f32x16 adk[2][4], adv[2][4];  // [key block][d block]
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) adk[a][b] = adv[a][b] = zero16();
+
+  for (int e = kv_off[page]; e < kv_off[page + 1]; ++e) {
+    const KEntry ent = ents[e];
+    const int lo = ent.lohi_diag & 0xff, hi_t = (ent.lohi_diag >> 8) & 0xff;
+    const bool diag = (ent.lohi_diag >> 16) & 1;
+    for (int lq = ent.lq0; lq < ent.lq1; ++lq) {
+      const int qph = page_table[ent.slot_base + lq];
+      const int nrows = page_nrows[qph];
+      const bf16_t* qb = qn + ((int64_t)qph * Hq + h) * 64 * kD;
+      const bf16_t* qtb = qt + ((int64_t)qph * Hq + h) * kD * 64;
+      const bf16_t* dtb = dOt + ((int64_t)qph * Hq + h) * kD * 64;
+      const float2* ldb = ldd + ((int64_t)qph * Hq + h) * 64;
+      for (int rb = 0; rb < 2; ++rb) {
+        if (rb * 32 >= nrows) break;
+        // S = Q K^T and dP = dO V^T for 32 rows x 64 keys (rows = M, keys = N)
+        f32x16 s[2], dp[2];
+        s[0] = s[1] = dp[0] = dp[1] = zero16();
+        const int arow = rb * 32 + l32;
+        const bf16_t* drow = dO + (((int64_t)qph * 64 + arow) * Hq + h) * kD;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const bf16x8 qa = ld8(qb + arow * kD + ks * 16 + hi * 8);
+          const bf16x8 da = ld8(drow + ks * 16 + hi * 8);
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const bf16x8 kb = ld8(lk + (nb * 32 + l32) * kKStride + ks * 16 + hi * 8);
+            const bf16x8 vb = ld8(lvv + (nb * 32 + l32) * kKStride + ks * 16 + hi * 8);
+            s[nb] = mfma(qa, kb, s[nb]);
+            dp[nb] = mfma(da, vb, dp[nb]);
+          }
+        }
+        // P and dS; this lane holds key nb*32 + l32 and rows rb*32 + acc_row(r, hi)
+        bf16x8 pf[2][2], sf[2][2];  // [k-step of 16 rows][key block]
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r0 = rb * 32 + 8 * j + 4 * hi;
+          float2 lr[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) lr[i] = ldb[r0 + i];
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int key = nb * 32 + l32;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int row = r0 + i;
+              const bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < nrows;
+              const float p = ok ? __builtin_amdgcn_exp2f(s[nb][4 * j + i] * sl2 - lr[i].x) : 0.f;
+              s[nb][4 * j + i] = p;
+              dp[nb][4 * j + i] = ok ? p * (dp[nb][4 * j + i] - lr[i].y) : 0.f;  // padding may hold NaN
+            }
+          }
+        }
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          pf[0][nb] = pack8(s[nb], 0);
+          pf[1][nb] = pack8(s[nb], 8);
+          sf[0][nb] = pack8(dp[nb], 0);
+          sf[1][nb] = pack8(dp[nb], 8);
+        }
+        // dV += P^T dO, dK += dS^T Q (keys = M, d = N, rows = contraction)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int col = (rb * 2 + kk) * 16 + hi * 8;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const bf16x8 dob = ld8(dtb + (b * 32 + l32) * 64 + col);
+            const bf16x8 qbt = ld8(qtb + (b * 32 + l32) * 64 + col);
+#pragma unroll
+            for (int nb = 0; nb < 2; ++nb) {
+              adv[nb][b] = mfma(pf[kk][nb], dob, adv[nb][b]);
+              adk[nb][b] = mfma(sf[kk][nb], qbt, adk[nb][b]);
+            }
+          }
+        }
+      }
+    }
+  }
+
+  // sum the four heads in order 0..3 through LDS, then write dk (un-rotated) and dv
+  for (int which = 0; which < 2; ++which) {
+    for (int w = 0; w < 4; ++w) {
+      __syncthreads();
+      if (wave == w) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = nb * 32 + acc_row(r, hi);
+              const int d = b * 32 + l32;
+              const float x = which == 0 ? adk[nb][b][r] : adv[nb][b][r];
+              float* slot = red + key * (kD + 1) + d;
+              *slot = (w == 0) ? x : *slot + x;
+            }
+      }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
+      const int key = idx / 64, i = idx % 64;
+      const int64_t grow = (int64_t)page * 64 + key;
+      float a = red[key * (kD + 1) + i], b = red[key * (kD + 1) + i + 64];
+      if (key >= krows) {
+        a = b = 0.f;
+      } else if (which == 0) {
+        a *= scale;
+        b *= scale;
+        if (cs) {
+          const float2 c = cs[grow * (kD / 2) + i];
+          const float a2 = a * c.x + b * c.y;
+          b = b * c.x - a * c.y;
+          a = a2;
+        }
+      }
+      bf16_t* out = (which == 0 ? dk : dv) + (grow * Hkv + g) * kD;
+      out[i] = f2bf(a);
+      out[i + 64] = f2bf(b);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Generic kernels (any even head dim <= 128, any GQA ratio, bf16 or fp32 tensors).
+// One thread per query row (forward, dQ) or key row (dK/dV); fp32 throughout.
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxD = 128;
+
+template <typename T>
+__global__ __launch_bounds__(64) void fwd_simple_kernel(
+    const float* __restrict__ qn, const float* __restrict__ kn, const T* __restrict__ v,
+    const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
+    T* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int D, float scale) {
+  const int item = blockIdx.x;
+  const QPage qp = qpages[order[item / Hq]];
+  const int h = item % Hq, g = h / (Hq / Hkv);
+  const int row = threadIdx.x;
+  float q[kMaxD], acc[kMaxD];
+  const float* qrow = qn + (((int64_t)qp.phys * Hq + h) * 64 + row) * D;
+  for (int d = 0; d < D; ++d) {
+    q[d] = qrow[d];
+    acc[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  for (int t = 0; t < qp.tile_count; ++t) {
+    const Tile tl = tiles[qp.tile_begin + t];
+    const int lo = tl.lohi & 0xff, hi_t = (tl.lohi >> 8) & 0xff;
+    const bool diag = (t == qp.tile_count - 1);
+    for (int key = lo; key < hi_t; ++key) {
+      if (diag && key > row) break;
+      const float* krow = kn + (((int64_t)tl.page * Hkv + g) * 64 + key) * D;
+      float s = 0.f;
+      for (int d = 0; d < D; ++d) s = fmaf(q[d], krow[d], s);
+      s *= scale;
+      const float mn = fmaxf(m, s);
+      const float alpha = expf(m - mn), p = expf(s - mn);
+      l = l * alpha + p;
+      m = mn;
+      const T* vrow = v + (((int64_t)tl.page * 64 + key) * Hkv + g) * D;
+      for (int d = 0; d < D; ++d) acc[d] = fmaf(p, ld_f(vrow + d), acc[d] * alpha);
+    }
+  }
+  const bool valid = row < qp.nrows;
+  const int64_t grow = (int64_t)qp.phys * 64 + row;
+  for (int d = 0; d < D; ++d) st_f(o + (grow * Hq + h) * D + d, valid ? acc[d] / l : 0.f);
+  lse[grow * Hq + h] = valid ? m + logf(l) : 0.f;
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void dq_simple_kernel(
+    const float* __restrict__ qn, const float* __restrict__ kn, const T* __restrict__ v,
+    const T* __restrict__ dO, const float2* __restrict__ ldd, const float2* __restrict__ cs,
+    const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
+    T* __restrict__ dq, int Hq, int Hkv, int D, float scale) {
+  const int item = blockIdx.x;
+  const QPage qp = qpages[order[item / Hq]];
+  const int h = item % Hq, g = h / (Hq / Hkv);
+  const int row = threadIdx.x;
+  const int64_t grow = (int64_t)qp.phys * 64 + row;
+  float q[kMaxD], gd[kMaxD], acc[kMaxD];
+  const float* qrow = qn + (((int64_t)qp.phys * Hq + h) * 64 + row) * D;
+  for (int d = 0; d < D; ++d) {
+    q[d] = qrow[d];
+    gd[d] = ld_f(dO + (grow * Hq + h) * D + d);
+    acc[d] = 0.f;
+  }
+  const float2 lD = ldd[((int64_t)qp.phys * Hq + h) * 64 + row];
+  const float lse_n = lD.x * kLn2;
+  const bool valid = row < qp.nrows;
+  if (valid)
+    for (int t = 0; t < qp.tile_count; ++t) {
+      const Tile tl = tiles[qp.tile_begin + t];
+      const int lo = tl.lohi & 0xff, hi_t = (tl.lohi >> 8) & 0xff;
+      const bool diag = (t == qp.tile_count - 1);
+      for (int key = lo; key < hi_t; ++key) {
+        if (diag && key > row) break;
+        const float* krow = kn + (((int64_t)tl.page * Hkv + g) * 64 + key) * D;
+        const T* vrow = v + (((int64_t)tl.page * 64 + key) * Hkv + g) * D;
+        float s = 0.f, dp = 0.f;
+        for (int d = 0; d < D; ++d) {
+          s = fmaf(q[d], krow[d], s);
+          dp = fmaf(gd[d], ld_f(vrow + d), dp);
+        }
+        const float p = expf(s * scale - lse_n);
+        const float ds = p * (dp - lD.y) * scale;
+        for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, krow[d], acc[d]);
+      }
+    }
+  const int half = D / 2;
+  for (int i = 0; i < half; ++i) {
+    float a = acc[i], b = acc[i + half];
+    if (cs && valid) {
+      const float2 c = cs[grow * half + i];
+      const float a2 = a * c.x + b * c.y;
+      b = b * c.x - a * c.y;
+      a = a2;
+    }
+    st_f(dq + (grow * Hq + h) * D + i, valid ? a : 0.f);
+    st_f(dq + (grow * Hq + h) * D + i + half, valid ? b : 0.f);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void dkdv_simple_kernel(
+    const float* __restrict__ qn, const float* __restrict__ kn, const T* __restrict__ v,
+    const T* __restrict__ dO, const float2* __restrict__ ldd, const float2* __restrict__ cs,
+    const int32_t* __restrict__ order, const int32_t* __restrict__ kv_off,
+    const KEntry* __restrict__ ents, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ page_nrows, T* __restrict__ dk, T* __restrict__ dv, int Hq, int Hkv,
+    int D, float scale) {
+  const int item = blockIdx.x;
+  const int page = order[item / Hkv];
+  const int g = item % Hkv;
+  const int key = threadIdx.x;
+  const int64_t grow = (int64_t)page * 64 + key;
+  const bool valid = key < page_nrows[page];
+  float k[kMaxD], vv[kMaxD], ak[kMaxD], av[kMaxD];
+  const float* krow = kn + (((int64_t)page * Hkv + g) * 64 + key) * D;
+  for (int d = 0; d < D; ++d) {
+    k[d] = krow[d];
+    vv[d] = ld_f(v + (grow * Hkv + g) * D + d);
+    ak[d] = av[d] = 0.f;
+  }
+  const int rep = Hq / Hkv;
+  if (valid)
+    for (int e = kv_off[page]; e < kv_off[page + 1]; ++e) {
+      const KEntry ent = ents[e];
+      const int lo = ent.lohi_diag & 0xff, hi_t = (ent.lohi_diag >> 8) & 0xff;
+      const bool diag = (ent.lohi_diag >> 16) & 1;
+      if (key < lo || key >= hi_t) continue;
+      for (int lq = ent.lq0; lq < ent.lq1; ++lq) {
+        const int qph = page_table[ent.slot_base + lq];
+        const int nrows = page_nrows[qph];
+        for (int r = diag ? key : 0; r < nrows; ++r) {
+          for (int hh = 0; hh < rep; ++hh) {
+            const int h = g * rep + hh;
+            const float* qrow = qn + (((int64_t)qph * Hq + h) * 64 + r) * D;
+            const T* drow = dO + (((int64_t)qph * 64 + r) * Hq + h) * D;
+            const float2 lD = ldd[((int64_t)qph * Hq + h) * 64 + r];
+            float s = 0.f, dp = 0.f;
+            for (int d = 0; d < D; ++d) {
+              s = fmaf(qrow[d], k[d], s);
+              dp = fmaf(ld_f(drow + d), vv[d], dp);
+            }
+            const float p = expf(s * scale - lD.x * kLn2);
+            const float ds = p * (dp - lD.y) * scale;
+            for (int d = 0; d < D; ++d) {
+              av[d] = fmaf(p, ld_f(drow + d), av[d]);
+              ak[d] = fmaf(ds, qrow[d], ak[d]);
+            }
+          }
+        }
+      }
+    }
+  const int half = D / 2;
+  for (int i = 0; i < half; ++i) {
+    float a = ak[i], b = ak[i + half];
+    if (cs && valid) {
+      const float2 c = cs[grow * half + i];
+      const float a2 = a * c.x + b * c.y;
+      b = b * c.x - a * c.y;
+      a = a2;
+    }
+    st_f(dk + (grow * Hkv + g) * D + i, valid ? a : 0.f);
+    st_f(dk + (grow * Hkv + g) * D + i + half, valid ? b : 0.f);
+  }
+  for (int d = 0; d < D; ++d) st_f(dv + (grow * Hkv + g) * D + d, valid ? av[d] : 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+
+static inline unsigned blocks_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+void launch_cs(const LaunchShape& s, const int32_t* pos_of_row, float2* cs, hipStream_t st) {
+  const int half = s.D / 2;
+  cs_kernel<<<blocks_for(s.C * half, 256), 256, 0, st>>>(pos_of_row, cs, s.C, half, s.log2_base, s.D);
+}
+
+template <typename Tin, typename Tout>
+void launch_relayout(const LaunchShape& s, const Tin* x, const float2* cs, const int32_t* page_nrows,
+                     Tout* out_n, Tout* out_t, int H, hipStream_t st) {
+  const size_t lds = (size_t)64 * (s.D + 1) * sizeof(float);
+  relayout_kernel<Tin, Tout><<<(unsigned)(s.pages * H), 256, lds, st>>>(x, cs, page_nrows, out_n, out_t, H, s.D);
+}
+
+template <typename T>
+void launch_rowdot(const LaunchShape& s, const T* o, const T* dO, const float* lse,
+                   const int32_t* page_nrows, float2* ld, hipStream_t st) {
+  rowdot_kernel<T><<<blocks_for(s.pages * 64 * s.Hq, 4), 256, 0, st>>>(o, dO, lse, page_nrows, ld, s.pages, s.Hq, s.D);
+}
+
+template void launch_relayout<bf16_t, bf16_t>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, bf16_t*, bf16_t*, int, hipStream_t);
+template void launch_relayout<bf16_t, float>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, float*, float*, int, hipStream_t);
+template void launch_relayout<float, float>(const LaunchShape&, const float*, const float2*, const int32_t*, float*, float*, int, hipStream_t);
+template void launch_rowdot<bf16_t>(const LaunchShape&, const bf16_t*, const bf16_t*, const float*, const int32_t*, float2*, hipStream_t);
+template void launch_rowdot<float>(const LaunchShape&, const float*, const float*, const float*, const int32_t*, float2*, hipStream_t);
+
+void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const bf16_t* kn, const bf16_t* vt,
+                     const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
+                     hipStream_t st) {
+  fwd_mfma_kernel<<<(unsigned)(n_qp * s.Hkv), 256, 0, st>>>(qn, kn, vt, qpages, order, tiles, o, lse, s.Hq,
+                                                            s.Hkv, s.scale * kLog2e);
+}
+
+void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const bf16_t* kn, const bf16_t* kt,
+                    const bf16_t* v, const bf16_t* dO, const float2* ld, const float2* cs, const QPage* qpages,
+                    const int32_t* order, const Tile* tiles, bf16_t* dq, hipStream_t st) {
+  dq_mfma_kernel<<<(unsigned)(n_qp * s.Hkv), 256, 0, st>>>(qn, kn, kt, v, dO, ld, cs, qpages, order, tiles, dq,
+                                                           s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
+}
+
+void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const bf16_t* qn, const bf16_t* qt, const bf16_t* kn,
+                      const bf16_t* v, const bf16_t* dO, const bf16_t* dOt, const float2* ld, const float2* cs,
+                      const int32_t* order, const int32_t* kv_off, const KEntry* ents, const int32_t* page_table,
+                      const int32_t* page_nrows, bf16_t* dk, bf16_t* dv, hipStream_t st) {
+  dkdv_mfma_kernel<<<(unsigned)(n_kvp * s.Hkv), 256, 0, st>>>(qn, qt, kn, v, dO, dOt, ld, cs, order, kv_off, ents,
+                                                              page_table, page_nrows, dk, dv, s.Hq, s.Hkv,
+                                                              s.scale * kLog2e, s.scale);
+}
+
+template <typename T>
+void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,
+                       const QPage* qpages, const int32_t* order, const Tile* tiles, T* o, float* lse,
+                       hipStream_t st) {
+  fwd_simple_kernel<T><<<(unsigned)(n_qp * s.Hq), 64, 0, st>>>(qn, kn, v, qpages, order, tiles, o, lse, s.Hq, s.Hkv,
+                                                              s.D, s.scale);
+}
+
+template <typename T>
+void launch_bwd_simple(const LaunchShape& s, int64_t n_qp, int64_t n_kvp, const float* qn, const float* kn,
+                       const T* v, const T* dO, const float2* ld, const float2* cs, const QPage* qpages,
+                       const int32_t* fwd_order, const Tile* tiles, const int32_t* bwd_order,
+                       const int32_t* kv_off, const KEntry* ents, const int32_t* page_table,
+                       const int32_t* page_nrows, T* dq, T* dk, T* dv, hipStream_t st) {
+  dq_simple_kernel<T><<<(unsigned)(n_qp * s.Hq), 64, 0, st>>>(qn, kn, v, dO, ld, cs, qpages, fwd_order, tiles, dq,
+                                                             s.Hq, s.Hkv, s.D, s.scale);
+  dkdv_simple_kernel<T><<<(unsigned)(n_kvp * s.Hkv), 64, 0, st>>>(qn, kn, v, dO, ld, cs, bwd_order, kv_off, ents,
+                                                                 page_table, page_nrows, dk, dv, s.Hq, s.Hkv, s.D,
+                                                                 s.scale);
+}
+
+template void launch_fwd_simple<bf16_t>(const LaunchShape&, int64_t, const float*, const float*, const bf16_t*, const QPage*, const int32_t*, const Tile*, bf16_t*, float*, hipStream_t);
+template void launch_fwd_simple<float>(const LaunchShape&, int64_t, const float*, const float*, const float*, const QPage*, const int32_t*, const Tile*, float*, float*, hipStream_t);
+template void launch_bwd_simple<bf16_t>(const LaunchShape&, int64_t, int64_t, const float*, const float*, const bf16_t*, const bf16_t*, const float2*, const float2*, const QPage*, const int32_t*, const Tile*, const int32_t*, const int32_t*, const KEntry*, const int32_t*, const int32_t*, bf16_t*, bf16_t*, bf16_t*, hipStream_t);
+template void launch_bwd_simple<float>(const LaunchShape&, int64_t, int64_t, const float*, const float*, const float*, const float*, const float2*, const float2*, const QPage*, const int32_t*, const Tile*, const int32_t*, const int32_t*, const KEntry*, const int32_t*, const int32_t*, float*, float*, float*, hipStream_t);
+
+}  // namespace dagattn

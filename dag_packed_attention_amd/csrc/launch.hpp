@@ -1,0 +1,47 @@
+// Launchers of the HIP kernels (defined in kernels.hip, called by abi.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "plan.hpp"
+
+namespace dagattn {
+
+typedef uint16_t bf16_t;
+
+struct LaunchShape {
+  int64_t C, pages;
+  int Hq, Hkv, D;
+  float scale;
+  double log2_base;  // log2 of the rotary base; 0 => no rotation
+};
+
+void launch_cs(const LaunchShape& s, const int32_t* pos_of_row, float2* cs, hipStream_t st);
+template <typename Tin, typename Tout>
+void launch_relayout(const LaunchShape& s, const Tin* x, const float2* cs, const int32_t* page_nrows,
+                     Tout* out_n, Tout* out_t, int H, hipStream_t st);
+template <typename T>
+void launch_rowdot(const LaunchShape& s, const T* o, const T* dO, const float* lse,
+                   const int32_t* page_nrows, float2* ld, hipStream_t st);
+void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const bf16_t* kn, const bf16_t* vt,
+                     const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
+                     hipStream_t st);
+void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const bf16_t* kn, const bf16_t* kt,
+                    const bf16_t* v, const bf16_t* dO, const float2* ld, const float2* cs, const QPage* qpages,
+                    const int32_t* order, const Tile* tiles, bf16_t* dq, hipStream_t st);
+void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const bf16_t* qn, const bf16_t* qt, const bf16_t* kn,
+                      const bf16_t* v, const bf16_t* dO, const bf16_t* dOt, const float2* ld, const float2* cs,
+                      const int32_t* order, const int32_t* kv_off, const KEntry* ents, const int32_t* page_table,
+                      const int32_t* page_nrows, bf16_t* dk, bf16_t* dv, hipStream_t st);
+template <typename T>
+void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,
+                       const QPage* qpages, const int32_t* order, const Tile* tiles, T* o, float* lse,
+                       hipStream_t st);
+template <typename T>
+void launch_bwd_simple(const LaunchShape& s, int64_t n_qp, int64_t n_kvp, const float* qn, const float* kn,
+                       const T* v, const T* dO, const float2* ld, const float2* cs, const QPage* qpages,
+                       const int32_t* fwd_order, const Tile* tiles, const int32_t* bwd_order,
+                       const int32_t* kv_off, const KEntry* ents, const int32_t* page_table,
+                       const int32_t* page_nrows, T* dq, T* dk, T* dv, hipStream_t st);
+
+}  // namespace dagattn

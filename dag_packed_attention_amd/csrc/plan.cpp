@@ -1,0 +1,373 @@
+// Host-side DAG compactor.
+//
+// Steps (each tied to the pages' definitions):
+//   1. validation of the node and mount tables;
+//   2. a dependency order in which every node follows its parent and the
+//      sources of its mounts (the execution graph is a DAG: Octopus Sec. 3);
+//   3. start positions by monotonic continuation (Octopus Sec. 3.2 Eq. 2):
+//      s(u) = max(s(parent) + len(parent), max over u's reads of end position + 1);
+//   4. active mounts per node: inherited along the chain, optionally closed
+//      over the sources' own active mounts (Octopus Sec. 3.3 item 1);
+//   5. non-self visibility as disjoint ranges of source-node offsets: mounted
+//      spans first, then the ancestors (Octopus Sec. 3.3 Eq. 4);
+//   6. pages: every node starts on a fresh 64-row page; a page table maps the
+//      node's page slots to physical pages;
+//   7. per-node tile lists (query blocks take a prefix: HARTS Eq. 22's
+//      bottom-right causal alignment puts the node's own pages last);
+//   8. per-KV-page reader lists in a fixed order (the deterministic order in
+//      which the backward sums reader contributions into producer pages,
+//      Octopus Sec. 3.4 Eq. 8, HARTS Sec. 3.4);
+//   9. launch orders, heaviest work first.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <climits>
+#include <cstdio>
+#include <numeric>
+#include <queue>
+
+namespace dagattn {
+namespace {
+
+struct Span {
+  int32_t src, b, e;
+  bool operator<(const Span& o) const {
+    if (src != o.src) return src < o.src;
+    if (b != o.b) return b < o.b;
+    return e < o.e;
+  }
+  bool operator==(const Span& o) const { return src == o.src && b == o.b && e == o.e; }
+};
+
+dag_status fail(std::string* err, dag_status code, const char* fmt, long long a = 0,
+                long long b = 0, long long c = 0) {
+  char buf[256];
+  std::snprintf(buf, sizeof buf, fmt, a, b, c);
+  *err = buf;
+  return code;
+}
+
+// splitmix64: a small, fully specified generator so shuffled page tables are
+// reproducible across compilers and standard libraries.
+uint64_t splitmix64(uint64_t& s) {
+  uint64_t z = (s += 0x9E3779B97F4A7C15ull);
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+}  // namespace
+
+dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts, int32_t nm,
+                      const dag_build_opts* opts_in, Plan* P, std::string* err) {
+  // ---- options ----------------------------------------------------------
+  dag_build_opts opts{64, 64, 1, 0};
+  if (opts_in) opts = *opts_in;
+  if (opts.page_size == 0) opts.page_size = kPage;
+  if (opts.q_block == 0) opts.q_block = kPage;
+  if (opts.page_size != kPage || opts.q_block != kPage)
+    return fail(err, DAG_E_UNSUPPORTED, "page_size and q_block must be 64 (got %lld, %lld)",
+                opts.page_size, opts.q_block);
+  if (opts.transitive != 0 && opts.transitive != 1)
+    return fail(err, DAG_E_INVALID, "transitive must be 0 or 1");
+  P->opts = opts;
+
+  // ---- 1. validation ------------------------------------------------------
+  if (n <= 0 || !nodes) return fail(err, DAG_E_INVALID, "a DAG needs at least one node");
+  if (nm < 0 || (nm > 0 && !mounts)) return fail(err, DAG_E_INVALID, "bad mount table");
+  for (int32_t u = 0; u < n; ++u) {
+    const int32_t p = nodes[u].parent;
+    if (p < -1 || p >= n) return fail(err, DAG_E_INVALID, "node %lld: parent %lld out of range", u, p);
+    if (p >= u) return fail(err, DAG_E_NOT_TOPO, "node %lld: parent %lld is not earlier", u, p);
+    if (nodes[u].length < 0) return fail(err, DAG_E_INVALID, "node %lld: negative length", u);
+  }
+  for (int32_t u = 0; u < n; ++u) {
+    const int64_t f = nodes[u].mount_first, c = nodes[u].mount_count;
+    if (c < 0 || f < 0 || f + c > nm)
+      return fail(err, DAG_E_INVALID, "node %lld: mount slice out of range", u);
+    for (int64_t i = f; i < f + c; ++i) {
+      const dag_mount& m = mounts[i];
+      if (m.src_node < 0 || m.src_node >= n)
+        return fail(err, DAG_E_INVALID, "node %lld: mount source %lld out of range", u, m.src_node);
+    }
+  }
+  P->n_nodes = n;
+  P->parent.resize(n);
+  P->length.resize(n);
+  P->direct.assign(n, {});
+  for (int32_t u = 0; u < n; ++u) {
+    P->parent[u] = nodes[u].parent;
+    P->length[u] = nodes[u].length;
+  }
+  for (int32_t u = 0; u < n; ++u) {
+    for (int64_t i = nodes[u].mount_first; i < nodes[u].mount_first + nodes[u].mount_count; ++i) {
+      const dag_mount& m = mounts[i];
+      if (!(0 <= m.begin && m.begin <= m.end && m.end <= P->length[m.src_node]))
+        return fail(err, DAG_E_MOUNT_RANGE, "node %lld: span [%lld,%lld) outside its source", u,
+                    m.begin, m.end);
+      if (m.end > m.begin) P->direct[u].push_back(m);
+    }
+  }
+  // reads of the reader's own chain
+  for (int32_t u = 0; u < n; ++u) {
+    for (const dag_mount& m : P->direct[u]) {
+      for (int32_t a = u; a >= 0; a = P->parent[a])
+        if (a == m.src_node)
+          return fail(err, DAG_E_SELF_ANCESTOR_MOUNT, "node %lld reads its own chain (node %lld)",
+                      u, m.src_node);
+    }
+  }
+
+  // ---- 2. dependency order (Kahn, smallest ready index first) ---------------
+  {
+    std::vector<int32_t> indeg(n, 0);
+    std::vector<std::vector<int32_t>> users(n);
+    for (int32_t u = 0; u < n; ++u) {
+      std::vector<int32_t> deps;
+      if (P->parent[u] >= 0) deps.push_back(P->parent[u]);
+      for (const dag_mount& m : P->direct[u]) deps.push_back(m.src_node);
+      std::sort(deps.begin(), deps.end());
+      deps.erase(std::unique(deps.begin(), deps.end()), deps.end());
+      indeg[u] = (int32_t)deps.size();
+      for (int32_t s : deps) users[s].push_back(u);
+    }
+    std::priority_queue<int32_t, std::vector<int32_t>, std::greater<int32_t>> ready;
+    for (int32_t u = 0; u < n; ++u)
+      if (indeg[u] == 0) ready.push(u);
+    P->order.clear();
+    while (!ready.empty()) {
+      int32_t u = ready.top();
+      ready.pop();
+      P->order.push_back(u);
+      for (int32_t w : users[u])
+        if (--indeg[w] == 0) ready.push(w);
+    }
+    if ((int32_t)P->order.size() != n)
+      return fail(err, DAG_E_MOUNT_CYCLE, "tree and mount edges form a cycle");
+  }
+
+  // ---- 3. positions (Octopus Eq. 2) -----------------------------------------
+  P->start.assign(n, 0);
+  int64_t max_pos = 0;
+  for (int32_t u : P->order) {
+    const int32_t p = P->parent[u];
+    int64_t s = p < 0 ? 0 : (int64_t)P->start[p] + P->length[p];
+    for (const dag_mount& m : P->direct[u]) {
+      const int64_t pos_end = (int64_t)P->start[m.src_node] + (m.end - 1);  // last mounted token
+      s = std::max(s, pos_end + 1);
+    }
+    if (s + P->length[u] > INT32_MAX) return fail(err, DAG_E_OVERFLOW, "positions exceed int32");
+    P->start[u] = (int32_t)s;
+    max_pos = std::max(max_pos, s + std::max(0, P->length[u] - 1));
+  }
+
+  // ---- 4. active mounts --------------------------------------------------------
+  std::vector<std::vector<Span>> act(n);
+  for (int32_t u : P->order) {
+    std::vector<Span> s;
+    if (P->parent[u] >= 0) s = act[P->parent[u]];
+    for (const dag_mount& m : P->direct[u]) {
+      s.push_back({m.src_node, m.begin, m.end});
+      if (opts.transitive) s.insert(s.end(), act[m.src_node].begin(), act[m.src_node].end());
+    }
+    std::sort(s.begin(), s.end());
+    s.erase(std::unique(s.begin(), s.end()), s.end());
+    act[u] = std::move(s);
+  }
+
+  // ---- 5. non-self visibility ranges -------------------------------------------
+  P->range_off.assign(n + 1, 0);
+  P->ranges.clear();
+  std::vector<char> is_anc(n, 0);
+  std::vector<int32_t> chain;
+  for (int32_t u = 0; u < n; ++u) {
+    P->range_off[u] = (int64_t)P->ranges.size() / 3;
+    chain.clear();
+    for (int32_t a = P->parent[u]; a >= 0; a = P->parent[a]) chain.push_back(a);
+    for (int32_t a : chain) is_anc[a] = 1;
+    // mounted spans, merged per source (act[u] is sorted by (src, b, e))
+    size_t i = 0;
+    const std::vector<Span>& s = act[u];
+    while (i < s.size()) {
+      const int32_t src = s[i].src;
+      if (is_anc[src]) {  // an ancestor is visible in full already
+        while (i < s.size() && s[i].src == src) ++i;
+        continue;
+      }
+      int32_t lo = s[i].b, hi = s[i].e;
+      ++i;
+      while (i < s.size() && s[i].src == src) {
+        if (s[i].b <= hi) {
+          hi = std::max(hi, s[i].e);
+        } else {
+          P->ranges.insert(P->ranges.end(), {src, lo, hi});
+          lo = s[i].b;
+          hi = s[i].e;
+        }
+        ++i;
+      }
+      P->ranges.insert(P->ranges.end(), {src, lo, hi});
+    }
+    // ancestors, root first
+    for (auto it = chain.rbegin(); it != chain.rend(); ++it)
+      if (P->length[*it] > 0) P->ranges.insert(P->ranges.end(), {*it, 0, P->length[*it]});
+    for (int32_t a : chain) is_anc[a] = 0;
+  }
+  P->range_off[n] = (int64_t)P->ranges.size() / 3;
+
+  // ---- 6. pages ------------------------------------------------------------------
+  P->slot0.assign(n, 0);
+  P->npages.assign(n, 0);
+  P->tok_off.assign(n, 0);
+  int64_t slots = 0, tokens = 0;
+  for (int32_t u = 0; u < n; ++u) {
+    P->slot0[u] = (int32_t)std::min<int64_t>(slots, INT32_MAX);
+    P->npages[u] = (P->length[u] + kPage - 1) / kPage;
+    P->tok_off[u] = tokens;
+    slots += P->npages[u];
+    tokens += P->length[u];
+  }
+  if (slots * kPage > INT32_MAX) return fail(err, DAG_E_OVERFLOW, "compact rows exceed int32");
+  const int32_t n_pages = (int32_t)slots;
+  P->page_table.resize(n_pages);
+  std::iota(P->page_table.begin(), P->page_table.end(), 0);
+  if (opts.page_shuffle) {
+    uint64_t st = (uint64_t)(uint32_t)opts.page_shuffle;
+    for (int32_t i = n_pages - 1; i > 0; --i) {
+      const int32_t j = (int32_t)(splitmix64(st) % (uint64_t)(i + 1));
+      std::swap(P->page_table[i], P->page_table[j]);
+    }
+  }
+  const int64_t C = (int64_t)n_pages * kPage;
+  P->page_nrows.assign(n_pages, 0);
+  P->pos_of_row.assign(C, -1);
+  P->row_of_token.assign(tokens, 0);
+  for (int32_t u = 0; u < n; ++u) {
+    for (int32_t lp = 0; lp < P->npages[u]; ++lp) {
+      const int32_t ph = P->page_table[P->slot0[u] + lp];
+      const int32_t nr = std::min(kPage, P->length[u] - lp * kPage);
+      P->page_nrows[ph] = nr;
+      for (int32_t r = 0; r < nr; ++r) {
+        const int64_t row = (int64_t)ph * kPage + r;
+        P->pos_of_row[row] = P->start[u] + lp * kPage + r;
+        P->row_of_token[P->tok_off[u] + lp * kPage + r] = (int32_t)row;
+      }
+    }
+  }
+
+  // ---- 7. tile lists and query pages -----------------------------------------------
+  P->tile_off.assign(n + 1, 0);
+  P->tile_nonself.assign(n, 0);
+  P->tiles.clear();
+  P->qpages.clear();
+  auto pack = [](int32_t lo, int32_t hi) { return lo | (hi << 8); };
+  for (int32_t u = 0; u < n; ++u) {
+    if ((int64_t)P->tiles.size() > INT32_MAX / 2) return fail(err, DAG_E_OVERFLOW, "tile lists too long");
+    P->tile_off[u] = (int32_t)P->tiles.size();
+    if (P->length[u] == 0) continue;
+    for (int64_t r = P->range_off[u]; r < P->range_off[u + 1]; ++r) {
+      const int32_t src = P->ranges[3 * r], lo = P->ranges[3 * r + 1], hi = P->ranges[3 * r + 2];
+      for (int32_t lp = lo / kPage; lp <= (hi - 1) / kPage; ++lp) {
+        const int32_t tlo = std::max(lo - lp * kPage, 0), thi = std::min(hi - lp * kPage, kPage);
+        P->tiles.push_back({P->page_table[P->slot0[src] + lp], pack(tlo, thi)});
+      }
+    }
+    P->tile_nonself[u] = (int32_t)P->tiles.size() - P->tile_off[u];
+    for (int32_t lp = 0; lp < P->npages[u]; ++lp) {
+      const int32_t ph = P->page_table[P->slot0[u] + lp];
+      P->tiles.push_back({ph, pack(0, P->page_nrows[ph])});
+    }
+    for (int32_t lp = 0; lp < P->npages[u]; ++lp) {
+      const int32_t ph = P->page_table[P->slot0[u] + lp];
+      P->qpages.push_back({ph, P->page_nrows[ph], P->tile_off[u], P->tile_nonself[u] + lp + 1});
+    }
+  }
+  P->tile_off[n] = (int32_t)P->tiles.size();
+
+  // ---- 8. reader lists per KV page (fixed order: reader node, then tile order) -------
+  std::vector<int64_t> cnt(n_pages + 1, 0);
+  auto for_each_entry = [&](auto&& emit) {
+    for (int32_t w = 0; w < n; ++w) {
+      if (P->length[w] == 0) continue;
+      for (int32_t t = P->tile_off[w]; t < P->tile_off[w] + P->tile_nonself[w]; ++t)
+        emit(P->tiles[t].page, KEntry{P->slot0[w], 0, P->npages[w], P->tiles[t].lohi});
+      for (int32_t lp = 0; lp < P->npages[w]; ++lp) {
+        const int32_t ph = P->page_table[P->slot0[w] + lp];
+        const int32_t nr = P->page_nrows[ph];
+        emit(ph, KEntry{P->slot0[w], lp, lp + 1, pack(0, nr) | (1 << 16)});
+        if (lp + 1 < P->npages[w]) emit(ph, KEntry{P->slot0[w], lp + 1, P->npages[w], pack(0, nr)});
+      }
+    }
+  };
+  for_each_entry([&](int32_t ph, const KEntry&) { cnt[ph + 1]++; });
+  for (int32_t i = 0; i < n_pages; ++i) cnt[i + 1] += cnt[i];
+  if (cnt[n_pages] > INT32_MAX) return fail(err, DAG_E_OVERFLOW, "reader lists too long");
+  P->kv_off.assign(n_pages + 1, 0);
+  for (int32_t i = 0; i <= n_pages; ++i) P->kv_off[i] = (int32_t)cnt[i];
+  P->kentries.assign(cnt[n_pages], KEntry{0, 0, 0, 0});
+  {
+    std::vector<int64_t> fill(cnt.begin(), cnt.end() - 1);
+    for_each_entry([&](int32_t ph, const KEntry& e) { P->kentries[fill[ph]++] = e; });
+  }
+
+  // ---- 9. launch orders (largest estimated work first; ties by index) ---------------
+  {
+    std::vector<int64_t> wq(P->qpages.size(), 0);
+    for (size_t i = 0; i < P->qpages.size(); ++i) {
+      const QPage& q = P->qpages[i];
+      int64_t keys = 0;
+      for (int32_t t = q.tile_begin; t < q.tile_begin + q.tile_count; ++t)
+        keys += ((P->tiles[t].lohi >> 8) & 0xff) - (P->tiles[t].lohi & 0xff);
+      wq[i] = keys;
+    }
+    P->fwd_order.resize(P->qpages.size());
+    std::iota(P->fwd_order.begin(), P->fwd_order.end(), 0);
+    std::stable_sort(P->fwd_order.begin(), P->fwd_order.end(),
+                     [&](int32_t a, int32_t b) { return wq[a] > wq[b]; });
+    std::vector<int64_t> wk(n_pages, 0);
+    for (int32_t ph = 0; ph < n_pages; ++ph) {
+      int64_t w = 0;
+      for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
+        const KEntry& k = P->kentries[e];
+        w += (int64_t)(k.lq1 - k.lq0) * (((k.lohi_diag >> 8) & 0xff) - (k.lohi_diag & 0xff));
+      }
+      wk[ph] = w;
+    }
+    P->bwd_order.clear();
+    for (int32_t ph = 0; ph < n_pages; ++ph)
+      if (P->page_nrows[ph] > 0) P->bwd_order.push_back(ph);
+    std::stable_sort(P->bwd_order.begin(), P->bwd_order.end(),
+                     [&](int32_t a, int32_t b) { return wk[a] > wk[b]; });
+  }
+
+  // ---- info ------------------------------------------------------------------------
+  dag_plan_info& I = P->info;
+  I = dag_plan_info{};
+  I.rows = C;
+  I.tokens = tokens;
+  I.pages = n_pages;
+  I.query_pages = (int64_t)P->qpages.size();
+  I.transitive = opts.transitive;
+  I.max_position = (int32_t)max_pos;
+  std::vector<char> has_child(n, 0);
+  for (int32_t u = 0; u < n; ++u)
+    if (P->parent[u] >= 0) has_child[P->parent[u]] = 1;
+  for (int32_t u = 0; u < n; ++u) {
+    int64_t nonself = 0;
+    for (int64_t r = P->range_off[u]; r < P->range_off[u + 1]; ++r)
+      nonself += P->ranges[3 * r + 2] - P->ranges[3 * r + 1];
+    const int64_t L = P->length[u];
+    I.visible_pairs += L * nonself + L * (L + 1) / 2;
+    if (!has_child[u]) {
+      const int64_t T = L + nonself;
+      I.n_trajectories += 1;
+      I.flat_rows += T;
+      I.flat_pairs += T * (T + 1) / 2;
+    }
+  }
+  for (const QPage& q : P->qpages) I.fwd_tiles += q.tile_count;
+  I.bwd_entries = (int64_t)P->kentries.size();
+  return DAG_OK;
+}
+
+}  // namespace dagattn

@@ -1,0 +1,79 @@
+// Host-side DAG compactor: turns tree and mount edges into an immutable plan.
+//
+// Plain C++17 with no HIP dependency, so it builds and is tested on a host
+// without a GPU (and under the host sanitizers).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "../../include/dag_attn.h"
+
+namespace dagattn {
+
+constexpr int kPage = 64;  // rows per KV page and per query block
+
+// One visited KV tile: a physical page and the half-open row range [lo, hi)
+// of it that is visible.  Packed so a kernel fetches it with one 8-byte load.
+struct Tile {
+  int32_t page;
+  int32_t lohi;  // lo | (hi << 8)
+};
+
+// One query block (= one page of a node's rows).  The tiles it visits are
+// the first `tile_count` entries of its node's tile list starting at
+// `tile_begin`: the node's visible non-self tiles, then the node's own pages
+// 0..lp; the last one is the diagonal page, masked causally.
+struct QPage {
+  int32_t phys;
+  int32_t nrows;
+  int32_t tile_begin;
+  int32_t tile_count;
+};
+
+// One reader-list entry of a KV page: the query pages [lq0, lq1) of the node
+// whose page-table slots start at slot_base see rows [lo, hi) of the page;
+// `diag` marks the page's own query block (causal mask).
+struct KEntry {
+  int32_t slot_base;
+  int32_t lq0;
+  int32_t lq1;
+  int32_t lohi_diag;  // lo | (hi << 8) | (diag << 16)
+};
+
+struct DeviceTables;  // defined by the HIP side
+struct Timing;        // defined by the HIP side
+
+struct Plan {
+  dag_build_opts opts{};
+  int32_t n_nodes = 0;
+  std::vector<int32_t> parent, length;
+  std::vector<std::vector<dag_mount>> direct;  // non-empty mounts per node
+  std::vector<int32_t> order;                  // dependency (topological) order
+  std::vector<int32_t> start;                  // Eq. 2 start position per node
+  std::vector<int64_t> tok_off;                // first token id per node
+  std::vector<int32_t> slot0, npages;          // page-table slots per node
+  std::vector<int32_t> page_table;             // slot -> physical page
+  std::vector<int32_t> page_nrows;             // physical page -> valid rows
+  std::vector<int64_t> range_off;              // node -> offset into ranges (triples)
+  std::vector<int32_t> ranges;                 // (src, lo, hi) non-self visibility
+  std::vector<int32_t> tile_off, tile_nonself; // node -> tile list
+  std::vector<Tile> tiles;
+  std::vector<QPage> qpages;
+  std::vector<int32_t> fwd_order;              // query-page ids, heaviest first
+  std::vector<int32_t> kv_off;                 // physical page -> first reader entry (size pages+1)
+  std::vector<KEntry> kentries;
+  std::vector<int32_t> bwd_order;              // physical pages with rows, heaviest first
+  std::vector<int32_t> pos_of_row;             // C
+  std::vector<int32_t> row_of_token;           // U
+  dag_plan_info info{};
+  DeviceTables* dev = nullptr;
+  Timing* timing = nullptr;
+};
+
+// Compile; returns DAG_OK or an error code with a message in `err`.
+dag_status build_plan(const dag_node* nodes, int32_t n_nodes, const dag_mount* mounts,
+                      int32_t n_mounts, const dag_build_opts* opts, Plan* out, std::string* err);
+
+}  // namespace dagattn

@@ -1,0 +1,201 @@
+/*
+ * dag_attn.h -- packed attention over a rollout DAG on AMD MI355X (gfx950).
+ *
+ * A rollout DAG has tree edges (continuation, fork, rewind) and read_thread
+ * mount edges (Octopus: One Brain, Many Branches for Latent-KV Multi-Agent RL,
+ * Sec. 3 and Table 2).  Every shared prefix is stored once, as compact token
+ * rows grouped into 64-row KV pages; each query token attends to its tree
+ * ancestors, to the spans mounted along its chain and to its own earlier
+ * tokens (Octopus Sec. 3.3 Eq. 4; HARTS: Hybrid-Attention RL over Tree
+ * Structures, Sec. 4.2 Eq. 21-22).  Mounted keys keep their native positions
+ * and a reader's later tokens jump past them (Octopus Sec. 3.2 Eq. 2).  The
+ * backward pass sends every reader's dK/dV into the producer's rows, summed
+ * over readers in a fixed order, with no floating-point atomics (Octopus
+ * Sec. 3.4 Eq. 8; HARTS Sec. 3.4).
+ *
+ * Two kinds of calls:
+ *   - dag_build & co. run on the host only: they validate the DAG and compile
+ *     it into an immutable plan (positions, page table, per-query-page
+ *     visibility tile lists, per-KV-page reader lists, launch orders).
+ *   - dag_attn_fwd / dag_attn_bwd enqueue HIP kernels on the caller's stream.
+ *     They neither allocate (once the plan is uploaded) nor synchronise.
+ *
+ * Conventions for every call:
+ *   - Return value: DAG_OK or an error code; nothing aborts, throws or prints.
+ *     dag_last_error() returns a thread-local description of the last error.
+ *   - Tensor arguments are device pointers owned by the caller.  Layout is
+ *     row-major [C, H, D]: C compact rows (dag_plan_info.rows), H heads, D the
+ *     head dimension, contiguous.  Callers place token (node u, own offset i)
+ *     at the row dag_plan_rows reports.  Padding rows are ignored on input and
+ *     written as zero on output.
+ *   - Gradients are written, not accumulated.
+ *   - Kernel launch failures return DAG_E_DEVICE; faults during execution
+ *     surface at the caller's next synchronisation.
+ */
+#ifndef DAG_ATTN_H
+#define DAG_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DAG_OK = 0,
+  DAG_E_INVALID = 1,             /* bad argument, malformed table, no nodes          */
+  DAG_E_NOT_TOPO = 2,            /* a node's parent index is not smaller than its own */
+  DAG_E_MOUNT_CYCLE = 3,         /* tree and mount edges together form a cycle        */
+  DAG_E_MOUNT_RANGE = 4,         /* mounted span outside the source's own tokens      */
+  DAG_E_SELF_ANCESTOR_MOUNT = 5, /* a node mounts itself or one of its ancestors      */
+  DAG_E_OVERFLOW = 6,            /* a row, page or pair count exceeds its integer type */
+  DAG_E_WORKSPACE = 7,           /* workspace pointer missing or too small            */
+  DAG_E_UNSUPPORTED = 8,         /* parameters outside what the kernels implement     */
+  DAG_E_DEVICE = 9               /* a HIP runtime call or kernel launch failed        */
+} dag_status;
+
+/* One node of the DAG: a maximal run of tokens between fork / rewind /
+ * read_thread boundaries (Octopus Sec. 3.3 item 1).  Nodes must be listed so
+ * that parent < own index.  The node's mounts are mounts[mount_first ..
+ * mount_first + mount_count) and are active from the node's first token; they
+ * stay active for all descendants. */
+typedef struct {
+  int32_t parent;       /* -1 for a root                                  */
+  int32_t length;       /* own tokens, >= 0                               */
+  int32_t mount_first;  /* first entry in the mount table                 */
+  int32_t mount_count;  /* number of entries, >= 0                        */
+} dag_node;
+
+/* A read_thread mount: the reader sees src's own tokens [begin, end) at their
+ * native positions (Octopus Table 2 and Sec. 3.2).  begin == end is a legal
+ * no-op (any source, any offset within 0..length(src)). */
+typedef struct {
+  int32_t src_node;
+  int32_t begin;
+  int32_t end;
+} dag_mount;
+
+typedef struct {
+  int32_t page_size;    /* must be 64 (0 selects 64)                                    */
+  int32_t q_block;      /* must be 64 (0 selects 64): one query block per KV page        */
+  int32_t transitive;   /* 1: a reader also sees what its mounted sources see (Octopus   */
+                        /*    Sec. 3.3 item 1, "including transitive mounts"); 0: direct */
+  int32_t page_shuffle; /* 0: pages in node order; otherwise a seed for a random physical */
+                        /*    page assignment (the page table stays exact)               */
+} dag_build_opts;
+
+typedef struct dag_plan dag_plan; /* opaque and immutable after dag_build */
+
+typedef struct {
+  int64_t rows;            /* C: compact rows including page padding (pages * 64)    */
+  int64_t tokens;          /* U: unique tokens = sum of node lengths                  */
+  int64_t pages;           /* physical KV pages                                       */
+  int64_t query_pages;     /* pages holding at least one row (one query block each)   */
+  int64_t visible_pairs;   /* P: visible (query, key) pairs over compact queries      */
+  int64_t flat_rows;       /* rows of the per-trajectory expansion incl. spliced spans */
+  int64_t flat_pairs;      /* causal pairs of that expansion over every trajectory row */
+  int64_t n_trajectories;  /* leaves                                                  */
+  int64_t fwd_tiles;       /* sum over query pages of visited KV tiles                 */
+  int64_t bwd_entries;     /* reader-list entries over all KV pages                    */
+  int32_t max_position;    /* largest Eq. 2 position                                  */
+  int32_t transitive;
+} dag_plan_info;
+
+/* Validate the node/mount tables and compile them into a plan.  Host only;
+ * does not touch the GPU.  On error *out is left NULL and the code names the
+ * first violated rule (checked in this order: table shape, parents, lengths,
+ * mount slices and sources (INVALID / NOT_TOPO), span ranges (MOUNT_RANGE),
+ * reads of the reader's own chain (SELF_ANCESTOR_MOUNT), cycles
+ * (MOUNT_CYCLE), integer overflow (OVERFLOW)).  Zero-length mounts are
+ * checked for range only and otherwise ignored. */
+dag_status dag_build(const dag_node* nodes, int32_t n_nodes, const dag_mount* mounts,
+                     int32_t n_mounts, const dag_build_opts* opts, dag_plan** out);
+
+void dag_plan_destroy(dag_plan* plan);
+
+dag_status dag_plan_info_get(const dag_plan* plan, dag_plan_info* out);
+
+/* Row of every token in node-major order (token (u, i) has index
+ * sum_{w<u} length(w) + i) -> row_of_token[U]; Eq. 2 position of every row
+ * -> pos_of_row[C] (-1 on padding rows).  Either pointer may be NULL. */
+dag_status dag_plan_rows(const dag_plan* plan, int32_t* row_of_token, int32_t* pos_of_row);
+
+/* Start position s(u) of every node (Octopus Sec. 3.2 Eq. 2) -> start[n_nodes]. */
+dag_status dag_plan_starts(const dag_plan* plan, int32_t* start);
+
+/* Non-self part of what node u's tokens see, as disjoint [lo, hi) ranges of
+ * source nodes' own offsets, ordered as the kernels visit them: mounted spans
+ * first, then ancestors root to parent (Octopus Eq. 4).  Writes up to cap
+ * triples (src, lo, hi) into out[3 * cap] and the total count into *n. */
+dag_status dag_plan_node_ranges(const dag_plan* plan, int32_t u, int32_t* out, int32_t cap,
+                                int32_t* n);
+
+/* Copy the plan's device tables to the current HIP device, on `hip_stream`,
+ * and wait for the copy.  Called implicitly by the first fwd/bwd; call it
+ * yourself before capturing fwd/bwd in a graph, since it allocates and
+ * synchronises.  A plan serves one device: using it from another returns
+ * DAG_E_DEVICE. */
+dag_status dag_plan_upload(dag_plan* plan, void* hip_stream);
+
+enum { DAG_DTYPE_BF16 = 0, DAG_DTYPE_FP32 = 1 };
+
+typedef struct {
+  int32_t n_q_heads;   /* Hq                                                            */
+  int32_t n_kv_heads;  /* Hkv; Hq % Hkv == 0, query head h reads KV head h / (Hq / Hkv) */
+  int32_t head_dim;    /* even, 2..128                                                  */
+  int32_t dtype;       /* DAG_DTYPE_BF16: bf16 tensors, fp32 accumulation (MFMA when     */
+                       /* head_dim == 128 and Hq == 4 Hkv); DAG_DTYPE_FP32: fp32 throughout */
+  float scale;         /* softmax scale; 0 selects 1/sqrt(head_dim)                      */
+  float rope_base;     /* rotary base (Octopus Eq. 1, pairs (i, i + D/2),                */
+                       /* theta_i = base^(-2i/D), angles in fp64); 0 disables rotation    */
+} dag_attn_params;
+
+/* Workspace bytes the forward and the backward need for this plan and shape. */
+dag_status dag_attn_workspace(const dag_plan* plan, const dag_attn_params* p, size_t* fwd_bytes,
+                              size_t* bwd_bytes);
+
+/* Forward (Octopus Eq. 4 with Eq. 1-2 positions; HARTS Eq. 22):
+ *   o[t,h]   = sum_{j in V(t)} softmax_j(scale <R(pos_t) q[t,h], R(pos_j) k[j,g]>) v[j,g]
+ *   lse[t,h] = log sum_{j in V(t)} exp(scale <R(pos_t) q[t,h], R(pos_j) k[j,g]>)
+ * q, o: [C, Hq, D]; k, v: [C, Hkv, D] (dtype); lse: [C, Hq] fp32.
+ * ws: device workspace of at least fwd_bytes. */
+dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k,
+                        const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
+                        void* hip_stream);
+
+/* Backward of dag_attn_fwd given the upstream gradient dO [C, Hq, D]:
+ * dq [C, Hq, D]; dk, dv [C, Hkv, D], where every key row's gradient is the sum
+ * over all readers (own branch, descendants, mount readers) taken in a fixed
+ * order, so results are bitwise reproducible (Octopus Sec. 3.4 Eq. 8, HARTS
+ * Sec. 3.4).  o and lse are the forward's outputs.  ws: at least bwd_bytes. */
+dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k,
+                        const void* v, const void* o, const float* lse, const void* dO, void* dq,
+                        void* dk, void* dv, void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Per-kernel timing, for profiling.  While enabled, dag_attn_fwd/bwd record a
+ * HIP event pair on their stream around each of their kernels (at most
+ * `capacity` pairs, created here; later launches go unrecorded).
+ * dag_attn_timing_read waits for the recorded events, writes for each kernel
+ * k in dag_kernel_id the summed duration ms[k] (milliseconds) and the number of
+ * launches counts[k] since the last read, and resets.  Disabling (enable = 0)
+ * destroys the events.  The plan must not be in use on another thread. */
+enum {
+  DAG_K_PROLOGUE_FWD = 0, /* rotary table and operand relayouts of the forward   */
+  DAG_K_FWD = 1,          /* attention forward                                    */
+  DAG_K_PROLOGUE_BWD = 2, /* rotary table, rowsum(dO * O) and relayouts          */
+  DAG_K_DKDV = 3,         /* per-KV-page dK/dV reduction                          */
+  DAG_K_DQ = 4,           /* per-query-block dQ                                   */
+  DAG_K_COUNT = 5
+};
+dag_status dag_attn_timing_enable(dag_plan* plan, int32_t enable, int32_t capacity);
+dag_status dag_attn_timing_read(dag_plan* plan, double* ms, int64_t* counts);
+
+/* Thread-local description of the last error ("" if none). */
+const char* dag_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DAG_ATTN_H */

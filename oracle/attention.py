@@ -49,12 +49,15 @@ class AttnParams:
 
 
 def _np(x):
+    """torch tensors become numpy arrays; numpy arrays and other indexable views pass through."""
     if hasattr(x, "detach"):
         x = x.detach().cpu()
         if str(x.dtype) == "torch.bfloat16":
             x = x.float()
-        x = x.numpy()
-    return np.asarray(x)
+        return x.numpy()
+    if isinstance(x, (list, tuple)):
+        return np.asarray(x)
+    return x
 
 
 def _softmax_rows(s: np.ndarray):
