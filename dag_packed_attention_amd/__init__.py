@@ -51,7 +51,7 @@ class DagPlanInfo(ctypes.Structure):
 
 class DagAttnParams(ctypes.Structure):
     _fields_ = [("n_q_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
-                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("rope_base", ctypes.c_float)]
 
 
@@ -199,16 +199,22 @@ class AttnParams:
     dtype: str = "bf16"          # "bf16" or "fp32"
     scale: float = 0.0           # 0 -> 1/sqrt(head_dim)
     rope_base: float = 10000.0   # 0 -> no rotation
+    grad_dtype: Optional[str] = None   # dq/dk/dv element type; None -> same as dtype
 
     def c(self) -> DagAttnParams:
-        dt = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}[self.dtype]
-        return DagAttnParams(self.n_q_heads, self.n_kv_heads, self.head_dim, dt, float(self.scale),
-                             float(self.rope_base))
+        m = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}
+        return DagAttnParams(self.n_q_heads, self.n_kv_heads, self.head_dim, m[self.dtype],
+                             m[self.grad_dtype or self.dtype], float(self.scale), float(self.rope_base))
 
     @property
     def torch_dtype(self):
         import torch
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    @property
+    def torch_grad_dtype(self):
+        import torch
+        return torch.bfloat16 if (self.grad_dtype or self.dtype) == "bf16" else torch.float32
 
 
 def _stream_ptr(stream) -> ctypes.c_void_p:
@@ -263,12 +269,15 @@ def attn_bwd(plan: Plan, p: AttnParams, q, k, v, o, lse, dO, dq=None, dk=None, d
     for name, t, h in (("q", q, p.n_q_heads), ("k", k, p.n_kv_heads), ("v", v, p.n_kv_heads),
                        ("o", o, p.n_q_heads), ("dO", dO, p.n_q_heads)):
         _check_tensor(name, t, C, h, p.head_dim, dt, dev)
+    gdt = p.torch_grad_dtype
     if dq is None:
-        dq = torch.empty_like(q)
+        dq = torch.empty(q.shape, dtype=gdt, device=dev)
     if dk is None:
-        dk = torch.empty_like(k)
+        dk = torch.empty(k.shape, dtype=gdt, device=dev)
     if dv is None:
-        dv = torch.empty_like(v)
+        dv = torch.empty(v.shape, dtype=gdt, device=dev)
+    for name, t, h in (("dq", dq, p.n_q_heads), ("dk", dk, p.n_kv_heads), ("dv", dv, p.n_kv_heads)):
+        _check_tensor(name, t, C, h, p.head_dim, gdt, dev)
     _, need = workspace_bytes(plan, p)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)

@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <type_traits>
 #include <string>
 #include <vector>
 
@@ -76,6 +77,10 @@ dag_status check_params(const dag_attn_params* p) {
     return set_err(DAG_E_UNSUPPORTED, "head_dim must be even and in [2, 128]");
   if (p->dtype != DAG_DTYPE_BF16 && p->dtype != DAG_DTYPE_FP32)
     return set_err(DAG_E_UNSUPPORTED, "dtype must be DAG_DTYPE_BF16 or DAG_DTYPE_FP32");
+  if (p->grad_dtype != DAG_DTYPE_BF16 && p->grad_dtype != DAG_DTYPE_FP32)
+    return set_err(DAG_E_UNSUPPORTED, "grad_dtype must be DAG_DTYPE_BF16 or DAG_DTYPE_FP32");
+  if (p->dtype == DAG_DTYPE_FP32 && p->grad_dtype != DAG_DTYPE_FP32)
+    return set_err(DAG_E_UNSUPPORTED, "fp32 inputs need fp32 gradients");
   if (!(p->rope_base >= 0.f) || std::isinf(p->rope_base) || (p->rope_base > 0.f && p->rope_base <= 1.f))
     return set_err(DAG_E_INVALID, "rope_base must be 0 (off) or > 1");
   if (!std::isfinite(p->scale)) return set_err(DAG_E_INVALID, "scale must be finite");
@@ -454,17 +459,24 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       launch_relayout<bf16_t, bf16_t>(s, k16, w.cs, D.page_nrows, (bf16_t*)w.kn, (bf16_t*)w.kt, s.Hkv, stream);
       launch_relayout<bf16_t, bf16_t>(s, d16, nullptr, D.page_nrows, nullptr, (bf16_t*)w.dOt, s.Hq, stream);
     }
-    {
-      Span sp(P, DAG_K_DKDV, stream);
-      launch_dkdv_mfma(s, n_kvp, (const bf16_t*)w.qn, (const bf16_t*)w.qt, (const bf16_t*)w.kn, v16, d16,
-                       (const bf16_t*)w.dOt, w.ld, w.cs, D.bwd_order, D.kv_off, D.kentries, D.page_table,
-                       D.page_nrows, (bf16_t*)dk, (bf16_t*)dv, stream);
-    }
-    {
-      Span sp(P, DAG_K_DQ, stream);
-      launch_dq_mfma(s, n_qp, (const bf16_t*)w.qn, (const bf16_t*)w.kn, (const bf16_t*)w.kt, v16, d16, w.ld, w.cs,
-                     D.qpages, D.fwd_order, D.tiles, (bf16_t*)dq, stream);
-    }
+    auto grads = [&](auto* tag) {
+      using TG = std::remove_pointer_t<decltype(tag)>;
+      {
+        Span sp(P, DAG_K_DKDV, stream);
+        launch_dkdv_mfma<TG>(s, n_kvp, (const bf16_t*)w.qn, (const bf16_t*)w.qt, (const bf16_t*)w.kn, v16, d16,
+                             (const bf16_t*)w.dOt, w.ld, w.cs, D.bwd_order, D.kv_off, D.kentries, D.page_table,
+                             D.page_nrows, (TG*)dk, (TG*)dv, stream);
+      }
+      {
+        Span sp(P, DAG_K_DQ, stream);
+        launch_dq_mfma<TG>(s, n_qp, (const bf16_t*)w.qn, (const bf16_t*)w.kn, (const bf16_t*)w.kt, v16, d16, w.ld,
+                           w.cs, D.qpages, D.fwd_order, D.tiles, (TG*)dq, stream);
+      }
+    };
+    if (p->grad_dtype == DAG_DTYPE_FP32)
+      grads((float*)nullptr);
+    else
+      grads((bf16_t*)nullptr);
   } else if (p->dtype == DAG_DTYPE_BF16) {
     {
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
@@ -474,9 +486,16 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv, stream);
     }
     Span sp(P, DAG_K_DKDV, stream);
-    launch_bwd_simple<bf16_t>(s, n_qp, n_kvp, (const float*)w.qn, (const float*)w.kn, (const bf16_t*)v,
-                              (const bf16_t*)dO, w.ld, w.cs, D.qpages, D.fwd_order, D.tiles, D.bwd_order, D.kv_off,
-                              D.kentries, D.page_table, D.page_nrows, (bf16_t*)dq, (bf16_t*)dk, (bf16_t*)dv, stream);
+    if (p->grad_dtype == DAG_DTYPE_FP32)
+      launch_bwd_simple<bf16_t, float>(s, n_qp, n_kvp, (const float*)w.qn, (const float*)w.kn, (const bf16_t*)v,
+                                       (const bf16_t*)dO, w.ld, w.cs, D.qpages, D.fwd_order, D.tiles, D.bwd_order,
+                                       D.kv_off, D.kentries, D.page_table, D.page_nrows, (float*)dq, (float*)dk,
+                                       (float*)dv, stream);
+    else
+      launch_bwd_simple<bf16_t, bf16_t>(s, n_qp, n_kvp, (const float*)w.qn, (const float*)w.kn, (const bf16_t*)v,
+                                        (const bf16_t*)dO, w.ld, w.cs, D.qpages, D.fwd_order, D.tiles, D.bwd_order,
+                                        D.kv_off, D.kentries, D.page_table, D.page_nrows, (bf16_t*)dq, (bf16_t*)dk,
+                                        (bf16_t*)dv, stream);
   } else {
     {
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
@@ -486,7 +505,7 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       launch_relayout<float, float>(s, (const float*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv, stream);
     }
     Span sp(P, DAG_K_DKDV, stream);
-    launch_bwd_simple<float>(s, n_qp, n_kvp, (const float*)w.qn, (const float*)w.kn, (const float*)v,
+    launch_bwd_simple<float, float>(s, n_qp, n_kvp, (const float*)w.qn, (const float*)w.kn, (const float*)v,
                              (const float*)dO, w.ld, w.cs, D.qpages, D.fwd_order, D.tiles, D.bwd_order, D.kv_off,
                              D.kentries, D.page_table, D.page_nrows, (float*)dq, (float*)dk, (float*)dv, stream);
   }

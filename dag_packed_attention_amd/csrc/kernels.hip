@@ -315,11 +315,12 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
 }
 
 // dQ for one query block (64 rows) x one KV head; waves = the four query heads.
+template <typename TG>
 __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
     const bf16_t* __restrict__ qn, const bf16_t* __restrict__ kn, const bf16_t* __restrict__ kt,
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO, const float2* __restrict__ ldd,
     const float2* __restrict__ cs, const QPage* __restrict__ qpages, const int32_t* __restrict__ order,
-    const Tile* __restrict__ tiles, bf16_t* __restrict__ dq, int Hq, int Hkv, float sl2, float scale) {
+    const Tile* __restrict__ tiles, TG* __restrict__ dq, int Hq, int Hkv, float sl2, float scale) {
   __shared__ bf16_t lk[64 * kKStride];
   __shared__ bf16_t lvv[64 * kKStride];
   __shared__ bf16_t lkt[kD * kTStride];
@@ -404,7 +405,7 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
     const int row = nb * 32 + l32;
     const bool valid = row < qp.nrows;
     const int64_t grow = (int64_t)qp.phys * 64 + row;
-    bf16_t* out = dq + (grow * Hq + h) * kD;
+    TG* out = dq + (grow * Hq + h) * kD;
 #pragma unroll
     for (int a = 0; a < 2; ++a)
 #pragma unroll
@@ -419,8 +420,8 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
             r1 = g1 * c.x + g2 * c.y;
             r2 = g2 * c.x - g1 * c.y;
           }
-          out[d] = f2bf(r1);
-          out[d + 64] = f2bf(r2);
+          st_f(out + d, r1);
+          st_f(out + d + 64, r2);
         }
   }
 }
@@ -428,13 +429,14 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
 // dK, dV for one KV page x one KV head.  Waves = the four query heads; each
 // wave walks the page's reader list and keeps its own dK/dV in registers; the
 // four are then summed through LDS in head order.
+template <typename TG>
 __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
     const bf16_t* __restrict__ qn, const bf16_t* __restrict__ qt, const bf16_t* __restrict__ kn,
     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO, const bf16_t* __restrict__ dOt,
     const float2* __restrict__ ldd, const float2* __restrict__ cs, const int32_t* __restrict__ order,
     const int32_t* __restrict__ kv_off, const KEntry* __restrict__ ents,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ page_nrows,
-    bf16_t* __restrict__ dk, bf16_t* __restrict__ dv, int Hq, int Hkv, float sl2, float scale) {
+    TG* __restrict__ dk, TG* __restrict__ dv, int Hq, int Hkv, float sl2, float scale) {
   // K/V tiles during the walk; the same bytes hold the head reduction afterwards
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemDkdv];
   bf16_t* lk = reinterpret_cast<bf16_t*>(smem);
@@ -571,9 +573,9 @@ __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
           a = a2;
         }
       }
-      bf16_t* out = (which == 0 ? dk : dv) + (grow * Hkv + g) * kD;
-      out[i] = f2bf(a);
-      out[i + 64] = f2bf(b);
+      TG* out = (which == 0 ? dk : dv) + (grow * Hkv + g) * kD;
+      st_f(out + i, a);
+      st_f(out + i + 64, b);
     }
   }
 }
@@ -625,12 +627,12 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(
   lse[grow * Hq + h] = valid ? m + logf(l) : 0.f;
 }
 
-template <typename T>
+template <typename T, typename TG>
 __global__ __launch_bounds__(64) void dq_simple_kernel(
     const float* __restrict__ qn, const float* __restrict__ kn, const T* __restrict__ v,
     const T* __restrict__ dO, const float2* __restrict__ ldd, const float2* __restrict__ cs,
     const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
-    T* __restrict__ dq, int Hq, int Hkv, int D, float scale) {
+    TG* __restrict__ dq, int Hq, int Hkv, int D, float scale) {
   const int item = blockIdx.x;
   const QPage qp = qpages[order[item / Hq]];
   const int h = item % Hq, g = h / (Hq / Hkv);
@@ -679,13 +681,13 @@ __global__ __launch_bounds__(64) void dq_simple_kernel(
   }
 }
 
-template <typename T>
+template <typename T, typename TG>
 __global__ __launch_bounds__(64) void dkdv_simple_kernel(
     const float* __restrict__ qn, const float* __restrict__ kn, const T* __restrict__ v,
     const T* __restrict__ dO, const float2* __restrict__ ldd, const float2* __restrict__ cs,
     const int32_t* __restrict__ order, const int32_t* __restrict__ kv_off,
     const KEntry* __restrict__ ents, const int32_t* __restrict__ page_table,
-    const int32_t* __restrict__ page_nrows, T* __restrict__ dk, T* __restrict__ dv, int Hq, int Hkv,
+    const int32_t* __restrict__ page_nrows, TG* __restrict__ dk, TG* __restrict__ dv, int Hq, int Hkv,
     int D, float scale) {
   const int item = blockIdx.x;
   const int page = order[item / Hkv];
@@ -783,21 +785,28 @@ void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const
                                                             s.Hkv, s.scale * kLog2e);
 }
 
+template <typename TG>
 void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const bf16_t* kn, const bf16_t* kt,
                     const bf16_t* v, const bf16_t* dO, const float2* ld, const float2* cs, const QPage* qpages,
-                    const int32_t* order, const Tile* tiles, bf16_t* dq, hipStream_t st) {
-  dq_mfma_kernel<<<(unsigned)(n_qp * s.Hkv), 256, 0, st>>>(qn, kn, kt, v, dO, ld, cs, qpages, order, tiles, dq,
-                                                           s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
+                    const int32_t* order, const Tile* tiles, TG* dq, hipStream_t st) {
+  dq_mfma_kernel<TG><<<(unsigned)(n_qp * s.Hkv), 256, 0, st>>>(qn, kn, kt, v, dO, ld, cs, qpages, order, tiles, dq,
+                                                               s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
 }
 
+template <typename TG>
 void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const bf16_t* qn, const bf16_t* qt, const bf16_t* kn,
                       const bf16_t* v, const bf16_t* dO, const bf16_t* dOt, const float2* ld, const float2* cs,
                       const int32_t* order, const int32_t* kv_off, const KEntry* ents, const int32_t* page_table,
-                      const int32_t* page_nrows, bf16_t* dk, bf16_t* dv, hipStream_t st) {
-  dkdv_mfma_kernel<<<(unsigned)(n_kvp * s.Hkv), 256, 0, st>>>(qn, qt, kn, v, dO, dOt, ld, cs, order, kv_off, ents,
-                                                              page_table, page_nrows, dk, dv, s.Hq, s.Hkv,
-                                                              s.scale * kLog2e, s.scale);
+                      const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st) {
+  dkdv_mfma_kernel<TG><<<(unsigned)(n_kvp * s.Hkv), 256, 0, st>>>(qn, qt, kn, v, dO, dOt, ld, cs, order, kv_off,
+                                                                  ents, page_table, page_nrows, dk, dv, s.Hq, s.Hkv,
+                                                                  s.scale * kLog2e, s.scale);
 }
+
+template void launch_dq_mfma<bf16_t>(const LaunchShape&, int64_t, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const float2*, const float2*, const QPage*, const int32_t*, const Tile*, bf16_t*, hipStream_t);
+template void launch_dq_mfma<float>(const LaunchShape&, int64_t, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const float2*, const float2*, const QPage*, const int32_t*, const Tile*, float*, hipStream_t);
+template void launch_dkdv_mfma<bf16_t>(const LaunchShape&, int64_t, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const float2*, const float2*, const int32_t*, const int32_t*, const KEntry*, const int32_t*, const int32_t*, bf16_t*, bf16_t*, hipStream_t);
+template void launch_dkdv_mfma<float>(const LaunchShape&, int64_t, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const float2*, const float2*, const int32_t*, const int32_t*, const KEntry*, const int32_t*, const int32_t*, float*, float*, hipStream_t);
 
 template <typename T>
 void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,
@@ -807,22 +816,29 @@ void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, cons
                                                               s.D, s.scale);
 }
 
-template <typename T>
+template <typename T, typename TG>
 void launch_bwd_simple(const LaunchShape& s, int64_t n_qp, int64_t n_kvp, const float* qn, const float* kn,
                        const T* v, const T* dO, const float2* ld, const float2* cs, const QPage* qpages,
                        const int32_t* fwd_order, const Tile* tiles, const int32_t* bwd_order,
                        const int32_t* kv_off, const KEntry* ents, const int32_t* page_table,
-                       const int32_t* page_nrows, T* dq, T* dk, T* dv, hipStream_t st) {
-  dq_simple_kernel<T><<<(unsigned)(n_qp * s.Hq), 64, 0, st>>>(qn, kn, v, dO, ld, cs, qpages, fwd_order, tiles, dq,
-                                                             s.Hq, s.Hkv, s.D, s.scale);
-  dkdv_simple_kernel<T><<<(unsigned)(n_kvp * s.Hkv), 64, 0, st>>>(qn, kn, v, dO, ld, cs, bwd_order, kv_off, ents,
-                                                                 page_table, page_nrows, dk, dv, s.Hq, s.Hkv, s.D,
-                                                                 s.scale);
+                       const int32_t* page_nrows, TG* dq, TG* dk, TG* dv, hipStream_t st) {
+  dq_simple_kernel<T, TG><<<(unsigned)(n_qp * s.Hq), 64, 0, st>>>(qn, kn, v, dO, ld, cs, qpages, fwd_order, tiles,
+                                                                  dq, s.Hq, s.Hkv, s.D, s.scale);
+  dkdv_simple_kernel<T, TG><<<(unsigned)(n_kvp * s.Hkv), 64, 0, st>>>(qn, kn, v, dO, ld, cs, bwd_order, kv_off,
+                                                                      ents, page_table, page_nrows, dk, dv, s.Hq,
+                                                                      s.Hkv, s.D, s.scale);
 }
 
 template void launch_fwd_simple<bf16_t>(const LaunchShape&, int64_t, const float*, const float*, const bf16_t*, const QPage*, const int32_t*, const Tile*, bf16_t*, float*, hipStream_t);
 template void launch_fwd_simple<float>(const LaunchShape&, int64_t, const float*, const float*, const float*, const QPage*, const int32_t*, const Tile*, float*, float*, hipStream_t);
-template void launch_bwd_simple<bf16_t>(const LaunchShape&, int64_t, int64_t, const float*, const float*, const bf16_t*, const bf16_t*, const float2*, const float2*, const QPage*, const int32_t*, const Tile*, const int32_t*, const int32_t*, const KEntry*, const int32_t*, const int32_t*, bf16_t*, bf16_t*, bf16_t*, hipStream_t);
-template void launch_bwd_simple<float>(const LaunchShape&, int64_t, int64_t, const float*, const float*, const float*, const float*, const float2*, const float2*, const QPage*, const int32_t*, const Tile*, const int32_t*, const int32_t*, const KEntry*, const int32_t*, const int32_t*, float*, float*, float*, hipStream_t);
+#define INST_BWD_SIMPLE(T, TG)                                                                                 \
+  template void launch_bwd_simple<T, TG>(const LaunchShape&, int64_t, int64_t, const float*, const float*,     \
+                                         const T*, const T*, const float2*, const float2*, const QPage*,        \
+                                         const int32_t*, const Tile*, const int32_t*, const int32_t*,           \
+                                         const KEntry*, const int32_t*, const int32_t*, TG*, TG*, TG*,          \
+                                         hipStream_t);
+INST_BWD_SIMPLE(bf16_t, bf16_t)
+INST_BWD_SIMPLE(bf16_t, float)
+INST_BWD_SIMPLE(float, float)
 
 }  // namespace dagattn

@@ -26,22 +26,24 @@ void launch_rowdot(const LaunchShape& s, const T* o, const T* dO, const float* l
 void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const bf16_t* kn, const bf16_t* vt,
                      const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
                      hipStream_t st);
+template <typename TG>
 void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const bf16_t* kn, const bf16_t* kt,
                     const bf16_t* v, const bf16_t* dO, const float2* ld, const float2* cs, const QPage* qpages,
-                    const int32_t* order, const Tile* tiles, bf16_t* dq, hipStream_t st);
+                    const int32_t* order, const Tile* tiles, TG* dq, hipStream_t st);
+template <typename TG>
 void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const bf16_t* qn, const bf16_t* qt, const bf16_t* kn,
                       const bf16_t* v, const bf16_t* dO, const bf16_t* dOt, const float2* ld, const float2* cs,
                       const int32_t* order, const int32_t* kv_off, const KEntry* ents, const int32_t* page_table,
-                      const int32_t* page_nrows, bf16_t* dk, bf16_t* dv, hipStream_t st);
+                      const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st);
 template <typename T>
 void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,
                        const QPage* qpages, const int32_t* order, const Tile* tiles, T* o, float* lse,
                        hipStream_t st);
-template <typename T>
+template <typename T, typename TG>
 void launch_bwd_simple(const LaunchShape& s, int64_t n_qp, int64_t n_kvp, const float* qn, const float* kn,
                        const T* v, const T* dO, const float2* ld, const float2* cs, const QPage* qpages,
                        const int32_t* fwd_order, const Tile* tiles, const int32_t* bwd_order,
                        const int32_t* kv_off, const KEntry* ents, const int32_t* page_table,
-                       const int32_t* page_nrows, T* dq, T* dk, T* dv, hipStream_t st);
+                       const int32_t* page_nrows, TG* dq, TG* dk, TG* dv, hipStream_t st);
 
 }  // namespace dagattn

@@ -146,6 +146,9 @@ typedef struct {
   int32_t head_dim;    /* even, 2..128                                                  */
   int32_t dtype;       /* DAG_DTYPE_BF16: bf16 tensors, fp32 accumulation (MFMA when     */
                        /* head_dim == 128 and Hq == 4 Hkv); DAG_DTYPE_FP32: fp32 throughout */
+  int32_t grad_dtype;  /* element type of dq, dk, dv: DAG_DTYPE_BF16 or DAG_DTYPE_FP32;    */
+                       /* must be FP32 when dtype is FP32.  Large shared-row gradients     */
+                       /* keep their precision in FP32                                      */
   float scale;         /* softmax scale; 0 selects 1/sqrt(head_dim)                      */
   float rope_base;     /* rotary base (Octopus Eq. 1, pairs (i, i + D/2),                */
                        /* theta_i = base^(-2i/D), angles in fp64); 0 disables rotation    */
@@ -164,8 +167,8 @@ dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q,
                         const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
                         void* hip_stream);
 
-/* Backward of dag_attn_fwd given the upstream gradient dO [C, Hq, D]:
- * dq [C, Hq, D]; dk, dv [C, Hkv, D], where every key row's gradient is the sum
+/* Backward of dag_attn_fwd given the upstream gradient dO [C, Hq, D] (dtype):
+ * dq [C, Hq, D]; dk, dv [C, Hkv, D] (grad_dtype), where every key row's gradient is the sum
  * over all readers (own branch, descendants, mount readers) taken in a fixed
  * order, so results are bitwise reproducible (Octopus Sec. 3.4 Eq. 8, HARTS
  * Sec. 3.4).  o and lse are the forward's outputs.  ws: at least bwd_bytes. */
