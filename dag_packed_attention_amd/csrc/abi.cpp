@@ -112,8 +112,11 @@ struct BwdWs {
   void* kn;
   void* qt;
   void* kt;
+  void* vn;
+  void* dOn;
   void* dOt;
   float2* ld;
+  uint32_t* dmax;
 };
 
 size_t carve_fwd(const LaunchShape& s, bool mfma, void* base, FwdWs* w) {
@@ -121,9 +124,9 @@ size_t carve_fwd(const LaunchShape& s, bool mfma, void* base, FwdWs* w) {
   const size_t C = (size_t)s.C;
   w->cs = s.log2_base > 0 ? c.take<float2>(C * (s.D / 2)) : nullptr;
   if (mfma) {
-    w->qn = c.take<bf16_t>(C * s.Hq * s.D);
-    w->kn = c.take<bf16_t>(C * s.Hkv * s.D);
-    w->vt = c.take<bf16_t>(C * s.Hkv * s.D);
+    w->qn = c.take<f16_t>(C * s.Hq * s.D);
+    w->kn = c.take<f16_t>(C * s.Hkv * s.D);
+    w->vt = c.take<f16_t>(C * s.Hkv * s.D);
   } else {
     w->qn = c.take<float>(C * s.Hq * s.D);
     w->kn = c.take<float>(C * s.Hkv * s.D);
@@ -137,16 +140,19 @@ size_t carve_bwd(const LaunchShape& s, bool mfma, void* base, BwdWs* w) {
   const size_t C = (size_t)s.C;
   w->cs = s.log2_base > 0 ? c.take<float2>(C * (s.D / 2)) : nullptr;
   w->ld = c.take<float2>(C * s.Hq);
+  w->dmax = c.take<uint32_t>(1);
   if (mfma) {
-    w->qn = c.take<bf16_t>(C * s.Hq * s.D);
-    w->qt = c.take<bf16_t>(C * s.Hq * s.D);
-    w->dOt = c.take<bf16_t>(C * s.Hq * s.D);
-    w->kn = c.take<bf16_t>(C * s.Hkv * s.D);
-    w->kt = c.take<bf16_t>(C * s.Hkv * s.D);
+    w->qn = c.take<f16_t>(C * s.Hq * s.D);
+    w->qt = c.take<f16_t>(C * s.Hq * s.D);
+    w->dOn = c.take<f16_t>(C * s.Hq * s.D);
+    w->dOt = c.take<f16_t>(C * s.Hq * s.D);
+    w->kn = c.take<f16_t>(C * s.Hkv * s.D);
+    w->kt = c.take<f16_t>(C * s.Hkv * s.D);
+    w->vn = c.take<f16_t>(C * s.Hkv * s.D);
   } else {
     w->qn = c.take<float>(C * s.Hq * s.D);
     w->kn = c.take<float>(C * s.Hkv * s.D);
-    w->qt = w->dOt = w->kt = nullptr;
+    w->qt = w->dOt = w->kt = w->vn = w->dOn = nullptr;
   }
   return c.off;
 }
@@ -399,23 +405,23 @@ dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q,
   {
     Span sp(P, DAG_K_PROLOGUE_FWD, stream);
     if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
+    const int32_t* nr = D.page_nrows;
     if (mfma) {
-      launch_relayout<bf16_t, bf16_t>(s, (const bf16_t*)q, w.cs, D.page_nrows, (bf16_t*)w.qn, nullptr, s.Hq, stream);
-      launch_relayout<bf16_t, bf16_t>(s, (const bf16_t*)k, w.cs, D.page_nrows, (bf16_t*)w.kn, nullptr, s.Hkv, stream);
-      launch_relayout<bf16_t, bf16_t>(s, (const bf16_t*)v, nullptr, D.page_nrows, nullptr, (bf16_t*)w.vt, s.Hkv,
-                                      stream);
+      launch_relayout<bf16_t, f16_t>(s, (const bf16_t*)q, w.cs, nr, nullptr, (f16_t*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<bf16_t, f16_t>(s, (const bf16_t*)k, w.cs, nr, nullptr, (f16_t*)w.kn, nullptr, s.Hkv, stream);
+      launch_relayout<bf16_t, f16_t>(s, (const bf16_t*)v, nullptr, nr, nullptr, nullptr, (f16_t*)w.vt, s.Hkv, stream);
     } else if (p->dtype == DAG_DTYPE_BF16) {
-      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, D.page_nrows, (float*)w.qn, nullptr, s.Hq, stream);
-      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv, stream);
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, nr, nullptr, (float*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, nr, nullptr, (float*)w.kn, nullptr, s.Hkv, stream);
     } else {
-      launch_relayout<float, float>(s, (const float*)q, w.cs, D.page_nrows, (float*)w.qn, nullptr, s.Hq, stream);
-      launch_relayout<float, float>(s, (const float*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv, stream);
+      launch_relayout<float, float>(s, (const float*)q, w.cs, nr, nullptr, (float*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<float, float>(s, (const float*)k, w.cs, nr, nullptr, (float*)w.kn, nullptr, s.Hkv, stream);
     }
   }
   {
     Span sp(P, DAG_K_FWD, stream);
     if (mfma)
-      launch_fwd_mfma(s, n_qp, (const bf16_t*)w.qn, (const bf16_t*)w.kn, (const bf16_t*)w.vt, D.qpages, D.fwd_order,
+      launch_fwd_mfma(s, n_qp, (const f16_t*)w.qn, (const f16_t*)w.kn, (const f16_t*)w.vt, D.qpages, D.fwd_order,
                       D.tiles, (bf16_t*)o, lse, stream);
     else if (p->dtype == DAG_DTYPE_BF16)
       launch_fwd_simple<bf16_t>(s, n_qp, (const float*)w.qn, (const float*)w.kn, (const bf16_t*)v, D.qpages,
@@ -452,25 +458,30 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
     const bf16_t *q16 = (const bf16_t*)q, *k16 = (const bf16_t*)k, *v16 = (const bf16_t*)v;
     const bf16_t *o16 = (const bf16_t*)o, *d16 = (const bf16_t*)dO;
     {
+      const int32_t* nr = D.page_nrows;
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
       if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
-      launch_rowdot<bf16_t>(s, o16, d16, lse, D.page_nrows, w.ld, stream);
-      launch_relayout<bf16_t, bf16_t>(s, q16, w.cs, D.page_nrows, (bf16_t*)w.qn, (bf16_t*)w.qt, s.Hq, stream);
-      launch_relayout<bf16_t, bf16_t>(s, k16, w.cs, D.page_nrows, (bf16_t*)w.kn, (bf16_t*)w.kt, s.Hkv, stream);
-      launch_relayout<bf16_t, bf16_t>(s, d16, nullptr, D.page_nrows, nullptr, (bf16_t*)w.dOt, s.Hq, stream);
+      launch_maxabs<bf16_t>(s, d16, s.Hq, nr, w.dmax, stream);
+      launch_rowdot<bf16_t>(s, o16, d16, lse, nr, w.dmax, w.ld, stream);
+      launch_relayout<bf16_t, f16_t>(s, q16, w.cs, nr, nullptr, (f16_t*)w.qn, (f16_t*)w.qt, s.Hq, stream);
+      launch_relayout<bf16_t, f16_t>(s, k16, w.cs, nr, nullptr, (f16_t*)w.kn, (f16_t*)w.kt, s.Hkv, stream);
+      launch_relayout<bf16_t, f16_t>(s, v16, nullptr, nr, nullptr, (f16_t*)w.vn, nullptr, s.Hkv, stream);
+      launch_relayout<bf16_t, f16_t>(s, d16, nullptr, nr, w.dmax, (f16_t*)w.dOn, (f16_t*)w.dOt, s.Hq, stream);
     }
     auto grads = [&](auto* tag) {
       using TG = std::remove_pointer_t<decltype(tag)>;
       {
         Span sp(P, DAG_K_DKDV, stream);
-        launch_dkdv_mfma<TG>(s, n_kvp, (const bf16_t*)w.qn, (const bf16_t*)w.qt, (const bf16_t*)w.kn, v16, d16,
-                             (const bf16_t*)w.dOt, w.ld, w.cs, D.bwd_order, D.kv_off, D.kentries, D.page_table,
-                             D.page_nrows, (TG*)dk, (TG*)dv, stream);
+        launch_dkdv_mfma<TG>(s, n_kvp, (const f16_t*)w.qn, (const f16_t*)w.qt, (const f16_t*)w.kn,
+                             (const f16_t*)w.vn, (const f16_t*)w.dOn, (const f16_t*)w.dOt, w.ld, w.cs, w.dmax,
+                             D.bwd_order, D.kv_off, D.kentries, D.page_table, D.page_nrows, (TG*)dk, (TG*)dv,
+                             stream);
       }
       {
         Span sp(P, DAG_K_DQ, stream);
-        launch_dq_mfma<TG>(s, n_qp, (const bf16_t*)w.qn, (const bf16_t*)w.kn, (const bf16_t*)w.kt, v16, d16, w.ld,
-                           w.cs, D.qpages, D.fwd_order, D.tiles, (TG*)dq, stream);
+        launch_dq_mfma<TG>(s, n_qp, (const f16_t*)w.qn, (const f16_t*)w.kn, (const f16_t*)w.kt,
+                           (const f16_t*)w.vn, (const f16_t*)w.dOn, w.ld, w.cs, w.dmax, D.qpages, D.fwd_order,
+                           D.tiles, (TG*)dq, stream);
       }
     };
     if (p->grad_dtype == DAG_DTYPE_FP32)
@@ -481,9 +492,11 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
     {
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
       if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
-      launch_rowdot<bf16_t>(s, (const bf16_t*)o, (const bf16_t*)dO, lse, D.page_nrows, w.ld, stream);
-      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, D.page_nrows, (float*)w.qn, nullptr, s.Hq, stream);
-      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv, stream);
+      launch_rowdot<bf16_t>(s, (const bf16_t*)o, (const bf16_t*)dO, lse, D.page_nrows, nullptr, w.ld, stream);
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, D.page_nrows, nullptr, (float*)w.qn, nullptr, s.Hq,
+                                     stream);
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, D.page_nrows, nullptr, (float*)w.kn, nullptr, s.Hkv,
+                                     stream);
     }
     Span sp(P, DAG_K_DKDV, stream);
     if (p->grad_dtype == DAG_DTYPE_FP32)
@@ -500,9 +513,11 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
     {
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
       if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
-      launch_rowdot<float>(s, (const float*)o, (const float*)dO, lse, D.page_nrows, w.ld, stream);
-      launch_relayout<float, float>(s, (const float*)q, w.cs, D.page_nrows, (float*)w.qn, nullptr, s.Hq, stream);
-      launch_relayout<float, float>(s, (const float*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv, stream);
+      launch_rowdot<float>(s, (const float*)o, (const float*)dO, lse, D.page_nrows, nullptr, w.ld, stream);
+      launch_relayout<float, float>(s, (const float*)q, w.cs, D.page_nrows, nullptr, (float*)w.qn, nullptr, s.Hq,
+                                    stream);
+      launch_relayout<float, float>(s, (const float*)k, w.cs, D.page_nrows, nullptr, (float*)w.kn, nullptr, s.Hkv,
+                                    stream);
     }
     Span sp(P, DAG_K_DKDV, stream);
     launch_bwd_simple<float, float>(s, n_qp, n_kvp, (const float*)w.qn, (const float*)w.kn, (const float*)v,

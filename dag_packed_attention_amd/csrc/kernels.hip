@@ -1,26 +1,31 @@
 // HIP kernels for packed attention over a rollout DAG, written for gfx950.
 //
 // Data layout in HBM (C compact rows = pages * 64):
-//   user tensors   q, o, dO, dq  [C][Hq][D]     k, v, dk, dv  [C][Hkv][D]    lse [C][Hq] fp32
-//   workspace      cs  [C][D/2]  float2        cos/sin of the Eq. 1 rotation per row
-//                  xn  [page][H][64][D]        rotated, page-major ("natural")
-//                  xt  [page][H][D][64]        rotated, page-major, transposed, rows of every
-//                                              16-group stored with bits 2 and 3 of the row
-//                                              index swapped (the order in which an MFMA
-//                                              accumulator lane holds them, see below)
-//                  ld  [page][Hq][64] float2   (lse * log2 e, rowsum(dO * O)) for the backward
+//   user tensors   q, o, dO  [C][Hq][D] bf16/fp32   k, v [C][Hkv][D]   lse [C][Hq] fp32
+//                  dq [C][Hq][D], dk, dv [C][Hkv][D] in the gradient type (bf16 or fp32)
+//   workspace      cs  [C][D/2] float2          cos/sin of the Eq. 1 rotation per row
+//                  xn  [page][H][64][D] fp16    rotated (q, k) or copied (v, dO), page-major
+//                  xt  [page][H][D][64] fp16    the same, transposed; the rows of every 16-group
+//                                               are stored with bits 2 and 3 of the row index
+//                                               swapped (the order in which an MFMA accumulator
+//                                               lane holds them, see below)
+//                  ld  [page][Hq][64] float2    (lse * log2 e, s * rowsum(dO * O)) for the backward
+//                  dmax                         largest |dO| (float bits); s = 2^-floor(log2 dmax)
 //
-// MFMA path (bf16, D = 128, Hq = 4 Hkv).  A work-group serves one 64-row block
-// and one KV head; its four waves are the four query heads of that GQA group,
-// so every K/V tile staged in LDS is read by four heads.  Products are taken
-// in the transposed orientation S^T = K Q^T and O^T = V^T P^T with
-// v_mfma_f32_32x32x16_bf16: a 32x32 accumulator lane then holds one query
-// row (column n = lane % 32) and 16 keys, so the online-softmax state is
-// per lane and only the max crosses lanes (lane ^ 32).  Accumulator element r
-// of lane l is row m = 8 (r / 4) + 4 (l / 32) + r % 4.  Feeding it straight
-// back as the B operand of the next product makes the contraction index of
-// the two operands follow that same order, hence the bit-swapped rows of the
-// transposed layouts.
+// MFMA path (D = 128, Hq = 4 Hkv).  Operands are fp16: bf16 inputs convert
+// exactly, the rotated q/k and the probabilities P and dS keep three more
+// mantissa bits than bf16, and dO is scaled by the power of two s so that
+// small gradients do not fall below fp16's normal range (undone exactly on
+// dq, dk, dv).  A work-group serves one 64-row block and one KV head; its four
+// waves are the four query heads of that GQA group, so every K/V tile staged
+// in LDS is read by four heads.  Products are taken in the transposed
+// orientation S^T = K Q^T and O^T = V^T P^T with v_mfma_f32_32x32x16_f16: a
+// 32x32 accumulator lane then holds one query row (column n = lane % 32) and
+// 16 keys, so the online-softmax state is per lane and only the max crosses
+// lanes (lane ^ 32).  Accumulator element r of lane l is row
+// m = 8 (r / 4) + 4 (l / 32) + r % 4.  Feeding it straight back as the B
+// operand of the next product makes the contraction index of the two operands
+// follow that same order, hence the bit-swapped rows of the transposed layouts.
 //
 // The backward is two kernels.  dK/dV: one work-group per KV page and KV head
 // walks the page's reader list (every query block that sees the page, in a
@@ -35,8 +40,9 @@
 
 namespace dagattn {
 
-typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef _Float16 f16_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -49,9 +55,19 @@ __device__ __forceinline__ bf16_t f2bf(float x) {
 template <typename T> __device__ __forceinline__ float ld_f(const T* p);
 template <> __device__ __forceinline__ float ld_f<float>(const float* p) { return *p; }
 template <> __device__ __forceinline__ float ld_f<bf16_t>(const bf16_t* p) { return bf2f(*p); }
+template <> __device__ __forceinline__ float ld_f<f16_t>(const f16_t* p) { return (float)*p; }
 template <typename T> __device__ __forceinline__ void st_f(T* p, float x);
 template <> __device__ __forceinline__ void st_f<float>(float* p, float x) { *p = x; }
 template <> __device__ __forceinline__ void st_f<bf16_t>(bf16_t* p, float x) { *p = f2bf(x); }
+template <> __device__ __forceinline__ void st_f<f16_t>(f16_t* p, float x) { *p = (f16_t)x; }
+
+// 2^-e for the largest |x| = m 2^e (m in [1, 2)), from the float bits of that maximum: a
+// power-of-two factor that maps a tensor's largest magnitude into [1, 2), exactly reversible.
+__device__ __forceinline__ float pow2_scale(uint32_t maxbits) {
+  const float m = __uint_as_float(maxbits);
+  if (!(m > 0.f) || !isfinite(m)) return 1.f;
+  return ldexpf(1.f, -ilogbf(m));
+}
 
 // position of row r inside its transposed 16-group (bits 2 and 3 swapped)
 __device__ __forceinline__ int tperm(int r) {
@@ -87,11 +103,12 @@ __global__ void cs_kernel(const int32_t* __restrict__ pos_of_row, float2* __rest
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(256) void relayout_kernel(
     const Tin* __restrict__ x, const float2* __restrict__ cs, const int32_t* __restrict__ page_nrows,
-    Tout* __restrict__ out_n, Tout* __restrict__ out_t, int H, int D) {
+    const uint32_t* __restrict__ smax, Tout* __restrict__ out_n, Tout* __restrict__ out_t, int H, int D) {
   extern __shared__ float tile[];  // [64][D + 1]
   const int page = blockIdx.x / H, h = blockIdx.x % H;
   const int nrows = page_nrows[page];
   const int half = D / 2, ld = D + 1;
+  const float sc = smax ? pow2_scale(*smax) : 1.f;
   for (int idx = threadIdx.x; idx < 64 * half; idx += blockDim.x) {
     const int r = idx / half, i = idx % half;
     float a = 0.f, b = 0.f;
@@ -107,8 +124,8 @@ __global__ __launch_bounds__(256) void relayout_kernel(
         a = a2;
       }
     }
-    tile[r * ld + i] = a;
-    tile[r * ld + i + half] = b;
+    tile[r * ld + i] = a * sc;
+    tile[r * ld + i + half] = b * sc;
   }
   __syncthreads();
   const int64_t base = ((int64_t)page * H + h) * 64 * D;
@@ -129,7 +146,8 @@ __global__ __launch_bounds__(256) void relayout_kernel(
 template <typename T>
 __global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ dO,
                               const float* __restrict__ lse, const int32_t* __restrict__ page_nrows,
-                              float2* __restrict__ ldout, int64_t n_pages, int Hq, int D) {
+                              const uint32_t* __restrict__ dmax, float2* __restrict__ ldout, int64_t n_pages,
+                              int Hq, int D) {
   const int64_t idx = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;  // one wave per (row, h)
   const int lane = threadIdx.x % 64;
   if (idx >= n_pages * 64 * Hq) return;
@@ -144,23 +162,46 @@ __global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ dO,
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (lane == 0) {
     float2 v = make_float2(0.f, 0.f);
-    if (valid) v = make_float2(lse[row * Hq + h] * kLog2e, acc);
+    if (valid) v = make_float2(lse[row * Hq + h] * kLog2e, acc * (dmax ? pow2_scale(*dmax) : 1.f));
     ldout[(page * Hq + h) * 64 + r] = v;
   }
 }
 
+// max |x| over the valid rows of a [C][H][D] tensor, as float bits (an integer maximum is
+// exact and order-free, so the result does not depend on scheduling).  *out must be 0 first.
+__global__ void zero_u32_kernel(uint32_t* out) { *out = 0u; }
+
+template <typename T>
+__global__ __launch_bounds__(256) void maxabs_kernel(const T* __restrict__ x, const int32_t* __restrict__ page_nrows,
+                                                     int64_t n_pages, int64_t row_elems, uint32_t* __restrict__ out) {
+  __shared__ float red[4];
+  float m = 0.f;
+  const int64_t total = n_pages * 64;
+  for (int64_t row = blockIdx.x; row < total; row += gridDim.x) {
+    if ((int)(row % 64) >= page_nrows[row / 64]) continue;
+    for (int64_t i = threadIdx.x; i < row_elems; i += blockDim.x) m = fmaxf(m, fabsf(ld_f(x + row * row_elems + i)));
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const float b = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomicMax(out, __float_as_uint(b));
+  }
+}
+
 // ---------------------------------------------------------------------------
-// MFMA kernels: bf16, D = 128, four query heads per KV head
+// MFMA kernels: D = 128, four query heads per KV head, fp16 operands
 // ---------------------------------------------------------------------------
 
 constexpr int kD = 128;
-constexpr int kKStride = kD + 8;   // LDS row stride (bf16) of a [64][128] tile: +16 B against bank conflicts
-constexpr int kTStride = 64 + 8;   // LDS row stride (bf16) of a [128][64] tile
+constexpr int kKStride = kD + 8;   // LDS row stride (16-bit elements) of a [64][128] tile: +16 B against bank conflicts
+constexpr int kTStride = 64 + 8;   // LDS row stride (16-bit elements) of a [128][64] tile
 // dK/dV work-group LDS: the K and V tiles, later overlaid by the [64][129] fp32 head sum
 constexpr int kSmemDkdv = (2 * 64 * kKStride * 2 > 64 * (kD + 1) * 4) ? 2 * 64 * kKStride * 2 : 64 * (kD + 1) * 4;
 
-__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x16 mfma(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
@@ -168,26 +209,26 @@ __device__ __forceinline__ f32x16 zero16() {
   for (int i = 0; i < 16; ++i) z[i] = 0.f;
   return z;
 }
-__device__ __forceinline__ bf16x8 ld8(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-__device__ __forceinline__ bf16x8 pack8(const f32x16& s, int base) {
-  bf16x8 r;
+__device__ __forceinline__ f16x8 ld8(const f16_t* p) { return *reinterpret_cast<const f16x8*>(p); }
+__device__ __forceinline__ f16x8 pack8(const f32x16& s, int base) {
+  f16x8 r;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) r[e] = (__bf16)s[base + e];
+  for (int e = 0; e < 8; ++e) r[e] = (f16_t)s[base + e];
   return r;
 }
 // key (or row) index within a 32-block held by accumulator element r of a lane in half `hi`
 __device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
 
-// Copy a contiguous [64][128] bf16 tile into LDS with row stride kKStride.
-__device__ __forceinline__ void stage_rows(bf16_t* lds, const bf16_t* g, int64_t g_row_stride) {
+// Copy a contiguous [64][128] 16-bit tile into LDS with row stride kKStride.
+__device__ __forceinline__ void stage_rows(f16_t* lds, const f16_t* g, int64_t g_row_stride) {
   for (int c = threadIdx.x; c < 64 * 16; c += 256) {
     const int r = c >> 4, col = (c & 15) * 8;
     *reinterpret_cast<uint4*>(lds + r * kKStride + col) =
         *reinterpret_cast<const uint4*>(g + (int64_t)r * g_row_stride + col);
   }
 }
-// Copy a contiguous [128][64] bf16 tile into LDS with row stride kTStride.
-__device__ __forceinline__ void stage_cols(bf16_t* lds, const bf16_t* g) {
+// Copy a contiguous [128][64] 16-bit tile into LDS with row stride kTStride.
+__device__ __forceinline__ void stage_cols(f16_t* lds, const f16_t* g) {
   for (int c = threadIdx.x; c < 128 * 8; c += 256) {
     const int r = c >> 3, col = (c & 7) * 8;
     *reinterpret_cast<uint4*>(lds + r * kTStride + col) =
@@ -196,11 +237,11 @@ __device__ __forceinline__ void stage_cols(bf16_t* lds, const bf16_t* g) {
 }
 
 __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
-    const bf16_t* __restrict__ qn, const bf16_t* __restrict__ kn, const bf16_t* __restrict__ vt,
+    const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vt,
     const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
     bf16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, float sl2) {
-  __shared__ bf16_t lk[64 * kKStride];
-  __shared__ bf16_t lv[kD * kTStride];
+  __shared__ f16_t lk[64 * kKStride];
+  __shared__ f16_t lv[kD * kTStride];
   const int item = blockIdx.x;
   const QPage qp = qpages[order[item / Hkv]];
   const int g = item % Hkv;
@@ -208,8 +249,8 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
   const int l32 = lane & 31, hi = lane >> 5;
   const int h = g * 4 + wave;
 
-  bf16x8 qf[2][8];
-  const bf16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
+  f16x8 qf[2][8];
+  const f16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
@@ -238,12 +279,12 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
       s[mb][1] = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = ld8(lk + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
+        const f16x8 a = ld8(lk + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
         s[mb][0] = mfma(a, qf[0][ks], s[mb][0]);
         s[mb][1] = mfma(a, qf[1][ks], s[mb][1]);
       }
     }
-    bf16x8 pf[4][2];
+    f16x8 pf[4][2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int row = nb * 32 + l32;
@@ -286,7 +327,7 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
     for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 va = ld8(lv + (a * 32 + l32) * kTStride + ks * 16 + hi * 8);
+        const f16x8 va = ld8(lv + (a * 32 + l32) * kTStride + ks * 16 + hi * 8);
         oacc[a][0] = mfma(va, pf[ks][0], oacc[a][0]);
         oacc[a][1] = mfma(va, pf[ks][1], oacc[a][1]);
       }
@@ -317,13 +358,14 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
 // dQ for one query block (64 rows) x one KV head; waves = the four query heads.
 template <typename TG>
 __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
-    const bf16_t* __restrict__ qn, const bf16_t* __restrict__ kn, const bf16_t* __restrict__ kt,
-    const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO, const float2* __restrict__ ldd,
-    const float2* __restrict__ cs, const QPage* __restrict__ qpages, const int32_t* __restrict__ order,
-    const Tile* __restrict__ tiles, TG* __restrict__ dq, int Hq, int Hkv, float sl2, float scale) {
-  __shared__ bf16_t lk[64 * kKStride];
-  __shared__ bf16_t lvv[64 * kKStride];
-  __shared__ bf16_t lkt[kD * kTStride];
+    const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ kt,
+    const f16_t* __restrict__ vn, const f16_t* __restrict__ dOn, const float2* __restrict__ ldd,
+    const float2* __restrict__ cs, const uint32_t* __restrict__ dmax, const QPage* __restrict__ qpages,
+    const int32_t* __restrict__ order, const Tile* __restrict__ tiles, TG* __restrict__ dq, int Hq, int Hkv,
+    float sl2, float scale) {
+  __shared__ f16_t lk[64 * kKStride];
+  __shared__ f16_t lvv[64 * kKStride];
+  __shared__ f16_t lkt[kD * kTStride];
   const int item = blockIdx.x;
   const QPage qp = qpages[order[item / Hkv]];
   const int g = item % Hkv;
@@ -331,13 +373,14 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
   const int l32 = lane & 31, hi = lane >> 5;
   const int h = g * 4 + wave;
 
-  bf16x8 qf[2][8], df[2][8];
-  const bf16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
+  f16x8 qf[2][8], df[2][8];
+  const f16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
+  const f16_t* db = dOn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
   float lse2[2], Dv[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int row = nb * 32 + l32;
-    const bf16_t* drow = dO + (((int64_t)qp.phys * 64 + row) * Hq + h) * kD;
+    const f16_t* drow = db + row * kD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       qf[nb][ks] = ld8(qb + row * kD + ks * 16 + hi * 8);
@@ -359,7 +402,7 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
     const bool diag = (t == qp.tile_count - 1);
     __syncthreads();
     stage_rows(lk, kn + ((int64_t)tl.page * Hkv + g) * 64 * kD, kD);
-    stage_rows(lvv, v + ((int64_t)tl.page * 64 * Hkv + g) * kD, (int64_t)Hkv * kD);
+    stage_rows(lvv, vn + ((int64_t)tl.page * Hkv + g) * 64 * kD, kD);
     stage_cols(lkt, kt + ((int64_t)tl.page * Hkv + g) * kD * 64);
     __syncthreads();
 #pragma unroll
@@ -368,14 +411,14 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
       s[0] = s[1] = dp[0] = dp[1] = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const bf16x8 a = ld8(lk + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
-        const bf16x8 b = ld8(lvv + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
+        const f16x8 a = ld8(lk + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
+        const f16x8 b = ld8(lvv + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
         s[0] = mfma(a, qf[0][ks], s[0]);
         s[1] = mfma(a, qf[1][ks], s[1]);
         dp[0] = mfma(b, df[0][ks], dp[0]);
         dp[1] = mfma(b, df[1][ks], dp[1]);
       }
-      bf16x8 dsf[2][2];
+      f16x8 dsf[2][2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int row = nb * 32 + l32;
@@ -393,13 +436,14 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const bf16x8 ka = ld8(lkt + (a * 32 + l32) * kTStride + (mb * 2 + kk) * 16 + hi * 8);
+          const f16x8 ka = ld8(lkt + (a * 32 + l32) * kTStride + (mb * 2 + kk) * 16 + hi * 8);
           acc[a][0] = mfma(ka, dsf[kk][0], acc[a][0]);
           acc[a][1] = mfma(ka, dsf[kk][1], acc[a][1]);
         }
     }
   }
 
+  const float gscale = scale / pow2_scale(*dmax);  // undo the dO scaling
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int row = nb * 32 + l32;
@@ -413,7 +457,7 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int d = a * 32 + 8 * j + 4 * hi + i;  // d < 64 pairs with d + 64 (block a + 2)
-          const float g1 = acc[a][nb][4 * j + i] * scale, g2 = acc[a + 2][nb][4 * j + i] * scale;
+          const float g1 = acc[a][nb][4 * j + i] * gscale, g2 = acc[a + 2][nb][4 * j + i] * gscale;
           float r1 = 0.f, r2 = 0.f;
           if (valid) {
             const float2 c = cs ? cs[grow * (kD / 2) + d] : make_float2(1.f, 0.f);
@@ -431,16 +475,17 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
 // four are then summed through LDS in head order.
 template <typename TG>
 __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
-    const bf16_t* __restrict__ qn, const bf16_t* __restrict__ qt, const bf16_t* __restrict__ kn,
-    const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO, const bf16_t* __restrict__ dOt,
-    const float2* __restrict__ ldd, const float2* __restrict__ cs, const int32_t* __restrict__ order,
+    const f16_t* __restrict__ qn, const f16_t* __restrict__ qt, const f16_t* __restrict__ kn,
+    const f16_t* __restrict__ vn, const f16_t* __restrict__ dOn, const f16_t* __restrict__ dOt,
+    const float2* __restrict__ ldd, const float2* __restrict__ cs, const uint32_t* __restrict__ dmax,
+    const int32_t* __restrict__ order,
     const int32_t* __restrict__ kv_off, const KEntry* __restrict__ ents,
     const int32_t* __restrict__ page_table, const int32_t* __restrict__ page_nrows,
     TG* __restrict__ dk, TG* __restrict__ dv, int Hq, int Hkv, float sl2, float scale) {
   // K/V tiles during the walk; the same bytes hold the head reduction afterwards
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemDkdv];
-  bf16_t* lk = reinterpret_cast<bf16_t*>(smem);
-  bf16_t* lvv = lk + 64 * kKStride;
+  f16_t* lk = reinterpret_cast<f16_t*>(smem);
+  f16_t* lvv = lk + 64 * kKStride;
   float* red = reinterpret_cast<float*>(smem);
   const int item = blockIdx.x;
   const int page = order[item / Hkv];
@@ -451,7 +496,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
   const int krows = page_nrows[page];
 
   stage_rows(lk, kn + ((int64_t)page * Hkv + g) * 64 * kD, kD);
-  stage_rows(lvv, v + ((int64_t)page * 64 * Hkv + g) * kD, (int64_t)Hkv * kD);
+  stage_rows(lvv, vn + ((int64_t)page * Hkv + g) * 64 * kD, kD);
   __syncthreads();
 
   f32x16 adk[2][4], adv[2][4];  // [key block][d block]
@@ -467,9 +512,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
     for (int lq = ent.lq0; lq < ent.lq1; ++lq) {
       const int qph = page_table[ent.slot_base + lq];
       const int nrows = page_nrows[qph];
-      const bf16_t* qb = qn + ((int64_t)qph * Hq + h) * 64 * kD;
-      const bf16_t* qtb = qt + ((int64_t)qph * Hq + h) * kD * 64;
-      const bf16_t* dtb = dOt + ((int64_t)qph * Hq + h) * kD * 64;
+      const f16_t* qb = qn + ((int64_t)qph * Hq + h) * 64 * kD;
+      const f16_t* qtb = qt + ((int64_t)qph * Hq + h) * kD * 64;
+      const f16_t* dnb = dOn + ((int64_t)qph * Hq + h) * 64 * kD;
+      const f16_t* dtb = dOt + ((int64_t)qph * Hq + h) * kD * 64;
       const float2* ldb = ldd + ((int64_t)qph * Hq + h) * 64;
       for (int rb = 0; rb < 2; ++rb) {
         if (rb * 32 >= nrows) break;
@@ -477,21 +523,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
         f32x16 s[2], dp[2];
         s[0] = s[1] = dp[0] = dp[1] = zero16();
         const int arow = rb * 32 + l32;
-        const bf16_t* drow = dO + (((int64_t)qph * 64 + arow) * Hq + h) * kD;
+        const f16_t* drow = dnb + arow * kD;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-          const bf16x8 qa = ld8(qb + arow * kD + ks * 16 + hi * 8);
-          const bf16x8 da = ld8(drow + ks * 16 + hi * 8);
+          const f16x8 qa = ld8(qb + arow * kD + ks * 16 + hi * 8);
+          const f16x8 da = ld8(drow + ks * 16 + hi * 8);
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb) {
-            const bf16x8 kb = ld8(lk + (nb * 32 + l32) * kKStride + ks * 16 + hi * 8);
-            const bf16x8 vb = ld8(lvv + (nb * 32 + l32) * kKStride + ks * 16 + hi * 8);
+            const f16x8 kb = ld8(lk + (nb * 32 + l32) * kKStride + ks * 16 + hi * 8);
+            const f16x8 vb = ld8(lvv + (nb * 32 + l32) * kKStride + ks * 16 + hi * 8);
             s[nb] = mfma(qa, kb, s[nb]);
             dp[nb] = mfma(da, vb, dp[nb]);
           }
         }
         // P and dS; this lane holds key nb*32 + l32 and rows rb*32 + acc_row(r, hi)
-        bf16x8 pf[2][2], sf[2][2];  // [k-step of 16 rows][key block]
+        f16x8 pf[2][2], sf[2][2];  // [k-step of 16 rows][key block]
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int r0 = rb * 32 + 8 * j + 4 * hi;
@@ -524,8 +570,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
           const int col = (rb * 2 + kk) * 16 + hi * 8;
 #pragma unroll
           for (int b = 0; b < 4; ++b) {
-            const bf16x8 dob = ld8(dtb + (b * 32 + l32) * 64 + col);
-            const bf16x8 qbt = ld8(qtb + (b * 32 + l32) * 64 + col);
+            const f16x8 dob = ld8(dtb + (b * 32 + l32) * 64 + col);
+            const f16x8 qbt = ld8(qtb + (b * 32 + l32) * 64 + col);
 #pragma unroll
             for (int nb = 0; nb < 2; ++nb) {
               adv[nb][b] = mfma(pf[kk][nb], dob, adv[nb][b]);
@@ -537,6 +583,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
     }
   }
 
+  const float inv_sdo = 1.f / pow2_scale(*dmax);  // undo the dO scaling
   // sum the four heads in order 0..3 through LDS, then write dk (un-rotated) and dv
   for (int which = 0; which < 2; ++which) {
     for (int w = 0; w < 4; ++w) {
@@ -561,6 +608,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
       const int key = idx / 64, i = idx % 64;
       const int64_t grow = (int64_t)page * 64 + key;
       float a = red[key * (kD + 1) + i], b = red[key * (kD + 1) + i + 64];
+      a *= inv_sdo;
+      b *= inv_sdo;
       if (key >= krows) {
         a = b = 0.f;
       } else if (which == 0) {
@@ -761,24 +810,36 @@ void launch_cs(const LaunchShape& s, const int32_t* pos_of_row, float2* cs, hipS
 
 template <typename Tin, typename Tout>
 void launch_relayout(const LaunchShape& s, const Tin* x, const float2* cs, const int32_t* page_nrows,
-                     Tout* out_n, Tout* out_t, int H, hipStream_t st) {
+                     const uint32_t* smax, Tout* out_n, Tout* out_t, int H, hipStream_t st) {
   const size_t lds = (size_t)64 * (s.D + 1) * sizeof(float);
-  relayout_kernel<Tin, Tout><<<(unsigned)(s.pages * H), 256, lds, st>>>(x, cs, page_nrows, out_n, out_t, H, s.D);
+  relayout_kernel<Tin, Tout><<<(unsigned)(s.pages * H), 256, lds, st>>>(x, cs, page_nrows, smax, out_n, out_t, H,
+                                                                         s.D);
 }
 
 template <typename T>
-void launch_rowdot(const LaunchShape& s, const T* o, const T* dO, const float* lse,
-                   const int32_t* page_nrows, float2* ld, hipStream_t st) {
-  rowdot_kernel<T><<<blocks_for(s.pages * 64 * s.Hq, 4), 256, 0, st>>>(o, dO, lse, page_nrows, ld, s.pages, s.Hq, s.D);
+void launch_rowdot(const LaunchShape& s, const T* o, const T* dO, const float* lse, const int32_t* page_nrows,
+                   const uint32_t* dmax, float2* ld, hipStream_t st) {
+  rowdot_kernel<T><<<blocks_for(s.pages * 64 * s.Hq, 4), 256, 0, st>>>(o, dO, lse, page_nrows, dmax, ld, s.pages,
+                                                                       s.Hq, s.D);
 }
 
-template void launch_relayout<bf16_t, bf16_t>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, bf16_t*, bf16_t*, int, hipStream_t);
-template void launch_relayout<bf16_t, float>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, float*, float*, int, hipStream_t);
-template void launch_relayout<float, float>(const LaunchShape&, const float*, const float2*, const int32_t*, float*, float*, int, hipStream_t);
-template void launch_rowdot<bf16_t>(const LaunchShape&, const bf16_t*, const bf16_t*, const float*, const int32_t*, float2*, hipStream_t);
-template void launch_rowdot<float>(const LaunchShape&, const float*, const float*, const float*, const int32_t*, float2*, hipStream_t);
+template <typename T>
+void launch_maxabs(const LaunchShape& s, const T* x, int H, const int32_t* page_nrows, uint32_t* out,
+                   hipStream_t st) {
+  zero_u32_kernel<<<1, 1, 0, st>>>(out);
+  const int64_t rows = s.pages * 64;
+  const unsigned grid = (unsigned)(rows < 4096 ? (rows > 0 ? rows : 1) : 4096);
+  maxabs_kernel<T><<<grid, 256, 0, st>>>(x, page_nrows, s.pages, (int64_t)H * s.D, out);
+}
 
-void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const bf16_t* kn, const bf16_t* vt,
+template void launch_relayout<bf16_t, f16_t>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, const uint32_t*, f16_t*, f16_t*, int, hipStream_t);
+template void launch_relayout<bf16_t, float>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, const uint32_t*, float*, float*, int, hipStream_t);
+template void launch_relayout<float, float>(const LaunchShape&, const float*, const float2*, const int32_t*, const uint32_t*, float*, float*, int, hipStream_t);
+template void launch_rowdot<bf16_t>(const LaunchShape&, const bf16_t*, const bf16_t*, const float*, const int32_t*, const uint32_t*, float2*, hipStream_t);
+template void launch_rowdot<float>(const LaunchShape&, const float*, const float*, const float*, const int32_t*, const uint32_t*, float2*, hipStream_t);
+template void launch_maxabs<bf16_t>(const LaunchShape&, const bf16_t*, int, const int32_t*, uint32_t*, hipStream_t);
+
+void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vt,
                      const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
                      hipStream_t st) {
   fwd_mfma_kernel<<<(unsigned)(n_qp * s.Hkv), 256, 0, st>>>(qn, kn, vt, qpages, order, tiles, o, lse, s.Hq,
@@ -786,27 +847,33 @@ void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const
 }
 
 template <typename TG>
-void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const bf16_t* kn, const bf16_t* kt,
-                    const bf16_t* v, const bf16_t* dO, const float2* ld, const float2* cs, const QPage* qpages,
-                    const int32_t* order, const Tile* tiles, TG* dq, hipStream_t st) {
-  dq_mfma_kernel<TG><<<(unsigned)(n_qp * s.Hkv), 256, 0, st>>>(qn, kn, kt, v, dO, ld, cs, qpages, order, tiles, dq,
-                                                               s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
+void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* kt,
+                    const f16_t* vn, const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
+                    const QPage* qpages, const int32_t* order, const Tile* tiles, TG* dq, hipStream_t st) {
+  dq_mfma_kernel<TG><<<(unsigned)(n_qp * s.Hkv), 256, 0, st>>>(qn, kn, kt, vn, dOn, ld, cs, dmax, qpages, order,
+                                                               tiles, dq, s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
 }
 
 template <typename TG>
-void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const bf16_t* qn, const bf16_t* qt, const bf16_t* kn,
-                      const bf16_t* v, const bf16_t* dO, const bf16_t* dOt, const float2* ld, const float2* cs,
-                      const int32_t* order, const int32_t* kv_off, const KEntry* ents, const int32_t* page_table,
-                      const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st) {
-  dkdv_mfma_kernel<TG><<<(unsigned)(n_kvp * s.Hkv), 256, 0, st>>>(qn, qt, kn, v, dO, dOt, ld, cs, order, kv_off,
-                                                                  ents, page_table, page_nrows, dk, dv, s.Hq, s.Hkv,
-                                                                  s.scale * kLog2e, s.scale);
+void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, const f16_t* qt, const f16_t* kn,
+                      const f16_t* vn, const f16_t* dOn, const f16_t* dOt, const float2* ld, const float2* cs,
+                      const uint32_t* dmax, const int32_t* order, const int32_t* kv_off, const KEntry* ents,
+                      const int32_t* page_table, const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st) {
+  dkdv_mfma_kernel<TG><<<(unsigned)(n_kvp * s.Hkv), 256, 0, st>>>(qn, qt, kn, vn, dOn, dOt, ld, cs, dmax, order,
+                                                                  kv_off, ents, page_table, page_nrows, dk, dv,
+                                                                  s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
 }
 
-template void launch_dq_mfma<bf16_t>(const LaunchShape&, int64_t, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const float2*, const float2*, const QPage*, const int32_t*, const Tile*, bf16_t*, hipStream_t);
-template void launch_dq_mfma<float>(const LaunchShape&, int64_t, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const float2*, const float2*, const QPage*, const int32_t*, const Tile*, float*, hipStream_t);
-template void launch_dkdv_mfma<bf16_t>(const LaunchShape&, int64_t, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const float2*, const float2*, const int32_t*, const int32_t*, const KEntry*, const int32_t*, const int32_t*, bf16_t*, bf16_t*, hipStream_t);
-template void launch_dkdv_mfma<float>(const LaunchShape&, int64_t, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const bf16_t*, const float2*, const float2*, const int32_t*, const int32_t*, const KEntry*, const int32_t*, const int32_t*, float*, float*, hipStream_t);
+#define INST_MFMA_BWD(TG)                                                                                      \
+  template void launch_dq_mfma<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,      \
+                                   const f16_t*, const f16_t*, const float2*, const float2*, const uint32_t*,  \
+                                   const QPage*, const int32_t*, const Tile*, TG*, hipStream_t);               \
+  template void launch_dkdv_mfma<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,    \
+                                     const f16_t*, const f16_t*, const f16_t*, const float2*, const float2*,   \
+                                     const uint32_t*, const int32_t*, const int32_t*, const KEntry*,           \
+                                     const int32_t*, const int32_t*, TG*, TG*, hipStream_t);
+INST_MFMA_BWD(bf16_t)
+INST_MFMA_BWD(float)
 
 template <typename T>
 void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,

@@ -7,7 +7,8 @@
 
 namespace dagattn {
 
-typedef uint16_t bf16_t;
+typedef uint16_t bf16_t;  // bf16 bits
+typedef _Float16 f16_t;
 
 struct LaunchShape {
   int64_t C, pages;
@@ -19,22 +20,25 @@ struct LaunchShape {
 void launch_cs(const LaunchShape& s, const int32_t* pos_of_row, float2* cs, hipStream_t st);
 template <typename Tin, typename Tout>
 void launch_relayout(const LaunchShape& s, const Tin* x, const float2* cs, const int32_t* page_nrows,
-                     Tout* out_n, Tout* out_t, int H, hipStream_t st);
+                     const uint32_t* smax, Tout* out_n, Tout* out_t, int H, hipStream_t st);
 template <typename T>
-void launch_rowdot(const LaunchShape& s, const T* o, const T* dO, const float* lse,
-                   const int32_t* page_nrows, float2* ld, hipStream_t st);
-void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const bf16_t* kn, const bf16_t* vt,
+void launch_rowdot(const LaunchShape& s, const T* o, const T* dO, const float* lse, const int32_t* page_nrows,
+                   const uint32_t* dmax, float2* ld, hipStream_t st);
+template <typename T>
+void launch_maxabs(const LaunchShape& s, const T* x, int H, const int32_t* page_nrows, uint32_t* out,
+                   hipStream_t st);
+void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vt,
                      const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
                      hipStream_t st);
 template <typename TG>
-void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const bf16_t* qn, const bf16_t* kn, const bf16_t* kt,
-                    const bf16_t* v, const bf16_t* dO, const float2* ld, const float2* cs, const QPage* qpages,
-                    const int32_t* order, const Tile* tiles, TG* dq, hipStream_t st);
+void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* kt,
+                    const f16_t* vn, const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
+                    const QPage* qpages, const int32_t* order, const Tile* tiles, TG* dq, hipStream_t st);
 template <typename TG>
-void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const bf16_t* qn, const bf16_t* qt, const bf16_t* kn,
-                      const bf16_t* v, const bf16_t* dO, const bf16_t* dOt, const float2* ld, const float2* cs,
-                      const int32_t* order, const int32_t* kv_off, const KEntry* ents, const int32_t* page_table,
-                      const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st);
+void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, const f16_t* qt, const f16_t* kn,
+                      const f16_t* vn, const f16_t* dOn, const f16_t* dOt, const float2* ld, const float2* cs,
+                      const uint32_t* dmax, const int32_t* order, const int32_t* kv_off, const KEntry* ents,
+                      const int32_t* page_table, const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st);
 template <typename T>
 void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,
                        const QPage* qpages, const int32_t* order, const Tile* tiles, T* o, float* lse,

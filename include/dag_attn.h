@@ -144,8 +144,11 @@ typedef struct {
   int32_t n_q_heads;   /* Hq                                                            */
   int32_t n_kv_heads;  /* Hkv; Hq % Hkv == 0, query head h reads KV head h / (Hq / Hkv) */
   int32_t head_dim;    /* even, 2..128                                                  */
-  int32_t dtype;       /* DAG_DTYPE_BF16: bf16 tensors, fp32 accumulation (MFMA when     */
-                       /* head_dim == 128 and Hq == 4 Hkv); DAG_DTYPE_FP32: fp32 throughout */
+  int32_t dtype;       /* DAG_DTYPE_BF16: bf16 tensors, fp32 accumulation.  When           */
+                       /* head_dim == 128 and Hq == 4 Hkv the products run on MFMA with     */
+                       /* fp16 operands (bf16 -> fp16 is exact for 2^-14 <= |x| < 2^15; dO  */
+                       /* is first scaled by a power of two so its largest |x| is in [1,2)) */
+                       /* DAG_DTYPE_FP32: fp32 throughout                                   */
   int32_t grad_dtype;  /* element type of dq, dk, dv: DAG_DTYPE_BF16 or DAG_DTYPE_FP32;    */
                        /* must be FP32 when dtype is FP32.  Large shared-row gradients     */
                        /* keep their precision in FP32                                      */

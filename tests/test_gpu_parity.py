@@ -8,7 +8,8 @@ by one, plus properties that hold at any size.  Padding rows of every input
 are filled with NaN to show that they are ignored.
 
 Tolerances: bf16 inputs, max-abs <= 2e-2 and mean-abs <= 2e-3 per tensor;
-fp32 mode, max-abs <= 1e-5.
+fp32 mode, max-abs <= 1e-5 on the tiny workload, and 1e-5 * max(1, max|ref|)
+on larger DAGs, whose shared rows sum many fp32 terms (|dV| reaches ~11).
 """
 import numpy as np
 import pytest
@@ -70,14 +71,15 @@ def _ref(spec, q, k, v, do, hq, hkv, rope=10000.0, transitive=True, brute=False,
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 
-def _assert_close(got, ref, dtype, names=("o", "lse", "dq", "dk", "dv"), tag=""):
+def _assert_close(got, ref, dtype, names=("o", "lse", "dq", "dk", "dv"), tag="", fp32_relative=False):
     for n in names:
         if n not in got:
             continue
         err = np.abs(got[n] - ref[n])
         assert np.isfinite(got[n]).all(), f"{tag} {n}: non-finite"
         if dtype == "fp32":
-            assert err.max() <= FP32_MAX, f"{tag} {n}: max {err.max():.3g}"
+            bar = FP32_MAX * (max(1.0, float(np.abs(ref[n]).max())) if fp32_relative else 1.0)
+            assert err.max() <= bar, f"{tag} {n}: max {err.max():.3g} > {bar:.3g}"
         else:
             assert err.max() <= BF16_MAX and err.mean() <= BF16_MEAN, \
                 f"{tag} {n}: max {err.max():.3g} mean {err.mean():.3g}"
@@ -163,7 +165,7 @@ def test_small_generic_path(dpa, name, shape):
     q, k, v, do = _inputs(spec, hq, hkv, d, 31, dt)
     got, _ = _run(dpa, spec, q, k, v, do, hq, hkv, d, dt, transitive=tr)
     ref = _ref(spec, q, k, v, do, hq, hkv, transitive=tr)
-    _assert_close(got, ref, dt, tag=f"{name}{shape}")
+    _assert_close(got, ref, dt, tag=f"{name}{shape}", fp32_relative=(name != "tiny"))
 
 
 def test_bf16_gradients_are_rounded_fp32_gradients(dpa):
