@@ -49,10 +49,10 @@ def gen(shape, seed, stream, dev):
 
 
 def run_steps(dpa, plan, p, tensors, ws, n):
-    q, k, v, o, lse, do, dq, dk, dv = tensors
+    q, k, v, o, lse, o_lo, do, dq, dk, dv = tensors
     for _ in range(n):
-        dpa.attn_fwd(plan, p, q, k, v, o=o, lse=lse, ws=ws)
-        dpa.attn_bwd(plan, p, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, ws=ws)
+        dpa.attn_fwd(plan, p, q, k, v, o=o, lse=lse, ws=ws, o_lo=o_lo)
+        dpa.attn_bwd(plan, p, q, k, v, o, lse, do, dq=dq, dk=dk, dv=dv, ws=ws, o_lo=o_lo)
 
 
 def alloc(dpa, plan, p, seed, dev):
@@ -60,12 +60,12 @@ def alloc(dpa, plan, p, seed, dev):
     C = plan.rows
     q, k, v = gen((C, HQ, D), seed, 1, dev), gen((C, HKV, D), seed, 2, dev), gen((C, HKV, D), seed, 3, dev)
     do = gen((C, HQ, D), seed, 4, dev)
-    o, dq = torch.empty_like(q), torch.empty_like(q)
+    o, o_lo, dq = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     lse = torch.empty((C, HQ), dtype=torch.float32, device=dev)
     dk, dv = torch.empty_like(k), torch.empty_like(v)
     fw, bw = dpa.workspace_bytes(plan, p)
     ws = torch.empty(max(fw, bw), dtype=torch.uint8, device=dev)
-    return (q, k, v, o, lse, do, dq, dk, dv), ws
+    return (q, k, v, o, lse, o_lo, do, dq, dk, dv), ws
 
 
 def flat_time(dpa, spec, plan, p, dev, steps, max_rows=3_000_000):

@@ -79,8 +79,8 @@ def _load() -> ctypes.CDLL:
         "dag_plan_upload": ([P, P], I32),
         "dag_attn_workspace": ([P, ctypes.POINTER(DagAttnParams), ctypes.POINTER(SZ),
                                 ctypes.POINTER(SZ)], I32),
-        "dag_attn_fwd": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, SZ, P], I32),
-        "dag_attn_bwd": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "dag_attn_fwd": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, P, SZ, P], I32),
+        "dag_attn_bwd": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
         "dag_attn_timing_enable": ([P, I32, I32], I32),
         "dag_attn_timing_read": ([P, P, P], I32),
         "dag_last_error": ([], ctypes.c_char_p),
@@ -241,8 +241,12 @@ def _check_tensor(name, t, rows, heads, d, dtype, device):
                          f"got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
-def attn_fwd(plan: Plan, p: AttnParams, q, k, v, o=None, lse=None, ws=None, stream=None):
-    """``dag_attn_fwd``: q [C,Hq,D], k/v [C,Hkv,D] in row layout -> (o [C,Hq,D], lse [C,Hq] fp32)."""
+def attn_fwd(plan: Plan, p: AttnParams, q, k, v, o=None, lse=None, ws=None, stream=None, o_lo=None):
+    """``dag_attn_fwd``: q [C,Hq,D], k/v [C,Hkv,D] in row layout -> (o [C,Hq,D], lse [C,Hq] fp32).
+
+    For bf16, ``o_lo=True`` (or a tensor) also returns O's rounding residual, which
+    :func:`attn_bwd` takes to form rowsum(dO * O) precisely; the result is then
+    (o, lse, o_lo)."""
     import torch
     C, dt, dev = plan.rows, p.torch_dtype, q.device
     _check_tensor("q", q, C, p.n_q_heads, p.head_dim, dt, dev)
@@ -255,14 +259,18 @@ def attn_fwd(plan: Plan, p: AttnParams, q, k, v, o=None, lse=None, ws=None, stre
     need, _ = workspace_bytes(plan, p)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    want_lo = o_lo is not None and o_lo is not False
+    if o_lo is True:
+        o_lo = torch.empty_like(q)
+    lo_ptr = _ptr(o_lo) if want_lo else None
     cp = p.c()
-    _check(_lib.dag_attn_fwd(plan._h, ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+    _check(_lib.dag_attn_fwd(plan._h, ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), lo_ptr,
                              _ptr(ws), ws.numel(), _stream_ptr(stream)))
-    return o, lse
+    return (o, lse, o_lo) if want_lo else (o, lse)
 
 
 def attn_bwd(plan: Plan, p: AttnParams, q, k, v, o, lse, dO, dq=None, dk=None, dv=None, ws=None,
-             stream=None):
+             stream=None, o_lo=None):
     """``dag_attn_bwd``: returns (dq [C,Hq,D], dk [C,Hkv,D], dv [C,Hkv,D])."""
     import torch
     C, dt, dev = plan.rows, p.torch_dtype, q.device
@@ -283,8 +291,8 @@ def attn_bwd(plan: Plan, p: AttnParams, q, k, v, o, lse, dO, dq=None, dk=None, d
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     cp = p.c()
     _check(_lib.dag_attn_bwd(plan._h, ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                             _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
-                             _stream_ptr(stream)))
+                             _ptr(o_lo) if o_lo is not None else None, _ptr(dO), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(ws), ws.numel(), _stream_ptr(stream)))
     return dq, dk, dv
 
 

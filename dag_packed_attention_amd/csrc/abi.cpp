@@ -384,13 +384,14 @@ dag_status dag_attn_workspace(const dag_plan* plan, const dag_attn_params* p, si
 }
 
 dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k, const void* v,
-                        void* o, float* lse, void* ws, size_t ws_bytes, void* hip_stream) {
+                        void* o, float* lse, void* o_lo, void* ws, size_t ws_bytes, void* hip_stream) {
   if (!plan) return set_err(DAG_E_INVALID, "null plan");
   dag_status st = check_params(p);
   if (st != DAG_OK) return st;
   Plan& P = plan->p;
   if (P.info.rows == 0) return DAG_OK;
   if (!q || !k || !v || !o || !lse) return set_err(DAG_E_INVALID, "null tensor pointer");
+  if (o_lo && p->dtype != DAG_DTYPE_BF16) return set_err(DAG_E_INVALID, "o_lo is for bf16 tensors only");
   const LaunchShape s = shape_of(P, p);
   const bool mfma = mfma_path(p);
   FwdWs w;
@@ -422,20 +423,20 @@ dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q,
     Span sp(P, DAG_K_FWD, stream);
     if (mfma)
       launch_fwd_mfma(s, n_qp, (const f16_t*)w.qn, (const f16_t*)w.kn, (const f16_t*)w.vt, D.qpages, D.fwd_order,
-                      D.tiles, (bf16_t*)o, lse, stream);
+                      D.tiles, (bf16_t*)o, lse, (bf16_t*)o_lo, stream);
     else if (p->dtype == DAG_DTYPE_BF16)
       launch_fwd_simple<bf16_t>(s, n_qp, (const float*)w.qn, (const float*)w.kn, (const bf16_t*)v, D.qpages,
-                                D.fwd_order, D.tiles, (bf16_t*)o, lse, stream);
+                                D.fwd_order, D.tiles, (bf16_t*)o, lse, (bf16_t*)o_lo, stream);
     else
       launch_fwd_simple<float>(s, n_qp, (const float*)w.qn, (const float*)w.kn, (const float*)v, D.qpages,
-                               D.fwd_order, D.tiles, (float*)o, lse, stream);
+                               D.fwd_order, D.tiles, (float*)o, lse, nullptr, stream);
   }
   return launched("dag_attn_fwd");
 }
 
 dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k, const void* v,
-                        const void* o, const float* lse, const void* dO, void* dq, void* dk, void* dv, void* ws,
-                        size_t ws_bytes, void* hip_stream) {
+                        const void* o, const float* lse, const void* o_lo, const void* dO, void* dq, void* dk,
+                        void* dv, void* ws, size_t ws_bytes, void* hip_stream) {
   if (!plan) return set_err(DAG_E_INVALID, "null plan");
   dag_status st = check_params(p);
   if (st != DAG_OK) return st;
@@ -443,6 +444,7 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
   if (P.info.rows == 0) return DAG_OK;
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv)
     return set_err(DAG_E_INVALID, "null tensor pointer");
+  if (o_lo && p->dtype != DAG_DTYPE_BF16) return set_err(DAG_E_INVALID, "o_lo is for bf16 tensors only");
   const LaunchShape s = shape_of(P, p);
   const bool mfma = mfma_path(p);
   BwdWs w;
@@ -462,7 +464,7 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
       if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
       launch_maxabs<bf16_t>(s, d16, s.Hq, nr, w.dmax, stream);
-      launch_rowdot<bf16_t>(s, o16, d16, lse, nr, w.dmax, w.ld, stream);
+      launch_rowdot<bf16_t>(s, o16, (const bf16_t*)o_lo, d16, lse, nr, w.dmax, w.ld, stream);
       launch_relayout<bf16_t, f16_t>(s, q16, w.cs, nr, nullptr, (f16_t*)w.qn, (f16_t*)w.qt, s.Hq, stream);
       launch_relayout<bf16_t, f16_t>(s, k16, w.cs, nr, nullptr, (f16_t*)w.kn, (f16_t*)w.kt, s.Hkv, stream);
       launch_relayout<bf16_t, f16_t>(s, v16, nullptr, nr, nullptr, (f16_t*)w.vn, nullptr, s.Hkv, stream);
@@ -492,7 +494,8 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
     {
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
       if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
-      launch_rowdot<bf16_t>(s, (const bf16_t*)o, (const bf16_t*)dO, lse, D.page_nrows, nullptr, w.ld, stream);
+      launch_rowdot<bf16_t>(s, (const bf16_t*)o, (const bf16_t*)o_lo, (const bf16_t*)dO, lse, D.page_nrows, nullptr,
+                            w.ld, stream);
       launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, D.page_nrows, nullptr, (float*)w.qn, nullptr, s.Hq,
                                      stream);
       launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, D.page_nrows, nullptr, (float*)w.kn, nullptr, s.Hkv,
@@ -513,7 +516,7 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
     {
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
       if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
-      launch_rowdot<float>(s, (const float*)o, (const float*)dO, lse, D.page_nrows, nullptr, w.ld, stream);
+      launch_rowdot<float>(s, (const float*)o, nullptr, (const float*)dO, lse, D.page_nrows, nullptr, w.ld, stream);
       launch_relayout<float, float>(s, (const float*)q, w.cs, D.page_nrows, nullptr, (float*)w.qn, nullptr, s.Hq,
                                     stream);
       launch_relayout<float, float>(s, (const float*)k, w.cs, D.page_nrows, nullptr, (float*)w.kn, nullptr, s.Hkv,

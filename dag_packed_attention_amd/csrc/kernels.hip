@@ -144,7 +144,7 @@ __global__ __launch_bounds__(256) void relayout_kernel(
 
 // ld[page][h][r] = (lse * log2 e, sum_d dO * O) for the backward; zero on padding rows.
 template <typename T>
-__global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ dO,
+__global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ o_lo, const T* __restrict__ dO,
                               const float* __restrict__ lse, const int32_t* __restrict__ page_nrows,
                               const uint32_t* __restrict__ dmax, float2* __restrict__ ldout, int64_t n_pages,
                               int Hq, int D) {
@@ -158,7 +158,11 @@ __global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ dO,
   float acc = 0.f;
   const bool valid = r < page_nrows[page];
   if (valid)
-    for (int d = lane; d < D; d += 64) acc += ld_f(o + (row * Hq + h) * D + d) * ld_f(dO + (row * Hq + h) * D + d);
+    for (int d = lane; d < D; d += 64) {
+      const int64_t e = (row * Hq + h) * D + d;
+      const float ov = o_lo ? ld_f(o + e) + ld_f(o_lo + e) : ld_f(o + e);
+      acc += ov * ld_f(dO + e);
+    }
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (lane == 0) {
     float2 v = make_float2(0.f, 0.f);
@@ -239,7 +243,7 @@ __device__ __forceinline__ void stage_cols(f16_t* lds, const f16_t* g) {
 __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vt,
     const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
-    bf16_t* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, float sl2) {
+    bf16_t* __restrict__ o, float* __restrict__ lse, bf16_t* __restrict__ o_lo, int Hq, int Hkv, float sl2) {
   __shared__ f16_t lk[64 * kKStride];
   __shared__ f16_t lv[kD * kTStride];
   const int item = blockIdx.x;
@@ -346,10 +350,22 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = a * 32 + 8 * j + 4 * hi;
+        bf16_t hv[4], lv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = oacc[a][nb][4 * j + i] * inv;
+          hv[i] = f2bf(x);
+          lv[i] = f2bf(x - bf2f(hv[i]));
+        }
         uint2 w;
-        w.x = (uint32_t)f2bf(oacc[a][nb][4 * j] * inv) | ((uint32_t)f2bf(oacc[a][nb][4 * j + 1] * inv) << 16);
-        w.y = (uint32_t)f2bf(oacc[a][nb][4 * j + 2] * inv) | ((uint32_t)f2bf(oacc[a][nb][4 * j + 3] * inv) << 16);
+        w.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+        w.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
         *reinterpret_cast<uint2*>(orow + d) = w;
+        if (o_lo) {
+          w.x = (uint32_t)lv[0] | ((uint32_t)lv[1] << 16);
+          w.y = (uint32_t)lv[2] | ((uint32_t)lv[3] << 16);
+          *reinterpret_cast<uint2*>(o_lo + (grow * Hq + h) * kD + d) = w;
+        }
       }
     if (hi == 0) lse[grow * Hq + h] = valid ? (mrow[nb] + __log2f(l)) * kLn2 : 0.f;
   }
@@ -640,7 +656,7 @@ template <typename T>
 __global__ __launch_bounds__(64) void fwd_simple_kernel(
     const float* __restrict__ qn, const float* __restrict__ kn, const T* __restrict__ v,
     const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
-    T* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int D, float scale) {
+    T* __restrict__ o, float* __restrict__ lse, T* __restrict__ o_lo, int Hq, int Hkv, int D, float scale) {
   const int item = blockIdx.x;
   const QPage qp = qpages[order[item / Hq]];
   const int h = item % Hq, g = h / (Hq / Hkv);
@@ -672,7 +688,11 @@ __global__ __launch_bounds__(64) void fwd_simple_kernel(
   }
   const bool valid = row < qp.nrows;
   const int64_t grow = (int64_t)qp.phys * 64 + row;
-  for (int d = 0; d < D; ++d) st_f(o + (grow * Hq + h) * D + d, valid ? acc[d] / l : 0.f);
+  for (int d = 0; d < D; ++d) {
+    const float x = valid ? acc[d] / l : 0.f;
+    st_f(o + (grow * Hq + h) * D + d, x);
+    if (o_lo) st_f(o_lo + (grow * Hq + h) * D + d, x - ld_f(o + (grow * Hq + h) * D + d));
+  }
   lse[grow * Hq + h] = valid ? m + logf(l) : 0.f;
 }
 
@@ -817,10 +837,10 @@ void launch_relayout(const LaunchShape& s, const Tin* x, const float2* cs, const
 }
 
 template <typename T>
-void launch_rowdot(const LaunchShape& s, const T* o, const T* dO, const float* lse, const int32_t* page_nrows,
-                   const uint32_t* dmax, float2* ld, hipStream_t st) {
-  rowdot_kernel<T><<<blocks_for(s.pages * 64 * s.Hq, 4), 256, 0, st>>>(o, dO, lse, page_nrows, dmax, ld, s.pages,
-                                                                       s.Hq, s.D);
+void launch_rowdot(const LaunchShape& s, const T* o, const T* o_lo, const T* dO, const float* lse,
+                   const int32_t* page_nrows, const uint32_t* dmax, float2* ld, hipStream_t st) {
+  rowdot_kernel<T><<<blocks_for(s.pages * 64 * s.Hq, 4), 256, 0, st>>>(o, o_lo, dO, lse, page_nrows, dmax, ld,
+                                                                       s.pages, s.Hq, s.D);
 }
 
 template <typename T>
@@ -835,14 +855,14 @@ void launch_maxabs(const LaunchShape& s, const T* x, int H, const int32_t* page_
 template void launch_relayout<bf16_t, f16_t>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, const uint32_t*, f16_t*, f16_t*, int, hipStream_t);
 template void launch_relayout<bf16_t, float>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, const uint32_t*, float*, float*, int, hipStream_t);
 template void launch_relayout<float, float>(const LaunchShape&, const float*, const float2*, const int32_t*, const uint32_t*, float*, float*, int, hipStream_t);
-template void launch_rowdot<bf16_t>(const LaunchShape&, const bf16_t*, const bf16_t*, const float*, const int32_t*, const uint32_t*, float2*, hipStream_t);
-template void launch_rowdot<float>(const LaunchShape&, const float*, const float*, const float*, const int32_t*, const uint32_t*, float2*, hipStream_t);
+template void launch_rowdot<bf16_t>(const LaunchShape&, const bf16_t*, const bf16_t*, const bf16_t*, const float*, const int32_t*, const uint32_t*, float2*, hipStream_t);
+template void launch_rowdot<float>(const LaunchShape&, const float*, const float*, const float*, const float*, const int32_t*, const uint32_t*, float2*, hipStream_t);
 template void launch_maxabs<bf16_t>(const LaunchShape&, const bf16_t*, int, const int32_t*, uint32_t*, hipStream_t);
 
 void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vt,
                      const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
-                     hipStream_t st) {
-  fwd_mfma_kernel<<<(unsigned)(n_qp * s.Hkv), 256, 0, st>>>(qn, kn, vt, qpages, order, tiles, o, lse, s.Hq,
+                     bf16_t* o_lo, hipStream_t st) {
+  fwd_mfma_kernel<<<(unsigned)(n_qp * s.Hkv), 256, 0, st>>>(qn, kn, vt, qpages, order, tiles, o, lse, o_lo, s.Hq,
                                                             s.Hkv, s.scale * kLog2e);
 }
 
@@ -877,10 +897,10 @@ INST_MFMA_BWD(float)
 
 template <typename T>
 void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,
-                       const QPage* qpages, const int32_t* order, const Tile* tiles, T* o, float* lse,
+                       const QPage* qpages, const int32_t* order, const Tile* tiles, T* o, float* lse, T* o_lo,
                        hipStream_t st) {
-  fwd_simple_kernel<T><<<(unsigned)(n_qp * s.Hq), 64, 0, st>>>(qn, kn, v, qpages, order, tiles, o, lse, s.Hq, s.Hkv,
-                                                              s.D, s.scale);
+  fwd_simple_kernel<T><<<(unsigned)(n_qp * s.Hq), 64, 0, st>>>(qn, kn, v, qpages, order, tiles, o, lse, o_lo, s.Hq,
+                                                              s.Hkv, s.D, s.scale);
 }
 
 template <typename T, typename TG>
@@ -896,8 +916,8 @@ void launch_bwd_simple(const LaunchShape& s, int64_t n_qp, int64_t n_kvp, const 
                                                                       s.Hkv, s.D, s.scale);
 }
 
-template void launch_fwd_simple<bf16_t>(const LaunchShape&, int64_t, const float*, const float*, const bf16_t*, const QPage*, const int32_t*, const Tile*, bf16_t*, float*, hipStream_t);
-template void launch_fwd_simple<float>(const LaunchShape&, int64_t, const float*, const float*, const float*, const QPage*, const int32_t*, const Tile*, float*, float*, hipStream_t);
+template void launch_fwd_simple<bf16_t>(const LaunchShape&, int64_t, const float*, const float*, const bf16_t*, const QPage*, const int32_t*, const Tile*, bf16_t*, float*, bf16_t*, hipStream_t);
+template void launch_fwd_simple<float>(const LaunchShape&, int64_t, const float*, const float*, const float*, const QPage*, const int32_t*, const Tile*, float*, float*, float*, hipStream_t);
 #define INST_BWD_SIMPLE(T, TG)                                                                                 \
   template void launch_bwd_simple<T, TG>(const LaunchShape&, int64_t, int64_t, const float*, const float*,     \
                                          const T*, const T*, const float2*, const float2*, const QPage*,        \

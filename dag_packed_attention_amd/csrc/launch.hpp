@@ -22,14 +22,14 @@ template <typename Tin, typename Tout>
 void launch_relayout(const LaunchShape& s, const Tin* x, const float2* cs, const int32_t* page_nrows,
                      const uint32_t* smax, Tout* out_n, Tout* out_t, int H, hipStream_t st);
 template <typename T>
-void launch_rowdot(const LaunchShape& s, const T* o, const T* dO, const float* lse, const int32_t* page_nrows,
-                   const uint32_t* dmax, float2* ld, hipStream_t st);
+void launch_rowdot(const LaunchShape& s, const T* o, const T* o_lo, const T* dO, const float* lse,
+                   const int32_t* page_nrows, const uint32_t* dmax, float2* ld, hipStream_t st);
 template <typename T>
 void launch_maxabs(const LaunchShape& s, const T* x, int H, const int32_t* page_nrows, uint32_t* out,
                    hipStream_t st);
 void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vt,
                      const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
-                     hipStream_t st);
+                     bf16_t* o_lo, hipStream_t st);
 template <typename TG>
 void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* kt,
                     const f16_t* vn, const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
@@ -41,7 +41,7 @@ void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, cons
                       const int32_t* page_table, const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st);
 template <typename T>
 void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,
-                       const QPage* qpages, const int32_t* order, const Tile* tiles, T* o, float* lse,
+                       const QPage* qpages, const int32_t* order, const Tile* tiles, T* o, float* lse, T* o_lo,
                        hipStream_t st);
 template <typename T, typename TG>
 void launch_bwd_simple(const LaunchShape& s, int64_t n_qp, int64_t n_kvp, const float* qn, const float* kn,

@@ -165,19 +165,25 @@ dag_status dag_attn_workspace(const dag_plan* plan, const dag_attn_params* p, si
  *   o[t,h]   = sum_{j in V(t)} softmax_j(scale <R(pos_t) q[t,h], R(pos_j) k[j,g]>) v[j,g]
  *   lse[t,h] = log sum_{j in V(t)} exp(scale <R(pos_t) q[t,h], R(pos_j) k[j,g]>)
  * q, o: [C, Hq, D]; k, v: [C, Hkv, D] (dtype); lse: [C, Hq] fp32.
+ * o_lo (optional, bf16 only, may be NULL): [C, Hq, D] bf16 receiving the rounding
+ * residual o_exact - o; passing it to dag_attn_bwd lets the backward form
+ * rowsum(dO * O) from an O accurate to ~2^-17 instead of bf16's 2^-9, which matters
+ * where attention is concentrated on few keys.
  * ws: device workspace of at least fwd_bytes. */
 dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k,
-                        const void* v, void* o, float* lse, void* ws, size_t ws_bytes,
+                        const void* v, void* o, float* lse, void* o_lo, void* ws, size_t ws_bytes,
                         void* hip_stream);
 
 /* Backward of dag_attn_fwd given the upstream gradient dO [C, Hq, D] (dtype):
  * dq [C, Hq, D]; dk, dv [C, Hkv, D] (grad_dtype), where every key row's gradient is the sum
  * over all readers (own branch, descendants, mount readers) taken in a fixed
  * order, so results are bitwise reproducible (Octopus Sec. 3.4 Eq. 8, HARTS
- * Sec. 3.4).  o and lse are the forward's outputs.  ws: at least bwd_bytes. */
+ * Sec. 3.4).  o, lse and o_lo (NULL if the forward wrote none) are the forward's
+ * outputs.  ws: at least bwd_bytes. */
 dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k,
-                        const void* v, const void* o, const float* lse, const void* dO, void* dq,
-                        void* dk, void* dv, void* ws, size_t ws_bytes, void* hip_stream);
+                        const void* v, const void* o, const float* lse, const void* o_lo,
+                        const void* dO, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                        void* hip_stream);
 
 /* Per-kernel timing, for profiling.  While enabled, dag_attn_fwd/bwd record a
  * HIP event pair on their stream around each of their kernels (at most

@@ -45,11 +45,15 @@ def _run(dpa, spec, q, k, v, do, hq, hkv, d, dtype, rope=10000.0, transitive=Non
     tdt = p.torch_dtype
     rows = lambda x: dpa.to_rows(plan, x.to(DEV, tdt), fill=float("nan"))
     qr, kr, vr = rows(q), rows(k), rows(v)
-    o, lse = dpa.attn_fwd(plan, p, qr, kr, vr)
+    o_lo = None
+    if dtype == "bf16":
+        o, lse, o_lo = dpa.attn_fwd(plan, p, qr, kr, vr, o_lo=True)
+    else:
+        o, lse = dpa.attn_fwd(plan, p, qr, kr, vr)
     out = {"o": o, "lse": lse}
     if bwd:
         dor = rows(do)
-        dq, dk, dv = dpa.attn_bwd(plan, p, qr, kr, vr, o, lse, dor)
+        dq, dk, dv = dpa.attn_bwd(plan, p, qr, kr, vr, o, lse, dor, o_lo=o_lo)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     rot, _ = plan.row_maps()
@@ -256,11 +260,11 @@ def _full_case(dpa, spec, seed, bwd, n_rows=24, n_keys=6, max_readers=96):
     q = synth.normal((C, 16, 128), seed, 1, DEV, torch.bfloat16)
     k = synth.normal((C, 4, 128), seed, 2, DEV, torch.bfloat16)
     v = synth.normal((C, 4, 128), seed, 3, DEV, torch.bfloat16)
-    o, lse = dpa.attn_fwd(plan, p, q, k, v)
+    o, lse, o_lo = dpa.attn_fwd(plan, p, q, k, v, o_lo=True)
     res = {"o": o, "lse": lse}
     if bwd:
         do = synth.normal((C, 16, 128), seed, 4, DEV, torch.bfloat16)
-        res["dq"], res["dk"], res["dv"] = dpa.attn_bwd(plan, p, q, k, v, o, lse, do)
+        res["dq"], res["dk"], res["dv"] = dpa.attn_bwd(plan, p, q, k, v, o, lse, do, o_lo=o_lo)
     torch.cuda.synchronize()
     for n, t in res.items():
         assert torch.isfinite(t).all(), n
