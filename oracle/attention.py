@@ -242,7 +242,7 @@ class RowSampler:
     def _fwd_one(self, t, q, k, v):
         g, p = self.g, self.p
         keys = g.visible_tokens(int(self.node_of[t]), int(self.off[t]))
-        d = q.shape[-1]
+        d = k.shape[-1]
         scale = p.scale_for(d)
         qt = rotate(np.asarray(q[t:t + 1], np.float64), self.pos[t:t + 1], p.rope_base)[0]
         kk = rotate(np.asarray(k[keys], np.float64), self.pos[keys], p.rope_base)
@@ -258,7 +258,7 @@ class RowSampler:
     def rows(self, tokens: Sequence[int], q, k, v):
         """(o [n,Hq,d], lse [n,Hq]) for the given compact tokens."""
         q, k, v = _np(q), _np(k), _np(v)
-        d = q.shape[-1]
+        d = k.shape[-1]
         o = np.zeros((len(tokens), self.p.hq, d))
         lse = np.zeros((len(tokens), self.p.hq))
         for a, t in enumerate(tokens):
@@ -283,7 +283,7 @@ class RowSampler:
         """(dk [n,Hkv,d], dv [n,Hkv,d]) for the given key tokens, summed over all readers."""
         q, k, v, do = _np(q), _np(k), _np(v), _np(do)
         p = self.p
-        d = q.shape[-1]
+        d = k.shape[-1]
         scale = p.scale_for(d)
         dk = np.zeros((len(keys), p.hkv, d))
         dv = np.zeros((len(keys), p.hkv, d))
