@@ -201,8 +201,11 @@ __global__ __launch_bounds__(256) void maxabs_kernel(const T* __restrict__ x, co
 constexpr int kD = 128;
 constexpr int kKStride = kD + 8;   // LDS row stride (16-bit elements) of a [64][128] tile: +16 B against bank conflicts
 constexpr int kTStride = 64 + 8;   // LDS row stride (16-bit elements) of a [128][64] tile
+constexpr int kTileRows = 64 * kKStride;  // elements of a staged [64][128] tile
+constexpr int kTileCols = kD * kTStride;  // elements of a staged [128][64] tile
 // dK/dV work-group LDS: the K and V tiles, later overlaid by the [64][129] fp32 head sum
-constexpr int kSmemDkdv = (2 * 64 * kKStride * 2 > 64 * (kD + 1) * 4) ? 2 * 64 * kKStride * 2 : 64 * (kD + 1) * 4;
+constexpr int kSmemDkdv = (2 * kTileRows * 2 > 64 * (kD + 1) * 4) ? 2 * kTileRows * 2 : 64 * (kD + 1) * 4;
+constexpr int kRun = 8;  // consecutive units of one head that go to one XCD
 
 __device__ __forceinline__ f32x16 mfma(const f16x8& a, const f16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -223,33 +226,75 @@ __device__ __forceinline__ f16x8 pack8(const f32x16& s, int base) {
 // key (or row) index within a 32-block held by accumulator element r of a lane in half `hi`
 __device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
 
-// Copy a contiguous [64][128] 16-bit tile into LDS with row stride kKStride.
-__device__ __forceinline__ void stage_rows(f16_t* lds, const f16_t* g, int64_t g_row_stride) {
-  for (int c = threadIdx.x; c < 64 * 16; c += 256) {
-    const int r = c >> 4, col = (c & 15) * 8;
-    *reinterpret_cast<uint4*>(lds + r * kKStride + col) =
-        *reinterpret_cast<const uint4*>(g + (int64_t)r * g_row_stride + col);
-  }
-}
-// Copy a contiguous [128][64] 16-bit tile into LDS with row stride kTStride.
-__device__ __forceinline__ void stage_cols(f16_t* lds, const f16_t* g) {
-  for (int c = threadIdx.x; c < 128 * 8; c += 256) {
-    const int r = c >> 3, col = (c & 7) * 8;
-    *reinterpret_cast<uint4*>(lds + r * kTStride + col) =
-        *reinterpret_cast<const uint4*>(g + (int64_t)r * 64 + col);
-  }
+// Work-group -> (unit, head).  The dispatcher deals work-groups round-robin over the
+// eight XCDs, each with its own L2.  Work-group b is the (b / 8)-th one of XCD b % 8;
+// giving every XCD runs of kRun consecutive units of one head lets units that share
+// tiles (one node's pages) meet in one L2, while the runs, in launch order, still
+// interleave over the XCDs so that the heaviest units start first everywhere.  The
+// grid is padded to a multiple of 8 * kRun; padding work-groups return at once.
+__device__ __forceinline__ bool map_item(int n_units, int H, int& unit, int& head) {
+  const int b = blockIdx.x;
+  const int x = b & 7, k = b >> 3;
+  const int L = (((k / kRun) << 3) + x) * kRun + (k % kRun);
+  const int R = L / kRun;
+  head = R % H;
+  unit = (R / H) * kRun + (L % kRun);
+  return unit < n_units;
 }
 
+// Direct global -> LDS tile loads (gfx950 global_load_lds_dwordx4).  Each wave
+// instruction writes 64 x 16 B contiguously at an LDS base held in M0, so the
+// tile's LDS layout is unpadded; the lane that fills a slot fetches the global
+// 16-byte chunk that belongs there under an XOR swizzle, which keeps the MFMA
+// fragment reads free of bank conflicts:
+//   [64][128] tiles (256 B rows):  chunk c of row r sits in slot c ^ (r & 15)
+//   [128][64] tiles (128 B rows):  chunk c of row r sits in slot c ^ ((r >> 1) & 7)
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ void load_tile_rows(f16_t* lds, const f16_t* g, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = (wave * 4 + i) * 64 + lane;  // 16-byte slot in the tile
+    const int r = q >> 4, c = (q & 15) ^ (r & 15);
+    __builtin_amdgcn_global_load_lds(g + r * 128 + c * 8, (lds_void*)(lds + (wave * 4 + i) * 512), 16, 0, 0);
+  }
+}
+__device__ __forceinline__ void load_tile_cols(f16_t* lds, const f16_t* g, int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int q = (wave * 4 + i) * 64 + lane;
+    const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+    __builtin_amdgcn_global_load_lds(g + r * 64 + c * 8, (lds_void*)(lds + (wave * 4 + i) * 512), 16, 0, 0);
+  }
+}
+// fragment reads: 8 elements of row r starting at column chunk c (16-byte chunks)
+__device__ __forceinline__ f16x8 frag_rows(const f16_t* lds, int r, int c) {
+  return ld8(lds + r * 128 + ((c ^ (r & 15)) << 3));
+}
+__device__ __forceinline__ f16x8 frag_cols(const f16_t* lds, int r, int c) {
+  return ld8(lds + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
+}
+// all of this thread's global->LDS loads (and everything else) have landed
+__device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
+
+constexpr int kTile = 64 * kD;  // elements of an unpadded 64 x 128 (or 128 x 64) tile
+
+// Forward for one 64-row query block x one KV head; waves = the four query heads.
+// K/V tiles are double-buffered in LDS and fetched straight from global memory
+// while the previous tile is multiplied; each 64-key tile is taken as two
+// 32-key halves to keep the score registers small.
 __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vt,
     const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
-    bf16_t* __restrict__ o, float* __restrict__ lse, bf16_t* __restrict__ o_lo, int Hq, int Hkv, float sl2) {
-  __shared__ f16_t lk[64 * kKStride];
-  __shared__ f16_t lv[kD * kTStride];
-  const int item = blockIdx.x;
-  const QPage qp = qpages[order[item / Hkv]];
-  const int g = item % Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    bf16_t* __restrict__ o, float* __restrict__ lse, bf16_t* __restrict__ o_lo, int n_qp, int Hq, int Hkv,
+    float sl2) {
+  __shared__ __attribute__((aligned(1024))) f16_t lk[2][kTile];
+  __shared__ __attribute__((aligned(1024))) f16_t lv[2][kTile];
+  int unit, g;
+  if (!map_item(n_qp, Hkv, unit, g)) return;
+  const QPage qp = qpages[order[unit]];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int h = g * 4 + wave;
 
@@ -267,74 +312,96 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
     for (int b = 0; b < 2; ++b) oacc[a][b] = zero16();
   float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
 
-  for (int t = 0; t < qp.tile_count; ++t) {
-    const Tile tl = tiles[qp.tile_begin + t];
-    const int lo = tl.lohi & 0xff, hi_t = (tl.lohi >> 8) & 0xff;
-    const bool diag = (t == qp.tile_count - 1);
-    __syncthreads();
-    stage_rows(lk, kn + ((int64_t)tl.page * Hkv + g) * 64 * kD, kD);
-    stage_cols(lv, vt + ((int64_t)tl.page * Hkv + g) * kD * 64);
-    __syncthreads();
+  const int T = qp.tile_count;
+  {
+    const int64_t base = ((int64_t)tiles[qp.tile_begin].page * Hkv + g) * kTile;
+    load_tile_rows(lk[0], kn + base, wave, lane);
+    load_tile_cols(lv[0], vt + base, wave, lane);
+  }
+  wait_all_loads();
+  __syncthreads();
 
-    f32x16 s[2][2];
+  for (int t = 0; t < T; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < T) {
+      const int64_t base = ((int64_t)tiles[qp.tile_begin + t + 1].page * Hkv + g) * kTile;
+      load_tile_rows(lk[buf ^ 1], kn + base, wave, lane);
+      load_tile_cols(lv[buf ^ 1], vt + base, wave, lane);
+    }
+    const int lohi = tiles[qp.tile_begin + t].lohi;
+    const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
+    const bool diag = (t == T - 1);
+    const bool full = lo == 0 && hi_t == 64 && !diag;
+    const f16_t* K = lk[buf];
+    const f16_t* V = lv[buf];
+
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      s[mb][0] = zero16();
-      s[mb][1] = zero16();
+    for (int mb = 0; mb < 2; ++mb) {  // 32-key halves
+      f32x16 s[2];
+      s[0] = zero16();
+      s[1] = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const f16x8 a = ld8(lk + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
-        s[mb][0] = mfma(a, qf[0][ks], s[mb][0]);
-        s[mb][1] = mfma(a, qf[1][ks], s[mb][1]);
+        const f16x8 a = frag_rows(K, mb * 32 + l32, ks * 2 + hi);
+        s[0] = mfma(a, qf[0][ks], s[0]);
+        s[1] = mfma(a, qf[1][ks], s[1]);
       }
-    }
-    f16x8 pf[4][2];
+      // Online softmax in the log2 domain.  The running max m is raised only when
+      // a row's new maximum exceeds it by more than kLazy (any lane of the wave),
+      // so the accumulator rescale is rare; in between, probabilities reach at most
+      // 2^kLazy, well inside fp16, and the final division by l removes the offset.
+      constexpr float kLazy = 8.f;
+      f16x8 pf[2][2];
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int row = nb * 32 + l32;
-      float mx = -INFINITY;
+      for (int nb = 0; nb < 2; ++nb) {
+        const int row = nb * 32 + l32;
+        if (!full) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = mb * 32 + acc_row(r, hi);
-          const bool ok = key >= lo && key < hi_t && (!diag || key <= row);
-          const float x = ok ? s[mb][nb][r] * sl2 : -INFINITY;
-          s[mb][nb][r] = x;
-          mx = fmaxf(mx, x);
+          for (int r = 0; r < 16; ++r) {
+            const int key = mb * 32 + acc_row(r, hi);
+            const bool ok = key >= lo && key < hi_t && (!diag || key <= row);
+            s[nb][r] = ok ? s[nb][r] : -INFINITY;
+          }
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(mrow[nb], mx);
-      const float alpha = __builtin_amdgcn_exp2f(mrow[nb] - mnew);
-      mrow[nb] = mnew;
-      float sum = 0.f;
+        float mx = s[nb][0];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+        if (__any(mx > mrow[nb] + kLazy)) {
+          const float mnew = fmaxf(mrow[nb], mx);
+          const float alpha = __builtin_amdgcn_exp2f(mrow[nb] - mnew);
+          mrow[nb] = mnew;
+          lrow[nb] *= alpha;
+#pragma unroll
+          for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[a][nb][r] *= alpha;
+        }
+        // a half-tile can be fully masked before a row has seen any key (a mounted
+        // span starting past key 32); then m is still -inf and every score is -inf
+        const float mneg = mrow[nb] == -INFINITY ? 0.f : -mrow[nb];
+        float sum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[mb][nb][r] - mnew);
-          s[mb][nb][r] = p;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, mneg));
+          s[nb][r] = p;
           sum += p;
         }
-      lrow[nb] = lrow[nb] * alpha + sum;
+        lrow[nb] += sum;
+        pf[0][nb] = pack8(s[nb], 0);
+        pf[1][nb] = pack8(s[nb], 8);
+      }
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[a][nb][r] *= alpha;
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        pf[2 * mb][nb] = pack8(s[mb][nb], 0);
-        pf[2 * mb + 1][nb] = pack8(s[mb][nb], 8);
-      }
+        for (int kk = 0; kk < 2; ++kk) {
+          const f16x8 va = frag_cols(V, a * 32 + l32, (mb * 2 + kk) * 2 + hi);
+          oacc[a][0] = mfma(va, pf[kk][0], oacc[a][0]);
+          oacc[a][1] = mfma(va, pf[kk][1], oacc[a][1]);
+        }
     }
-#pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const f16x8 va = ld8(lv + (a * 32 + l32) * kTStride + ks * 16 + hi * 8);
-        oacc[a][0] = mfma(va, pf[ks][0], oacc[a][0]);
-        oacc[a][1] = mfma(va, pf[ks][1], oacc[a][1]);
-      }
+    wait_all_loads();
+    __syncthreads();
   }
 
 #pragma unroll
@@ -350,20 +417,20 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int d = a * 32 + 8 * j + 4 * hi;
-        bf16_t hv[4], lv[4];
+        bf16_t hv[4], lv4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const float x = oacc[a][nb][4 * j + i] * inv;
           hv[i] = f2bf(x);
-          lv[i] = f2bf(x - bf2f(hv[i]));
+          lv4[i] = f2bf(x - bf2f(hv[i]));
         }
         uint2 w;
         w.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
         w.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
         *reinterpret_cast<uint2*>(orow + d) = w;
         if (o_lo) {
-          w.x = (uint32_t)lv[0] | ((uint32_t)lv[1] << 16);
-          w.y = (uint32_t)lv[2] | ((uint32_t)lv[3] << 16);
+          w.x = (uint32_t)lv4[0] | ((uint32_t)lv4[1] << 16);
+          w.y = (uint32_t)lv4[2] | ((uint32_t)lv4[3] << 16);
           *reinterpret_cast<uint2*>(o_lo + (grow * Hq + h) * kD + d) = w;
         }
       }
@@ -372,20 +439,22 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
 }
 
 // dQ for one query block (64 rows) x one KV head; waves = the four query heads.
+// The K, V and K^T tiles are double-buffered in LDS like the forward's.
 template <typename TG>
 __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ kt,
     const f16_t* __restrict__ vn, const f16_t* __restrict__ dOn, const float2* __restrict__ ldd,
     const float2* __restrict__ cs, const uint32_t* __restrict__ dmax, const QPage* __restrict__ qpages,
-    const int32_t* __restrict__ order, const Tile* __restrict__ tiles, TG* __restrict__ dq, int Hq, int Hkv,
-    float sl2, float scale) {
-  __shared__ f16_t lk[64 * kKStride];
-  __shared__ f16_t lvv[64 * kKStride];
-  __shared__ f16_t lkt[kD * kTStride];
-  const int item = blockIdx.x;
-  const QPage qp = qpages[order[item / Hkv]];
-  const int g = item % Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int32_t* __restrict__ order, const Tile* __restrict__ tiles, TG* __restrict__ dq, int n_qp, int Hq,
+    int Hkv, float sl2, float scale) {
+  __shared__ __attribute__((aligned(1024))) f16_t lk[2][kTile];
+  __shared__ __attribute__((aligned(1024))) f16_t lvv[2][kTile];
+  __shared__ __attribute__((aligned(1024))) f16_t lkt[2][kTile];
+  int unit, g;
+  if (!map_item(n_qp, Hkv, unit, g)) return;
+  const QPage qp = qpages[order[unit]];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
   const int h = g * 4 + wave;
 
@@ -396,11 +465,10 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int row = nb * 32 + l32;
-    const f16_t* drow = db + row * kD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
       qf[nb][ks] = ld8(qb + row * kD + ks * 16 + hi * 8);
-      df[nb][ks] = ld8(drow + ks * 16 + hi * 8);
+      df[nb][ks] = ld8(db + row * kD + ks * 16 + hi * 8);
     }
     const float2 t = ldd[((int64_t)qp.phys * Hq + h) * 64 + row];
     lse2[nb] = t.x;
@@ -412,23 +480,39 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
 #pragma unroll
     for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
 
-  for (int t = 0; t < qp.tile_count; ++t) {
-    const Tile tl = tiles[qp.tile_begin + t];
-    const int lo = tl.lohi & 0xff, hi_t = (tl.lohi >> 8) & 0xff;
-    const bool diag = (t == qp.tile_count - 1);
-    __syncthreads();
-    stage_rows(lk, kn + ((int64_t)tl.page * Hkv + g) * 64 * kD, kD);
-    stage_rows(lvv, vn + ((int64_t)tl.page * Hkv + g) * 64 * kD, kD);
-    stage_cols(lkt, kt + ((int64_t)tl.page * Hkv + g) * kD * 64);
-    __syncthreads();
+  const int T = qp.tile_count;
+  {
+    const int64_t base = ((int64_t)tiles[qp.tile_begin].page * Hkv + g) * kTile;
+    load_tile_rows(lk[0], kn + base, wave, lane);
+    load_tile_rows(lvv[0], vn + base, wave, lane);
+    load_tile_cols(lkt[0], kt + base, wave, lane);
+  }
+  wait_all_loads();
+  __syncthreads();
+
+  for (int t = 0; t < T; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < T) {
+      const int64_t base = ((int64_t)tiles[qp.tile_begin + t + 1].page * Hkv + g) * kTile;
+      load_tile_rows(lk[buf ^ 1], kn + base, wave, lane);
+      load_tile_rows(lvv[buf ^ 1], vn + base, wave, lane);
+      load_tile_cols(lkt[buf ^ 1], kt + base, wave, lane);
+    }
+    const int lohi = tiles[qp.tile_begin + t].lohi;
+    const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
+    const bool diag = (t == T - 1);
+    const bool full = lo == 0 && hi_t == 64 && !diag && qp.nrows == 64;
+    const f16_t* K = lk[buf];
+    const f16_t* V = lvv[buf];
+    const f16_t* KT = lkt[buf];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       f32x16 s[2], dp[2];
       s[0] = s[1] = dp[0] = dp[1] = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const f16x8 a = ld8(lk + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
-        const f16x8 b = ld8(lvv + (mb * 32 + l32) * kKStride + ks * 16 + hi * 8);
+        const f16x8 a = frag_rows(K, mb * 32 + l32, ks * 2 + hi);
+        const f16x8 b = frag_rows(V, mb * 32 + l32, ks * 2 + hi);
         s[0] = mfma(a, qf[0][ks], s[0]);
         s[1] = mfma(a, qf[1][ks], s[1]);
         dp[0] = mfma(b, df[0][ks], dp[0]);
@@ -438,12 +522,19 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int row = nb * 32 + l32;
+        const float nl = -lse2[nb];
+        if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = mb * 32 + acc_row(r, hi);
-          const bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < qp.nrows;
-          const float p = ok ? __builtin_amdgcn_exp2f(s[nb][r] * sl2 - lse2[nb]) : 0.f;
-          s[nb][r] = ok ? p * (dp[nb][r] - Dv[nb]) : 0.f;  // padding rows may hold NaN
+          for (int r = 0; r < 16; ++r)
+            s[nb][r] = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, nl)) * (dp[nb][r] - Dv[nb]);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = mb * 32 + acc_row(r, hi);
+            const bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < qp.nrows;
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, nl));
+            s[nb][r] = ok ? p * (dp[nb][r] - Dv[nb]) : 0.f;  // padding may hold NaN
+          }
         }
         dsf[0][nb] = pack8(s[nb], 0);
         dsf[1][nb] = pack8(s[nb], 8);
@@ -452,11 +543,13 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
       for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-          const f16x8 ka = ld8(lkt + (a * 32 + l32) * kTStride + (mb * 2 + kk) * 16 + hi * 8);
+          const f16x8 ka = frag_cols(KT, a * 32 + l32, (mb * 2 + kk) * 2 + hi);
           acc[a][0] = mfma(ka, dsf[kk][0], acc[a][0]);
           acc[a][1] = mfma(ka, dsf[kk][1], acc[a][1]);
         }
     }
+    wait_all_loads();
+    __syncthreads();
   }
 
   const float gscale = scale / pow2_scale(*dmax);  // undo the dO scaling
@@ -486,147 +579,141 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
   }
 }
 
-// dK, dV for one KV page x one KV head.  Waves = the four query heads; each
-// wave walks the page's reader list and keeps its own dK/dV in registers; the
-// four are then summed through LDS in head order.
+// dK, dV for one KV page x one KV head.  Eight waves: wave w serves query head
+// 4 g + (w % 4) and the page's keys [32 (w / 4), 32 (w / 4) + 32), so two waves
+// share each SIMD and hide each other's load latency.  Each wave walks the page's
+// reader list in its fixed order, keeping its dK and dV slice in registers; the
+// four heads are then summed through LDS in head order and written once.
 template <typename TG>
-__global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
+__global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ qt, const f16_t* __restrict__ kn,
     const f16_t* __restrict__ vn, const f16_t* __restrict__ dOn, const f16_t* __restrict__ dOt,
     const float2* __restrict__ ldd, const float2* __restrict__ cs, const uint32_t* __restrict__ dmax,
-    const int32_t* __restrict__ order,
-    const int32_t* __restrict__ kv_off, const KEntry* __restrict__ ents,
-    const int32_t* __restrict__ page_table, const int32_t* __restrict__ page_nrows,
-    TG* __restrict__ dk, TG* __restrict__ dv, int Hq, int Hkv, float sl2, float scale) {
+    const int32_t* __restrict__ order, const int32_t* __restrict__ kv_off, const KEntry* __restrict__ ents,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ page_nrows, TG* __restrict__ dk,
+    TG* __restrict__ dv, int n_kvp, int Hq, int Hkv, float sl2, float scale) {
   // K/V tiles during the walk; the same bytes hold the head reduction afterwards
   __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemDkdv];
   f16_t* lk = reinterpret_cast<f16_t*>(smem);
-  f16_t* lvv = lk + 64 * kKStride;
+  f16_t* lvv = lk + kTileRows;
   float* red = reinterpret_cast<float*>(smem);
-  const int item = blockIdx.x;
-  const int page = order[item / Hkv];
-  const int g = item % Hkv;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int unit, g;
+  if (!map_item(n_kvp, Hkv, unit, g)) return;
+  const int page = order[unit];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int h = g * 4 + wave;
+  const int hh = wave & 3, kh = wave >> 2;
+  const int h = g * 4 + hh;
   const int krows = page_nrows[page];
+  const int key = kh * 32 + l32;  // the key this lane's accumulator columns belong to
 
-  stage_rows(lk, kn + ((int64_t)page * Hkv + g) * 64 * kD, kD);
-  stage_rows(lvv, vn + ((int64_t)page * Hkv + g) * 64 * kD, kD);
+  {
+    const int64_t base = ((int64_t)page * Hkv + g) * 64 * kD;
+    for (int c = tid; c < 64 * 16; c += 512) {
+      const int r = c >> 4, col = (c & 15) * 8;
+      *reinterpret_cast<uint4*>(lk + r * kKStride + col) = *reinterpret_cast<const uint4*>(kn + base + c * 8);
+      *reinterpret_cast<uint4*>(lvv + r * kKStride + col) = *reinterpret_cast<const uint4*>(vn + base + c * 8);
+    }
+  }
   __syncthreads();
 
-  f32x16 adk[2][4], adv[2][4];  // [key block][d block]
+  f32x16 adk[4], adv[4];  // keys (this wave's 32) x d blocks of 32
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) adk[a][b] = adv[a][b] = zero16();
+  for (int b = 0; b < 4; ++b) adk[b] = adv[b] = zero16();
 
+  const f16_t* Krow = lk + key * kKStride + hi * 8;
+  const f16_t* Vrow = lvv + key * kKStride + hi * 8;
   for (int e = kv_off[page]; e < kv_off[page + 1]; ++e) {
     const KEntry ent = ents[e];
     const int lo = ent.lohi_diag & 0xff, hi_t = (ent.lohi_diag >> 8) & 0xff;
     const bool diag = (ent.lohi_diag >> 16) & 1;
+    const bool key_ok = key >= lo && key < hi_t;
     for (int lq = ent.lq0; lq < ent.lq1; ++lq) {
       const int qph = page_table[ent.slot_base + lq];
       const int nrows = page_nrows[qph];
-      const f16_t* qb = qn + ((int64_t)qph * Hq + h) * 64 * kD;
-      const f16_t* qtb = qt + ((int64_t)qph * Hq + h) * kD * 64;
-      const f16_t* dnb = dOn + ((int64_t)qph * Hq + h) * 64 * kD;
-      const f16_t* dtb = dOt + ((int64_t)qph * Hq + h) * kD * 64;
+      const bool full = lo == 0 && hi_t == 64 && !diag && nrows == 64;
+      const int64_t hb = ((int64_t)qph * Hq + h) * 64 * kD;  // [64][128] and [128][64] blocks share offsets
+      const f16_t* qb = qn + hb;
+      const f16_t* qtb = qt + hb;
+      const f16_t* dnb = dOn + hb;
+      const f16_t* dtb = dOt + hb;
       const float2* ldb = ldd + ((int64_t)qph * Hq + h) * 64;
       for (int rb = 0; rb < 2; ++rb) {
         if (rb * 32 >= nrows) break;
-        // S = Q K^T and dP = dO V^T for 32 rows x 64 keys (rows = M, keys = N)
-        f32x16 s[2], dp[2];
-        s[0] = s[1] = dp[0] = dp[1] = zero16();
+        // this lane's 16 rows: rb*32 + acc_row(r, hi); fetch their (lse, D) first
+        float2 lr[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) lr[r] = ldb[rb * 32 + acc_row(r, hi)];
+        // S = Q K^T and dP = dO V^T for 32 rows (M) x this wave's 32 keys (N)
+        f32x16 s = zero16(), dp = zero16();
         const int arow = rb * 32 + l32;
-        const f16_t* drow = dnb + arow * kD;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
           const f16x8 qa = ld8(qb + arow * kD + ks * 16 + hi * 8);
-          const f16x8 da = ld8(drow + ks * 16 + hi * 8);
+          const f16x8 da = ld8(dnb + arow * kD + ks * 16 + hi * 8);
+          s = mfma(qa, ld8(Krow + ks * 16), s);
+          dp = mfma(da, ld8(Vrow + ks * 16), dp);
+        }
+        // P and dS; this lane holds key `key` and rows rb*32 + acc_row(r, hi)
+        if (full) {
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const f16x8 kb = ld8(lk + (nb * 32 + l32) * kKStride + ks * 16 + hi * 8);
-            const f16x8 vb = ld8(lvv + (nb * 32 + l32) * kKStride + ks * 16 + hi * 8);
-            s[nb] = mfma(qa, kb, s[nb]);
-            dp[nb] = mfma(da, vb, dp[nb]);
+          for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr[r].x));
+            s[r] = p;
+            dp[r] = p * (dp[r] - lr[r].y);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rb * 32 + acc_row(r, hi);
+            const bool ok = key_ok && (!diag || key <= row) && row < nrows;
+            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr[r].x)) : 0.f;
+            s[r] = p;
+            dp[r] = ok ? p * (dp[r] - lr[r].y) : 0.f;  // padding may hold NaN
           }
         }
-        // P and dS; this lane holds key nb*32 + l32 and rows rb*32 + acc_row(r, hi)
-        f16x8 pf[2][2], sf[2][2];  // [k-step of 16 rows][key block]
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r0 = rb * 32 + 8 * j + 4 * hi;
-          float2 lr[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) lr[i] = ldb[r0 + i];
-#pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int key = nb * 32 + l32;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int row = r0 + i;
-              const bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < nrows;
-              const float p = ok ? __builtin_amdgcn_exp2f(s[nb][4 * j + i] * sl2 - lr[i].x) : 0.f;
-              s[nb][4 * j + i] = p;
-              dp[nb][4 * j + i] = ok ? p * (dp[nb][4 * j + i] - lr[i].y) : 0.f;  // padding may hold NaN
-            }
-          }
-        }
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          pf[0][nb] = pack8(s[nb], 0);
-          pf[1][nb] = pack8(s[nb], 8);
-          sf[0][nb] = pack8(dp[nb], 0);
-          sf[1][nb] = pack8(dp[nb], 8);
-        }
+        const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8), sf0 = pack8(dp, 0), sf1 = pack8(dp, 8);
         // dV += P^T dO, dK += dS^T Q (keys = M, d = N, rows = contraction)
+        const int col = rb * 32 + hi * 8;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int col = (rb * 2 + kk) * 16 + hi * 8;
-#pragma unroll
-          for (int b = 0; b < 4; ++b) {
-            const f16x8 dob = ld8(dtb + (b * 32 + l32) * 64 + col);
-            const f16x8 qbt = ld8(qtb + (b * 32 + l32) * 64 + col);
-#pragma unroll
-            for (int nb = 0; nb < 2; ++nb) {
-              adv[nb][b] = mfma(pf[kk][nb], dob, adv[nb][b]);
-              adk[nb][b] = mfma(sf[kk][nb], qbt, adk[nb][b]);
-            }
-          }
+        for (int b = 0; b < 4; ++b) {
+          const f16_t* dt = dtb + (b * 32 + l32) * 64 + col;
+          const f16_t* qtt = qtb + (b * 32 + l32) * 64 + col;
+          adv[b] = mfma(pf0, ld8(dt), adv[b]);
+          adv[b] = mfma(pf1, ld8(dt + 16), adv[b]);
+          adk[b] = mfma(sf0, ld8(qtt), adk[b]);
+          adk[b] = mfma(sf1, ld8(qtt + 16), adk[b]);
         }
       }
     }
   }
 
   const float inv_sdo = 1.f / pow2_scale(*dmax);  // undo the dO scaling
-  // sum the four heads in order 0..3 through LDS, then write dk (un-rotated) and dv
+  // sum the four heads in order 0..3 through LDS (both key halves at once), then
+  // write dk (un-rotated) and dv
   for (int which = 0; which < 2; ++which) {
     for (int w = 0; w < 4; ++w) {
       __syncthreads();
-      if (wave == w) {
+      if (hh == w) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = nb * 32 + acc_row(r, hi);
-              const int d = b * 32 + l32;
-              const float x = which == 0 ? adk[nb][b][r] : adv[nb][b][r];
-              float* slot = red + key * (kD + 1) + d;
-              *slot = (w == 0) ? x : *slot + x;
-            }
+          for (int r = 0; r < 16; ++r) {
+            const int k2 = kh * 32 + acc_row(r, hi);
+            const int d = b * 32 + l32;
+            const float x = which == 0 ? adk[b][r] : adv[b][r];
+            float* slot = red + k2 * (kD + 1) + d;
+            *slot = (w == 0) ? x : *slot + x;
+          }
       }
     }
     __syncthreads();
-    for (int idx = threadIdx.x; idx < 64 * 64; idx += 256) {
-      const int key = idx / 64, i = idx % 64;
-      const int64_t grow = (int64_t)page * 64 + key;
-      float a = red[key * (kD + 1) + i], b = red[key * (kD + 1) + i + 64];
-      a *= inv_sdo;
-      b *= inv_sdo;
-      if (key >= krows) {
+    for (int idx = tid; idx < 64 * 64; idx += 512) {
+      const int k2 = idx / 64, i = idx % 64;
+      const int64_t grow = (int64_t)page * 64 + k2;
+      float a = red[k2 * (kD + 1) + i] * inv_sdo, b = red[k2 * (kD + 1) + i + 64] * inv_sdo;
+      if (k2 >= krows) {
         a = b = 0.f;
       } else if (which == 0) {
         a *= scale;
@@ -859,19 +946,27 @@ template void launch_rowdot<bf16_t>(const LaunchShape&, const bf16_t*, const bf1
 template void launch_rowdot<float>(const LaunchShape&, const float*, const float*, const float*, const float*, const int32_t*, const uint32_t*, float2*, hipStream_t);
 template void launch_maxabs<bf16_t>(const LaunchShape&, const bf16_t*, int, const int32_t*, uint32_t*, hipStream_t);
 
+// Grid for map_item: whole runs of kRun units per head, padded to a multiple of 8 runs.
+static unsigned run_grid(int64_t n_units, int H) {
+  const int64_t runs = (n_units + kRun - 1) / kRun;
+  const int64_t quantum = 8 * kRun;
+  return (unsigned)((runs * H * kRun + quantum - 1) / quantum * quantum);
+}
+
 void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vt,
                      const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
                      bf16_t* o_lo, hipStream_t st) {
-  fwd_mfma_kernel<<<(unsigned)(n_qp * s.Hkv), 256, 0, st>>>(qn, kn, vt, qpages, order, tiles, o, lse, o_lo, s.Hq,
-                                                            s.Hkv, s.scale * kLog2e);
+  fwd_mfma_kernel<<<run_grid(n_qp, s.Hkv), 256, 0, st>>>(qn, kn, vt, qpages, order, tiles, o, lse, o_lo, (int)n_qp,
+                                                         s.Hq, s.Hkv, s.scale * kLog2e);
 }
 
 template <typename TG>
 void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* kt,
                     const f16_t* vn, const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
                     const QPage* qpages, const int32_t* order, const Tile* tiles, TG* dq, hipStream_t st) {
-  dq_mfma_kernel<TG><<<(unsigned)(n_qp * s.Hkv), 256, 0, st>>>(qn, kn, kt, vn, dOn, ld, cs, dmax, qpages, order,
-                                                               tiles, dq, s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
+  dq_mfma_kernel<TG><<<run_grid(n_qp, s.Hkv), 256, 0, st>>>(qn, kn, kt, vn, dOn, ld, cs, dmax, qpages, order,
+                                                            tiles, dq, (int)n_qp, s.Hq, s.Hkv, s.scale * kLog2e,
+                                                            s.scale);
 }
 
 template <typename TG>
@@ -879,9 +974,9 @@ void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, cons
                       const f16_t* vn, const f16_t* dOn, const f16_t* dOt, const float2* ld, const float2* cs,
                       const uint32_t* dmax, const int32_t* order, const int32_t* kv_off, const KEntry* ents,
                       const int32_t* page_table, const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st) {
-  dkdv_mfma_kernel<TG><<<(unsigned)(n_kvp * s.Hkv), 256, 0, st>>>(qn, qt, kn, vn, dOn, dOt, ld, cs, dmax, order,
-                                                                  kv_off, ents, page_table, page_nrows, dk, dv,
-                                                                  s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
+  dkdv_mfma_kernel<TG><<<run_grid(n_kvp, s.Hkv), 512, 0, st>>>(qn, qt, kn, vn, dOn, dOt, ld, cs, dmax, order,
+                                                               kv_off, ents, page_table, page_nrows, dk, dv,
+                                                               (int)n_kvp, s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
 }
 
 #define INST_MFMA_BWD(TG)                                                                                      \

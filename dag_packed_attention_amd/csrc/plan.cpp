@@ -17,7 +17,7 @@
 //   8. per-KV-page reader lists in a fixed order (the deterministic order in
 //      which the backward sums reader contributions into producer pages,
 //      Octopus Sec. 3.4 Eq. 8, HARTS Sec. 3.4);
-//   9. launch orders, heaviest work first.
+//   9. launch orders: node-grouped, heaviest first.
 #include "plan.hpp"
 
 #include <algorithm>
@@ -310,7 +310,11 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
     for_each_entry([&](int32_t ph, const KEntry& e) { P->kentries[fill[ph]++] = e; });
   }
 
-  // ---- 9. launch orders (largest estimated work first; ties by index) ---------------
+  // ---- 9. launch orders -------------------------------------------------------------
+  // Node-grouped, heaviest first: nodes sorted by their heaviest page's work, each
+  // node's pages listed together (heaviest first).  Neighbouring work-groups then
+  // share K/V tiles (forward, dQ: one node's query pages see the same tiles) or
+  // reader lists (dK/dV: one node's KV pages are read by the same query pages).
   {
     std::vector<int64_t> wq(P->qpages.size(), 0);
     for (size_t i = 0; i < P->qpages.size(); ++i) {
@@ -320,10 +324,21 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
         keys += ((P->tiles[t].lohi >> 8) & 0xff) - (P->tiles[t].lohi & 0xff);
       wq[i] = keys;
     }
-    P->fwd_order.resize(P->qpages.size());
-    std::iota(P->fwd_order.begin(), P->fwd_order.end(), 0);
-    std::stable_sort(P->fwd_order.begin(), P->fwd_order.end(),
-                     [&](int32_t a, int32_t b) { return wq[a] > wq[b]; });
+    // query pages of node u are contiguous in qpages, lp ascending (heaviest last)
+    std::vector<int32_t> qp_first(n + 1, 0);
+    for (int32_t u = 0, c = 0; u < n; ++u) {
+      qp_first[u] = c;
+      c += P->length[u] > 0 ? P->npages[u] : 0;
+      qp_first[u + 1] = c;
+    }
+    std::vector<int32_t> nodes_by(n);
+    std::iota(nodes_by.begin(), nodes_by.end(), 0);
+    auto node_wq = [&](int32_t u) { return qp_first[u + 1] > qp_first[u] ? wq[qp_first[u + 1] - 1] : -1; };
+    std::stable_sort(nodes_by.begin(), nodes_by.end(), [&](int32_t a, int32_t b) { return node_wq(a) > node_wq(b); });
+    P->fwd_order.clear();
+    for (int32_t u : nodes_by)
+      for (int32_t i = qp_first[u + 1] - 1; i >= qp_first[u]; --i) P->fwd_order.push_back(i);
+
     std::vector<int64_t> wk(n_pages, 0);
     for (int32_t ph = 0; ph < n_pages; ++ph) {
       int64_t w = 0;
@@ -333,11 +348,14 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
       }
       wk[ph] = w;
     }
+    auto node_wk = [&](int32_t u) {  // a node's first page has the most readers
+      return P->length[u] > 0 ? wk[P->page_table[P->slot0[u]]] : -1;
+    };
+    std::stable_sort(nodes_by.begin(), nodes_by.end(), [&](int32_t a, int32_t b) { return node_wk(a) > node_wk(b); });
     P->bwd_order.clear();
-    for (int32_t ph = 0; ph < n_pages; ++ph)
-      if (P->page_nrows[ph] > 0) P->bwd_order.push_back(ph);
-    std::stable_sort(P->bwd_order.begin(), P->bwd_order.end(),
-                     [&](int32_t a, int32_t b) { return wk[a] > wk[b]; });
+    for (int32_t u : nodes_by)
+      if (P->length[u] > 0)
+        for (int32_t lp = 0; lp < P->npages[u]; ++lp) P->bwd_order.push_back(P->page_table[P->slot0[u] + lp]);
   }
 
   // ---- info ------------------------------------------------------------------------
