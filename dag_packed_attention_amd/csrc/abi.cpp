@@ -27,6 +27,7 @@ struct DeviceTables {
   int32_t* fwd_order = nullptr;
   KEntry* kentries = nullptr;
   int32_t* kv_off = nullptr;
+  int32_t* kv_steps = nullptr;
   int32_t* bwd_order = nullptr;
   int32_t* page_table = nullptr;
   int32_t* page_nrows = nullptr;
@@ -110,11 +111,9 @@ struct BwdWs {
   float2* cs;
   void* qn;
   void* kn;
-  void* qt;
   void* kt;
   void* vn;
   void* dOn;
-  void* dOt;
   float2* ld;
   uint32_t* dmax;
 };
@@ -143,16 +142,14 @@ size_t carve_bwd(const LaunchShape& s, bool mfma, void* base, BwdWs* w) {
   w->dmax = c.take<uint32_t>(1);
   if (mfma) {
     w->qn = c.take<f16_t>(C * s.Hq * s.D);
-    w->qt = c.take<f16_t>(C * s.Hq * s.D);
     w->dOn = c.take<f16_t>(C * s.Hq * s.D);
-    w->dOt = c.take<f16_t>(C * s.Hq * s.D);
     w->kn = c.take<f16_t>(C * s.Hkv * s.D);
     w->kt = c.take<f16_t>(C * s.Hkv * s.D);
     w->vn = c.take<f16_t>(C * s.Hkv * s.D);
   } else {
     w->qn = c.take<float>(C * s.Hq * s.D);
     w->kn = c.take<float>(C * s.Hkv * s.D);
-    w->qt = w->dOt = w->kt = w->vn = w->dOn = nullptr;
+    w->kt = w->vn = w->dOn = nullptr;
   }
   return c.off;
 }
@@ -176,6 +173,7 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
   bytes += align256(P.pos_of_row.size() * 4) + align256(P.tiles.size() * sizeof(Tile)) +
            align256(P.qpages.size() * sizeof(QPage)) + align256(P.fwd_order.size() * 4) +
            align256(P.kentries.size() * sizeof(KEntry)) + align256(P.kv_off.size() * 4) +
+           align256(P.kv_steps.size() * 4) +
            align256(P.bwd_order.size() * 4) + align256(P.page_table.size() * 4) +
            align256(P.page_nrows.size() * 4) + 256;
   DeviceTables* D = new (std::nothrow) DeviceTables();
@@ -194,6 +192,7 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
   D->fwd_order = dev_take<int32_t>(b, off, P.fwd_order.size());
   D->kentries = dev_take<KEntry>(b, off, P.kentries.size());
   D->kv_off = dev_take<int32_t>(b, off, P.kv_off.size());
+  D->kv_steps = dev_take<int32_t>(b, off, P.kv_steps.size());
   D->bwd_order = dev_take<int32_t>(b, off, P.bwd_order.size());
   D->page_table = dev_take<int32_t>(b, off, P.page_table.size());
   D->page_nrows = dev_take<int32_t>(b, off, P.page_nrows.size());
@@ -206,6 +205,7 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
             put(D->fwd_order, P.fwd_order.data(), P.fwd_order.size() * 4) &&
             put(D->kentries, P.kentries.data(), P.kentries.size() * sizeof(KEntry)) &&
             put(D->kv_off, P.kv_off.data(), P.kv_off.size() * 4) &&
+            put(D->kv_steps, P.kv_steps.data(), P.kv_steps.size() * 4) &&
             put(D->bwd_order, P.bwd_order.data(), P.bwd_order.size() * 4) &&
             put(D->page_table, P.page_table.data(), P.page_table.size() * 4) &&
             put(D->page_nrows, P.page_nrows.data(), P.page_nrows.size() * 4);
@@ -465,19 +465,18 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
       launch_maxabs<bf16_t>(s, d16, s.Hq, nr, w.dmax, stream);
       launch_rowdot<bf16_t>(s, o16, (const bf16_t*)o_lo, d16, lse, nr, w.dmax, w.ld, stream);
-      launch_relayout<bf16_t, f16_t>(s, q16, w.cs, nr, nullptr, (f16_t*)w.qn, (f16_t*)w.qt, s.Hq, stream);
+      launch_relayout<bf16_t, f16_t>(s, q16, w.cs, nr, nullptr, (f16_t*)w.qn, nullptr, s.Hq, stream);
       launch_relayout<bf16_t, f16_t>(s, k16, w.cs, nr, nullptr, (f16_t*)w.kn, (f16_t*)w.kt, s.Hkv, stream);
       launch_relayout<bf16_t, f16_t>(s, v16, nullptr, nr, nullptr, (f16_t*)w.vn, nullptr, s.Hkv, stream);
-      launch_relayout<bf16_t, f16_t>(s, d16, nullptr, nr, w.dmax, (f16_t*)w.dOn, (f16_t*)w.dOt, s.Hq, stream);
+      launch_relayout<bf16_t, f16_t>(s, d16, nullptr, nr, w.dmax, (f16_t*)w.dOn, nullptr, s.Hq, stream);
     }
     auto grads = [&](auto* tag) {
       using TG = std::remove_pointer_t<decltype(tag)>;
       {
         Span sp(P, DAG_K_DKDV, stream);
-        launch_dkdv_mfma<TG>(s, n_kvp, (const f16_t*)w.qn, (const f16_t*)w.qt, (const f16_t*)w.kn,
-                             (const f16_t*)w.vn, (const f16_t*)w.dOn, (const f16_t*)w.dOt, w.ld, w.cs, w.dmax,
-                             D.bwd_order, D.kv_off, D.kentries, D.page_table, D.page_nrows, (TG*)dk, (TG*)dv,
-                             stream);
+        launch_dkdv_mfma<TG>(s, n_kvp, (const f16_t*)w.qn, (const f16_t*)w.kn, (const f16_t*)w.vn,
+                             (const f16_t*)w.dOn, w.ld, w.cs, w.dmax, D.bwd_order, D.kv_off, D.kv_steps, D.kentries,
+                             D.page_table, D.page_nrows, (TG*)dk, (TG*)dv, stream);
       }
       {
         Span sp(P, DAG_K_DQ, stream);

@@ -579,157 +579,252 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
   }
 }
 
-// dK, dV for one KV page x one KV head.  Eight waves: wave w serves query head
-// 4 g + (w % 4) and the page's keys [32 (w / 4), 32 (w / 4) + 32), so two waves
-// share each SIMD and hide each other's load latency.  Each wave walks the page's
-// reader list in its fixed order, keeping its dK and dV slice in registers; the
-// four heads are then summed through LDS in head order and written once.
+// LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
+// lanes, lane i receives element i % 4 of the 8-byte pieces fetched by lanes
+// 4 j + i / 4 (j = 0..3).  So if source lane 4 j + q reads row (r0 + j) at
+// columns (c0 + 4 q .. + 3), lane i gets column c0 + i of rows r0 .. r0 + 3: a
+// column of the tile, as an MFMA operand wants it when the contraction runs
+// over rows.
+typedef __fp16 v4fp16 __attribute__((__vector_size__(8)));
+typedef __attribute__((address_space(3))) v4fp16 lds_v4fp16;
+
+// [32][128] row tiles staged for the dK/dV kernel use a bit-permuting swizzle:
+// chunk c of row r sits in slot c ^ f(r), f(r) = (r & 8) | ((r & 3) << 1) | ((r >> 2) & 1).
+// Sixteen consecutive rows hit sixteen different slots (row-fragment reads),
+// and four consecutive rows keep their 32-byte chunk pairs apart (transpose reads).
+__device__ __forceinline__ int swz32(int r) { return (r & 8) | ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ f16x8 frag_q(const f16_t* t, int r, int c) {
+  return ld8(t + r * 128 + ((c ^ swz32(r)) << 3));
+}
+// 8 contraction elements for the lane's column d of tile t, rows
+// 16 kk + {4 hi .. 4 hi + 3, 8 + 4 hi .. 8 + 4 hi + 3}: the order in which a 32x32
+// accumulator lane of half `hi` holds rows 16 kk .. 16 kk + 15.
+__device__ __forceinline__ f16x8 frag_tr(const f16_t* t, int kk, int dblk, int lane) {
+  const int G = lane >> 4, a = lane & 15;
+  const int col = dblk * 32 + (G & 1) * 16 + 4 * (a & 3);
+  const int c = col >> 3, w = col & 7;
+  f16x8 out;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = kk * 16 + half * 8 + 4 * (G >> 1) + (a >> 2);
+    const f16_t* p = t + row * 128 + ((c ^ swz32(row)) << 3) + w;
+    const v4fp16 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4fp16*)p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[half * 4 + j] = (f16_t)v[j];
+  }
+  return out;
+}
+
+// Sum one accumulator set (dK or dV, 64 keys x 128 d) over the work-group's four
+// waves in head order through LDS, scale it and write it out; dK is rotated back
+// by R(pos)^T.
+template <bool kRotate, typename TG>
+__device__ __forceinline__ void dkdv_reduce_store(const f32x16 (&acc)[2][4], float* red, int wave, int hi,
+                                                  int l32, int tid, int page, int g, int krows, int Hkv,
+                                                  float mul, const float2* __restrict__ cs, TG* __restrict__ out) {
+  for (int w = 0; w < 4; ++w) {
+    __syncthreads();
+    if (wave == w) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float* slot = red + (kb * 32 + acc_row(r, hi)) * (kD + 1) + b * 32 + l32;
+            *slot = (w == 0) ? acc[kb][b][r] : *slot + acc[kb][b][r];
+          }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 64 * 64; idx += 256) {
+    const int k2 = idx / 64, i = idx % 64;
+    const int64_t grow = (int64_t)page * 64 + k2;
+    float a = red[k2 * (kD + 1) + i] * mul, b = red[k2 * (kD + 1) + i + 64] * mul;
+    if (k2 >= krows) {
+      a = b = 0.f;
+    } else if (kRotate && cs) {
+      const float2 c = cs[grow * (kD / 2) + i];
+      const float a2 = a * c.x + b * c.y;
+      b = b * c.x - a * c.y;
+      a = a2;
+    }
+    TG* o = out + (grow * Hkv + g) * kD;
+    st_f(o + i, a);
+    st_f(o + i + 64, b);
+  }
+}
+
+// dK, dV for one KV page x one KV head.  Four waves = the four query heads of
+// the group; each owns all 64 keys of the page and keeps its dK and dV
+// (64 x 128 each) in accumulation registers across the page's whole reader
+// list, with the page's K and V fragments in registers too.  The reader list is
+// walked in steps of 32 query rows: each step stages the four heads' Q and dO
+// rows (and their (lse, D) pairs) in LDS with direct global loads, double
+// buffered; S and dP read row fragments from those tiles, dV and dK read
+// column fragments of the same tiles with the transpose read.  At the end the
+// four heads are summed through LDS in head order and written once:
+// deterministic, no atomics.
 template <typename TG>
-__global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
-    const f16_t* __restrict__ qn, const f16_t* __restrict__ qt, const f16_t* __restrict__ kn,
-    const f16_t* __restrict__ vn, const f16_t* __restrict__ dOn, const f16_t* __restrict__ dOt,
-    const float2* __restrict__ ldd, const float2* __restrict__ cs, const uint32_t* __restrict__ dmax,
-    const int32_t* __restrict__ order, const int32_t* __restrict__ kv_off, const KEntry* __restrict__ ents,
-    const int32_t* __restrict__ page_table, const int32_t* __restrict__ page_nrows, TG* __restrict__ dk,
-    TG* __restrict__ dv, int n_kvp, int Hq, int Hkv, float sl2, float scale) {
-  // K/V tiles during the walk; the same bytes hold the head reduction afterwards
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kSmemDkdv];
-  f16_t* lk = reinterpret_cast<f16_t*>(smem);
-  f16_t* lvv = lk + kTileRows;
-  float* red = reinterpret_cast<float*>(smem);
+__global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
+    const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vn,
+    const f16_t* __restrict__ dOn, const float2* __restrict__ ldd, const float2* __restrict__ cs,
+    const uint32_t* __restrict__ dmax, const int32_t* __restrict__ order, const int32_t* __restrict__ kv_off,
+    const int32_t* __restrict__ kv_steps, const KEntry* __restrict__ ents, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ page_nrows, TG* __restrict__ dk, TG* __restrict__ dv, int n_kvp, int Hq, int Hkv,
+    float sl2, float scale) {
+  constexpr int kStep = 32 * kD;  // elements of one [32][128] tile
+  // [buffer][head][Q, dO][32 x 128] f16, then [buffer][head][32] (lse, D); the
+  // first 33 KiB are reused for the head reduction at the end.  The page's V
+  // tile sits in its own [64][128] block.
+  __shared__ __attribute__((aligned(1024))) f16_t qd[2][4][2][kStep];
+  __shared__ __attribute__((aligned(1024))) f16_t lvp[kTile];
+  __shared__ __attribute__((aligned(16))) float2 lds_ld[2][4][32];
   int unit, g;
   if (!map_item(n_kvp, Hkv, unit, g)) return;
   const int page = order[unit];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int hh = wave & 3, kh = wave >> 2;
-  const int h = g * 4 + hh;
+  const int h = g * 4 + wave;
   const int krows = page_nrows[page];
-  const int key = kh * 32 + l32;  // the key this lane's accumulator columns belong to
 
+  // this page's K fragments (B operand of S = Q K^T) live in registers; its V
+  // tile (B operand of dP = dO V^T) in LDS
+  f16x8 kf[2][8];
   {
     const int64_t base = ((int64_t)page * Hkv + g) * 64 * kD;
-    for (int c = tid; c < 64 * 16; c += 512) {
-      const int r = c >> 4, col = (c & 15) * 8;
-      *reinterpret_cast<uint4*>(lk + r * kKStride + col) = *reinterpret_cast<const uint4*>(kn + base + c * 8);
-      *reinterpret_cast<uint4*>(lvv + r * kKStride + col) = *reinterpret_cast<const uint4*>(vn + base + c * 8);
-    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kf[kb][ks] = ld8(kn + base + (kb * 32 + l32) * kD + ks * 16 + hi * 8);
+    load_tile_rows(lvp, vn + base, wave, lane);
   }
-  __syncthreads();
+  f32x16 adk[2][4], adv[2][4];  // [key block][d block]
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) adk[a][b] = adv[a][b] = zero16();
 
-  f32x16 adk[4], adv[4];  // keys (this wave's 32) x d blocks of 32
+  // reader-list cursor: entry e, reader page lq, row block rb (32 rows)
+  const int n_steps = kv_steps[page];
+  int e = kv_off[page];
+  KEntry ent = ents[e];
+  int lq = ent.lq0, rb = 0;
+  int qph = page_table[ent.slot_base + lq];
+  auto stage = [&](int buf, int qp_, int rb_) {
+    // wave w fetches head 4 g + w: Q rows then dO rows, 8 KiB each = 8 + 8 wave loads
+    const int64_t src = (((int64_t)qp_ * Hq + g * 4 + wave) * 64 + rb_ * 32) * kD;
 #pragma unroll
-  for (int b = 0; b < 4; ++b) adk[b] = adv[b] = zero16();
-
-  const f16_t* Krow = lk + key * kKStride + hi * 8;
-  const f16_t* Vrow = lvv + key * kKStride + hi * 8;
-  for (int e = kv_off[page]; e < kv_off[page + 1]; ++e) {
-    const KEntry ent = ents[e];
-    const int lo = ent.lohi_diag & 0xff, hi_t = (ent.lohi_diag >> 8) & 0xff;
-    const bool diag = (ent.lohi_diag >> 16) & 1;
-    const bool key_ok = key >= lo && key < hi_t;
-    for (int lq = ent.lq0; lq < ent.lq1; ++lq) {
-      const int qph = page_table[ent.slot_base + lq];
-      const int nrows = page_nrows[qph];
-      const bool full = lo == 0 && hi_t == 64 && !diag && nrows == 64;
-      const int64_t hb = ((int64_t)qph * Hq + h) * 64 * kD;  // [64][128] and [128][64] blocks share offsets
-      const f16_t* qb = qn + hb;
-      const f16_t* qtb = qt + hb;
-      const f16_t* dnb = dOn + hb;
-      const f16_t* dtb = dOt + hb;
-      const float2* ldb = ldd + ((int64_t)qph * Hq + h) * 64;
-      for (int rb = 0; rb < 2; ++rb) {
-        if (rb * 32 >= nrows) break;
-        // this lane's 16 rows: rb*32 + acc_row(r, hi); fetch their (lse, D) first
-        float2 lr[16];
+    for (int t = 0; t < 2; ++t) {
+      const f16_t* gsrc = (t == 0 ? qn : dOn) + src;
+      f16_t* dst = qd[buf][wave][t];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) lr[r] = ldb[rb * 32 + acc_row(r, hi)];
-        // S = Q K^T and dP = dO V^T for 32 rows (M) x this wave's 32 keys (N)
-        f32x16 s = zero16(), dp = zero16();
-        const int arow = rb * 32 + l32;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          const f16x8 qa = ld8(qb + arow * kD + ks * 16 + hi * 8);
-          const f16x8 da = ld8(dnb + arow * kD + ks * 16 + hi * 8);
-          s = mfma(qa, ld8(Krow + ks * 16), s);
-          dp = mfma(da, ld8(Vrow + ks * 16), dp);
-        }
-        // P and dS; this lane holds key `key` and rows rb*32 + acc_row(r, hi)
-        if (full) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr[r].x));
-            s[r] = p;
-            dp[r] = p * (dp[r] - lr[r].y);
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = rb * 32 + acc_row(r, hi);
-            const bool ok = key_ok && (!diag || key <= row) && row < nrows;
-            const float p = ok ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr[r].x)) : 0.f;
-            s[r] = p;
-            dp[r] = ok ? p * (dp[r] - lr[r].y) : 0.f;  // padding may hold NaN
-          }
-        }
-        const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8), sf0 = pack8(dp, 0), sf1 = pack8(dp, 8);
-        // dV += P^T dO, dK += dS^T Q (keys = M, d = N, rows = contraction)
-        const int col = rb * 32 + hi * 8;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const f16_t* dt = dtb + (b * 32 + l32) * 64 + col;
-          const f16_t* qtt = qtb + (b * 32 + l32) * 64 + col;
-          adv[b] = mfma(pf0, ld8(dt), adv[b]);
-          adv[b] = mfma(pf1, ld8(dt + 16), adv[b]);
-          adk[b] = mfma(sf0, ld8(qtt), adk[b]);
-          adk[b] = mfma(sf1, ld8(qtt + 16), adk[b]);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const int q = i * 64 + lane;  // 16-byte slot
+        const int r = q >> 4, c = (q & 15) ^ swz32(r);
+        __builtin_amdgcn_global_load_lds(gsrc + r * kD + c * 8, (lds_void*)(dst + i * 512), 16, 0, 0);
       }
     }
+    if (lane < 16)
+      __builtin_amdgcn_global_load_lds(ldd + ((int64_t)qp_ * Hq + g * 4 + wave) * 64 + rb_ * 32 + lane * 2,
+                                       (lds_void*)(&lds_ld[buf][wave][0]), 16, 0, 0);
+  };
+  stage(0, qph, 0);
+  wait_all_loads();
+  __syncthreads();
+
+  int buf = 0;
+  for (int it = 0; it < n_steps; ++it) {
+    // where the next step is (a reader page of <= 32 rows has one row block)
+    const bool more = it + 1 < n_steps;
+    int n_e = e, n_lq = lq, n_rb = rb + 1, n_qph = qph;
+    const int nrows = page_nrows[qph];
+    if (n_rb == 2 || n_rb * 32 >= nrows) {
+      n_rb = 0;
+      if (++n_lq == ent.lq1) {
+        ++n_e;
+        if (more) n_lq = ents[n_e].lq0;
+      }
+      if (more) n_qph = page_table[ents[n_e].slot_base + n_lq];
+    }
+    if (more) stage(buf ^ 1, n_qph, n_rb);
+
+    const int lo = ent.lohi_diag & 0xff, hi_t = (ent.lohi_diag >> 8) & 0xff;
+    const bool diag = (ent.lohi_diag >> 16) & 1;
+    const bool full = lo == 0 && hi_t == 64 && !diag && nrows >= rb * 32 + 32;
+    const f16_t* Qt = qd[buf][wave][0];
+    const f16_t* Dt = qd[buf][wave][1];
+    const float2* LD = lds_ld[buf][wave];
+    // S = Q K^T, dP = dO V^T: 32 rows (M) x 64 keys (N, two blocks); lane holds keys
+    // kb*32 + l32 and rows rb*32 + acc_row(r, hi)
+    f32x16 sa[2], dpa[2];
+    sa[0] = sa[1] = dpa[0] = dpa[1] = zero16();
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const f16x8 qa = frag_q(Qt, l32, ks * 2 + hi), da = frag_q(Dt, l32, ks * 2 + hi);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        sa[kb] = mfma(qa, kf[kb][ks], sa[kb]);
+        dpa[kb] = mfma(da, frag_rows(lvp, kb * 32 + l32, ks * 2 + hi), dpa[kb]);
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16& s = sa[kb];
+      f32x16& dp = dpa[kb];
+      const int key = kb * 32 + l32;
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float2 lr = LD[acc_row(r, hi)];
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr.x));
+          s[r] = p;
+          dp[r] = p * (dp[r] - lr.y);
+        }
+      } else {
+        // every operand here comes from the zero-padded relayouts, so all values are
+        // finite and a 0/1 factor masks without branches
+        const bool key_ok = key >= lo && key < hi_t;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float2 lr = LD[acc_row(r, hi)];
+          const int row = rb * 32 + acc_row(r, hi);
+          const float okf = (key_ok && (!diag || key <= row) && row < nrows) ? 1.f : 0.f;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr.x)) * okf;
+          s[r] = p;
+          dp[r] = p * (dp[r] - lr.y);
+        }
+      }
+      const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8), sf0 = pack8(dp, 0), sf1 = pack8(dp, 8);
+      // dV += P^T dO, dK += dS^T Q: keys (M) x d (N), the 32 rows contracted
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        // a compiler-only fence per block: without it the scheduler hoists every
+        // block's fragment reads at once and runs out of registers
+        asm volatile("" ::: "memory");
+        adv[kb][b] = mfma(pf0, frag_tr(Dt, 0, b, lane), adv[kb][b]);
+        adv[kb][b] = mfma(pf1, frag_tr(Dt, 1, b, lane), adv[kb][b]);
+        adk[kb][b] = mfma(sf0, frag_tr(Qt, 0, b, lane), adk[kb][b]);
+        adk[kb][b] = mfma(sf1, frag_tr(Qt, 1, b, lane), adk[kb][b]);
+      }
+    }
+    wait_all_loads();
+    __syncthreads();
+    buf ^= 1;
+    if (more && n_e != e) ent = ents[n_e];
+    e = n_e;
+    lq = n_lq;
+    rb = n_rb;
+    qph = n_qph;
   }
 
   const float inv_sdo = 1.f / pow2_scale(*dmax);  // undo the dO scaling
-  // sum the four heads in order 0..3 through LDS (both key halves at once), then
-  // write dk (un-rotated) and dv
-  for (int which = 0; which < 2; ++which) {
-    for (int w = 0; w < 4; ++w) {
-      __syncthreads();
-      if (hh == w) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int k2 = kh * 32 + acc_row(r, hi);
-            const int d = b * 32 + l32;
-            const float x = which == 0 ? adk[b][r] : adv[b][r];
-            float* slot = red + k2 * (kD + 1) + d;
-            *slot = (w == 0) ? x : *slot + x;
-          }
-      }
-    }
-    __syncthreads();
-    for (int idx = tid; idx < 64 * 64; idx += 512) {
-      const int k2 = idx / 64, i = idx % 64;
-      const int64_t grow = (int64_t)page * 64 + k2;
-      float a = red[k2 * (kD + 1) + i] * inv_sdo, b = red[k2 * (kD + 1) + i + 64] * inv_sdo;
-      if (k2 >= krows) {
-        a = b = 0.f;
-      } else if (which == 0) {
-        a *= scale;
-        b *= scale;
-        if (cs) {
-          const float2 c = cs[grow * (kD / 2) + i];
-          const float a2 = a * c.x + b * c.y;
-          b = b * c.x - a * c.y;
-          a = a2;
-        }
-      }
-      TG* out = (which == 0 ? dk : dv) + (grow * Hkv + g) * kD;
-      st_f(out + i, a);
-      st_f(out + i + 64, b);
-    }
-  }
+  float* red = reinterpret_cast<float*>(&qd[0][0][0][0]);  // [64][129] fp32
+  // sum the four heads in order 0..3 through LDS, then write dk (scaled, un-rotated)
+  // and dv
+  dkdv_reduce_store<true>(adk, red, wave, hi, l32, tid, page, g, krows, Hkv, inv_sdo * scale, cs, dk);
+  dkdv_reduce_store<false>(adv, red, wave, hi, l32, tid, page, g, krows, Hkv, inv_sdo, cs, dv);
 }
 
 // ---------------------------------------------------------------------------
@@ -970,12 +1065,12 @@ void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f
 }
 
 template <typename TG>
-void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, const f16_t* qt, const f16_t* kn,
-                      const f16_t* vn, const f16_t* dOn, const f16_t* dOt, const float2* ld, const float2* cs,
-                      const uint32_t* dmax, const int32_t* order, const int32_t* kv_off, const KEntry* ents,
+void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, const f16_t* kn, const f16_t* vn,
+                      const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
+                      const int32_t* order, const int32_t* kv_off, const int32_t* kv_steps, const KEntry* ents,
                       const int32_t* page_table, const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st) {
-  dkdv_mfma_kernel<TG><<<run_grid(n_kvp, s.Hkv), 512, 0, st>>>(qn, qt, kn, vn, dOn, dOt, ld, cs, dmax, order,
-                                                               kv_off, ents, page_table, page_nrows, dk, dv,
+  dkdv_mfma_kernel<TG><<<run_grid(n_kvp, s.Hkv), 256, 0, st>>>(qn, kn, vn, dOn, ld, cs, dmax, order, kv_off,
+                                                               kv_steps, ents, page_table, page_nrows, dk, dv,
                                                                (int)n_kvp, s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
 }
 
@@ -984,8 +1079,8 @@ void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, cons
                                    const f16_t*, const f16_t*, const float2*, const float2*, const uint32_t*,  \
                                    const QPage*, const int32_t*, const Tile*, TG*, hipStream_t);               \
   template void launch_dkdv_mfma<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,    \
-                                     const f16_t*, const f16_t*, const f16_t*, const float2*, const float2*,   \
-                                     const uint32_t*, const int32_t*, const int32_t*, const KEntry*,           \
+                                     const f16_t*, const float2*, const float2*, const uint32_t*,              \
+                                     const int32_t*, const int32_t*, const int32_t*, const KEntry*,            \
                                      const int32_t*, const int32_t*, TG*, TG*, hipStream_t);
 INST_MFMA_BWD(bf16_t)
 INST_MFMA_BWD(float)

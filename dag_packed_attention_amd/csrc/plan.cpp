@@ -310,6 +310,18 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
     for_each_entry([&](int32_t ph, const KEntry& e) { P->kentries[fill[ph]++] = e; });
   }
 
+  // 32-row reader blocks per KV page (the dK/dV kernel's loop count)
+  P->kv_steps.assign(n_pages, 0);
+  for (int32_t ph = 0; ph < n_pages; ++ph) {
+    int64_t steps = 0;
+    for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
+      const KEntry& k = P->kentries[e];
+      for (int32_t lq = k.lq0; lq < k.lq1; ++lq) steps += P->page_nrows[P->page_table[k.slot_base + lq]] > 32 ? 2 : 1;
+    }
+    if (steps > INT32_MAX) return fail(err, DAG_E_OVERFLOW, "reader list too long");
+    P->kv_steps[ph] = (int32_t)steps;
+  }
+
   // ---- 9. launch orders -------------------------------------------------------------
   // Node-grouped, heaviest first: nodes sorted by their heaviest page's work, each
   // node's pages listed together (heaviest first).  Neighbouring work-groups then

@@ -63,6 +63,7 @@ struct Plan {
   std::vector<QPage> qpages;
   std::vector<int32_t> fwd_order;              // query-page ids, heaviest first
   std::vector<int32_t> kv_off;                 // physical page -> first reader entry (size pages+1)
+  std::vector<int32_t> kv_steps;               // physical page -> 32-row reader blocks over its list
   std::vector<KEntry> kentries;
   std::vector<int32_t> bwd_order;              // physical pages with rows, heaviest first
   std::vector<int32_t> pos_of_row;             // C
