@@ -176,6 +176,8 @@ def main() -> int:
     ap.add_argument("--flat-steps", type=int, default=1)
     ap.add_argument("--no-flat", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB -> 1 GiB device copy kernel 3 times (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus "
@@ -189,6 +191,15 @@ def main() -> int:
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)                              # one elementwise kernel: 1 GiB in, 1 GiB out
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
+                                               "launches": 3}}))
+        return 0
     t0 = time.perf_counter()
     spec = synth.config3()
     plan = dpa.Plan(spec)
