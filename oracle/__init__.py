@@ -19,8 +19,16 @@ rounding order):
                    brute force (explicit loops), flat per-trajectory dense causal
                    attention (the reference), a dense packed mask, and per-row /
                    per-key evaluations for sampling large inputs.
+* ``gdn``       -- the gated delta rule over the same tree as a plain token
+                   recurrence per root-to-leaf trajectory (mounted spans
+                   skipped), with back-propagation through time.
+* ``gdn_plan``  -- HARTS's minimum-call planning of chunked linear-attention
+                   execution: segment tree, T_pre / T_in, the recovery of
+                   rounds, mandatory replay, and a brute-force minimum.
 
 Parity unpinned: the RoPE pairing convention (first half / second half of the
 head dimension) and the frequency base (10000) are a textbook choice the pages
-do not fix; both sides take them as parameters.
+do not fix; both sides take them as parameters.  Likewise the gated delta
+rule's parameterisation and its output scale (default 1): the pages name the
+layer but print no recurrence for it.
 """

@@ -39,3 +39,29 @@ def attn_inputs(n_tokens: int, hq: int, hkv: int, d: int, seed: int, device="cpu
     v = normal((n_tokens, hkv, d), seed, STREAM_V, device, dtype)
     do = normal((n_tokens, hq, d), seed, STREAM_DO, device, dtype) if with_grad else None
     return q, k, v, do
+
+
+STREAM_GQ, STREAM_GK, STREAM_GV, STREAM_GBETA, STREAM_GALPHA, STREAM_GDO = 11, 12, 13, 14, 15, 16
+
+
+def gdn_inputs(n_tokens: int, h: int, dk: int, dv: int, seed: int, device="cpu",
+               dtype=torch.float32, decay_scale: float = 1.0, with_grad: bool = True):
+    """Inputs of one gated-delta-rule layer, token-major.
+
+    q, k [U,H,dk]: standard normal, each head's vector divided by its L2 norm
+    (the layer receives normalised queries and keys); v [U,H,dv] standard
+    normal; beta [U,H] = sigmoid(N(0,1)); alpha [U,H] = exp(-decay_scale *
+    softplus(N(0,1))) (decay_scale < 1 gives slower decay, so that state carries
+    across many chunks); dO [U,H,dv] standard normal.  q, k, v, dO are rounded
+    to ``dtype`` after normalisation; beta and alpha stay float32.
+    """
+    def unit(x):
+        return x / x.norm(dim=-1, keepdim=True)
+    q = unit(normal((n_tokens, h, dk), seed, STREAM_GQ, device)).to(dtype)
+    k = unit(normal((n_tokens, h, dk), seed, STREAM_GK, device)).to(dtype)
+    v = normal((n_tokens, h, dv), seed, STREAM_GV, device, dtype)
+    beta = torch.sigmoid(normal((n_tokens, h), seed, STREAM_GBETA, device))
+    alpha = torch.exp(-decay_scale * torch.nn.functional.softplus(normal((n_tokens, h), seed, STREAM_GALPHA,
+                                                                          device)))
+    do = normal((n_tokens, h, dv), seed, STREAM_GDO, device, dtype) if with_grad else None
+    return q, k, v, beta, alpha, do
