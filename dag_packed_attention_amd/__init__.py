@@ -39,14 +39,23 @@ class DagMount(ctypes.Structure):
 
 class DagBuildOpts(ctypes.Structure):
     _fields_ = [("page_size", ctypes.c_int32), ("q_block", ctypes.c_int32),
-                ("transitive", ctypes.c_int32), ("page_shuffle", ctypes.c_int32)]
+                ("transitive", ctypes.c_int32), ("page_shuffle", ctypes.c_int32),
+                ("gdn_chunk", ctypes.c_int32)]
 
 
 class DagPlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("rows", "tokens", "pages", "query_pages", "visible_pairs",
                                              "flat_rows", "flat_pairs", "n_trajectories", "fwd_tiles",
                                              "bwd_entries")] + \
-               [("max_position", ctypes.c_int32), ("transitive", ctypes.c_int32)]
+               [("max_position", ctypes.c_int32), ("transitive", ctypes.c_int32),
+                ("gdn_chunk", ctypes.c_int32), ("gdn_rounds", ctypes.c_int32)] + \
+               [(n, ctypes.c_int64) for n in ("gdn_sequences", "gdn_replay", "gdn_slots", "gdn_chunks",
+                                             "gdn_segments")]
+
+
+class DagGdnSeq(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("round", "first_node", "last_node", "start", "fork",
+                                             "own_tokens", "init_seq", "init_boundary")]
 
 
 class DagAttnParams(ctypes.Structure):
@@ -77,6 +86,7 @@ def _load() -> ctypes.CDLL:
         "dag_plan_starts": ([P, P], I32),
         "dag_plan_node_ranges": ([P, I32, P, I32, ctypes.POINTER(I32)], I32),
         "dag_plan_upload": ([P, P], I32),
+        "dag_plan_gdn_seqs": ([P, P, I32, ctypes.POINTER(I32)], I32),
         "dag_attn_workspace": ([P, ctypes.POINTER(DagAttnParams), ctypes.POINTER(SZ),
                                 ctypes.POINTER(SZ)], I32),
         "dag_attn_fwd": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, P, SZ, P], I32),
@@ -113,7 +123,7 @@ class Plan:
     tables as attributes ``parent, length, mount_first, mount_count, mount_src,
     mount_begin, mount_end``."""
 
-    def __init__(self, spec, transitive: Optional[bool] = None, page_shuffle: int = 0):
+    def __init__(self, spec, transitive: Optional[bool] = None, page_shuffle: int = 0, gdn_chunk: int = 0):
         if transitive is None:
             transitive = bool(getattr(spec, "meta", {}).get("transitive", True))
         n = len(spec.parent)
@@ -125,7 +135,7 @@ class Plan:
         mounts = (DagMount * max(m, 1))()
         for i in range(m):
             mounts[i] = DagMount(int(spec.mount_src[i]), int(spec.mount_begin[i]), int(spec.mount_end[i]))
-        opts = DagBuildOpts(64, 64, 1 if transitive else 0, int(page_shuffle))
+        opts = DagBuildOpts(64, 64, 1 if transitive else 0, int(page_shuffle), int(gdn_chunk))
         self._h = ctypes.c_void_p()
         _check(_lib.dag_build(nodes, n, mounts, m, ctypes.byref(opts), ctypes.byref(self._h)))
         info = DagPlanInfo()
@@ -169,6 +179,14 @@ class Plan:
         buf = np.zeros(max(3 * n.value, 3), np.int32)
         _check(_lib.dag_plan_node_ranges(self._h, int(u), buf.ctypes.data, n.value, ctypes.byref(n)))
         return [tuple(int(x) for x in buf[3 * i: 3 * i + 3]) for i in range(n.value)]
+
+    def gdn_seqs(self):
+        """The linear-attention schedule's sequences (``dag_plan_gdn_seqs``) as dicts."""
+        n = ctypes.c_int32(0)
+        _check(_lib.dag_plan_gdn_seqs(self._h, None, 0, ctypes.byref(n)))
+        buf = (DagGdnSeq * max(n.value, 1))()
+        _check(_lib.dag_plan_gdn_seqs(self._h, buf, n.value, ctypes.byref(n)))
+        return [{f: getattr(buf[i], f) for f, _ in DagGdnSeq._fields_} for i in range(n.value)]
 
     def upload(self, stream=None) -> None:
         _check(_lib.dag_plan_upload(self._h, _stream_ptr(stream)))

@@ -2,7 +2,7 @@
 
     python dag_packed_attention_amd/build_lib.py      (or call build())
 
-The host compactor (plan.cpp) is plain C++ and is compiled with g++; the ABI
+The host compactor (plan.cpp, gdn_plan.cpp) is plain C++ and is compiled with g++; the ABI
 glue and the kernels are compiled with hipcc for gfx950.  Packed-fp32 code
 generation is switched off for the device code.
 """
@@ -34,11 +34,15 @@ def _run(cmd):
     return r
 
 
+OBJS = ("plan.o", "gdn_plan.o", "abi.o", "kernels.o")
+
+
 def build(verbose: bool = False) -> str:
     obj_dir = os.path.join(HERE, "_build")
     os.makedirs(obj_dir, exist_ok=True)
     steps = [
         ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "plan.cpp"), "-o", os.path.join(obj_dir, "plan.o")],
+        ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "gdn_plan.cpp"), "-o", os.path.join(obj_dir, "gdn_plan.o")],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "abi.cpp"), "-o", os.path.join(obj_dir, "abi.o")],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "kernels.hip"), "-o", os.path.join(obj_dir, "kernels.o")],
     ]
@@ -48,7 +52,7 @@ def build(verbose: bool = False) -> str:
                 sys.stderr.write(r.stderr)
     tmp = LIB + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp,
-          *(os.path.join(obj_dir, f) for f in ("plan.o", "abi.o", "kernels.o"))])
+          *(os.path.join(obj_dir, f) for f in OBJS)])
     os.replace(tmp, LIB)
     return LIB
 

@@ -326,6 +326,15 @@ dag_status dag_plan_node_ranges(const dag_plan* plan, int32_t u, int32_t* out, i
   return DAG_OK;
 }
 
+dag_status dag_plan_gdn_seqs(const dag_plan* plan, dag_gdn_seq* out, int32_t cap, int32_t* n) {
+  if (!plan || !n) return set_err(DAG_E_INVALID, "null argument");
+  const Plan& P = plan->p;
+  if (P.info.gdn_chunk <= 0) return set_err(DAG_E_INVALID, "plan was built without a linear-attention schedule");
+  *n = (int32_t)P.gseq_info.size();
+  for (int32_t i = 0; out && i < *n && i < cap; ++i) out[i] = P.gseq_info[i];
+  return DAG_OK;
+}
+
 dag_status dag_attn_timing_enable(dag_plan* plan, int32_t enable, int32_t capacity) {
   if (!plan) return set_err(DAG_E_INVALID, "null plan");
   destroy_timing(plan->p);

@@ -204,7 +204,7 @@ constexpr int kTStride = 64 + 8;   // LDS row stride (16-bit elements) of a [128
 constexpr int kTileRows = 64 * kKStride;  // elements of a staged [64][128] tile
 constexpr int kTileCols = kD * kTStride;  // elements of a staged [128][64] tile
 // dK/dV work-group LDS: the K and V tiles, later overlaid by the [64][129] fp32 head sum
-constexpr int kSmemDkdv = (2 * kTileRows * 2 > 64 * (kD + 1) * 4) ? 2 * kTileRows * 2 : 64 * (kD + 1) * 4;
+
 constexpr int kRun = 8;  // consecutive units of one head that go to one XCD
 
 __device__ __forceinline__ f32x16 mfma(const f16x8& a, const f16x8& b, const f32x16& c) {

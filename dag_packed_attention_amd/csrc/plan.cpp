@@ -17,7 +17,8 @@
 //   8. per-KV-page reader lists in a fixed order (the deterministic order in
 //      which the backward sums reader contributions into producer pages,
 //      Octopus Sec. 3.4 Eq. 8, HARTS Sec. 3.4);
-//   9. launch orders: node-grouped, heaviest first.
+//   9. launch orders: node-grouped, heaviest first;
+//  10. optionally, the chunked linear-attention schedule (gdn_plan.cpp).
 #include "plan.hpp"
 
 #include <algorithm>
@@ -61,7 +62,7 @@ uint64_t splitmix64(uint64_t& s) {
 dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts, int32_t nm,
                       const dag_build_opts* opts_in, Plan* P, std::string* err) {
   // ---- options ----------------------------------------------------------
-  dag_build_opts opts{64, 64, 1, 0};
+  dag_build_opts opts{64, 64, 1, 0, 0};
   if (opts_in) opts = *opts_in;
   if (opts.page_size == 0) opts.page_size = kPage;
   if (opts.q_block == 0) opts.q_block = kPage;
@@ -70,6 +71,8 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
                 opts.page_size, opts.q_block);
   if (opts.transitive != 0 && opts.transitive != 1)
     return fail(err, DAG_E_INVALID, "transitive must be 0 or 1");
+  if (opts.gdn_chunk < 0 || opts.gdn_chunk > 4096)
+    return fail(err, DAG_E_INVALID, "gdn_chunk must be in [0, 4096] (got %lld)", opts.gdn_chunk);
   P->opts = opts;
 
   // ---- 1. validation ------------------------------------------------------
@@ -397,6 +400,7 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
   }
   for (const QPage& q : P->qpages) I.fwd_tiles += q.tile_count;
   I.bwd_entries = (int64_t)P->kentries.size();
+  if (opts.gdn_chunk > 0) return build_gdn_schedule(P, opts.gdn_chunk, err);
   return DAG_OK;
 }
 

@@ -42,6 +42,25 @@ struct KEntry {
   int32_t lohi_diag;  // lo | (hi << 8) | (diag << 16)
 };
 
+// One packed gated-delta-rule input sequence as the kernels read it.  Its
+// tokens are rows[tok_off .. tok_off + n_tok): n_replay replayed ancestor
+// tokens (state updates only), then its own tokens.  Token j sits at
+// recurrent index start + j; start is a multiple of the chunk, so chunk c of
+// the sequence is tokens [c B, c B + B).
+struct GSeq {
+  int32_t tok_off, n_tok, n_replay, start;
+  int32_t init_slot;  // boundary state it starts from; -1: zero
+  int32_t cgrad;      // index of its initial-state gradient buffer; -1 when init_slot < 0
+  int32_t exp_off, exp_cnt;  // its exported boundary states: gexports[exp_off ..)
+  int32_t chunk_off;  // first entry of its per-chunk saved states
+  int32_t round, pad0, pad1;
+};
+// An exported boundary: the state after `chunk` chunks of the sequence goes to `slot`.
+struct GExport {
+  int32_t chunk;
+  int32_t slot;
+};
+
 struct DeviceTables;  // defined by the HIP side
 struct Timing;        // defined by the HIP side
 
@@ -68,6 +87,15 @@ struct Plan {
   std::vector<int32_t> bwd_order;              // physical pages with rows, heaviest first
   std::vector<int32_t> pos_of_row;             // C
   std::vector<int32_t> row_of_token;           // U
+  // gated-delta-rule schedule (empty when opts.gdn_chunk == 0)
+  std::vector<dag_gdn_seq> gseq_info;          // per sequence, for queries
+  std::vector<GSeq> gseqs;
+  std::vector<int32_t> grows;                  // compact row of each sequence token
+  std::vector<GExport> gexports;
+  std::vector<int32_t> gslot_off, gslot_cons;  // slot -> consumers' cgrad ids, sequence order
+  std::vector<int32_t> ground_off, ground_seq; // round r (0-based) -> sequences, most tokens first
+  std::vector<int32_t> grep_rows, grep_off, grep_tok;  // replay fix-up: row -> token indices into grows
+  int32_t gdn_ncgrad = 0;
   dag_plan_info info{};
   DeviceTables* dev = nullptr;
   Timing* timing = nullptr;
@@ -76,5 +104,9 @@ struct Plan {
 // Compile; returns DAG_OK or an error code with a message in `err`.
 dag_status build_plan(const dag_node* nodes, int32_t n_nodes, const dag_mount* mounts,
                       int32_t n_mounts, const dag_build_opts* opts, Plan* out, std::string* err);
+
+// Linear-attention schedule (HARTS Sec. 3.3) over the plan's parent tree;
+// needs the plan's rows (row_of_token) to be built.
+dag_status build_gdn_schedule(Plan* P, int32_t chunk, std::string* err);
 
 }  // namespace dagattn

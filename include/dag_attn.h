@@ -83,6 +83,9 @@ typedef struct {
                         /*    Sec. 3.3 item 1, "including transitive mounts"); 0: direct */
   int32_t page_shuffle; /* 0: pages in node order; otherwise a seed for a random physical */
                         /*    page assignment (the page table stays exact)               */
+  int32_t gdn_chunk;    /* 0: no linear-attention schedule; B > 0: also plan the chunked  */
+                        /*    gated-delta-rule execution with chunk length B (HARTS Sec.  */
+                        /*    3.3; the GDN kernels take B = 64 only)                      */
 } dag_build_opts;
 
 typedef struct dag_plan dag_plan; /* opaque and immutable after dag_build */
@@ -100,6 +103,14 @@ typedef struct {
   int64_t bwd_entries;     /* reader-list entries over all KV pages                    */
   int32_t max_position;    /* largest Eq. 2 position                                  */
   int32_t transitive;
+  /* linear-attention schedule (zero when gdn_chunk == 0) */
+  int32_t gdn_chunk;       /* B                                                       */
+  int32_t gdn_rounds;      /* sequential packed calls (HARTS T_pre of the roots)      */
+  int64_t gdn_sequences;   /* packed input sequences over all rounds                  */
+  int64_t gdn_replay;      /* R: replayed state-update positions (HARTS Eq. 15)       */
+  int64_t gdn_slots;       /* exported boundary states                                */
+  int64_t gdn_chunks;      /* execution chunks over all sequences, replay included    */
+  int64_t gdn_segments;    /* fork-free segments of the (mount-free) tree             */
 } dag_plan_info;
 
 /* Validate the node/mount tables and compile them into a plan.  Host only;
@@ -185,9 +196,78 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
                         const void* dO, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
                         void* hip_stream);
 
+/* ---- Gated delta rule over the same tree (HARTS Sec. 2.2 and 3.3-3.4) ----------
+ *
+ * A recurrent layer follows each token's own root-to-node path; mounted spans
+ * are not part of it (Octopus Sec. 3: read_thread only changes what attention
+ * sees).  Per head, with state S of shape [dv, dk], S = 0 at every root:
+ *   S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = scale S_t q_t.
+ * The pages name the layer but print no recurrence; this is the textbook gated
+ * delta rule.  Execution is chunked (B = 64 tokens per chunk, chunk boundaries
+ * on the recurrent index, HARTS Eq. 2): the plan contracts the tree into
+ * fork-free segments, picks each fork's direct continuation so that the number
+ * of sequential rounds is minimal (HARTS Eq. 12-14, Algorithm 1), and starts
+ * every other branch from the state at the chunk boundary a(fork) = B floor(fork / B),
+ * re-running the ancestor tokens [a(fork), fork) state-only ("replay", HARTS
+ * Eq. 15).  All sequences of a round run in one launch; boundary states pass
+ * between rounds through the workspace and their gradients flow back into the
+ * producing sequence (HARTS Sec. 3.4 Eq. 16). */
+
+/* One packed input sequence of the schedule.  Its own tokens are the path from
+ * first_node to last_node (a chain of direct continuations); before them it
+ * replays the ancestor positions [start, fork). */
+typedef struct {
+  int32_t round;         /* 1-based round (packed call) it runs in                      */
+  int32_t first_node;    /* DAG node where its own tokens begin                         */
+  int32_t last_node;     /* DAG node where they end (a leaf)                            */
+  int32_t start;         /* recurrent index of its first (replayed) token, a multiple of B */
+  int32_t fork;          /* recurrent index of its first own token                      */
+  int32_t own_tokens;
+  int32_t init_seq;      /* sequence whose exported state it starts from; -1: zero state */
+  int32_t init_boundary; /* recurrent index of that state (a multiple of B), -1 if none  */
+} dag_gdn_seq;
+
+/* The schedule's sequences in creation order (trees in table order; within a
+ * tree, the recovery's depth-first order).  Writes min(cap, count) entries and
+ * the count into *n.  DAG_E_INVALID if the plan was built with gdn_chunk == 0. */
+dag_status dag_plan_gdn_seqs(const dag_plan* plan, dag_gdn_seq* out, int32_t cap, int32_t* n);
+
+typedef struct {
+  int32_t n_heads;     /* H                                                      */
+  int32_t head_dim;    /* dk = dv; must be 128                                   */
+  int32_t dtype;       /* q, k, v, o, dO element type; must be DAG_DTYPE_BF16    */
+  int32_t grad_dtype;  /* dq, dk, dv: DAG_DTYPE_BF16 or DAG_DTYPE_FP32           */
+  float scale;         /* output scale; 0 selects 1                              */
+} dag_gdn_params;
+
+/* Workspace bytes for dag_gdn_fwd and dag_gdn_bwd. */
+dag_status dag_gdn_workspace(const dag_plan* plan, const dag_gdn_params* p, size_t* fwd_bytes,
+                             size_t* bwd_bytes);
+
+/* Forward: q, k [C, H, dk] (each head's vector already L2-normalised by the
+ * caller), v [C, H, dv] (dtype); beta, alpha [C, H] fp32 (beta in [0, 1], alpha in (0, 1]);
+ * o [C, H, dv] (dtype) receives every token's output once.  One launch per
+ * round; products on MFMA with fp16 operands and fp32 accumulation, state in
+ * fp32.  ws: at least fwd_bytes. */
+dag_status dag_gdn_fwd(dag_plan* plan, const dag_gdn_params* p, const void* q, const void* k,
+                       const void* v, const float* beta, const float* alpha, void* o, void* ws,
+                       size_t ws_bytes, void* hip_stream);
+
+/* Backward given dO [C, H, dv]: dq, dk [C, H, dk], dv [C, H, dv] (grad_dtype),
+ * dbeta, dalpha [C, H] fp32.  Rounds run in reverse; the gradient of each
+ * exported boundary state is the sum over its consumers in a fixed order, and a
+ * replayed token's contributions are added to its own row after its own
+ * sequence's, in a fixed order: results are bitwise reproducible.  Recomputes
+ * the forward's states; ws: at least bwd_bytes. */
+dag_status dag_gdn_bwd(dag_plan* plan, const dag_gdn_params* p, const void* q, const void* k,
+                       const void* v, const float* beta, const float* alpha, const void* dO,
+                       void* dq, void* dk, void* dv, float* dbeta, float* dalpha, void* ws,
+                       size_t ws_bytes, void* hip_stream);
+
 /* Per-kernel timing, for profiling.  While enabled, dag_attn_fwd/bwd record a
  * HIP event pair on their stream around each of their kernels (at most
  * `capacity` pairs, created here; later launches go unrecorded).
+ * The same holds for dag_gdn_fwd/bwd.
  * dag_attn_timing_read waits for the recorded events, writes for each kernel
  * k in dag_kernel_id the summed duration ms[k] (milliseconds) and the number of
  * launches counts[k] since the last read, and resets.  Disabling (enable = 0)
@@ -198,7 +278,10 @@ enum {
   DAG_K_PROLOGUE_BWD = 2, /* rotary table, rowsum(dO * O) and relayouts          */
   DAG_K_DKDV = 3,         /* per-KV-page dK/dV reduction                          */
   DAG_K_DQ = 4,           /* per-query-block dQ                                   */
-  DAG_K_COUNT = 5
+  DAG_K_GDN_FWD = 5,      /* gated delta rule forward, all rounds                  */
+  DAG_K_GDN_STATES = 6,   /* backward's recomputation of chunk and boundary states */
+  DAG_K_GDN_BWD = 7,      /* gated delta rule backward, all rounds, and replay fix-up */
+  DAG_K_COUNT = 8
 };
 dag_status dag_attn_timing_enable(dag_plan* plan, int32_t enable, int32_t capacity);
 dag_status dag_attn_timing_read(dag_plan* plan, double* ms, int64_t* counts);

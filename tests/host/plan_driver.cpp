@@ -41,6 +41,44 @@ static int check(const Plan& P) {
   return 0;
 }
 
+// Linear-attention schedule: every token row lies in the plan, every own token
+// appears once, exports fall inside their producer, consumers and fix-up lists
+// index valid entries.
+static int check_gdn(const Plan& P) {
+  const int B = P.info.gdn_chunk;
+  if (B <= 0) return 0;
+  const int64_t C = P.info.rows;
+  std::vector<int> own(C, 0);
+  const int NS = (int)P.gseqs.size();
+  const int nslots = (int)P.gslot_off.size() - 1;
+  for (int q = 0; q < NS; ++q) {
+    const GSeq& g = P.gseqs[q];
+    if (g.tok_off < 0 || g.n_tok <= g.n_replay || g.tok_off + g.n_tok > (int64_t)P.grows.size()) return 31;
+    if (g.start % B || g.n_replay >= B) return 32;
+    for (int j = 0; j < g.n_tok; ++j) {
+      const int r = P.grows[g.tok_off + j];
+      if (r < 0 || r >= C || P.pos_of_row[r] < 0) return 33;
+      if (j >= g.n_replay) own[r]++;
+    }
+    const int nch = (g.n_tok + B - 1) / B;
+    for (int e = g.exp_off; e < g.exp_off + g.exp_cnt; ++e) {
+      if (P.gexports[e].chunk < 1 || P.gexports[e].chunk > nch) return 34;
+      if (P.gexports[e].slot < 0 || P.gexports[e].slot >= nslots) return 35;
+      if (e > g.exp_off && P.gexports[e].chunk <= P.gexports[e - 1].chunk) return 36;
+    }
+    if ((g.init_slot < 0) != (g.cgrad < 0) || g.init_slot >= nslots || g.cgrad >= P.gdn_ncgrad) return 37;
+  }
+  for (int64_t r = 0; r < C; ++r)
+    if (own[r] != (P.pos_of_row[r] >= 0 ? 1 : 0)) return 38;
+  for (int s = 0; s < nslots; ++s)
+    for (int i = P.gslot_off[s]; i < P.gslot_off[s + 1]; ++i)
+      if (P.gslot_cons[i] < 0 || P.gslot_cons[i] >= P.gdn_ncgrad) return 39;
+  for (size_t i = 0; i + 1 < P.grep_off.size(); ++i)
+    for (int t = P.grep_off[i]; t < P.grep_off[i + 1]; ++t)
+      if (P.grows[P.grep_tok[t]] != P.grep_rows[i]) return 40;
+  return 0;
+}
+
 int main(int argc, char** argv) {
   const int iters = argc > 1 ? std::atoi(argv[1]) : 100;
   int built = 0, rejected = 0;
@@ -67,7 +105,7 @@ int main(int argc, char** argv) {
       }
       nodes[u].mount_count = (int)mounts.size() - nodes[u].mount_first;
     }
-    dag_build_opts o{64, 64, (int)rnd(2), (int)rnd(3)};
+    dag_build_opts o{64, 64, (int)rnd(2), (int)rnd(3), rnd(3) ? 1 + (int)rnd(70) : 0};
     Plan P;
     std::string err;
     const dag_status st = build_plan(nodes.data(), n, mounts.data(), (int)mounts.size(), &o, &P, &err);
@@ -77,7 +115,8 @@ int main(int argc, char** argv) {
       continue;
     }
     ++built;
-    const int c = check(P);
+    int c = check(P);
+    if (!c) c = check_gdn(P);
     if (c) {
       std::printf("table check %d failed at iteration %d\n", c, it);
       return 20 + c;
