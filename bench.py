@@ -18,6 +18,10 @@ Printed JSON (one line on stdout; progress goes to stderr):
               trajectory one causal chain, mounted spans copied in), timed in the
               same process, divided by the packed time
   cpu_baseline  the CPU oracle (float32 NumPy) on one trajectory of the workload
+  gdn         one chunked gated-delta-rule layer (16 heads, dk = dv = 128, chunk 64)
+              on the same DAG, forward and backward: milliseconds, the schedule's
+              rounds / sequences / replayed tokens, and executed MFMA TFLOP/s;
+              hybrid_step_ms = the attention step + 3 such layers (the hybrid stack)
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -112,6 +116,55 @@ def flat_time(dpa, spec, plan, p, dev, steps, max_rows=3_000_000):
     return total, pairs, sum(lengths), len(lengths)
 
 
+# Executed MFMA FLOPs of the gated-delta-rule kernels per (chunk, head): products of
+# 64x64x128 (mmd) and 64x128x128 (mdd) shapes, two FLOPs per multiply-add.
+_MMD, _MDD = 2 * 64 * 64 * 128, 2 * 64 * 128 * 128
+GDN_FLOPS = {"gdn_fwd": 3 * _MMD + 3 * _MDD, "gdn_states": _MMD + 2 * _MDD, "gdn_bwd": 11 * _MMD + 8 * _MDD}
+GDN_H = 16
+
+
+def gdn_time(dpa, spec, dev, steps, warmup):
+    """One gated-delta-rule layer (fwd + bwd) on the workload's tree: per-kernel ms per call."""
+    import torch
+
+    import synth
+    plan = dpa.Plan(spec, gdn_chunk=64)
+    info = plan.info
+    C = plan.rows
+    q, k, v, b, a, do = synth.gdn_inputs(C, GDN_H, 128, 128, 1105, device=dev, dtype=torch.bfloat16)
+    p = dpa.GdnParams(GDN_H, grad_dtype="bf16")
+    o = torch.empty_like(v)
+    grads = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v), torch.empty_like(b),
+             torch.empty_like(a))
+    fw, bw = dpa.gdn_workspace_bytes(plan, p)
+    ws = torch.empty(max(fw, bw, 1), dtype=torch.uint8, device=dev)
+    plan.upload()
+    for _ in range(warmup):
+        dpa.gdn_fwd(plan, p, q, k, v, b, a, o=o, ws=ws)
+        dpa.gdn_bwd(plan, p, q, k, v, b, a, do, ws=ws, out=grads)
+    torch.cuda.synchronize()
+    plan.timing_enable(True, capacity=8 * (steps + 1))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dpa.gdn_fwd(plan, p, q, k, v, b, a, o=o, ws=ws)
+        dpa.gdn_bwd(plan, p, q, k, v, b, a, do, ws=ws, out=grads)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / steps
+    kt = plan.timing_read()
+    plan.timing_enable(False)
+    ch = info["gdn_chunks"] * GDN_H
+    ms = {n: kt[n][0] / max(kt[n][1], 1) for n in GDN_FLOPS}
+    out = {"layer": "gated delta rule, 16 heads, dk = dv = 128, chunk 64, bf16 in / fp32 state",
+           "rounds": info["gdn_rounds"], "sequences": info["gdn_sequences"], "replay_tokens": info["gdn_replay"],
+           "chunks": info["gdn_chunks"], "fwd_ms": round(ms["gdn_fwd"], 3),
+           "bwd_ms": round(ms["gdn_states"] + ms["gdn_bwd"], 3), "fwd_bwd_ms_wall": round(wall * 1e3, 3),
+           "ms_per_launch": {n: round(v, 3) for n, v in ms.items()},
+           "mfma_tflops": {n: round(GDN_FLOPS[n] * ch / (ms[n] * 1e-3) / 1e12, 2) for n in GDN_FLOPS}}
+    del q, k, v, b, a, do, o, grads, ws
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(spec, plan, budget_s=15.0):
     """The oracle (float32) on one causal trajectory of the workload, sized to ~budget_s."""
     import numpy as np
@@ -176,6 +229,7 @@ def main() -> int:
     ap.add_argument("--flat-steps", type=int, default=1)
     ap.add_argument("--no-flat", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-gdn", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB -> 1 GiB device copy kernel 3 times (scales HBM counters)")
     args = ap.parse_args()
@@ -251,6 +305,12 @@ def main() -> int:
 
     del tensors, ws
     torch.cuda.empty_cache()
+    if not args.no_gdn:
+        g = gdn_time(dpa, spec, dev, max(1, min(args.steps, 3)), 1)
+        g["hybrid_step_ms"] = round(dt * 1e3 + 3 * g["fwd_bwd_ms_wall"], 2)
+        out["gdn"] = g
+        log(f"gdn layer: fwd {g['fwd_ms']:.2f} ms, bwd {g['bwd_ms']:.2f} ms ({g['rounds']} rounds, "
+            f"{g['sequences']} sequences); hybrid step {g['hybrid_step_ms']:.1f} ms")
     if not args.no_flat:
         t_flat, fpairs, frows, ntraj = flat_time(dpa, spec, plan, p, dev, args.flat_steps)
         out["x_vs_flat"] = round(t_flat / dt, 3)

@@ -64,6 +64,11 @@ class DagAttnParams(ctypes.Structure):
                 ("scale", ctypes.c_float), ("rope_base", ctypes.c_float)]
 
 
+class DagGdnParams(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("grad_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
 class DagError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
@@ -72,6 +77,9 @@ class DagError(RuntimeError):
 
 
 def _load() -> ctypes.CDLL:
+    # PyTorch's HIP runtime must be the one the library binds to (it provides the device
+    # memory and streams); loading torch first makes the dynamic linker reuse it.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         from . import build_lib
         build_lib.build()
@@ -91,6 +99,9 @@ def _load() -> ctypes.CDLL:
                                 ctypes.POINTER(SZ)], I32),
         "dag_attn_fwd": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, P, SZ, P], I32),
         "dag_attn_bwd": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "dag_gdn_workspace": ([P, ctypes.POINTER(DagGdnParams), ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I32),
+        "dag_gdn_fwd": ([P, ctypes.POINTER(DagGdnParams), P, P, P, P, P, P, P, SZ, P], I32),
+        "dag_gdn_bwd": ([P, ctypes.POINTER(DagGdnParams), P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
         "dag_attn_timing_enable": ([P, I32, I32], I32),
         "dag_attn_timing_read": ([P, P, P], I32),
         "dag_last_error": ([], ctypes.c_char_p),
@@ -191,7 +202,7 @@ class Plan:
     def upload(self, stream=None) -> None:
         _check(_lib.dag_plan_upload(self._h, _stream_ptr(stream)))
 
-    KERNELS = ("prologue_fwd", "fwd", "prologue_bwd", "dkdv", "dq")
+    KERNELS = ("prologue_fwd", "fwd", "prologue_bwd", "dkdv", "dq", "gdn_fwd", "gdn_states", "gdn_bwd")
 
     def timing_enable(self, enable: bool = True, capacity: int = 256) -> None:
         """Record HIP events around each kernel the library launches for this plan."""
@@ -312,6 +323,83 @@ def attn_bwd(plan: Plan, p: AttnParams, q, k, v, o, lse, dO, dq=None, dk=None, d
                              _ptr(o_lo) if o_lo is not None else None, _ptr(dO), _ptr(dq), _ptr(dk),
                              _ptr(dv), _ptr(ws), ws.numel(), _stream_ptr(stream)))
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# gated delta rule
+# ---------------------------------------------------------------------------
+
+@dataclass
+class GdnParams:
+    n_heads: int
+    head_dim: int = 128
+    scale: float = 0.0               # 0 -> 1
+    grad_dtype: str = "bf16"         # dq/dk/dv element type: "bf16" or "fp32"
+
+    def c(self) -> DagGdnParams:
+        m = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}
+        return DagGdnParams(self.n_heads, self.head_dim, DTYPE_BF16, m[self.grad_dtype], float(self.scale))
+
+    @property
+    def torch_grad_dtype(self):
+        import torch
+        return torch.bfloat16 if self.grad_dtype == "bf16" else torch.float32
+
+
+def gdn_workspace_bytes(plan: Plan, p: GdnParams) -> Tuple[int, int]:
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    cp = p.c()
+    _check(_lib.dag_gdn_workspace(plan._h, ctypes.byref(cp), ctypes.byref(f), ctypes.byref(b)))
+    return int(f.value), int(b.value)
+
+
+def _check_gates(name, t, rows, heads, device):
+    import torch
+    if t.dtype != torch.float32 or tuple(t.shape) != (rows, heads) or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name}: expected contiguous float32 [{rows}, {heads}] on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def gdn_fwd(plan: Plan, p: GdnParams, q, k, v, beta, alpha, o=None, ws=None, stream=None):
+    """``dag_gdn_fwd``: q, k, v [C,H,128] bf16, beta/alpha [C,H] fp32 -> o [C,H,128] bf16."""
+    import torch
+    C, dev = plan.rows, q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_tensor(name, t, C, p.n_heads, p.head_dim, torch.bfloat16, dev)
+    _check_gates("beta", beta, C, p.n_heads, dev)
+    _check_gates("alpha", alpha, C, p.n_heads, dev)
+    if o is None:
+        o = torch.empty_like(v)
+    need, _ = gdn_workspace_bytes(plan, p)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    cp = p.c()
+    _check(_lib.dag_gdn_fwd(plan._h, ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+                            _ptr(o), _ptr(ws), ws.numel(), _stream_ptr(stream)))
+    return o
+
+
+def gdn_bwd(plan: Plan, p: GdnParams, q, k, v, beta, alpha, dO, ws=None, stream=None, out=None):
+    """``dag_gdn_bwd``: returns (dq, dk, dv [C,H,128] grad_dtype, dbeta, dalpha [C,H] fp32)."""
+    import torch
+    C, dev = plan.rows, q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("dO", dO)):
+        _check_tensor(name, t, C, p.n_heads, p.head_dim, torch.bfloat16, dev)
+    _check_gates("beta", beta, C, p.n_heads, dev)
+    _check_gates("alpha", alpha, C, p.n_heads, dev)
+    gdt = p.torch_grad_dtype
+    if out is None:
+        out = (torch.empty(q.shape, dtype=gdt, device=dev), torch.empty(k.shape, dtype=gdt, device=dev),
+               torch.empty(v.shape, dtype=gdt, device=dev), torch.empty_like(beta), torch.empty_like(alpha))
+    dq, dk, dv, db, da = out
+    _, need = gdn_workspace_bytes(plan, p)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    cp = p.c()
+    _check(_lib.dag_gdn_bwd(plan._h, ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha),
+                            _ptr(dO), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(db), _ptr(da), _ptr(ws), ws.numel(),
+                            _stream_ptr(stream)))
+    return dq, dk, dv, db, da
 
 
 # ---------------------------------------------------------------------------

@@ -34,7 +34,7 @@ def _run(cmd):
     return r
 
 
-OBJS = ("plan.o", "gdn_plan.o", "abi.o", "kernels.o")
+OBJS = ("plan.o", "gdn_plan.o", "abi.o", "kernels.o", "gdn.o")
 
 
 def build(verbose: bool = False) -> str:
@@ -45,6 +45,7 @@ def build(verbose: bool = False) -> str:
         ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "gdn_plan.cpp"), "-o", os.path.join(obj_dir, "gdn_plan.o")],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "abi.cpp"), "-o", os.path.join(obj_dir, "abi.o")],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "kernels.hip"), "-o", os.path.join(obj_dir, "kernels.o")],
+        [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "gdn.hip"), "-o", os.path.join(obj_dir, "gdn.o")],
     ]
     with ThreadPoolExecutor(len(steps)) as ex:
         for r in ex.map(_run, steps):

@@ -9,6 +9,7 @@
 #include <string>
 #include <vector>
 
+#include "gdn.hpp"
 #include "launch.hpp"
 #include "plan.hpp"
 
@@ -31,6 +32,17 @@ struct DeviceTables {
   int32_t* bwd_order = nullptr;
   int32_t* page_table = nullptr;
   int32_t* page_nrows = nullptr;
+  // linear-attention schedule
+  GSeq* gseqs = nullptr;
+  int32_t* grows = nullptr;
+  GExport* gexports = nullptr;
+  int32_t* gslot_off = nullptr;
+  int32_t* gslot_cons = nullptr;
+  int32_t* ground_seq = nullptr;
+  int32_t* grep_rows = nullptr;
+  int32_t* grep_off = nullptr;
+  int32_t* grep_tok = nullptr;
+  int32_t* grep_slot = nullptr;
 };
 
 struct Timing {
@@ -175,7 +187,11 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
            align256(P.kentries.size() * sizeof(KEntry)) + align256(P.kv_off.size() * 4) +
            align256(P.kv_steps.size() * 4) +
            align256(P.bwd_order.size() * 4) + align256(P.page_table.size() * 4) +
-           align256(P.page_nrows.size() * 4) + 256;
+           align256(P.page_nrows.size() * 4) + align256(P.gseqs.size() * sizeof(GSeq)) +
+           align256(P.grows.size() * 4) + align256(P.gexports.size() * sizeof(GExport)) +
+           align256(P.gslot_off.size() * 4) + align256(P.gslot_cons.size() * 4) + align256(P.ground_seq.size() * 4) +
+           align256(P.grep_rows.size() * 4) + align256(P.grep_off.size() * 4) + align256(P.grep_tok.size() * 4) +
+           align256(P.grep_slot.size() * 4) + 256;
   DeviceTables* D = new (std::nothrow) DeviceTables();
   if (!D) return set_err(DAG_E_DEVICE, "out of host memory");
   D->device = dev;
@@ -196,6 +212,16 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
   D->bwd_order = dev_take<int32_t>(b, off, P.bwd_order.size());
   D->page_table = dev_take<int32_t>(b, off, P.page_table.size());
   D->page_nrows = dev_take<int32_t>(b, off, P.page_nrows.size());
+  D->gseqs = dev_take<GSeq>(b, off, P.gseqs.size());
+  D->grows = dev_take<int32_t>(b, off, P.grows.size());
+  D->gexports = dev_take<GExport>(b, off, P.gexports.size());
+  D->gslot_off = dev_take<int32_t>(b, off, P.gslot_off.size());
+  D->gslot_cons = dev_take<int32_t>(b, off, P.gslot_cons.size());
+  D->ground_seq = dev_take<int32_t>(b, off, P.ground_seq.size());
+  D->grep_rows = dev_take<int32_t>(b, off, P.grep_rows.size());
+  D->grep_off = dev_take<int32_t>(b, off, P.grep_off.size());
+  D->grep_tok = dev_take<int32_t>(b, off, P.grep_tok.size());
+  D->grep_slot = dev_take<int32_t>(b, off, P.grep_slot.size());
   auto put = [&](void* dst, const void* src, size_t n) {
     return n == 0 || hipMemcpyAsync(dst, src, n, hipMemcpyHostToDevice, st) == hipSuccess;
   };
@@ -208,7 +234,17 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
             put(D->kv_steps, P.kv_steps.data(), P.kv_steps.size() * 4) &&
             put(D->bwd_order, P.bwd_order.data(), P.bwd_order.size() * 4) &&
             put(D->page_table, P.page_table.data(), P.page_table.size() * 4) &&
-            put(D->page_nrows, P.page_nrows.data(), P.page_nrows.size() * 4);
+            put(D->page_nrows, P.page_nrows.data(), P.page_nrows.size() * 4) &&
+            put(D->gseqs, P.gseqs.data(), P.gseqs.size() * sizeof(GSeq)) &&
+            put(D->grows, P.grows.data(), P.grows.size() * 4) &&
+            put(D->gexports, P.gexports.data(), P.gexports.size() * sizeof(GExport)) &&
+            put(D->gslot_off, P.gslot_off.data(), P.gslot_off.size() * 4) &&
+            put(D->gslot_cons, P.gslot_cons.data(), P.gslot_cons.size() * 4) &&
+            put(D->ground_seq, P.ground_seq.data(), P.ground_seq.size() * 4) &&
+            put(D->grep_rows, P.grep_rows.data(), P.grep_rows.size() * 4) &&
+            put(D->grep_off, P.grep_off.data(), P.grep_off.size() * 4) &&
+            put(D->grep_tok, P.grep_tok.data(), P.grep_tok.size() * 4) &&
+            put(D->grep_slot, P.grep_slot.data(), P.grep_slot.size() * 4);
   // the host vectors are pageable: finish the copies before returning
   ok = ok && hipStreamSynchronize(st) == hipSuccess;
   if (!ok) {
@@ -249,6 +285,57 @@ dag_status launched(const char* what) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_err(DAG_E_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
   return DAG_OK;
+}
+
+
+// ---- gated delta rule -------------------------------------------------------------
+dag_status check_gdn(const Plan& P, const dag_gdn_params* p) {
+  if (!p) return set_err(DAG_E_INVALID, "null params");
+  if (P.info.gdn_chunk != 64)
+    return set_err(DAG_E_UNSUPPORTED, "the plan needs a linear-attention schedule with gdn_chunk = 64");
+  if (p->n_heads <= 0) return set_err(DAG_E_UNSUPPORTED, "n_heads must be positive");
+  if (p->head_dim != 128) return set_err(DAG_E_UNSUPPORTED, "head_dim must be 128");
+  if (p->dtype != DAG_DTYPE_BF16) return set_err(DAG_E_UNSUPPORTED, "dtype must be DAG_DTYPE_BF16");
+  if (p->grad_dtype != DAG_DTYPE_BF16 && p->grad_dtype != DAG_DTYPE_FP32)
+    return set_err(DAG_E_UNSUPPORTED, "grad_dtype must be DAG_DTYPE_BF16 or DAG_DTYPE_FP32");
+  if (!std::isfinite(p->scale)) return set_err(DAG_E_INVALID, "scale must be finite");
+  return DAG_OK;
+}
+
+struct GdnWs {
+  float* slots;
+  f16_t* states;
+  float* cgrad;
+  float* rside;
+  float* rbuf;
+};
+
+size_t carve_gdn(const Plan& P, int H, bool bwd, void* base, GdnWs* w) {
+  Carve c(base);
+  const size_t st = (size_t)H * 128 * 128;
+  w->slots = c.take<float>((size_t)P.info.gdn_slots * st);
+  w->states = bwd ? c.take<f16_t>((size_t)P.info.gdn_chunks * 2 * st) : nullptr;
+  w->cgrad = bwd ? c.take<float>((size_t)P.gdn_ncgrad * st) : nullptr;
+  w->rside = bwd ? c.take<float>(P.grep_rows.size() * H * 256) : nullptr;
+  w->rbuf = bwd ? c.take<float>((size_t)P.info.gdn_replay * H * 258) : nullptr;
+  return c.off;
+}
+
+GdnShape gdn_shape(const Plan& P, const dag_gdn_params* p) {
+  const DeviceTables& D = *P.dev;
+  GdnShape g;
+  g.seqs = D.gseqs;
+  g.rows = D.grows;
+  g.exports = D.gexports;
+  g.slot_off = D.gslot_off;
+  g.slot_cons = D.gslot_cons;
+  g.rep_slot = D.grep_slot;
+  g.rep_rows = D.grep_rows;
+  g.rep_off = D.grep_off;
+  g.rep_tok = D.grep_tok;
+  g.H = p->n_heads;
+  g.scale = p->scale != 0.f ? p->scale : 1.f;
+  return g;
 }
 
 }  // namespace
@@ -536,6 +623,92 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
                              D.kentries, D.page_table, D.page_nrows, (float*)dq, (float*)dk, (float*)dv, stream);
   }
   return launched("dag_attn_bwd");
+}
+
+dag_status dag_gdn_workspace(const dag_plan* plan, const dag_gdn_params* p, size_t* fwd_bytes, size_t* bwd_bytes) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  dag_status st = check_gdn(plan->p, p);
+  if (st != DAG_OK) return st;
+  GdnWs w;
+  if (fwd_bytes) *fwd_bytes = carve_gdn(plan->p, p->n_heads, false, nullptr, &w);
+  if (bwd_bytes) *bwd_bytes = carve_gdn(plan->p, p->n_heads, true, nullptr, &w);
+  return DAG_OK;
+}
+
+dag_status dag_gdn_fwd(dag_plan* plan, const dag_gdn_params* p, const void* q, const void* k, const void* v,
+                       const float* beta, const float* alpha, void* o, void* ws, size_t ws_bytes, void* hip_stream) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  Plan& P = plan->p;
+  dag_status st = check_gdn(P, p);
+  if (st != DAG_OK) return st;
+  if (P.info.rows == 0) return DAG_OK;
+  if (!q || !k || !v || !beta || !alpha || !o) return set_err(DAG_E_INVALID, "null tensor pointer");
+  GdnWs w;
+  const size_t need = carve_gdn(P, p->n_heads, false, nullptr, &w);
+  if (need && (!ws || ws_bytes < need))
+    return set_err(DAG_E_WORKSPACE, "linear-attention forward workspace needs " + std::to_string(need) + " bytes");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if ((st = ensure_uploaded(P, stream)) != DAG_OK) return st;
+  carve_gdn(P, p->n_heads, false, ws, &w);
+  const GdnShape g = gdn_shape(P, p);
+  const DeviceTables& D = *P.dev;
+  {
+    Span sp(P, DAG_K_GDN_FWD, stream);
+    for (int r = 0; r < P.info.gdn_rounds; ++r)
+      launch_gdn_fwd(g, P.ground_off[r + 1] - P.ground_off[r], D.ground_seq + P.ground_off[r], false,
+                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, beta, alpha, (bf16_t*)o, w.slots, nullptr,
+                     stream);
+    launch_gdn_pad<bf16_t>(P.info.pages, D.page_nrows, (bf16_t*)o, p->n_heads, 128, stream);
+  }
+  return launched("dag_gdn_fwd");
+}
+
+dag_status dag_gdn_bwd(dag_plan* plan, const dag_gdn_params* p, const void* q, const void* k, const void* v,
+                       const float* beta, const float* alpha, const void* dO, void* dq, void* dk, void* dv,
+                       float* dbeta, float* dalpha, void* ws, size_t ws_bytes, void* hip_stream) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  Plan& P = plan->p;
+  dag_status st = check_gdn(P, p);
+  if (st != DAG_OK) return st;
+  if (P.info.rows == 0) return DAG_OK;
+  if (!q || !k || !v || !beta || !alpha || !dO || !dq || !dk || !dv || !dbeta || !dalpha)
+    return set_err(DAG_E_INVALID, "null tensor pointer");
+  GdnWs w;
+  const size_t need = carve_gdn(P, p->n_heads, true, nullptr, &w);
+  if (need && (!ws || ws_bytes < need))
+    return set_err(DAG_E_WORKSPACE, "linear-attention backward workspace needs " + std::to_string(need) + " bytes");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if ((st = ensure_uploaded(P, stream)) != DAG_OK) return st;
+  carve_gdn(P, p->n_heads, true, ws, &w);
+  const GdnShape g = gdn_shape(P, p);
+  const DeviceTables& D = *P.dev;
+  const int H = p->n_heads;
+  const bf16_t *q16 = (const bf16_t*)q, *k16 = (const bf16_t*)k, *v16 = (const bf16_t*)v, *d16 = (const bf16_t*)dO;
+  {
+    Span sp(P, DAG_K_GDN_STATES, stream);
+    for (int r = 0; r < P.info.gdn_rounds; ++r)
+      launch_gdn_fwd(g, P.ground_off[r + 1] - P.ground_off[r], D.ground_seq + P.ground_off[r], true, q16, k16, v16,
+                     beta, alpha, nullptr, w.slots, w.states, stream);
+  }
+  auto run = [&](auto* tag) {
+    using TG = std::remove_pointer_t<decltype(tag)>;
+    Span sp(P, DAG_K_GDN_BWD, stream);
+    for (int r = P.info.gdn_rounds - 1; r >= 0; --r)
+      launch_gdn_bwd<TG>(g, P.ground_off[r + 1] - P.ground_off[r], D.ground_seq + P.ground_off[r], q16, k16, v16,
+                         beta, alpha, d16, w.states, w.cgrad, (TG*)dq, (TG*)dk, (TG*)dv, dbeta, dalpha, w.rside,
+                         w.rbuf, stream);
+    launch_gdn_fixup<TG>(g, (int)P.grep_rows.size(), w.rside, w.rbuf, (TG*)dk, (TG*)dv, dbeta, dalpha, stream);
+    launch_gdn_pad<TG>(P.info.pages, D.page_nrows, (TG*)dq, H, 128, stream);
+    launch_gdn_pad<TG>(P.info.pages, D.page_nrows, (TG*)dk, H, 128, stream);
+    launch_gdn_pad<TG>(P.info.pages, D.page_nrows, (TG*)dv, H, 128, stream);
+    launch_gdn_pad<float>(P.info.pages, D.page_nrows, dbeta, H, 1, stream);
+    launch_gdn_pad<float>(P.info.pages, D.page_nrows, dalpha, H, 1, stream);
+  };
+  if (p->grad_dtype == DAG_DTYPE_FP32)
+    run((float*)nullptr);
+  else
+    run((bf16_t*)nullptr);
+  return launched("dag_gdn_bwd");
 }
 
 }  // extern "C"

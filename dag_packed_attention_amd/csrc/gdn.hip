@@ -1,0 +1,988 @@
+// Chunked gated delta rule over a rollout tree (MI355X, gfx950).
+//
+// What is computed (per head, state S of shape [dv, dk], fp32):
+//   S_t = alpha_t S_{t-1} (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,   o_t = scale S_t q_t
+// along every token's own root-to-node path (mounted spans are not part of a
+// recurrent layer's history, Octopus Sec. 3).  The pages name this layer but
+// print no recurrence for it; this is the textbook gated delta rule.
+//
+// How it is executed (HARTS: Hybrid-Attention RL over Tree Structures):
+//   * chunks of B = 64 tokens on the recurrent index (Sec. 2.2 Eq. 2); a
+//     branch forking at p starts from the state at a(p) = 64 floor(p / 64) and
+//     re-runs the ancestor tokens [a(p), p) without outputs ("replay");
+//   * the host schedule (gdn_plan.cpp, Sec. 3.3 Algorithm 1) packs the
+//     sequences of each round into one launch; a sequence exports the boundary
+//     states its side branches start from, and in the backward the gradient of
+//     each exported state is the sum of its consumers' initial-state gradients
+//     (Sec. 3.4 Eq. 16), added in a fixed order;
+//   * within a chunk (t, i = 0..63 token indices, g_t = sum_{s<=t} log alpha_s,
+//     gamma_t = exp(g_t), E_ti = exp(g_t - g_i)), with S0 the state at the
+//     chunk's start (the unrolled recurrence written blockwise):
+//         A   = strict_lower(beta_t E_ti k_t.k_i)        (unit-lower system I + A)
+//         R   = diag(beta) (V - diag(gamma) K S0^T)
+//         U   = (I + A)^{-1} R                            (u_t = beta_t (v_t - alpha_t S_{t-1} k_t))
+//         O   = scale (diag(gamma) Q S0^T + lower(E o Q K^T) U)
+//         S64 = gamma_63 S0 + (diag(E_63,.) U)^T K
+//     and the backward is the exact derivative of these lines.
+//
+// One work-group (256 threads, 4 waves) owns one (sequence, head) and walks
+// its chunks in order (backward: in reverse).  Dense products run on
+// v_mfma_f32_32x32x16_f16 with fp16 operands staged in LDS (transposed
+// operands through ds_read_b64_tr_b16) and fp32 accumulation; the triangular
+// solves are forward / backward substitution in registers.
+#include <hip/hip_runtime.h>
+
+#include "gdn.hpp"
+
+namespace dagattn {
+namespace gdn {
+
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __fp16 v4fp16 __attribute__((__vector_size__(8)));
+typedef __attribute__((address_space(3))) v4fp16 lds_v4fp16;
+
+constexpr int kB = 64;    // chunk length
+constexpr int kD = 128;   // dk = dv
+constexpr int LDK = 136;  // halfs per row of an fp16 tile with 128 columns (16-byte pad)
+constexpr int LDP = 72;   // halfs per row of an fp16 tile with 64 columns
+constexpr int LDA = 68;   // floats per row of an fp32 [64][64] tile
+constexpr int LDR = 132;  // floats per row of an fp32 [64][128] tile
+constexpr int kRep = 2 * kD + 2;  // replay-gradient record: dk[128], dv[128], dbeta, dalpha
+
+__device__ __forceinline__ float bf2f(bf16_t x) { return __uint_as_float(((uint32_t)x) << 16); }
+__device__ __forceinline__ bf16_t f2bf(float x) {
+  __bf16 b = (__bf16)x;
+  return *reinterpret_cast<bf16_t*>(&b);
+}
+template <typename T> __device__ __forceinline__ void st_g(T* p, float x);
+template <> __device__ __forceinline__ void st_g<float>(float* p, float x) { *p = x; }
+template <> __device__ __forceinline__ void st_g<bf16_t>(bf16_t* p, float x) { *p = f2bf(x); }
+
+__device__ __forceinline__ f32x16 mfma(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+// Row of element r of a 32x32 accumulator in lane half `hi` (column = lane % 32).
+__device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
+
+// MFMA operand with the contraction index contiguous: rows mn0 + lane % 32 of
+// X[.][ld], elements k0 + 8 (lane / 32) .. + 7.
+__device__ __forceinline__ f16x8 frag_n(const f16_t* X, int ld, int mn0, int k0, int lane) {
+  return *reinterpret_cast<const f16x8*>(X + (mn0 + (lane & 31)) * ld + k0 + 8 * (lane >> 5));
+}
+// MFMA operand with the contraction index along rows of an LDS tile X[k][mn]:
+// lane gets X[k0 + 8 (lane / 32) + j][mn0 + lane % 32], j = 0..7.  Within a
+// group of 16 lanes, a transpose read gives lane i element i % 4 of the 8 bytes
+// fetched by lane 4 j + i / 4; so lane s fetches row (s / 4) at columns 4 (s % 4) ...
+__device__ __forceinline__ f16x8 frag_t(const f16_t* X, int ld, int k0, int mn0, int lane) {
+  const int G = lane >> 4, a = lane & 15;
+  const int row = k0 + 8 * (G >> 1) + (a >> 2);
+  const int col = mn0 + 16 * (G & 1) + 4 * (a & 3);
+  const v4fp16 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4fp16*)(X + row * ld + col));
+  const v4fp16 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4fp16*)(X + (row + 4) * ld + col));
+  f16x8 o;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    o[j] = (f16_t)v0[j];
+    o[4 + j] = (f16_t)v1[j];
+  }
+  return o;
+}
+// Same operand layout as frag_n, read from global memory.
+__device__ __forceinline__ f16x8 frag_g(const f16_t* __restrict__ X, int mn0, int k0, int lane) {
+  return *reinterpret_cast<const f16x8*>(X + (mn0 + (lane & 31)) * kD + k0 + 8 * (lane >> 5));
+}
+__device__ __forceinline__ f16x8 scale8(f16x8 a, const float (&s)[8]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = (f16_t)((float)a[j] * s[j]);
+  return a;
+}
+
+// 8 bf16 (16 bytes) -> 8 fp16.
+__device__ __forceinline__ f16x8 bf8_to_h8(uint4 u) {
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+  f16x8 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    o[2 * i] = (f16_t)__uint_as_float(w[i] << 16);
+    o[2 * i + 1] = (f16_t)__uint_as_float(w[i] & 0xffff0000u);
+  }
+  return o;
+}
+
+// Sum of the 16 accumulator values of each row over the 32 lanes of one lane
+// half, in a fixed butterfly order: afterwards lane 2 r (and 2 r + 1) of the
+// half holds the sum for element r (row acc_row(r, hi)).
+__device__ __forceinline__ float rowsum16(const float (&x)[16], int lane) {
+  float a8[8], a4[4], a2[2], a1;
+  const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float send = b4 ? x[j] : x[8 + j];
+    const float keep = b4 ? x[8 + j] : x[j];
+    a8[j] = keep + __shfl_xor(send, 16);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float send = b3 ? a8[j] : a8[4 + j];
+    const float keep = b3 ? a8[4 + j] : a8[j];
+    a4[j] = keep + __shfl_xor(send, 8);
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float send = b2 ? a4[j] : a4[2 + j];
+    const float keep = b2 ? a4[2 + j] : a4[j];
+    a2[j] = keep + __shfl_xor(send, 4);
+  }
+  {
+    const float send = b1 ? a2[0] : a2[1];
+    const float keep = b1 ? a2[1] : a2[0];
+    a1 = keep + __shfl_xor(send, 2);
+  }
+  return a1 + __shfl_xor(a1, 1);
+}
+// Element index of the row whose sum rowsum16 leaves in this lane.
+__device__ __forceinline__ int rowsum16_elem(int lane) {
+  return 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 1) & 1);
+}
+// Sum over the 32 rows of one accumulator column (both lane halves).
+__device__ __forceinline__ float colsum16(const float (&x)[16]) {
+  float s = 0.f;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s += x[r];
+  return s + __shfl_xor(s, 32);
+}
+
+// ---------------------------------------------------------------------------------
+// LDS tiles shared by both kernels
+// ---------------------------------------------------------------------------------
+struct ChunkIn {
+  const int32_t* rows;  // sequence token -> compact row
+  int n_tok, n_replay;
+};
+
+// Load chunk c's K and Q (and dO) rows into LDS as fp16, row numbers, beta and the
+// cumulative log decay.  Tokens past the sequence's end are zero (beta = 0,
+// log alpha = 0), which makes them inert in every product.
+template <bool kDO>
+__device__ __forceinline__ void load_chunk(const ChunkIn& ci, int j0, const bf16_t* __restrict__ k,
+                                           const bf16_t* __restrict__ q, const bf16_t* __restrict__ dO,
+                                           const float* __restrict__ beta, const float* __restrict__ alpha,
+                                           int H, int head, f16_t* Kr, f16_t* Qr, f16_t* dOr, int* rw, float* gs,
+                                           float* bs, float* al, int tid) {
+  for (int i = tid; i < kB * 16; i += 256) {
+    const int t = i >> 4, c8 = (i & 15) * 8;
+    const int j = j0 + t;
+    f16x8 kk = {}, qq = {}, dd = {};
+    if (j < ci.n_tok) {
+      const int64_t base = ((int64_t)ci.rows[j] * H + head) * kD + c8;
+      kk = bf8_to_h8(*reinterpret_cast<const uint4*>(k + base));
+      qq = bf8_to_h8(*reinterpret_cast<const uint4*>(q + base));
+      if (kDO && j >= ci.n_replay) dd = bf8_to_h8(*reinterpret_cast<const uint4*>(dO + base));
+    }
+    *reinterpret_cast<f16x8*>(Kr + t * LDK + c8) = kk;
+    *reinterpret_cast<f16x8*>(Qr + t * LDK + c8) = qq;
+    if (kDO) *reinterpret_cast<f16x8*>(dOr + t * LDK + c8) = dd;
+  }
+  if (tid < kB) {
+    const int t = tid, j = j0 + t;
+    int row = -1;
+    float b = 0.f, la = 0.f, a = 1.f;
+    if (j < ci.n_tok) {
+      row = ci.rows[j];
+      b = beta[(int64_t)row * H + head];
+      a = alpha[(int64_t)row * H + head];
+      la = logf(a);
+    }
+    rw[t] = row;
+    bs[t] = b;
+    if (al) al[t] = a;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(la, off, 64);
+      if (t >= off) la += y;
+    }
+    gs[t] = la;
+  }
+}
+
+// Write the state accumulators (wave w: dv rows 32 w .., four dk blocks) as fp16 into
+// an LDS tile [dv][LDK].
+__device__ __forceinline__ void state_to_lds(const f32x16 (&S)[4], f16_t* Sh, int wave, int lane) {
+  const int hi = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Sh[(32 * wave + acc_row(r, hi)) * LDK + 32 * nb + l32] = (f16_t)S[nb][r];
+}
+
+// Save the state as fp16 in both layouts: [dv][dk] then [dk][dv].
+__device__ __forceinline__ void state_save(const f32x16 (&S)[4], f16_t* __restrict__ dst, int wave, int lane) {
+  const int hi = lane >> 5, l32 = lane & 31;
+  f16_t* nat = dst;
+  f16_t* tr = dst + kD * kD;
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nat[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32] = (f16_t)S[nb][r];
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
+      f16x4 w;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] = (f16_t)S[nb][4 * r4 + j];
+      *reinterpret_cast<f16x4*>(tr + (32 * nb + l32) * kD + 32 * wave + 8 * r4 + 4 * hi) = w;
+    }
+  }
+}
+
+// Triangular solves with the unit-lower matrix I + A (A strictly lower), for
+// the 128 columns of an [64][.] tile; thread c (< 128) owns column c.  A is
+// kept transposed in LDS (At[i][t] = A[t][i], row stride LDA).  Rows go in four
+// blocks of 16: a block first takes the contributions of the solved blocks
+// (a runtime loop over their rows), then solves its own 16 rows in registers.
+
+// 16 consecutive entries At[row][col0 .. col0 + 15] (broadcast LDS reads).
+__device__ __forceinline__ void at_row16(const float* At, int row, int col0, float (&a)[16]) {
+  const float4* p = reinterpret_cast<const float4*>(At + row * LDA + col0);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 v = p[q];
+    a[4 * q] = v.x;
+    a[4 * q + 1] = v.y;
+    a[4 * q + 2] = v.z;
+    a[4 * q + 3] = v.w;
+  }
+}
+
+// (I + A) X = R, right-looking: once x_i is final, every later row t takes
+// -A[t][i] x_i, and A[t][i] for t in a block is a contiguous run of row i of At.
+// X overwrites R in `x` (row stride ldx); the solved rows also go to `out` as
+// fp16 if given.
+template <typename TX>
+__device__ __forceinline__ void solve_lower(const float* At, TX* x, int ldx, f16_t* out, int c) {
+  for (int b = 0; b < 4; ++b) {
+    float acc[16], a[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = (float)x[(16 * b + j) * ldx + c];
+#pragma unroll 2
+    for (int i = 0; i < 16 * b; ++i) {
+      const float xi = (float)x[i * ldx + c];
+      at_row16(At, i, 16 * b, a);
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc[j] = fmaf(-a[j], xi, acc[j]);
+    }
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+      at_row16(At, 16 * b + m, 16 * b, a);
+#pragma unroll
+      for (int j = m + 1; j < 16; ++j) acc[j] = fmaf(-a[j], acc[m], acc[j]);
+      x[(16 * b + m) * ldx + c] = (TX)acc[m];
+      if (out) out[(16 * b + m) * LDK + c] = (f16_t)acc[m];
+    }
+  }
+}
+
+// (I + A)^T Y = D, left-looking: y_t = d_t - sum_{i > t} A[i][t] y_i, a dot
+// product with a contiguous run of row t of At.  Y overwrites D in `x`;
+// `emit(t, y_t)` sees every solved value.
+template <typename TX, typename Emit>
+__device__ __forceinline__ void solve_upper_t(const float* At, TX* x, int ldx, int c, Emit emit) {
+  for (int b = 3; b >= 0; --b) {
+    float acc[16], a[16], y[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc[j] = (float)x[(16 * b + j) * ldx + c];
+    for (int ib = b + 1; ib < 4; ++ib) {
+#pragma unroll
+      for (int m = 0; m < 16; ++m) y[m] = (float)x[(16 * ib + m) * ldx + c];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        at_row16(At, 16 * b + j, 16 * ib, a);
+#pragma unroll
+        for (int m = 0; m < 16; ++m) acc[j] = fmaf(-a[m], y[m], acc[j]);
+      }
+    }
+#pragma unroll
+    for (int j = 15; j >= 0; --j) {
+      at_row16(At, 16 * b + j, 16 * b, a);
+#pragma unroll
+      for (int m = j + 1; m < 16; ++m) acc[j] = fmaf(-a[m], acc[m], acc[j]);
+      x[(16 * b + j) * ldx + c] = (TX)acc[j];
+      emit(16 * b + j, acc[j]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Forward (kStates = false: outputs; true: the backward's recomputation, which
+// instead saves every chunk's starting state).  Both export boundary states.
+// ---------------------------------------------------------------------------------
+template <bool kStates>
+__global__ __launch_bounds__(256) void gdn_fwd_kernel(
+    const GSeq* __restrict__ seqs, const int32_t* __restrict__ order, const int32_t* __restrict__ grows,
+    const GExport* __restrict__ exports, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+    const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ alpha,
+    bf16_t* __restrict__ o, float* __restrict__ slots, f16_t* __restrict__ states, int H, float scale) {
+  __shared__ __attribute__((aligned(16))) f16_t Kr[kB * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t Qr[kB * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t Sh[kD * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t Pr[kB * LDP];
+  __shared__ __attribute__((aligned(16))) f16_t Ur[kB * LDK];
+  __shared__ __attribute__((aligned(16))) float Ar[kB * LDA];  // A^T
+  __shared__ __attribute__((aligned(16))) float Rr[kB * LDR];
+  __shared__ float gs[kB], bs[kB];
+  __shared__ int rw[kB];
+
+  const int head = blockIdx.x % H;
+  const GSeq sq = seqs[order[blockIdx.x / H]];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int nch = (sq.n_tok + kB - 1) / kB;
+  const ChunkIn ci{grows + sq.tok_off, sq.n_tok, sq.n_replay};
+
+  f32x16 S[4];
+  if (sq.init_slot >= 0) {
+    const float* src = slots + ((int64_t)sq.init_slot * H + head) * kD * kD;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) S[nb][r] = src[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32];
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) S[nb] = zero16();
+  }
+  state_to_lds(S, Sh, wave, lane);
+  if (kStates) state_save(S, states + ((int64_t)sq.chunk_off * H + head) * 2 * kD * kD, wave, lane);
+  int ex = sq.exp_off;
+  const int ex_end = sq.exp_off + sq.exp_cnt;
+
+  for (int c = 0; c < nch; ++c) {
+    const int j0 = c * kB;
+    load_chunk<false>(ci, j0, k, q, nullptr, beta, alpha, H, head, Kr, Qr, nullptr, rw, gs, bs, nullptr, tid);
+    __syncthreads();
+
+    // -- products with K, Q and the chunk's starting state --------------------------
+    {
+      const int bm = wave >> 1, bn = wave & 1;
+      f32x16 kk = zero16(), qk = zero16();
+      if (bm >= bn) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const f16x8 b = frag_n(Kr, LDK, 32 * bn, 16 * s, lane);
+          kk = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), b, kk);
+          if (!kStates) qk = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), b, qk);
+        }
+      }
+      const int i = 32 * bn + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * bm + acc_row(r, hi);
+        const float e = i <= t ? __expf(gs[t] - gs[i]) : 0.f;
+        Ar[i * LDA + t] = i < t ? bs[t] * e * kk[r] : 0.f;
+        if (!kStates) Pr[t * LDP + i] = (f16_t)(scale * e * qk[r]);
+      }
+    }
+    {
+      f32x16 ks[2];
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm) ks[bm] = zero16();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 b = frag_n(Sh, LDK, 32 * wave, 16 * s, lane);
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm) ks[bm] = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), b, ks[bm]);
+      }
+      const int cc = 32 * wave + l32;
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * bm + acc_row(r, hi);
+          const int row = rw[t];
+          const float vv = row >= 0 ? bf2f(v[((int64_t)row * H + head) * kD + cc]) : 0.f;
+          Rr[t * LDR + cc] = bs[t] * (vv - __expf(gs[t]) * ks[bm][r]);
+        }
+    }
+    __syncthreads();
+
+    // -- U = (I + A)^{-1} R  (only the state is live across the solve) ------------------
+    if (tid < kD) solve_lower<float>(Ar, Rr, LDR, Ur, tid);
+    __syncthreads();
+
+    // -- outputs: O = scale diag(gamma) Q S0^T + (scale E o QK) U -------------------------
+    if (!kStates) {
+      f32x16 acc_o[2];
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm) acc_o[bm] = zero16();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 b = frag_n(Sh, LDK, 32 * wave, 16 * s, lane);
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm) acc_o[bm] = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), b, acc_o[bm]);
+      }
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[bm][r] *= scale * __expf(gs[32 * bm + acc_row(r, hi)]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 b = frag_t(Ur, LDK, 16 * s, 32 * wave, lane);
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm) acc_o[bm] = mfma(frag_n(Pr, LDP, 32 * bm, 16 * s, lane), b, acc_o[bm]);
+      }
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * bm + acc_row(r, hi);
+          const int j = j0 + t;
+          if (j >= sq.n_replay && j < sq.n_tok)
+            o[((int64_t)rw[t] * H + head) * kD + 32 * wave + l32] = f2bf(acc_o[bm][r]);
+        }
+    }
+
+    // -- state update: S <- gamma_63 S + (diag(E_63,.) U)^T K ------------------------------
+    {
+      const float g63 = gs[kB - 1];
+      const float gn = __expf(g63);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[nb][r] *= gn;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float e[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) e[j] = __expf(g63 - gs[16 * s + 8 * hi + j]);
+        const f16x8 a = scale8(frag_t(Ur, LDK, 16 * s, 32 * wave, lane), e);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) S[nb] = mfma(a, frag_t(Kr, LDK, 16 * s, 32 * nb, lane), S[nb]);
+      }
+    }
+    if (ex < ex_end && exports[ex].chunk == c + 1) {
+      float* dst = slots + ((int64_t)exports[ex].slot * H + head) * kD * kD;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32] = S[nb][r];
+      ++ex;
+    }
+    __syncthreads();
+    if (c + 1 < nch) {
+      state_to_lds(S, Sh, wave, lane);
+      if (kStates) state_save(S, states + ((int64_t)(sq.chunk_off + c + 1) * H + head) * 2 * kD * kD, wave, lane);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Backward: one round, sequences in any order; chunks in reverse.
+// ---------------------------------------------------------------------------------
+template <typename TG>
+__global__ __launch_bounds__(256) void gdn_bwd_kernel(
+    const GSeq* __restrict__ seqs, const int32_t* __restrict__ order, const int32_t* __restrict__ grows,
+    const GExport* __restrict__ exports, const int32_t* __restrict__ slot_off, const int32_t* __restrict__ slot_cons,
+    const int32_t* __restrict__ rep_slot, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+    const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ alpha,
+    const bf16_t* __restrict__ dO, const f16_t* __restrict__ states, float* __restrict__ cgrad,
+    TG* __restrict__ dq, TG* __restrict__ dk, TG* __restrict__ dv, float* __restrict__ dbeta,
+    float* __restrict__ dalpha, float* __restrict__ rside, float* __restrict__ rbuf, int H, float scale) {
+  __shared__ __attribute__((aligned(16))) f16_t dSh[kD * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t Kr[kB * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t Qr[kB * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t dOr[kB * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t Ur[kB * LDK];   // R, then U
+  __shared__ __attribute__((aligned(16))) f16_t dRr[kB * LDK];  // dU, then dR
+  __shared__ __attribute__((aligned(16))) f16_t Pr[kB * LDP];   // scale E o QK, then dP~
+  __shared__ __attribute__((aligned(16))) float Ar[kB * LDA];   // A^T, then dKk (fp16 [64][LDP])
+  __shared__ float gs[kB], bs[kB], al[kB];
+  __shared__ int rw[kB];
+  __shared__ float red_dg[4][kB], red_g[4][kB], red_b[4][kB], red_e[4][kB], red_s[4];
+
+  const int head = blockIdx.x % H;
+  const GSeq sq = seqs[order[blockIdx.x / H]];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int nch = (sq.n_tok + kB - 1) / kB;
+  const ChunkIn ci{grows + sq.tok_off, sq.n_tok, sq.n_replay};
+  f16_t* Kk = reinterpret_cast<f16_t*>(Ar);
+  const int bm = wave >> 1, bn = wave & 1;  // this wave's 32x32 block of a 64x64 matrix
+
+  f32x16 D[4];  // dS: dv rows 32 wave .., four dk blocks
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) D[nb] = zero16();
+  int ex = sq.exp_off + sq.exp_cnt - 1;
+
+  for (int c = nch - 1; c >= 0; --c) {
+    const int j0 = c * kB;
+    // -- consumers' initial-state gradients enter at exported boundaries ----------------
+    if (ex >= sq.exp_off && exports[ex].chunk == c + 1) {
+      const int slot = exports[ex].slot;
+      for (int e = slot_off[slot]; e < slot_off[slot + 1]; ++e) {
+        const float* src = cgrad + ((int64_t)slot_cons[e] * H + head) * kD * kD;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) D[nb][r] += src[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32];
+      }
+      --ex;
+    }
+    state_to_lds(D, dSh, wave, lane);
+    load_chunk<true>(ci, j0, k, q, dO, beta, alpha, H, head, Kr, Qr, dOr, rw, gs, bs, al, tid);
+    red_dg[wave][lane] = 0.f;
+    red_g[wave][lane] = 0.f;
+    red_b[wave][lane] = 0.f;
+    red_e[wave][lane] = 0.f;
+    __syncthreads();
+    const f16_t* S0n = states + ((int64_t)(sq.chunk_off + c) * H + head) * 2 * kD * kD;
+    const f16_t* S0t = S0n + kD * kD;
+    const float g63 = gs[kB - 1];
+
+    // -- recompute A, P = scale E o QK and R ---------------------------------------------------
+    {
+      f32x16 kk = zero16(), qk = zero16();
+      if (bm >= bn) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const f16x8 b = frag_n(Kr, LDK, 32 * bn, 16 * s, lane);
+          kk = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), b, kk);
+          qk = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), b, qk);
+        }
+      }
+      const int i = 32 * bn + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * bm + acc_row(r, hi);
+        const float e = i <= t ? __expf(gs[t] - gs[i]) : 0.f;
+        Ar[i * LDA + t] = i < t ? bs[t] * e * kk[r] : 0.f;
+        Pr[t * LDP + i] = (f16_t)(scale * e * qk[r]);
+      }
+    }
+    const int cc = 32 * wave + l32;
+    {
+      f32x16 ks[2];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) ks[b2] = zero16();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 b = frag_g(S0n, 32 * wave, 16 * s, lane);
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) ks[b2] = mfma(frag_n(Kr, LDK, 32 * b2, 16 * s, lane), b, ks[b2]);
+      }
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * b2 + acc_row(r, hi);
+          const int row = rw[t];
+          const float vv = row >= 0 ? bf2f(v[((int64_t)row * H + head) * kD + cc]) : 0.f;
+          Ur[t * LDK + cc] = (f16_t)(bs[t] * (vv - __expf(gs[t]) * ks[b2][r]));
+        }
+    }
+    __syncthreads();
+    if (tid < kD) solve_lower<f16_t>(Ar, Ur, LDK, nullptr, tid);
+    __syncthreads();
+
+    // -- dU = scale P^T dO + diag(E_63,.) K dS^T --------------------------------------------
+    {
+      f32x16 du[2];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) du[b2] = zero16();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 b = frag_n(dSh, LDK, 32 * wave, 16 * s, lane);
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) du[b2] = mfma(frag_n(Kr, LDK, 32 * b2, 16 * s, lane), b, du[b2]);
+      }
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) du[b2][r] *= __expf(g63 - gs[32 * b2 + acc_row(r, hi)]);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 b = frag_t(dOr, LDK, 16 * s, 32 * wave, lane);
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) du[b2] = mfma(frag_t(Pr, LDP, 16 * s, 32 * b2, lane), b, du[b2]);
+      }
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dRr[(32 * b2 + acc_row(r, hi)) * LDK + cc] = (f16_t)du[b2][r];
+    }
+    __syncthreads();
+
+    // -- dR = (I + A)^{-T} dU; dV = diag(beta) dR -------------------------------------------
+    if (tid < kD) {
+      const int col = tid;
+      solve_upper_t<f16_t>(Ar, dRr, LDK, col, [&](int t, float y) {
+        const int j = j0 + t;
+        if (j >= sq.n_tok) return;
+        const float g = bs[t] * y;
+        if (j < sq.n_replay) {
+          rbuf[((int64_t)(sq.rep_off + j) * H + head) * kRep + kD + col] = g;
+        } else {
+          const int rs = rep_slot[rw[t]];
+          if (rs >= 0) rside[((int64_t)rs * H + head) * 2 * kD + kD + col] = g;
+          else st_g<TG>(dv + ((int64_t)rw[t] * H + head) * kD + col, g);
+        }
+      });
+    }
+    __syncthreads();
+
+    // -- <dS, S0> for the decay of the whole chunk ------------------------------------------
+    {
+      float s = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += D[nb][r] * (float)S0n[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32];
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+      if (lane == 0) red_s[wave] = s;
+    }
+    // -- dP = dO U^T, dA = -dR U^T on this wave's block -----------------------------------------
+    {
+      f32x16 dp = zero16(), da = zero16(), kk = zero16(), qk = zero16();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 b = frag_n(Ur, LDK, 32 * bn, 16 * s, lane);
+        dp = mfma(frag_n(dOr, LDK, 32 * bm, 16 * s, lane), b, dp);
+        if (bm >= bn) {
+          const f16x8 bk = frag_n(Kr, LDK, 32 * bn, 16 * s, lane);
+          da = mfma(frag_n(dRr, LDK, 32 * bm, 16 * s, lane), b, da);
+          kk = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), bk, kk);
+          qk = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), bk, qk);
+        }
+      }
+      const int i = 32 * bn + l32;
+      float xy[16], z[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * bm + acc_row(r, hi);
+        const float e = i <= t ? __expf(gs[t] - gs[i]) : 0.f;
+        const float dpt = scale * e * dp[r];          // dP~ = d(QK) (scale and decay folded)
+        const float dat = i < t ? -da[r] : 0.f;       // dA
+        const float dkk = dat * bs[t] * e;            // d(KK)
+        Pr[t * LDP + i] = (f16_t)dpt;
+        Kk[t * LDP + i] = (f16_t)dkk;
+        xy[r] = dpt * qk[r] + dkk * kk[r];            // dg from E_ti inside P and A
+        z[r] = dat * e * kk[r];                       // dbeta through A
+      }
+      const float rs = rowsum16(xy, lane);
+      const float rz = rowsum16(z, lane);
+      const float cs = colsum16(xy);
+      if (!(lane & 1)) {
+        const int t = 32 * bm + acc_row(rowsum16_elem(lane), hi);
+        red_dg[wave][t] += rs;
+        red_b[wave][t] += rz;
+      }
+      if (hi == 0) red_dg[wave][i] -= cs;
+    }
+    // -- R's dependence on beta and gamma ------------------------------------------------------
+    f32x16 ks[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) ks[b2] = zero16();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const f16x8 b = frag_g(S0n, 32 * wave, 16 * s, lane);
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) ks[b2] = mfma(frag_n(Kr, LDK, 32 * b2, 16 * s, lane), b, ks[b2]);
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      float xb[16], xg[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * b2 + acc_row(r, hi);
+        const int row = rw[t];
+        const float vv = row >= 0 ? bf2f(v[((int64_t)row * H + head) * kD + cc]) : 0.f;
+        const float dr = (float)dRr[t * LDK + cc];
+        xb[r] = dr * (vv - __expf(gs[t]) * ks[b2][r]);
+        xg[r] = -bs[t] * dr * ks[b2][r];
+      }
+      const float sb = rowsum16(xb, lane);
+      const float sg = rowsum16(xg, lane);
+      if (!(lane & 1)) {
+        const int t = 32 * b2 + acc_row(rowsum16_elem(lane), hi);
+        red_b[wave][t] += sb;
+        red_g[wave][t] += sg;
+      }
+    }
+    // -- dS_prev = gamma_63 dS + scale (diag(gamma) dO)^T Q - (diag(beta gamma) dR)^T K -----------
+    {
+      const float gn = __expf(g63);
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) D[nb][r] *= gn;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        float e1[8], e2[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int t = 16 * s + 8 * hi + j;
+          const float gam = __expf(gs[t]);
+          e1[j] = scale * gam;
+          e2[j] = -bs[t] * gam;
+        }
+        const f16x8 a1 = scale8(frag_t(dOr, LDK, 16 * s, 32 * wave, lane), e1);
+        const f16x8 a2 = scale8(frag_t(dRr, LDK, 16 * s, 32 * wave, lane), e2);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          D[nb] = mfma(a1, frag_t(Qr, LDK, 16 * s, 32 * nb, lane), D[nb]);
+          D[nb] = mfma(a2, frag_t(Kr, LDK, 16 * s, 32 * nb, lane), D[nb]);
+        }
+      }
+    }
+    __syncthreads();
+
+    // -- dQ = scale diag(gamma) dO S0 + dP~ K ----------------------------------------------------
+    {
+      f32x16 aq[2];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) aq[b2] = zero16();
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 b = frag_g(S0t, 32 * wave, 16 * s, lane);
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) aq[b2] = mfma(frag_n(dOr, LDK, 32 * b2, 16 * s, lane), b, aq[b2]);
+      }
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        float xg[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * b2 + acc_row(r, hi);
+          xg[r] = scale * aq[b2][r] * (float)Qr[t * LDK + cc];
+          aq[b2][r] *= scale * __expf(gs[t]);
+        }
+        const float sg = rowsum16(xg, lane);
+        if (!(lane & 1)) red_g[wave][32 * b2 + acc_row(rowsum16_elem(lane), hi)] += sg;
+      }
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 b = frag_t(Kr, LDK, 16 * s, 32 * wave, lane);
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) aq[b2] = mfma(frag_n(Pr, LDP, 32 * b2, 16 * s, lane), b, aq[b2]);
+      }
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * b2 + acc_row(r, hi);
+          const int j = j0 + t;
+          if (j >= sq.n_replay && j < sq.n_tok) st_g<TG>(dq + ((int64_t)rw[t] * H + head) * kD + cc, aq[b2][r]);
+        }
+    }
+    // -- dK = dP~^T Q + dKk K + dKk^T K + diag(E_63,.) U dS - diag(beta gamma) dR S0 -----------
+    {
+      f32x16 ak[2];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) ak[b2] = zero16();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 bq = frag_t(Qr, LDK, 16 * s, 32 * wave, lane);
+        const f16x8 bk = frag_t(Kr, LDK, 16 * s, 32 * wave, lane);
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+          ak[b2] = mfma(frag_t(Pr, LDP, 16 * s, 32 * b2, lane), bq, ak[b2]);
+          ak[b2] = mfma(frag_n(Kk, LDP, 32 * b2, 16 * s, lane), bk, ak[b2]);
+          ak[b2] = mfma(frag_t(Kk, LDP, 16 * s, 32 * b2, lane), bk, ak[b2]);
+        }
+      }
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        f32x16 ud = zero16();
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          ud = mfma(frag_n(Ur, LDK, 32 * b2, 16 * s, lane), frag_t(dSh, LDK, 16 * s, 32 * wave, lane), ud);
+        float xe[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * b2 + acc_row(r, hi);
+          xe[r] = ud[r] * (float)Kr[t * LDK + cc];
+          ak[b2][r] = fmaf(__expf(g63 - gs[t]), ud[r], ak[b2][r]);
+        }
+        const float se = rowsum16(xe, lane);
+        if (!(lane & 1)) red_e[wave][32 * b2 + acc_row(rowsum16_elem(lane), hi)] += se;
+      }
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        f32x16 rs0 = zero16();
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          rs0 = mfma(frag_n(dRr, LDK, 32 * b2, 16 * s, lane), frag_g(S0t, 32 * wave, 16 * s, lane), rs0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * b2 + acc_row(r, hi);
+          ak[b2][r] = fmaf(-bs[t] * __expf(gs[t]), rs0[r], ak[b2][r]);
+        }
+      }
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * b2 + acc_row(r, hi);
+          const int j = j0 + t;
+          if (j >= sq.n_tok) continue;
+          if (j < sq.n_replay) {
+            rbuf[((int64_t)(sq.rep_off + j) * H + head) * kRep + cc] = ak[b2][r];
+          } else {
+            const int rsl = rep_slot[rw[t]];
+            if (rsl >= 0) rside[((int64_t)rsl * H + head) * 2 * kD + cc] = ak[b2][r];
+            else st_g<TG>(dk + ((int64_t)rw[t] * H + head) * kD + cc, ak[b2][r]);
+          }
+        }
+    }
+    __syncthreads();
+
+    // -- per-token dbeta, dalpha (reverse cumulative sum of dg) --------------------------------
+    if (tid < kB) {
+      const int t = tid;
+      const float en = __expf(g63 - gs[t]);
+      float e_t = 0.f, dgp = 0.f, dgam = 0.f, db = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        dgp += red_dg[w][t];
+        dgam += red_g[w][t];
+        db += red_b[w][t];
+        e_t += red_e[w][t];
+      }
+      float dg = dgp + __expf(gs[t]) * dgam - e_t * en;
+      float tot = e_t * en;  // sum over the chunk of dEn_i E_63,i goes to g_63
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off);
+      if (t == kB - 1) dg += tot + __expf(g63) * (red_s[0] + red_s[1] + red_s[2] + red_s[3]);
+      // reverse inclusive scan: dlogalpha_t = sum_{s >= t} dg_s
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_down(dg, off, 64);
+        if (t + off < 64) dg += y;
+      }
+      const int j = j0 + t;
+      if (j < sq.n_tok) {
+        const float da = dg / al[t];
+        if (j < sq.n_replay) {
+          float* rb = rbuf + ((int64_t)(sq.rep_off + j) * H + head) * kRep;
+          rb[2 * kD] = db;
+          rb[2 * kD + 1] = da;
+        } else {
+          dbeta[(int64_t)rw[t] * H + head] = db;
+          dalpha[(int64_t)rw[t] * H + head] = da;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  if (sq.cgrad >= 0) {
+    float* dst = cgrad + ((int64_t)sq.cgrad * H + head) * kD * kD;
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32] = D[nb][r];
+  }
+}
+
+// Rows that are replayed somewhere: own contribution (kept in fp32) plus every
+// replayed occurrence's, in schedule order.  Grid: (rows with replays) x H;
+// kFixThreads >= kRep threads, one per record element.
+constexpr int kFixThreads = 320;
+template <typename TG>
+__global__ __launch_bounds__(kFixThreads) void gdn_fixup_kernel(const int32_t* __restrict__ rep_rows,
+                                                        const int32_t* __restrict__ rep_off,
+                                                        const int32_t* __restrict__ rep_tok,
+                                                        const float* __restrict__ rside,
+                                                        const float* __restrict__ rbuf, TG* __restrict__ dk,
+                                                        TG* __restrict__ dv, float* __restrict__ dbeta,
+                                                        float* __restrict__ dalpha, int H) {
+  const int head = blockIdx.x % H;
+  const int rs = blockIdx.x / H;
+  const int row = rep_rows[rs];
+  const int tid = threadIdx.x;
+  const int e0 = rep_off[rs], e1 = rep_off[rs + 1];
+  float acc = tid < 2 * kD ? rside[((int64_t)rs * H + head) * 2 * kD + tid] : 0.f;
+  if (tid == 2 * kD) acc = dbeta[(int64_t)row * H + head];
+  if (tid == 2 * kD + 1) acc = dalpha[(int64_t)row * H + head];
+  if (tid < kRep)
+    for (int e = e0; e < e1; ++e) acc += rbuf[((int64_t)rep_tok[e] * H + head) * kRep + tid];
+  if (tid < kD) st_g<TG>(dk + ((int64_t)row * H + head) * kD + tid, acc);
+  else if (tid < 2 * kD) st_g<TG>(dv + ((int64_t)row * H + head) * kD + tid - kD, acc);
+  else if (tid == 2 * kD) dbeta[(int64_t)row * H + head] = acc;
+  else if (tid == 2 * kD + 1) dalpha[(int64_t)row * H + head] = acc;
+}
+
+// Zero the padding rows of a [C, H, W] tensor.  Grid: pages x H.
+template <typename T>
+__global__ __launch_bounds__(256) void gdn_pad_kernel(T* __restrict__ x, const int32_t* __restrict__ page_nrows,
+                                                      int H, int W) {
+  const int head = blockIdx.x % H;
+  const int64_t page = blockIdx.x / H;
+  const int n = page_nrows[page];
+  for (int i = threadIdx.x; i < (kB - n) * W; i += 256) {
+    const int64_t row = page * kB + n + i / W;
+    x[(row * H + head) * W + i % W] = T(0);
+  }
+}
+
+}  // namespace gdn
+
+// ---------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------
+void launch_gdn_fwd(const GdnShape& s, int n_seq, const int32_t* order, bool states_only, const bf16_t* q,
+                    const bf16_t* k, const bf16_t* v, const float* beta, const float* alpha, bf16_t* o,
+                    float* slots, f16_t* states, hipStream_t st) {
+  if (n_seq <= 0) return;
+  const dim3 grid((unsigned)(n_seq * s.H));
+  if (states_only)
+    gdn::gdn_fwd_kernel<true><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha, o,
+                                                    slots, states, s.H, s.scale);
+  else
+    gdn::gdn_fwd_kernel<false><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha, o,
+                                                     slots, states, s.H, s.scale);
+}
+
+template <typename TG>
+void launch_gdn_bwd(const GdnShape& s, int n_seq, const int32_t* order, const bf16_t* q, const bf16_t* k,
+                    const bf16_t* v, const float* beta, const float* alpha, const bf16_t* dO, const f16_t* states,
+                    float* cgrad, TG* dq, TG* dk, TG* dv, float* dbeta, float* dalpha, float* rside, float* rbuf,
+                    hipStream_t st) {
+  if (n_seq <= 0) return;
+  gdn::gdn_bwd_kernel<TG><<<dim3((unsigned)(n_seq * s.H)), 256, 0, st>>>(
+      s.seqs, order, s.rows, s.exports, s.slot_off, s.slot_cons, s.rep_slot, q, k, v, beta, alpha, dO, states, cgrad,
+      dq, dk, dv, dbeta, dalpha, rside, rbuf, s.H, s.scale);
+}
+
+template <typename TG>
+void launch_gdn_fixup(const GdnShape& s, int n_rows, const float* rside, const float* rbuf, TG* dk, TG* dv,
+                      float* dbeta, float* dalpha, hipStream_t st) {
+  if (n_rows <= 0) return;
+  static_assert(gdn::kFixThreads >= gdn::kRep, "one thread per replay-record element");
+  gdn::gdn_fixup_kernel<TG><<<dim3((unsigned)(n_rows * s.H)), gdn::kFixThreads, 0, st>>>(s.rep_rows, s.rep_off, s.rep_tok, rside,
+                                                                           rbuf, dk, dv, dbeta, dalpha, s.H);
+}
+
+template <typename T>
+void launch_gdn_pad(int64_t pages, const int32_t* page_nrows, T* x, int H, int W, hipStream_t st) {
+  if (pages <= 0) return;
+  gdn::gdn_pad_kernel<T><<<dim3((unsigned)(pages * H)), 256, 0, st>>>(x, page_nrows, H, W);
+}
+
+template void launch_gdn_bwd<bf16_t>(const GdnShape&, int, const int32_t*, const bf16_t*, const bf16_t*,
+                                     const bf16_t*, const float*, const float*, const bf16_t*, const f16_t*, float*,
+                                     bf16_t*, bf16_t*, bf16_t*, float*, float*, float*, float*, hipStream_t);
+template void launch_gdn_bwd<float>(const GdnShape&, int, const int32_t*, const bf16_t*, const bf16_t*,
+                                    const bf16_t*, const float*, const float*, const bf16_t*, const f16_t*, float*,
+                                    float*, float*, float*, float*, float*, float*, float*, hipStream_t);
+template void launch_gdn_fixup<bf16_t>(const GdnShape&, int, const float*, const float*, bf16_t*, bf16_t*, float*,
+                                       float*, hipStream_t);
+template void launch_gdn_fixup<float>(const GdnShape&, int, const float*, const float*, float*, float*, float*,
+                                      float*, hipStream_t);
+template void launch_gdn_pad<bf16_t>(int64_t, const int32_t*, bf16_t*, int, int, hipStream_t);
+template void launch_gdn_pad<float>(int64_t, const int32_t*, float*, int, int, hipStream_t);
+
+}  // namespace dagattn

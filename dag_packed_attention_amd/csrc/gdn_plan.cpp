@@ -173,7 +173,7 @@ dag_status build_gdn_schedule(Plan* P, int32_t B, std::string* err) {
   P->gseqs.assign(NS, GSeq{});
   P->gseq_info.assign(NS, dag_gdn_seq{});
   P->grows.clear();
-  std::vector<std::pair<int32_t, int32_t>> rep;  // (row, token index) of replayed tokens
+  std::vector<std::pair<int32_t, int32_t>> rep;  // (row, replay index) of replayed tokens
   int64_t replay_total = 0, chunks = 0;
   int32_t rounds = 0;
   for (int32_t q = 0; q < NS; ++q) {
@@ -182,6 +182,7 @@ dag_status build_gdn_schedule(Plan* P, int32_t B, std::string* err) {
     g.tok_off = (int32_t)P->grows.size();
     g.start = (int32_t)s.start;
     g.n_replay = (int32_t)(s.fork - s.start);
+    g.rep_off = (int32_t)replay_total;
     if (g.n_replay > 0) {
       std::vector<int64_t> back;  // token ids, last first
       int32_t x = segs[segs[s.segs[0]].parent].nodes.back();
@@ -192,7 +193,7 @@ dag_status build_gdn_schedule(Plan* P, int32_t B, std::string* err) {
         x = P->parent[x];
       }
       for (auto it = back.rbegin(); it != back.rend(); ++it) {
-        rep.push_back({P->row_of_token[*it], (int32_t)P->grows.size()});
+        rep.push_back({P->row_of_token[*it], (int32_t)rep.size()});
         P->grows.push_back(P->row_of_token[*it]);
       }
     }
@@ -276,13 +277,16 @@ dag_status build_gdn_schedule(Plan* P, int32_t B, std::string* err) {
   }
 
   // -- 8. replay fix-up lists: per row, its replayed occurrences in schedule order ------
+  // (replay index = position of the token among all replayed tokens, sequence order)
   std::sort(rep.begin(), rep.end());
+  P->grep_slot.assign(P->info.rows, -1);
   P->grep_rows.clear();
   P->grep_off.assign(1, 0);
   P->grep_tok.clear();
   for (size_t i = 0; i < rep.size(); ++i) {
     if (i == 0 || rep[i].first != rep[i - 1].first) {
       if (i) P->grep_off.push_back((int32_t)P->grep_tok.size());
+      P->grep_slot[rep[i].first] = (int32_t)P->grep_rows.size();
       P->grep_rows.push_back(rep[i].first);
     }
     P->grep_tok.push_back(rep[i].second);

@@ -53,7 +53,9 @@ struct GSeq {
   int32_t cgrad;      // index of its initial-state gradient buffer; -1 when init_slot < 0
   int32_t exp_off, exp_cnt;  // its exported boundary states: gexports[exp_off ..)
   int32_t chunk_off;  // first entry of its per-chunk saved states
-  int32_t round, pad0, pad1;
+  int32_t round;
+  int32_t rep_off;    // replay index of its first replayed token (replay gradients)
+  int32_t pad0;
 };
 // An exported boundary: the state after `chunk` chunks of the sequence goes to `slot`.
 struct GExport {
@@ -94,7 +96,9 @@ struct Plan {
   std::vector<GExport> gexports;
   std::vector<int32_t> gslot_off, gslot_cons;  // slot -> consumers' cgrad ids, sequence order
   std::vector<int32_t> ground_off, ground_seq; // round r (0-based) -> sequences, most tokens first
-  std::vector<int32_t> grep_rows, grep_off, grep_tok;  // replay fix-up: row -> token indices into grows
+  // replay fix-up: rows that are replayed somewhere, each with its replay indices
+  // (in schedule order); grep_slot maps every row to its position in grep_rows or -1
+  std::vector<int32_t> grep_rows, grep_off, grep_tok, grep_slot;
   int32_t gdn_ncgrad = 0;
   dag_plan_info info{};
   DeviceTables* dev = nullptr;
