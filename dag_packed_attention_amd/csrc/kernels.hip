@@ -615,29 +615,27 @@ __device__ __forceinline__ f16x8 frag_tr(const f16_t* t, int kk, int dblk, int l
   return out;
 }
 
-// Sum one accumulator set (dK or dV, 64 keys x 128 d) over the work-group's four
-// waves in head order through LDS, scale it and write it out; dK is rotated back
-// by R(pos)^T.
+// Sum one accumulator set (dK or dV) over the four query heads through LDS, in
+// head order, then scale, rotate dK back by R(pos)^T and write the page's 64
+// rows once.  Wave (head hh, key block kb) holds keys 32 kb .. 32 kb + 31.
 template <bool kRotate, typename TG>
-__device__ __forceinline__ void dkdv_reduce_store(const f32x16 (&acc)[2][4], float* red, int wave, int hi,
+__device__ __forceinline__ void dkdv_reduce_store(const f32x16 (&acc)[4], float* red, int hh, int kb, int hi,
                                                   int l32, int tid, int page, int g, int krows, int Hkv,
                                                   float mul, const float2* __restrict__ cs, TG* __restrict__ out) {
   for (int w = 0; w < 4; ++w) {
     __syncthreads();
-    if (wave == w) {
+    if (hh == w) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int b = 0; b < 4; ++b)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float* slot = red + (kb * 32 + acc_row(r, hi)) * (kD + 1) + b * 32 + l32;
-            *slot = (w == 0) ? acc[kb][b][r] : *slot + acc[kb][b][r];
-          }
+        for (int r = 0; r < 16; ++r) {
+          float* slot = red + (kb * 32 + acc_row(r, hi)) * (kD + 1) + b * 32 + l32;
+          *slot = (w == 0) ? acc[b][r] : *slot + acc[b][r];
+        }
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < 64 * 64; idx += 256) {
+  for (int idx = tid; idx < 64 * 64; idx += 512) {
     const int k2 = idx / 64, i = idx % 64;
     const int64_t grow = (int64_t)page * 64 + k2;
     float a = red[k2 * (kD + 1) + i] * mul, b = red[k2 * (kD + 1) + i + 64] * mul;
@@ -655,18 +653,18 @@ __device__ __forceinline__ void dkdv_reduce_store(const f32x16 (&acc)[2][4], flo
   }
 }
 
-// dK, dV for one KV page x one KV head.  Four waves = the four query heads of
-// the group; each owns all 64 keys of the page and keeps its dK and dV
-// (64 x 128 each) in accumulation registers across the page's whole reader
-// list, with the page's K and V fragments in registers too.  The reader list is
-// walked in steps of 32 query rows: each step stages the four heads' Q and dO
-// rows (and their (lse, D) pairs) in LDS with direct global loads, double
-// buffered; S and dP read row fragments from those tiles, dV and dK read
-// column fragments of the same tiles with the transpose read.  At the end the
-// four heads are summed through LDS in head order and written once:
-// deterministic, no atomics.
+// dK, dV for one KV page x one KV head.  Eight waves: wave (hh, kb) serves
+// query head 4 g + hh and keys 32 kb .. 32 kb + 31 of the page, keeping its dK
+// and dV (32 x 128 each) in accumulation registers across the page's whole
+// reader list, with its K fragments in registers too; two waves per SIMD hide
+// each other's LDS and barrier waits.  The reader list is walked in steps of 32
+// query rows: each step stages the four heads' Q and dO rows (and their
+// (lse, D) pairs) in LDS with direct global loads, double buffered; S and dP
+// read row fragments from those tiles, dV and dK read column fragments of the
+// same tiles with the transpose read.  At the end the four heads are summed
+// through LDS in head order and written once: deterministic, no atomics.
 template <typename TG>
-__global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
+__global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vn,
     const f16_t* __restrict__ dOn, const float2* __restrict__ ldd, const float2* __restrict__ cs,
     const uint32_t* __restrict__ dmax, const int32_t* __restrict__ order, const int32_t* __restrict__ kv_off,
@@ -686,25 +684,21 @@ __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int h = g * 4 + wave;
+  const int hh = wave & 3, kb = wave >> 2;
   const int krows = page_nrows[page];
 
-  // this page's K fragments (B operand of S = Q K^T) live in registers; its V
-  // tile (B operand of dP = dO V^T) in LDS
-  f16x8 kf[2][8];
+  // this wave's K fragments (B operand of S = Q K^T) live in registers; the page's
+  // V tile (B operand of dP = dO V^T) in LDS
+  f16x8 kf[8];
   {
     const int64_t base = ((int64_t)page * Hkv + g) * 64 * kD;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) kf[kb][ks] = ld8(kn + base + (kb * 32 + l32) * kD + ks * 16 + hi * 8);
-    load_tile_rows(lvp, vn + base, wave, lane);
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = ld8(kn + base + (kb * 32 + l32) * kD + ks * 16 + hi * 8);
+    if (wave < 4) load_tile_rows(lvp, vn + base, wave, lane);
   }
-  f32x16 adk[2][4], adv[2][4];  // [key block][d block]
+  f32x16 adk[4], adv[4];  // [d block]
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) adk[a][b] = adv[a][b] = zero16();
+  for (int b = 0; b < 4; ++b) adk[b] = adv[b] = zero16();
 
   // reader-list cursor: entry e, reader page lq, row block rb (32 rows)
   const int n_steps = kv_steps[page];
@@ -713,28 +707,26 @@ __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
   int lq = ent.lq0, rb = 0;
   int qph = page_table[ent.slot_base + lq];
   auto stage = [&](int buf, int qp_, int rb_) {
-    // wave w fetches head 4 g + w: Q rows then dO rows, 8 KiB each = 8 + 8 wave loads
-    const int64_t src = (((int64_t)qp_ * Hq + g * 4 + wave) * 64 + rb_ * 32) * kD;
+    // wave (hh, kb) fetches head 4 g + hh's Q rows (kb = 0) or dO rows (kb = 1): 8 KiB
+    const int64_t src = (((int64_t)qp_ * Hq + g * 4 + hh) * 64 + rb_ * 32) * kD;
+    const f16_t* gsrc = (kb == 0 ? qn : dOn) + src;
+    f16_t* dst = qd[buf][hh][kb];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const f16_t* gsrc = (t == 0 ? qn : dOn) + src;
-      f16_t* dst = qd[buf][wave][t];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int q = i * 64 + lane;  // 16-byte slot
-        const int r = q >> 4, c = (q & 15) ^ swz32(r);
-        __builtin_amdgcn_global_load_lds(gsrc + r * kD + c * 8, (lds_void*)(dst + i * 512), 16, 0, 0);
-      }
+    for (int i = 0; i < 8; ++i) {
+      const int q = i * 64 + lane;  // 16-byte slot
+      const int r = q >> 4, c = (q & 15) ^ swz32(r);
+      __builtin_amdgcn_global_load_lds(gsrc + r * kD + c * 8, (lds_void*)(dst + i * 512), 16, 0, 0);
     }
-    if (lane < 16)
-      __builtin_amdgcn_global_load_lds(ldd + ((int64_t)qp_ * Hq + g * 4 + wave) * 64 + rb_ * 32 + lane * 2,
-                                       (lds_void*)(&lds_ld[buf][wave][0]), 16, 0, 0);
+    if (kb == 0 && lane < 16)
+      __builtin_amdgcn_global_load_lds(ldd + ((int64_t)qp_ * Hq + g * 4 + hh) * 64 + rb_ * 32 + lane * 2,
+                                       (lds_void*)(&lds_ld[buf][hh][0]), 16, 0, 0);
   };
   stage(0, qph, 0);
   wait_all_loads();
   __syncthreads();
 
   int buf = 0;
+  const int key = kb * 32 + l32;
   for (int it = 0; it < n_steps; ++it) {
     // where the next step is (a reader page of <= 32 rows has one row block)
     const bool more = it + 1 < n_steps;
@@ -753,61 +745,47 @@ __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
     const int lo = ent.lohi_diag & 0xff, hi_t = (ent.lohi_diag >> 8) & 0xff;
     const bool diag = (ent.lohi_diag >> 16) & 1;
     const bool full = lo == 0 && hi_t == 64 && !diag && nrows >= rb * 32 + 32;
-    const f16_t* Qt = qd[buf][wave][0];
-    const f16_t* Dt = qd[buf][wave][1];
-    const float2* LD = lds_ld[buf][wave];
-    // S = Q K^T, dP = dO V^T: 32 rows (M) x 64 keys (N, two blocks); lane holds keys
+    const f16_t* Qt = qd[buf][hh][0];
+    const f16_t* Dt = qd[buf][hh][1];
+    const float2* LD = lds_ld[buf][hh];
+    // S = Q K^T, dP = dO V^T: 32 rows (M) x this wave's 32 keys (N); lane holds key
     // kb*32 + l32 and rows rb*32 + acc_row(r, hi)
-    f32x16 sa[2], dpa[2];
-    sa[0] = sa[1] = dpa[0] = dpa[1] = zero16();
+    f32x16 s = zero16(), dp = zero16();
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-      const f16x8 qa = frag_q(Qt, l32, ks * 2 + hi), da = frag_q(Dt, l32, ks * 2 + hi);
+      s = mfma(frag_q(Qt, l32, ks * 2 + hi), kf[ks], s);
+      dp = mfma(frag_q(Dt, l32, ks * 2 + hi), frag_rows(lvp, key, ks * 2 + hi), dp);
+    }
+    if (full) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        sa[kb] = mfma(qa, kf[kb][ks], sa[kb]);
-        dpa[kb] = mfma(da, frag_rows(lvp, kb * 32 + l32, ks * 2 + hi), dpa[kb]);
+      for (int r = 0; r < 16; ++r) {
+        const float2 lr = LD[acc_row(r, hi)];
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr.x));
+        s[r] = p;
+        dp[r] = p * (dp[r] - lr.y);
+      }
+    } else {
+      // every operand here comes from the zero-padded relayouts, so all values are
+      // finite and a 0/1 factor masks without branches
+      const bool key_ok = key >= lo && key < hi_t;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float2 lr = LD[acc_row(r, hi)];
+        const int row = rb * 32 + acc_row(r, hi);
+        const float okf = (key_ok && (!diag || key <= row) && row < nrows) ? 1.f : 0.f;
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr.x)) * okf;
+        s[r] = p;
+        dp[r] = p * (dp[r] - lr.y);
       }
     }
+    const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8), sf0 = pack8(dp, 0), sf1 = pack8(dp, 8);
+    // dV += P^T dO, dK += dS^T Q: keys (M) x d (N), the 32 rows contracted
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16& s = sa[kb];
-      f32x16& dp = dpa[kb];
-      const int key = kb * 32 + l32;
-      if (full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float2 lr = LD[acc_row(r, hi)];
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr.x));
-          s[r] = p;
-          dp[r] = p * (dp[r] - lr.y);
-        }
-      } else {
-        // every operand here comes from the zero-padded relayouts, so all values are
-        // finite and a 0/1 factor masks without branches
-        const bool key_ok = key >= lo && key < hi_t;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float2 lr = LD[acc_row(r, hi)];
-          const int row = rb * 32 + acc_row(r, hi);
-          const float okf = (key_ok && (!diag || key <= row) && row < nrows) ? 1.f : 0.f;
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr.x)) * okf;
-          s[r] = p;
-          dp[r] = p * (dp[r] - lr.y);
-        }
-      }
-      const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8), sf0 = pack8(dp, 0), sf1 = pack8(dp, 8);
-      // dV += P^T dO, dK += dS^T Q: keys (M) x d (N), the 32 rows contracted
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        // a compiler-only fence per block: without it the scheduler hoists every
-        // block's fragment reads at once and runs out of registers
-        asm volatile("" ::: "memory");
-        adv[kb][b] = mfma(pf0, frag_tr(Dt, 0, b, lane), adv[kb][b]);
-        adv[kb][b] = mfma(pf1, frag_tr(Dt, 1, b, lane), adv[kb][b]);
-        adk[kb][b] = mfma(sf0, frag_tr(Qt, 0, b, lane), adk[kb][b]);
-        adk[kb][b] = mfma(sf1, frag_tr(Qt, 1, b, lane), adk[kb][b]);
-      }
+    for (int b = 0; b < 4; ++b) {
+      adv[b] = mfma(pf0, frag_tr(Dt, 0, b, lane), adv[b]);
+      adv[b] = mfma(pf1, frag_tr(Dt, 1, b, lane), adv[b]);
+      adk[b] = mfma(sf0, frag_tr(Qt, 0, b, lane), adk[b]);
+      adk[b] = mfma(sf1, frag_tr(Qt, 1, b, lane), adk[b]);
     }
     wait_all_loads();
     __syncthreads();
@@ -823,8 +801,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_mfma_kernel(
   float* red = reinterpret_cast<float*>(&qd[0][0][0][0]);  // [64][129] fp32
   // sum the four heads in order 0..3 through LDS, then write dk (scaled, un-rotated)
   // and dv
-  dkdv_reduce_store<true>(adk, red, wave, hi, l32, tid, page, g, krows, Hkv, inv_sdo * scale, cs, dk);
-  dkdv_reduce_store<false>(adv, red, wave, hi, l32, tid, page, g, krows, Hkv, inv_sdo, cs, dv);
+  dkdv_reduce_store<true>(adk, red, hh, kb, hi, l32, tid, page, g, krows, Hkv, inv_sdo * scale, cs, dk);
+  dkdv_reduce_store<false>(adv, red, hh, kb, hi, l32, tid, page, g, krows, Hkv, inv_sdo, cs, dv);
 }
 
 // ---------------------------------------------------------------------------
@@ -1069,7 +1047,7 @@ void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, cons
                       const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
                       const int32_t* order, const int32_t* kv_off, const int32_t* kv_steps, const KEntry* ents,
                       const int32_t* page_table, const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st) {
-  dkdv_mfma_kernel<TG><<<run_grid(n_kvp, s.Hkv), 256, 0, st>>>(qn, kn, vn, dOn, ld, cs, dmax, order, kv_off,
+  dkdv_mfma_kernel<TG><<<run_grid(n_kvp, s.Hkv), 512, 0, st>>>(qn, kn, vn, dOn, ld, cs, dmax, order, kv_off,
                                                                kv_steps, ents, page_table, page_nrows, dk, dv,
                                                                (int)n_kvp, s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
 }
