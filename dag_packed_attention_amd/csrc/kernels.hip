@@ -279,11 +279,12 @@ __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0)
 
 constexpr int kTile = 64 * kD;  // elements of an unpadded 64 x 128 (or 128 x 64) tile
 
-// Forward for one 64-row query block x one KV head; waves = the four query heads.
-// K/V tiles are double-buffered in LDS and fetched straight from global memory
-// while the previous tile is multiplied; each 64-key tile is taken as two
-// 32-key halves to keep the score registers small.
-__global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
+// Forward for one 64-row query block x one KV head.  Eight waves: wave (hh, nb)
+// serves query head 4 g + hh and rows 32 nb .. 32 nb + 31 (two waves per SIMD,
+// so one wave's softmax overlaps the other's products).  K/V tiles are
+// double-buffered in LDS and fetched straight from global memory while the
+// previous tile is multiplied; each 64-key tile is taken as two 32-key halves.
+__global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vt,
     const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
     bf16_t* __restrict__ o, float* __restrict__ lse, bf16_t* __restrict__ o_lo, int n_qp, int Hq, int Hkv,
@@ -296,24 +297,22 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int h = g * 4 + wave;
+  const int hh = wave & 3, nb = wave >> 2;
+  const int h = g * 4 + hh;
+  const int row = nb * 32 + l32;
 
-  f16x8 qf[2][8];
+  f16x8 qf[8];
   const f16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[nb][ks] = ld8(qb + (nb * 32 + l32) * kD + ks * 16 + hi * 8);
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = ld8(qb + row * kD + ks * 16 + hi * 8);
 
-  f32x16 oacc[4][2];
+  f32x16 oacc[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) oacc[a][b] = zero16();
-  float mrow[2] = {-INFINITY, -INFINITY}, lrow[2] = {0.f, 0.f};
+  for (int a = 0; a < 4; ++a) oacc[a] = zero16();
+  float mrow = -INFINITY, lrow = 0.f;
 
   const int T = qp.tile_count;
-  {
+  if (wave < 4) {
     const int64_t base = ((int64_t)tiles[qp.tile_begin].page * Hkv + g) * kTile;
     load_tile_rows(lk[0], kn + base, wave, lane);
     load_tile_cols(lv[0], vt + base, wave, lane);
@@ -323,7 +322,7 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
 
   for (int t = 0; t < T; ++t) {
     const int buf = t & 1;
-    if (t + 1 < T) {
+    if (t + 1 < T && wave < 4) {
       const int64_t base = ((int64_t)tiles[qp.tile_begin + t + 1].page * Hkv + g) * kTile;
       load_tile_rows(lk[buf ^ 1], kn + base, wave, lane);
       load_tile_cols(lv[buf ^ 1], vt + base, wave, lane);
@@ -337,111 +336,93 @@ __global__ __launch_bounds__(256, 1) void fwd_mfma_kernel(
 
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {  // 32-key halves
-      f32x16 s[2];
-      s[0] = zero16();
-      s[1] = zero16();
+      f32x16 s = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const f16x8 a = frag_rows(K, mb * 32 + l32, ks * 2 + hi);
-        s[0] = mfma(a, qf[0][ks], s[0]);
-        s[1] = mfma(a, qf[1][ks], s[1]);
-      }
+      for (int ks = 0; ks < 8; ++ks) s = mfma(frag_rows(K, mb * 32 + l32, ks * 2 + hi), qf[ks], s);
       // Online softmax in the log2 domain.  The running max m is raised only when
       // a row's new maximum exceeds it by more than kLazy (any lane of the wave),
       // so the accumulator rescale is rare; in between, probabilities reach at most
       // 2^kLazy, well inside fp16, and the final division by l removes the offset.
       constexpr float kLazy = 8.f;
-      f16x8 pf[2][2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int row = nb * 32 + l32;
-        if (!full) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = mb * 32 + acc_row(r, hi);
-            const bool ok = key >= lo && key < hi_t && (!diag || key <= row);
-            s[nb][r] = ok ? s[nb][r] : -INFINITY;
-          }
-        }
-        float mx = s[nb][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[nb][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-        if (__any(mx > mrow[nb] + kLazy)) {
-          const float mnew = fmaxf(mrow[nb], mx);
-          const float alpha = __builtin_amdgcn_exp2f(mrow[nb] - mnew);
-          mrow[nb] = mnew;
-          lrow[nb] *= alpha;
-#pragma unroll
-          for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[a][nb][r] *= alpha;
-        }
-        // a half-tile can be fully masked before a row has seen any key (a mounted
-        // span starting past key 32); then m is still -inf and every score is -inf
-        const float mneg = mrow[nb] == -INFINITY ? 0.f : -mrow[nb];
-        float sum = 0.f;
+      if (!full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, mneg));
-          s[nb][r] = p;
-          sum += p;
+          const int key = mb * 32 + acc_row(r, hi);
+          const bool ok = key >= lo && key < hi_t && (!diag || key <= row);
+          s[r] = ok ? s[r] : -INFINITY;
         }
-        lrow[nb] += sum;
-        pf[0][nb] = pack8(s[nb], 0);
-        pf[1][nb] = pack8(s[nb], 8);
       }
+      float mx = s[0];
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      if (__any(mx > mrow + kLazy)) {
+        const float mnew = fmaxf(mrow, mx);
+        const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+        mrow = mnew;
+        lrow *= alpha;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const f16x8 va = frag_cols(V, a * 32 + l32, (mb * 2 + kk) * 2 + hi);
-          oacc[a][0] = mfma(va, pf[kk][0], oacc[a][0]);
-          oacc[a][1] = mfma(va, pf[kk][1], oacc[a][1]);
-        }
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[a][r] *= alpha;
+      }
+      // a half-tile can be fully masked before a row has seen any key (a mounted
+      // span starting past key 32); then m is still -inf and every score is -inf
+      const float mneg = mrow == -INFINITY ? 0.f : -mrow;
+      float sum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, mneg));
+        s[r] = p;
+        sum += p;
+      }
+      lrow += sum;
+      const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        oacc[a] = mfma(frag_cols(V, a * 32 + l32, (mb * 2 + 0) * 2 + hi), pf0, oacc[a]);
+        oacc[a] = mfma(frag_cols(V, a * 32 + l32, (mb * 2 + 1) * 2 + hi), pf1, oacc[a]);
+      }
     }
     wait_all_loads();
     __syncthreads();
   }
 
+  const float l = lrow + __shfl_xor(lrow, 32);
+  const bool valid = row < qp.nrows;
+  const float inv = valid ? 1.f / l : 0.f;
+  const int64_t grow = (int64_t)qp.phys * 64 + row;
+  bf16_t* orow = o + (grow * Hq + h) * kD;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int row = nb * 32 + l32;
-    const float l = lrow[nb] + __shfl_xor(lrow[nb], 32);
-    const bool valid = row < qp.nrows;
-    const float inv = valid ? 1.f / l : 0.f;
-    const int64_t grow = (int64_t)qp.phys * 64 + row;
-    bf16_t* orow = o + (grow * Hq + h) * kD;
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+    for (int j = 0; j < 4; ++j) {
+      const int d = a * 32 + 8 * j + 4 * hi;
+      bf16_t hv[4], lv4[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = a * 32 + 8 * j + 4 * hi;
-        bf16_t hv[4], lv4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = oacc[a][nb][4 * j + i] * inv;
-          hv[i] = f2bf(x);
-          lv4[i] = f2bf(x - bf2f(hv[i]));
-        }
-        uint2 w;
-        w.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
-        w.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
-        *reinterpret_cast<uint2*>(orow + d) = w;
-        if (o_lo) {
-          w.x = (uint32_t)lv4[0] | ((uint32_t)lv4[1] << 16);
-          w.y = (uint32_t)lv4[2] | ((uint32_t)lv4[3] << 16);
-          *reinterpret_cast<uint2*>(o_lo + (grow * Hq + h) * kD + d) = w;
-        }
+      for (int i = 0; i < 4; ++i) {
+        const float x = oacc[a][4 * j + i] * inv;
+        hv[i] = f2bf(x);
+        lv4[i] = f2bf(x - bf2f(hv[i]));
       }
-    if (hi == 0) lse[grow * Hq + h] = valid ? (mrow[nb] + __log2f(l)) * kLn2 : 0.f;
-  }
+      uint2 w;
+      w.x = (uint32_t)hv[0] | ((uint32_t)hv[1] << 16);
+      w.y = (uint32_t)hv[2] | ((uint32_t)hv[3] << 16);
+      *reinterpret_cast<uint2*>(orow + d) = w;
+      if (o_lo) {
+        w.x = (uint32_t)lv4[0] | ((uint32_t)lv4[1] << 16);
+        w.y = (uint32_t)lv4[2] | ((uint32_t)lv4[3] << 16);
+        *reinterpret_cast<uint2*>(o_lo + (grow * Hq + h) * kD + d) = w;
+      }
+    }
+  if (hi == 0) lse[grow * Hq + h] = valid ? (mrow + __log2f(l)) * kLn2 : 0.f;
 }
 
-// dQ for one query block (64 rows) x one KV head; waves = the four query heads.
-// The K, V and K^T tiles are double-buffered in LDS like the forward's.
+// dQ for one query block (64 rows) x one KV head.  Eight waves, wave (hh, nb) =
+// query head 4 g + hh and rows 32 nb ..; the K, V and K^T tiles are
+// double-buffered in LDS like the forward's.
 template <typename TG>
-__global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
+__global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ kt,
     const f16_t* __restrict__ vn, const f16_t* __restrict__ dOn, const float2* __restrict__ ldd,
     const float2* __restrict__ cs, const uint32_t* __restrict__ dmax, const QPage* __restrict__ qpages,
@@ -456,32 +437,26 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int l32 = lane & 31, hi = lane >> 5;
-  const int h = g * 4 + wave;
+  const int hh = wave & 3, nb = wave >> 2;
+  const int h = g * 4 + hh;
+  const int row = nb * 32 + l32;
 
-  f16x8 qf[2][8], df[2][8];
+  f16x8 qf[8], df[8];
   const f16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
   const f16_t* db = dOn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
-  float lse2[2], Dv[2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int row = nb * 32 + l32;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      qf[nb][ks] = ld8(qb + row * kD + ks * 16 + hi * 8);
-      df[nb][ks] = ld8(db + row * kD + ks * 16 + hi * 8);
-    }
-    const float2 t = ldd[((int64_t)qp.phys * Hq + h) * 64 + row];
-    lse2[nb] = t.x;
-    Dv[nb] = t.y;
+  for (int ks = 0; ks < 8; ++ks) {
+    qf[ks] = ld8(qb + row * kD + ks * 16 + hi * 8);
+    df[ks] = ld8(db + row * kD + ks * 16 + hi * 8);
   }
-  f32x16 acc[4][2];
+  const float2 lt = ldd[((int64_t)qp.phys * Hq + h) * 64 + row];
+  const float nl = -lt.x, Dv = lt.y;
+  f32x16 acc[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = zero16();
+  for (int a = 0; a < 4; ++a) acc[a] = zero16();
 
   const int T = qp.tile_count;
-  {
+  if (wave < 4) {
     const int64_t base = ((int64_t)tiles[qp.tile_begin].page * Hkv + g) * kTile;
     load_tile_rows(lk[0], kn + base, wave, lane);
     load_tile_rows(lvv[0], vn + base, wave, lane);
@@ -492,7 +467,7 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
 
   for (int t = 0; t < T; ++t) {
     const int buf = t & 1;
-    if (t + 1 < T) {
+    if (t + 1 < T && wave < 4) {
       const int64_t base = ((int64_t)tiles[qp.tile_begin + t + 1].page * Hkv + g) * kTile;
       load_tile_rows(lk[buf ^ 1], kn + base, wave, lane);
       load_tile_rows(lvv[buf ^ 1], vn + base, wave, lane);
@@ -507,76 +482,56 @@ __global__ __launch_bounds__(256, 1) void dq_mfma_kernel(
     const f16_t* KT = lkt[buf];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      f32x16 s[2], dp[2];
-      s[0] = s[1] = dp[0] = dp[1] = zero16();
+      f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        const f16x8 a = frag_rows(K, mb * 32 + l32, ks * 2 + hi);
-        const f16x8 b = frag_rows(V, mb * 32 + l32, ks * 2 + hi);
-        s[0] = mfma(a, qf[0][ks], s[0]);
-        s[1] = mfma(a, qf[1][ks], s[1]);
-        dp[0] = mfma(b, df[0][ks], dp[0]);
-        dp[1] = mfma(b, df[1][ks], dp[1]);
+        s = mfma(frag_rows(K, mb * 32 + l32, ks * 2 + hi), qf[ks], s);
+        dp = mfma(frag_rows(V, mb * 32 + l32, ks * 2 + hi), df[ks], dp);
       }
-      f16x8 dsf[2][2];
+      if (full) {
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int row = nb * 32 + l32;
-        const float nl = -lse2[nb];
-        if (full) {
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl)) * (dp[r] - Dv);
+      } else {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            s[nb][r] = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, nl)) * (dp[nb][r] - Dv[nb]);
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = mb * 32 + acc_row(r, hi);
-            const bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < qp.nrows;
-            const float p = __builtin_amdgcn_exp2f(fmaf(s[nb][r], sl2, nl));
-            s[nb][r] = ok ? p * (dp[nb][r] - Dv[nb]) : 0.f;  // padding may hold NaN
-          }
+        for (int r = 0; r < 16; ++r) {
+          const int key = mb * 32 + acc_row(r, hi);
+          const bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < qp.nrows;
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl));
+          s[r] = ok ? p * (dp[r] - Dv) : 0.f;  // padding may hold NaN
         }
-        dsf[0][nb] = pack8(s[nb], 0);
-        dsf[1][nb] = pack8(s[nb], 8);
       }
+      const f16x8 d0 = pack8(s, 0), d1 = pack8(s, 8);
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const f16x8 ka = frag_cols(KT, a * 32 + l32, (mb * 2 + kk) * 2 + hi);
-          acc[a][0] = mfma(ka, dsf[kk][0], acc[a][0]);
-          acc[a][1] = mfma(ka, dsf[kk][1], acc[a][1]);
-        }
+      for (int a = 0; a < 4; ++a) {
+        acc[a] = mfma(frag_cols(KT, a * 32 + l32, (mb * 2 + 0) * 2 + hi), d0, acc[a]);
+        acc[a] = mfma(frag_cols(KT, a * 32 + l32, (mb * 2 + 1) * 2 + hi), d1, acc[a]);
+      }
     }
     wait_all_loads();
     __syncthreads();
   }
 
   const float gscale = scale / pow2_scale(*dmax);  // undo the dO scaling
+  const bool valid = row < qp.nrows;
+  const int64_t grow = (int64_t)qp.phys * 64 + row;
+  TG* out = dq + (grow * Hq + h) * kD;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int row = nb * 32 + l32;
-    const bool valid = row < qp.nrows;
-    const int64_t grow = (int64_t)qp.phys * 64 + row;
-    TG* out = dq + (grow * Hq + h) * kD;
+  for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int d = a * 32 + 8 * j + 4 * hi + i;  // d < 64 pairs with d + 64 (block a + 2)
-          const float g1 = acc[a][nb][4 * j + i] * gscale, g2 = acc[a + 2][nb][4 * j + i] * gscale;
-          float r1 = 0.f, r2 = 0.f;
-          if (valid) {
-            const float2 c = cs ? cs[grow * (kD / 2) + d] : make_float2(1.f, 0.f);
-            r1 = g1 * c.x + g2 * c.y;
-            r2 = g2 * c.x - g1 * c.y;
-          }
-          st_f(out + d, r1);
-          st_f(out + d + 64, r2);
+      for (int i = 0; i < 4; ++i) {
+        const int d = a * 32 + 8 * j + 4 * hi + i;  // d < 64 pairs with d + 64 (block a + 2)
+        const float g1 = acc[a][4 * j + i] * gscale, g2 = acc[a + 2][4 * j + i] * gscale;
+        float r1 = 0.f, r2 = 0.f;
+        if (valid) {
+          const float2 c = cs ? cs[grow * (kD / 2) + d] : make_float2(1.f, 0.f);
+          r1 = g1 * c.x + g2 * c.y;
+          r2 = g2 * c.x - g1 * c.y;
         }
-  }
+        st_f(out + d, r1);
+        st_f(out + d + 64, r2);
+      }
 }
 
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
@@ -1029,7 +984,7 @@ static unsigned run_grid(int64_t n_units, int H) {
 void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vt,
                      const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
                      bf16_t* o_lo, hipStream_t st) {
-  fwd_mfma_kernel<<<run_grid(n_qp, s.Hkv), 256, 0, st>>>(qn, kn, vt, qpages, order, tiles, o, lse, o_lo, (int)n_qp,
+  fwd_mfma_kernel<<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, vt, qpages, order, tiles, o, lse, o_lo, (int)n_qp,
                                                          s.Hq, s.Hkv, s.scale * kLog2e);
 }
 
@@ -1037,7 +992,7 @@ template <typename TG>
 void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* kt,
                     const f16_t* vn, const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
                     const QPage* qpages, const int32_t* order, const Tile* tiles, TG* dq, hipStream_t st) {
-  dq_mfma_kernel<TG><<<run_grid(n_qp, s.Hkv), 256, 0, st>>>(qn, kn, kt, vn, dOn, ld, cs, dmax, qpages, order,
+  dq_mfma_kernel<TG><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, kt, vn, dOn, ld, cs, dmax, qpages, order,
                                                             tiles, dq, (int)n_qp, s.Hq, s.Hkv, s.scale * kLog2e,
                                                             s.scale);
 }
