@@ -706,10 +706,30 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     // S = Q K^T, dP = dO V^T: 32 rows (M) x this wave's 32 keys (N); lane holds key
     // kb*32 + l32 and rows rb*32 + acc_row(r, hi)
     f32x16 s = zero16(), dp = zero16();
+    {
+      // software-pipelined: k-step ks + 1's three fragments are read while k-step
+      // ks's two products run (the group barriers pin that interleave)
+      f16x8 qa[2], da[2], va[2];
+      qa[0] = frag_q(Qt, l32, hi);
+      da[0] = frag_q(Dt, l32, hi);
+      va[0] = frag_rows(lvp, key, hi);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      s = mfma(frag_q(Qt, l32, ks * 2 + hi), kf[ks], s);
-      dp = mfma(frag_q(Dt, l32, ks * 2 + hi), frag_rows(lvp, key, ks * 2 + hi), dp);
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks < 7) {
+          qa[(ks + 1) & 1] = frag_q(Qt, l32, (ks + 1) * 2 + hi);
+          da[(ks + 1) & 1] = frag_q(Dt, l32, (ks + 1) * 2 + hi);
+          va[(ks + 1) & 1] = frag_rows(lvp, key, (ks + 1) * 2 + hi);
+        }
+        s = mfma(qa[ks & 1], kf[ks], s);
+        dp = mfma(da[ks & 1], va[ks & 1], dp);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+#pragma unroll
+      for (int ks = 0; ks < 7; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
     if (full) {
 #pragma unroll
@@ -734,13 +754,35 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
       }
     }
     const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8), sf0 = pack8(dp, 0), sf1 = pack8(dp, 8);
-    // dV += P^T dO, dK += dS^T Q: keys (M) x d (N), the 32 rows contracted
+    // dV += P^T dO, dK += dS^T Q: keys (M) x d (N), the 32 rows contracted; d block
+    // b + 1's four fragments (eight transpose reads) are read while block b's four
+    // products run
+    {
+      f16x8 fr[2][4];
+      fr[0][0] = frag_tr(Dt, 0, 0, lane);
+      fr[0][1] = frag_tr(Dt, 1, 0, lane);
+      fr[0][2] = frag_tr(Qt, 0, 0, lane);
+      fr[0][3] = frag_tr(Qt, 1, 0, lane);
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      adv[b] = mfma(pf0, frag_tr(Dt, 0, b, lane), adv[b]);
-      adv[b] = mfma(pf1, frag_tr(Dt, 1, b, lane), adv[b]);
-      adk[b] = mfma(sf0, frag_tr(Qt, 0, b, lane), adk[b]);
-      adk[b] = mfma(sf1, frag_tr(Qt, 1, b, lane), adk[b]);
+      for (int b = 0; b < 4; ++b) {
+        if (b < 3) {
+          fr[(b + 1) & 1][0] = frag_tr(Dt, 0, b + 1, lane);
+          fr[(b + 1) & 1][1] = frag_tr(Dt, 1, b + 1, lane);
+          fr[(b + 1) & 1][2] = frag_tr(Qt, 0, b + 1, lane);
+          fr[(b + 1) & 1][3] = frag_tr(Qt, 1, b + 1, lane);
+        }
+        adv[b] = mfma(pf0, fr[b & 1][0], adv[b]);
+        adv[b] = mfma(pf1, fr[b & 1][1], adv[b]);
+        adk[b] = mfma(sf0, fr[b & 1][2], adk[b]);
+        adk[b] = mfma(sf1, fr[b & 1][3], adk[b]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int b = 0; b < 3; ++b) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     }
     wait_all_loads();
     __syncthreads();
