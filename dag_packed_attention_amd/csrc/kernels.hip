@@ -336,9 +336,21 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
 
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {  // 32-key halves
+      // all eight K fragments are read first, so the products wait only for the first;
+      // the V fragments of this half go out before the softmax and arrive under it
+      f16x8 kfr[8], vfr[8];
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) kfr[ks] = frag_rows(K, mb * 32 + l32, ks * 2 + hi);
       f32x16 s = zero16();
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) s = mfma(frag_rows(K, mb * 32 + l32, ks * 2 + hi), qf[ks], s);
+      for (int ks = 0; ks < 8; ++ks) s = mfma(kfr[ks], qf[ks], s);
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) vfr[a * 2 + kk] = frag_cols(V, a * 32 + l32, (mb * 2 + kk) * 2 + hi);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
       // Online softmax in the log2 domain.  The running max m is raised only when
       // a row's new maximum exceeds it by more than kLazy (any lane of the wave),
       // so the accumulator rescale is rare; in between, probabilities reach at most
@@ -380,8 +392,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
       const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        oacc[a] = mfma(frag_cols(V, a * 32 + l32, (mb * 2 + 0) * 2 + hi), pf0, oacc[a]);
-        oacc[a] = mfma(frag_cols(V, a * 32 + l32, (mb * 2 + 1) * 2 + hi), pf1, oacc[a]);
+        oacc[a] = mfma(vfr[a * 2], pf0, oacc[a]);
+        oacc[a] = mfma(vfr[a * 2 + 1], pf1, oacc[a]);
       }
     }
     wait_all_loads();
