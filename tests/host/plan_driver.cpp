@@ -73,9 +73,17 @@ static int check_gdn(const Plan& P) {
   for (int s = 0; s < nslots; ++s)
     for (int i = P.gslot_off[s]; i < P.gslot_off[s + 1]; ++i)
       if (P.gslot_cons[i] < 0 || P.gslot_cons[i] >= P.gdn_ncgrad) return 39;
-  for (size_t i = 0; i + 1 < P.grep_off.size(); ++i)
+  std::vector<int> rep_rows;
+  for (int q = 0; q < NS; ++q) {
+    if (P.gseqs[q].rep_off != (int)rep_rows.size()) return 40;
+    for (int j = 0; j < P.gseqs[q].n_replay; ++j) rep_rows.push_back(P.grows[P.gseqs[q].tok_off + j]);
+  }
+  if ((int64_t)P.grep_slot.size() != C) return 41;
+  for (size_t i = 0; i + 1 < P.grep_off.size(); ++i) {
+    if (P.grep_slot[P.grep_rows[i]] != (int)i) return 42;
     for (int t = P.grep_off[i]; t < P.grep_off[i + 1]; ++t)
-      if (P.grows[P.grep_tok[t]] != P.grep_rows[i]) return 40;
+      if (P.grep_tok[t] < 0 || P.grep_tok[t] >= (int)rep_rows.size() || rep_rows[P.grep_tok[t]] != P.grep_rows[i]) return 43;
+  }
   return 0;
 }
 
