@@ -242,6 +242,78 @@ __device__ __forceinline__ void state_save(const f32x16 (&S)[4], f16_t* __restri
   }
 }
 
+// The next chunk's inputs, fetched into registers while the current chunk
+// computes (one work-group per CU leaves nothing else to hide their latency).
+struct ChunkRegs {
+  uint4 k4[4], q4[4];  // 16-byte pieces: rows (tid >> 4) + 16 m, columns 8 (tid & 15) ..
+  float v[2][16];      // V at this lane's accumulator positions of R
+  int row;             // tid < 64: the chunk's token tid (-1 past the end)
+  float b, a;          //           and its beta, alpha
+};
+
+// Rows and gates of the chunk starting at token j0 (threads < 64).
+__device__ __forceinline__ void fetch_rows(const ChunkIn& ci, int j0, const float* __restrict__ beta,
+                                           const float* __restrict__ alpha, int H, int head, int tid,
+                                           ChunkRegs& nx) {
+  if (tid < kB) {
+    const int j = j0 + tid;
+    nx.row = -1;
+    nx.b = 0.f;
+    nx.a = 1.f;
+    if (j < ci.n_tok) {
+      nx.row = ci.rows[j];
+      nx.b = beta[(int64_t)nx.row * H + head];
+      nx.a = alpha[(int64_t)nx.row * H + head];
+    }
+  }
+}
+
+// K, Q rows and V values of that chunk, given its rows in LDS (rwn).
+__device__ __forceinline__ void fetch_kqv(const int* rwn, const bf16_t* __restrict__ k, const bf16_t* __restrict__ q,
+                                          const bf16_t* __restrict__ v, int H, int head, int tid, int wave,
+                                          int hi, int l32, ChunkRegs& nx) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int row = rwn[(tid >> 4) + 16 * m];
+    nx.k4[m] = nx.q4[m] = make_uint4(0, 0, 0, 0);
+    if (row >= 0) {
+      const int64_t base = ((int64_t)row * H + head) * kD + (tid & 15) * 8;
+      nx.k4[m] = *reinterpret_cast<const uint4*>(k + base);
+      nx.q4[m] = *reinterpret_cast<const uint4*>(q + base);
+    }
+  }
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = rwn[32 * bm + acc_row(r, hi)];
+      nx.v[bm][r] = row >= 0 ? bf2f(v[((int64_t)row * H + head) * kD + 32 * wave + l32]) : 0.f;
+    }
+}
+
+// Make the fetched chunk current: K, Q rows (fp16) into LDS, row numbers, beta and the
+// cumulative log decay.
+__device__ __forceinline__ void commit_chunk(const ChunkRegs& nx, f16_t* Kr, f16_t* Qr, int* rw, float* gs,
+                                             float* bs, int tid) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int t = (tid >> 4) + 16 * m, c8 = (tid & 15) * 8;
+    *reinterpret_cast<f16x8*>(Kr + t * LDK + c8) = bf8_to_h8(nx.k4[m]);
+    *reinterpret_cast<f16x8*>(Qr + t * LDK + c8) = bf8_to_h8(nx.q4[m]);
+  }
+  if (tid < kB) {
+    rw[tid] = nx.row;
+    bs[tid] = nx.b;
+    float la = logf(nx.a);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(la, off, 64);
+      if (tid >= off) la += y;
+    }
+    gs[tid] = la;
+  }
+}
+
 // Triangular solves with the unit-lower matrix I + A (A strictly lower), for
 // the 128 columns of an [64][.] tile; thread c (< 128) owns column c.  A is
 // kept transposed in LDS (At[i][t] = A[t][i], row stride LDA).  Rows go in four
@@ -337,7 +409,7 @@ __global__ __launch_bounds__(256) void gdn_fwd_kernel(
   __shared__ __attribute__((aligned(16))) float Ar[kB * LDA];  // A^T
   __shared__ __attribute__((aligned(16))) float Rr[kB * LDR];
   __shared__ float gs[kB], bs[kB];
-  __shared__ int rw[kB];
+  __shared__ int rw[kB], rwn[kB];
 
   const int head = blockIdx.x % H;
   const GSeq sq = seqs[order[blockIdx.x / H]];
@@ -361,10 +433,24 @@ __global__ __launch_bounds__(256) void gdn_fwd_kernel(
   int ex = sq.exp_off;
   const int ex_end = sq.exp_off + sq.exp_cnt;
 
+  // chunk 0 is fetched up front; chunk c + 1's inputs are fetched during chunk c
+  ChunkRegs nx;
+  float vcur[2][16];
+  fetch_rows(ci, 0, beta, alpha, H, head, tid, nx);
+  if (tid < kB) rwn[tid] = nx.row;
+  __syncthreads();
+  fetch_kqv(rwn, k, q, v, H, head, tid, wave, hi, l32, nx);
+  commit_chunk(nx, Kr, Qr, rw, gs, bs, tid);
+#pragma unroll
+  for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) vcur[bm][r] = nx.v[bm][r];
+  __syncthreads();
+
   for (int c = 0; c < nch; ++c) {
     const int j0 = c * kB;
-    load_chunk<false>(ci, j0, k, q, nullptr, beta, alpha, H, head, Kr, Qr, nullptr, rw, gs, bs, nullptr, tid);
-    __syncthreads();
+    const bool has_next = c + 1 < nch;
+    if (has_next) fetch_rows(ci, j0 + kB, beta, alpha, H, head, tid, nx);
 
     // -- products with K, Q and the chunk's starting state --------------------------
     {
@@ -403,12 +489,12 @@ __global__ __launch_bounds__(256) void gdn_fwd_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = 32 * bm + acc_row(r, hi);
-          const int row = rw[t];
-          const float vv = row >= 0 ? bf2f(v[((int64_t)row * H + head) * kD + cc]) : 0.f;
-          Rr[t * LDR + cc] = bs[t] * (vv - __expf(gs[t]) * ks[bm][r]);
+          Rr[t * LDR + cc] = bs[t] * (vcur[bm][r] - __expf(gs[t]) * ks[bm][r]);
         }
     }
+    if (tid < kB) rwn[tid] = has_next ? nx.row : -1;
     __syncthreads();
+    if (has_next) fetch_kqv(rwn, k, q, v, H, head, tid, wave, hi, l32, nx);
 
     // -- U = (I + A)^{-1} R  (only the state is live across the solve) ------------------
     if (tid < kD) solve_lower<float>(Ar, Rr, LDR, Ur, tid);
@@ -473,9 +559,15 @@ __global__ __launch_bounds__(256) void gdn_fwd_kernel(
       ++ex;
     }
     __syncthreads();
-    if (c + 1 < nch) {
+    if (has_next) {
+      commit_chunk(nx, Kr, Qr, rw, gs, bs, tid);
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) vcur[bm][r] = nx.v[bm][r];
       state_to_lds(S, Sh, wave, lane);
       if (kStates) state_save(S, states + ((int64_t)(sq.chunk_off + c + 1) * H + head) * 2 * kD * kD, wave, lane);
+      __syncthreads();
     }
   }
 }
