@@ -142,12 +142,15 @@ __global__ __launch_bounds__(256) void relayout_kernel(
     }
 }
 
-// ld[page][h][r] = (lse * log2 e, sum_d dO * O) for the backward; zero on padding rows.
+// ld[page][h][r] = (-lse / scale, -sum_d dO * O) for the backward; zero on padding rows.
+// These are the offsets a row's raw score s = q.k and dP = dO.v take in the backward:
+// P = exp(scale (s - lse / scale)) and dS = P (dP - D), so the MFMA kernels start their
+// S and dP accumulators from them.
 template <typename T>
 __global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ o_lo, const T* __restrict__ dO,
                               const float* __restrict__ lse, const int32_t* __restrict__ page_nrows,
                               const uint32_t* __restrict__ dmax, float2* __restrict__ ldout, int64_t n_pages,
-                              int Hq, int D) {
+                              int Hq, int D, float inv_scale) {
   const int64_t idx = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;  // one wave per (row, h)
   const int lane = threadIdx.x % 64;
   if (idx >= n_pages * 64 * Hq) return;
@@ -166,7 +169,7 @@ __global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ o_l
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (lane == 0) {
     float2 v = make_float2(0.f, 0.f);
-    if (valid) v = make_float2(lse[row * Hq + h] * kLog2e, acc * (dmax ? pow2_scale(*dmax) : 1.f));
+    if (valid) v = make_float2(-lse[row * Hq + h] * inv_scale, -acc * (dmax ? pow2_scale(*dmax) : 1.f));
     ldout[(page * Hq + h) * 64 + r] = v;
   }
 }
@@ -462,7 +465,7 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
     df[ks] = ld8(db + row * kD + ks * 16 + hi * 8);
   }
   const float2 lt = ldd[((int64_t)qp.phys * Hq + h) * 64 + row];
-  const float nl = -lt.x, Dv = lt.y;
+  const float nl = lt.x * sl2, nD = lt.y;  // exponent offset (log2 domain) and -D
   f32x16 acc[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) acc[a] = zero16();
@@ -502,14 +505,14 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
       }
       if (full) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl)) * (dp[r] - Dv);
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl)) * (dp[r] + nD);
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = mb * 32 + acc_row(r, hi);
           const bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < qp.nrows;
           const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl));
-          s[r] = ok ? p * (dp[r] - Dv) : 0.f;  // padding may hold NaN
+          s[r] = ok ? p * (dp[r] + nD) : 0.f;  // padding may hold NaN
         }
       }
       const f16x8 d0 = pack8(s, 0), d1 = pack8(s, 8);
@@ -555,26 +558,51 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
 typedef __fp16 v4fp16 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) v4fp16 lds_v4fp16;
 
-// [32][128] row tiles staged for the dK/dV kernel use a bit-permuting swizzle:
-// chunk c of row r sits in slot c ^ f(r), f(r) = (r & 8) | ((r & 3) << 1) | ((r >> 2) & 1).
-// Sixteen consecutive rows hit sixteen different slots (row-fragment reads),
-// and four consecutive rows keep their 32-byte chunk pairs apart (transpose reads).
-__device__ __forceinline__ int swz32(int r) { return (r & 8) | ((r & 3) << 1) | ((r >> 2) & 1); }
-__device__ __forceinline__ f16x8 frag_q(const f16_t* t, int r, int c) {
-  return ld8(t + r * 128 + ((c ^ swz32(r)) << 3));
+// [rows][128] f16 tiles staged for the dK/dV kernel are stored in bricks of four
+// rows: brick b (rows 4 b .. 4 b + 3) takes 1040 bytes, 1024 of data and 16 of
+// padding, and inside it element (rr, col) sits at (col / 16) * 64 + rr * 16 +
+// col % 16 elements: per 16 columns, the four rows' 32-byte pieces side by side.
+// One direct-load instruction fills one brick from a contiguous 1 KiB of global
+// memory.  Every fragment address is a per-lane base plus an immediate that
+// carries the k-step or d block, and both reads are free of bank conflicts:
+// eight consecutive rows at one 16-byte column chunk land in eight different
+// bank groups (the 16-byte padding shifts the second brick by one), and the
+// transpose read's four rows x 32 bytes fill one 128-byte span of a brick.
+constexpr int kBrick = 520;           // elements per 4-row brick, padding included
+constexpr int kStepB = 8 * kBrick;    // a staged [32][128] tile
+constexpr int kPageB = 16 * kBrick;   // a staged [64][128] tile
+
+__device__ __forceinline__ int brick_off(int r, int col) {
+  return (r >> 2) * kBrick + (col >> 4) * 64 + (r & 3) * 16 + (col & 15);
 }
-// 8 contraction elements for the lane's column d of tile t, rows
+// Stage rows 4 b0 .. 4 (b0 + n) - 1 of a row-major [.][128] f16 block: instruction i
+// fills brick b0 + i; lane l brings the 16-byte piece that belongs in slot l.
+template <int N>
+__device__ __forceinline__ void stage_bricks(f16_t* lds, const f16_t* g, int b0, int lane) {
+  const int rr = (lane >> 1) & 3, col = 16 * (lane >> 3) + 8 * (lane & 1);
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+    __builtin_amdgcn_global_load_lds(g + (4 * (b0 + i) + rr) * kD + col, (lds_void*)(lds + (b0 + i) * kBrick), 16,
+                                     0, 0);
+}
+// lane's base for 16-byte row fragments of row r (column chunk 2 ks + hi is base + 64 ks)
+__device__ __forceinline__ int frag_base(int r, int hi) { return brick_off(r, 8 * hi); }
+
+// 8 contraction elements for the lane's column d of a staged tile, rows
 // 16 kk + {4 hi .. 4 hi + 3, 8 + 4 hi .. 8 + 4 hi + 3}: the order in which a 32x32
-// accumulator lane of half `hi` holds rows 16 kk .. 16 kk + 15.
-__device__ __forceinline__ f16x8 frag_tr(const f16_t* t, int kk, int dblk, int lane) {
+// accumulator lane of half `hi` holds rows 16 kk .. 16 kk + 15.  Source lane
+// 16 G + a addresses row 16 kk + 8 half + 4 (G >> 1) + a / 4 at columns
+// 32 dblk + 16 (G & 1) + 4 (a & 3) ..: its per-lane part is tr_base(lane), the
+// rest (kk, half, dblk) is an immediate.
+__device__ __forceinline__ int tr_base(int lane) {
   const int G = lane >> 4, a = lane & 15;
-  const int col = dblk * 32 + (G & 1) * 16 + 4 * (a & 3);
-  const int c = col >> 3, w = col & 7;
+  return (G >> 1) * kBrick + (G & 1) * 64 + (a >> 2) * 16 + 4 * (a & 3);
+}
+__device__ __forceinline__ f16x8 frag_tr(const f16_t* tb, int kk, int dblk) {
   f16x8 out;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
-    const int row = kk * 16 + half * 8 + 4 * (G >> 1) + (a >> 2);
-    const f16_t* p = t + row * 128 + ((c ^ swz32(row)) << 3) + w;
+    const f16_t* p = tb + (4 * kk + 2 * half) * kBrick + dblk * 128;
     const v4fp16 v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4fp16*)p);
 #pragma unroll
     for (int j = 0; j < 4; ++j) out[half * 4 + j] = (f16_t)v[j];
@@ -638,13 +666,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const int32_t* __restrict__ kv_steps, const KEntry* __restrict__ ents, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ page_nrows, TG* __restrict__ dk, TG* __restrict__ dv, int n_kvp, int Hq, int Hkv,
     float sl2, float scale) {
-  constexpr int kStep = 32 * kD;  // elements of one [32][128] tile
-  // [buffer][head][Q, dO][32 x 128] f16, then [buffer][head][32] (lse, D); the
-  // first 33 KiB are reused for the head reduction at the end.  The page's V
-  // tile sits in its own [64][128] block.
-  __shared__ __attribute__((aligned(1024))) f16_t qd[2][4][2][kStep];
-  __shared__ __attribute__((aligned(1024))) f16_t lvp[kTile];
-  __shared__ __attribute__((aligned(16))) float2 lds_ld[2][4][32];
+  // [buffer][head][Q, dO][32 x 128] f16, then [buffer][head] the 32 rows'
+  // accumulator offsets, -lse / scale for S and then -D for dP; the first 33 KiB
+  // are reused for the head reduction at the end.  The page's V tile sits in its
+  // own [64][128] block.
+  __shared__ __attribute__((aligned(1024))) f16_t qd[2][4][2][kStepB];
+  __shared__ __attribute__((aligned(1024))) f16_t lvp[kPageB];
+  __shared__ __attribute__((aligned(16))) float lds_ld[2][4][64];
   int unit, g;
   if (!map_item(n_kvp, Hkv, unit, g)) return;
   const int page = order[unit];
@@ -661,7 +689,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const int64_t base = ((int64_t)page * Hkv + g) * 64 * kD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kf[ks] = ld8(kn + base + (kb * 32 + l32) * kD + ks * 16 + hi * 8);
-    if (wave < 4) load_tile_rows(lvp, vn + base, wave, lane);
+    if (wave < 4) stage_bricks<4>(lvp, vn + base, 4 * wave, lane);
   }
   f32x16 adk[4], adv[4];  // [d block]
 #pragma unroll
@@ -676,17 +704,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
   auto stage = [&](int buf, int qp_, int rb_) {
     // wave (hh, kb) fetches head 4 g + hh's Q rows (kb = 0) or dO rows (kb = 1): 8 KiB
     const int64_t src = (((int64_t)qp_ * Hq + g * 4 + hh) * 64 + rb_ * 32) * kD;
-    const f16_t* gsrc = (kb == 0 ? qn : dOn) + src;
-    f16_t* dst = qd[buf][hh][kb];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = i * 64 + lane;  // 16-byte slot
-      const int r = q >> 4, c = (q & 15) ^ swz32(r);
-      __builtin_amdgcn_global_load_lds(gsrc + r * kD + c * 8, (lds_void*)(dst + i * 512), 16, 0, 0);
+    stage_bricks<8>(qd[buf][hh][kb], (kb == 0 ? qn : dOn) + src, 0, lane);
+    if (kb == 0) {
+      // lane i < 32 takes row i's S offset, lane 32 + i its dP offset (4 bytes each,
+      // landing at slot i of the 64-float block)
+      const float* lsrc = reinterpret_cast<const float*>(ldd + ((int64_t)qp_ * Hq + g * 4 + hh) * 64 + rb_ * 32);
+      __builtin_amdgcn_global_load_lds(lsrc + 2 * (lane & 31) + (lane >> 5), (lds_void*)(&lds_ld[buf][hh][0]), 4,
+                                       0, 0);
     }
-    if (kb == 0 && lane < 16)
-      __builtin_amdgcn_global_load_lds(ldd + ((int64_t)qp_ * Hq + g * 4 + hh) * 64 + rb_ * 32 + lane * 2,
-                                       (lds_void*)(&lds_ld[buf][hh][0]), 16, 0, 0);
   };
   stage(0, qph, 0);
   wait_all_loads();
@@ -694,6 +719,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
 
   int buf = 0;
   const int key = kb * 32 + l32;
+  const int qb = frag_base(l32, hi), vb = frag_base(key, hi), tb = tr_base(lane);
   for (int it = 0; it < n_steps; ++it) {
     // where the next step is (a reader page of <= 32 rows has one row block)
     const bool more = it + 1 < n_steps;
@@ -714,23 +740,34 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const bool full = lo == 0 && hi_t == 64 && !diag && nrows >= rb * 32 + 32;
     const f16_t* Qt = qd[buf][hh][0];
     const f16_t* Dt = qd[buf][hh][1];
-    const float2* LD = lds_ld[buf][hh];
-    // S = Q K^T, dP = dO V^T: 32 rows (M) x this wave's 32 keys (N); lane holds key
-    // kb*32 + l32 and rows rb*32 + acc_row(r, hi)
-    f32x16 s = zero16(), dp = zero16();
+    // S = Q K^T - lse / scale, dP = dO V^T - D: 32 rows (M) x this wave's 32 keys (N);
+    // lane holds key kb*32 + l32 and rows rb*32 + acc_row(r, hi), so the offsets of
+    // its rows come as four runs of four consecutive floats straight into the
+    // accumulators
+    f32x16 s, dp;
+    {
+      const float* L = lds_ld[buf][hh];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 a = *reinterpret_cast<const float4*>(L + 8 * j + 4 * hi);
+        const float4 b = *reinterpret_cast<const float4*>(L + 32 + 8 * j + 4 * hi);
+        s[4 * j] = a.x, s[4 * j + 1] = a.y, s[4 * j + 2] = a.z, s[4 * j + 3] = a.w;
+        dp[4 * j] = b.x, dp[4 * j + 1] = b.y, dp[4 * j + 2] = b.z, dp[4 * j + 3] = b.w;
+      }
+    }
     {
       // software-pipelined: k-step ks + 1's three fragments are read while k-step
       // ks's two products run (the group barriers pin that interleave)
       f16x8 qa[2], da[2], va[2];
-      qa[0] = frag_q(Qt, l32, hi);
-      da[0] = frag_q(Dt, l32, hi);
-      va[0] = frag_rows(lvp, key, hi);
+      qa[0] = ld8(Qt + qb);
+      da[0] = ld8(Dt + qb);
+      va[0] = ld8(lvp + vb);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         if (ks < 7) {
-          qa[(ks + 1) & 1] = frag_q(Qt, l32, (ks + 1) * 2 + hi);
-          da[(ks + 1) & 1] = frag_q(Dt, l32, (ks + 1) * 2 + hi);
-          va[(ks + 1) & 1] = frag_rows(lvp, key, (ks + 1) * 2 + hi);
+          qa[(ks + 1) & 1] = ld8(Qt + qb + (ks + 1) * 64);
+          da[(ks + 1) & 1] = ld8(Dt + qb + (ks + 1) * 64);
+          va[(ks + 1) & 1] = ld8(lvp + vb + (ks + 1) * 64);
         }
         s = mfma(qa[ks & 1], kf[ks], s);
         dp = mfma(da[ks & 1], va[ks & 1], dp);
@@ -746,23 +783,20 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     if (full) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float2 lr = LD[acc_row(r, hi)];
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr.x));
+        const float p = __builtin_amdgcn_exp2f(s[r] * sl2);
         s[r] = p;
-        dp[r] = p * (dp[r] - lr.y);
+        dp[r] = p * dp[r];
       }
     } else {
-      // every operand here comes from the zero-padded relayouts, so all values are
-      // finite and a 0/1 factor masks without branches
+      // every operand here comes from the zero-padded relayouts, so all values are finite
       const bool key_ok = key >= lo && key < hi_t;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float2 lr = LD[acc_row(r, hi)];
         const int row = rb * 32 + acc_row(r, hi);
-        const float okf = (key_ok && (!diag || key <= row) && row < nrows) ? 1.f : 0.f;
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lr.x)) * okf;
+        const bool ok = key_ok && (!diag || key <= row) && row < nrows;
+        const float p = ok ? __builtin_amdgcn_exp2f(s[r] * sl2) : 0.f;  // a hidden score may overflow
         s[r] = p;
-        dp[r] = p * (dp[r] - lr.y);
+        dp[r] = p * dp[r];
       }
     }
     const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8), sf0 = pack8(dp, 0), sf1 = pack8(dp, 8);
@@ -771,17 +805,19 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     // products run
     {
       f16x8 fr[2][4];
-      fr[0][0] = frag_tr(Dt, 0, 0, lane);
-      fr[0][1] = frag_tr(Dt, 1, 0, lane);
-      fr[0][2] = frag_tr(Qt, 0, 0, lane);
-      fr[0][3] = frag_tr(Qt, 1, 0, lane);
+      const f16_t* Dtb = Dt + tb;
+      const f16_t* Qtb = Qt + tb;
+      fr[0][0] = frag_tr(Dtb, 0, 0);
+      fr[0][1] = frag_tr(Dtb, 1, 0);
+      fr[0][2] = frag_tr(Qtb, 0, 0);
+      fr[0][3] = frag_tr(Qtb, 1, 0);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if (b < 3) {
-          fr[(b + 1) & 1][0] = frag_tr(Dt, 0, b + 1, lane);
-          fr[(b + 1) & 1][1] = frag_tr(Dt, 1, b + 1, lane);
-          fr[(b + 1) & 1][2] = frag_tr(Qt, 0, b + 1, lane);
-          fr[(b + 1) & 1][3] = frag_tr(Qt, 1, b + 1, lane);
+          fr[(b + 1) & 1][0] = frag_tr(Dtb, 0, b + 1);
+          fr[(b + 1) & 1][1] = frag_tr(Dtb, 1, b + 1);
+          fr[(b + 1) & 1][2] = frag_tr(Qtb, 0, b + 1);
+          fr[(b + 1) & 1][3] = frag_tr(Qtb, 1, b + 1);
         }
         adv[b] = mfma(pf0, fr[b & 1][0], adv[b]);
         adv[b] = mfma(pf1, fr[b & 1][1], adv[b]);
@@ -884,7 +920,7 @@ __global__ __launch_bounds__(64) void dq_simple_kernel(
     acc[d] = 0.f;
   }
   const float2 lD = ldd[((int64_t)qp.phys * Hq + h) * 64 + row];
-  const float lse_n = lD.x * kLn2;
+  const float lse_n = -lD.x * scale;
   const bool valid = row < qp.nrows;
   if (valid)
     for (int t = 0; t < qp.tile_count; ++t) {
@@ -901,7 +937,7 @@ __global__ __launch_bounds__(64) void dq_simple_kernel(
           dp = fmaf(gd[d], ld_f(vrow + d), dp);
         }
         const float p = expf(s * scale - lse_n);
-        const float ds = p * (dp - lD.y) * scale;
+        const float ds = p * (dp + lD.y) * scale;
         for (int d = 0; d < D; ++d) acc[d] = fmaf(ds, krow[d], acc[d]);
       }
     }
@@ -961,8 +997,8 @@ __global__ __launch_bounds__(64) void dkdv_simple_kernel(
               s = fmaf(qrow[d], k[d], s);
               dp = fmaf(ld_f(drow + d), vv[d], dp);
             }
-            const float p = expf(s * scale - lD.x * kLn2);
-            const float ds = p * (dp - lD.y) * scale;
+            const float p = expf(s * scale + lD.x * scale);
+            const float ds = p * (dp + lD.y) * scale;
             for (int d = 0; d < D; ++d) {
               av[d] = fmaf(p, ld_f(drow + d), av[d]);
               ak[d] = fmaf(ds, qrow[d], ak[d]);
@@ -1009,7 +1045,7 @@ template <typename T>
 void launch_rowdot(const LaunchShape& s, const T* o, const T* o_lo, const T* dO, const float* lse,
                    const int32_t* page_nrows, const uint32_t* dmax, float2* ld, hipStream_t st) {
   rowdot_kernel<T><<<blocks_for(s.pages * 64 * s.Hq, 4), 256, 0, st>>>(o, o_lo, dO, lse, page_nrows, dmax, ld,
-                                                                       s.pages, s.Hq, s.D);
+                                                                       s.pages, s.Hq, s.D, 1.f / s.scale);
 }
 
 template <typename T>
