@@ -202,11 +202,6 @@ __global__ __launch_bounds__(256) void maxabs_kernel(const T* __restrict__ x, co
 // ---------------------------------------------------------------------------
 
 constexpr int kD = 128;
-constexpr int kKStride = kD + 8;   // LDS row stride (16-bit elements) of a [64][128] tile: +16 B against bank conflicts
-constexpr int kTStride = 64 + 8;   // LDS row stride (16-bit elements) of a [128][64] tile
-constexpr int kTileRows = 64 * kKStride;  // elements of a staged [64][128] tile
-constexpr int kTileCols = kD * kTStride;  // elements of a staged [128][64] tile
-// dK/dV work-group LDS: the K and V tiles, later overlaid by the [64][129] fp32 head sum
 
 constexpr int kRun = 8;  // consecutive units of one head that go to one XCD
 
@@ -246,41 +241,71 @@ __device__ __forceinline__ bool map_item(int n_units, int H, int& unit, int& hea
 }
 
 // Direct global -> LDS tile loads (gfx950 global_load_lds_dwordx4).  Each wave
-// instruction writes 64 x 16 B contiguously at an LDS base held in M0, so the
-// tile's LDS layout is unpadded; the lane that fills a slot fetches the global
-// 16-byte chunk that belongs there under an XOR swizzle, which keeps the MFMA
-// fragment reads free of bank conflicts:
-//   [64][128] tiles (256 B rows):  chunk c of row r sits in slot c ^ (r & 15)
-//   [128][64] tiles (128 B rows):  chunk c of row r sits in slot c ^ ((r >> 1) & 7)
+// instruction writes 64 x 16 B contiguously at an LDS base held in M0; the lane
+// that fills a slot fetches the global 16-byte chunk that belongs there.
 typedef __attribute__((address_space(3))) void lds_void;
 
-__device__ __forceinline__ void load_tile_rows(f16_t* lds, const f16_t* g, int wave, int lane) {
+// LDS on gfx950 serves 256 bytes (64 banks) per cycle: a 16-byte read takes 16
+// lanes per cycle, an 8-byte read 32.  Staged tiles are laid out so that those
+// lane groups never meet in a bank, and so that every fragment address is a
+// per-lane base plus a compile-time offset (the k-step or d block).
+//
+// [rows][128] f16 tiles (K, V, Q, dO) sit in bricks of four rows: brick b (rows
+// 4 b .. 4 b + 3) takes 1040 bytes, 1024 of data and 16 of padding, and inside it
+// element (rr, col) sits at (col / 32) * 128 + rr * 32 + col % 32: per 32
+// columns, the four rows' 64-byte pieces side by side.  Sixteen consecutive rows
+// at one 16-byte chunk fall in sixteen different 16-byte bank groups (64 B apart
+// inside a brick, one group further per brick), and a transpose read's 32 lanes
+// (four rows x 64 bytes) cover one contiguous 256-byte span.  One direct-load
+// instruction fills one brick from a contiguous 1 KiB of global memory.
+constexpr int kBrick = 520;           // elements per 4-row brick, padding included
+constexpr int kStepB = 8 * kBrick;    // a staged [32][128] tile
+constexpr int kPageB = 16 * kBrick;   // a staged [64][128] tile
+
+__device__ __forceinline__ int brick_off(int r, int col) {
+  return (r >> 2) * kBrick + (col >> 5) * 128 + (r & 3) * 32 + (col & 31);
+}
+// Stage rows 4 b0 .. 4 (b0 + N) - 1 of a row-major [.][128] f16 block: instruction i
+// fills brick b0 + i; lane l brings the 16-byte piece that belongs in slot l.
+template <int N>
+__device__ __forceinline__ void stage_bricks(f16_t* lds, const f16_t* g, int b0, int lane) {
+  const int rr = (lane >> 2) & 3, col = 32 * (lane >> 4) + 8 * (lane & 3);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = (wave * 4 + i) * 64 + lane;  // 16-byte slot in the tile
-    const int r = q >> 4, c = (q & 15) ^ (r & 15);
-    __builtin_amdgcn_global_load_lds(g + r * 128 + c * 8, (lds_void*)(lds + (wave * 4 + i) * 512), 16, 0, 0);
-  }
+  for (int i = 0; i < N; ++i)
+    __builtin_amdgcn_global_load_lds(g + (4 * (b0 + i) + rr) * kD + col, (lds_void*)(lds + (b0 + i) * kBrick), 16,
+                                     0, 0);
 }
-__device__ __forceinline__ void load_tile_cols(f16_t* lds, const f16_t* g, int wave, int lane) {
+// 16-byte row fragments: lane base for row r in half hi, plus kstep(ks) for column
+// chunk 2 ks + hi
+__device__ __forceinline__ int frag_base(int r, int hi) { return brick_off(r, 8 * hi); }
+__device__ __forceinline__ constexpr int kstep(int ks) { return (ks >> 1) * 128 + (ks & 1) * 16; }
+
+// [128][64] f16 tiles (a page's V^T or K^T, 128-byte rows) sit in bricks of eight
+// rows, 1152 bytes each (128 of padding), inside which element (rr, col) sits at
+// (col / 8) * 64 + rr * 8 + col % 8: the eight rows' 16-byte chunks of one column
+// chunk side by side.  Eight consecutive rows at one chunk fill 128 contiguous
+// bytes, and the padding puts the next eight rows in the other half of the
+// 256-byte bank span.
+constexpr int kCBrick = 576;
+constexpr int kPageC = 16 * kCBrick;  // a staged [128][64] tile
+__device__ __forceinline__ int cbrick_off(int r, int col) {
+  return (r >> 3) * kCBrick + (col >> 3) * 64 + (r & 7) * 8 + (col & 7);
+}
+template <int N>
+__device__ __forceinline__ void stage_cbricks(f16_t* lds, const f16_t* g, int b0, int lane) {
+  const int rr = lane & 7, col = 8 * (lane >> 3);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = (wave * 4 + i) * 64 + lane;
-    const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
-    __builtin_amdgcn_global_load_lds(g + r * 64 + c * 8, (lds_void*)(lds + (wave * 4 + i) * 512), 16, 0, 0);
-  }
+  for (int i = 0; i < N; ++i)
+    __builtin_amdgcn_global_load_lds(g + (8 * (b0 + i) + rr) * 64 + col, (lds_void*)(lds + (b0 + i) * kCBrick), 16,
+                                     0, 0);
 }
-// fragment reads: 8 elements of row r starting at column chunk c (16-byte chunks)
-__device__ __forceinline__ f16x8 frag_rows(const f16_t* lds, int r, int c) {
-  return ld8(lds + r * 128 + ((c ^ (r & 15)) << 3));
-}
-__device__ __forceinline__ f16x8 frag_cols(const f16_t* lds, int r, int c) {
-  return ld8(lds + r * 64 + ((c ^ ((r >> 1) & 7)) << 3));
-}
+// lane's base for 16-byte fragments of row r of a column-brick tile (chunk c is base + 64 c)
+__device__ __forceinline__ int cfrag_base(int r, int hi) { return cbrick_off(r, 8 * hi); }
+
 // all of this thread's global->LDS loads (and everything else) have landed
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
 
-constexpr int kTile = 64 * kD;  // elements of an unpadded 64 x 128 (or 128 x 64) tile
+constexpr int kTile = 64 * kD;  // elements of a page's 64 x 128 (or 128 x 64) block in global memory
 
 // Forward for one 64-row query block x one KV head.  Eight waves: wave (hh, nb)
 // serves query head 4 g + hh and rows 32 nb .. 32 nb + 31 (two waves per SIMD,
@@ -292,8 +317,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
     const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
     bf16_t* __restrict__ o, float* __restrict__ lse, bf16_t* __restrict__ o_lo, int n_qp, int Hq, int Hkv,
     float sl2) {
-  __shared__ __attribute__((aligned(1024))) f16_t lk[2][kTile];
-  __shared__ __attribute__((aligned(1024))) f16_t lv[2][kTile];
+  __shared__ __attribute__((aligned(1024))) f16_t lk[2][kPageB];
+  __shared__ __attribute__((aligned(1024))) f16_t lv[2][kPageC];
   int unit, g;
   if (!map_item(n_qp, Hkv, unit, g)) return;
   const QPage qp = qpages[order[unit]];
@@ -303,6 +328,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
   const int hh = wave & 3, nb = wave >> 2;
   const int h = g * 4 + hh;
   const int row = nb * 32 + l32;
+  const int kb0 = frag_base(l32, hi), vb0 = cfrag_base(l32, hi);
 
   f16x8 qf[8];
   const f16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
@@ -317,8 +343,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
   const int T = qp.tile_count;
   if (wave < 4) {
     const int64_t base = ((int64_t)tiles[qp.tile_begin].page * Hkv + g) * kTile;
-    load_tile_rows(lk[0], kn + base, wave, lane);
-    load_tile_cols(lv[0], vt + base, wave, lane);
+    stage_bricks<4>(lk[0], kn + base, 4 * wave, lane);
+    stage_cbricks<4>(lv[0], vt + base, 4 * wave, lane);
   }
   wait_all_loads();
   __syncthreads();
@@ -327,8 +353,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
     const int buf = t & 1;
     if (t + 1 < T && wave < 4) {
       const int64_t base = ((int64_t)tiles[qp.tile_begin + t + 1].page * Hkv + g) * kTile;
-      load_tile_rows(lk[buf ^ 1], kn + base, wave, lane);
-      load_tile_cols(lv[buf ^ 1], vt + base, wave, lane);
+      stage_bricks<4>(lk[buf ^ 1], kn + base, 4 * wave, lane);
+      stage_cbricks<4>(lv[buf ^ 1], vt + base, 4 * wave, lane);
     }
     const int lohi = tiles[qp.tile_begin + t].lohi;
     const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
@@ -343,14 +369,14 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
       // the V fragments of this half go out before the softmax and arrive under it
       f16x8 kfr[8], vfr[8];
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) kfr[ks] = frag_rows(K, mb * 32 + l32, ks * 2 + hi);
+      for (int ks = 0; ks < 8; ++ks) kfr[ks] = ld8(K + kb0 + mb * 8 * kBrick + kstep(ks));
       f32x16 s = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) s = mfma(kfr[ks], qf[ks], s);
 #pragma unroll
       for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk) vfr[a * 2 + kk] = frag_cols(V, a * 32 + l32, (mb * 2 + kk) * 2 + hi);
+        for (int kk = 0; kk < 2; ++kk) vfr[a * 2 + kk] = ld8(V + vb0 + a * 4 * kCBrick + (mb * 2 + kk) * 128);
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
@@ -443,9 +469,9 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
     const float2* __restrict__ cs, const uint32_t* __restrict__ dmax, const QPage* __restrict__ qpages,
     const int32_t* __restrict__ order, const Tile* __restrict__ tiles, TG* __restrict__ dq, int n_qp, int Hq,
     int Hkv, float sl2, float scale) {
-  __shared__ __attribute__((aligned(1024))) f16_t lk[2][kTile];
-  __shared__ __attribute__((aligned(1024))) f16_t lvv[2][kTile];
-  __shared__ __attribute__((aligned(1024))) f16_t lkt[2][kTile];
+  __shared__ __attribute__((aligned(1024))) f16_t lk[2][kPageB];
+  __shared__ __attribute__((aligned(1024))) f16_t lvv[2][kPageB];
+  __shared__ __attribute__((aligned(1024))) f16_t lkt[2][kPageC];
   int unit, g;
   if (!map_item(n_qp, Hkv, unit, g)) return;
   const QPage qp = qpages[order[unit]];
@@ -455,6 +481,7 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
   const int hh = wave & 3, nb = wave >> 2;
   const int h = g * 4 + hh;
   const int row = nb * 32 + l32;
+  const int kb0 = frag_base(l32, hi), tb0 = cfrag_base(l32, hi);
 
   f16x8 qf[8], df[8];
   const f16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
@@ -473,9 +500,9 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
   const int T = qp.tile_count;
   if (wave < 4) {
     const int64_t base = ((int64_t)tiles[qp.tile_begin].page * Hkv + g) * kTile;
-    load_tile_rows(lk[0], kn + base, wave, lane);
-    load_tile_rows(lvv[0], vn + base, wave, lane);
-    load_tile_cols(lkt[0], kt + base, wave, lane);
+    stage_bricks<4>(lk[0], kn + base, 4 * wave, lane);
+    stage_bricks<4>(lvv[0], vn + base, 4 * wave, lane);
+    stage_cbricks<4>(lkt[0], kt + base, 4 * wave, lane);
   }
   wait_all_loads();
   __syncthreads();
@@ -484,9 +511,9 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
     const int buf = t & 1;
     if (t + 1 < T && wave < 4) {
       const int64_t base = ((int64_t)tiles[qp.tile_begin + t + 1].page * Hkv + g) * kTile;
-      load_tile_rows(lk[buf ^ 1], kn + base, wave, lane);
-      load_tile_rows(lvv[buf ^ 1], vn + base, wave, lane);
-      load_tile_cols(lkt[buf ^ 1], kt + base, wave, lane);
+      stage_bricks<4>(lk[buf ^ 1], kn + base, 4 * wave, lane);
+      stage_bricks<4>(lvv[buf ^ 1], vn + base, 4 * wave, lane);
+      stage_cbricks<4>(lkt[buf ^ 1], kt + base, 4 * wave, lane);
     }
     const int lohi = tiles[qp.tile_begin + t].lohi;
     const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
@@ -500,8 +527,8 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        s = mfma(frag_rows(K, mb * 32 + l32, ks * 2 + hi), qf[ks], s);
-        dp = mfma(frag_rows(V, mb * 32 + l32, ks * 2 + hi), df[ks], dp);
+        s = mfma(ld8(K + kb0 + mb * 8 * kBrick + kstep(ks)), qf[ks], s);
+        dp = mfma(ld8(V + kb0 + mb * 8 * kBrick + kstep(ks)), df[ks], dp);
       }
       if (full) {
 #pragma unroll
@@ -518,8 +545,8 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
       const f16x8 d0 = pack8(s, 0), d1 = pack8(s, 8);
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        acc[a] = mfma(frag_cols(KT, a * 32 + l32, (mb * 2 + 0) * 2 + hi), d0, acc[a]);
-        acc[a] = mfma(frag_cols(KT, a * 32 + l32, (mb * 2 + 1) * 2 + hi), d1, acc[a]);
+        acc[a] = mfma(ld8(KT + tb0 + a * 4 * kCBrick + (mb * 2 + 0) * 128), d0, acc[a]);
+        acc[a] = mfma(ld8(KT + tb0 + a * 4 * kCBrick + (mb * 2 + 1) * 128), d1, acc[a]);
       }
     }
     wait_all_loads();
@@ -558,36 +585,6 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
 typedef __fp16 v4fp16 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) v4fp16 lds_v4fp16;
 
-// [rows][128] f16 tiles staged for the dK/dV kernel are stored in bricks of four
-// rows: brick b (rows 4 b .. 4 b + 3) takes 1040 bytes, 1024 of data and 16 of
-// padding, and inside it element (rr, col) sits at (col / 16) * 64 + rr * 16 +
-// col % 16 elements: per 16 columns, the four rows' 32-byte pieces side by side.
-// One direct-load instruction fills one brick from a contiguous 1 KiB of global
-// memory.  Every fragment address is a per-lane base plus an immediate that
-// carries the k-step or d block, and both reads are free of bank conflicts:
-// eight consecutive rows at one 16-byte column chunk land in eight different
-// bank groups (the 16-byte padding shifts the second brick by one), and the
-// transpose read's four rows x 32 bytes fill one 128-byte span of a brick.
-constexpr int kBrick = 520;           // elements per 4-row brick, padding included
-constexpr int kStepB = 8 * kBrick;    // a staged [32][128] tile
-constexpr int kPageB = 16 * kBrick;   // a staged [64][128] tile
-
-__device__ __forceinline__ int brick_off(int r, int col) {
-  return (r >> 2) * kBrick + (col >> 4) * 64 + (r & 3) * 16 + (col & 15);
-}
-// Stage rows 4 b0 .. 4 (b0 + n) - 1 of a row-major [.][128] f16 block: instruction i
-// fills brick b0 + i; lane l brings the 16-byte piece that belongs in slot l.
-template <int N>
-__device__ __forceinline__ void stage_bricks(f16_t* lds, const f16_t* g, int b0, int lane) {
-  const int rr = (lane >> 1) & 3, col = 16 * (lane >> 3) + 8 * (lane & 1);
-#pragma unroll
-  for (int i = 0; i < N; ++i)
-    __builtin_amdgcn_global_load_lds(g + (4 * (b0 + i) + rr) * kD + col, (lds_void*)(lds + (b0 + i) * kBrick), 16,
-                                     0, 0);
-}
-// lane's base for 16-byte row fragments of row r (column chunk 2 ks + hi is base + 64 ks)
-__device__ __forceinline__ int frag_base(int r, int hi) { return brick_off(r, 8 * hi); }
-
 // 8 contraction elements for the lane's column d of a staged tile, rows
 // 16 kk + {4 hi .. 4 hi + 3, 8 + 4 hi .. 8 + 4 hi + 3}: the order in which a 32x32
 // accumulator lane of half `hi` holds rows 16 kk .. 16 kk + 15.  Source lane
@@ -596,7 +593,7 @@ __device__ __forceinline__ int frag_base(int r, int hi) { return brick_off(r, 8 
 // rest (kk, half, dblk) is an immediate.
 __device__ __forceinline__ int tr_base(int lane) {
   const int G = lane >> 4, a = lane & 15;
-  return (G >> 1) * kBrick + (G & 1) * 64 + (a >> 2) * 16 + 4 * (a & 3);
+  return (G >> 1) * kBrick + (a >> 2) * 32 + (G & 1) * 16 + 4 * (a & 3);
 }
 __device__ __forceinline__ f16x8 frag_tr(const f16_t* tb, int kk, int dblk) {
   f16x8 out;
@@ -765,9 +762,9 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
         if (ks < 7) {
-          qa[(ks + 1) & 1] = ld8(Qt + qb + (ks + 1) * 64);
-          da[(ks + 1) & 1] = ld8(Dt + qb + (ks + 1) * 64);
-          va[(ks + 1) & 1] = ld8(lvp + vb + (ks + 1) * 64);
+          qa[(ks + 1) & 1] = ld8(Qt + qb + kstep(ks + 1));
+          da[(ks + 1) & 1] = ld8(Dt + qb + kstep(ks + 1));
+          va[(ks + 1) & 1] = ld8(lvp + vb + kstep(ks + 1));
         }
         s = mfma(qa[ks & 1], kf[ks], s);
         dp = mfma(da[ks & 1], va[ks & 1], dp);
