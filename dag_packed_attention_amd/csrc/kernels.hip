@@ -240,9 +240,6 @@ __device__ __forceinline__ bool map_item(int n_units, int H, int& unit, int& hea
   return unit < n_units;
 }
 
-// Direct global -> LDS tile loads (gfx950 global_load_lds_dwordx4).  Each wave
-// instruction writes 64 x 16 B contiguously at an LDS base held in M0; the lane
-// that fills a slot fetches the global 16-byte chunk that belongs there.
 typedef __attribute__((address_space(3))) void lds_void;
 
 // LDS on gfx950 serves 256 bytes (64 banks) per cycle: a 16-byte read takes 16
@@ -267,13 +264,51 @@ __device__ __forceinline__ int brick_off(int r, int col) {
 }
 // Stage rows 4 b0 .. 4 (b0 + N) - 1 of a row-major [.][128] f16 block: instruction i
 // fills brick b0 + i; lane l brings the 16-byte piece that belongs in slot l.
+// Tiles are staged with buffer loads that write LDS directly (buffer_load ... lds):
+// each wave instruction writes 64 x 16 B (or 64 x 4 B) contiguously at the LDS
+// address held in M0, and the lane that fills a slot fetches the global piece that
+// belongs there.  The tile's base is a buffer descriptor in SGPRs sized to the
+// tile, so the hardware range-checks every access (reads past it return zero);
+// the instruction's place in the tile is a scalar offset and the lane's a 32-bit
+// VGPR offset that is computed once and never rewritten.  The loads are issued
+// from inline assembly: the compiler cannot tell a load into one LDS buffer from
+// a read of the other and would wait for the whole prefetch before the first
+// read of the current step.  Every kernel that issues them waits for all of them
+// (s_waitcnt 0) and then synchronises before the staged data is read.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 tile_rsrc(const void* p, int bytes) {
+  const uint64_t a = (uint64_t)p;
+  i32x4 r;
+  r.x = (int)(uint32_t)a;
+  r.y = (int)((uint32_t)(a >> 32) & 0xffffu);  // stride 0: raw byte offsets
+  r.z = bytes;                                  // range limit
+  r.w = 0x00020000;                             // 32-bit data format
+  return r;
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void*)p;
+}
+__device__ __forceinline__ void dma16(const void* lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr(lds)), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* lds, uint32_t voff, i32x4 rsrc, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr(lds)), "v"(voff), "s"(rsrc), "s"(soff)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t brick_lane_off(int lane) {
+  return (uint32_t)((((lane >> 2) & 3) * kD + 32 * (lane >> 4) + 8 * (lane & 3)) * 2);
+}
+// Stage rows 4 b0 .. 4 (b0 + N) - 1 of a row-major [.][128] f16 block: instruction i
+// fills brick b0 + i; lane l brings the 16-byte piece that belongs in slot l.
 template <int N>
-__device__ __forceinline__ void stage_bricks(f16_t* lds, const f16_t* g, int b0, int lane) {
-  const int rr = (lane >> 2) & 3, col = 32 * (lane >> 4) + 8 * (lane & 3);
+__device__ __forceinline__ void stage_bricks(f16_t* lds, i32x4 src, int b0, uint32_t loff) {
 #pragma unroll
-  for (int i = 0; i < N; ++i)
-    __builtin_amdgcn_global_load_lds(g + (4 * (b0 + i) + rr) * kD + col, (lds_void*)(lds + (b0 + i) * kBrick), 16,
-                                     0, 0);
+  for (int i = 0; i < N; ++i) dma16(lds + (b0 + i) * kBrick, loff, src, (b0 + i) * 4 * kD * 2);
 }
 // 16-byte row fragments: lane base for row r in half hi, plus kstep(ks) for column
 // chunk 2 ks + hi
@@ -291,13 +326,11 @@ constexpr int kPageC = 16 * kCBrick;  // a staged [128][64] tile
 __device__ __forceinline__ int cbrick_off(int r, int col) {
   return (r >> 3) * kCBrick + (col >> 3) * 64 + (r & 7) * 8 + (col & 7);
 }
+__device__ __forceinline__ uint32_t cbrick_lane_off(int lane) { return (uint32_t)(((lane & 7) * 64 + 8 * (lane >> 3)) * 2); }
 template <int N>
-__device__ __forceinline__ void stage_cbricks(f16_t* lds, const f16_t* g, int b0, int lane) {
-  const int rr = lane & 7, col = 8 * (lane >> 3);
+__device__ __forceinline__ void stage_cbricks(f16_t* lds, i32x4 src, int b0, uint32_t loff) {
 #pragma unroll
-  for (int i = 0; i < N; ++i)
-    __builtin_amdgcn_global_load_lds(g + (8 * (b0 + i) + rr) * 64 + col, (lds_void*)(lds + (b0 + i) * kCBrick), 16,
-                                     0, 0);
+  for (int i = 0; i < N; ++i) dma16(lds + (b0 + i) * kCBrick, loff, src, (b0 + i) * 8 * 64 * 2);
 }
 // lane's base for 16-byte fragments of row r of a column-brick tile (chunk c is base + 64 c)
 __device__ __forceinline__ int cfrag_base(int r, int hi) { return cbrick_off(r, 8 * hi); }
@@ -323,12 +356,13 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
   if (!map_item(n_qp, Hkv, unit, g)) return;
   const QPage qp = qpages[order[unit]];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
   const int l32 = lane & 31, hi = lane >> 5;
   const int hh = wave & 3, nb = wave >> 2;
   const int h = g * 4 + hh;
   const int row = nb * 32 + l32;
   const int kb0 = frag_base(l32, hi), vb0 = cfrag_base(l32, hi);
+  const uint32_t rlo = brick_lane_off(lane), clo = cbrick_lane_off(lane);
 
   f16x8 qf[8];
   const f16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
@@ -343,8 +377,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
   const int T = qp.tile_count;
   if (wave < 4) {
     const int64_t base = ((int64_t)tiles[qp.tile_begin].page * Hkv + g) * kTile;
-    stage_bricks<4>(lk[0], kn + base, 4 * wave, lane);
-    stage_cbricks<4>(lv[0], vt + base, 4 * wave, lane);
+    stage_bricks<4>(lk[0], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
+    stage_cbricks<4>(lv[0], tile_rsrc(vt + base, kTile * 2), 4 * wave, clo);
   }
   wait_all_loads();
   __syncthreads();
@@ -353,8 +387,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
     const int buf = t & 1;
     if (t + 1 < T && wave < 4) {
       const int64_t base = ((int64_t)tiles[qp.tile_begin + t + 1].page * Hkv + g) * kTile;
-      stage_bricks<4>(lk[buf ^ 1], kn + base, 4 * wave, lane);
-      stage_cbricks<4>(lv[buf ^ 1], vt + base, 4 * wave, lane);
+      stage_bricks<4>(lk[buf ^ 1], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
+      stage_cbricks<4>(lv[buf ^ 1], tile_rsrc(vt + base, kTile * 2), 4 * wave, clo);
     }
     const int lohi = tiles[qp.tile_begin + t].lohi;
     const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
@@ -476,12 +510,13 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
   if (!map_item(n_qp, Hkv, unit, g)) return;
   const QPage qp = qpages[order[unit]];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
   const int l32 = lane & 31, hi = lane >> 5;
   const int hh = wave & 3, nb = wave >> 2;
   const int h = g * 4 + hh;
   const int row = nb * 32 + l32;
   const int kb0 = frag_base(l32, hi), tb0 = cfrag_base(l32, hi);
+  const uint32_t rlo = brick_lane_off(lane), clo = cbrick_lane_off(lane);
 
   f16x8 qf[8], df[8];
   const f16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
@@ -500,9 +535,9 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
   const int T = qp.tile_count;
   if (wave < 4) {
     const int64_t base = ((int64_t)tiles[qp.tile_begin].page * Hkv + g) * kTile;
-    stage_bricks<4>(lk[0], kn + base, 4 * wave, lane);
-    stage_bricks<4>(lvv[0], vn + base, 4 * wave, lane);
-    stage_cbricks<4>(lkt[0], kt + base, 4 * wave, lane);
+    stage_bricks<4>(lk[0], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
+    stage_bricks<4>(lvv[0], tile_rsrc(vn + base, kTile * 2), 4 * wave, rlo);
+    stage_cbricks<4>(lkt[0], tile_rsrc(kt + base, kTile * 2), 4 * wave, clo);
   }
   wait_all_loads();
   __syncthreads();
@@ -511,9 +546,9 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
     const int buf = t & 1;
     if (t + 1 < T && wave < 4) {
       const int64_t base = ((int64_t)tiles[qp.tile_begin + t + 1].page * Hkv + g) * kTile;
-      stage_bricks<4>(lk[buf ^ 1], kn + base, 4 * wave, lane);
-      stage_bricks<4>(lvv[buf ^ 1], vn + base, 4 * wave, lane);
-      stage_cbricks<4>(lkt[buf ^ 1], kt + base, 4 * wave, lane);
+      stage_bricks<4>(lk[buf ^ 1], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
+      stage_bricks<4>(lvv[buf ^ 1], tile_rsrc(vn + base, kTile * 2), 4 * wave, rlo);
+      stage_cbricks<4>(lkt[buf ^ 1], tile_rsrc(kt + base, kTile * 2), 4 * wave, clo);
     }
     const int lohi = tiles[qp.tile_begin + t].lohi;
     const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
@@ -674,7 +709,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
   if (!map_item(n_kvp, Hkv, unit, g)) return;
   const int page = order[unit];
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
   const int l32 = lane & 31, hi = lane >> 5;
   const int hh = wave & 3, kb = wave >> 2;
   const int krows = page_nrows[page];
@@ -686,7 +721,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const int64_t base = ((int64_t)page * Hkv + g) * 64 * kD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kf[ks] = ld8(kn + base + (kb * 32 + l32) * kD + ks * 16 + hi * 8);
-    if (wave < 4) stage_bricks<4>(lvp, vn + base, 4 * wave, lane);
+    if (wave < 4) stage_bricks<4>(lvp, tile_rsrc(vn + base, kTile * 2), 4 * wave, brick_lane_off(lane));
   }
   f32x16 adk[4], adv[4];  // [d block]
 #pragma unroll
@@ -698,16 +733,16 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
   KEntry ent = ents[e];
   int lq = ent.lq0, rb = 0;
   int qph = page_table[ent.slot_base + lq];
+  const uint32_t rlo = brick_lane_off(lane);
+  const uint32_t llo = (uint32_t)((2 * (lane & 31) + (lane >> 5)) * 4);
   auto stage = [&](int buf, int qp_, int rb_) {
     // wave (hh, kb) fetches head 4 g + hh's Q rows (kb = 0) or dO rows (kb = 1): 8 KiB
     const int64_t src = (((int64_t)qp_ * Hq + g * 4 + hh) * 64 + rb_ * 32) * kD;
-    stage_bricks<8>(qd[buf][hh][kb], (kb == 0 ? qn : dOn) + src, 0, lane);
+    stage_bricks<8>(qd[buf][hh][kb], tile_rsrc((kb == 0 ? qn : dOn) + src, 32 * kD * 2), 0, rlo);
     if (kb == 0) {
       // lane i < 32 takes row i's S offset, lane 32 + i its dP offset (4 bytes each,
       // landing at slot i of the 64-float block)
-      const float* lsrc = reinterpret_cast<const float*>(ldd + ((int64_t)qp_ * Hq + g * 4 + hh) * 64 + rb_ * 32);
-      __builtin_amdgcn_global_load_lds(lsrc + 2 * (lane & 31) + (lane >> 5), (lds_void*)(&lds_ld[buf][hh][0]), 4,
-                                       0, 0);
+      dma4(&lds_ld[buf][hh][0], llo, tile_rsrc(ldd + ((int64_t)qp_ * Hq + g * 4 + hh) * 64 + rb_ * 32, 256), 0);
     }
   };
   stage(0, qph, 0);
