@@ -694,9 +694,8 @@ template <typename TG>
 __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vn,
     const f16_t* __restrict__ dOn, const float2* __restrict__ ldd, const float2* __restrict__ cs,
-    const uint32_t* __restrict__ dmax, const int32_t* __restrict__ order, const int32_t* __restrict__ kv_off,
-    const int32_t* __restrict__ kv_steps, const KEntry* __restrict__ ents, const int32_t* __restrict__ page_table,
-    const int32_t* __restrict__ page_nrows, TG* __restrict__ dk, TG* __restrict__ dv, int n_kvp, int Hq, int Hkv,
+    const uint32_t* __restrict__ dmax, const int32_t* __restrict__ order, const int64_t* __restrict__ kstep_off,
+    const KStep* __restrict__ ksteps, const int32_t* __restrict__ page_nrows, TG* __restrict__ dk, TG* __restrict__ dv, int n_kvp, int Hq, int Hkv,
     float sl2, float scale) {
   // [buffer][head][Q, dO][32 x 128] f16, then [buffer][head] the 32 rows'
   // accumulator offsets, -lse / scale for S and then -D for dP; the first 33 KiB
@@ -727,12 +726,28 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
 #pragma unroll
   for (int b = 0; b < 4; ++b) adk[b] = adv[b] = zero16();
 
-  // reader-list cursor: entry e, reader page lq, row block rb (32 rows)
-  const int n_steps = kv_steps[page];
-  int e = kv_off[page];
-  KEntry ent = ents[e];
-  int lq = ent.lq0, rb = 0;
-  int qph = page_table[ent.slot_base + lq];
+  // The page's reader steps.  Step it + 1's descriptor is in SGPRs when step it
+  // begins (its tiles are staged then).  Descriptors come from a 64-step window
+  // held one per lane in VGPRs and picked with readlane; the window is refilled
+  // right after a step's closing wait, when no load is in flight, so a step never
+  // waits on a descriptor load (one load latency per 64 steps).
+  const int64_t s_begin = kstep_off[page];
+  const int n_steps = (int)(kstep_off[page + 1] - s_begin);
+  const KStep* kst = ksteps + s_begin;
+  int wbase = 0;
+  KStep wdesc = kst[min(lane, n_steps - 1)];
+  auto desc = [&](int i) {
+    if (i - wbase >= 64) {
+      wbase = i;
+      wdesc = kst[min(i + lane, n_steps - 1)];
+    }
+    KStep d;
+    d.qph = __builtin_amdgcn_readlane(wdesc.qph, i - wbase);
+    d.info = __builtin_amdgcn_readlane(wdesc.info, i - wbase);
+    return d;
+  };
+  KStep cur = desc(0);
+  KStep nxt = desc(min(1, n_steps - 1));
   const uint32_t rlo = brick_lane_off(lane);
   const uint32_t llo = (uint32_t)((2 * (lane & 31) + (lane >> 5)) * 4);
   auto stage = [&](int buf, int qp_, int rb_) {
@@ -745,7 +760,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
       dma4(&lds_ld[buf][hh][0], llo, tile_rsrc(ldd + ((int64_t)qp_ * Hq + g * 4 + hh) * 64 + rb_ * 32, 256), 0);
     }
   };
-  stage(0, qph, 0);
+  stage(0, cur.qph, cur.info & 1);
   wait_all_loads();
   __syncthreads();
 
@@ -753,22 +768,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
   const int key = kb * 32 + l32;
   const int qb = frag_base(l32, hi), vb = frag_base(key, hi), tb = tr_base(lane);
   for (int it = 0; it < n_steps; ++it) {
-    // where the next step is (a reader page of <= 32 rows has one row block)
     const bool more = it + 1 < n_steps;
-    int n_e = e, n_lq = lq, n_rb = rb + 1, n_qph = qph;
-    const int nrows = page_nrows[qph];
-    if (n_rb == 2 || n_rb * 32 >= nrows) {
-      n_rb = 0;
-      if (++n_lq == ent.lq1) {
-        ++n_e;
-        if (more) n_lq = ents[n_e].lq0;
-      }
-      if (more) n_qph = page_table[ents[n_e].slot_base + n_lq];
-    }
-    if (more) stage(buf ^ 1, n_qph, n_rb);
+    if (more) stage(buf ^ 1, nxt.qph, nxt.info & 1);
 
-    const int lo = ent.lohi_diag & 0xff, hi_t = (ent.lohi_diag >> 8) & 0xff;
-    const bool diag = (ent.lohi_diag >> 16) & 1;
+    const int rb = cur.info & 1, lo = (cur.info >> 1) & 0x7f, hi_t = (cur.info >> 8) & 0x7f;
+    const bool diag = (cur.info >> 15) & 1;
+    const int nrows = (cur.info >> 16) & 0x7f;
     const bool full = lo == 0 && hi_t == 64 && !diag && nrows >= rb * 32 + 32;
     const f16_t* Qt = qd[buf][hh][0];
     const f16_t* Dt = qd[buf][hh][1];
@@ -867,11 +872,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     wait_all_loads();
     __syncthreads();
     buf ^= 1;
-    if (more && n_e != e) ent = ents[n_e];
-    e = n_e;
-    lq = n_lq;
-    rb = n_rb;
-    qph = n_qph;
+    cur = nxt;
+    nxt = desc(min(it + 2, n_steps - 1));
   }
 
   const float inv_sdo = 1.f / pow2_scale(*dmax);  // undo the dO scaling
@@ -1122,10 +1124,10 @@ void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f
 template <typename TG>
 void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, const f16_t* kn, const f16_t* vn,
                       const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
-                      const int32_t* order, const int32_t* kv_off, const int32_t* kv_steps, const KEntry* ents,
-                      const int32_t* page_table, const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st) {
-  dkdv_mfma_kernel<TG><<<run_grid(n_kvp, s.Hkv), 512, 0, st>>>(qn, kn, vn, dOn, ld, cs, dmax, order, kv_off,
-                                                               kv_steps, ents, page_table, page_nrows, dk, dv,
+                      const int32_t* order, const int64_t* kstep_off, const KStep* ksteps,
+                      const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st) {
+  dkdv_mfma_kernel<TG><<<run_grid(n_kvp, s.Hkv), 512, 0, st>>>(qn, kn, vn, dOn, ld, cs, dmax, order, kstep_off,
+                                                               ksteps, page_nrows, dk, dv,
                                                                (int)n_kvp, s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
 }
 
@@ -1135,8 +1137,8 @@ void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, cons
                                    const QPage*, const int32_t*, const Tile*, TG*, hipStream_t);               \
   template void launch_dkdv_mfma<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,    \
                                      const f16_t*, const float2*, const float2*, const uint32_t*,              \
-                                     const int32_t*, const int32_t*, const int32_t*, const KEntry*,            \
-                                     const int32_t*, const int32_t*, TG*, TG*, hipStream_t);
+                                     const int32_t*, const int64_t*, const KStep*, const int32_t*, TG*, TG*,    \
+                                     hipStream_t);
 INST_MFMA_BWD(bf16_t)
 INST_MFMA_BWD(float)
 

@@ -37,8 +37,8 @@ void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f
 template <typename TG>
 void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, const f16_t* kn, const f16_t* vn,
                       const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
-                      const int32_t* order, const int32_t* kv_off, const int32_t* kv_steps, const KEntry* ents,
-                      const int32_t* page_table, const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st);
+                      const int32_t* order, const int64_t* kstep_off, const KStep* ksteps,
+                      const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st);
 template <typename T>
 void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,
                        const QPage* qpages, const int32_t* order, const Tile* tiles, T* o, float* lse, T* o_lo,

@@ -313,8 +313,8 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
     for_each_entry([&](int32_t ph, const KEntry& e) { P->kentries[fill[ph]++] = e; });
   }
 
-  // 32-row reader blocks per KV page (the dK/dV kernel's loop count)
-  P->kv_steps.assign(n_pages, 0);
+  // reader lists unrolled into 32-row steps (the dK/dV kernel's loop), in list order
+  P->kstep_off.assign(n_pages + 1, 0);
   for (int32_t ph = 0; ph < n_pages; ++ph) {
     int64_t steps = 0;
     for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
@@ -322,7 +322,21 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
       for (int32_t lq = k.lq0; lq < k.lq1; ++lq) steps += P->page_nrows[P->page_table[k.slot_base + lq]] > 32 ? 2 : 1;
     }
     if (steps > INT32_MAX) return fail(err, DAG_E_OVERFLOW, "reader list too long");
-    P->kv_steps[ph] = (int32_t)steps;
+    P->kstep_off[ph + 1] = P->kstep_off[ph] + steps;
+  }
+  P->ksteps.resize((size_t)P->kstep_off[n_pages]);
+  for (int32_t ph = 0; ph < n_pages; ++ph) {
+    int64_t i = P->kstep_off[ph];
+    for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
+      const KEntry& k = P->kentries[e];
+      const int32_t vis = k.lohi_diag & 0x1ffff;  // lo | hi << 8 | diag << 16
+      const int32_t packed = ((vis & 0xff) << 1) | (((vis >> 8) & 0xff) << 8) | (((vis >> 16) & 1) << 15);
+      for (int32_t lq = k.lq0; lq < k.lq1; ++lq) {
+        const int32_t qph = P->page_table[k.slot_base + lq];
+        const int32_t nr = P->page_nrows[qph];
+        for (int32_t rb = 0; rb < (nr > 32 ? 2 : 1); ++rb) P->ksteps[(size_t)i++] = KStep{qph, rb | packed | (nr << 16)};
+      }
+    }
   }
 
   // ---- 9. launch orders -------------------------------------------------------------

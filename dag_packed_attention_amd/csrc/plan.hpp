@@ -42,6 +42,15 @@ struct KEntry {
   int32_t lohi_diag;  // lo | (hi << 8) | (diag << 16)
 };
 
+// One 32-row step of a KV page's reader list, as the dK/dV kernel walks it: rows
+// 32 rb .. 32 rb + 31 of physical query page qph see rows [lo, hi) of the KV page
+// (diag: the page's own query block, masked causally); nrows = qph's valid rows.
+// Packed so a kernel fetches a step with one 8-byte load.
+struct KStep {
+  int32_t qph;
+  int32_t info;  // rb | lo << 1 | hi << 8 | diag << 15 | nrows << 16
+};
+
 // One packed gated-delta-rule input sequence as the kernels read it.  Its
 // tokens are rows[tok_off .. tok_off + n_tok): n_replay replayed ancestor
 // tokens (state updates only), then its own tokens.  Token j sits at
@@ -84,7 +93,8 @@ struct Plan {
   std::vector<QPage> qpages;
   std::vector<int32_t> fwd_order;              // query-page ids, heaviest first
   std::vector<int32_t> kv_off;                 // physical page -> first reader entry (size pages+1)
-  std::vector<int32_t> kv_steps;               // physical page -> 32-row reader blocks over its list
+  std::vector<int64_t> kstep_off;              // physical page -> its first reader step (size pages+1)
+  std::vector<KStep> ksteps;                   // reader lists unrolled into 32-row steps
   std::vector<KEntry> kentries;
   std::vector<int32_t> bwd_order;              // physical pages with rows, heaviest first
   std::vector<int32_t> pos_of_row;             // C

@@ -38,6 +38,31 @@ static int check(const Plan& P) {
       const int lo = k.lohi_diag & 0xff, hi = (k.lohi_diag >> 8) & 0xff;
       if (lo >= hi || hi > P.page_nrows[ph]) return 7;
     }
+  // reader steps: the entries unrolled in order, one step per 32-row block
+  if ((int64_t)P.kstep_off.size() != pages + 1 || P.kstep_off[0] != 0) return 8;
+  for (int64_t ph = 0; ph < pages; ++ph) {
+    int64_t i = P.kstep_off[ph];
+    for (int e = P.kv_off[ph]; e < P.kv_off[ph + 1]; ++e) {
+      const KEntry& k = P.kentries[e];
+      for (int lq = k.lq0; lq < k.lq1; ++lq) {
+        const int qph = P.page_table[k.slot_base + lq];
+        const int nr = P.page_nrows[qph];
+        for (int rb = 0; rb * 32 < nr; ++rb, ++i) {
+          if (i >= P.kstep_off[ph + 1]) return 9;
+          const KStep& st = P.ksteps[i];
+          const int lo = (st.info >> 1) & 0x7f, hi = (st.info >> 8) & 0x7f;
+          if (st.qph != qph || (st.info & 1) != rb || ((st.info >> 16) & 0x7f) != nr) return 10;
+          if (lo != (k.lohi_diag & 0xff) || hi != ((k.lohi_diag >> 8) & 0xff) ||
+              ((st.info >> 15) & 1) != ((k.lohi_diag >> 16) & 1) || (st.info >> 23) != 0)
+            return 11;
+        }
+      }
+    }
+    if (i != P.kstep_off[ph + 1]) return 12;
+  }
+  if ((int64_t)P.ksteps.size() != P.kstep_off[pages]) return 13;
+  for (int32_t ph : P.bwd_order)
+    if (ph < 0 || ph >= pages || P.kstep_off[ph + 1] <= P.kstep_off[ph]) return 14;  // a launched page has steps
   return 0;
 }
 
