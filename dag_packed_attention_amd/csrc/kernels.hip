@@ -768,8 +768,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
   const int key = kb * 32 + l32;
   const int qb = frag_base(l32, hi), vb = frag_base(key, hi), tb = tr_base(lane);
   for (int it = 0; it < n_steps; ++it) {
-    const bool more = it + 1 < n_steps;
-    if (more) stage(buf ^ 1, nxt.qph, nxt.info & 1);
+    // Step it + 1's staging goes out one instruction per k-step of the S/dP
+    // products below: issued all at once, the eight waves' loads fill the memory
+    // pipeline's queue and every wave stalls at issue until it drains.  On the last
+    // step nxt repeats the current step (harmless: buf ^ 1 is not read again).
+    const int64_t nsrc = (((int64_t)nxt.qph * Hq + g * 4 + hh) * 64 + (nxt.info & 1) * 32) * kD;
+    const i32x4 nrs = tile_rsrc((kb == 0 ? qn : dOn) + nsrc, 32 * kD * 2);
+    f16_t* ndst = qd[buf ^ 1][hh][kb];
 
     const int rb = cur.info & 1, lo = (cur.info >> 1) & 0x7f, hi_t = (cur.info >> 8) & 0x7f;
     const bool diag = (cur.info >> 15) & 1;
@@ -808,7 +813,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
         }
         s = mfma(qa[ks & 1], kf[ks], s);
         dp = mfma(da[ks & 1], va[ks & 1], dp);
+        dma16(ndst + ks * kBrick, rlo, nrs, ks * 4 * kD * 2);
       }
+      // both waves of a head fetch the same offsets into the same place (same bytes)
+      dma4(&lds_ld[buf ^ 1][hh][0], llo,
+           tile_rsrc(ldd + ((int64_t)nxt.qph * Hq + g * 4 + hh) * 64 + (nxt.info & 1) * 32, 256), 0);
       __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
       for (int ks = 0; ks < 7; ++ks) {
