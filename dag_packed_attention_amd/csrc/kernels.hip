@@ -726,28 +726,16 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
 #pragma unroll
   for (int b = 0; b < 4; ++b) adk[b] = adv[b] = zero16();
 
-  // The page's reader steps.  Step it + 1's descriptor is in SGPRs when step it
-  // begins (its tiles are staged then).  Descriptors come from a 64-step window
-  // held one per lane in VGPRs and picked with readlane; the window is refilled
-  // right after a step's closing wait, when no load is in flight, so a step never
-  // waits on a descriptor load (one load latency per 64 steps).
+  // The page's reader steps.  Descriptors are uniform and come through the scalar
+  // cache three steps ahead of the step they describe, so no step waits on one and
+  // no vector-memory wait is needed for them (that would also wait for the staging
+  // loads in flight).
   const int64_t s_begin = kstep_off[page];
   const int n_steps = (int)(kstep_off[page + 1] - s_begin);
   const KStep* kst = ksteps + s_begin;
-  int wbase = 0;
-  KStep wdesc = kst[min(lane, n_steps - 1)];
-  auto desc = [&](int i) {
-    if (i - wbase >= 64) {
-      wbase = i;
-      wdesc = kst[min(i + lane, n_steps - 1)];
-    }
-    KStep d;
-    d.qph = __builtin_amdgcn_readlane(wdesc.qph, i - wbase);
-    d.info = __builtin_amdgcn_readlane(wdesc.info, i - wbase);
-    return d;
-  };
-  KStep cur = desc(0);
-  KStep nxt = desc(min(1, n_steps - 1));
+  KStep cur = kst[0];
+  KStep nxt = kst[min(1, n_steps - 1)];
+  KStep n2 = kst[min(2, n_steps - 1)];
   const uint32_t rlo = brick_lane_off(lane);
   const uint32_t llo = (uint32_t)((2 * (lane & 31) + (lane >> 5)) * 4);
   auto stage = [&](int buf, int qp_, int rb_) {
@@ -778,8 +766,6 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
 
     const int rb = cur.info & 1, lo = (cur.info >> 1) & 0x7f, hi_t = (cur.info >> 8) & 0x7f;
     const bool diag = (cur.info >> 15) & 1;
-    const int nrows = (cur.info >> 16) & 0x7f;
-    const bool full = lo == 0 && hi_t == 64 && !diag && nrows >= rb * 32 + 32;
     const f16_t* Qt = qd[buf][hh][0];
     const f16_t* Dt = qd[buf][hh][1];
     // S = Q K^T - lse / scale, dP = dO V^T - D: 32 rows (M) x this wave's 32 keys (N);
@@ -797,92 +783,131 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
         dp[4 * j] = b.x, dp[4 * j + 1] = b.y, dp[4 * j + 2] = b.z, dp[4 * j + 3] = b.w;
       }
     }
+    // The four products run as four chains of eight MFMAs, S, dP, dV, dK, and each
+    // chain carries the vector work of the previous one: the exponentials of S run
+    // between the dP products, dS = P (dP - D) between the dV products.  A key
+    // outside the step's visible range gets -inf added before the exponential.
+    const float koff = (key >= lo && key < hi_t) ? 0.f : -INFINITY;
     {
-      // software-pipelined: k-step ks + 1's three fragments are read while k-step
-      // ks's two products run (the group barriers pin that interleave)
-      f16x8 qa[2], da[2], va[2];
+      // S: Q fragments read one k-step ahead; step it + 1's staging goes out one
+      // load per k-step
+      f16x8 qa[2];
       qa[0] = ld8(Qt + qb);
-      da[0] = ld8(Dt + qb);
-      va[0] = ld8(lvp + vb);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        if (ks < 7) {
-          qa[(ks + 1) & 1] = ld8(Qt + qb + kstep(ks + 1));
-          da[(ks + 1) & 1] = ld8(Dt + qb + kstep(ks + 1));
-          va[(ks + 1) & 1] = ld8(lvp + vb + kstep(ks + 1));
-        }
+        if (ks < 7) qa[(ks + 1) & 1] = ld8(Qt + qb + kstep(ks + 1));
         s = mfma(qa[ks & 1], kf[ks], s);
-        dp = mfma(da[ks & 1], va[ks & 1], dp);
         dma16(ndst + ks * kBrick, rlo, nrs, ks * 4 * kD * 2);
       }
       // both waves of a head fetch the same offsets into the same place (same bytes)
       dma4(&lds_ld[buf ^ 1][hh][0], llo,
            tile_rsrc(ldd + ((int64_t)nxt.qph * Hq + g * 4 + hh) * 64 + (nxt.info & 1) * 32, 256), 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
 #pragma unroll
       for (int ks = 0; ks < 7; ++ks) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     }
-    if (full) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(s[r] * sl2);
-        s[r] = p;
-        dp[r] = p * dp[r];
-      }
-    } else {
-      // every operand here comes from the zero-padded relayouts, so all values are finite
-      const bool key_ok = key >= lo && key < hi_t;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = rb * 32 + acc_row(r, hi);
-        const bool ok = key_ok && (!diag || key <= row) && row < nrows;
-        const float p = ok ? __builtin_amdgcn_exp2f(s[r] * sl2) : 0.f;  // a hidden score may overflow
-        s[r] = p;
-        dp[r] = p * dp[r];
-      }
-    }
-    const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8), sf0 = pack8(dp, 0), sf1 = pack8(dp, 8);
-    // dV += P^T dO, dK += dS^T Q: keys (M) x d (N), the 32 rows contracted; d block
-    // b + 1's four fragments (eight transpose reads) are read while block b's four
-    // products run
+    __builtin_amdgcn_sched_barrier(0);
     {
-      f16x8 fr[2][4];
-      const f16_t* Dtb = Dt + tb;
-      const f16_t* Qtb = Qt + tb;
+      // dP, with P = 2^(S scale log2 e) computed in between
+      f16x8 da[2], va[2];
+      da[0] = ld8(Dt + qb);
+      va[0] = ld8(lvp + vb);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks < 7) {
+          da[(ks + 1) & 1] = ld8(Dt + qb + kstep(ks + 1));
+          va[(ks + 1) & 1] = ld8(lvp + vb + kstep(ks + 1));
+        }
+        dp = mfma(da[ks & 1], va[ks & 1], dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, koff));
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if (ks < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (diag) {
+      // the reader's own page: key <= row (a hidden score may have overflowed: select)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[r] = key <= rb * 32 + acc_row(r, hi) ? s[r] : 0.f;
+    }
+    // Padding rows need no mask: their Q and dO rows and offsets are zero, so they add
+    // exact zeros to dV and dK.
+    const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8);
+    // dV += P^T dO, then dK += dS^T Q: keys (M) x d (N), the 32 rows contracted; d
+    // block b + 1's fragments (transpose reads) are read while block b's products run
+    const f16_t* Dtb = Dt + tb;
+    const f16_t* Qtb = Qt + tb;
+    f16x8 sf0, sf1;
+    f16x8 frq[2];
+    {
+      f16x8 fr[2][2];
       fr[0][0] = frag_tr(Dtb, 0, 0);
       fr[0][1] = frag_tr(Dtb, 1, 0);
-      fr[0][2] = frag_tr(Qtb, 0, 0);
-      fr[0][3] = frag_tr(Qtb, 1, 0);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
         if (b < 3) {
           fr[(b + 1) & 1][0] = frag_tr(Dtb, 0, b + 1);
           fr[(b + 1) & 1][1] = frag_tr(Dtb, 1, b + 1);
-          fr[(b + 1) & 1][2] = frag_tr(Qtb, 0, b + 1);
-          fr[(b + 1) & 1][3] = frag_tr(Qtb, 1, b + 1);
         }
         adv[b] = mfma(pf0, fr[b & 1][0], adv[b]);
         adv[b] = mfma(pf1, fr[b & 1][1], adv[b]);
-        adk[b] = mfma(sf0, fr[b & 1][2], adk[b]);
-        adk[b] = mfma(sf1, fr[b & 1][3], adk[b]);
       }
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dp[r] *= s[r];
+      sf0 = pack8(dp, 0);
+      sf1 = pack8(dp, 8);
+      frq[0] = frag_tr(Qtb, 0, 0);
+      frq[1] = frag_tr(Qtb, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      f16x8 fr[2][2];
+      fr[0][0] = frq[0];
+      fr[0][1] = frq[1];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        if (b < 3) {
+          fr[(b + 1) & 1][0] = frag_tr(Qtb, 0, b + 1);
+          fr[(b + 1) & 1][1] = frag_tr(Qtb, 1, b + 1);
+        }
+        adk[b] = mfma(sf0, fr[b & 1][0], adk[b]);
+        adk[b] = mfma(sf1, fr[b & 1][1], adk[b]);
+      }
 #pragma unroll
       for (int b = 0; b < 3; ++b) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
+    // step it + 3's descriptor: issued here, where the closing wait covers it
+    __builtin_amdgcn_sched_barrier(0);
+    const KStep n3 = kst[min(it + 3, n_steps - 1)];
     wait_all_loads();
     __syncthreads();
     buf ^= 1;
     cur = nxt;
-    nxt = desc(min(it + 2, n_steps - 1));
+    nxt = n2;
+    n2 = n3;
   }
 
   const float inv_sdo = 1.f / pow2_scale(*dmax);  // undo the dO scaling
