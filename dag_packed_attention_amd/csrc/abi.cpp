@@ -507,9 +507,9 @@ dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q,
     if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
     const int32_t* nr = D.page_nrows;
     if (mfma) {
-      launch_relayout<bf16_t, f16_t>(s, (const bf16_t*)q, w.cs, nr, nullptr, (f16_t*)w.qn, nullptr, s.Hq, stream);
-      launch_relayout<bf16_t, f16_t>(s, (const bf16_t*)k, w.cs, nr, nullptr, (f16_t*)w.kn, nullptr, s.Hkv, stream);
-      launch_relayout<bf16_t, f16_t>(s, (const bf16_t*)v, nullptr, nr, nullptr, nullptr, (f16_t*)w.vt, s.Hkv, stream);
+      launch_prep16(s, (const bf16_t*)q, w.cs, nr, nullptr, (f16_t*)w.qn, nullptr, nullptr, s.Hq, stream);
+      launch_prep16(s, (const bf16_t*)k, w.cs, nr, nullptr, (f16_t*)w.kn, nullptr, nullptr, s.Hkv, stream);
+      launch_prep16(s, (const bf16_t*)v, nullptr, nr, nullptr, nullptr, (f16_t*)w.vt, nullptr, s.Hkv, stream);
     } else if (p->dtype == DAG_DTYPE_BF16) {
       launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, nr, nullptr, (float*)w.qn, nullptr, s.Hq, stream);
       launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, nr, nullptr, (float*)w.kn, nullptr, s.Hkv, stream);
@@ -562,12 +562,11 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       const int32_t* nr = D.page_nrows;
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
       if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
-      launch_maxabs<bf16_t>(s, d16, s.Hq, nr, w.dmax, stream);
-      launch_rowdot<bf16_t>(s, o16, (const bf16_t*)o_lo, d16, lse, nr, w.dmax, w.ld, stream);
-      launch_relayout<bf16_t, f16_t>(s, q16, w.cs, nr, nullptr, (f16_t*)w.qn, nullptr, s.Hq, stream);
-      launch_relayout<bf16_t, f16_t>(s, k16, w.cs, nr, nullptr, (f16_t*)w.kn, (f16_t*)w.kt, s.Hkv, stream);
-      launch_relayout<bf16_t, f16_t>(s, v16, nullptr, nr, nullptr, (f16_t*)w.vn, nullptr, s.Hkv, stream);
-      launch_relayout<bf16_t, f16_t>(s, d16, nullptr, nr, w.dmax, (f16_t*)w.dOn, nullptr, s.Hq, stream);
+      launch_rowdot16(s, o16, (const bf16_t*)o_lo, d16, lse, nr, w.ld, w.dmax, stream);
+      launch_prep16(s, q16, w.cs, nr, nullptr, (f16_t*)w.qn, nullptr, nullptr, s.Hq, stream);
+      launch_prep16(s, k16, w.cs, nr, nullptr, (f16_t*)w.kn, (f16_t*)w.kt, nullptr, s.Hkv, stream);
+      launch_prep16(s, v16, nullptr, nr, nullptr, (f16_t*)w.vn, nullptr, nullptr, s.Hkv, stream);
+      launch_prep16(s, d16, nullptr, nr, w.dmax, (f16_t*)w.dOn, nullptr, w.ld, s.Hq, stream);
     }
     auto grads = [&](auto* tag) {
       using TG = std::remove_pointer_t<decltype(tag)>;

@@ -174,28 +174,8 @@ __global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ o_l
   }
 }
 
-// max |x| over the valid rows of a [C][H][D] tensor, as float bits (an integer maximum is
-// exact and order-free, so the result does not depend on scheduling).  *out must be 0 first.
+// *out = 0 (before a kernel that takes an integer maximum into it)
 __global__ void zero_u32_kernel(uint32_t* out) { *out = 0u; }
-
-template <typename T>
-__global__ __launch_bounds__(256) void maxabs_kernel(const T* __restrict__ x, const int32_t* __restrict__ page_nrows,
-                                                     int64_t n_pages, int64_t row_elems, uint32_t* __restrict__ out) {
-  __shared__ float red[4];
-  float m = 0.f;
-  const int64_t total = n_pages * 64;
-  for (int64_t row = blockIdx.x; row < total; row += gridDim.x) {
-    if ((int)(row % 64) >= page_nrows[row / 64]) continue;
-    for (int64_t i = threadIdx.x; i < row_elems; i += blockDim.x) m = fmaxf(m, fabsf(ld_f(x + row * row_elems + i)));
-  }
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const float b = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    atomicMax(out, __float_as_uint(b));
-  }
-}
 
 // ---------------------------------------------------------------------------
 // MFMA kernels: D = 128, four query heads per KV head, fp16 operands
@@ -204,6 +184,125 @@ __global__ __launch_bounds__(256) void maxabs_kernel(const T* __restrict__ x, co
 constexpr int kD = 128;
 
 constexpr int kRun = 8;  // consecutive units of one head that go to one XCD
+
+// Prologue of the MFMA path (D = 128, bf16 in, fp16 out).  One block of 512
+// threads per 64-row page walks the page's heads; thread (r, j) owns row r's
+// columns 8 j .. 8 j + 7 and 64 + 8 j .. 64 + 8 j + 7 (rotation pairs), read and
+// written as 16-byte pieces, so every global access is a full 128-byte run per
+// eight threads.  Optional: rotation by R(pos) (kRot), the page-major natural
+// copy [page][H][64][128] (kNat), the transposed copy [page][H][128][64] with
+// rows in MFMA order (kTrans, through LDS), a power-of-two scale from smax, and
+// the same scale applied to the -D offsets in ld (the dO copy).  Padding rows
+// become zeros.
+typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
+template <bool kRot, bool kNat, bool kTrans>
+__global__ __launch_bounds__(512) void prep16_kernel(const bf16_t* __restrict__ x, const float2* __restrict__ cs,
+                                                     const int32_t* __restrict__ page_nrows,
+                                                     const uint32_t* __restrict__ smax, f16_t* __restrict__ out_n,
+                                                     f16_t* __restrict__ out_t, float2* __restrict__ ld_fix, int H) {
+  constexpr int kTs = 72;  // padded row of the transposed tile (elements)
+  __shared__ __attribute__((aligned(16))) f16_t tt[kTrans ? 128 * kTs : 8];
+  const int page = blockIdx.x, t = threadIdx.x, r = t >> 3, j = t & 7;
+  const bool valid = r < page_nrows[page];
+  const int64_t row = (int64_t)page * 64 + r;
+  float c[8], sn[8];
+  if (kRot) {
+    const float4* cp = reinterpret_cast<const float4*>(cs + row * 64 + 8 * j);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float4 v = valid ? cp[e] : make_float4(1.f, 0.f, 1.f, 0.f);
+      c[2 * e] = v.x, sn[2 * e] = v.y, c[2 * e + 1] = v.z, sn[2 * e + 1] = v.w;
+    }
+  }
+  const float sc = smax ? pow2_scale(*smax) : 1.f;
+  for (int h = 0; h < H; ++h) {
+    const bf16_t* src = x + (row * H + h) * kD + 8 * j;
+    u16x8 ua = {}, ub = {};
+    if (valid) {
+      ua = *reinterpret_cast<const u16x8*>(src);
+      ub = *reinterpret_cast<const u16x8*>(src + 64);
+    }
+    f16x8 fa, fb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float a = bf2f(ua[e]), b = bf2f(ub[e]);
+      if (kRot) {
+        const float a2 = a * c[e] - b * sn[e];
+        b = b * c[e] + a * sn[e];
+        a = a2;
+      }
+      fa[e] = (f16_t)(a * sc);
+      fb[e] = (f16_t)(b * sc);
+    }
+    if (kNat) {
+      f16_t* dst = out_n + (((int64_t)page * H + h) * 64 + r) * kD + 8 * j;
+      *reinterpret_cast<f16x8*>(dst) = fa;
+      *reinterpret_cast<f16x8*>(dst + 64) = fb;
+    }
+    if (kTrans) {
+      const int p = tperm(r);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        tt[(8 * j + e) * kTs + p] = fa[e];
+        tt[(64 + 8 * j + e) * kTs + p] = fb[e];
+      }
+      __syncthreads();
+      f16_t* dst = out_t + ((int64_t)page * H + h) * kD * 64;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int q = t + 512 * k, d = q >> 3, p0 = (q & 7) * 8;
+        *reinterpret_cast<f16x8*>(dst + d * 64 + p0) = *reinterpret_cast<const f16x8*>(&tt[d * kTs + p0]);
+      }
+      __syncthreads();
+    }
+    if (ld_fix && j == 0) ld_fix[((int64_t)page * H + h) * 64 + r].y *= sc;
+  }
+}
+
+// ld[page][h][r] = (-lse / scale, -sum_d dO O) with O = o (+ o_lo), zero on padding
+// rows, and *dmax = max |dO| over valid rows (float bits; an integer maximum is exact
+// and order-free).  Sixteen lanes per (row, head), eight elements each (16-byte loads),
+// summed in a fixed order; grid-stride over (row, head).  *dmax must be 0 first.
+__global__ __launch_bounds__(256) void rowdot16_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ o_lo,
+                                                       const bf16_t* __restrict__ dO, const float* __restrict__ lse,
+                                                       const int32_t* __restrict__ page_nrows,
+                                                       float2* __restrict__ ldout, uint32_t* __restrict__ dmax,
+                                                       int64_t n_pages, int Hq, float inv_scale) {
+  __shared__ float red[4];
+  const int sub = threadIdx.x & 15;
+  const int64_t total = n_pages * 64 * Hq;
+  float m = 0.f;
+  for (int64_t it = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); it < total; it += (int64_t)gridDim.x * 16) {
+    const int64_t row = it / Hq;
+    const int h = (int)(it % Hq);
+    const int64_t page = row >> 6;
+    const int r = (int)(row & 63);
+    const bool valid = r < page_nrows[page];
+    float acc = 0.f;
+    if (valid) {
+      const int64_t e = (row * Hq + h) * kD + 8 * sub;
+      const u16x8 uo = *reinterpret_cast<const u16x8*>(o + e);
+      const u16x8 ud = *reinterpret_cast<const u16x8*>(dO + e);
+      u16x8 ul = {};
+      if (o_lo) ul = *reinterpret_cast<const u16x8*>(o_lo + e);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float dv = bf2f(ud[k]);
+        acc += (bf2f(uo[k]) + bf2f(ul[k])) * dv;
+        m = fmaxf(m, fabsf(dv));
+      }
+    }
+#pragma unroll
+    for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    if (sub == 0)
+      ldout[(page * Hq + h) * 64 + r] = valid ? make_float2(-lse[row * Hq + h] * inv_scale, -acc) : make_float2(0.f, 0.f);
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(dmax, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+}
+
 
 __device__ __forceinline__ f32x16 mfma(const f16x8& a, const f16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -1116,13 +1215,30 @@ void launch_rowdot(const LaunchShape& s, const T* o, const T* o_lo, const T* dO,
                                                                        s.pages, s.Hq, s.D, 1.f / s.scale);
 }
 
-template <typename T>
-void launch_maxabs(const LaunchShape& s, const T* x, int H, const int32_t* page_nrows, uint32_t* out,
-                   hipStream_t st) {
-  zero_u32_kernel<<<1, 1, 0, st>>>(out);
-  const int64_t rows = s.pages * 64;
-  const unsigned grid = (unsigned)(rows < 4096 ? (rows > 0 ? rows : 1) : 4096);
-  maxabs_kernel<T><<<grid, 256, 0, st>>>(x, page_nrows, s.pages, (int64_t)H * s.D, out);
+void launch_prep16(const LaunchShape& s, const bf16_t* x, const float2* cs, const int32_t* page_nrows,
+                   const uint32_t* smax, f16_t* out_n, f16_t* out_t, float2* ld_fix, int H, hipStream_t st) {
+  const unsigned grid = (unsigned)s.pages;
+  if (cs) {
+    if (out_n && out_t)
+      prep16_kernel<true, true, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, ld_fix, H);
+    else
+      prep16_kernel<true, true, false><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, ld_fix, H);
+  } else if (out_n && out_t) {
+    prep16_kernel<false, true, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, ld_fix, H);
+  } else if (out_t) {
+    prep16_kernel<false, false, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, ld_fix, H);
+  } else {
+    prep16_kernel<false, true, false><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, ld_fix, H);
+  }
+}
+
+void launch_rowdot16(const LaunchShape& s, const bf16_t* o, const bf16_t* o_lo, const bf16_t* dO, const float* lse,
+                     const int32_t* page_nrows, float2* ld, uint32_t* dmax, hipStream_t st) {
+  zero_u32_kernel<<<1, 1, 0, st>>>(dmax);
+  const int64_t items = s.pages * 64 * s.Hq;
+  const int64_t blocks = (items + 15) / 16;
+  rowdot16_kernel<<<(unsigned)(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192), 256, 0, st>>>(
+      o, o_lo, dO, lse, page_nrows, ld, dmax, s.pages, s.Hq, 1.f / s.scale);
 }
 
 template void launch_relayout<bf16_t, f16_t>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, const uint32_t*, f16_t*, f16_t*, int, hipStream_t);
@@ -1130,7 +1246,6 @@ template void launch_relayout<bf16_t, float>(const LaunchShape&, const bf16_t*, 
 template void launch_relayout<float, float>(const LaunchShape&, const float*, const float2*, const int32_t*, const uint32_t*, float*, float*, int, hipStream_t);
 template void launch_rowdot<bf16_t>(const LaunchShape&, const bf16_t*, const bf16_t*, const bf16_t*, const float*, const int32_t*, const uint32_t*, float2*, hipStream_t);
 template void launch_rowdot<float>(const LaunchShape&, const float*, const float*, const float*, const float*, const int32_t*, const uint32_t*, float2*, hipStream_t);
-template void launch_maxabs<bf16_t>(const LaunchShape&, const bf16_t*, int, const int32_t*, uint32_t*, hipStream_t);
 
 // Grid for map_item: whole runs of kRun units per head, padded to a multiple of 8 runs.
 static unsigned run_grid(int64_t n_units, int H) {

@@ -24,9 +24,14 @@ void launch_relayout(const LaunchShape& s, const Tin* x, const float2* cs, const
 template <typename T>
 void launch_rowdot(const LaunchShape& s, const T* o, const T* o_lo, const T* dO, const float* lse,
                    const int32_t* page_nrows, const uint32_t* dmax, float2* ld, hipStream_t st);
-template <typename T>
-void launch_maxabs(const LaunchShape& s, const T* x, int H, const int32_t* page_nrows, uint32_t* out,
-                   hipStream_t st);
+// MFMA-path prologue (D = 128, bf16 in): rotate / scale / relayout one tensor into its fp16
+// page-major copy (out_n) and/or transposed copy (out_t); ld_fix, if given, has its -D
+// offsets multiplied by the same scale.
+void launch_prep16(const LaunchShape& s, const bf16_t* x, const float2* cs, const int32_t* page_nrows,
+                   const uint32_t* smax, f16_t* out_n, f16_t* out_t, float2* ld_fix, int H, hipStream_t st);
+// ld = (-lse / scale, -rowsum(dO (o + o_lo))) per (page, head, row) and dmax = max |dO|.
+void launch_rowdot16(const LaunchShape& s, const bf16_t* o, const bf16_t* o_lo, const bf16_t* dO, const float* lse,
+                     const int32_t* page_nrows, float2* ld, uint32_t* dmax, hipStream_t st);
 void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vt,
                      const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
                      bf16_t* o_lo, hipStream_t st);
