@@ -13,7 +13,8 @@ Printed JSON (one line on stdout; progress goes to stderr):
               backward 5)
   roofline    the dominant kernel's counted FLOPs per launch over its mean launch
               time (HIP events on the launch stream), against the 2.5 PFLOP/s
-              dense bf16 MFMA peak
+              dense bf16 MFMA peak; frac_of_gemm = the same over torch.matmul's
+              fp16 rate on random data measured in the same run (gemm_reference)
   x_vs_flat   the same kernels on the flat per-trajectory expansion (each
               trajectory one causal chain, mounted spans copied in), timed in the
               same process, divided by the packed time
@@ -205,6 +206,33 @@ def cpu_baseline(spec, plan, budget_s=15.0):
                       f"float32 NumPy, {t:.1f} s"}
 
 
+def gemm_reference(dev, n=16384, reps=20):
+    """torch.matmul (the vendor GEMM) on random N(0,1) operands, n^3 products: TFLOP/s per dtype.
+
+    Context for the roofline: on this GPU a dense product of random data is held well below
+    the 2.5 PFLOP/s nominal peak by the board's power limit, and this is what the library's
+    own MFMA kernels are compared with in "frac_of_gemm"."""
+    import torch
+    out = {}
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    for name, dt in (("fp16", torch.float16), ("bf16", torch.bfloat16)):
+        a = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(dt)
+        b = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(dt)
+        c = torch.empty((n, n), device=dev, dtype=dt)
+        for _ in range(3):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            torch.matmul(a, b, out=c)
+        torch.cuda.synchronize()
+        out[name] = round(2.0 * n ** 3 * reps / (time.perf_counter() - t0) / 1e12, 1)
+        del a, b, c
+    torch.cuda.empty_cache()
+    return out
+
+
 def traffic_record(kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, if it matches the source."""
     import hashlib
@@ -230,6 +258,7 @@ def main() -> int:
     ap.add_argument("--no-flat", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gdn", action="store_true")
+    ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB -> 1 GiB device copy kernel 3 times (scales HBM counters)")
     args = ap.parse_args()
@@ -305,6 +334,13 @@ def main() -> int:
 
     del tensors, ws
     torch.cuda.empty_cache()
+    if not args.no_gemm:
+        gemm = gemm_reference(dev)
+        roof["frac_of_gemm"] = round(achieved / gemm["fp16"], 4)
+        out["gemm_reference"] = {"torch_matmul_tflops": gemm, "shape": "16384 x 16384 x 16384, N(0,1) operands",
+                                 "note": "the vendor GEMM on random data in this run; the library's MFMA "
+                                         "kernels take fp16 operands, so frac_of_gemm compares with fp16"}
+        log(f"torch.matmul 16384^3: fp16 {gemm['fp16']} TFLOP/s, bf16 {gemm['bf16']} TFLOP/s")
     if not args.no_gdn:
         g = gdn_time(dpa, spec, dev, max(1, min(args.steps, 3)), 1)
         g["hybrid_step_ms"] = round(dt * 1e3 + 3 * g["fwd_bwd_ms_wall"], 2)
