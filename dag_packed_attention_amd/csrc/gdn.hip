@@ -173,22 +173,25 @@ struct ChunkIn {
 template <bool kDO>
 __device__ __forceinline__ void load_chunk(const ChunkIn& ci, int j0, const bf16_t* __restrict__ k,
                                            const bf16_t* __restrict__ q, const bf16_t* __restrict__ dO,
-                                           const float* __restrict__ beta, const float* __restrict__ alpha,
-                                           int H, int head, f16_t* Kr, f16_t* Qr, f16_t* dOr, int* rw, float* gs,
-                                           float* bs, float* al, int tid) {
+                                           const bf16_t* __restrict__ v, const float* __restrict__ beta,
+                                           const float* __restrict__ alpha, int H, int head, f16_t* Kr, f16_t* Qr,
+                                           f16_t* dOr, f16_t* Vr, int* rw, float* gs, float* bs, float* al,
+                                           int tid) {
   for (int i = tid; i < kB * 16; i += 256) {
     const int t = i >> 4, c8 = (i & 15) * 8;
     const int j = j0 + t;
-    f16x8 kk = {}, qq = {}, dd = {};
+    f16x8 kk = {}, qq = {}, dd = {}, vv = {};
     if (j < ci.n_tok) {
       const int64_t base = ((int64_t)ci.rows[j] * H + head) * kD + c8;
       kk = bf8_to_h8(*reinterpret_cast<const uint4*>(k + base));
       qq = bf8_to_h8(*reinterpret_cast<const uint4*>(q + base));
       if (kDO && j >= ci.n_replay) dd = bf8_to_h8(*reinterpret_cast<const uint4*>(dO + base));
+      if (Vr) vv = bf8_to_h8(*reinterpret_cast<const uint4*>(v + base));
     }
     *reinterpret_cast<f16x8*>(Kr + t * LDK + c8) = kk;
     *reinterpret_cast<f16x8*>(Qr + t * LDK + c8) = qq;
     if (kDO) *reinterpret_cast<f16x8*>(dOr + t * LDK + c8) = dd;
+    if (Vr) *reinterpret_cast<f16x8*>(Vr + t * LDK + c8) = vv;
   }
   if (tid < kB) {
     const int t = tid, j = j0 + t;
@@ -245,9 +248,8 @@ __device__ __forceinline__ void state_save(const f32x16 (&S)[4], f16_t* __restri
 // The next chunk's inputs, fetched into registers while the current chunk
 // computes (one work-group per CU leaves nothing else to hide their latency).
 struct ChunkRegs {
-  uint4 k4[4], q4[4];  // 16-byte pieces: rows (tid >> 4) + 16 m, columns 8 (tid & 15) ..
-  float v[2][16];      // V at this lane's accumulator positions of R
-  int row;             // tid < 64: the chunk's token tid (-1 past the end)
+  uint4 k4[4], q4[4], v4[4];  // 16-byte pieces: rows (tid >> 4) + 16 m, columns 8 (tid & 15) ..
+  int row;                    // tid < 64: the chunk's token tid (-1 past the end)
   float b, a;          //           and its beta, alpha
 };
 
@@ -268,38 +270,39 @@ __device__ __forceinline__ void fetch_rows(const ChunkIn& ci, int j0, const floa
   }
 }
 
-// K, Q rows and V values of that chunk, given its rows in LDS (rwn).
+// K, Q and V rows of that chunk, given its rows in LDS (rwn): whole 16-byte pieces of
+// each row, so one load instruction covers sixteen rows' 256 contiguous bytes.
 __device__ __forceinline__ void fetch_kqv(const int* rwn, const bf16_t* __restrict__ k, const bf16_t* __restrict__ q,
-                                          const bf16_t* __restrict__ v, int H, int head, int tid, int wave,
-                                          int hi, int l32, ChunkRegs& nx) {
+                                          const bf16_t* __restrict__ v, int H, int head, int tid, ChunkRegs& nx) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int row = rwn[(tid >> 4) + 16 * m];
-    nx.k4[m] = nx.q4[m] = make_uint4(0, 0, 0, 0);
+    nx.k4[m] = nx.q4[m] = nx.v4[m] = make_uint4(0, 0, 0, 0);
     if (row >= 0) {
       const int64_t base = ((int64_t)row * H + head) * kD + (tid & 15) * 8;
       nx.k4[m] = *reinterpret_cast<const uint4*>(k + base);
       nx.q4[m] = *reinterpret_cast<const uint4*>(q + base);
+      nx.v4[m] = *reinterpret_cast<const uint4*>(v + base);
     }
   }
-#pragma unroll
-  for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = rwn[32 * bm + acc_row(r, hi)];
-      nx.v[bm][r] = row >= 0 ? bf2f(v[((int64_t)row * H + head) * kD + 32 * wave + l32]) : 0.f;
-    }
 }
 
-// Make the fetched chunk current: K, Q rows (fp16) into LDS, row numbers, beta and the
+// Make the fetched chunk current: K, Q rows (fp16) into LDS, V rows (fp32, exact) into
+// the R tile that the next R computation overwrites in place, row numbers, beta and the
 // cumulative log decay.
-__device__ __forceinline__ void commit_chunk(const ChunkRegs& nx, f16_t* Kr, f16_t* Qr, int* rw, float* gs,
-                                             float* bs, int tid) {
+__device__ __forceinline__ void commit_chunk(const ChunkRegs& nx, f16_t* Kr, f16_t* Qr, float* Rr, int* rw,
+                                             float* gs, float* bs, int tid) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int t = (tid >> 4) + 16 * m, c8 = (tid & 15) * 8;
     *reinterpret_cast<f16x8*>(Kr + t * LDK + c8) = bf8_to_h8(nx.k4[m]);
     *reinterpret_cast<f16x8*>(Qr + t * LDK + c8) = bf8_to_h8(nx.q4[m]);
+    const uint32_t w[4] = {nx.v4[m].x, nx.v4[m].y, nx.v4[m].z, nx.v4[m].w};
+    float4* rv = reinterpret_cast<float4*>(Rr + t * LDR + c8);
+    rv[0] = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                        __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u));
+    rv[1] = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xffff0000u),
+                        __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xffff0000u));
   }
   if (tid < kB) {
     rw[tid] = nx.row;
@@ -396,7 +399,7 @@ __device__ __forceinline__ void solve_upper_t(const float* At, TX* x, int ldx, i
 // instead saves every chunk's starting state).  Both export boundary states.
 // ---------------------------------------------------------------------------------
 template <bool kStates>
-__global__ __launch_bounds__(256) void gdn_fwd_kernel(
+__global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
     const GSeq* __restrict__ seqs, const int32_t* __restrict__ order, const int32_t* __restrict__ grows,
     const GExport* __restrict__ exports, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ alpha,
@@ -435,16 +438,11 @@ __global__ __launch_bounds__(256) void gdn_fwd_kernel(
 
   // chunk 0 is fetched up front; chunk c + 1's inputs are fetched during chunk c
   ChunkRegs nx;
-  float vcur[2][16];
   fetch_rows(ci, 0, beta, alpha, H, head, tid, nx);
   if (tid < kB) rwn[tid] = nx.row;
   __syncthreads();
-  fetch_kqv(rwn, k, q, v, H, head, tid, wave, hi, l32, nx);
-  commit_chunk(nx, Kr, Qr, rw, gs, bs, tid);
-#pragma unroll
-  for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) vcur[bm][r] = nx.v[bm][r];
+  fetch_kqv(rwn, k, q, v, H, head, tid, nx);
+  commit_chunk(nx, Kr, Qr, Rr, rw, gs, bs, tid);
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
@@ -489,12 +487,12 @@ __global__ __launch_bounds__(256) void gdn_fwd_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = 32 * bm + acc_row(r, hi);
-          Rr[t * LDR + cc] = bs[t] * (vcur[bm][r] - __expf(gs[t]) * ks[bm][r]);
+          Rr[t * LDR + cc] = bs[t] * (Rr[t * LDR + cc] - __expf(gs[t]) * ks[bm][r]);  // V in, R out
         }
     }
     if (tid < kB) rwn[tid] = has_next ? nx.row : -1;
     __syncthreads();
-    if (has_next) fetch_kqv(rwn, k, q, v, H, head, tid, wave, hi, l32, nx);
+    if (has_next) fetch_kqv(rwn, k, q, v, H, head, tid, nx);
 
     // -- U = (I + A)^{-1} R  (only the state is live across the solve) ------------------
     if (tid < kD) solve_lower<float>(Ar, Rr, LDR, Ur, tid);
@@ -560,11 +558,7 @@ __global__ __launch_bounds__(256) void gdn_fwd_kernel(
     }
     __syncthreads();
     if (has_next) {
-      commit_chunk(nx, Kr, Qr, rw, gs, bs, tid);
-#pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) vcur[bm][r] = nx.v[bm][r];
+      commit_chunk(nx, Kr, Qr, Rr, rw, gs, bs, tid);
       state_to_lds(S, Sh, wave, lane);
       if (kStates) state_save(S, states + ((int64_t)(sq.chunk_off + c + 1) * H + head) * 2 * kD * kD, wave, lane);
       __syncthreads();
@@ -576,7 +570,7 @@ __global__ __launch_bounds__(256) void gdn_fwd_kernel(
 // Backward: one round, sequences in any order; chunks in reverse.
 // ---------------------------------------------------------------------------------
 template <typename TG>
-__global__ __launch_bounds__(256) void gdn_bwd_kernel(
+__global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
     const GSeq* __restrict__ seqs, const int32_t* __restrict__ order, const int32_t* __restrict__ grows,
     const GExport* __restrict__ exports, const int32_t* __restrict__ slot_off, const int32_t* __restrict__ slot_cons,
     const int32_t* __restrict__ rep_slot, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -624,7 +618,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_kernel(
       --ex;
     }
     state_to_lds(D, dSh, wave, lane);
-    load_chunk<true>(ci, j0, k, q, dO, beta, alpha, H, head, Kr, Qr, dOr, rw, gs, bs, al, tid);
+    load_chunk<true>(ci, j0, k, q, dO, v, beta, alpha, H, head, Kr, Qr, dOr, dRr, rw, gs, bs, al, tid);
     red_dg[wave][lane] = 0.f;
     red_g[wave][lane] = 0.f;
     red_b[wave][lane] = 0.f;
@@ -670,8 +664,7 @@ __global__ __launch_bounds__(256) void gdn_bwd_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = 32 * b2 + acc_row(r, hi);
-          const int row = rw[t];
-          const float vv = row >= 0 ? bf2f(v[((int64_t)row * H + head) * kD + cc]) : 0.f;
+          const float vv = (float)dRr[t * LDK + cc];  // V rows, staged by load_chunk
           Ur[t * LDK + cc] = (f16_t)(bs[t] * (vv - __expf(gs[t]) * ks[b2][r]));
         }
     }
