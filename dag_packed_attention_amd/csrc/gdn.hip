@@ -339,55 +339,74 @@ __device__ __forceinline__ void at_row16(const float* At, int row, int col0, flo
 // (I + A) X = R, right-looking: once x_i is final, every later row t takes
 // -A[t][i] x_i, and A[t][i] for t in a block is a contiguous run of row i of At.
 // X overwrites R in `x` (row stride ldx); the solved rows also go to `out` as
-// fp16 if given.
-template <typename TX>
-__device__ __forceinline__ void solve_lower(const float* At, TX* x, int ldx, f16_t* out, int c) {
+// fp16 if kOut.  The solved rows' contributions are taken four rows at a time
+// with all their LDS reads issued first, and row m + 1's coefficients are read
+// while row m is finished, so the loop waits on LDS once per group instead of
+// once per read.  The order of the additions is fixed (row by row, ascending).
+template <typename TX, bool kOut>
+__device__ __forceinline__ void solve_lower(const float* __restrict__ At, TX* __restrict__ x, int ldx,
+                                            f16_t* __restrict__ out, int c) {
   for (int b = 0; b < 4; ++b) {
-    float acc[16], a[16];
+    float acc[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = (float)x[(16 * b + j) * ldx + c];
-#pragma unroll 2
-    for (int i = 0; i < 16 * b; ++i) {
-      const float xi = (float)x[i * ldx + c];
-      at_row16(At, i, 16 * b, a);
+    for (int i = 0; i < 16 * b; i += 4) {
+      float xi[4], a[4][16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) acc[j] = fmaf(-a[j], xi, acc[j]);
+      for (int u = 0; u < 4; ++u) {
+        xi[u] = (float)x[(i + u) * ldx + c];
+        at_row16(At, i + u, 16 * b, a[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) acc[j] = fmaf(-a[u][j], xi[u], acc[j]);
     }
+    float a[2][16];
+    at_row16(At, 16 * b, 16 * b, a[0]);
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
-      at_row16(At, 16 * b + m, 16 * b, a);
+      if (m < 15) at_row16(At, 16 * b + m + 1, 16 * b, a[(m + 1) & 1]);
 #pragma unroll
-      for (int j = m + 1; j < 16; ++j) acc[j] = fmaf(-a[j], acc[m], acc[j]);
+      for (int j = m + 1; j < 16; ++j) acc[j] = fmaf(-a[m & 1][j], acc[m], acc[j]);
       x[(16 * b + m) * ldx + c] = (TX)acc[m];
-      if (out) out[(16 * b + m) * LDK + c] = (f16_t)acc[m];
+      if (kOut) out[(16 * b + m) * LDK + c] = (f16_t)acc[m];
     }
   }
 }
 
 // (I + A)^T Y = D, left-looking: y_t = d_t - sum_{i > t} A[i][t] y_i, a dot
 // product with a contiguous run of row t of At.  Y overwrites D in `x`;
-// `emit(t, y_t)` sees every solved value.
+// `emit(t, y_t)` sees every solved value.  Reads are grouped as in solve_lower;
+// the additions keep their fixed order.
 template <typename TX, typename Emit>
-__device__ __forceinline__ void solve_upper_t(const float* At, TX* x, int ldx, int c, Emit emit) {
+__device__ __forceinline__ void solve_upper_t(const float* __restrict__ At, TX* __restrict__ x, int ldx, int c,
+                                              Emit emit) {
   for (int b = 3; b >= 0; --b) {
-    float acc[16], a[16], y[16];
+    float acc[16], y[16];
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc[j] = (float)x[(16 * b + j) * ldx + c];
     for (int ib = b + 1; ib < 4; ++ib) {
 #pragma unroll
       for (int m = 0; m < 16; ++m) y[m] = (float)x[(16 * ib + m) * ldx + c];
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        at_row16(At, 16 * b + j, 16 * ib, a);
+      for (int j0 = 0; j0 < 16; j0 += 4) {
+        float a[4][16];
 #pragma unroll
-        for (int m = 0; m < 16; ++m) acc[j] = fmaf(-a[m], y[m], acc[j]);
+        for (int u = 0; u < 4; ++u) at_row16(At, 16 * b + j0 + u, 16 * ib, a[u]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+          for (int m = 0; m < 16; ++m) acc[j0 + u] = fmaf(-a[u][m], y[m], acc[j0 + u]);
       }
     }
+    float a[2][16];
+    at_row16(At, 16 * b + 15, 16 * b, a[1]);
 #pragma unroll
     for (int j = 15; j >= 0; --j) {
-      at_row16(At, 16 * b + j, 16 * b, a);
+      if (j > 0) at_row16(At, 16 * b + j - 1, 16 * b, a[(j - 1) & 1]);
 #pragma unroll
-      for (int m = j + 1; m < 16; ++m) acc[j] = fmaf(-a[m], acc[m], acc[j]);
+      for (int m = j + 1; m < 16; ++m) acc[j] = fmaf(-a[j & 1][m], acc[m], acc[j]);
       x[(16 * b + j) * ldx + c] = (TX)acc[j];
       emit(16 * b + j, acc[j]);
     }
@@ -495,7 +514,7 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
     if (has_next) fetch_kqv(rwn, k, q, v, H, head, tid, nx);
 
     // -- U = (I + A)^{-1} R  (only the state is live across the solve) ------------------
-    if (tid < kD) solve_lower<float>(Ar, Rr, LDR, Ur, tid);
+    if (tid < kD) solve_lower<float, true>(Ar, Rr, LDR, Ur, tid);
     __syncthreads();
 
     // -- outputs: O = scale diag(gamma) Q S0^T + (scale E o QK) U -------------------------
@@ -669,7 +688,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
         }
     }
     __syncthreads();
-    if (tid < kD) solve_lower<f16_t>(Ar, Ur, LDK, nullptr, tid);
+    if (tid < kD) solve_lower<f16_t, false>(Ar, Ur, LDK, nullptr, tid);
     __syncthreads();
 
     // -- dU = scale P^T dO + diag(E_63,.) K dS^T --------------------------------------------
