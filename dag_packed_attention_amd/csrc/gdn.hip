@@ -668,8 +668,8 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
       }
     }
     const int cc = 32 * wave + l32;
+    f32x16 ks[2];  // K S0^T: used for R here and for R's beta/gamma derivatives below
     {
-      f32x16 ks[2];
 #pragma unroll
       for (int b2 = 0; b2 < 2; ++b2) ks[b2] = zero16();
 #pragma unroll
@@ -739,11 +739,17 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
 
     // -- <dS, S0> for the decay of the whole chunk ------------------------------------------
     {
+      // S0 from its transposed copy: a lane's four consecutive rows are one 8-byte read
+      typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
       float s = 0.f;
 #pragma unroll
       for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s += D[nb][r] * (float)S0n[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f16x4 w = *reinterpret_cast<const f16x4*>(S0t + (32 * nb + l32) * kD + 32 * wave + 8 * r4 + 4 * hi);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) s += D[nb][4 * r4 + j] * (float)w[j];
+        }
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
       if (lane == 0) red_s[wave] = s;
@@ -787,15 +793,6 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
       if (hi == 0) red_dg[wave][i] -= cs;
     }
     // -- R's dependence on beta and gamma ------------------------------------------------------
-    f32x16 ks[2];
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) ks[b2] = zero16();
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const f16x8 b = frag_g(S0n, 32 * wave, 16 * s, lane);
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) ks[b2] = mfma(frag_n(Kr, LDK, 32 * b2, 16 * s, lane), b, ks[b2]);
-    }
 #pragma unroll
     for (int b2 = 0; b2 < 2; ++b2) {
       float xb[16], xg[16];
