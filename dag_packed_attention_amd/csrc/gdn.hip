@@ -607,7 +607,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
   __shared__ __attribute__((aligned(16))) float Ar[kB * LDA];   // A^T, then dKk (fp16 [64][LDP])
   __shared__ float gs[kB], bs[kB], al[kB];
   __shared__ int rw[kB];
-  __shared__ float red_dg[4][kB], red_g[4][kB], red_b[4][kB], red_e[4][kB], red_s[4];
+  __shared__ float red_dg[4][kB], red_g[4][kB], red_b[4][kB], red_e[4][kB], red_s[4], red_v[kB];
 
   const int head = blockIdx.x % H;
   const GSeq sq = seqs[order[blockIdx.x / H]];
@@ -737,6 +737,18 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
     }
     __syncthreads();
 
+    // V rows for sum_c dR[t][c] V[t][c] (beta's derivative through R): thread (t, part)
+    // takes row t's columns 32 part .. 32 part + 31 as four 16-byte pieces, read here and
+    // used after the products below
+    uint4 vrow[4];
+    {
+      const int t = tid >> 2, part = tid & 3;
+      const int row = rw[t];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+        vrow[m] = row >= 0 ? *reinterpret_cast<const uint4*>(v + ((int64_t)row * H + head) * kD + 32 * part + 8 * m)
+                           : make_uint4(0, 0, 0, 0);
+    }
     // -- <dS, S0> for the decay of the whole chunk ------------------------------------------
     {
       // S0 from its transposed copy: a lane's four consecutive rows are one 8-byte read
@@ -799,10 +811,8 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 32 * b2 + acc_row(r, hi);
-        const int row = rw[t];
-        const float vv = row >= 0 ? bf2f(v[((int64_t)row * H + head) * kD + cc]) : 0.f;
         const float dr = (float)dRr[t * LDK + cc];
-        xb[r] = dr * (vv - __expf(gs[t]) * ks[b2][r]);
+        xb[r] = -dr * __expf(gs[t]) * ks[b2][r];  // the dR V part is red_v
         xg[r] = -bs[t] * dr * ks[b2][r];
       }
       const float sb = rowsum16(xb, lane);
@@ -812,6 +822,23 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
         red_b[wave][t] += sb;
         red_g[wave][t] += sg;
       }
+    }
+    {
+      const int t = tid >> 2, part = tid & 3;
+      float acc = 0.f;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const f16x8 d8 = *reinterpret_cast<const f16x8*>(dRr + t * LDK + 32 * part + 8 * m);
+        const uint32_t w[4] = {vrow[m].x, vrow[m].y, vrow[m].z, vrow[m].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc = fmaf((float)d8[2 * e], __uint_as_float(w[e] << 16), acc);
+          acc = fmaf((float)d8[2 * e + 1], __uint_as_float(w[e] & 0xffff0000u), acc);
+        }
+      }
+      acc += __shfl_xor(acc, 1);
+      acc += __shfl_xor(acc, 2);
+      if (part == 0) red_v[t] = acc;
     }
     // -- dS_prev = gamma_63 dS + scale (diag(gamma) dO)^T Q - (diag(beta gamma) dR)^T K -----------
     {
@@ -953,6 +980,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
         db += red_b[w][t];
         e_t += red_e[w][t];
       }
+      db += red_v[t];
       float dg = dgp + __expf(gs[t]) * dgam - e_t * en;
       float tot = e_t * en;  // sum over the chunk of dEn_i E_63,i goes to g_63
 #pragma unroll
