@@ -606,7 +606,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
   __shared__ __attribute__((aligned(16))) f16_t Pr[kB * LDP];   // scale E o QK, then dP~
   __shared__ __attribute__((aligned(16))) float Ar[kB * LDA];   // A^T, then dKk (fp16 [64][LDP])
   __shared__ float gs[kB], bs[kB], al[kB];
-  __shared__ int rw[kB];
+  __shared__ int rw[kB], rsl_s[kB];
   __shared__ float red_dg[4][kB], red_g[4][kB], red_b[4][kB], red_e[4][kB], red_s[4], red_v[kB];
 
   const int head = blockIdx.x % H;
@@ -638,6 +638,10 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
     }
     state_to_lds(D, dSh, wave, lane);
     load_chunk<true>(ci, j0, k, q, dO, v, beta, alpha, H, head, Kr, Qr, dOr, dRr, rw, gs, bs, al, tid);
+    if (tid < kB) {  // side-buffer slot of each row with replays (looked up once, not per element)
+      const int row = rw[tid];
+      rsl_s[tid] = row >= 0 ? rep_slot[row] : -1;
+    }
     red_dg[wave][lane] = 0.f;
     red_g[wave][lane] = 0.f;
     red_b[wave][lane] = 0.f;
@@ -729,7 +733,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
         if (j < sq.n_replay) {
           rbuf[((int64_t)(sq.rep_off + j) * H + head) * kRep + kD + col] = g;
         } else {
-          const int rs = rep_slot[rw[t]];
+          const int rs = rsl_s[t];
           if (rs >= 0) rside[((int64_t)rs * H + head) * 2 * kD + kD + col] = g;
           else st_g<TG>(dv + ((int64_t)rw[t] * H + head) * kD + col, g);
         }
@@ -960,7 +964,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
           if (j < sq.n_replay) {
             rbuf[((int64_t)(sq.rep_off + j) * H + head) * kRep + cc] = ak[b2][r];
           } else {
-            const int rsl = rep_slot[rw[t]];
+            const int rsl = rsl_s[t];
             if (rsl >= 0) rside[((int64_t)rsl * H + head) * 2 * kD + cc] = ak[b2][r];
             else st_g<TG>(dk + ((int64_t)rw[t] * H + head) * kD + cc, ak[b2][r]);
           }
