@@ -28,9 +28,11 @@ struct DeviceTables {
   int32_t* fwd_order = nullptr;
   KEntry* kentries = nullptr;
   int32_t* kv_off = nullptr;
-  int64_t* kstep_off = nullptr;
-  KStep* ksteps = nullptr;
   int32_t* bwd_order = nullptr;
+  int32_t* kpairs = nullptr;
+  int64_t* kpair_off = nullptr;
+  KStep* kpsteps = nullptr;
+  int32_t* pair_order = nullptr;
   int32_t* page_table = nullptr;
   int32_t* page_nrows = nullptr;
   // linear-attention schedule
@@ -186,8 +188,9 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
   bytes += align256(P.pos_of_row.size() * 4) + align256(P.tiles.size() * sizeof(Tile)) +
            align256(P.qpages.size() * sizeof(QPage)) + align256(P.fwd_order.size() * 4) +
            align256(P.kentries.size() * sizeof(KEntry)) + align256(P.kv_off.size() * 4) +
-           align256(P.kstep_off.size() * 8) + align256(P.ksteps.size() * sizeof(KStep)) +
-           align256(P.bwd_order.size() * 4) + align256(P.page_table.size() * 4) +
+           align256(P.bwd_order.size() * 4) + align256(P.kpairs.size() * 4) + align256(P.kpair_off.size() * 8) +
+           align256(P.kpsteps.size() * sizeof(KStep)) + align256(P.pair_order.size() * 4) +
+           align256(P.page_table.size() * 4) +
            align256(P.page_nrows.size() * 4) + align256(P.gseqs.size() * sizeof(GSeq)) +
            align256(P.grows.size() * 4) + align256(P.gexports.size() * sizeof(GExport)) +
            align256(P.gslot_off.size() * 4) + align256(P.gslot_cons.size() * 4) + align256(P.ground_seq.size() * 4) +
@@ -209,9 +212,11 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
   D->fwd_order = dev_take<int32_t>(b, off, P.fwd_order.size());
   D->kentries = dev_take<KEntry>(b, off, P.kentries.size());
   D->kv_off = dev_take<int32_t>(b, off, P.kv_off.size());
-  D->kstep_off = dev_take<int64_t>(b, off, P.kstep_off.size());
-  D->ksteps = dev_take<KStep>(b, off, P.ksteps.size());
   D->bwd_order = dev_take<int32_t>(b, off, P.bwd_order.size());
+  D->kpairs = dev_take<int32_t>(b, off, P.kpairs.size());
+  D->kpair_off = dev_take<int64_t>(b, off, P.kpair_off.size());
+  D->kpsteps = dev_take<KStep>(b, off, P.kpsteps.size());
+  D->pair_order = dev_take<int32_t>(b, off, P.pair_order.size());
   D->page_table = dev_take<int32_t>(b, off, P.page_table.size());
   D->page_nrows = dev_take<int32_t>(b, off, P.page_nrows.size());
   D->gseqs = dev_take<GSeq>(b, off, P.gseqs.size());
@@ -233,9 +238,11 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
             put(D->fwd_order, P.fwd_order.data(), P.fwd_order.size() * 4) &&
             put(D->kentries, P.kentries.data(), P.kentries.size() * sizeof(KEntry)) &&
             put(D->kv_off, P.kv_off.data(), P.kv_off.size() * 4) &&
-            put(D->kstep_off, P.kstep_off.data(), P.kstep_off.size() * 8) &&
-            put(D->ksteps, P.ksteps.data(), P.ksteps.size() * sizeof(KStep)) &&
             put(D->bwd_order, P.bwd_order.data(), P.bwd_order.size() * 4) &&
+            put(D->kpairs, P.kpairs.data(), P.kpairs.size() * 4) &&
+            put(D->kpair_off, P.kpair_off.data(), P.kpair_off.size() * 8) &&
+            put(D->kpsteps, P.kpsteps.data(), P.kpsteps.size() * sizeof(KStep)) &&
+            put(D->pair_order, P.pair_order.data(), P.pair_order.size() * 4) &&
             put(D->page_table, P.page_table.data(), P.page_table.size() * 4) &&
             put(D->page_nrows, P.page_nrows.data(), P.page_nrows.size() * 4) &&
             put(D->gseqs, P.gseqs.data(), P.gseqs.size() * sizeof(GSeq)) &&
@@ -572,9 +579,9 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       using TG = std::remove_pointer_t<decltype(tag)>;
       {
         Span sp(P, DAG_K_DKDV, stream);
-        launch_dkdv_mfma<TG>(s, n_kvp, (const f16_t*)w.qn, (const f16_t*)w.kn, (const f16_t*)w.vn,
-                             (const f16_t*)w.dOn, w.ld, w.cs, w.dmax, D.bwd_order, D.kstep_off, D.ksteps,
-                             D.page_nrows, (TG*)dk, (TG*)dv, stream);
+        launch_dkdv_mfma<TG>(s, (int64_t)P.pair_order.size(), (const f16_t*)w.qn, (const f16_t*)w.kn,
+                             (const f16_t*)w.vn, (const f16_t*)w.dOn, w.ld, w.cs, w.dmax, D.pair_order, D.kpairs,
+                             D.kpair_off, D.kpsteps, D.page_nrows, (TG*)dk, (TG*)dv, stream);
       }
       {
         Span sp(P, DAG_K_DQ, stream);

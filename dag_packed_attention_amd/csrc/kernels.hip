@@ -741,31 +741,36 @@ __device__ __forceinline__ f16x8 frag_tr(const f16_t* tb, int kk, int dblk) {
   return out;
 }
 
-// Sum one accumulator set (dK or dV) over the four query heads through LDS, in
-// head order, then scale, rotate dK back by R(pos)^T and write the page's 64
-// rows once.  Wave (head hh, key block kb) holds keys 32 kb .. 32 kb + 31.
+// Sum the two head-parity waves' dK (or dV) accumulators of every 32-key tile
+// through LDS (parity 0 first, then 1: a fixed order), then scale, rotate dK back
+// by R(pos)^T and write the pair's rows once.  Wave (kt, j) holds keys
+// 32 kt .. 32 kt + 31 of the pair's 128 (page A: kt = 0, 1; page B: kt = 2, 3).
 template <bool kRotate, typename TG>
-__device__ __forceinline__ void dkdv_reduce_store(const f32x16 (&acc)[4], float* red, int hh, int kb, int hi,
-                                                  int l32, int tid, int page, int g, int krows, int Hkv,
-                                                  float mul, const float2* __restrict__ cs, TG* __restrict__ out) {
-  for (int w = 0; w < 4; ++w) {
+__device__ __forceinline__ void dkdv_reduce_store(const f32x16 (&acc)[4], float* red, int kt, int j, bool active,
+                                                  int hi, int l32, int tid, int physA, int physB, int rowsA,
+                                                  int rowsB, int g, int Hkv, float mul,
+                                                  const float2* __restrict__ cs, TG* __restrict__ out) {
+  for (int jj = 0; jj < 2; ++jj) {
     __syncthreads();
-    if (hh == w) {
+    if (j == jj && active) {
 #pragma unroll
       for (int b = 0; b < 4; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float* slot = red + (kb * 32 + acc_row(r, hi)) * (kD + 1) + b * 32 + l32;
-          *slot = (w == 0) ? acc[b][r] : *slot + acc[b][r];
+          float* slot = red + (kt * 32 + acc_row(r, hi)) * (kD + 1) + b * 32 + l32;
+          *slot = (jj == 0) ? acc[b][r] : *slot + acc[b][r];
         }
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < 64 * 64; idx += 512) {
-    const int k2 = idx / 64, i = idx % 64;
-    const int64_t grow = (int64_t)page * 64 + k2;
+  for (int idx = tid; idx < 128 * 64; idx += 512) {
+    const int k2 = idx / 64, i = idx % 64;  // key of the pair, column pair (i, i + 64)
+    const int side = k2 >> 6, row = k2 & 63;
+    const int page = side ? physB : physA;
+    if (page < 0) continue;
+    const int64_t grow = (int64_t)page * 64 + row;
     float a = red[k2 * (kD + 1) + i] * mul, b = red[k2 * (kD + 1) + i + 64] * mul;
-    if (k2 >= krows) {
+    if (row >= (side ? rowsB : rowsA)) {
       a = b = 0.f;
     } else if (kRotate && cs) {
       const float2 c = cs[grow * (kD / 2) + i];
@@ -779,242 +784,260 @@ __device__ __forceinline__ void dkdv_reduce_store(const f32x16 (&acc)[4], float*
   }
 }
 
-// dK, dV for one KV page x one KV head.  Eight waves: wave (hh, kb) serves
-// query head 4 g + hh and keys 32 kb .. 32 kb + 31 of the page, keeping its dK
-// and dV (32 x 128 each) in accumulation registers across the page's whole
-// reader list, with its K fragments in registers too; two waves per SIMD hide
-// each other's LDS and barrier waits.  The reader list is walked in steps of 32
-// query rows: each step stages the four heads' Q and dO rows (and their
-// (lse, D) pairs) in LDS with direct global loads, double buffered; S and dP
-// read row fragments from those tiles, dV and dK read column fragments of the
-// same tiles with the transpose read.  At the end the four heads are summed
-// through LDS in head order and written once: deterministic, no atomics.
+// dK, dV for a pair of KV pages (pages 2 i and 2 i + 1 of one node, or a lone last
+// page) and one KV head.  Each 32-row reader step of the pair's merged reader list
+// is taken as two half-steps, query heads 4 g + 2 hp + {0, 1} (hp = 0, 1).  Eight
+// waves: wave (kt, j) serves keys 32 (kt % 2) .. of page kt / 2 and the query heads
+// 4 g + j and 4 g + 2 + j, keeping its dK and dV (32 x 128 each) in accumulation
+// registers and its K fragments in registers; the two waves of a SIMD share the
+// key tile.  A half-step stages two heads' Q and dO rows (32 KiB) in LDS with
+// direct loads, double buffered: every staged byte now feeds 128 keys, so a pair
+// moves half the staging bytes per product that one page would.  Within a
+// half-step the products run as four MFMA chains S, dP, dV, dK (exponentials
+// between the dP products, dS between the dV products); hidden keys get a
+// per-lane -inf offset.  At the end the two head parities are summed through LDS in
+// a fixed order and each page is written once: deterministic, no atomics.
 template <typename TG>
 __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vn,
     const f16_t* __restrict__ dOn, const float2* __restrict__ ldd, const float2* __restrict__ cs,
-    const uint32_t* __restrict__ dmax, const int32_t* __restrict__ order, const int64_t* __restrict__ kstep_off,
-    const KStep* __restrict__ ksteps, const int32_t* __restrict__ page_nrows, TG* __restrict__ dk, TG* __restrict__ dv, int n_kvp, int Hq, int Hkv,
-    float sl2, float scale) {
-  // [buffer][head][Q, dO][32 x 128] f16, then [buffer][head] the 32 rows'
-  // accumulator offsets, -lse / scale for S and then -D for dP; the first 33 KiB
-  // are reused for the head reduction at the end.  The page's V tile sits in its
-  // own [64][128] block.
-  __shared__ __attribute__((aligned(1024))) f16_t qd[2][4][2][kStepB];
-  __shared__ __attribute__((aligned(1024))) f16_t lvp[kPageB];
-  __shared__ __attribute__((aligned(16))) float lds_ld[2][4][64];
+    const uint32_t* __restrict__ dmax, const int32_t* __restrict__ pair_order, const int32_t* __restrict__ pairs,
+    const int64_t* __restrict__ pair_off, const KStep* __restrict__ psteps, const int32_t* __restrict__ page_nrows,
+    TG* __restrict__ dk, TG* __restrict__ dv, int n_pairs, int Hq, int Hkv, float sl2, float scale) {
+  // [buffer][head of the half-step][Q, dO][32 x 128] f16 (the first 65 KiB are reused
+  // for the head-parity sum at the end), the V tiles of pages A and B, and
+  // [buffer][head] the 32 rows' offsets: -lse / scale for S, then -D for dP
+  __shared__ __attribute__((aligned(1024))) f16_t qd[2][2][2][kStepB];
+  __shared__ __attribute__((aligned(1024))) f16_t lvp[2][kPageB];
+  __shared__ __attribute__((aligned(16))) float lds_ld[2][2][64];
   int unit, g;
-  if (!map_item(n_kvp, Hkv, unit, g)) return;
-  const int page = order[unit];
+  if (!map_item(n_pairs, Hkv, unit, g)) return;
+  const int pr = pair_order[unit];
+  const int physA = pairs[2 * pr], physB = pairs[2 * pr + 1];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
   const int l32 = lane & 31, hi = lane >> 5;
-  const int hh = wave & 3, kb = wave >> 2;
-  const int krows = page_nrows[page];
+  const int kt = wave & 3, j = wave >> 2;  // key tile of the pair, head parity
+  const int side = kt >> 1, kb = kt & 1;
+  const int page = side ? physB : physA;
+  const bool active = page >= 0;  // page B of a lone page: this wave only stages
 
-  // this wave's K fragments (B operand of S = Q K^T) live in registers; the page's
-  // V tile (B operand of dP = dO V^T) in LDS
   f16x8 kf[8];
   {
-    const int64_t base = ((int64_t)page * Hkv + g) * 64 * kD;
+    const int64_t base = ((int64_t)(active ? page : physA) * Hkv + g) * 64 * kD;
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) kf[ks] = ld8(kn + base + (kb * 32 + l32) * kD + ks * 16 + hi * 8);
-    if (wave < 4) stage_bricks<4>(lvp, tile_rsrc(vn + base, kTile * 2), 4 * wave, brick_lane_off(lane));
+    // wave w stages bricks 4 (w % 4) .. of page w / 4's V tile
+    const int vp = (wave >> 2) ? physB : physA;
+    if (vp >= 0)
+      stage_bricks<4>(lvp[wave >> 2], tile_rsrc(vn + ((int64_t)vp * Hkv + g) * kTile, kTile * 2), 4 * (wave & 3),
+                      brick_lane_off(lane));
   }
   f32x16 adk[4], adv[4];  // [d block]
 #pragma unroll
   for (int b = 0; b < 4; ++b) adk[b] = adv[b] = zero16();
 
-  // The page's reader steps.  Descriptors are uniform and come through the scalar
-  // cache three steps ahead of the step they describe, so no step waits on one and
-  // no vector-memory wait is needed for them (that would also wait for the staging
-  // loads in flight).
-  const int64_t s_begin = kstep_off[page];
-  const int n_steps = (int)(kstep_off[page + 1] - s_begin);
-  const KStep* kst = ksteps + s_begin;
+  // Step descriptors are uniform and come through the scalar cache ahead of their
+  // use (no vector-memory wait for them, which would also wait for the staging loads).
+  const int64_t s_begin = pair_off[pr];
+  const int n_steps = (int)(pair_off[pr + 1] - s_begin);
+  const int n_units = 2 * n_steps;
+  const KStep* kst = psteps + s_begin;
   KStep cur = kst[0];
   KStep nxt = kst[min(1, n_steps - 1)];
   KStep n2 = kst[min(2, n_steps - 1)];
+  // staging role: head sj of the half-step, tensor ts (0: Q, 1: dO), bricks sb0 .. sb0 + 3
+  const int sj = wave & 1, ts = (wave >> 1) & 1, sb0 = 4 * (wave >> 2);
   const uint32_t rlo = brick_lane_off(lane);
   const uint32_t llo = (uint32_t)((2 * (lane & 31) + (lane >> 5)) * 4);
-  auto stage = [&](int buf, int qp_, int rb_) {
-    // wave (hh, kb) fetches head 4 g + hh's Q rows (kb = 0) or dO rows (kb = 1): 8 KiB
-    const int64_t src = (((int64_t)qp_ * Hq + g * 4 + hh) * 64 + rb_ * 32) * kD;
-    stage_bricks<8>(qd[buf][hh][kb], tile_rsrc((kb == 0 ? qn : dOn) + src, 32 * kD * 2), 0, rlo);
-    if (kb == 0) {
-      // lane i < 32 takes row i's S offset, lane 32 + i its dP offset (4 bytes each,
-      // landing at slot i of the 64-float block)
-      dma4(&lds_ld[buf][hh][0], llo, tile_rsrc(ldd + ((int64_t)qp_ * Hq + g * 4 + hh) * 64 + rb_ * 32, 256), 0);
-    }
+  const f16_t* stsrc = ts == 0 ? qn : dOn;
+  auto head_row0 = [&](const KStep& d, int hp, int jj) -> int64_t {  // first staged row of head jj
+    return ((int64_t)d.qph * Hq + g * 4 + 2 * hp + jj) * 64 + (d.info & 1) * 32;
   };
-  stage(0, cur.qph, cur.info & 1);
+  {
+    const int64_t r0 = head_row0(cur, 0, sj);
+    stage_bricks<4>(qd[0][sj][ts], tile_rsrc(stsrc + r0 * kD, 32 * kD * 2), sb0, rlo);
+    if (ts == 0 && sb0 == 0) dma4(&lds_ld[0][sj][0], llo, tile_rsrc(ldd + r0, 256), 0);
+  }
   wait_all_loads();
   __syncthreads();
 
-  int buf = 0;
   const int key = kb * 32 + l32;
   const int qb = frag_base(l32, hi), vb = frag_base(key, hi), tb = tr_base(lane);
-  for (int it = 0; it < n_steps; ++it) {
-    // Step it + 1's staging goes out one instruction per k-step of the S/dP
-    // products below: issued all at once, the eight waves' loads fill the memory
-    // pipeline's queue and every wave stalls at issue until it drains.  On the last
-    // step nxt repeats the current step (harmless: buf ^ 1 is not read again).
-    const int64_t nsrc = (((int64_t)nxt.qph * Hq + g * 4 + hh) * 64 + (nxt.info & 1) * 32) * kD;
-    const i32x4 nrs = tile_rsrc((kb == 0 ? qn : dOn) + nsrc, 32 * kD * 2);
-    f16_t* ndst = qd[buf ^ 1][hh][kb];
+  for (int u = 0; u < n_units; ++u) {
+    const int buf = u & 1, hp = u & 1;
+    // staging of unit u + 1 (the same step's second half, or the next step's first);
+    // on the last unit it repeats this one into the idle buffer (harmless)
+    const KStep& sd = hp ? nxt : cur;
+    const int64_t nr0 = head_row0(sd, hp ^ 1, sj);
+    const i32x4 nrs = tile_rsrc(stsrc + nr0 * kD, 32 * kD * 2);
+    f16_t* ndst = qd[buf ^ 1][sj][ts];
+    const bool offs = ts == 0 && sb0 == 0;
 
-    const int rb = cur.info & 1, lo = (cur.info >> 1) & 0x7f, hi_t = (cur.info >> 8) & 0x7f;
-    const bool diag = (cur.info >> 15) & 1;
-    const f16_t* Qt = qd[buf][hh][0];
-    const f16_t* Dt = qd[buf][hh][1];
-    // S = Q K^T - lse / scale, dP = dO V^T - D: 32 rows (M) x this wave's 32 keys (N);
-    // lane holds key kb*32 + l32 and rows rb*32 + acc_row(r, hi), so the offsets of
-    // its rows come as four runs of four consecutive floats straight into the
-    // accumulators
-    f32x16 s, dp;
-    {
-      const float* L = lds_ld[buf][hh];
+    const uint32_t inf = ((uint32_t)cur.info >> (16 * side)) & 0xffffu;
+    const int rb = cur.info & 1, lo = (inf >> 1) & 0x7f, hi_t = (inf >> 8) & 0x7f;
+    const bool diag = (inf >> 15) & 1;
+    if (!active || lo >= hi_t) {
+      // this wave's page is not read by this step: stage only
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float4 a = *reinterpret_cast<const float4*>(L + 8 * j + 4 * hi);
-        const float4 b = *reinterpret_cast<const float4*>(L + 32 + 8 * j + 4 * hi);
-        s[4 * j] = a.x, s[4 * j + 1] = a.y, s[4 * j + 2] = a.z, s[4 * j + 3] = a.w;
-        dp[4 * j] = b.x, dp[4 * j + 1] = b.y, dp[4 * j + 2] = b.z, dp[4 * j + 3] = b.w;
+      for (int i = 0; i < 4; ++i) dma16(ndst + (sb0 + i) * kBrick, rlo, nrs, (sb0 + i) * 4 * kD * 2);
+      if (offs) dma4(&lds_ld[buf ^ 1][sj][0], llo, tile_rsrc(ldd + nr0, 256), 0);
+    } else {
+      const f16_t* Qt = qd[buf][j][0];
+      const f16_t* Dt = qd[buf][j][1];
+      const f16_t* Vp = lvp[side];
+      // S = Q K^T - lse / scale, dP = dO V^T - D: 32 rows (M) x this wave's 32 keys (N);
+      // lane holds key kb*32 + l32 and rows rb*32 + acc_row(r, hi), so the offsets of
+      // its rows come as four runs of four consecutive floats straight into the
+      // accumulators
+      f32x16 s, dp;
+      {
+        const float* L = lds_ld[buf][j];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float4 a = *reinterpret_cast<const float4*>(L + 8 * q4 + 4 * hi);
+          const float4 b = *reinterpret_cast<const float4*>(L + 32 + 8 * q4 + 4 * hi);
+          s[4 * q4] = a.x, s[4 * q4 + 1] = a.y, s[4 * q4 + 2] = a.z, s[4 * q4 + 3] = a.w;
+          dp[4 * q4] = b.x, dp[4 * q4 + 1] = b.y, dp[4 * q4 + 2] = b.z, dp[4 * q4 + 3] = b.w;
+        }
       }
-    }
-    // The four products run as four chains of eight MFMAs, S, dP, dV, dK, and each
-    // chain carries the vector work of the previous one: the exponentials of S run
-    // between the dP products, dS = P (dP - D) between the dV products.  A key
-    // outside the step's visible range gets -inf added before the exponential.
-    const float koff = (key >= lo && key < hi_t) ? 0.f : -INFINITY;
-    {
-      // S: Q fragments read one k-step ahead; step it + 1's staging goes out one
-      // load per k-step
-      f16x8 qa[2];
-      qa[0] = ld8(Qt + qb);
+      // The four products run as four chains of eight MFMAs, S, dP, dV, dK, and each
+      // chain carries the vector work of the previous one: the exponentials of S run
+      // between the dP products, dS = P (dP - D) between the dV products.  A key
+      // outside the step's visible range gets -inf added before the exponential.
+      const float koff = (key >= lo && key < hi_t) ? 0.f : -INFINITY;
+      {
+        // S: Q fragments read one k-step ahead; the next unit's staging goes out one
+        // load per two k-steps
+        f16x8 qa[2];
+        qa[0] = ld8(Qt + qb);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        if (ks < 7) qa[(ks + 1) & 1] = ld8(Qt + qb + kstep(ks + 1));
-        s = mfma(qa[ks & 1], kf[ks], s);
-        dma16(ndst + ks * kBrick, rlo, nrs, ks * 4 * kD * 2);
-      }
-      // both waves of a head fetch the same offsets into the same place (same bytes)
-      dma4(&lds_ld[buf ^ 1][hh][0], llo,
-           tile_rsrc(ldd + ((int64_t)nxt.qph * Hq + g * 4 + hh) * 64 + (nxt.info & 1) * 32, 256), 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-#pragma unroll
-      for (int ks = 0; ks < 7; ++ks) {
+        for (int ks = 0; ks < 8; ++ks) {
+          if (ks < 7) qa[(ks + 1) & 1] = ld8(Qt + qb + kstep(ks + 1));
+          s = mfma(qa[ks & 1], kf[ks], s);
+          if ((ks & 1) == 0)
+            dma16(ndst + (sb0 + ks / 2) * kBrick, rlo, nrs, (sb0 + ks / 2) * 4 * kD * 2);
+        }
+        if (offs) dma4(&lds_ld[buf ^ 1][sj][0], llo, tile_rsrc(ldd + nr0, 256), 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+        for (int ks = 0; ks < 7; ++ks) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      // dP, with P = 2^(S scale log2 e) computed in between
-      f16x8 da[2], va[2];
-      da[0] = ld8(Dt + qb);
-      va[0] = ld8(lvp + vb);
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        // dP, with P = 2^(S scale log2 e) computed in between
+        f16x8 da[2], va[2];
+        da[0] = ld8(Dt + qb);
+        va[0] = ld8(Vp + vb);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        if (ks < 7) {
-          da[(ks + 1) & 1] = ld8(Dt + qb + kstep(ks + 1));
-          va[(ks + 1) & 1] = ld8(lvp + vb + kstep(ks + 1));
+        for (int ks = 0; ks < 8; ++ks) {
+          if (ks < 7) {
+            da[(ks + 1) & 1] = ld8(Dt + qb + kstep(ks + 1));
+            va[(ks + 1) & 1] = ld8(Vp + vb + kstep(ks + 1));
+          }
+          dp = mfma(da[ks & 1], va[ks & 1], dp);
         }
-        dp = mfma(da[ks & 1], va[ks & 1], dp);
-      }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, koff));
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, koff));
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        if (ks < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (diag) {
-      // the reader's own page: key <= row (a hidden score may have overflowed: select)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = key <= rb * 32 + acc_row(r, hi) ? s[r] : 0.f;
-    }
-    // Padding rows need no mask: their Q and dO rows and offsets are zero, so they add
-    // exact zeros to dV and dK.
-    const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8);
-    // dV += P^T dO, then dK += dS^T Q: keys (M) x d (N), the 32 rows contracted; d
-    // block b + 1's fragments (transpose reads) are read while block b's products run
-    const f16_t* Dtb = Dt + tb;
-    const f16_t* Qtb = Qt + tb;
-    f16x8 sf0, sf1;
-    f16x8 frq[2];
-    {
-      f16x8 fr[2][2];
-      fr[0][0] = frag_tr(Dtb, 0, 0);
-      fr[0][1] = frag_tr(Dtb, 1, 0);
-#pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b < 3) {
-          fr[(b + 1) & 1][0] = frag_tr(Dtb, 0, b + 1);
-          fr[(b + 1) & 1][1] = frag_tr(Dtb, 1, b + 1);
+        for (int ks = 0; ks < 8; ++ks) {
+          if (ks < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
-        adv[b] = mfma(pf0, fr[b & 1][0], adv[b]);
-        adv[b] = mfma(pf1, fr[b & 1][1], adv[b]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      if (diag) {
+        // the reader's own page: key <= row (a hidden score may have overflowed: select)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dp[r] *= s[r];
-      sf0 = pack8(dp, 0);
-      sf1 = pack8(dp, 8);
-      frq[0] = frag_tr(Qtb, 0, 0);
-      frq[1] = frag_tr(Qtb, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        for (int r = 0; r < 16; ++r) s[r] = key <= rb * 32 + acc_row(r, hi) ? s[r] : 0.f;
+      }
+      // Padding rows need no mask: their Q and dO rows and offsets are zero, so they add
+      // exact zeros to dV and dK.
+      const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8);
+      // dV += P^T dO, then dK += dS^T Q: keys (M) x d (N), the 32 rows contracted; d
+      // block b + 1's fragments (transpose reads) are read while block b's products run
+      const f16_t* Dtb = Dt + tb;
+      const f16_t* Qtb = Qt + tb;
+      f16x8 sf0, sf1;
+      f16x8 frq[2];
+      {
+        f16x8 fr[2][2];
+        fr[0][0] = frag_tr(Dtb, 0, 0);
+        fr[0][1] = frag_tr(Dtb, 1, 0);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < 4; ++b) {
+          if (b < 3) {
+            fr[(b + 1) & 1][0] = frag_tr(Dtb, 0, b + 1);
+            fr[(b + 1) & 1][1] = frag_tr(Dtb, 1, b + 1);
+          }
+          adv[b] = mfma(pf0, fr[b & 1][0], adv[b]);
+          adv[b] = mfma(pf1, fr[b & 1][1], adv[b]);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] *= s[r];
+        sf0 = pack8(dp, 0);
+        sf1 = pack8(dp, 8);
+        frq[0] = frag_tr(Qtb, 0, 0);
+        frq[1] = frag_tr(Qtb, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    {
-      f16x8 fr[2][2];
-      fr[0][0] = frq[0];
-      fr[0][1] = frq[1];
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        if (b < 3) {
-          fr[(b + 1) & 1][0] = frag_tr(Qtb, 0, b + 1);
-          fr[(b + 1) & 1][1] = frag_tr(Qtb, 1, b + 1);
+        for (int b = 0; b < 4; ++b) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
         }
-        adk[b] = mfma(sf0, fr[b & 1][0], adk[b]);
-        adk[b] = mfma(sf1, fr[b & 1][1], adk[b]);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        f16x8 fr[2][2];
+        fr[0][0] = frq[0];
+        fr[0][1] = frq[1];
 #pragma unroll
-      for (int b = 0; b < 3; ++b) {
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        for (int b = 0; b < 4; ++b) {
+          if (b < 3) {
+            fr[(b + 1) & 1][0] = frag_tr(Qtb, 0, b + 1);
+            fr[(b + 1) & 1][1] = frag_tr(Qtb, 1, b + 1);
+          }
+          adk[b] = mfma(sf0, fr[b & 1][0], adk[b]);
+          adk[b] = mfma(sf1, fr[b & 1][1], adk[b]);
+        }
+#pragma unroll
+        for (int b = 0; b < 3; ++b) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
-    // step it + 3's descriptor: issued here, where the closing wait covers it
+    // the descriptor three steps ahead: issued here, where the closing wait covers it
     __builtin_amdgcn_sched_barrier(0);
-    const KStep n3 = kst[min(it + 3, n_steps - 1)];
+    const KStep n3 = kst[min((u >> 1) + 3, n_steps - 1)];
     wait_all_loads();
     __syncthreads();
-    buf ^= 1;
-    cur = nxt;
-    nxt = n2;
-    n2 = n3;
+    if (hp) {
+      cur = nxt;
+      nxt = n2;
+      n2 = n3;
+    }
   }
 
   const float inv_sdo = 1.f / pow2_scale(*dmax);  // undo the dO scaling
-  float* red = reinterpret_cast<float*>(&qd[0][0][0][0]);  // [64][129] fp32
-  // sum the four heads in order 0..3 through LDS, then write dk (scaled, un-rotated)
-  // and dv
-  dkdv_reduce_store<true>(adk, red, hh, kb, hi, l32, tid, page, g, krows, Hkv, inv_sdo * scale, cs, dk);
-  dkdv_reduce_store<false>(adv, red, hh, kb, hi, l32, tid, page, g, krows, Hkv, inv_sdo, cs, dv);
+  float* red = reinterpret_cast<float*>(&qd[0][0][0][0]);  // [128][129] fp32
+  const int rowsA = page_nrows[physA], rowsB = physB >= 0 ? page_nrows[physB] : 0;
+  // sum the two head parities in order 0, 1 through LDS, then write dk (scaled,
+  // un-rotated) and dv for both pages
+  dkdv_reduce_store<true>(adk, red, kt, j, active, hi, l32, tid, physA, physB, rowsA, rowsB, g, Hkv,
+                          inv_sdo * scale, cs, dk);
+  dkdv_reduce_store<false>(adv, red, kt, j, active, hi, l32, tid, physA, physB, rowsA, rowsB, g, Hkv, inv_sdo,
+                           cs, dv);
 }
 
 // ---------------------------------------------------------------------------
@@ -1271,13 +1294,13 @@ void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f
 }
 
 template <typename TG>
-void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, const f16_t* kn, const f16_t* vn,
+void launch_dkdv_mfma(const LaunchShape& s, int64_t n_pairs, const f16_t* qn, const f16_t* kn, const f16_t* vn,
                       const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
-                      const int32_t* order, const int64_t* kstep_off, const KStep* ksteps,
+                      const int32_t* pair_order, const int32_t* pairs, const int64_t* pair_off, const KStep* psteps,
                       const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st) {
-  dkdv_mfma_kernel<TG><<<run_grid(n_kvp, s.Hkv), 512, 0, st>>>(qn, kn, vn, dOn, ld, cs, dmax, order, kstep_off,
-                                                               ksteps, page_nrows, dk, dv,
-                                                               (int)n_kvp, s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
+  dkdv_mfma_kernel<TG><<<run_grid(n_pairs, s.Hkv), 512, 0, st>>>(qn, kn, vn, dOn, ld, cs, dmax, pair_order, pairs,
+                                                                 pair_off, psteps, page_nrows, dk, dv, (int)n_pairs,
+                                                                 s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
 }
 
 #define INST_MFMA_BWD(TG)                                                                                      \
@@ -1286,8 +1309,8 @@ void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, cons
                                    const QPage*, const int32_t*, const Tile*, TG*, hipStream_t);               \
   template void launch_dkdv_mfma<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,    \
                                      const f16_t*, const float2*, const float2*, const uint32_t*,              \
-                                     const int32_t*, const int64_t*, const KStep*, const int32_t*, TG*, TG*,    \
-                                     hipStream_t);
+                                     const int32_t*, const int32_t*, const int64_t*, const KStep*,             \
+                                     const int32_t*, TG*, TG*, hipStream_t);
 INST_MFMA_BWD(bf16_t)
 INST_MFMA_BWD(float)
 

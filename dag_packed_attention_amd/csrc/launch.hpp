@@ -40,9 +40,9 @@ void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f
                     const f16_t* vn, const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
                     const QPage* qpages, const int32_t* order, const Tile* tiles, TG* dq, hipStream_t st);
 template <typename TG>
-void launch_dkdv_mfma(const LaunchShape& s, int64_t n_kvp, const f16_t* qn, const f16_t* kn, const f16_t* vn,
+void launch_dkdv_mfma(const LaunchShape& s, int64_t n_pairs, const f16_t* qn, const f16_t* kn, const f16_t* vn,
                       const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
-                      const int32_t* order, const int64_t* kstep_off, const KStep* ksteps,
+                      const int32_t* pair_order, const int32_t* pairs, const int64_t* pair_off, const KStep* psteps,
                       const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st);
 template <typename T>
 void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,

@@ -313,28 +313,67 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
     for_each_entry([&](int32_t ph, const KEntry& e) { P->kentries[fill[ph]++] = e; });
   }
 
-  // reader lists unrolled into 32-row steps (the dK/dV kernel's loop), in list order
-  P->kstep_off.assign(n_pages + 1, 0);
-  for (int32_t ph = 0; ph < n_pages; ++ph) {
-    int64_t steps = 0;
-    for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
-      const KEntry& k = P->kentries[e];
-      for (int32_t lq = k.lq0; lq < k.lq1; ++lq) steps += P->page_nrows[P->page_table[k.slot_base + lq]] > 32 ? 2 : 1;
-    }
-    if (steps > INT32_MAX) return fail(err, DAG_E_OVERFLOW, "reader list too long");
-    P->kstep_off[ph + 1] = P->kstep_off[ph] + steps;
-  }
-  P->ksteps.resize((size_t)P->kstep_off[n_pages]);
-  for (int32_t ph = 0; ph < n_pages; ++ph) {
-    int64_t i = P->kstep_off[ph];
-    for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
-      const KEntry& k = P->kentries[e];
-      const int32_t vis = k.lohi_diag & 0x1ffff;  // lo | hi << 8 | diag << 16
-      const int32_t packed = ((vis & 0xff) << 1) | (((vis >> 8) & 0xff) << 8) | (((vis >> 16) & 1) << 15);
-      for (int32_t lq = k.lq0; lq < k.lq1; ++lq) {
-        const int32_t qph = P->page_table[k.slot_base + lq];
-        const int32_t nr = P->page_nrows[qph];
-        for (int32_t rb = 0; rb < (nr > 32 ? 2 : 1); ++rb) P->ksteps[(size_t)i++] = KStep{qph, rb | packed | (nr << 16)};
+  // KV page pairs for the dK/dV kernel: pages (0, 1), (2, 3), ... of each node; an odd
+  // last page goes alone (B = -1).  A pair's reader steps are its two pages' reader lists
+  // unrolled into 32-row steps and merged by (reader node, query page, occurrence of that
+  // query page in the page's list): a step that both pages see carries both visible
+  // ranges, a step that one page sees has an empty range for the other.  Every key is
+  // logical, so the merged order does not depend on the physical page placement.
+  {
+    std::vector<int32_t> node_of_slot(n_pages, -1);
+    for (int32_t w = 0; w < n; ++w)
+      if (P->length[w] > 0) node_of_slot[P->slot0[w]] = w;
+    struct Item {
+      int32_t w, lq, k, qph, info;  // info: lo << 1 | hi << 8 | diag << 15
+    };
+    auto items_of = [&](int32_t ph, std::vector<Item>& out) {
+      out.clear();
+      for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
+        const KEntry& k = P->kentries[e];
+        const int32_t w = node_of_slot[k.slot_base];
+        const int32_t vis = k.lohi_diag;
+        const int32_t info = ((vis & 0xff) << 1) | (((vis >> 8) & 0xff) << 8) | (((vis >> 16) & 1) << 15);
+        for (int32_t lq = k.lq0; lq < k.lq1; ++lq)
+          out.push_back(Item{w, lq, 0, P->page_table[k.slot_base + lq], info});
+      }
+      std::stable_sort(out.begin(), out.end(),
+                       [](const Item& a, const Item& b) { return a.w != b.w ? a.w < b.w : a.lq < b.lq; });
+      for (size_t i = 1; i < out.size(); ++i)
+        if (out[i].w == out[i - 1].w && out[i].lq == out[i - 1].lq) out[i].k = out[i - 1].k + 1;
+    };
+    auto key_less = [](const Item& a, const Item& b) {
+      if (a.w != b.w) return a.w < b.w;
+      if (a.lq != b.lq) return a.lq < b.lq;
+      return a.k < b.k;
+    };
+    P->kpairs.clear();
+    P->kpair_off.assign(1, 0);
+    P->kpsteps.clear();
+    std::vector<Item> la, lb;
+    for (int32_t u = 0; u < n; ++u) {
+      if (P->length[u] == 0) continue;
+      for (int32_t lp = 0; lp < P->npages[u]; lp += 2) {
+        const int32_t pa = P->page_table[P->slot0[u] + lp];
+        const int32_t pb = lp + 1 < P->npages[u] ? P->page_table[P->slot0[u] + lp + 1] : -1;
+        items_of(pa, la);
+        if (pb >= 0) items_of(pb, lb); else lb.clear();
+        size_t ia = 0, ib = 0;
+        while (ia < la.size() || ib < lb.size()) {
+          int32_t qph, infa = 0, infb = 0;
+          if (ib == lb.size() || (ia < la.size() && key_less(la[ia], lb[ib]))) {
+            qph = la[ia].qph, infa = la[ia++].info;
+          } else if (ia == la.size() || key_less(lb[ib], la[ia])) {
+            qph = lb[ib].qph, infb = lb[ib++].info;
+          } else {
+            qph = la[ia].qph, infa = la[ia++].info, infb = lb[ib++].info;
+          }
+          const int32_t nr = P->page_nrows[qph];
+          for (int32_t rb = 0; rb < (nr > 32 ? 2 : 1); ++rb)
+            P->kpsteps.push_back(KStep{qph, (int32_t)((uint32_t)(rb | infa) | ((uint32_t)infb << 16))});
+        }
+        P->kpairs.push_back(pa);
+        P->kpairs.push_back(pb);
+        P->kpair_off.push_back((int64_t)P->kpsteps.size());
       }
     }
   }
@@ -385,6 +424,16 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
     for (int32_t u : nodes_by)
       if (P->length[u] > 0)
         for (int32_t lp = 0; lp < P->npages[u]; ++lp) P->bwd_order.push_back(P->page_table[P->slot0[u] + lp]);
+    // pairs in the same node order (a node's pairs are consecutive in kpairs)
+    std::vector<int32_t> pair0(n + 1, 0);
+    for (int32_t u = 0, c = 0; u < n; ++u) {
+      pair0[u] = c;
+      if (P->length[u] > 0) c += (P->npages[u] + 1) / 2;
+      pair0[u + 1] = c;
+    }
+    P->pair_order.clear();
+    for (int32_t u : nodes_by)
+      for (int32_t i = pair0[u]; i < pair0[u + 1]; ++i) P->pair_order.push_back(i);
   }
 
   // ---- info ------------------------------------------------------------------------

@@ -42,13 +42,14 @@ struct KEntry {
   int32_t lohi_diag;  // lo | (hi << 8) | (diag << 16)
 };
 
-// One 32-row step of a KV page's reader list, as the dK/dV kernel walks it: rows
-// 32 rb .. 32 rb + 31 of physical query page qph see rows [lo, hi) of the KV page
-// (diag: the page's own query block, masked causally); nrows = qph's valid rows.
-// Packed so a kernel fetches a step with one 8-byte load.
+// One 32-row step of a KV page pair's merged reader list, as the dK/dV kernel walks
+// it: rows 32 rb .. 32 rb + 31 of physical query page qph see rows [loA, hiA) of
+// page A and [loB, hiB) of page B (an empty range: that page is not read by this
+// step; diag: the page's own query block, masked causally).  Packed so a kernel
+// fetches a step with one 8-byte load.
 struct KStep {
   int32_t qph;
-  int32_t info;  // rb | lo << 1 | hi << 8 | diag << 15 | nrows << 16
+  int32_t info;  // rb | loA << 1 | hiA << 8 | diagA << 15 | loB << 17 | hiB << 24 | diagB << 31
 };
 
 // One packed gated-delta-rule input sequence as the kernels read it.  Its
@@ -93,10 +94,12 @@ struct Plan {
   std::vector<QPage> qpages;
   std::vector<int32_t> fwd_order;              // query-page ids, heaviest first
   std::vector<int32_t> kv_off;                 // physical page -> first reader entry (size pages+1)
-  std::vector<int64_t> kstep_off;              // physical page -> its first reader step (size pages+1)
-  std::vector<KStep> ksteps;                   // reader lists unrolled into 32-row steps
   std::vector<KEntry> kentries;
   std::vector<int32_t> bwd_order;              // physical pages with rows, heaviest first
+  std::vector<int32_t> kpairs;                 // KV page pairs (A, B; B = -1 for a lone page)
+  std::vector<int64_t> kpair_off;              // pair -> its first merged reader step (size pairs+1)
+  std::vector<KStep> kpsteps;                  // merged reader steps of every pair
+  std::vector<int32_t> pair_order;             // pair ids, node-grouped, heaviest first
   std::vector<int32_t> pos_of_row;             // C
   std::vector<int32_t> row_of_token;           // U
   // gated-delta-rule schedule (empty when opts.gdn_chunk == 0)

@@ -1,6 +1,8 @@
 // Host driver for the DAG compactor, built with sanitizers by the test-suite.
 // Builds many random DAGs (valid and invalid) and walks every plan table,
 // checking the structural properties the kernels rely on.
+#include <array>
+#include <algorithm>
 #include <cstdio>
 #include <cstdlib>
 #include <string>
@@ -38,31 +40,53 @@ static int check(const Plan& P) {
       const int lo = k.lohi_diag & 0xff, hi = (k.lohi_diag >> 8) & 0xff;
       if (lo >= hi || hi > P.page_nrows[ph]) return 7;
     }
-  // reader steps: the entries unrolled in order, one step per 32-row block
-  if ((int64_t)P.kstep_off.size() != pages + 1 || P.kstep_off[0] != 0) return 8;
-  for (int64_t ph = 0; ph < pages; ++ph) {
-    int64_t i = P.kstep_off[ph];
-    for (int e = P.kv_off[ph]; e < P.kv_off[ph + 1]; ++e) {
-      const KEntry& k = P.kentries[e];
-      for (int lq = k.lq0; lq < k.lq1; ++lq) {
-        const int qph = P.page_table[k.slot_base + lq];
-        const int nr = P.page_nrows[qph];
-        for (int rb = 0; rb * 32 < nr; ++rb, ++i) {
-          if (i >= P.kstep_off[ph + 1]) return 9;
-          const KStep& st = P.ksteps[i];
-          const int lo = (st.info >> 1) & 0x7f, hi = (st.info >> 8) & 0x7f;
-          if (st.qph != qph || (st.info & 1) != rb || ((st.info >> 16) & 0x7f) != nr) return 10;
-          if (lo != (k.lohi_diag & 0xff) || hi != ((k.lohi_diag >> 8) & 0xff) ||
-              ((st.info >> 15) & 1) != ((k.lohi_diag >> 16) & 1) || (st.info >> 23) != 0)
-            return 11;
+  // KV page pairs: two consecutive pages of one node (or one lone last page); each
+  // pair's merged steps, projected on each of its pages (steps with a non-empty range
+  // for it), are exactly that page's reader entries unrolled into 32-row steps
+  const int64_t npairs = (int64_t)P.kpairs.size() / 2;
+  if ((int64_t)P.kpair_off.size() != npairs + 1 || P.kpair_off[0] != 0) return 8;
+  if ((int64_t)P.kpsteps.size() != P.kpair_off[npairs]) return 13;
+  std::vector<int> seen(pages, 0);
+  for (int64_t pr = 0; pr < npairs; ++pr) {
+    for (int side = 0; side < 2; ++side) {
+      const int ph = P.kpairs[2 * pr + side];
+      if (ph < 0) {
+        if (side == 0) return 9;
+        for (int64_t i = P.kpair_off[pr]; i < P.kpair_off[pr + 1]; ++i)
+          if ((uint32_t)P.kpsteps[i].info >> 16) return 10;  // a missing page is never read
+        continue;
+      }
+      if (ph >= pages || seen[ph]++) return 9;
+      std::vector<std::array<int, 5>> want, got;  // qph, rb, lo, hi, diag
+      for (int e = P.kv_off[ph]; e < P.kv_off[ph + 1]; ++e) {
+        const KEntry& k = P.kentries[e];
+        for (int lq = k.lq0; lq < k.lq1; ++lq) {
+          const int qph = P.page_table[k.slot_base + lq];
+          for (int rb = 0; rb * 32 < P.page_nrows[qph]; ++rb)
+            want.push_back({qph, rb, k.lohi_diag & 0xff, (k.lohi_diag >> 8) & 0xff, (k.lohi_diag >> 16) & 1});
         }
       }
+      for (int64_t i = P.kpair_off[pr]; i < P.kpair_off[pr + 1]; ++i) {
+        const KStep& st = P.kpsteps[i];
+        const uint32_t inf = ((uint32_t)st.info >> (16 * side)) & 0xffffu;
+        const int lo = (inf >> 1) & 0x7f, hi = (inf >> 8) & 0x7f;
+        if (lo == hi) continue;
+        got.push_back({st.qph, (int)(st.info & 1), lo, hi, (int)((inf >> 15) & 1)});
+      }
+      std::sort(want.begin(), want.end());
+      std::sort(got.begin(), got.end());
+      if (want != got) return 11;
     }
-    if (i != P.kstep_off[ph + 1]) return 12;
+    if (P.kpair_off[pr + 1] <= P.kpair_off[pr]) return 14;  // a launched pair has steps
   }
-  if ((int64_t)P.ksteps.size() != P.kstep_off[pages]) return 13;
-  for (int32_t ph : P.bwd_order)
-    if (ph < 0 || ph >= pages || P.kstep_off[ph + 1] <= P.kstep_off[ph]) return 14;  // a launched page has steps
+  for (int64_t ph = 0; ph < pages; ++ph)
+    if (!seen[ph] && P.page_nrows[ph] > 0) return 12;  // every page with rows is in a pair
+  if ((int64_t)P.pair_order.size() != npairs) return 15;
+  {
+    std::vector<int> cnt(npairs, 0);
+    for (int32_t pr : P.pair_order)
+      if (pr < 0 || pr >= npairs || cnt[pr]++) return 15;
+  }
   return 0;
 }
 
