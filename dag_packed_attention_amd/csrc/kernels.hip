@@ -436,6 +436,12 @@ __device__ __forceinline__ int cfrag_base(int r, int hi) { return cbrick_off(r, 
 
 // all of this thread's global->LDS loads (and everything else) have landed
 __device__ __forceinline__ void wait_all_loads() { __builtin_amdgcn_s_waitcnt(0); }
+// An empty statement that takes x in registers: the compiler waits for x's load
+// here.  Used on values loaded before a loop and read inside it, so that the
+// compiler's own waits for them (which it counts without the loads issued from
+// inline assembly, and so sets too tight) stay out of the loop instead of draining
+// the staging loads in flight there.
+__device__ __forceinline__ void pin(const f16x8& x) { asm volatile("" : : "v"(x)); }
 
 constexpr int kTile = 64 * kD;  // elements of a page's 64 x 128 (or 128 x 64) block in global memory
 
@@ -832,6 +838,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     if (vp >= 0)
       stage_bricks<4>(lvp[wave >> 2], tile_rsrc(vn + ((int64_t)vp * Hkv + g) * kTile, kTile * 2), 4 * (wave & 3),
                       brick_lane_off(lane));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) pin(kf[ks]);
   }
   f32x16 adk[4], adv[4];  // [d block]
 #pragma unroll
