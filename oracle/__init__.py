@@ -25,6 +25,9 @@ rounding order):
 * ``gdn_plan``  -- HARTS's minimum-call planning of chunked linear-attention
                    execution: segment tree, T_pre / T_in, the recovery of
                    rounds, mandatory replay, and a brute-force minimum.
+* ``logprob``   -- compact-to-semantic log-probabilities (HARTS Eq. 17) on
+                   expanded per-position rows, the semantic position map of
+                   the original batch, and the reused-row gradient (Eq. 19-20).
 
 Parity unpinned: the RoPE pairing convention (first half / second half of the
 head dimension) and the frequency base (10000) are a textbook choice the pages

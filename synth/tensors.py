@@ -65,3 +65,23 @@ def gdn_inputs(n_tokens: int, h: int, dk: int, dv: int, seed: int, device="cpu",
                                                                           device)))
     do = normal((n_tokens, h, dv), seed, STREAM_GDO, device, dtype) if with_grad else None
     return q, k, v, beta, alpha, do
+
+
+STREAM_LOGITS, STREAM_LABELS, STREAM_LPGRAD = 21, 22, 23
+
+
+def logprob_inputs(n_rows: int, vocab: int, n_tokens: int, n_pos: int, seed: int, device="cpu",
+                   dtype=torch.float32, spread: float = 2.0, with_grad: bool = True):
+    """Inputs of the log-probability step.
+
+    z [n_rows, vocab]: logits, normal with standard deviation ``spread``,
+    rounded to ``dtype``; labels [n_tokens]: vocabulary ids uniform over
+    [0, vocab), int64; g [n_pos]: upstream gradients of the log-probabilities,
+    standard normal float32.
+    """
+    z = (normal((n_rows, vocab), seed, STREAM_LOGITS, device) * spread).to(dtype)
+    gen = torch.Generator(device="cpu")
+    gen.manual_seed(_seed(seed, STREAM_LABELS))
+    labels = torch.randint(0, vocab, (n_tokens,), generator=gen, dtype=torch.int64)
+    g = normal((n_pos,), seed, STREAM_LPGRAD, device) if with_grad else None
+    return z, labels, g
