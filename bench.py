@@ -23,6 +23,8 @@ Printed JSON (one line on stdout; progress goes to stderr):
               on the same DAG, forward and backward: milliseconds, the schedule's
               rounds / sequences / replayed tokens, and executed MFMA TFLOP/s;
               hybrid_step_ms = the attention step + 3 such layers (the hybrid stack)
+  logprob     compact-to-semantic log-probabilities and their gradient on 65,536 rows
+              of the workload's semantic map, V = 131,072: ms and GB/s against 8 TB/s
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -166,6 +168,63 @@ def gdn_time(dpa, spec, dev, steps, warmup):
     return out
 
 
+LP_VOCAB, LP_ROWS = 131072, 65536
+HBM_PEAK_GBPS = 8000.0
+
+
+def logprob_time(dpa, plan, dev, steps, warmup):
+    """Compact-to-semantic log-probabilities on the first 65,536 rows of the workload's map.
+
+    Logits [65536, 131072] bf16, upstream gradients fp32, dz bf16.  Algorithmic HBM bytes:
+    the forward reads every row that holds a position once (2 V bytes) plus per position its
+    map entries, target logit and lambda (14 bytes) and per row lse and row_first (8 bytes);
+    the backward also writes every row's gradient (2 V bytes) and reads g (4 bytes/position)."""
+    import numpy as np
+    import torch
+
+    import synth
+    V, CH = LP_VOCAB, LP_ROWS
+    lab = np.random.default_rng(21).integers(0, V, plan.rows).astype(np.int32)
+    m = plan.logprob_map(lab)
+    rf_all, rp, pt = (torch.as_tensor(m[k], device=dev) for k in ("row_first", "row_pos", "pos_target"))
+    rf = rf_all[:CH + 1]
+    n = len(m["pos_row"])
+    counts = np.diff(m["row_first"][:CH + 1])
+    used, npos = int((counts > 0).sum()), int(counts.sum())
+    z = synth.normal((CH, V), 21, 1, dev).mul_(2.0).to(torch.bfloat16)
+    g = synth.normal((n,), 21, 2, dev)
+    lse = torch.empty(CH, dtype=torch.float32, device=dev)
+    lam = torch.empty(n, dtype=torch.float32, device=dev)
+    dz = torch.empty_like(z)
+    for _ in range(warmup):
+        dpa.logprob_fwd(z, rf, rp, pt, lse=lse, lam=lam)
+        dpa.logprob_bwd(z, lse, rf, rp, pt, g, dz=dz)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    fwd_ms = bwd_ms = 0.0
+    for _ in range(steps):
+        ev[0].record()
+        dpa.logprob_fwd(z, rf, rp, pt, lse=lse, lam=lam)
+        ev[1].record()
+        dpa.logprob_bwd(z, lse, rf, rp, pt, g, dz=dz)
+        ev[2].record()
+        torch.cuda.synchronize()
+        fwd_ms += ev[0].elapsed_time(ev[1]) / steps
+        bwd_ms += ev[1].elapsed_time(ev[2]) / steps
+    b_fwd = used * 2 * V + 14 * npos + 8 * CH
+    b_bwd = used * 2 * V + CH * 2 * V + 18 * npos + 8 * CH
+    gf, gb = b_fwd / (fwd_ms * 1e-3) / 1e9, b_bwd / (bwd_ms * 1e-3) / 1e9
+    del z, dz, g, lse, lam
+    torch.cuda.empty_cache()
+    return {"step": "compact-to-semantic log-probabilities (mapped cross-entropy) and reused-row gradient",
+            "rows": CH, "rows_with_positions": used, "positions": npos, "vocab": V,
+            "logits": "bf16", "dz": "bf16",
+            "positions_per_row": round(npos / max(used, 1), 3),
+            "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+            "roofline": {"bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+                         "fwd": {"achieved": round(gf, 1), "frac": round(gf / HBM_PEAK_GBPS, 4), "bytes": b_fwd},
+                         "bwd": {"achieved": round(gb, 1), "frac": round(gb / HBM_PEAK_GBPS, 4), "bytes": b_bwd}}}
+
+
 def cpu_baseline(spec, plan, budget_s=15.0):
     """The oracle (float32) on one causal trajectory of the workload, sized to ~budget_s."""
     import numpy as np
@@ -259,6 +318,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-gdn", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-logprob", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB -> 1 GiB device copy kernel 3 times (scales HBM counters)")
     args = ap.parse_args()
@@ -347,6 +407,11 @@ def main() -> int:
         out["gdn"] = g
         log(f"gdn layer: fwd {g['fwd_ms']:.2f} ms, bwd {g['bwd_ms']:.2f} ms ({g['rounds']} rounds, "
             f"{g['sequences']} sequences); hybrid step {g['hybrid_step_ms']:.1f} ms")
+    if not args.no_logprob:
+        lp = logprob_time(dpa, plan, dev, max(1, min(args.steps, 5)), 1)
+        out["logprob"] = lp
+        log(f"logprob: fwd {lp['fwd_ms']:.3f} ms ({lp['roofline']['fwd']['achieved']:.0f} GB/s), "
+            f"bwd {lp['bwd_ms']:.3f} ms ({lp['roofline']['bwd']['achieved']:.0f} GB/s)")
     if not args.no_flat:
         t_flat, fpairs, frows, ntraj = flat_time(dpa, spec, plan, p, dev, args.flat_steps)
         out["x_vs_flat"] = round(t_flat / dt, 3)

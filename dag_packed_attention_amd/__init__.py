@@ -8,7 +8,8 @@ importing this package fails.
 
 Names follow the C ABI: :class:`Plan` wraps ``dag_build`` and the plan
 queries, :func:`attn_fwd` / :func:`attn_bwd` wrap ``dag_attn_fwd`` /
-``dag_attn_bwd``.
+``dag_attn_bwd``; :func:`gdn_fwd` / :func:`gdn_bwd` and :func:`logprob_fwd` /
+:func:`logprob_bwd` likewise, with :meth:`Plan.logprob_map` for the position map.
 """
 from __future__ import annotations
 
@@ -69,6 +70,11 @@ class DagGdnParams(ctypes.Structure):
                 ("grad_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
+class DagLogprobParams(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int64), ("n_pos", ctypes.c_int64), ("vocab", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32)]
+
+
 class DagError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
@@ -102,6 +108,9 @@ def _load() -> ctypes.CDLL:
         "dag_gdn_workspace": ([P, ctypes.POINTER(DagGdnParams), ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I32),
         "dag_gdn_fwd": ([P, ctypes.POINTER(DagGdnParams), P, P, P, P, P, P, P, SZ, P], I32),
         "dag_gdn_bwd": ([P, ctypes.POINTER(DagGdnParams), P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "dag_plan_logprob_map": ([P, P, I64, P, P, P, P, ctypes.POINTER(I64)], I32),
+        "dag_logprob_fwd": ([ctypes.POINTER(DagLogprobParams), P, P, P, P, P, P, P], I32),
+        "dag_logprob_bwd": ([ctypes.POINTER(DagLogprobParams), P, P, P, P, P, P, P, P], I32),
         "dag_attn_timing_enable": ([P, I32, I32], I32),
         "dag_attn_timing_read": ([P, P, P], I32),
         "dag_last_error": ([], ctypes.c_char_p),
@@ -198,6 +207,25 @@ class Plan:
         buf = (DagGdnSeq * max(n.value, 1))()
         _check(_lib.dag_plan_gdn_seqs(self._h, buf, n.value, ctypes.byref(n)))
         return [{f: getattr(buf[i], f) for f, _ in DagGdnSeq._fields_} for i in range(n.value)]
+
+    def logprob_map(self, labels) -> dict:
+        """``dag_plan_logprob_map``: labels [C] (vocabulary id per row) -> the semantic map.
+
+        Returns int32 arrays ``pos_row``, ``pos_target`` [n], ``row_first`` [C+1], ``row_pos`` [n]."""
+        lab = np.ascontiguousarray(labels, dtype=np.int32)
+        if lab.shape != (self.rows,):
+            raise ValueError(f"labels: expected [{self.rows}], got {lab.shape}")
+        n = ctypes.c_int64(0)
+        _check(_lib.dag_plan_logprob_map(self._h, lab.ctypes.data, 0, None, None, None, None, ctypes.byref(n)))
+        k = n.value
+        out = {"pos_row": np.zeros(max(k, 1), np.int32), "pos_target": np.zeros(max(k, 1), np.int32),
+               "row_first": np.zeros(self.rows + 1, np.int32), "row_pos": np.zeros(max(k, 1), np.int32)}
+        _check(_lib.dag_plan_logprob_map(self._h, lab.ctypes.data, k, out["pos_row"].ctypes.data,
+                                         out["pos_target"].ctypes.data, out["row_first"].ctypes.data,
+                                         out["row_pos"].ctypes.data, ctypes.byref(n)))
+        for name in ("pos_row", "pos_target", "row_pos"):
+            out[name] = out[name][:k]
+        return out
 
     def upload(self, stream=None) -> None:
         _check(_lib.dag_plan_upload(self._h, _stream_ptr(stream)))
@@ -403,6 +431,63 @@ def gdn_bwd(plan: Plan, p: GdnParams, q, k, v, beta, alpha, dO, ws=None, stream=
 
 
 # ---------------------------------------------------------------------------
+# compact-to-semantic log-probabilities
+# ---------------------------------------------------------------------------
+
+_LP_DT = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}
+
+
+def _lp_params(z, n_pos: int, grad_dtype: str) -> DagLogprobParams:
+    import torch
+    if z.dim() != 2 or not z.is_contiguous() or z.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"z: expected contiguous bf16/fp32 [C, V], got {z.dtype} {tuple(z.shape)}")
+    dt = DTYPE_BF16 if z.dtype == torch.bfloat16 else DTYPE_FP32
+    return DagLogprobParams(z.shape[0], int(n_pos), z.shape[1], dt, _LP_DT[grad_dtype])
+
+
+def _check_map(z, row_first, row_pos, pos_target):
+    import torch
+    for name, t, n in (("row_first", row_first, z.shape[0] + 1), ("row_pos", row_pos, pos_target.numel()),
+                       ("pos_target", pos_target, row_pos.numel())):
+        if t.dtype != torch.int32 or t.dim() != 1 or t.numel() != n or not t.is_contiguous() or t.device != z.device:
+            raise ValueError(f"{name}: expected contiguous int32 [{n}] on {z.device}, "
+                             f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def logprob_fwd(z, row_first, row_pos, pos_target, lse=None, lam=None, stream=None):
+    """``dag_logprob_fwd``: z [C, V] (bf16/fp32), the row-grouped map (int32 device tensors)
+    -> (lse [C] fp32, lambda [n] fp32)."""
+    import torch
+    _check_map(z, row_first, row_pos, pos_target)
+    n = pos_target.numel()
+    if lse is None:
+        lse = torch.empty(z.shape[0], dtype=torch.float32, device=z.device)
+    if lam is None:
+        lam = torch.empty(n, dtype=torch.float32, device=z.device)
+    cp = _lp_params(z, n, "fp32")
+    _check(_lib.dag_logprob_fwd(ctypes.byref(cp), _ptr(z), _ptr(row_first), _ptr(row_pos), _ptr(pos_target),
+                                _ptr(lse), _ptr(lam), _stream_ptr(stream)))
+    return lse, lam
+
+
+def logprob_bwd(z, lse, row_first, row_pos, pos_target, g, grad_dtype: str = "bf16", dz=None, stream=None):
+    """``dag_logprob_bwd``: g [n] fp32 (dL/dlambda) -> dz [C, V] in ``grad_dtype``."""
+    import torch
+    _check_map(z, row_first, row_pos, pos_target)
+    n = pos_target.numel()
+    if g.dtype != torch.float32 or g.numel() != n or not g.is_contiguous():
+        raise ValueError(f"g: expected contiguous float32 [{n}]")
+    if lse.dtype != torch.float32 or lse.numel() != z.shape[0]:
+        raise ValueError(f"lse: expected float32 [{z.shape[0]}]")
+    if dz is None:
+        dz = torch.empty(z.shape, dtype=torch.bfloat16 if grad_dtype == "bf16" else torch.float32, device=z.device)
+    cp = _lp_params(z, n, grad_dtype)
+    _check(_lib.dag_logprob_bwd(ctypes.byref(cp), _ptr(z), _ptr(lse), _ptr(row_first), _ptr(row_pos),
+                                _ptr(pos_target), _ptr(g), _ptr(dz), _stream_ptr(stream)))
+    return dz
+
+
+# ---------------------------------------------------------------------------
 # layout helpers (token-major <-> row layout); pure data movement
 # ---------------------------------------------------------------------------
 
@@ -423,5 +508,6 @@ def from_rows(plan: Plan, x_rows):
     return x_rows[torch.as_tensor(rot, dtype=torch.long, device=x_rows.device)]
 
 
-__all__ = ["Plan", "AttnParams", "DagError", "attn_fwd", "attn_bwd", "workspace_bytes", "to_rows",
-           "from_rows", "last_error", "LIB_PATH"]
+__all__ = ["Plan", "AttnParams", "GdnParams", "DagError", "attn_fwd", "attn_bwd", "workspace_bytes", "gdn_fwd",
+           "gdn_bwd", "gdn_workspace_bytes", "logprob_fwd", "logprob_bwd", "to_rows", "from_rows", "last_error",
+           "LIB_PATH"]

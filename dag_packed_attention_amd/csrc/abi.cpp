@@ -11,6 +11,7 @@
 
 #include "gdn.hpp"
 #include "launch.hpp"
+#include "logprob.hpp"
 #include "plan.hpp"
 
 struct dag_plan {
@@ -718,6 +719,104 @@ dag_status dag_gdn_bwd(dag_plan* plan, const dag_gdn_params* p, const void* q, c
   else
     run((bf16_t*)nullptr);
   return launched("dag_gdn_bwd");
+}
+
+// ---- compact-to-semantic log-probabilities -----------------------------------------
+dag_status dag_plan_logprob_map(const dag_plan* plan, const int32_t* labels, int64_t cap, int32_t* pos_row,
+                                int32_t* pos_target, int32_t* row_first, int32_t* row_pos, int64_t* n_pos) {
+  if (!plan || !labels || !n_pos) return set_err(DAG_E_INVALID, "null argument");
+  const Plan& P = plan->p;
+  std::vector<int32_t> rows, targets;
+  std::string err;
+  dag_status st;
+  try {
+    st = build_logprob_map(P, labels, &rows, &targets, &err);
+  } catch (const std::bad_alloc&) {
+    return set_err(DAG_E_OVERFLOW, "out of host memory building the position map");
+  }
+  if (st != DAG_OK) return set_err(st, err);
+  const int64_t n = (int64_t)rows.size();
+  *n_pos = n;
+  if (cap < n || !pos_row || !pos_target || !row_first || !row_pos) return DAG_OK;
+  const int64_t C = P.info.rows;
+  if (n) {
+    std::memcpy(pos_row, rows.data(), n * 4);
+    std::memcpy(pos_target, targets.data(), n * 4);
+  }
+  // counting sort by row, stable: batch order within a row
+  std::vector<int32_t> cnt(C + 1, 0);
+  for (int32_t r : rows) ++cnt[r + 1];
+  for (int64_t c = 0; c < C; ++c) cnt[c + 1] += cnt[c];
+  std::memcpy(row_first, cnt.data(), (C + 1) * 4);
+  for (int64_t s = 0; s < n; ++s) row_pos[cnt[rows[s]]++] = (int32_t)s;
+  return DAG_OK;
+}
+
+namespace {
+dag_status check_lp(const dag_logprob_params* p) {
+  if (!p) return set_err(DAG_E_INVALID, "null params");
+  if (p->rows < 0 || p->n_pos < 0 || p->vocab < 1) return set_err(DAG_E_INVALID, "negative size or vocab < 1");
+  if (p->n_pos > INT32_MAX) return set_err(DAG_E_OVERFLOW, "more than 2^31 - 1 positions");
+  if ((p->dtype != DAG_DTYPE_BF16 && p->dtype != DAG_DTYPE_FP32) ||
+      (p->grad_dtype != DAG_DTYPE_BF16 && p->grad_dtype != DAG_DTYPE_FP32))
+    return set_err(DAG_E_UNSUPPORTED, "dtype must be DAG_DTYPE_BF16 or DAG_DTYPE_FP32");
+  if (p->rows > INT64_MAX / 4 / p->vocab) return set_err(DAG_E_OVERFLOW, "rows * vocab overflows");
+  return DAG_OK;
+}
+
+bool aligned_to(const void* x, size_t a) { return (reinterpret_cast<uintptr_t>(x) % a) == 0; }
+}  // namespace
+
+dag_status dag_logprob_fwd(const dag_logprob_params* p, const void* z, const int32_t* row_first,
+                           const int32_t* row_pos, const int32_t* pos_target, float* lse, float* lambda,
+                           void* hip_stream) {
+  dag_status st = check_lp(p);
+  if (st != DAG_OK) return st;
+  if (p->rows == 0) return DAG_OK;
+  if (!z || !row_first || !lse || (p->n_pos > 0 && (!row_pos || !pos_target || !lambda)))
+    return set_err(DAG_E_INVALID, "null tensor pointer");
+  const size_t ez = p->dtype == DAG_DTYPE_BF16 ? 2 : 4;
+  if (!aligned_to(z, ez)) return set_err(DAG_E_INVALID, "z is not aligned to its element size");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if (p->dtype == DAG_DTYPE_BF16)
+    launch_lp_fwd<uint16_t>((const uint16_t*)z, p->rows, p->vocab, row_first, row_pos, pos_target, p->n_pos, lse,
+                            lambda, stream);
+  else
+    launch_lp_fwd<float>((const float*)z, p->rows, p->vocab, row_first, row_pos, pos_target, p->n_pos, lse, lambda,
+                         stream);
+  return launched("dag_logprob_fwd");
+}
+
+dag_status dag_logprob_bwd(const dag_logprob_params* p, const void* z, const float* lse, const int32_t* row_first,
+                           const int32_t* row_pos, const int32_t* pos_target, const float* g, void* dz,
+                           void* hip_stream) {
+  dag_status st = check_lp(p);
+  if (st != DAG_OK) return st;
+  if (p->rows == 0) return DAG_OK;
+  if (!z || !lse || !row_first || !dz || (p->n_pos > 0 && (!row_pos || !pos_target || !g)))
+    return set_err(DAG_E_INVALID, "null tensor pointer");
+  const size_t ez = p->dtype == DAG_DTYPE_BF16 ? 2 : 4, eg = p->grad_dtype == DAG_DTYPE_BF16 ? 2 : 4;
+  if (!aligned_to(z, ez) || !aligned_to(dz, eg))
+    return set_err(DAG_E_INVALID, "z or dz is not aligned to its element size");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  const int64_t C = p->rows, n = p->n_pos;
+  const int V = p->vocab;
+  if (p->dtype == DAG_DTYPE_BF16) {
+    if (p->grad_dtype == DAG_DTYPE_BF16)
+      launch_lp_bwd<uint16_t, uint16_t>((const uint16_t*)z, lse, C, V, row_first, row_pos, pos_target, g, n,
+                                        (uint16_t*)dz, stream);
+    else
+      launch_lp_bwd<uint16_t, float>((const uint16_t*)z, lse, C, V, row_first, row_pos, pos_target, g, n, (float*)dz,
+                                     stream);
+  } else {
+    if (p->grad_dtype == DAG_DTYPE_BF16)
+      launch_lp_bwd<float, uint16_t>((const float*)z, lse, C, V, row_first, row_pos, pos_target, g, n,
+                                     (uint16_t*)dz, stream);
+    else
+      launch_lp_bwd<float, float>((const float*)z, lse, C, V, row_first, row_pos, pos_target, g, n, (float*)dz,
+                                  stream);
+  }
+  return launched("dag_logprob_bwd");
 }
 
 }  // extern "C"

@@ -126,4 +126,9 @@ dag_status build_plan(const dag_node* nodes, int32_t n_nodes, const dag_mount* m
 // needs the plan's rows (row_of_token) to be built.
 dag_status build_gdn_schedule(Plan* P, int32_t chunk, std::string* err);
 
+// Semantic position map of the original batch (HARTS Sec. 3.5): m(s) and y_s of
+// every nonterminal position in batch order.  labels: vocabulary id per compact row.
+dag_status build_logprob_map(const Plan& P, const int32_t* labels, std::vector<int32_t>* pos_row,
+                             std::vector<int32_t>* pos_target, std::string* err);
+
 }  // namespace dagattn

@@ -264,6 +264,65 @@ dag_status dag_gdn_bwd(dag_plan* plan, const dag_gdn_params* p, const void* q, c
                        void* dq, void* dk, void* dv, float* dbeta, float* dalpha, void* ws,
                        size_t ws_bytes, void* hip_stream);
 
+/* ---- compact-to-semantic log-probabilities ------------------------------------
+ *
+ * HARTS Sec. 3.5 Eq. 17: for every nonterminal semantic position s of the
+ * original batch, lambda_s = z[m(s), y_s] - log sum_v exp z[m(s), v], where
+ * m(s) is the compact logit row of s and y_s the vocabulary id of the next
+ * token of s's trajectory.  Eq. 19-20: the gradient of a compact row is the sum
+ * over the positions that map to it, dz[c, v] = sum_{m(s)=c, y_s=v} g_s -
+ * (sum_{m(s)=c} g_s) softmax(z[c])_v with g_s = dL/dlambda_s.  Vocabulary-wide
+ * work runs once per compact row; no [positions x V] array is formed.
+ *
+ * The original batch: every root-to-leaf trajectory, leaves in depth-first
+ * order (roots and children in table order), each the flat sequence that visits
+ * node by node the mounted tokens that become visible there (not spliced
+ * before, in token order) and then the node's own tokens.  Its positions are
+ * its own tokens that have a next token, in sequence order; the target of an
+ * own token followed by a splice is the splice's first token.  Spliced tokens
+ * hold no position (Octopus Sec. 3.4: mounted spans carry a zero loss mask; their
+ * compact rows hold the producer's logits, not the reader's). */
+
+/* Build the map, host only.  labels[C]: vocabulary id of the token on each
+ * compact row (padding rows ignored; a negative id on a row that is some
+ * position's target is DAG_E_INVALID).  Writes *n_pos = the number of
+ * positions n and, when cap >= n and every output is non-NULL:
+ *   pos_row[n]      m(s), in batch order
+ *   pos_target[n]   y_s
+ *   row_first[C+1]  positions of row c are row_pos[row_first[c] .. row_first[c+1])
+ *   row_pos[n]      position indices grouped by row, batch order within a row.
+ * Otherwise only *n_pos is written.  DAG_E_OVERFLOW beyond 2^31 - 1 positions. */
+dag_status dag_plan_logprob_map(const dag_plan* plan, const int32_t* labels, int64_t cap, int32_t* pos_row,
+                                int32_t* pos_target, int32_t* row_first, int32_t* row_pos, int64_t* n_pos);
+
+typedef struct {
+  int64_t rows;        /* C: rows of z and dz                                       */
+  int64_t n_pos;       /* n: entries of pos_target, lambda and g (< 2^31)           */
+  int32_t vocab;       /* V >= 1; z and dz are [C, V] row-major                     */
+  int32_t dtype;       /* z: DAG_DTYPE_BF16 or DAG_DTYPE_FP32                       */
+  int32_t grad_dtype;  /* dz: DAG_DTYPE_BF16 or DAG_DTYPE_FP32                      */
+} dag_logprob_params;
+
+/* Forward.  Device pointers: z [C, V] (dtype, element-aligned), the map of
+ * dag_plan_logprob_map (or any row-grouped map: row_first[C+1] non-decreasing,
+ * row_pos a permutation of 0..n-1, pos_target[n]); lse [C] fp32 receives
+ * log sum_v exp z[c, v] for every row that holds a position and 0 for the
+ * others, whose z is not read; lambda [n] fp32.  A target outside [0, V) gives
+ * lambda = NaN; out-of-range map entries are skipped, never dereferenced.
+ * Sums over the vocabulary run in fp32 in a fixed order (bitwise reproducible).
+ * Enqueued on hip_stream; no allocation, no synchronisation. */
+dag_status dag_logprob_fwd(const dag_logprob_params* p, const void* z, const int32_t* row_first,
+                           const int32_t* row_pos, const int32_t* pos_target, float* lse, float* lambda,
+                           void* hip_stream);
+
+/* Backward given g [n] fp32 and the forward's lse: dz [C, V] (grad_dtype) is
+ * written for every row (zero on rows with no position).  Each target term is
+ * added to the softmax term in fp32 before the single rounding; positions of a
+ * row that share a target are summed in map order. */
+dag_status dag_logprob_bwd(const dag_logprob_params* p, const void* z, const float* lse, const int32_t* row_first,
+                           const int32_t* row_pos, const int32_t* pos_target, const float* g, void* dz,
+                           void* hip_stream);
+
 /* Per-kernel timing, for profiling.  While enabled, dag_attn_fwd/bwd record a
  * HIP event pair on their stream around each of their kernels (at most
  * `capacity` pairs, created here; later launches go unrecorded).

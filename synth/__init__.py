@@ -8,7 +8,7 @@ arithmetic -- no positions, no visibility, no attention -- so that the CPU
 oracle and the GPU path can both consume it without sharing any computation.
 """
 from .dags import DagSpec, DagBuilder, config1, config1_variant, config2, config3, config4, random_tiny_dag
-from .tensors import bf16_round, normal, attn_inputs, gdn_inputs
+from .tensors import bf16_round, normal, attn_inputs, gdn_inputs, logprob_inputs
 
 __all__ = ["DagSpec", "DagBuilder", "config1", "config1_variant", "config2", "config3",
            "config4", "random_tiny_dag", "bf16_round", "normal", "attn_inputs", "gdn_inputs"]
