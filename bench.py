@@ -24,7 +24,9 @@ Printed JSON (one line on stdout; progress goes to stderr):
               rounds / sequences / replayed tokens, and executed MFMA TFLOP/s;
               hybrid_step_ms = the attention step + 3 such layers (the hybrid stack)
   logprob     compact-to-semantic log-probabilities and their gradient on 65,536 rows
-              of the workload's semantic map, V = 131,072: ms and GB/s against 8 TB/s
+              of the workload's semantic map, V = 131,072: ms and GB/s against 8 TB/s,
+              with torch's copy of the same logits (the backward's read + write volume)
+              as context
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -213,16 +215,42 @@ def logprob_time(dpa, plan, dev, steps, warmup):
     b_fwd = used * 2 * V + 14 * npos + 8 * CH
     b_bwd = used * 2 * V + CH * 2 * V + 18 * npos + 8 * CH
     gf, gb = b_fwd / (fwd_ms * 1e-3) / 1e9, b_bwd / (bwd_ms * 1e-3) / 1e9
+    # context: torch's device copy of the same logits (the same read + write volume as the backward)
+    ev[0].record()
+    for _ in range(steps):
+        dz.copy_(z)
+    ev[1].record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * z.numel() * 2 / (ev[0].elapsed_time(ev[1]) / steps * 1e-3) / 1e9
     del z, dz, g, lse, lam
     torch.cuda.empty_cache()
+    traffic = lp_traffic_record()
     return {"step": "compact-to-semantic log-probabilities (mapped cross-entropy) and reused-row gradient",
             "rows": CH, "rows_with_positions": used, "positions": npos, "vocab": V,
             "logits": "bf16", "dz": "bf16",
             "positions_per_row": round(npos / max(used, 1), 3),
             "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+            "torch_copy_gbps": round(copy_gbps, 1),
             "roofline": {"bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
-                         "fwd": {"achieved": round(gf, 1), "frac": round(gf / HBM_PEAK_GBPS, 4), "bytes": b_fwd},
-                         "bwd": {"achieved": round(gb, 1), "frac": round(gb / HBM_PEAK_GBPS, 4), "bytes": b_bwd}}}
+                         "fwd": {"achieved": round(gf, 1), "frac": round(gf / HBM_PEAK_GBPS, 4), "bytes": b_fwd,
+                                 "traffic": traffic.get("fwd")},
+                         "bwd": {"achieved": round(gb, 1), "frac": round(gb / HBM_PEAK_GBPS, 4), "bytes": b_bwd,
+                                 "traffic": traffic.get("bwd")}}}
+
+
+def lp_traffic_record():
+    """HBM bytes per launch of the log-probability kernels from the committed counter summary,
+    if it was taken on the current source; {} otherwise."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_logprob.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "logprob.hip")
+    if rec.get("logprob_hip_sha256_16") != hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]:
+        return {}
+    return {k: v.get("bytes_per_launch") for k, v in rec.get("kernels", {}).items()}
 
 
 def cpu_baseline(spec, plan, budget_s=15.0):
@@ -319,6 +347,8 @@ def main() -> int:
     ap.add_argument("--no-gdn", action="store_true")
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-logprob", action="store_true")
+    ap.add_argument("--logprob-only", action="store_true",
+                    help="only time the log-probability step (for profiling); prints its record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB -> 1 GiB device copy kernel 3 times (scales HBM counters)")
     args = ap.parse_args()
@@ -347,6 +377,9 @@ def main() -> int:
     spec = synth.config3()
     plan = dpa.Plan(spec)
     info = plan.info
+    if args.logprob_only:
+        print(json.dumps({"logprob": logprob_time(dpa, plan, dev, args.steps, args.warmup)}), flush=True)
+        return 0
     log(f"plan: {spec.n_nodes} nodes, {info['tokens']} tokens, {info['rows']} rows, P={info['visible_pairs']}, "
         f"built in {time.perf_counter() - t0:.1f} s")
     p = dpa.AttnParams(HQ, HKV, D, "bf16")

@@ -43,9 +43,14 @@ __device__ __forceinline__ void st1(float* p, float x) { *p = x; }
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Rows are touched once: stream them past the caches both ways.
 __device__ __forceinline__ uint4 ld_stream(const uint4* p) {
   const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void st_stream(void* p, uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  const u32x4 v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
 // elements of one 16-byte load
@@ -71,12 +76,10 @@ template <typename TG, int n>
 __device__ __forceinline__ void store_vec(TG* p, const float* d);
 template <>
 __device__ __forceinline__ void store_vec<uint16_t, 8>(uint16_t* p, const float* d) {
-  uint4 w;
-  w.x = (uint32_t)to_bf(d[0]) | ((uint32_t)to_bf(d[1]) << 16);
-  w.y = (uint32_t)to_bf(d[2]) | ((uint32_t)to_bf(d[3]) << 16);
-  w.z = (uint32_t)to_bf(d[4]) | ((uint32_t)to_bf(d[5]) << 16);
-  w.w = (uint32_t)to_bf(d[6]) | ((uint32_t)to_bf(d[7]) << 16);
-  *reinterpret_cast<uint4*>(p) = w;
+  st_stream(p, (uint32_t)to_bf(d[0]) | ((uint32_t)to_bf(d[1]) << 16),
+            (uint32_t)to_bf(d[2]) | ((uint32_t)to_bf(d[3]) << 16),
+            (uint32_t)to_bf(d[4]) | ((uint32_t)to_bf(d[5]) << 16),
+            (uint32_t)to_bf(d[6]) | ((uint32_t)to_bf(d[7]) << 16));
 }
 template <>
 __device__ __forceinline__ void store_vec<uint16_t, 4>(uint16_t* p, const float* d) {
@@ -87,12 +90,12 @@ __device__ __forceinline__ void store_vec<uint16_t, 4>(uint16_t* p, const float*
 }
 template <>
 __device__ __forceinline__ void store_vec<float, 8>(float* p, const float* d) {
-  reinterpret_cast<float4*>(p)[0] = make_float4(d[0], d[1], d[2], d[3]);
-  reinterpret_cast<float4*>(p)[1] = make_float4(d[4], d[5], d[6], d[7]);
+  st_stream(p, __float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]), __float_as_uint(d[3]));
+  st_stream(p + 4, __float_as_uint(d[4]), __float_as_uint(d[5]), __float_as_uint(d[6]), __float_as_uint(d[7]));
 }
 template <>
 __device__ __forceinline__ void store_vec<float, 4>(float* p, const float* d) {
-  *reinterpret_cast<float4*>(p) = make_float4(d[0], d[1], d[2], d[3]);
+  st_stream(p, __float_as_uint(d[0]), __float_as_uint(d[1]), __float_as_uint(d[2]), __float_as_uint(d[3]));
 }
 
 // Running (max m, sum s of exp(x - m)).  m = -inf with s = 0 is the empty state.
