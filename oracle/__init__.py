@@ -28,10 +28,14 @@ rounding order):
 * ``logprob``   -- compact-to-semantic log-probabilities (HARTS Eq. 17) on
                    expanded per-position rows, the semantic position map of
                    the original batch, and the reused-row gradient (Eq. 19-20).
+* ``conv``      -- the short causal convolution of a linear-attention block
+                   along each trajectory's own tokens (mounted spans skipped),
+                   one output per compact token, gradients summed over readers.
 
 Parity unpinned: the RoPE pairing convention (first half / second half of the
 head dimension) and the frequency base (10000) are a textbook choice the pages
 do not fix; both sides take them as parameters.  Likewise the gated delta
 rule's parameterisation and its output scale (default 1): the pages name the
-layer but print no recurrence for it.
+layer but print no recurrence for it.  And the short convolution's activation
+(identity or SiLU, a parameter) and tap order.
 """
