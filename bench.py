@@ -23,6 +23,8 @@ Printed JSON (one line on stdout; progress goes to stderr):
               on the same DAG, forward and backward: milliseconds, the schedule's
               rounds / sequences / replayed tokens, and executed MFMA TFLOP/s;
               hybrid_step_ms = the attention step + 3 such layers (the hybrid stack)
+  conv        the GDN block's short causal convolution (width 4, SiLU) over q, k and v
+              (6,144 channels) on the same tree: ms and GB/s against 8 TB/s
   logprob     compact-to-semantic log-probabilities and their gradient on 65,536 rows
               of the workload's semantic map, V = 131,072: ms and GB/s against 8 TB/s,
               with torch's copy of the same logits (the backward's read + write volume)
@@ -238,6 +240,53 @@ def logprob_time(dpa, plan, dev, steps, warmup):
                                  "traffic": traffic.get("bwd")}}}
 
 
+CONV_CH, CONV_W = 6144, 4
+
+
+def conv_time(dpa, plan, dev, steps, warmup):
+    """The gated-delta-rule block's short causal convolution on the workload's tree:
+    q, k and v of 16 heads x 128 side by side (6,144 channels), width 4, SiLU, bf16
+    in and out.  Algorithmic HBM bytes: the forward reads x once for the U token rows
+    and writes y for all C rows (padding rows are written as zero); the backward reads
+    x and dy once and writes dx for all C rows."""
+    import torch
+    C, U, Ch = plan.rows, plan.tokens, CONV_CH
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(51)
+    x = torch.empty((C, Ch), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+    dy = torch.empty((C, Ch), dtype=torch.bfloat16, device=dev).normal_(generator=gen)
+    W = torch.empty((Ch, CONV_W), dtype=torch.float32, device=dev).normal_(generator=gen).mul_(0.5)
+    p = dpa.ConvParams(Ch, CONV_W, "silu", "bf16")
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    dW = torch.empty_like(W)
+    ws = torch.empty(max(dpa.conv_workspace_bytes(plan, p), 16), dtype=torch.uint8, device=dev)
+    plan.upload()
+    for _ in range(warmup):
+        dpa.conv_fwd(plan, p, x, W, y=y)
+        dpa.conv_bwd(plan, p, x, W, dy, dx=dx, dweight=dW, ws=ws)
+    torch.cuda.synchronize()
+    plan.timing_enable(True, capacity=4 * (steps + 1))
+    for _ in range(steps):
+        dpa.conv_fwd(plan, p, x, W, y=y)
+        dpa.conv_bwd(plan, p, x, W, dy, dx=dx, dweight=dW, ws=ws)
+    kt = plan.timing_read()
+    plan.timing_enable(False)
+    fwd_ms = kt["conv_fwd"][0] / max(kt["conv_fwd"][1], 1)
+    bwd_ms = kt["conv_bwd"][0] / max(kt["conv_bwd"][1], 1)
+    b_fwd = 2 * Ch * (U + C)
+    b_bwd = 2 * Ch * (2 * U + C)
+    gf, gb = b_fwd / (fwd_ms * 1e-3) / 1e9, b_bwd / (bwd_ms * 1e-3) / 1e9
+    del x, dy, W, y, dx, dW, ws
+    torch.cuda.empty_cache()
+    return {"step": "short causal convolution with true-ancestor context (q, k, v of the GDN block)",
+            "channels": Ch, "width": CONV_W, "activation": "silu", "rows": C, "tokens": U,
+            "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
+            "roofline": {"bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
+                         "fwd": {"achieved": round(gf, 1), "frac": round(gf / HBM_PEAK_GBPS, 4), "bytes": b_fwd},
+                         "bwd": {"achieved": round(gb, 1), "frac": round(gb / HBM_PEAK_GBPS, 4), "bytes": b_bwd}}}
+
+
 def lp_traffic_record():
     """HBM bytes per launch of the log-probability kernels from the committed counter summary,
     if it was taken on the current source; {} otherwise."""
@@ -349,6 +398,9 @@ def main() -> int:
     ap.add_argument("--no-logprob", action="store_true")
     ap.add_argument("--logprob-only", action="store_true",
                     help="only time the log-probability step (for profiling); prints its record")
+    ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--conv-only", action="store_true",
+                    help="only time the short convolution (for profiling); prints its record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB -> 1 GiB device copy kernel 3 times (scales HBM counters)")
     args = ap.parse_args()
@@ -379,6 +431,9 @@ def main() -> int:
     info = plan.info
     if args.logprob_only:
         print(json.dumps({"logprob": logprob_time(dpa, plan, dev, args.steps, args.warmup)}), flush=True)
+        return 0
+    if args.conv_only:
+        print(json.dumps({"conv": conv_time(dpa, plan, dev, args.steps, args.warmup)}), flush=True)
         return 0
     log(f"plan: {spec.n_nodes} nodes, {info['tokens']} tokens, {info['rows']} rows, P={info['visible_pairs']}, "
         f"built in {time.perf_counter() - t0:.1f} s")
@@ -440,6 +495,11 @@ def main() -> int:
         out["gdn"] = g
         log(f"gdn layer: fwd {g['fwd_ms']:.2f} ms, bwd {g['bwd_ms']:.2f} ms ({g['rounds']} rounds, "
             f"{g['sequences']} sequences); hybrid step {g['hybrid_step_ms']:.1f} ms")
+    if not args.no_conv:
+        cv = conv_time(dpa, plan, dev, max(1, min(args.steps, 5)), 1)
+        out["conv"] = cv
+        log(f"conv: fwd {cv['fwd_ms']:.2f} ms ({cv['roofline']['fwd']['achieved']:.0f} GB/s), "
+            f"bwd {cv['bwd_ms']:.2f} ms ({cv['roofline']['bwd']['achieved']:.0f} GB/s)")
     if not args.no_logprob:
         lp = logprob_time(dpa, plan, dev, max(1, min(args.steps, 5)), 1)
         out["logprob"] = lp

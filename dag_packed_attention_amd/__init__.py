@@ -9,7 +9,8 @@ importing this package fails.
 Names follow the C ABI: :class:`Plan` wraps ``dag_build`` and the plan
 queries, :func:`attn_fwd` / :func:`attn_bwd` wrap ``dag_attn_fwd`` /
 ``dag_attn_bwd``; :func:`gdn_fwd` / :func:`gdn_bwd` and :func:`logprob_fwd` /
-:func:`logprob_bwd` likewise, with :meth:`Plan.logprob_map` for the position map.
+:func:`logprob_bwd` likewise, with :meth:`Plan.logprob_map` for the position map, and
+:func:`conv_fwd` / :func:`conv_bwd` for the short causal convolution.
 """
 from __future__ import annotations
 
@@ -75,6 +76,11 @@ class DagLogprobParams(ctypes.Structure):
                 ("dtype", ctypes.c_int32), ("grad_dtype", ctypes.c_int32)]
 
 
+class DagConvParams(ctypes.Structure):
+    _fields_ = [("channels", ctypes.c_int32), ("width", ctypes.c_int32), ("activation", ctypes.c_int32),
+                ("grad_dtype", ctypes.c_int32)]
+
+
 class DagError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
@@ -111,6 +117,9 @@ def _load() -> ctypes.CDLL:
         "dag_plan_logprob_map": ([P, P, I64, P, P, P, P, ctypes.POINTER(I64)], I32),
         "dag_logprob_fwd": ([ctypes.POINTER(DagLogprobParams), P, P, P, P, P, P, P], I32),
         "dag_logprob_bwd": ([ctypes.POINTER(DagLogprobParams), P, P, P, P, P, P, P, P], I32),
+        "dag_conv_workspace": ([P, ctypes.POINTER(DagConvParams), ctypes.POINTER(SZ)], I32),
+        "dag_conv_fwd": ([P, ctypes.POINTER(DagConvParams), P, P, P, P], I32),
+        "dag_conv_bwd": ([P, ctypes.POINTER(DagConvParams), P, P, P, P, P, P, SZ, P], I32),
         "dag_attn_timing_enable": ([P, I32, I32], I32),
         "dag_attn_timing_read": ([P, P, P], I32),
         "dag_last_error": ([], ctypes.c_char_p),
@@ -230,7 +239,8 @@ class Plan:
     def upload(self, stream=None) -> None:
         _check(_lib.dag_plan_upload(self._h, _stream_ptr(stream)))
 
-    KERNELS = ("prologue_fwd", "fwd", "prologue_bwd", "dkdv", "dq", "gdn_fwd", "gdn_states", "gdn_bwd")
+    KERNELS = ("prologue_fwd", "fwd", "prologue_bwd", "dkdv", "dq", "gdn_fwd", "gdn_states", "gdn_bwd",
+               "conv_fwd", "conv_bwd")
 
     def timing_enable(self, enable: bool = True, capacity: int = 256) -> None:
         """Record HIP events around each kernel the library launches for this plan."""
@@ -431,6 +441,68 @@ def gdn_bwd(plan: Plan, p: GdnParams, q, k, v, beta, alpha, dO, ws=None, stream=
 
 
 # ---------------------------------------------------------------------------
+# short causal convolution
+# ---------------------------------------------------------------------------
+
+ACT_NONE, ACT_SILU = 0, 1
+
+
+@dataclass
+class ConvParams:
+    channels: int
+    width: int = 4
+    activation: str = "silu"         # "none" or "silu"
+    grad_dtype: str = "bf16"         # dx element type: "bf16" or "fp32"
+
+    def c(self) -> DagConvParams:
+        a = {"none": ACT_NONE, "silu": ACT_SILU}[self.activation]
+        return DagConvParams(self.channels, self.width, a, {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}[self.grad_dtype])
+
+
+def conv_workspace_bytes(plan: Plan, p: ConvParams) -> int:
+    b = ctypes.c_size_t(0)
+    cp = p.c()
+    _check(_lib.dag_conv_workspace(plan._h, ctypes.byref(cp), ctypes.byref(b)))
+    return int(b.value)
+
+
+def _check_conv(name, t, rows, ch, dtype, device):
+    if t.dtype != dtype or tuple(t.shape) != (rows, ch) or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"{name}: expected contiguous {dtype} [{rows}, {ch}] on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def conv_fwd(plan: Plan, p: ConvParams, x, weight, y=None, stream=None):
+    """``dag_conv_fwd``: x [C, Ch] bf16, weight [Ch, w] fp32 -> y [C, Ch] bf16."""
+    import torch
+    _check_conv("x", x, plan.rows, p.channels, torch.bfloat16, x.device)
+    _check_conv("weight", weight, p.channels, p.width, torch.float32, x.device)
+    if y is None:
+        y = torch.empty_like(x)
+    cp = p.c()
+    _check(_lib.dag_conv_fwd(plan._h, ctypes.byref(cp), _ptr(x), _ptr(weight), _ptr(y), _stream_ptr(stream)))
+    return y
+
+
+def conv_bwd(plan: Plan, p: ConvParams, x, weight, dy, dx=None, dweight=None, ws=None, stream=None):
+    """``dag_conv_bwd``: returns (dx [C, Ch] grad_dtype, dweight [Ch, w] fp32)."""
+    import torch
+    _check_conv("x", x, plan.rows, p.channels, torch.bfloat16, x.device)
+    _check_conv("dy", dy, plan.rows, p.channels, torch.bfloat16, x.device)
+    _check_conv("weight", weight, p.channels, p.width, torch.float32, x.device)
+    if dx is None:
+        dx = torch.empty(x.shape, dtype=torch.bfloat16 if p.grad_dtype == "bf16" else torch.float32, device=x.device)
+    if dweight is None:
+        dweight = torch.empty_like(weight)
+    if ws is None:
+        ws = torch.empty(max(conv_workspace_bytes(plan, p), 16), dtype=torch.uint8, device=x.device)
+    cp = p.c()
+    _check(_lib.dag_conv_bwd(plan._h, ctypes.byref(cp), _ptr(x), _ptr(weight), _ptr(dy), _ptr(dx), _ptr(dweight),
+                             _ptr(ws), ws.numel(), _stream_ptr(stream)))
+    return dx, dweight
+
+
+# ---------------------------------------------------------------------------
 # compact-to-semantic log-probabilities
 # ---------------------------------------------------------------------------
 
@@ -509,5 +581,6 @@ def from_rows(plan: Plan, x_rows):
 
 
 __all__ = ["Plan", "AttnParams", "GdnParams", "DagError", "attn_fwd", "attn_bwd", "workspace_bytes", "gdn_fwd",
-           "gdn_bwd", "gdn_workspace_bytes", "logprob_fwd", "logprob_bwd", "to_rows", "from_rows", "last_error",
+           "gdn_bwd", "gdn_workspace_bytes", "ConvParams", "conv_fwd", "conv_bwd", "conv_workspace_bytes",
+           "logprob_fwd", "logprob_bwd", "to_rows", "from_rows", "last_error",
            "LIB_PATH"]

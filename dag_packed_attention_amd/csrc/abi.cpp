@@ -9,6 +9,7 @@
 #include <string>
 #include <vector>
 
+#include "conv.hpp"
 #include "gdn.hpp"
 #include "launch.hpp"
 #include "logprob.hpp"
@@ -47,6 +48,10 @@ struct DeviceTables {
   int32_t* grep_off = nullptr;
   int32_t* grep_tok = nullptr;
   int32_t* grep_slot = nullptr;
+  // short convolution
+  int32_t* conv_prev = nullptr;
+  int64_t* conv_ext_off = nullptr;
+  ConvExt* conv_ext = nullptr;
 };
 
 struct Timing {
@@ -196,7 +201,8 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
            align256(P.grows.size() * 4) + align256(P.gexports.size() * sizeof(GExport)) +
            align256(P.gslot_off.size() * 4) + align256(P.gslot_cons.size() * 4) + align256(P.ground_seq.size() * 4) +
            align256(P.grep_rows.size() * 4) + align256(P.grep_off.size() * 4) + align256(P.grep_tok.size() * 4) +
-           align256(P.grep_slot.size() * 4) + 256;
+           align256(P.grep_slot.size() * 4) + align256(P.conv_prev.size() * 4) +
+           align256(P.conv_ext_off.size() * 8) + align256(P.conv_ext.size() * sizeof(ConvExt)) + 256;
   DeviceTables* D = new (std::nothrow) DeviceTables();
   if (!D) return set_err(DAG_E_DEVICE, "out of host memory");
   D->device = dev;
@@ -230,6 +236,9 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
   D->grep_off = dev_take<int32_t>(b, off, P.grep_off.size());
   D->grep_tok = dev_take<int32_t>(b, off, P.grep_tok.size());
   D->grep_slot = dev_take<int32_t>(b, off, P.grep_slot.size());
+  D->conv_prev = dev_take<int32_t>(b, off, P.conv_prev.size());
+  D->conv_ext_off = dev_take<int64_t>(b, off, P.conv_ext_off.size());
+  D->conv_ext = dev_take<ConvExt>(b, off, P.conv_ext.size());
   auto put = [&](void* dst, const void* src, size_t n) {
     return n == 0 || hipMemcpyAsync(dst, src, n, hipMemcpyHostToDevice, st) == hipSuccess;
   };
@@ -255,7 +264,10 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
             put(D->grep_rows, P.grep_rows.data(), P.grep_rows.size() * 4) &&
             put(D->grep_off, P.grep_off.data(), P.grep_off.size() * 4) &&
             put(D->grep_tok, P.grep_tok.data(), P.grep_tok.size() * 4) &&
-            put(D->grep_slot, P.grep_slot.data(), P.grep_slot.size() * 4);
+            put(D->grep_slot, P.grep_slot.data(), P.grep_slot.size() * 4) &&
+            put(D->conv_prev, P.conv_prev.data(), P.conv_prev.size() * 4) &&
+            put(D->conv_ext_off, P.conv_ext_off.data(), P.conv_ext_off.size() * 8) &&
+            put(D->conv_ext, P.conv_ext.data(), P.conv_ext.size() * sizeof(ConvExt));
   // the host vectors are pageable: finish the copies before returning
   ok = ok && hipStreamSynchronize(st) == hipSuccess;
   if (!ok) {
@@ -817,6 +829,81 @@ dag_status dag_logprob_bwd(const dag_logprob_params* p, const void* z, const flo
                                   stream);
   }
   return launched("dag_logprob_bwd");
+}
+
+// ---- short causal convolution ------------------------------------------------------
+namespace {
+dag_status check_conv(const dag_conv_params* p) {
+  if (!p) return set_err(DAG_E_INVALID, "null params");
+  if (p->channels < 8 || p->channels % 8) return set_err(DAG_E_UNSUPPORTED, "channels must be a positive multiple of 8");
+  if (p->width < 1 || p->width > 4) return set_err(DAG_E_UNSUPPORTED, "width must be 1..4");
+  if (p->activation != DAG_ACT_NONE && p->activation != DAG_ACT_SILU)
+    return set_err(DAG_E_UNSUPPORTED, "activation must be DAG_ACT_NONE or DAG_ACT_SILU");
+  if (p->grad_dtype != DAG_DTYPE_BF16 && p->grad_dtype != DAG_DTYPE_FP32)
+    return set_err(DAG_E_UNSUPPORTED, "grad_dtype must be DAG_DTYPE_BF16 or DAG_DTYPE_FP32");
+  return DAG_OK;
+}
+size_t conv_ws_bytes(const Plan& P, const dag_conv_params* p) {
+  return P.info.pages ? (size_t)conv_bwd_blocks(P.info.pages) * p->channels * 4 * sizeof(float) : 0;
+}
+bool aligned16(const void* x) { return (reinterpret_cast<uintptr_t>(x) & 15) == 0; }
+}  // namespace
+
+dag_status dag_conv_workspace(const dag_plan* plan, const dag_conv_params* p, size_t* bwd_bytes) {
+  if (!plan || !bwd_bytes) return set_err(DAG_E_INVALID, "null argument");
+  dag_status st = check_conv(p);
+  if (st != DAG_OK) return st;
+  *bwd_bytes = conv_ws_bytes(plan->p, p);
+  return DAG_OK;
+}
+
+dag_status dag_conv_fwd(dag_plan* plan, const dag_conv_params* p, const void* x, const float* weight, void* y,
+                        void* hip_stream) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  Plan& P = plan->p;
+  dag_status st = check_conv(p);
+  if (st != DAG_OK) return st;
+  if (P.info.rows == 0) return DAG_OK;
+  if (!x || !weight || !y) return set_err(DAG_E_INVALID, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(y)) return set_err(DAG_E_INVALID, "x and y must be 16-byte aligned");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if ((st = ensure_uploaded(P, stream)) != DAG_OK) return st;
+  {
+    Span sp(P, DAG_K_CONV_FWD, stream);
+    launch_conv_fwd((const uint16_t*)x, weight, p->channels, p->width, p->activation, P.dev->page_nrows,
+                    P.dev->conv_prev, P.info.pages, (uint16_t*)y, stream);
+  }
+  return launched("dag_conv_fwd");
+}
+
+dag_status dag_conv_bwd(dag_plan* plan, const dag_conv_params* p, const void* x, const float* weight,
+                        const void* dy, void* dx, float* dweight, void* ws, size_t ws_bytes, void* hip_stream) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  Plan& P = plan->p;
+  dag_status st = check_conv(p);
+  if (st != DAG_OK) return st;
+  if (P.info.rows == 0) return DAG_OK;
+  if (!x || !weight || !dy || !dx || !dweight) return set_err(DAG_E_INVALID, "null tensor pointer");
+  if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(ws))
+    return set_err(DAG_E_INVALID, "x, dy, dx and the workspace must be 16-byte aligned");
+  const size_t need = conv_ws_bytes(P, p);
+  if (!ws || ws_bytes < need)
+    return set_err(DAG_E_WORKSPACE, "convolution backward workspace needs " + std::to_string(need) + " bytes");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if ((st = ensure_uploaded(P, stream)) != DAG_OK) return st;
+  const DeviceTables& D = *P.dev;
+  {
+    Span sp(P, DAG_K_CONV_BWD, stream);
+    if (p->grad_dtype == DAG_DTYPE_FP32)
+      launch_conv_bwd<float>((const uint16_t*)x, (const uint16_t*)dy, weight, p->channels, p->width, p->activation,
+                             D.page_nrows, D.conv_prev, D.conv_ext_off, D.conv_ext, P.info.pages, (float*)dx, dweight,
+                             (float*)ws, stream);
+    else
+      launch_conv_bwd<uint16_t>((const uint16_t*)x, (const uint16_t*)dy, weight, p->channels, p->width,
+                                p->activation, D.page_nrows, D.conv_prev, D.conv_ext_off, D.conv_ext, P.info.pages,
+                                (uint16_t*)dx, dweight, (float*)ws, stream);
+  }
+  return launched("dag_conv_bwd");
 }
 
 }  // extern "C"

@@ -463,6 +463,8 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
   }
   for (const QPage& q : P->qpages) I.fwd_tiles += q.tile_count;
   I.bwd_entries = (int64_t)P->kentries.size();
+  const dag_status cst = build_conv_tables(P, err);
+  if (cst != DAG_OK) return cst;
   if (opts.gdn_chunk > 0) return build_gdn_schedule(P, opts.gdn_chunk, err);
   return DAG_OK;
 }

@@ -52,6 +52,13 @@ struct KStep {
   int32_t info;  // rb | loA << 1 | hiA << 8 | diagA << 15 | loB << 17 | hiB << 24 | diagB << 31
 };
 
+// A token within 3 steps after a page's last token on some path, with the rows
+// 1, 2 and 3 steps before it on its own path (-1: none); the short convolution's
+// backward reads these successors.
+struct ConvExt {
+  int32_t s, p1, p2, p3;
+};
+
 // One packed gated-delta-rule input sequence as the kernels read it.  Its
 // tokens are rows[tok_off .. tok_off + n_tok): n_replay replayed ancestor
 // tokens (state updates only), then its own tokens.  Token j sits at
@@ -100,6 +107,10 @@ struct Plan {
   std::vector<int64_t> kpair_off;              // pair -> its first merged reader step (size pairs+1)
   std::vector<KStep> kpsteps;                  // merged reader steps of every pair
   std::vector<int32_t> pair_order;             // pair ids, node-grouped, heaviest first
+  // short causal convolution (see conv_plan.cpp)
+  std::vector<int32_t> conv_prev;              // 4 per physical page: rows 1..3 steps before its first token
+  std::vector<int64_t> conv_ext_off;           // physical page -> first successor entry (size pages+1)
+  std::vector<ConvExt> conv_ext;
   std::vector<int32_t> pos_of_row;             // C
   std::vector<int32_t> row_of_token;           // U
   // gated-delta-rule schedule (empty when opts.gdn_chunk == 0)
@@ -121,6 +132,9 @@ struct Plan {
 // Compile; returns DAG_OK or an error code with a message in `err`.
 dag_status build_plan(const dag_node* nodes, int32_t n_nodes, const dag_mount* mounts,
                       int32_t n_mounts, const dag_build_opts* opts, Plan* out, std::string* err);
+
+// Short-convolution tables (HARTS Sec. 4.2) over the plan's parent tree and rows.
+dag_status build_conv_tables(Plan* P, std::string* err);
 
 // Linear-attention schedule (HARTS Sec. 3.3) over the plan's parent tree;
 // needs the plan's rows (row_of_token) to be built.

@@ -323,10 +323,46 @@ dag_status dag_logprob_bwd(const dag_logprob_params* p, const void* z, const flo
                            const int32_t* row_pos, const int32_t* pos_target, const float* g, void* dz,
                            void* hip_stream);
 
+/* ---- short causal convolution of a linear-attention block -------------------
+ *
+ * HARTS Sec. 4.2 and Octopus App. C: the depthwise causal convolution in front of
+ * a gated-delta-rule layer takes its history only from a token's true
+ * ancestors, i.e. its own root-to-node path with mounted spans skipped; one
+ * result is kept per compact token, and the input gradient of a token sums the
+ * contributions of every output that reads it, on every branch below it.  Per
+ * channel c with taps W[c, 0..w-1] (the last one multiplies the current token):
+ *   pre_t = sum_{k<w} W[c, w-1-k] x_{t-k}   (x = 0 before a root),
+ *   y_t = act(pre_t),   act = identity or SiLU(p) = p / (1 + e^-p).
+ * The pages name the operator but print neither its activation nor its tap
+ * order; both are this textbook form. */
+enum { DAG_ACT_NONE = 0, DAG_ACT_SILU = 1 };
+
+typedef struct {
+  int32_t channels;    /* Ch: a multiple of 8 (e.g. the q, k and v projections side by side) */
+  int32_t width;       /* w, 1..4                                                          */
+  int32_t activation;  /* DAG_ACT_NONE or DAG_ACT_SILU                                     */
+  int32_t grad_dtype;  /* dx: DAG_DTYPE_BF16 or DAG_DTYPE_FP32                             */
+} dag_conv_params;
+
+/* Workspace bytes of dag_conv_bwd (per-block dW partials). */
+dag_status dag_conv_workspace(const dag_plan* plan, const dag_conv_params* p, size_t* bwd_bytes);
+
+/* Forward: x [C, Ch] bf16 (row layout), weight [Ch, w] fp32 -> y [C, Ch] bf16
+ * (padding rows zero).  fp32 arithmetic, one rounding per output. */
+dag_status dag_conv_fwd(dag_plan* plan, const dag_conv_params* p, const void* x, const float* weight, void* y,
+                        void* hip_stream);
+
+/* Backward given dy [C, Ch] bf16: dx [C, Ch] (grad_dtype; padding rows zero) and
+ * dweight [Ch, w] fp32 (written, not accumulated).  The forward's pre-activation
+ * is recomputed; every sum has a fixed order (bitwise reproducible, no atomics).
+ * ws: at least the bytes dag_conv_workspace reports. */
+dag_status dag_conv_bwd(dag_plan* plan, const dag_conv_params* p, const void* x, const float* weight,
+                        const void* dy, void* dx, float* dweight, void* ws, size_t ws_bytes, void* hip_stream);
+
 /* Per-kernel timing, for profiling.  While enabled, dag_attn_fwd/bwd record a
  * HIP event pair on their stream around each of their kernels (at most
  * `capacity` pairs, created here; later launches go unrecorded).
- * The same holds for dag_gdn_fwd/bwd.
+ * The same holds for dag_gdn_fwd/bwd and dag_conv_fwd/bwd.
  * dag_attn_timing_read waits for the recorded events, writes for each kernel
  * k in dag_kernel_id the summed duration ms[k] (milliseconds) and the number of
  * launches counts[k] since the last read, and resets.  Disabling (enable = 0)
@@ -340,7 +376,9 @@ enum {
   DAG_K_GDN_FWD = 5,      /* gated delta rule forward, all rounds                  */
   DAG_K_GDN_STATES = 6,   /* backward's recomputation of chunk and boundary states */
   DAG_K_GDN_BWD = 7,      /* gated delta rule backward, all rounds, and replay fix-up */
-  DAG_K_COUNT = 8
+  DAG_K_CONV_FWD = 8,     /* short convolution forward                             */
+  DAG_K_CONV_BWD = 9,     /* short convolution backward and its dW reduction       */
+  DAG_K_COUNT = 10
 };
 dag_status dag_attn_timing_enable(dag_plan* plan, int32_t enable, int32_t capacity);
 dag_status dag_attn_timing_read(dag_plan* plan, double* ms, int64_t* counts);

@@ -133,3 +133,60 @@ def conv_paths(spec, x, W, act: int, dy_per_path: Optional[list] = None):
         np.add.at(dx, ids, a)
         dW += b
     return dx, dW
+
+
+def path_pred(spec) -> np.ndarray:
+    """pred[t]: the token before t on t's own root-to-node path (mounts skipped), -1 at a root's start."""
+    dag = Dag(spec)
+    pred = np.full(dag.n_tokens, -1, np.int64)
+    for u in range(dag.n):
+        o, ln = dag.offset[u], dag.length[u]
+        if ln == 0:
+            continue
+        pred[o + 1:o + ln] = np.arange(o, o + ln - 1)
+        a = dag.parent[u]
+        while a >= 0 and dag.length[a] == 0:
+            a = dag.parent[a]
+        pred[o] = dag.offset[a] + dag.length[a] - 1 if a >= 0 else -1
+    return pred
+
+
+def conv_compact(spec, x, W, act: int = ACT_NONE, dy=None) -> Dict[str, np.ndarray]:
+    """The same results as ``conv_flat`` evaluated once per compact token.
+
+    A token's window is the last w tokens of its own path, the same on every
+    trajectory that holds it, so y is a sum over its path predecessors; the input
+    gradient scatters each output's dpre back onto the tokens of its window.
+    Vectorised one channel at a time (usable on the full workloads for a few
+    channels); a missing predecessor reads a zero appended after the last token.
+    """
+    x = np.asarray(x, np.float64)
+    W = np.asarray(W, np.float64)
+    U, Ch = x.shape
+    w = W.shape[1]
+    p1 = np.append(path_pred(spec), -1)
+    p1[p1 < 0] = U                               # index U holds the zero
+    preds = [np.arange(U)]
+    for _ in range(1, w):
+        preds.append(p1[preds[-1]])
+    y = np.zeros_like(x)
+    out = {"y": y}
+    if dy is not None:
+        dy = np.asarray(dy, np.float64)
+        out["dx"] = np.zeros_like(x)
+        out["dW"] = np.zeros(W.shape)
+    for c in range(Ch):
+        xc = np.append(x[:, c], 0.0)
+        pre = np.zeros(U)
+        for k, q in enumerate(preds):
+            pre += W[c, w - 1 - k] * xc[q]
+        y[:, c] = _act(pre, act)
+        if dy is None:
+            continue
+        dpre = dy[:, c] * _act_grad(pre, act)
+        dxc = np.zeros(U + 1)
+        for k, q in enumerate(preds):
+            dxc += np.bincount(q, weights=W[c, w - 1 - k] * dpre, minlength=U + 1)
+            out["dW"][c, w - 1 - k] = dpre @ xc[q]
+        out["dx"][:, c] = dxc[:U]
+    return out

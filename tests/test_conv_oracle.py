@@ -157,3 +157,18 @@ def test_compact_gradient_is_sum_over_semantic_positions():
     out = CV.conv_flat(spec, x, W, CV.ACT_NONE, dy)
     np.testing.assert_allclose(out["dx"], dx, rtol=0, atol=1e-12)
     np.testing.assert_allclose(out["dW"], dW, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_compact_evaluation_equals_per_trajectory(seed):
+    rng = np.random.default_rng(40 + seed)
+    spec = D.random_tiny_dag(rng, n_nodes=int(rng.integers(2, 12)), max_len=int(rng.integers(1, 9)),
+                             p_mount=0.5, max_mounts=2, n_roots=int(rng.integers(1, 3)))
+    w = int(rng.integers(1, 5))
+    x = rng.standard_normal((spec.n_tokens, 3))
+    W = rng.standard_normal((3, w))
+    dy = rng.standard_normal((spec.n_tokens, 3))
+    for act in (CV.ACT_NONE, CV.ACT_SILU):
+        a, b = CV.conv_flat(spec, x, W, act, dy), CV.conv_compact(spec, x, W, act, dy)
+        for k in a:
+            np.testing.assert_allclose(b[k], a[k], rtol=0, atol=1e-12)

@@ -167,9 +167,10 @@ def test_host_compactor_under_sanitizers(tmp_path):
     exe = tmp_path / "plan_san"
     src = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "plan.cpp")
     gsrc = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "gdn_plan.cpp")
+    csrc = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "conv_plan.cpp")
     drv = os.path.join(ROOT, "tests", "host", "plan_driver.cpp")
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
-           f"-I{os.path.join(ROOT, 'include')}", src, gsrc, drv, "-o", str(exe)]
+           f"-I{os.path.join(ROOT, 'include')}", src, gsrc, csrc, drv, "-o", str(exe)]
     subprocess.run(cmd, check=True, capture_output=True)
     r = subprocess.run([str(exe), "300"], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
