@@ -10,7 +10,7 @@
 // its node, and the first rows of every branch below it) of W[c, w-1-d(s,t)] dpre_s;
 // dW[c, w-1-k] = sum_t dpre_t x_{t-k}.
 //
-// Work split: one 64-row page per block (and 2048 channels, 8 per thread, 16-byte
+// Work split: one 64-row page per block (and 1,024 channels, 4 per thread, 8-byte
 // loads).  The forward walks the page's rows with the previous three inputs in
 // registers, starting from the three path predecessors of the page's first token
 // (conv_prev).  The backward walks the rows downwards with the window of inputs
@@ -30,27 +30,37 @@ namespace dagattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kChan = 8 * kThreads;  // channels per block
+constexpr int kNV = 4;                   // channels per thread (8-byte bf16 loads)
+constexpr int kChan = kNV * kThreads;    // channels per block
 constexpr float kL2e = 1.4426950408889634f;
 
-struct F8 {
-  float v[8];
+// kNV channels of one row: bf16 bits as loaded (B) and as fp32 values (F)
+struct B {
+  uint32_t w[kNV / 2];
+};
+struct F {
+  float v[kNV];
 };
 
-__device__ __forceinline__ F8 zero8() {
-  F8 r;
+__device__ __forceinline__ F zeroF() {
+  F r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r.v[i] = 0.f;
+  for (int i = 0; i < kNV; ++i) r.v[i] = 0.f;
+  return r;
+}
+__device__ __forceinline__ B zeroB() {
+  B r;
+#pragma unroll
+  for (int i = 0; i < kNV / 2; ++i) r.w[i] = 0;
   return r;
 }
 
-__device__ __forceinline__ F8 unpack8(uint4 w) {
-  F8 r;
-  const uint32_t a[4] = {w.x, w.y, w.z, w.w};
+__device__ __forceinline__ F unpack(const B& b) {
+  F r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r.v[2 * i] = __uint_as_float(a[i] << 16);
-    r.v[2 * i + 1] = __uint_as_float(a[i] & 0xffff0000u);
+  for (int i = 0; i < kNV / 2; ++i) {
+    r.v[2 * i] = __uint_as_float(b.w[i] << 16);
+    r.v[2 * i + 1] = __uint_as_float(b.w[i] & 0xffff0000u);
   }
   return r;
 }
@@ -60,19 +70,31 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) {
   return (uint32_t)(*reinterpret_cast<uint16_t*>(&b));
 }
 
-__device__ __forceinline__ uint4 load8(const uint16_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-__device__ __forceinline__ void store8(uint16_t* p, const F8& d) {
-  uint4 w;
-  w.x = bf16_bits(d.v[0]) | (bf16_bits(d.v[1]) << 16);
-  w.y = bf16_bits(d.v[2]) | (bf16_bits(d.v[3]) << 16);
-  w.z = bf16_bits(d.v[4]) | (bf16_bits(d.v[5]) << 16);
-  w.w = bf16_bits(d.v[6]) | (bf16_bits(d.v[7]) << 16);
-  *reinterpret_cast<uint4*>(p) = w;
+__device__ __forceinline__ B loadB(const uint16_t* p) {
+  B r;
+  if constexpr (kNV == 8) {
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    r.w[0] = q.x; r.w[1] = q.y; r.w[2] = q.z; r.w[3] = q.w;
+  } else {
+    const uint2 q = *reinterpret_cast<const uint2*>(p);
+    r.w[0] = q.x; r.w[1] = q.y;
+  }
+  return r;
 }
-__device__ __forceinline__ void store8(float* p, const F8& d) {
-  reinterpret_cast<float4*>(p)[0] = make_float4(d.v[0], d.v[1], d.v[2], d.v[3]);
-  reinterpret_cast<float4*>(p)[1] = make_float4(d.v[4], d.v[5], d.v[6], d.v[7]);
+
+__device__ __forceinline__ void storeV(uint16_t* p, const F& d) {
+  uint32_t w[kNV / 2];
+#pragma unroll
+  for (int i = 0; i < kNV / 2; ++i) w[i] = bf16_bits(d.v[2 * i]) | (bf16_bits(d.v[2 * i + 1]) << 16);
+  if constexpr (kNV == 8)
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  else
+    *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+}
+__device__ __forceinline__ void storeV(float* p, const F& d) {
+#pragma unroll
+  for (int i = 0; i < kNV / 4; ++i)
+    reinterpret_cast<float4*>(p)[i] = make_float4(d.v[4 * i], d.v[4 * i + 1], d.v[4 * i + 2], d.v[4 * i + 3]);
 }
 
 // 1 / (1 + e^-p)
@@ -95,10 +117,10 @@ __device__ __forceinline__ float act_grad(float p) {
   return 1.f;
 }
 
-// Taps of this thread's 8 channels, left-padded to 4: T[m] multiplies the input
+// Taps of this thread's channels, left-padded to 4: T[m] multiplies the input
 // 3 - m steps back (T[3] the current one).
 struct Taps {
-  float t[4][8];
+  float t[4][kNV];
 };
 
 __device__ __forceinline__ Taps load_taps(const float* W, int w, int c0) {
@@ -106,7 +128,7 @@ __device__ __forceinline__ Taps load_taps(const float* W, int w, int c0) {
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kNV; ++i) {
       const int j = m - (4 - w);
       T.t[m][i] = j >= 0 ? W[(int64_t)(c0 + i) * w + j] : 0.f;
     }
@@ -124,30 +146,30 @@ __global__ __launch_bounds__(kThreads) void conv_fwd_kernel(const uint16_t* __re
                                                             const int32_t* __restrict__ page_nrows,
                                                             const int32_t* __restrict__ prev, int64_t pages,
                                                             uint16_t* __restrict__ y) {
-  const int c0 = (blockIdx.y * kThreads + threadIdx.x) * 8;
+  const int c0 = (blockIdx.y * kThreads + threadIdx.x) * kNV;
   if (c0 >= Ch) return;
   const Taps T = load_taps(W, w, c0);
   for (int64_t p = blockIdx.x; p < pages; p += gridDim.x) {
     const int n = page_nrows[p];
-    F8 h[3];  // inputs 1, 2, 3 steps back
+    F h[3];  // inputs 1, 2, 3 steps back
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
       const int32_t r = prev[4 * p + k];
-      h[k] = r >= 0 ? unpack8(load8(x + (int64_t)r * Ch + c0)) : zero8();
+      h[k] = r >= 0 ? unpack(loadB(x + (int64_t)r * Ch + c0)) : zeroF();
     }
     const uint16_t* xp = x + p * 64 * (int64_t)Ch + c0;
     uint16_t* yp = y + p * 64 * (int64_t)Ch + c0;
     for (int r0 = 0; r0 < 64; r0 += 8) {
-      uint4 raw[8];
+      B raw[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) raw[q] = r0 + q < n ? load8(xp + (int64_t)(r0 + q) * Ch) : make_uint4(0, 0, 0, 0);
+      for (int q = 0; q < 8; ++q) raw[q] = r0 + q < n ? loadB(xp + (int64_t)(r0 + q) * Ch) : zeroB();
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
-        const F8 cur = unpack8(raw[q]);
-        F8 out;
+        const F cur = unpack(raw[q]);
+        F out;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) out.v[i] = act<kAct>(tap4(T, i, cur.v[i], h[0].v[i], h[1].v[i], h[2].v[i]));
-        store8(yp + (int64_t)(r0 + q) * Ch, r0 + q < n ? out : zero8());
+        for (int i = 0; i < kNV; ++i) out.v[i] = act<kAct>(tap4(T, i, cur.v[i], h[0].v[i], h[1].v[i], h[2].v[i]));
+        storeV(yp + (int64_t)(r0 + q) * Ch, r0 + q < n ? out : zeroF());
         h[2] = h[1];
         h[1] = h[0];
         h[0] = cur;
@@ -165,32 +187,32 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(const uint16_t* __re
                                                             const int64_t* __restrict__ ext_off,
                                                             const ConvExt* __restrict__ ext, int64_t pages,
                                                             TG* __restrict__ dx, float* __restrict__ part) {
-  const int c0 = (blockIdx.y * kThreads + threadIdx.x) * 8;
+  const int c0 = (blockIdx.y * kThreads + threadIdx.x) * kNV;
   if (c0 >= Ch) return;
   const Taps T = load_taps(W, w, c0);
-  float dW[4][8];
+  float dW[4][kNV];
 #pragma unroll
   for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) dW[m][i] = 0.f;
-  auto xrow = [&](int32_t r) { return r >= 0 ? unpack8(load8(x + (int64_t)r * Ch + c0)) : zero8(); };
+    for (int i = 0; i < kNV; ++i) dW[m][i] = 0.f;
+  auto xrow = [&](int32_t r) { return r >= 0 ? loadB(x + (int64_t)r * Ch + c0) : zeroB(); };
   for (int64_t p = blockIdx.x; p < pages; p += gridDim.x) {
     const int n = page_nrows[p];
     const int64_t base = p * 64;
     TG* dxp = dx + base * Ch + c0;
-    for (int r = n; r < 64; ++r) store8(dxp + (int64_t)r * Ch, zero8());
+    for (int r = n; r < 64; ++r) storeV(dxp + (int64_t)r * Ch, zeroF());
     if (n == 0) continue;
     // successors outside the page: their taps on this page's last three rows
-    F8 tail[3];  // tail[q] belongs to row n - 1 - q
+    F tail[3];  // tail[q] belongs to row n - 1 - q
 #pragma unroll
-    for (int q = 0; q < 3; ++q) tail[q] = zero8();
+    for (int q = 0; q < 3; ++q) tail[q] = zeroF();
     for (int64_t e = ext_off[p]; e < ext_off[p + 1]; ++e) {
       const ConvExt E = ext[e];
-      const F8 x0 = xrow(E.s), x1 = xrow(E.p1), x2 = xrow(E.p2), x3 = xrow(E.p3);
-      const F8 g = unpack8(load8(dy + (int64_t)E.s * Ch + c0));
-      F8 dp;
+      const F x0 = unpack(xrow(E.s)), x1 = unpack(xrow(E.p1)), x2 = unpack(xrow(E.p2)), x3 = unpack(xrow(E.p3));
+      const F g = unpack(loadB(dy + (int64_t)E.s * Ch + c0));
+      F dp;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kNV; ++i)
         dp.v[i] = g.v[i] * act_grad<kAct>(tap4(T, i, x0.v[i], x1.v[i], x2.v[i], x3.v[i]));
       const int32_t pk[3] = {E.p1, E.p2, E.p3};
 #pragma unroll
@@ -201,38 +223,43 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(const uint16_t* __re
         for (int qq = 0; qq < 3; ++qq)
           if (qq == q)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) tail[qq].v[i] = fmaf(T.t[3 - k][i], dp.v[i], tail[qq].v[i]);
+            for (int i = 0; i < kNV; ++i) tail[qq].v[i] = fmaf(T.t[3 - k][i], dp.v[i], tail[qq].v[i]);
       }
     }
-    // rows n-1 .. 0: X[j] = input at row r - j; dn[k] = dpre at row r + 1 + k (0 past the page)
+    // rows n-1 .. 0: X[j] = input at row r - j (as loaded); dn[k] = dpre at row r + 1 + k (0 past the page)
     const uint16_t* xp = x + base * Ch + c0;
     const uint16_t* gp = dy + base * Ch + c0;
-    auto xin = [&](int rr) -> F8 {
-      if (rr >= 0) return unpack8(load8(xp + (int64_t)rr * Ch));
-      return -rr <= 3 ? xrow(prev[4 * p + (-rr - 1)]) : zero8();
+    auto xin = [&](int rr) -> B {
+      if (rr >= 0) return loadB(xp + (int64_t)rr * Ch);
+      return -rr <= 3 ? xrow(prev[4 * p + (-rr - 1)]) : zeroB();
     };
-    F8 X[8], dn[3];
+    B X[8];
+    F dn[3];
 #pragma unroll
-    for (int k = 0; k < 3; ++k) dn[k] = zero8();
+    for (int k = 0; k < 3; ++k) dn[k] = zeroF();
 #pragma unroll
     for (int j = 0; j < 4; ++j) X[j] = xin(n - 1 - j);
     for (int r = n - 1; r >= 0; r -= 4) {
-      F8 g[4];
+      B g[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         X[4 + j] = xin(r - 4 - j);
-        g[j] = r - j >= 0 ? unpack8(load8(gp + (int64_t)(r - j) * Ch)) : zero8();
+        g[j] = r - j >= 0 ? loadB(gp + (int64_t)(r - j) * Ch) : zeroB();
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int rr = r - q;
         if (rr < 0) break;
-        F8 dp, out;
+        const F x0 = unpack(X[q]), x1 = unpack(X[q + 1]), x2 = unpack(X[q + 2]), x3 = unpack(X[q + 3]);
+        const F gq = unpack(g[q]);
+        F dp, out;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          dp.v[i] = g[q].v[i] * act_grad<kAct>(tap4(T, i, X[q].v[i], X[q + 1].v[i], X[q + 2].v[i], X[q + 3].v[i]));
-#pragma unroll
-          for (int m = 0; m < 4; ++m) dW[m][i] = fmaf(dp.v[i], X[q + 3 - m].v[i], dW[m][i]);
+        for (int i = 0; i < kNV; ++i) {
+          dp.v[i] = gq.v[i] * act_grad<kAct>(tap4(T, i, x0.v[i], x1.v[i], x2.v[i], x3.v[i]));
+          dW[3][i] = fmaf(dp.v[i], x0.v[i], dW[3][i]);
+          dW[2][i] = fmaf(dp.v[i], x1.v[i], dW[2][i]);
+          dW[1][i] = fmaf(dp.v[i], x2.v[i], dW[1][i]);
+          dW[0][i] = fmaf(dp.v[i], x3.v[i], dW[0][i]);
           out.v[i] = fmaf(T.t[0][i], dn[2].v[i], fmaf(T.t[1][i], dn[1].v[i], fmaf(T.t[2][i], dn[0].v[i],
                                                                                 T.t[3][i] * dp.v[i])));
         }
@@ -242,8 +269,8 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(const uint16_t* __re
           for (int qq = 0; qq < 3; ++qq)
             if (qq == qt)
 #pragma unroll
-              for (int i = 0; i < 8; ++i) out.v[i] += tail[qq].v[i];
-        store8(dxp + (int64_t)rr * Ch, out);
+              for (int i = 0; i < kNV; ++i) out.v[i] += tail[qq].v[i];
+        storeV(dxp + (int64_t)rr * Ch, out);
         dn[2] = dn[1];
         dn[1] = dn[0];
         dn[0] = dp;
@@ -254,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void conv_bwd_kernel(const uint16_t* __re
   }
   float* pp = part + (int64_t)blockIdx.x * Ch * 4;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kNV; ++i)
     *reinterpret_cast<float4*>(pp + (int64_t)(c0 + i) * 4) = make_float4(dW[0][i], dW[1][i], dW[2][i], dW[3][i]);
 }
 
