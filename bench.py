@@ -279,27 +279,35 @@ def conv_time(dpa, plan, dev, steps, warmup):
     gf, gb = b_fwd / (fwd_ms * 1e-3) / 1e9, b_bwd / (bwd_ms * 1e-3) / 1e9
     del x, dy, W, y, dx, dW, ws
     torch.cuda.empty_cache()
+    traffic = step_traffic_record("hbm_traffic_conv.json", "conv.hip", "conv_hip_sha256_16")
     return {"step": "short causal convolution with true-ancestor context (q, k, v of the GDN block)",
             "channels": Ch, "width": CONV_W, "activation": "silu", "rows": C, "tokens": U,
             "fwd_ms": round(fwd_ms, 3), "bwd_ms": round(bwd_ms, 3),
             "roofline": {"bound": "hbm", "unit": "GB/s", "peak": HBM_PEAK_GBPS,
-                         "fwd": {"achieved": round(gf, 1), "frac": round(gf / HBM_PEAK_GBPS, 4), "bytes": b_fwd},
-                         "bwd": {"achieved": round(gb, 1), "frac": round(gb / HBM_PEAK_GBPS, 4), "bytes": b_bwd}}}
+                         "fwd": {"achieved": round(gf, 1), "frac": round(gf / HBM_PEAK_GBPS, 4), "bytes": b_fwd,
+                                 "traffic": traffic.get("fwd")},
+                         "bwd": {"achieved": round(gb, 1), "frac": round(gb / HBM_PEAK_GBPS, 4), "bytes": b_bwd,
+                                 "traffic": (traffic["bwd"] + traffic.get("dw_reduce", 0)) if "bwd" in traffic
+                                 else None}}}
 
 
-def lp_traffic_record():
-    """HBM bytes per launch of the log-probability kernels from the committed counter summary,
+def step_traffic_record(json_name: str, src_name: str, sha_key: str):
+    """HBM bytes per launch of a step's kernels from its committed counter summary,
     if it was taken on the current source; {} otherwise."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "hbm_traffic_logprob.json")
+    path = os.path.join(ROOT, "profiles", json_name)
     if not os.path.exists(path):
         return {}
     with open(path) as f:
         rec = json.load(f)
-    src = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "logprob.hip")
-    if rec.get("logprob_hip_sha256_16") != hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]:
+    src = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", src_name)
+    if rec.get(sha_key) != hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]:
         return {}
     return {k: v.get("bytes_per_launch") for k, v in rec.get("kernels", {}).items()}
+
+
+def lp_traffic_record():
+    return step_traffic_record("hbm_traffic_logprob.json", "logprob.hip", "logprob_hip_sha256_16")
 
 
 def cpu_baseline(spec, plan, budget_s=15.0):
