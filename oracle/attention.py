@@ -73,14 +73,15 @@ def _softmax_rows(s: np.ndarray):
 
 def attn_flat(spec, q, k, v, do, p: AttnParams, transitive: bool = True,
               dtype=np.float64, traj_do: Optional[Dict[int, np.ndarray]] = None,
-              block: int = 1024, with_grad: bool = True):
+              block: int = 1024, with_grad: bool = True, view: str = "mounted"):
     """Returns (o, lse, dq, dk, dv) over compact tokens (token-major, float64 arrays).
 
     ``traj_do`` maps a leaf to the upstream gradient of its trajectory's rows
     ([len(trajectory), Hq, d]); without it each compact token's ``do`` is placed
-    on its owner trajectory and zero elsewhere.
+    on its owner trajectory and zero elsewhere.  ``view`` selects the table
+    pair's view (``oracle.dag.VIEWS``).
     """
-    g = Dag(spec, transitive)
+    g = Dag(spec, transitive, view)
     q, k, v = _np(q), _np(k), _np(v)
     do = None if do is None else _np(do)
     U, hq, d = q.shape
@@ -148,8 +149,8 @@ def attn_flat(spec, q, k, v, do, p: AttnParams, transitive: bool = True,
 # brute force: explicit loops, float64, tiny inputs only
 # ---------------------------------------------------------------------------
 
-def attn_brute(spec, q, k, v, do, p: AttnParams, transitive: bool = True):
-    g = Dag(spec, transitive)
+def attn_brute(spec, q, k, v, do, p: AttnParams, transitive: bool = True, view: str = "mounted"):
+    g = Dag(spec, transitive, view)
     q, k, v, do = (np.asarray(_np(x), np.float64) for x in (q, k, v, do))
     U, hq, d = q.shape
     scale = p.scale_for(d)

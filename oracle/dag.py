@@ -20,6 +20,18 @@ Readings where the pages are silent (each one is listed in the design notes):
 * a direct mount onto the reader's own ancestor chain is rejected; spans that
   reach the chain through transitive closure, and overlapping spans, merge by
   set union (visibility is a set).
+
+Views of one table pair (Octopus App. C: a dense model mounts in a subset of its
+layers and gives the others a mount-free view; Octopus Table 5's "unshifted"
+regime mounts without the position jump):
+
+* ``mounted``    -- the default: mounted spans visible, positions by Eq. 2;
+* ``mount_free`` -- positions by Eq. 2 (they belong to the tokens), mounted
+                    spans not visible (reading: the layers that do not mount see
+                    their tree ancestors only);
+* ``unshifted``  -- mounted spans visible, every node continuing from its
+                    parent's next position as if it had no reads.
+The tables are validated the same way in every view.
 """
 from __future__ import annotations
 
@@ -31,6 +43,9 @@ INVALID, NOT_TOPO, MOUNT_CYCLE, MOUNT_RANGE, SELF_ANCESTOR_MOUNT = (
     "INVALID", "NOT_TOPO", "MOUNT_CYCLE", "MOUNT_RANGE", "SELF_ANCESTOR_MOUNT")
 
 
+VIEWS = ("mounted", "mount_free", "unshifted")
+
+
 class DagError(ValueError):
     def __init__(self, code: str, msg: str):
         super().__init__(f"{code}: {msg}")
@@ -40,7 +55,10 @@ class DagError(ValueError):
 class Dag:
     """Plain-Python view of a node/mount table pair with the derived semantics."""
 
-    def __init__(self, spec, transitive: bool = True):
+    def __init__(self, spec, transitive: bool = True, view: str = "mounted"):
+        if view not in VIEWS:
+            raise ValueError(f"view must be one of {VIEWS}")
+        self.view = view
         self.n = int(len(spec.parent))
         self.parent = [int(x) for x in spec.parent]
         self.length = [int(x) for x in spec.length]
@@ -140,9 +158,10 @@ class Dag:
         for u in self.order:
             p = self.parent[u]
             s = 0 if p < 0 else start[p] + self.length[p]
-            for src, b, e in self.nonempty_direct(u):
-                pos_end = start[src] + (e - 1)          # position of the last mounted token
-                s = max(s, pos_end + 1)
+            if self.view != "unshifted":
+                for src, b, e in self.nonempty_direct(u):
+                    pos_end = start[src] + (e - 1)      # position of the last mounted token
+                    s = max(s, pos_end + 1)
             start[u] = s
         return start
 
@@ -159,7 +178,7 @@ class Dag:
         for u in self.order:
             p = self.parent[u]
             spans = list(act[p]) if p >= 0 else []
-            for m in self.nonempty_direct(u):
+            for m in (self.nonempty_direct(u) if self.view != "mount_free" else []):
                 spans.append(m)
                 if self.transitive:
                     spans.extend(act[m[0]])
