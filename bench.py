@@ -23,6 +23,8 @@ Printed JSON (one line on stdout; progress goes to stderr):
               on the same DAG, forward and backward: milliseconds, the schedule's
               rounds / sequences / replayed tokens, and executed MFMA TFLOP/s;
               hybrid_step_ms = the attention step + 3 such layers (the hybrid stack)
+  views       the same step in the mount-free view (layers that do not mount) and
+              the unshifted regime, on the same tensors
   conv        the GDN block's short causal convolution (width 4, SiLU) over q, k and v
               (6,144 channels) on the same tree: ms and GB/s against 8 TB/s
   logprob     compact-to-semantic log-probabilities and their gradient on 65,536 rows
@@ -77,6 +79,31 @@ def alloc(dpa, plan, p, seed, dev):
     fw, bw = dpa.workspace_bytes(plan, p)
     ws = torch.empty(max(fw, bw), dtype=torch.uint8, device=dev)
     return (q, k, v, o, lse, o_lo, do, dq, dk, dv), ws
+
+
+def views_time(dpa, spec, p, tensors, ws, dev, steps=2):
+    """The attention step in the two other views of the same tables, on the same tensors:
+    the mount-free view of the layers that do not mount (Octopus App. C) and the
+    unshifted regime (Octopus Table 5).  ms per fwd+bwd step and counted TFLOP/s on
+    each view's own visible pairs."""
+    import torch
+    out = {}
+    for view in ("mount_free", "unshifted"):
+        vplan = dpa.Plan(spec, view=view)
+        fw, bw = dpa.workspace_bytes(vplan, p)
+        vws = ws if ws.numel() >= max(fw, bw) else torch.empty(max(fw, bw), dtype=torch.uint8, device=dev)
+        vplan.upload()
+        run_steps(dpa, vplan, p, tensors, vws, 1)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        run_steps(dpa, vplan, p, tensors, vws, steps)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / steps
+        P = vplan.info["visible_pairs"]
+        out[view] = {"ms_per_step": round(dt * 1e3, 2), "visible_pairs": P,
+                     "tflops": round(3.5 * 4.0 * D * HQ * P / dt / 1e12, 2)}
+        del vplan, vws
+    return out
 
 
 def flat_time(dpa, spec, plan, p, dev, steps, max_rows=3_000_000):
@@ -415,6 +442,7 @@ def main() -> int:
     ap.add_argument("--logprob-only", action="store_true",
                     help="only time the log-probability step (for profiling); prints its record")
     ap.add_argument("--no-conv", action="store_true")
+    ap.add_argument("--no-views", action="store_true")
     ap.add_argument("--conv-only", action="store_true",
                     help="only time the short convolution (for profiling); prints its record")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -496,6 +524,9 @@ def main() -> int:
                       "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "page": 64},
            "roofline": roof}
 
+    if not args.no_views:
+        out["views"] = views_time(dpa, spec, p, tensors, ws, dev)
+        log("views: " + ", ".join(f"{k} {v['ms_per_step']} ms/step" for k, v in out["views"].items()))
     del tensors, ws
     torch.cuda.empty_cache()
     if not args.no_gemm:

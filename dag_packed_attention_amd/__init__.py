@@ -42,7 +42,7 @@ class DagMount(ctypes.Structure):
 class DagBuildOpts(ctypes.Structure):
     _fields_ = [("page_size", ctypes.c_int32), ("q_block", ctypes.c_int32),
                 ("transitive", ctypes.c_int32), ("page_shuffle", ctypes.c_int32),
-                ("gdn_chunk", ctypes.c_int32)]
+                ("gdn_chunk", ctypes.c_int32), ("view", ctypes.c_int32)]
 
 
 class DagPlanInfo(ctypes.Structure):
@@ -52,7 +52,9 @@ class DagPlanInfo(ctypes.Structure):
                [("max_position", ctypes.c_int32), ("transitive", ctypes.c_int32),
                 ("gdn_chunk", ctypes.c_int32), ("gdn_rounds", ctypes.c_int32)] + \
                [(n, ctypes.c_int64) for n in ("gdn_sequences", "gdn_replay", "gdn_slots", "gdn_chunks",
-                                             "gdn_segments")]
+                                             "gdn_segments")] + [("view", ctypes.c_int32)]
+
+VIEWS = {"mounted": 0, "mount_free": 1, "unshifted": 2}
 
 
 class DagGdnSeq(ctypes.Structure):
@@ -152,7 +154,8 @@ class Plan:
     tables as attributes ``parent, length, mount_first, mount_count, mount_src,
     mount_begin, mount_end``."""
 
-    def __init__(self, spec, transitive: Optional[bool] = None, page_shuffle: int = 0, gdn_chunk: int = 0):
+    def __init__(self, spec, transitive: Optional[bool] = None, page_shuffle: int = 0, gdn_chunk: int = 0,
+                 view: str = "mounted"):
         if transitive is None:
             transitive = bool(getattr(spec, "meta", {}).get("transitive", True))
         n = len(spec.parent)
@@ -164,7 +167,7 @@ class Plan:
         mounts = (DagMount * max(m, 1))()
         for i in range(m):
             mounts[i] = DagMount(int(spec.mount_src[i]), int(spec.mount_begin[i]), int(spec.mount_end[i]))
-        opts = DagBuildOpts(64, 64, 1 if transitive else 0, int(page_shuffle), int(gdn_chunk))
+        opts = DagBuildOpts(64, 64, 1 if transitive else 0, int(page_shuffle), int(gdn_chunk), VIEWS[view])
         self._h = ctypes.c_void_p()
         _check(_lib.dag_build(nodes, n, mounts, m, ctypes.byref(opts), ctypes.byref(self._h)))
         info = DagPlanInfo()

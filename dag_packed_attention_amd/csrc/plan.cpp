@@ -62,7 +62,7 @@ uint64_t splitmix64(uint64_t& s) {
 dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts, int32_t nm,
                       const dag_build_opts* opts_in, Plan* P, std::string* err) {
   // ---- options ----------------------------------------------------------
-  dag_build_opts opts{64, 64, 1, 0, 0};
+  dag_build_opts opts{64, 64, 1, 0, 0, DAG_VIEW_MOUNTED};
   if (opts_in) opts = *opts_in;
   if (opts.page_size == 0) opts.page_size = kPage;
   if (opts.q_block == 0) opts.q_block = kPage;
@@ -71,6 +71,8 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
                 opts.page_size, opts.q_block);
   if (opts.transitive != 0 && opts.transitive != 1)
     return fail(err, DAG_E_INVALID, "transitive must be 0 or 1");
+  if (opts.view != DAG_VIEW_MOUNTED && opts.view != DAG_VIEW_MOUNT_FREE && opts.view != DAG_VIEW_UNSHIFTED)
+    return fail(err, DAG_E_INVALID, "view must be 0, 1 or 2 (got %lld)", opts.view);
   if (opts.gdn_chunk < 0 || opts.gdn_chunk > 4096)
     return fail(err, DAG_E_INVALID, "gdn_chunk must be in [0, 4096] (got %lld)", opts.gdn_chunk);
   P->opts = opts;
@@ -155,9 +157,11 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
   for (int32_t u : P->order) {
     const int32_t p = P->parent[u];
     int64_t s = p < 0 ? 0 : (int64_t)P->start[p] + P->length[p];
-    for (const dag_mount& m : P->direct[u]) {
-      const int64_t pos_end = (int64_t)P->start[m.src_node] + (m.end - 1);  // last mounted token
-      s = std::max(s, pos_end + 1);
+    if (opts.view != DAG_VIEW_UNSHIFTED) {  // the unshifted regime continues from the parent
+      for (const dag_mount& m : P->direct[u]) {
+        const int64_t pos_end = (int64_t)P->start[m.src_node] + (m.end - 1);  // last mounted token
+        s = std::max(s, pos_end + 1);
+      }
     }
     if (s + P->length[u] > INT32_MAX) return fail(err, DAG_E_OVERFLOW, "positions exceed int32");
     P->start[u] = (int32_t)s;
@@ -169,9 +173,11 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
   for (int32_t u : P->order) {
     std::vector<Span> s;
     if (P->parent[u] >= 0) s = act[P->parent[u]];
-    for (const dag_mount& m : P->direct[u]) {
-      s.push_back({m.src_node, m.begin, m.end});
-      if (opts.transitive) s.insert(s.end(), act[m.src_node].begin(), act[m.src_node].end());
+    if (opts.view != DAG_VIEW_MOUNT_FREE) {  // the mount-free view: ancestors only
+      for (const dag_mount& m : P->direct[u]) {
+        s.push_back({m.src_node, m.begin, m.end});
+        if (opts.transitive) s.insert(s.end(), act[m.src_node].begin(), act[m.src_node].end());
+      }
     }
     std::sort(s.begin(), s.end());
     s.erase(std::unique(s.begin(), s.end()), s.end());
@@ -444,6 +450,7 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
   I.pages = n_pages;
   I.query_pages = (int64_t)P->qpages.size();
   I.transitive = opts.transitive;
+  I.view = opts.view;
   I.max_position = (int32_t)max_pos;
   std::vector<char> has_child(n, 0);
   for (int32_t u = 0; u < n; ++u)

@@ -86,7 +86,18 @@ typedef struct {
   int32_t gdn_chunk;    /* 0: no linear-attention schedule; B > 0: also plan the chunked  */
                         /*    gated-delta-rule execution with chunk length B (HARTS Sec.  */
                         /*    3.3; the GDN kernels take B = 64 only)                      */
+  int32_t view;         /* which layers' view of the tables the plan serves:               */
+                        /*  DAG_VIEW_MOUNTED (0): mounted spans visible, positions by Eq. 2; */
+                        /*  DAG_VIEW_MOUNT_FREE (1): the layers that do not mount (Octopus   */
+                        /*    App. C: a dense model mounts in a subset of its layers): Eq. 2 */
+                        /*    positions, mounted spans not visible;                          */
+                        /*  DAG_VIEW_UNSHIFTED (2): mounted spans visible, every node        */
+                        /*    continuing from its parent without the jump (Octopus Table 5's */
+                        /*    unshifted regime).  Row layout and page table are the same in  */
+                        /*    every view, so one set of tensors serves plans of all views.   */
 } dag_build_opts;
+
+enum { DAG_VIEW_MOUNTED = 0, DAG_VIEW_MOUNT_FREE = 1, DAG_VIEW_UNSHIFTED = 2 };
 
 typedef struct dag_plan dag_plan; /* opaque and immutable after dag_build */
 
@@ -111,6 +122,7 @@ typedef struct {
   int64_t gdn_slots;       /* exported boundary states                                */
   int64_t gdn_chunks;      /* execution chunks over all sequences, replay included    */
   int64_t gdn_segments;    /* fork-free segments of the (mount-free) tree             */
+  int32_t view;            /* the build option                                        */
 } dag_plan_info;
 
 /* Validate the node/mount tables and compile them into a plan.  Host only;

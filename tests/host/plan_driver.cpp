@@ -162,7 +162,7 @@ int main(int argc, char** argv) {
       }
       nodes[u].mount_count = (int)mounts.size() - nodes[u].mount_first;
     }
-    dag_build_opts o{64, 64, (int)rnd(2), (int)rnd(3), rnd(3) ? 1 + (int)rnd(70) : 0};
+    dag_build_opts o{64, 64, (int)rnd(2), (int)rnd(3), rnd(3) ? 1 + (int)rnd(70) : 0, (int)rnd(3)};
     Plan P;
     std::string err;
     const dag_status st = build_plan(nodes.data(), n, mounts.data(), (int)mounts.size(), &o, &P, &err);

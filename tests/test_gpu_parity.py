@@ -34,13 +34,13 @@ def dpa():
 
 
 def _run(dpa, spec, q, k, v, do, hq, hkv, d, dtype, rope=10000.0, transitive=None, shuffle=0, bwd=True,
-         scale=0.0, grad="fp32"):
+         scale=0.0, grad="fp32", view="mounted"):
     """Token-major CPU tensors in, token-major CPU float64 results out (via the row layout).
 
     Gradients come back in fp32 by default: in these small DAGs a shared row's dK/dV reaches
     magnitudes (~11) where bf16 storage alone is 0.03 away from the exact value.
     """
-    plan = dpa.Plan(spec, transitive=transitive, page_shuffle=shuffle)
+    plan = dpa.Plan(spec, transitive=transitive, page_shuffle=shuffle, view=view)
     p = dpa.AttnParams(hq, hkv, d, dtype, scale=scale, rope_base=rope, grad_dtype=grad)
     tdt = p.torch_dtype
     rows = lambda x: dpa.to_rows(plan, x.to(DEV, tdt), fill=float("nan"))
@@ -65,13 +65,14 @@ def _run(dpa, spec, q, k, v, do, hq, hkv, d, dtype, rope=10000.0, transitive=Non
     return res, plan
 
 
-def _ref(spec, q, k, v, do, hq, hkv, rope=10000.0, transitive=True, brute=False, bwd=True, scale=None):
+def _ref(spec, q, k, v, do, hq, hkv, rope=10000.0, transitive=True, brute=False, bwd=True, scale=None,
+         view="mounted"):
     p = OParams(hq, hkv, scale=scale, rope_base=rope)
     args = [x.double().numpy() for x in (q, k, v)] + [do.double().numpy() if do is not None else None]
     if brute:
-        o, lse, dq, dk, dv = attn_brute(spec, *args, p, transitive=transitive)
+        o, lse, dq, dk, dv = attn_brute(spec, *args, p, transitive=transitive, view=view)
     else:
-        o, lse, dq, dk, dv = attn_flat(spec, *args, p, transitive=transitive, with_grad=bwd)
+        o, lse, dq, dk, dv = attn_flat(spec, *args, p, transitive=transitive, with_grad=bwd, view=view)
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv}
 
 
@@ -158,6 +159,30 @@ def test_small_bf16_mfma_path(dpa, name):
     got, _ = _run(dpa, spec, q, k, v, do, 16, 4, 128, "bf16", transitive=tr)
     ref = _ref(spec, q, k, v, do, 16, 4, transitive=tr)
     _assert_close(got, ref, "bf16", tag=name)
+
+
+@pytest.mark.parametrize("view", ["mount_free", "unshifted"])
+@pytest.mark.parametrize("name", ["mini3", "mini4"])
+def test_layer_group_views_on_device(dpa, name, view):
+    # Octopus App. C layer groups and Table 5's unshifted regime: plans of the same
+    # tables in another view, run on the same row-layout tensors
+    spec = SMALL[name]()
+    tr = bool(spec.meta.get("transitive", True))
+    print(f"view {view} {name}", flush=True)
+    q, k, v, do = _inputs(spec, 16, 4, 128, 3000 + len(name), "bf16")
+    got, plan = _run(dpa, spec, q, k, v, do, 16, 4, 128, "bf16", transitive=tr, view=view)
+    assert plan.info["view"] == dpa.VIEWS[view]
+    ref = _ref(spec, q, k, v, do, 16, 4, transitive=tr, view=view)
+    _assert_close(got, ref, "bf16", tag=f"{name}/{view}")
+
+
+@pytest.mark.parametrize("view", ["mount_free", "unshifted"])
+def test_tiny_views_fp32_vs_brute(dpa, view):
+    spec = synth.config1()
+    q, k, v, do = _inputs(spec, 2, 2, 64, 1001, "fp32")
+    got, _ = _run(dpa, spec, q, k, v, do, 2, 2, 64, "fp32", view=view)
+    ref = _ref(spec, q, k, v, do, 2, 2, brute=True, view=view)
+    _assert_close(got, ref, "fp32", tag=f"tiny/{view}")
 
 
 @pytest.mark.parametrize("name", ["mini3", "tiny"])

@@ -30,9 +30,9 @@ def test_library_exports_every_declared_symbol():
     assert declared <= exported
 
 
-def _compare(spec, transitive=True, shuffle=0):
-    plan = dpa.Plan(spec, transitive=transitive, page_shuffle=shuffle)
-    dag = Dag(spec, transitive=transitive)
+def _compare(spec, transitive=True, shuffle=0, view="mounted"):
+    plan = dpa.Plan(spec, transitive=transitive, page_shuffle=shuffle, view=view)
+    dag = Dag(spec, transitive=transitive, view=view)
     assert list(plan.starts()) == dag.start
     for u in range(dag.n):
         got = plan.node_ranges(u)
@@ -69,6 +69,18 @@ def test_random_dags(seed):
     spec = synth.random_tiny_dag(rng, n_nodes=int(rng.integers(1, 14)), max_len=int(rng.integers(1, 150)),
                                  p_mount=0.7, max_mounts=3, n_roots=int(rng.integers(1, 3)))
     _compare(spec, transitive=bool(seed % 2), shuffle=seed % 3)
+
+
+@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("view", ["mount_free", "unshifted"])
+def test_views_match_the_oracle_and_share_the_row_layout(seed, view):
+    rng = np.random.default_rng(5000 + seed)
+    spec = synth.random_tiny_dag(rng, n_nodes=int(rng.integers(1, 14)), max_len=int(rng.integers(1, 150)),
+                                 p_mount=0.7, max_mounts=3, n_roots=int(rng.integers(1, 3)))
+    plan, _ = _compare(spec, transitive=bool(seed % 2), shuffle=seed % 3, view=view)
+    assert plan.info["view"] == dpa.VIEWS[view]
+    base = dpa.Plan(spec, transitive=bool(seed % 2), page_shuffle=seed % 3)
+    assert np.array_equal(plan.row_maps()[0], base.row_maps()[0])      # same rows: tensors are shared
 
 
 def test_transitive_golden():
