@@ -28,6 +28,10 @@ rounding order):
 * ``logprob``   -- compact-to-semantic log-probabilities (HARTS Eq. 17) on
                    expanded per-position rows, the semantic position map of
                    the original batch, and the reused-row gradient (Eq. 19-20).
+* ``harts_plan`` -- HARTS's prefix-aware microbatch planning over raw
+                   trajectories: compact work (Eq. 5-6), natural partition,
+                   K range, exact DP, sampled-K evolution, trie-aware greedy
+                   with Eq. 10, repair and refinement, replica/slot assignment.
 * ``conv``      -- the short causal convolution of a linear-attention block
                    along each trajectory's own tokens (mounted spans skipped),
                    one output per compact token, gradients summed over readers.
