@@ -25,6 +25,8 @@ Printed JSON (one line on stdout; progress goes to stderr):
               hybrid_step_ms = the attention step + 3 such layers (the hybrid stack)
   views       the same step in the mount-free view (layers that do not mount) and
               the unshifted regime, on the same tensors
+  planner     host front end: the workload's raw trajectories through the trie and the
+              prefix-aware microbatch planner (8 replicas, 262,144 tokens per microbatch)
   conv        the GDN block's short causal convolution (width 4, SiLU) over q, k and v
               (6,144 channels) on the same tree: ms and GB/s against 8 TB/s
   logprob     compact-to-semantic log-probabilities and their gradient on 65,536 rows
@@ -337,6 +339,35 @@ def lp_traffic_record():
     return step_traffic_record("hbm_traffic_logprob.json", "logprob.hip", "logprob_hip_sha256_16")
 
 
+PLAN_REPLICAS, PLAN_CAPACITY = 8, 262144
+
+
+def planner_time(spec):
+    """Host-side front end on the workload's raw trajectories: every leaf's root-to-leaf
+    sequence of its own tokens (vocabulary ids drawn uniformly from [0, 131072), one per
+    compact token), then the trie (dag_trie_build) and HARTS's prefix-aware microbatch plan
+    for 8 data-parallel replicas and 262,144 compact tokens per microbatch
+    (dag_microbatch_plan).  Wall time of each call on the host."""
+    import dag_packed_attention_amd as dpa
+    from synth.dags import raw_trajectories
+    tok, off = raw_trajectories(spec, 61)
+    lens = off[1:] - off[:-1]
+    t0 = time.perf_counter()
+    trie = dpa.trie_build((tok, off))
+    t1 = time.perf_counter()
+    mb = dpa.microbatch_plan((tok, off), PLAN_REPLICAS, PLAN_CAPACITY)
+    t2 = time.perf_counter()
+    info = mb["info"]
+    return {"step": "trajectory ingestion (trie) and prefix-aware microbatch / replica planning, host",
+            "trajectories": len(lens), "semantic_tokens": int(off[-1]), "trie_tokens": int(len(trie["node_tokens"])),
+            "trie_nodes": int(len(trie["parent"])), "replicas": PLAN_REPLICAS, "capacity": PLAN_CAPACITY,
+            "trie_ms": round((t1 - t0) * 1e3, 1), "plan_ms": round((t2 - t1) * 1e3, 1),
+            "microbatches": info["microbatches"], "natural_microbatches": info["natural_microbatches"],
+            "candidates": info["candidates"], "exact_search": bool(info["exact"]),
+            "J": [info["total_work"], info["slot_critical_work"], info["max_replica_work"]],
+            "trie_work": info["trie_work"]}
+
+
 def cpu_baseline(spec, plan, budget_s=15.0):
     """The oracle (float32) on one causal trajectory of the workload, sized to ~budget_s."""
     import numpy as np
@@ -443,6 +474,7 @@ def main() -> int:
                     help="only time the log-probability step (for profiling); prints its record")
     ap.add_argument("--no-conv", action="store_true")
     ap.add_argument("--no-views", action="store_true")
+    ap.add_argument("--no-planner", action="store_true")
     ap.add_argument("--conv-only", action="store_true",
                     help="only time the short convolution (for profiling); prints its record")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -557,6 +589,10 @@ def main() -> int:
         out["x_vs_flat"] = round(t_flat / dt, 3)
         out["flat"] = {"ms_per_step": round(t_flat * 1e3, 1), "rows": frows, "pairs": fpairs,
                        "trajectories": ntraj, "pairs_ratio": round(fpairs / P, 3)}
+    if not args.no_planner:
+        out["planner"] = planner_time(spec)
+        pl = out["planner"]
+        log(f"planner: trie {pl['trie_ms']} ms, plan {pl['plan_ms']} ms, K = {pl['microbatches']}")
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(spec, plan)
     print(json.dumps(out), flush=True)

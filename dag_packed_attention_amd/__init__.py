@@ -83,6 +83,17 @@ class DagConvParams(ctypes.Structure):
                 ("grad_dtype", ctypes.c_int32)]
 
 
+class DagMbOpts(ctypes.Structure):
+    _fields_ = [("replicas", ctypes.c_int32), ("exact_max", ctypes.c_int32), ("capacity", ctypes.c_int64)]
+
+
+class DagMbInfo(ctypes.Structure):
+    _fields_ = [("microbatches", ctypes.c_int32), ("exact", ctypes.c_int32),
+                ("natural_microbatches", ctypes.c_int32), ("candidates", ctypes.c_int32),
+                ("total_work", ctypes.c_int64), ("slot_critical_work", ctypes.c_int64),
+                ("max_replica_work", ctypes.c_int64), ("trie_work", ctypes.c_int64)]
+
+
 class DagError(RuntimeError):
     def __init__(self, status: int, msg: str):
         super().__init__(f"{STATUS.get(status, status)}: {msg}")
@@ -122,6 +133,9 @@ def _load() -> ctypes.CDLL:
         "dag_conv_workspace": ([P, ctypes.POINTER(DagConvParams), ctypes.POINTER(SZ)], I32),
         "dag_conv_fwd": ([P, ctypes.POINTER(DagConvParams), P, P, P, P], I32),
         "dag_conv_bwd": ([P, ctypes.POINTER(DagConvParams), P, P, P, P, P, P, SZ, P], I32),
+        "dag_trie_build": ([P, P, I32, I32, P, P, I64, P, P, ctypes.POINTER(I32), ctypes.POINTER(I64)], I32),
+        "dag_microbatch_plan": ([P, P, I32, ctypes.POINTER(DagMbOpts), P, I32, P, P, P,
+                                 ctypes.POINTER(DagMbInfo)], I32),
         "dag_attn_timing_enable": ([P, I32, I32], I32),
         "dag_attn_timing_read": ([P, P, P], I32),
         "dag_last_error": ([], ctypes.c_char_p),
@@ -563,6 +577,84 @@ def logprob_bwd(z, lse, row_first, row_pos, pos_target, g, grad_dtype: str = "bf
 
 
 # ---------------------------------------------------------------------------
+# trajectory ingestion and prefix-aware microbatch planning (host only)
+# ---------------------------------------------------------------------------
+
+def _traj_arrays(trajs):
+    """(tokens int32, offsets int64) from a list of sequences, or passed through when
+    ``trajs`` already is such a pair."""
+    if isinstance(trajs, tuple) and len(trajs) == 2 and isinstance(trajs[0], np.ndarray):
+        tok, off = np.ascontiguousarray(trajs[0], np.int32), np.ascontiguousarray(trajs[1], np.int64)
+        return (tok if tok.size else np.zeros(1, np.int32)), off
+    off = np.zeros(len(trajs) + 1, np.int64)
+    for i, t in enumerate(trajs):
+        off[i + 1] = off[i] + len(t)
+    tok = np.zeros(max(int(off[-1]), 1), np.int32)
+    for i, t in enumerate(trajs):
+        tok[off[i]:off[i + 1]] = np.asarray(t, np.int32)
+    return tok, off
+
+
+def _n_traj(trajs) -> int:
+    if isinstance(trajs, tuple) and len(trajs) == 2 and isinstance(trajs[0], np.ndarray):
+        return len(trajs[1]) - 1
+    return len(trajs)
+
+
+def trie_build(trajs) -> dict:
+    """``dag_trie_build``: raw token sequences (a list, or a (tokens, offsets) pair of
+    arrays) -> the trie as a node table.
+
+    Returns {"parent", "length" (int32 [n_nodes]), "node_tok_off" (int64 [n_nodes+1]),
+    "node_tokens" (int32), "leaf_of_traj" (int32 [N])} plus ``spec`` (a node-table object
+    accepted by :class:`Plan`)."""
+    tok, off = _traj_arrays(trajs)
+    N = _n_traj(trajs)
+    nn, nt = ctypes.c_int32(0), ctypes.c_int64(0)
+    _check(_lib.dag_trie_build(tok.ctypes.data, off.ctypes.data, N, 0, None, None, 0, None, None,
+                               ctypes.byref(nn), ctypes.byref(nt)))
+    nodes = (DagNode * max(nn.value, 1))()
+    noff = np.zeros(nn.value + 1, np.int64)
+    ntok = np.zeros(max(nt.value, 1), np.int32)
+    leaf = np.zeros(N, np.int32)
+    _check(_lib.dag_trie_build(tok.ctypes.data, off.ctypes.data, N, nn.value, nodes, noff.ctypes.data,
+                               nt.value, ntok.ctypes.data, leaf.ctypes.data, ctypes.byref(nn), ctypes.byref(nt)))
+    parent = np.array([nodes[i].parent for i in range(nn.value)], np.int32)
+    length = np.array([nodes[i].length for i in range(nn.value)], np.int32)
+
+    class _Spec:
+        pass
+    spec = _Spec()
+    spec.parent, spec.length = parent, length
+    spec.mount_first = np.zeros(nn.value, np.int32)
+    spec.mount_count = np.zeros(nn.value, np.int32)
+    spec.mount_src = spec.mount_begin = spec.mount_end = np.zeros(0, np.int32)
+    spec.n_tokens = int(nt.value)
+    spec.meta = {"transitive": True}
+    return {"parent": parent, "length": length, "node_tok_off": noff, "node_tokens": ntok[:nt.value],
+            "leaf_of_traj": leaf, "spec": spec}
+
+
+def microbatch_plan(trajs, replicas: int, capacity: int, exact_max: int = 0) -> dict:
+    """``dag_microbatch_plan``: {"mb_of_traj", "replica", "slot", "work", "info"}."""
+    tok, off = _traj_arrays(trajs)
+    N = _n_traj(trajs)
+    o = DagMbOpts(int(replicas), int(exact_max), int(capacity))
+    info = DagMbInfo()
+    _check(_lib.dag_microbatch_plan(tok.ctypes.data, off.ctypes.data, N, ctypes.byref(o), None, 0, None,
+                                    None, None, ctypes.byref(info)))
+    K = info.microbatches
+    mb = np.zeros(N, np.int32)
+    rep, slot = np.zeros(max(K, 1), np.int32), np.zeros(max(K, 1), np.int32)
+    work = np.zeros(max(K, 1), np.int64)
+    _check(_lib.dag_microbatch_plan(tok.ctypes.data, off.ctypes.data, N, ctypes.byref(o),
+                                    mb.ctypes.data, K, rep.ctypes.data, slot.ctypes.data, work.ctypes.data,
+                                    ctypes.byref(info)))
+    return {"mb_of_traj": mb, "replica": rep[:K], "slot": slot[:K], "work": work[:K],
+            "info": {f: getattr(info, f) for f, _ in DagMbInfo._fields_}}
+
+
+# ---------------------------------------------------------------------------
 # layout helpers (token-major <-> row layout); pure data movement
 # ---------------------------------------------------------------------------
 
@@ -585,5 +677,5 @@ def from_rows(plan: Plan, x_rows):
 
 __all__ = ["Plan", "AttnParams", "GdnParams", "DagError", "attn_fwd", "attn_bwd", "workspace_bytes", "gdn_fwd",
            "gdn_bwd", "gdn_workspace_bytes", "ConvParams", "conv_fwd", "conv_bwd", "conv_workspace_bytes",
-           "logprob_fwd", "logprob_bwd", "to_rows", "from_rows", "last_error",
+           "logprob_fwd", "logprob_bwd", "trie_build", "microbatch_plan", "to_rows", "from_rows", "last_error",
            "LIB_PATH"]

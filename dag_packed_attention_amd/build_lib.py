@@ -2,7 +2,7 @@
 
     python dag_packed_attention_amd/build_lib.py      (or call build())
 
-The host compactor (plan.cpp, gdn_plan.cpp, logprob_map.cpp, conv_plan.cpp) is plain C++ and is compiled with g++; the ABI
+The host compactor (plan.cpp, gdn_plan.cpp, logprob_map.cpp, conv_plan.cpp, harts_plan.cpp) is plain C++ and is compiled with g++; the ABI
 glue and the kernels are compiled with hipcc for gfx950.  Packed-fp32 code
 generation is switched off for the device code.
 """
@@ -34,7 +34,7 @@ def _run(cmd):
     return r
 
 
-OBJS = ("plan.o", "gdn_plan.o", "logprob_map.o", "conv_plan.o", "abi.o", "kernels.o", "gdn.o", "logprob.o",
+OBJS = ("plan.o", "gdn_plan.o", "logprob_map.o", "conv_plan.o", "harts_plan.o", "abi.o", "kernels.o", "gdn.o", "logprob.o",
         "conv.o")
 
 
@@ -48,6 +48,7 @@ def build(verbose: bool = False) -> str:
          "-o", os.path.join(obj_dir, "logprob_map.o")],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "logprob.hip"), "-o", os.path.join(obj_dir, "logprob.o")],
         ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "conv_plan.cpp"), "-o", os.path.join(obj_dir, "conv_plan.o")],
+        ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "harts_plan.cpp"), "-o", os.path.join(obj_dir, "harts_plan.o")],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "conv.hip"), "-o", os.path.join(obj_dir, "conv.o")],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "abi.cpp"), "-o", os.path.join(obj_dir, "abi.o")],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "kernels.hip"), "-o", os.path.join(obj_dir, "kernels.o")],

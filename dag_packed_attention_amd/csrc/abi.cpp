@@ -11,6 +11,7 @@
 
 #include "conv.hpp"
 #include "gdn.hpp"
+#include "harts_plan.hpp"
 #include "launch.hpp"
 #include "logprob.hpp"
 #include "plan.hpp"
@@ -904,6 +905,56 @@ dag_status dag_conv_bwd(dag_plan* plan, const dag_conv_params* p, const void* x,
                                 (uint16_t*)dx, dweight, (float*)ws, stream);
   }
   return launched("dag_conv_bwd");
+}
+
+// ---- trajectory ingestion and microbatch planning ------------------------------------
+dag_status dag_trie_build(const int32_t* tokens, const int64_t* traj_off, int32_t n_traj, int32_t cap_nodes,
+                          dag_node* nodes, int64_t* node_tok_off, int64_t cap_tokens, int32_t* node_tokens,
+                          int32_t* leaf_of_traj, int32_t* n_nodes, int64_t* n_tokens) {
+  if (!n_nodes || !n_tokens) return set_err(DAG_E_INVALID, "null argument");
+  TrieOut t;
+  std::string err;
+  dag_status st;
+  try {
+    st = trie_build(tokens, traj_off, n_traj, &t, &err);
+  } catch (const std::bad_alloc&) {
+    return set_err(DAG_E_OVERFLOW, "out of host memory building the trie");
+  }
+  if (st != DAG_OK) return set_err(st, err);
+  *n_nodes = (int32_t)t.nodes.size();
+  *n_tokens = (int64_t)t.tokens.size();
+  if (cap_nodes < *n_nodes || cap_tokens < *n_tokens || !nodes || !node_tok_off || !leaf_of_traj ||
+      (*n_tokens > 0 && !node_tokens))
+    return DAG_OK;
+  std::memcpy(nodes, t.nodes.data(), t.nodes.size() * sizeof(dag_node));
+  std::memcpy(node_tok_off, t.tok_off.data(), t.tok_off.size() * 8);
+  if (*n_tokens) std::memcpy(node_tokens, t.tokens.data(), t.tokens.size() * 4);
+  std::memcpy(leaf_of_traj, t.leaf_of_traj.data(), t.leaf_of_traj.size() * 4);
+  return DAG_OK;
+}
+
+dag_status dag_microbatch_plan(const int32_t* tokens, const int64_t* traj_off, int32_t n_traj,
+                               const dag_mb_opts* opts, int32_t* mb_of_traj, int32_t cap_mb,
+                               int32_t* replica_of_mb, int32_t* slot_of_mb, int64_t* work_of_mb,
+                               dag_mb_info* info) {
+  if (!info) return set_err(DAG_E_INVALID, "null argument");
+  MbOut m;
+  std::string err;
+  dag_status st;
+  try {
+    st = microbatch_plan(tokens, traj_off, n_traj, opts, &m, &err);
+  } catch (const std::bad_alloc&) {
+    return set_err(DAG_E_OVERFLOW, "out of host memory planning microbatches");
+  }
+  if (st != DAG_OK) return set_err(st, err);
+  *info = m.info;
+  const int32_t K = m.info.microbatches;
+  if (cap_mb < K || !mb_of_traj || !replica_of_mb || !slot_of_mb || !work_of_mb) return DAG_OK;
+  std::memcpy(mb_of_traj, m.mb_of_traj.data(), m.mb_of_traj.size() * 4);
+  std::memcpy(replica_of_mb, m.replica.data(), K * 4);
+  std::memcpy(slot_of_mb, m.slot.data(), K * 4);
+  std::memcpy(work_of_mb, m.work.data(), K * 8);
+  return DAG_OK;
 }
 
 }  // extern "C"

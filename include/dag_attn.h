@@ -371,6 +371,57 @@ dag_status dag_conv_fwd(dag_plan* plan, const dag_conv_params* p, const void* x,
 dag_status dag_conv_bwd(dag_plan* plan, const dag_conv_params* p, const void* x, const float* weight,
                         const void* dy, void* dx, float* dweight, void* ws, size_t ws_bytes, void* hip_stream);
 
+/* ---- trajectory ingestion and prefix-aware microbatch planning (host only) ----
+ *
+ * HARTS Sec. 3.1-3.2.  Input: N raw root-to-leaf trajectories as token ids,
+ * tokens[traj_off[i] .. traj_off[i+1]) for trajectory i (traj_off[0] = 0,
+ * non-decreasing).  Neither call touches the GPU. */
+
+/* The trie of the trajectories' shared prefixes as a DAG node table for dag_build
+ * (no mounts): nodes are the trie's maximal unbranched runs, numbered depth-first
+ * with children in token order (so parent < child and the leaves come in the
+ * trajectories' lexicographic order); a trajectory that is a prefix or a repeat of
+ * another gets a zero-length leaf of its own, so every trajectory ends at its own
+ * leaf.  The compact work C(X) of Eq. 5 is the number of tokens.  Writes *n_nodes
+ * and *n_tokens and, when cap_nodes >= *n_nodes, cap_tokens >= *n_tokens and every
+ * output is non-NULL: nodes[n_nodes], node_tok_off[n_nodes + 1] (node u's tokens are
+ * node_tokens[node_tok_off[u] .. node_tok_off[u+1])), node_tokens[n_tokens] and
+ * leaf_of_traj[N].  Otherwise only the counts. */
+dag_status dag_trie_build(const int32_t* tokens, const int64_t* traj_off, int32_t n_traj, int32_t cap_nodes,
+                          dag_node* nodes, int64_t* node_tok_off, int64_t cap_tokens, int32_t* node_tokens,
+                          int32_t* leaf_of_traj, int32_t* n_nodes, int64_t* n_tokens);
+
+typedef struct {
+  int32_t replicas;   /* D >= 1: data-parallel replicas                                     */
+  int32_t exact_max;  /* N0: exact search up to this many trajectories; 0 selects 512          */
+  int64_t capacity;   /* T >= 1: compact tokens per microbatch                                 */
+} dag_mb_opts;
+
+typedef struct {
+  int32_t microbatches;          /* K, a multiple of D                                        */
+  int32_t exact;                 /* 1: exact DP over contiguous partitions (N <= N0)          */
+  int32_t natural_microbatches;  /* K0 of the natural partition                               */
+  int32_t candidates;            /* fully assigned candidate plans compared                   */
+  int64_t total_work;            /* J (Eq. 4): sum of microbatch compact work,                 */
+  int64_t slot_critical_work;    /*   sum over slots of the heaviest microbatch,               */
+  int64_t max_replica_work;      /*   largest work on one replica                              */
+  int64_t trie_work;             /* C(X): all trajectories in one trie                         */
+} dag_mb_info;
+
+/* Prefix-aware microbatch plan: membership, DP replica and slot of every
+ * microbatch (Eq. 4-10; the search is exact over contiguous partitions of the
+ * lexicographic order for N <= N0 and heuristic otherwise, with one trie-aware
+ * greedy candidate in every case; ties are broken deterministically).
+ * Guarantees: every trajectory in exactly one microbatch, no microbatch empty or
+ * above capacity, K mod D = 0 and exactly K / D microbatches per replica, one
+ * per slot.  Writes info and, when cap_mb >= K and the outputs are non-NULL,
+ * mb_of_traj[N], replica_of_mb[K], slot_of_mb[K], work_of_mb[K].  DAG_E_INVALID
+ * when a trajectory is longer than the capacity, N < D, or no feasible plan exists. */
+dag_status dag_microbatch_plan(const int32_t* tokens, const int64_t* traj_off, int32_t n_traj,
+                               const dag_mb_opts* opts, int32_t* mb_of_traj, int32_t cap_mb,
+                               int32_t* replica_of_mb, int32_t* slot_of_mb, int64_t* work_of_mb,
+                               dag_mb_info* info);
+
 /* Per-kernel timing, for profiling.  While enabled, dag_attn_fwd/bwd record a
  * HIP event pair on their stream around each of their kernels (at most
  * `capacity` pairs, created here; later launches go unrecorded).

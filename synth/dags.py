@@ -289,3 +289,40 @@ def random_tiny_dag(rng: np.random.Generator, n_nodes: int = 8, max_len: int = 9
             e = int(rng.integers(b, g.length[s] + 1))
             g.mount(u, s, b, e)
     return g.build(name="random_tiny")
+
+
+# ---------------------------------------------------------------------------
+# Raw trajectories of a tree, for the trie / microbatch planner front end: every
+# leaf's root-to-leaf sequence of own tokens (mounts are not part of a raw
+# trajectory), each compact token carrying a seeded vocabulary id.
+# ---------------------------------------------------------------------------
+
+def leaves_and_chains(spec: DagSpec) -> List[List[int]]:
+    """Root-to-leaf node chains, leaves depth-first (roots and children in table order)."""
+    n = len(spec.parent)
+    kids: List[List[int]] = [[] for _ in range(n)]
+    for u in range(n):
+        if spec.parent[u] >= 0:
+            kids[int(spec.parent[u])].append(u)
+    out: List[List[int]] = []
+    stack = [(r, [r]) for r in reversed(range(n)) if spec.parent[r] < 0]
+    while stack:
+        u, chain = stack.pop()
+        if not kids[u]:
+            out.append(chain)
+        for c in reversed(kids[u]):
+            stack.append((c, chain + [c]))
+    return out
+
+
+def raw_trajectories(spec: DagSpec, seed: int, vocab: int = 131072):
+    """(tokens int32, offsets int64): the trajectories as flat arrays; every compact token
+    gets a vocabulary id drawn uniformly from [0, vocab)."""
+    ids = np.random.default_rng(seed).integers(0, vocab, int(np.sum(spec.length)), dtype=np.int64).astype(np.int32)
+    offs = np.concatenate([[0], np.cumsum(spec.length)]).astype(np.int64)
+    parts, lens = [], []
+    for chain in leaves_and_chains(spec):
+        seq = np.concatenate([ids[offs[u]:offs[u + 1]] for u in chain])
+        parts.append(seq)
+        lens.append(len(seq))
+    return np.concatenate(parts).astype(np.int32), np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
