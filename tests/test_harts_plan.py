@@ -92,6 +92,6 @@ def test_trie_of_a_workload_recovers_its_tree():
     assert len(t["node_tokens"]) == int(np.sum(spec.length))
     trajs = [tok[off[i]:off[i + 1]].tolist() for i in range(len(off) - 1)]
     assert len(t["node_tokens"]) == HP.compact_work(trajs)
-    mb = dpa.microbatch_plan((tok, off), 2, 600)
+    mb = dpa.microbatch_plan((tok, off), 2, int(np.diff(off).max()) * 2)
     assert mb["info"]["trie_work"] == len(t["node_tokens"])
     assert sorted(np.unique(mb["mb_of_traj"]).tolist()) == list(range(mb["info"]["microbatches"]))
