@@ -465,6 +465,10 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
+    // opaque thread indices inside the chunk loop (see the backward kernel)
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
     const int j0 = c * kB;
     const bool has_next = c + 1 < nch;
     if (has_next) fetch_rows(ci, j0 + kB, beta, alpha, H, head, tid, nx);
@@ -623,6 +627,14 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
   int ex = sq.exp_off + sq.exp_cnt - 1;
 
   for (int c = nch - 1; c >= 0; --c) {
+    // The thread's indices, opaque to the compiler inside the chunk loop: otherwise it
+    // hoists hundreds of LDS fragment addresses out of the loop and spills them to
+    // scratch (or parks them in AGPRs), reloading them every chunk; recomputing them
+    // costs a few VALU ops.
+    int tid_o = threadIdx.x;
+    asm volatile("" : "+v"(tid_o));
+    const int tid = tid_o, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+    const int bm = wave >> 1, bn = wave & 1;
     const int j0 = c * kB;
     // -- consumers' initial-state gradients enter at exported boundaries ----------------
     if (ex >= sq.exp_off && exports[ex].chunk == c + 1) {
