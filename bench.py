@@ -401,10 +401,10 @@ def cpu_baseline(spec, plan, budget_s=15.0):
                    for u in np.nonzero(~has_child)[0]), reverse=True)
     done, total_t, total_flops = [], 0.0, 0.0
     scale = (t0, L0)                       # time estimate t * (L / L_ref)^2, refined by each run
-    for L in lens:
+    for L in lens + [lens[-1]]:                  # the shortest once more if nothing fitted
         if total_t >= 0.7 * budget_s:
             break
-        if scale[0] * (L / scale[1]) ** 2 > budget_s - total_t and done:
+        if scale[0] * (L / scale[1]) ** 2 > budget_s - total_t and (done or L != lens[-1]):
             continue
         t = run(L)
         scale = (t, L)
