@@ -234,8 +234,8 @@ def attn_packed_mask(spec, q, k, v, do, p: AttnParams, transitive: bool = True):
 class RowSampler:
     """Per-token evaluation of outputs and key gradients straight from V(t)."""
 
-    def __init__(self, spec, p: AttnParams, transitive: bool = True):
-        self.g = Dag(spec, transitive)
+    def __init__(self, spec, p: AttnParams, transitive: bool = True, view: str = "mounted"):
+        self.g = Dag(spec, transitive, view)
         self.p = p
         self.pos = self.g.token_positions()
         self.node_of, self.off = self.g.token_node()

@@ -277,9 +277,9 @@ class _TokenView:
         return self.data[self.idx[int(key)]]
 
 
-def _full_case(dpa, spec, seed, bwd, n_rows=24, n_keys=6, max_readers=96):
+def _full_case(dpa, spec, seed, bwd, n_rows=24, n_keys=6, max_readers=96, view="mounted"):
     tr = bool(spec.meta.get("transitive", True))
-    plan = dpa.Plan(spec, transitive=tr)
+    plan = dpa.Plan(spec, transitive=tr, view=view)
     p = dpa.AttnParams(16, 4, 128, "bf16")          # the benchmark's configuration (bf16 gradients)
     C = plan.rows
     q = synth.normal((C, 16, 128), seed, 1, DEV, torch.bfloat16)
@@ -293,7 +293,7 @@ def _full_case(dpa, spec, seed, bwd, n_rows=24, n_keys=6, max_readers=96):
     torch.cuda.synchronize()
     for n, t in res.items():
         assert torch.isfinite(t).all(), n
-    dag = Dag(spec, transitive=tr)
+    dag = Dag(spec, transitive=tr, view=view)
     rot, _ = plan.row_maps()
     rot_t = torch.as_tensor(rot, dtype=torch.long, device=DEV)
     kh = k[rot_t].float().cpu().numpy()
@@ -305,7 +305,7 @@ def _full_case(dpa, spec, seed, bwd, n_rows=24, n_keys=6, max_readers=96):
         if dag.length[u]:
             picks += [dag.offset[u], dag.offset[u] + dag.length[u] - 1]
     picks = np.array(sorted(set(int(x) for x in picks)))
-    rs = RowSampler(spec, OParams(16, 4), transitive=tr)
+    rs = RowSampler(spec, OParams(16, 4), transitive=tr, view=view)
     o_ref, l_ref = rs.rows(picks, _TokenView(q, rot_t, picks), kh, vh)
     _assert_close({"o": res["o"][rot_t[picks]].double().cpu().numpy(),
                    "lse": res["lse"][rot_t[picks]].double().cpu().numpy()},
@@ -333,6 +333,14 @@ def _full_case(dpa, spec, seed, bwd, n_rows=24, n_keys=6, max_readers=96):
                        "dv": res["dv"][rot_t[keys]].double().cpu().numpy()},
                       {"dk": dk_ref, "dv": dv_ref}, "bf16", names=("dk", "dv"), tag="sampled keys")
     return plan, res
+
+
+@pytest.mark.parametrize("view", ["mount_free", "unshifted"])
+def test_full_size_views_sampled(dpa, view):
+    # the benchmark's views record: the 16-tree workload in the other two views
+    print(f"full-size view {view}", flush=True)
+    _full_case(dpa, synth.config3(), seed=1103, bwd=True, view=view)
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("which", ["w2", "w4", "w3"])
