@@ -377,7 +377,8 @@ __device__ __forceinline__ void solve_lower(const float* __restrict__ At, TX* __
 
 // (I + A)^T Y = D, left-looking: y_t = d_t - sum_{i > t} A[i][t] y_i, a dot
 // product with a contiguous run of row t of At.  Y overwrites D in `x`;
-// `emit(t, y_t)` sees every solved value.  Reads are grouped as in solve_lower;
+// `emit(t, y_t)` sees every solved value (a block's 16 values after the block's
+// substitution, off its dependent chain).  Reads are grouped as in solve_lower;
 // the additions keep their fixed order.
 template <typename TX, typename Emit>
 __device__ __forceinline__ void solve_upper_t(const float* __restrict__ At, TX* __restrict__ x, int ldx, int c,
@@ -408,8 +409,9 @@ __device__ __forceinline__ void solve_upper_t(const float* __restrict__ At, TX* 
 #pragma unroll
       for (int m = j + 1; m < 16; ++m) acc[j] = fmaf(-a[j & 1][m], acc[m], acc[j]);
       x[(16 * b + j) * ldx + c] = (TX)acc[j];
-      emit(16 * b + j, acc[j]);
     }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) emit(16 * b + j, acc[j]);
   }
 }
 
@@ -610,7 +612,11 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
   __shared__ __attribute__((aligned(16))) f16_t Pr[kB * LDP];   // scale E o QK, then dP~
   __shared__ __attribute__((aligned(16))) float Ar[kB * LDA];   // A^T, then dKk (fp16 [64][LDP])
   __shared__ float gs[kB], bs[kB], al[kB];
-  __shared__ int rw[kB], rsl_s[kB];
+  __shared__ int rw[kB];
+  // where row t's gradients go: 0 nowhere (past the sequence), 1 the replay buffer,
+  // 2 the side buffer of a replayed row, 3 its own dk / dv row; with the base offset
+  __shared__ int dst_kind[kB];
+  __shared__ int64_t dst_off[kB];
   __shared__ float red_dg[4][kB], red_g[4][kB], red_b[4][kB], red_e[4][kB], red_s[4], red_v[kB];
 
   const int head = blockIdx.x % H;
@@ -650,9 +656,26 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
     }
     state_to_lds(D, dSh, wave, lane);
     load_chunk<true>(ci, j0, k, q, dO, v, beta, alpha, H, head, Kr, Qr, dOr, dRr, rw, gs, bs, al, tid);
-    if (tid < kB) {  // side-buffer slot of each row with replays (looked up once, not per element)
-      const int row = rw[tid];
-      rsl_s[tid] = row >= 0 ? rep_slot[row] : -1;
+    if (tid < kB) {  // each row's destination, looked up once per chunk, not per element
+      const int t = tid, row = rw[t], j = j0 + t;
+      const int rs = row >= 0 ? rep_slot[row] : -1;
+      int kind;
+      int64_t off;
+      if (j >= sq.n_tok) {
+        kind = 0;
+        off = 0;
+      } else if (j < sq.n_replay) {
+        kind = 1;
+        off = ((int64_t)(sq.rep_off + j) * H + head) * kRep;
+      } else if (rs >= 0) {
+        kind = 2;
+        off = ((int64_t)rs * H + head) * 2 * kD;
+      } else {
+        kind = 3;
+        off = ((int64_t)row * H + head) * kD;
+      }
+      dst_kind[t] = kind;
+      dst_off[t] = off;
     }
     red_dg[wave][lane] = 0.f;
     red_g[wave][lane] = 0.f;
@@ -739,16 +762,12 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
     if (tid < kD) {
       const int col = tid;
       solve_upper_t<f16_t>(Ar, dRr, LDK, col, [&](int t, float y) {
-        const int j = j0 + t;
-        if (j >= sq.n_tok) return;
+        const int kind = dst_kind[t];
+        const int64_t off = dst_off[t];
         const float g = bs[t] * y;
-        if (j < sq.n_replay) {
-          rbuf[((int64_t)(sq.rep_off + j) * H + head) * kRep + kD + col] = g;
-        } else {
-          const int rs = rsl_s[t];
-          if (rs >= 0) rside[((int64_t)rs * H + head) * 2 * kD + kD + col] = g;
-          else st_g<TG>(dv + ((int64_t)rw[t] * H + head) * kD + col, g);
-        }
+        if (kind == 1) rbuf[off + kD + col] = g;
+        else if (kind == 2) rside[off + kD + col] = g;
+        else if (kind == 3) st_g<TG>(dv + off + col, g);
       });
     }
     __syncthreads();
@@ -971,15 +990,11 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = 32 * b2 + acc_row(r, hi);
-          const int j = j0 + t;
-          if (j >= sq.n_tok) continue;
-          if (j < sq.n_replay) {
-            rbuf[((int64_t)(sq.rep_off + j) * H + head) * kRep + cc] = ak[b2][r];
-          } else {
-            const int rsl = rsl_s[t];
-            if (rsl >= 0) rside[((int64_t)rsl * H + head) * 2 * kD + cc] = ak[b2][r];
-            else st_g<TG>(dk + ((int64_t)rw[t] * H + head) * kD + cc, ak[b2][r]);
-          }
+          const int kind = dst_kind[t];
+          const int64_t off = dst_off[t];
+          if (kind == 1) rbuf[off + cc] = ak[b2][r];
+          else if (kind == 2) rside[off + cc] = ak[b2][r];
+          else if (kind == 3) st_g<TG>(dk + off + cc, ak[b2][r]);
         }
     }
     __syncthreads();
