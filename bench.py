@@ -481,7 +481,7 @@ def main() -> int:
                     help="only run a plain 1 GiB -> 1 GiB device copy kernel 3 times (scales HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus "
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus "
               f"{args.gpus}).", file=sys.stderr)
         return 2
 
