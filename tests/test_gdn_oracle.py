@@ -162,7 +162,8 @@ def _golden_plan(name):
     return d, g.build(name=name)
 
 
-@pytest.mark.parametrize("name", ["harts_fig2_plan.json", "harts_case1_plan.json"])
+@pytest.mark.parametrize("name", ["harts_fig2_plan.json", "harts_case1_plan.json", "harts_case2_plan.json",
+                                  "harts_case3_plan.json"])
 def test_planner_reproduces_the_pages_examples(name):
     d, spec = _golden_plan(name)
     B = d["chunk"]

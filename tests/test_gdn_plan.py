@@ -51,7 +51,8 @@ def _golden(name):
     return d, g.build(name=name)
 
 
-@pytest.mark.parametrize("name", ["harts_fig2_plan.json", "harts_case1_plan.json"])
+@pytest.mark.parametrize("name", ["harts_fig2_plan.json", "harts_case1_plan.json", "harts_case2_plan.json",
+                                  "harts_case3_plan.json"])
 def test_schedule_on_the_pages_examples(name):
     d, spec = _golden(name)
     plan, got = _check(spec, d["chunk"])
