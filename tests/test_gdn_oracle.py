@@ -184,6 +184,26 @@ def test_planner_reproduces_the_pages_examples(name):
         assert r == [s["call"]], s["name"]
 
 
+def test_planner_on_fig3_fork_inside_a_chunk():
+    # HARTS Fig. 3(a)-(b): the shared path P0-P1 forks into A, B, C after P1, inside a
+    # chunk; A continues directly (round 1: P0-P1-A), and B and C run together in
+    # round 2, each replaying P1 from the state H0 at the chunk boundary after P0.  The
+    # figure prints no sizes: P0 is one chunk and P1 ten tokens of the next.
+    B = 64
+    g = D.DagBuilder()
+    p = g.node(-1, B + 10)
+    for n in (20, 30, 40):
+        g.node(p, n)
+    segs = gdn_plan.segments(g.build())
+    t_pre, _ = gdn_plan.min_calls(segs, B)
+    assert t_pre[0] == 2
+    seqs = gdn_plan.recover(segs, B)
+    assert [(s.round, s.segs, s.replay) for s in seqs] == [(1, [0, 1], (0, 0)), (2, [2], (B, B + 10)),
+                                                            (2, [3], (B, B + 10))]
+    assert seqs[1].init == seqs[2].init == (0, B)       # H0: exported by round 1 at the boundary after P0
+    assert gdn_plan.replay_total(segs, B) == 20
+
+
 def _random_tree(rng, n=9, max_len=9):
     g = D.DagBuilder()
     for u in range(n):

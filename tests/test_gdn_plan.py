@@ -60,6 +60,23 @@ def test_schedule_on_the_pages_examples(name):
     assert plan.info["gdn_replay"] == d["replay_total"]
 
 
+def test_schedule_on_fig3_fork_inside_a_chunk():
+    # HARTS Fig. 3(b): B and C start in round 2 from the boundary state after P0 and
+    # replay P1 (P0 one chunk, P1 ten tokens of the next; the figure prints no sizes)
+    g = D.DagBuilder()
+    p = g.node(-1, 74)
+    for n in (20, 30, 40):
+        g.node(p, n)
+    plan = dpa.Plan(g.build(), gdn_chunk=64)
+    seqs = plan.gdn_seqs()
+    assert plan.info["gdn_rounds"] == 2 and plan.info["gdn_replay"] == 20
+    side = [s for s in seqs if s["round"] == 2]
+    assert len(side) == 2
+    for s in side:
+        assert (s["start"], s["fork"], s["init_boundary"]) == (64, 74, 64)
+        assert seqs[s["init_seq"]]["round"] == 1
+
+
 @pytest.mark.parametrize("seed", range(30))
 @pytest.mark.parametrize("B", [1, 4, 64])
 def test_schedule_matches_oracle_on_random_dags(seed, B):
