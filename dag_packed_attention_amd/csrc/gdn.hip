@@ -167,54 +167,6 @@ struct ChunkIn {
   int n_tok, n_replay;
 };
 
-// Load chunk c's K and Q (and dO) rows into LDS as fp16, row numbers, beta and the
-// cumulative log decay.  Tokens past the sequence's end are zero (beta = 0,
-// log alpha = 0), which makes them inert in every product.
-template <bool kDO>
-__device__ __forceinline__ void load_chunk(const ChunkIn& ci, int j0, const bf16_t* __restrict__ k,
-                                           const bf16_t* __restrict__ q, const bf16_t* __restrict__ dO,
-                                           const bf16_t* __restrict__ v, const float* __restrict__ beta,
-                                           const float* __restrict__ alpha, int H, int head, f16_t* Kr, f16_t* Qr,
-                                           f16_t* dOr, f16_t* Vr, int* rw, float* gs, float* bs, float* al,
-                                           int tid) {
-  for (int i = tid; i < kB * 16; i += 256) {
-    const int t = i >> 4, c8 = (i & 15) * 8;
-    const int j = j0 + t;
-    f16x8 kk = {}, qq = {}, dd = {}, vv = {};
-    if (j < ci.n_tok) {
-      const int64_t base = ((int64_t)ci.rows[j] * H + head) * kD + c8;
-      kk = bf8_to_h8(*reinterpret_cast<const uint4*>(k + base));
-      qq = bf8_to_h8(*reinterpret_cast<const uint4*>(q + base));
-      if (kDO && j >= ci.n_replay) dd = bf8_to_h8(*reinterpret_cast<const uint4*>(dO + base));
-      if (Vr) vv = bf8_to_h8(*reinterpret_cast<const uint4*>(v + base));
-    }
-    *reinterpret_cast<f16x8*>(Kr + t * LDK + c8) = kk;
-    *reinterpret_cast<f16x8*>(Qr + t * LDK + c8) = qq;
-    if (kDO) *reinterpret_cast<f16x8*>(dOr + t * LDK + c8) = dd;
-    if (Vr) *reinterpret_cast<f16x8*>(Vr + t * LDK + c8) = vv;
-  }
-  if (tid < kB) {
-    const int t = tid, j = j0 + t;
-    int row = -1;
-    float b = 0.f, la = 0.f, a = 1.f;
-    if (j < ci.n_tok) {
-      row = ci.rows[j];
-      b = beta[(int64_t)row * H + head];
-      a = alpha[(int64_t)row * H + head];
-      la = logf(a);
-    }
-    rw[t] = row;
-    bs[t] = b;
-    if (al) al[t] = a;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(la, off, 64);
-      if (t >= off) la += y;
-    }
-    gs[t] = la;
-  }
-}
-
 // Write the state accumulators (wave w: dv rows 32 w .., four dk blocks) as fp16 into
 // an LDS tile [dv][LDK].
 __device__ __forceinline__ void state_to_lds(const f32x16 (&S)[4], f16_t* Sh, int wave, int lane) {
@@ -307,6 +259,79 @@ __device__ __forceinline__ void commit_chunk(const ChunkRegs& nx, f16_t* Kr, f16
   if (tid < kB) {
     rw[tid] = nx.row;
     bs[tid] = nx.b;
+    float la = logf(nx.a);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(la, off, 64);
+      if (tid >= off) la += y;
+    }
+    gs[tid] = la;
+  }
+}
+
+// The backward's next chunk (the one before the current), fetched into registers in
+// two steps while the current chunk computes: its row numbers first, then the K, Q,
+// dO, V pieces and the gates once the row numbers have arrived.
+struct BwdRegs {
+  uint4 k4[4], q4[4], d4[4], v4[4];  // rows (tid >> 4) + 16 m, columns 8 (tid & 15) ..
+  int r4[4];                         // those rows' compact row (-1 past the sequence)
+  int row;                           // tid < 64: token tid's compact row (-1 past the end)
+  float b, a;                        //           and its beta, alpha
+};
+
+__device__ __forceinline__ void bwd_fetch_rows(const ChunkIn& ci, int j0, int tid, BwdRegs& nx) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int j = j0 + (tid >> 4) + 16 * m;
+    nx.r4[m] = j < ci.n_tok ? ci.rows[j] : -1;
+  }
+  if (tid < kB) nx.row = j0 + tid < ci.n_tok ? ci.rows[j0 + tid] : -1;
+}
+
+__device__ __forceinline__ void bwd_fetch_data(const ChunkIn& ci, int j0, const bf16_t* __restrict__ k,
+                                               const bf16_t* __restrict__ q, const bf16_t* __restrict__ dO,
+                                               const bf16_t* __restrict__ v, const float* __restrict__ beta,
+                                               const float* __restrict__ alpha, int H, int head, int tid,
+                                               BwdRegs& nx) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int j = j0 + (tid >> 4) + 16 * m;
+    nx.k4[m] = nx.q4[m] = nx.d4[m] = nx.v4[m] = make_uint4(0, 0, 0, 0);
+    if (nx.r4[m] >= 0) {
+      const int64_t base = ((int64_t)nx.r4[m] * H + head) * kD + (tid & 15) * 8;
+      nx.k4[m] = *reinterpret_cast<const uint4*>(k + base);
+      nx.q4[m] = *reinterpret_cast<const uint4*>(q + base);
+      nx.v4[m] = *reinterpret_cast<const uint4*>(v + base);
+      if (j >= ci.n_replay) nx.d4[m] = *reinterpret_cast<const uint4*>(dO + base);
+    }
+  }
+  if (tid < kB) {
+    nx.b = 0.f;
+    nx.a = 1.f;
+    if (nx.row >= 0) {
+      nx.b = beta[(int64_t)nx.row * H + head];
+      nx.a = alpha[(int64_t)nx.row * H + head];
+    }
+  }
+}
+
+// Make the fetched chunk current: K, Q, dO, V rows as fp16 in LDS, row numbers, beta,
+// alpha and the cumulative log decay.  Tokens past the sequence's end are zero (beta
+// = 0, log alpha = 0), which makes them inert in every product.
+__device__ __forceinline__ void bwd_commit(const BwdRegs& nx, f16_t* Kr, f16_t* Qr, f16_t* dOr, f16_t* Vr, int* rw,
+                                           float* gs, float* bs, float* al, int tid) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int t = (tid >> 4) + 16 * m, c8 = (tid & 15) * 8;
+    *reinterpret_cast<f16x8*>(Kr + t * LDK + c8) = bf8_to_h8(nx.k4[m]);
+    *reinterpret_cast<f16x8*>(Qr + t * LDK + c8) = bf8_to_h8(nx.q4[m]);
+    *reinterpret_cast<f16x8*>(dOr + t * LDK + c8) = bf8_to_h8(nx.d4[m]);
+    *reinterpret_cast<f16x8*>(Vr + t * LDK + c8) = bf8_to_h8(nx.v4[m]);
+  }
+  if (tid < kB) {
+    rw[tid] = nx.row;
+    bs[tid] = nx.b;
+    al[tid] = nx.a;
     float la = logf(nx.a);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -631,6 +656,11 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) D[nb] = zero16();
   int ex = sq.exp_off + sq.exp_cnt - 1;
+  BwdRegs nx;
+  if (nch > 0) {
+    bwd_fetch_rows(ci, (nch - 1) * kB, tid, nx);
+    bwd_fetch_data(ci, (nch - 1) * kB, k, q, dO, v, beta, alpha, H, head, tid, nx);
+  }
 
   for (int c = nch - 1; c >= 0; --c) {
     // The thread's indices, opaque to the compiler inside the chunk loop: otherwise it
@@ -655,7 +685,8 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
       --ex;
     }
     state_to_lds(D, dSh, wave, lane);
-    load_chunk<true>(ci, j0, k, q, dO, v, beta, alpha, H, head, Kr, Qr, dOr, dRr, rw, gs, bs, al, tid);
+    bwd_commit(nx, Kr, Qr, dOr, dRr, rw, gs, bs, al, tid);
+    if (c > 0) bwd_fetch_rows(ci, j0 - kB, tid, nx);
     if (tid < kB) {  // each row's destination, looked up once per chunk, not per element
       const int t = tid, row = rw[t], j = j0 + t;
       const int rs = row >= 0 ? rep_slot[row] : -1;
@@ -722,10 +753,11 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = 32 * b2 + acc_row(r, hi);
-          const float vv = (float)dRr[t * LDK + cc];  // V rows, staged by load_chunk
+          const float vv = (float)dRr[t * LDK + cc];  // V rows, staged by bwd_commit
           Ur[t * LDK + cc] = (f16_t)(bs[t] * (vv - __expf(gs[t]) * ks[b2][r]));
         }
     }
+    if (c > 0) bwd_fetch_data(ci, j0 - kB, k, q, dO, v, beta, alpha, H, head, tid, nx);
     __syncthreads();
     if (tid < kD) solve_lower<f16_t, false>(Ar, Ur, LDK, nullptr, tid);
     __syncthreads();
