@@ -320,6 +320,70 @@ def conv_time(dpa, plan, dev, steps, warmup):
                                  else None}}}
 
 
+def attn_alg_bytes(C: int) -> dict:
+    """Algorithmic HBM bytes per launch of the attention kernels over C rows (page
+    padding included: the kernels stream whole pages): each input read once and each
+    output written once.  Forward: fp16 q, k, v in; o (bf16) with its fp16 low part
+    and lse (fp32) out.  dK/dV: fp16 q, dO, k, v and the (lse, rowsum) float2 per row
+    and query head in; dk, dv out.  dQ: fp16 q, dO, k, v and the transposed k copy,
+    the row statistics in; dq out."""
+    return {"fwd": C * (HQ + 2 * HKV) * D * 2 + C * HQ * D * 2 * 2 + C * HQ * 4,
+            "dkdv": C * (2 * HQ + 2 * HKV) * D * 2 + C * HQ * 8 + C * 2 * HKV * D * 2,
+            "dq": C * (2 * HQ + 3 * HKV) * D * 2 + C * HQ * 8 + C * HQ * D * 2}
+
+
+def gather_time(dpa, dev, steps, warmup):
+    """Page-gather diagnostic: the 16-tree topology with segments of 1-64 tokens.  Pages
+    hold few tokens and query blocks few rows, so every K/V or Q/dO tile a work-group
+    stages feeds few products and the attention kernels stream tiles from HBM.  Per
+    kernel: ms per launch, counted TFLOP/s, and GB/s on the algorithmic bytes and (when
+    the committed counter summary was taken on the current source) on the measured HBM
+    bytes, both against 8 TB/s."""
+    import torch
+    import synth
+    spec = synth.dags.config3_short_segments()
+    plan = dpa.Plan(spec)
+    info = plan.info
+    p = dpa.AttnParams(HQ, HKV, D, "bf16")
+    tensors, ws = alloc(dpa, plan, p, 1013, dev)
+    plan.upload()
+    run_steps(dpa, plan, p, tensors, ws, warmup)
+    torch.cuda.synchronize()
+    plan.timing_enable(True, capacity=8 * (steps + 1))
+    t0 = time.perf_counter()
+    run_steps(dpa, plan, p, tensors, ws, steps)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+    kt = plan.timing_read()
+    plan.timing_enable(False)
+    C, P = info["rows"], info["visible_pairs"]
+    f_fwd = 4.0 * D * HQ * P
+    flops = {"fwd": f_fwd, "dkdv": 2.0 * f_fwd, "dq": 0.5 * f_fwd}
+    alg = attn_alg_bytes(C)
+    traffic = step_traffic_record("hbm_traffic_gather.json", "kernels.hip", "kernels_hip_sha256_16")
+    kern = {}
+    for k in ("fwd", "dkdv", "dq"):
+        ms = kt[k][0] / max(kt[k][1], 1)
+        gbs = alg[k] / (ms * 1e-3) / 1e9
+        tr = traffic.get(k)
+        kern[k] = {"ms": round(ms, 4), "tflops": round(flops[k] / (ms * 1e-3) / 1e12, 2),
+                   "alg_bytes": alg[k], "alg_gbps": round(gbs, 1), "alg_frac": round(gbs / HBM_PEAK_GBPS, 4),
+                   "traffic": tr,
+                   "traffic_gbps": round(tr / (ms * 1e-3) / 1e9, 1) if tr else None,
+                   "traffic_frac": round(tr / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4) if tr else None}
+    for k in ("prologue_fwd", "prologue_bwd"):
+        ms = kt[k][0] / max(kt[k][1], 1)
+        tr = traffic.get(k)
+        kern[k] = {"ms": round(ms, 4), "traffic": tr,
+                   "traffic_gbps": round(tr / (ms * 1e-3) / 1e9, 1) if tr else None}
+    del tensors, ws
+    torch.cuda.empty_cache()
+    return {"workload": "16-tree topology (seed %d) with segments of 1-64 tokens" % int(spec.meta["seed"]),
+            "unique_tokens": info["tokens"], "rows": C, "pages": info["pages"], "visible_pairs": P,
+            "ms_per_step": round(dt * 1e3, 3), "tflops": round(3.5 * f_fwd / dt / 1e12, 2),
+            "hbm_peak_gbps": HBM_PEAK_GBPS, "kernels": kern}
+
+
 def step_traffic_record(json_name: str, src_name: str, sha_key: str):
     """HBM bytes per launch of a step's kernels from its committed counter summary,
     if it was taken on the current source; {} otherwise."""
@@ -477,6 +541,9 @@ def main() -> int:
     ap.add_argument("--no-planner", action="store_true")
     ap.add_argument("--conv-only", action="store_true",
                     help="only time the short convolution (for profiling); prints its record")
+    ap.add_argument("--no-gather", action="store_true")
+    ap.add_argument("--gather-only", action="store_true",
+                    help="only time the page-gather diagnostic (for profiling); prints its record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB -> 1 GiB device copy kernel 3 times (scales HBM counters)")
     args = ap.parse_args()
@@ -500,6 +567,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration": {"bytes_read": src.numel() * 4, "bytes_written": dst.numel() * 4,
                                                "launches": 3}}))
+        return 0
+    if args.gather_only:
+        print(json.dumps({"gather": gather_time(dpa, dev, args.steps, args.warmup)}), flush=True)
         return 0
     t0 = time.perf_counter()
     spec = synth.config3()
@@ -584,6 +654,12 @@ def main() -> int:
         out["logprob"] = lp
         log(f"logprob: fwd {lp['fwd_ms']:.3f} ms ({lp['roofline']['fwd']['achieved']:.0f} GB/s), "
             f"bwd {lp['bwd_ms']:.3f} ms ({lp['roofline']['bwd']['achieved']:.0f} GB/s)")
+    if not args.no_gather:
+        ga = gather_time(dpa, dev, max(1, min(args.steps, 5)), 1)
+        out["gather"] = ga
+        log("gather diagnostic: " + ", ".join(f"{k} {v['ms']} ms" + (f" ({v['alg_gbps']:.0f} GB/s alg)"
+                                                                    if "alg_gbps" in v else "")
+                                              for k, v in ga["kernels"].items()))
     if not args.no_flat:
         t_flat, fpairs, frows, ntraj = flat_time(dpa, spec, plan, p, dev, args.flat_steps)
         out["x_vs_flat"] = round(t_flat / dt, 3)

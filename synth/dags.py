@@ -239,6 +239,17 @@ def config3(seed: int | None = None, **kw) -> DagSpec:
     return config3_structure(s, **kw)
 
 
+def config3_short_segments(seed: int | None = None, n_trees: int = 16) -> DagSpec:
+    """Page-gather diagnostic: workload 3's topology (same seed, depth, fan-out and
+    read rule) with segments of 1-64 tokens, so that pages hold few tokens and query
+    blocks few rows.  A read still asks for the source's last 256-2048 tokens, which
+    the short segments clip to the whole source."""
+    s = CONFIG3_SEED if seed is None else seed
+    spec = config3_structure(s, n_trees=n_trees, seg=(1, 64))
+    spec.name = f"trees16_short_segments(seed={s})"
+    return spec
+
+
 # ---------------------------------------------------------------------------
 # Workload 4: commander-worker episodes.  An 8192-token commander prefix forks 8
 # workers of 32768 own tokens; worker w reads at own offset 16384 + 2048 w the

@@ -148,7 +148,14 @@ def _mini4():
                          read_step=70)
 
 
-SMALL = {"mini2": _mini_trees2, "mini3": _mini3, "mini4": _mini4, "tiny": synth.config1}
+def _mini_short():
+    # the page-gather diagnostic's shape in small: segments of 1-64 tokens, most pages
+    # partly padding, reads clipped to whole sources
+    return synth.dags.config3_structure(7, n_trees=2, seg=(1, 64), depth_hi=3, fan=(2, 4))
+
+
+SMALL = {"mini2": _mini_trees2, "mini3": _mini3, "mini4": _mini4, "tiny": synth.config1,
+         "mini_short": _mini_short}
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -343,8 +350,10 @@ def test_full_size_views_sampled(dpa, view):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("which", ["w2", "w4", "w3"])
+@pytest.mark.parametrize("which", ["w2", "w4", "w3", "short"])
 def test_full_size_sampled(dpa, which):
-    spec = {"w2": synth.config2, "w4": synth.config4, "w3": synth.config3}[which]()
-    _full_case(dpa, spec, seed=1000 + int(which[1]), bwd=(which != "w2"))
+    spec = {"w2": synth.config2, "w4": synth.config4, "w3": synth.config3,
+            "short": synth.dags.config3_short_segments}[which]()
+    seed = {"w2": 1002, "w4": 1004, "w3": 1003, "short": 1013}[which]
+    _full_case(dpa, spec, seed=seed, bwd=(which != "w2"))
     torch.cuda.empty_cache()

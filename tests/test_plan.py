@@ -98,9 +98,10 @@ def test_transitive_golden():
         _compare(spec, transitive=tr)
 
 
-@pytest.mark.parametrize("which", ["w2", "w4", "w3"])
+@pytest.mark.parametrize("which", ["w2", "w4", "w3", "short"])
 def test_workload_plans(which):
-    spec = {"w2": synth.config2, "w4": synth.config4, "w3": synth.config3}[which]()
+    spec = {"w2": synth.config2, "w4": synth.config4, "w3": synth.config3,
+            "short": synth.dags.config3_short_segments}[which]()
     plan, dag = _compare(spec, transitive=bool(spec.meta.get("transitive", True)))
     if which == "w4":
         assert plan.info["tokens"] == 1_081_344
