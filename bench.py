@@ -188,14 +188,33 @@ def gdn_time(dpa, spec, dev, steps, warmup):
     wall = (time.perf_counter() - t0) / steps
     kt = plan.timing_read()
     plan.timing_enable(False)
+    # the same layer with the forward keeping every chunk's state for the backward
+    pk = dpa.GdnParams(GDN_H, grad_dtype="bf16", keep_states=True)
+    for _ in range(warmup):
+        dpa.gdn_fwd(plan, pk, q, k, v, b, a, o=o, ws=ws)
+        dpa.gdn_bwd(plan, pk, q, k, v, b, a, do, ws=ws, out=grads)
+    torch.cuda.synchronize()
+    plan.timing_enable(True, capacity=8 * (steps + 1))
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        dpa.gdn_fwd(plan, pk, q, k, v, b, a, o=o, ws=ws)
+        dpa.gdn_bwd(plan, pk, q, k, v, b, a, do, ws=ws, out=grads)
+    torch.cuda.synchronize()
+    wall_k = (time.perf_counter() - t0) / steps
+    ktk = plan.timing_read()
+    plan.timing_enable(False)
     ch = info["gdn_chunks"] * GDN_H
     ms = {n: kt[n][0] / max(kt[n][1], 1) for n in GDN_FLOPS}
+    msk = {n: ktk[n][0] / max(ktk[n][1], 1) for n in ("gdn_fwd", "gdn_bwd")}
     out = {"layer": "gated delta rule, 16 heads, dk = dv = 128, chunk 64, bf16 in / fp32 state",
            "rounds": info["gdn_rounds"], "sequences": info["gdn_sequences"], "replay_tokens": info["gdn_replay"],
            "chunks": info["gdn_chunks"], "fwd_ms": round(ms["gdn_fwd"], 3),
            "bwd_ms": round(ms["gdn_states"] + ms["gdn_bwd"], 3), "fwd_bwd_ms_wall": round(wall * 1e3, 3),
            "ms_per_launch": {n: round(v, 3) for n, v in ms.items()},
-           "mfma_tflops": {n: round(GDN_FLOPS[n] * ch / (ms[n] * 1e-3) / 1e12, 2) for n in GDN_FLOPS}}
+           "mfma_tflops": {n: round(GDN_FLOPS[n] * ch / (ms[n] * 1e-3) / 1e12, 2) for n in GDN_FLOPS},
+           "keep_states": {"fwd_ms": round(msk["gdn_fwd"], 3), "bwd_ms": round(msk["gdn_bwd"], 3),
+                           "fwd_bwd_ms_wall": round(wall_k * 1e3, 3),
+                           "state_bytes": int(info["gdn_chunks"]) * GDN_H * 2 * 128 * 128 * 2}}
     del q, k, v, b, a, do, o, grads, ws
     torch.cuda.empty_cache()
     return out
@@ -641,9 +660,13 @@ def main() -> int:
     if not args.no_gdn:
         g = gdn_time(dpa, spec, dev, max(1, min(args.steps, 3)), 1)
         g["hybrid_step_ms"] = round(dt * 1e3 + 3 * g["fwd_bwd_ms_wall"], 2)
+        # three layers keeping their states hold 3 x state_bytes from forward to backward
+        g["hybrid_step_ms_keep_states"] = round(dt * 1e3 + 3 * g["keep_states"]["fwd_bwd_ms_wall"], 2)
         out["gdn"] = g
         log(f"gdn layer: fwd {g['fwd_ms']:.2f} ms, bwd {g['bwd_ms']:.2f} ms ({g['rounds']} rounds, "
-            f"{g['sequences']} sequences); hybrid step {g['hybrid_step_ms']:.1f} ms")
+            f"{g['sequences']} sequences); hybrid step {g['hybrid_step_ms']:.1f} ms; keeping states: fwd "
+            f"{g['keep_states']['fwd_ms']:.2f} ms, bwd {g['keep_states']['bwd_ms']:.2f} ms, hybrid step "
+            f"{g['hybrid_step_ms_keep_states']:.1f} ms")
     if not args.no_conv:
         cv = conv_time(dpa, plan, dev, max(1, min(args.steps, 5)), 1)
         out["conv"] = cv

@@ -70,7 +70,7 @@ class DagAttnParams(ctypes.Structure):
 
 class DagGdnParams(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("grad_dtype", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("grad_dtype", ctypes.c_int32), ("scale", ctypes.c_float), ("keep_states", ctypes.c_int32)]
 
 
 class DagLogprobParams(ctypes.Structure):
@@ -390,10 +390,12 @@ class GdnParams:
     head_dim: int = 128
     scale: float = 0.0               # 0 -> 1
     grad_dtype: str = "bf16"         # dq/dk/dv element type: "bf16" or "fp32"
+    keep_states: bool = False        # forward saves chunk states in ws for the backward
 
     def c(self) -> DagGdnParams:
         m = {"bf16": DTYPE_BF16, "fp32": DTYPE_FP32}
-        return DagGdnParams(self.n_heads, self.head_dim, DTYPE_BF16, m[self.grad_dtype], float(self.scale))
+        return DagGdnParams(self.n_heads, self.head_dim, DTYPE_BF16, m[self.grad_dtype], float(self.scale),
+                            int(bool(self.keep_states)))
 
     @property
     def torch_grad_dtype(self):
@@ -416,8 +418,12 @@ def _check_gates(name, t, rows, heads, device):
 
 
 def gdn_fwd(plan: Plan, p: GdnParams, q, k, v, beta, alpha, o=None, ws=None, stream=None):
-    """``dag_gdn_fwd``: q, k, v [C,H,128] bf16, beta/alpha [C,H] fp32 -> o [C,H,128] bf16."""
+    """``dag_gdn_fwd``: q, k, v [C,H,128] bf16, beta/alpha [C,H] fp32 -> o [C,H,128] bf16.
+    With ``p.keep_states`` the caller passes ``ws`` (backward size) and hands the same
+    buffer, untouched, to ``gdn_bwd``."""
     import torch
+    if p.keep_states and ws is None:
+        raise ValueError("keep_states: pass the workspace that the backward will read")
     C, dev = plan.rows, q.device
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_tensor(name, t, C, p.n_heads, p.head_dim, torch.bfloat16, dev)
@@ -435,8 +441,11 @@ def gdn_fwd(plan: Plan, p: GdnParams, q, k, v, beta, alpha, o=None, ws=None, str
 
 
 def gdn_bwd(plan: Plan, p: GdnParams, q, k, v, beta, alpha, dO, ws=None, stream=None, out=None):
-    """``dag_gdn_bwd``: returns (dq, dk, dv [C,H,128] grad_dtype, dbeta, dalpha [C,H] fp32)."""
+    """``dag_gdn_bwd``: returns (dq, dk, dv [C,H,128] grad_dtype, dbeta, dalpha [C,H] fp32).
+    With ``p.keep_states``, ``ws`` must be the buffer the forward filled."""
     import torch
+    if p.keep_states and ws is None:
+        raise ValueError("keep_states: pass the workspace the forward filled")
     C, dev = plan.rows, q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("dO", dO)):
         _check_tensor(name, t, C, p.n_heads, p.head_dim, torch.bfloat16, dev)

@@ -323,6 +323,7 @@ dag_status check_gdn(const Plan& P, const dag_gdn_params* p) {
   if (p->grad_dtype != DAG_DTYPE_BF16 && p->grad_dtype != DAG_DTYPE_FP32)
     return set_err(DAG_E_UNSUPPORTED, "grad_dtype must be DAG_DTYPE_BF16 or DAG_DTYPE_FP32");
   if (!std::isfinite(p->scale)) return set_err(DAG_E_INVALID, "scale must be finite");
+  if (p->keep_states != 0 && p->keep_states != 1) return set_err(DAG_E_INVALID, "keep_states must be 0 or 1");
   return DAG_OK;
 }
 
@@ -653,7 +654,7 @@ dag_status dag_gdn_workspace(const dag_plan* plan, const dag_gdn_params* p, size
   dag_status st = check_gdn(plan->p, p);
   if (st != DAG_OK) return st;
   GdnWs w;
-  if (fwd_bytes) *fwd_bytes = carve_gdn(plan->p, p->n_heads, false, nullptr, &w);
+  if (fwd_bytes) *fwd_bytes = carve_gdn(plan->p, p->n_heads, p->keep_states != 0, nullptr, &w);
   if (bwd_bytes) *bwd_bytes = carve_gdn(plan->p, p->n_heads, true, nullptr, &w);
   return DAG_OK;
 }
@@ -667,19 +668,20 @@ dag_status dag_gdn_fwd(dag_plan* plan, const dag_gdn_params* p, const void* q, c
   if (P.info.rows == 0) return DAG_OK;
   if (!q || !k || !v || !beta || !alpha || !o) return set_err(DAG_E_INVALID, "null tensor pointer");
   GdnWs w;
-  const size_t need = carve_gdn(P, p->n_heads, false, nullptr, &w);
+  const bool keep = p->keep_states != 0;
+  const size_t need = carve_gdn(P, p->n_heads, keep, nullptr, &w);
   if (need && (!ws || ws_bytes < need))
     return set_err(DAG_E_WORKSPACE, "linear-attention forward workspace needs " + std::to_string(need) + " bytes");
   hipStream_t stream = (hipStream_t)hip_stream;
   if ((st = ensure_uploaded(P, stream)) != DAG_OK) return st;
-  carve_gdn(P, p->n_heads, false, ws, &w);
+  carve_gdn(P, p->n_heads, keep, ws, &w);
   const GdnShape g = gdn_shape(P, p);
   const DeviceTables& D = *P.dev;
   {
     Span sp(P, DAG_K_GDN_FWD, stream);
     for (int r = 0; r < P.info.gdn_rounds; ++r)
-      launch_gdn_fwd(g, P.ground_off[r + 1] - P.ground_off[r], D.ground_seq + P.ground_off[r], false,
-                     (const bf16_t*)q, (const bf16_t*)k, (const bf16_t*)v, beta, alpha, (bf16_t*)o, w.slots, nullptr,
+      launch_gdn_fwd(g, P.ground_off[r + 1] - P.ground_off[r], D.ground_seq + P.ground_off[r], (const bf16_t*)q,
+                     (const bf16_t*)k, (const bf16_t*)v, beta, alpha, (bf16_t*)o, w.slots, keep ? w.states : nullptr,
                      stream);
     launch_gdn_pad<bf16_t>(P.info.pages, D.page_nrows, (bf16_t*)o, p->n_heads, 128, stream);
   }
@@ -707,11 +709,11 @@ dag_status dag_gdn_bwd(dag_plan* plan, const dag_gdn_params* p, const void* q, c
   const DeviceTables& D = *P.dev;
   const int H = p->n_heads;
   const bf16_t *q16 = (const bf16_t*)q, *k16 = (const bf16_t*)k, *v16 = (const bf16_t*)v, *d16 = (const bf16_t*)dO;
-  {
+  if (!p->keep_states) {  // otherwise the forward left every chunk's state in ws
     Span sp(P, DAG_K_GDN_STATES, stream);
     for (int r = 0; r < P.info.gdn_rounds; ++r)
-      launch_gdn_fwd(g, P.ground_off[r + 1] - P.ground_off[r], D.ground_seq + P.ground_off[r], true, q16, k16, v16,
-                     beta, alpha, nullptr, w.slots, w.states, stream);
+      launch_gdn_fwd(g, P.ground_off[r + 1] - P.ground_off[r], D.ground_seq + P.ground_off[r], q16, k16, v16, beta,
+                     alpha, nullptr, w.slots, w.states, stream);
   }
   auto run = [&](auto* tag) {
     using TG = std::remove_pointer_t<decltype(tag)>;

@@ -441,10 +441,11 @@ __device__ __forceinline__ void solve_upper_t(const float* __restrict__ At, TX* 
 }
 
 // ---------------------------------------------------------------------------------
-// Forward (kStates = false: outputs; true: the backward's recomputation, which
-// instead saves every chunk's starting state).  Both export boundary states.
+// Forward.  kOut: the outputs; kSave: every chunk's starting state, saved for the
+// backward.  Outputs alone are the plain forward, states alone the backward's
+// recomputation, both a forward that keeps its states.  All export boundary states.
 // ---------------------------------------------------------------------------------
-template <bool kStates>
+template <bool kOut, bool kSave>
 __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
     const GSeq* __restrict__ seqs, const int32_t* __restrict__ order, const int32_t* __restrict__ grows,
     const GExport* __restrict__ exports, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
@@ -478,7 +479,7 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
     for (int nb = 0; nb < 4; ++nb) S[nb] = zero16();
   }
   state_to_lds(S, Sh, wave, lane);
-  if (kStates) state_save(S, states + ((int64_t)sq.chunk_off * H + head) * 2 * kD * kD, wave, lane);
+  if (kSave) state_save(S, states + ((int64_t)sq.chunk_off * H + head) * 2 * kD * kD, wave, lane);
   int ex = sq.exp_off;
   const int ex_end = sq.exp_off + sq.exp_cnt;
 
@@ -509,7 +510,7 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
         for (int s = 0; s < 8; ++s) {
           const f16x8 b = frag_n(Kr, LDK, 32 * bn, 16 * s, lane);
           kk = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), b, kk);
-          if (!kStates) qk = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), b, qk);
+          if (kOut) qk = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), b, qk);
         }
       }
       const int i = 32 * bn + l32;
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
         const int t = 32 * bm + acc_row(r, hi);
         const float e = i <= t ? __expf(gs[t] - gs[i]) : 0.f;
         Ar[i * LDA + t] = i < t ? bs[t] * e * kk[r] : 0.f;
-        if (!kStates) Pr[t * LDP + i] = (f16_t)(scale * e * qk[r]);
+        if (kOut) Pr[t * LDP + i] = (f16_t)(scale * e * qk[r]);
       }
     }
     {
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
     __syncthreads();
 
     // -- outputs: O = scale diag(gamma) Q S0^T + (scale E o QK) U -------------------------
-    if (!kStates) {
+    if (kOut) {
       f32x16 acc_o[2];
 #pragma unroll
       for (int bm = 0; bm < 2; ++bm) acc_o[bm] = zero16();
@@ -610,7 +611,7 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
     if (has_next) {
       commit_chunk(nx, Kr, Qr, Rr, rw, gs, bs, tid);
       state_to_lds(S, Sh, wave, lane);
-      if (kStates) state_save(S, states + ((int64_t)(sq.chunk_off + c + 1) * H + head) * 2 * kD * kD, wave, lane);
+      if (kSave) state_save(S, states + ((int64_t)(sq.chunk_off + c + 1) * H + head) * 2 * kD * kD, wave, lane);
       __syncthreads();
     }
   }
@@ -1125,17 +1126,20 @@ __global__ __launch_bounds__(256) void gdn_pad_kernel(T* __restrict__ x, const i
 // ---------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------
-void launch_gdn_fwd(const GdnShape& s, int n_seq, const int32_t* order, bool states_only, const bf16_t* q,
+void launch_gdn_fwd(const GdnShape& s, int n_seq, const int32_t* order, const bf16_t* q,
                     const bf16_t* k, const bf16_t* v, const float* beta, const float* alpha, bf16_t* o,
                     float* slots, f16_t* states, hipStream_t st) {
   if (n_seq <= 0) return;
   const dim3 grid((unsigned)(n_seq * s.H));
-  if (states_only)
-    gdn::gdn_fwd_kernel<true><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha, o,
-                                                    slots, states, s.H, s.scale);
+  if (o && states)
+    gdn::gdn_fwd_kernel<true, true><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha, o,
+                                                          slots, states, s.H, s.scale);
+  else if (states)
+    gdn::gdn_fwd_kernel<false, true><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha,
+                                                           o, slots, states, s.H, s.scale);
   else
-    gdn::gdn_fwd_kernel<false><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha, o,
-                                                     slots, states, s.H, s.scale);
+    gdn::gdn_fwd_kernel<true, false><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha,
+                                                           o, slots, states, s.H, s.scale);
 }
 
 template <typename TG>

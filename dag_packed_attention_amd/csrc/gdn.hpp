@@ -22,10 +22,12 @@ struct GdnShape {
   float scale;
 };
 
-// One round of the forward.  states_only: the backward's recomputation, which
-// writes no outputs and saves every chunk's starting state (fp16, [dv][dk] then
-// [dk][dv]) into `states`.  Both export boundary states into `slots` (fp32).
-void launch_gdn_fwd(const GdnShape& s, int n_seq, const int32_t* order, bool states_only, const bf16_t* q,
+// One round of the forward.  o non-null: write the outputs; states non-null: save
+// every chunk's starting state (fp16, [dv][dk] then [dk][dv]) into `states` (the
+// backward's recomputation passes only states; a forward that keeps its states for
+// the backward passes both).  Every variant exports boundary states into `slots`
+// (fp32).
+void launch_gdn_fwd(const GdnShape& s, int n_seq, const int32_t* order, const bf16_t* q,
                     const bf16_t* k, const bf16_t* v, const float* beta, const float* alpha, bf16_t* o,
                     float* slots, f16_t* states, hipStream_t st);
 // One round of the backward.

@@ -250,9 +250,18 @@ typedef struct {
   int32_t dtype;       /* q, k, v, o, dO element type; must be DAG_DTYPE_BF16    */
   int32_t grad_dtype;  /* dq, dk, dv: DAG_DTYPE_BF16 or DAG_DTYPE_FP32           */
   float scale;         /* output scale; 0 selects 1                              */
+  int32_t keep_states; /* 0: the backward recomputes every chunk's starting state
+                          from the inputs; 1: the forward saves them (fp16) into
+                          its workspace and the backward reads them there: pass
+                          the same ws to both calls and leave it untouched in
+                          between.  Trades a recomputation pass for keeping
+                          2 * H * 128 * 128 * 2 bytes per execution chunk alive
+                          from the forward to the backward                      */
 } dag_gdn_params;
 
-/* Workspace bytes for dag_gdn_fwd and dag_gdn_bwd. */
+/* Workspace bytes for dag_gdn_fwd and dag_gdn_bwd (with keep_states the two are
+ * equal: the forward fills the part of the backward's workspace that holds the
+ * states). */
 dag_status dag_gdn_workspace(const dag_plan* plan, const dag_gdn_params* p, size_t* fwd_bytes,
                              size_t* bwd_bytes);
 
@@ -260,7 +269,8 @@ dag_status dag_gdn_workspace(const dag_plan* plan, const dag_gdn_params* p, size
  * caller), v [C, H, dv] (dtype); beta, alpha [C, H] fp32 (beta in [0, 1], alpha in (0, 1]);
  * o [C, H, dv] (dtype) receives every token's output once.  One launch per
  * round; products on MFMA with fp16 operands and fp32 accumulation, state in
- * fp32.  ws: at least fwd_bytes. */
+ * fp32.  ws: at least fwd_bytes; with keep_states the call also leaves every
+ * chunk's starting state in ws for dag_gdn_bwd. */
 dag_status dag_gdn_fwd(dag_plan* plan, const dag_gdn_params* p, const void* q, const void* k,
                        const void* v, const float* beta, const float* alpha, void* o, void* ws,
                        size_t ws_bytes, void* hip_stream);
@@ -270,7 +280,8 @@ dag_status dag_gdn_fwd(dag_plan* plan, const dag_gdn_params* p, const void* q, c
  * exported boundary state is the sum over its consumers in a fixed order, and a
  * replayed token's contributions are added to its own row after its own
  * sequence's, in a fixed order: results are bitwise reproducible.  Recomputes
- * the forward's states; ws: at least bwd_bytes. */
+ * the forward's states, or with keep_states reads them from ws as the forward
+ * left it (same plan, same params, same inputs); ws: at least bwd_bytes. */
 dag_status dag_gdn_bwd(dag_plan* plan, const dag_gdn_params* p, const void* q, const void* k,
                        const void* v, const float* beta, const float* alpha, const void* dO,
                        void* dq, void* dk, void* dv, float* dbeta, float* dalpha, void* ws,

@@ -231,3 +231,89 @@ def _last_fork(dag, leaf):
 
 def _alive(dag, u):
     return dag.length[u] > 0 or any(_alive(dag, c) for c in dag.children[u])
+
+
+def _run_keep(dpa, spec, ins, h, grad="fp32", scale=0.0):
+    """Forward with keep_states, then the backward reading the states it left in ws;
+    ws is filled with NaN first, so nothing relies on a cleared workspace."""
+    q, k, v, b, a, do = ins
+    plan = dpa.Plan(spec, gdn_chunk=64)
+    p = dpa.GdnParams(h, scale=scale, grad_dtype=grad, keep_states=True)
+    fw, bw = dpa.gdn_workspace_bytes(plan, p)
+    assert fw == bw
+    ws = torch.full((max(bw, 4) // 4,), float("nan"), dtype=torch.float32, device=DEV).view(torch.uint8)
+    rows = lambda x: dpa.to_rows(plan, x.to(DEV), fill=float("nan"))
+    qr, kr, vr, br, ar, dr = (rows(x) for x in (q, k, v, b, a, do))
+    o = dpa.gdn_fwd(plan, p, qr, kr, vr, br, ar, ws=ws)
+    dq, dk, dv, db, da = dpa.gdn_bwd(plan, p, qr, kr, vr, br, ar, dr, ws=ws)
+    torch.cuda.synchronize()
+    out = {"o": o, "dq": dq, "dk": dk, "dv": dv, "dbeta": db, "dalpha": da}
+    return {n: dpa.from_rows(plan, t).double().cpu().numpy() for n, t in out.items()}
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_kept_states_match_the_oracle_and_the_recomputation(dpa, case):
+    # the forward that keeps its states runs the same state arithmetic as the
+    # backward's recomputation: outputs and gradients are bitwise those of the
+    # recomputing path, which the oracle pins
+    fn, args = CASES[case]
+    spec = fn(*args)
+    ins = _inputs(spec, 2, 500 + case, 0.05)
+    kept = _run_keep(dpa, spec, ins, 2)
+    _close(kept, _ref(spec, ins), tag=f"{spec.name} kept states")
+    recomputed, _ = _run(dpa, spec, ins, 2)
+    for n in NAMES:
+        assert np.array_equal(kept[n], recomputed[n]), n
+
+
+def test_kept_states_on_random_trees_two_calls(dpa):
+    rng = np.random.default_rng(9)
+    for it in range(3):                        # second and third call reuse nothing from the first
+        spec = synth.dags.random_tiny_dag(rng, n_nodes=12, max_len=150, n_roots=2)
+        ins = _inputs(spec, 3, 600 + it, 0.1)
+        kept = _run_keep(dpa, spec, ins, 3, grad="bf16", scale=0.5)
+        recomputed, _ = _run(dpa, spec, ins, 3, grad="bf16", scale=0.5)
+        for n in NAMES:
+            assert np.array_equal(kept[n], recomputed[n]), (it, n)
+
+
+def test_kept_states_need_the_workspace(dpa):
+    spec = _replay_chain()
+    plan = dpa.Plan(spec, gdn_chunk=64)
+    p = dpa.GdnParams(2, keep_states=True)
+    fw, bw = dpa.gdn_workspace_bytes(plan, p)
+    f0, b0 = dpa.gdn_workspace_bytes(plan, dpa.GdnParams(2))
+    assert fw == bw == b0 and f0 < b0
+    q = torch.zeros((plan.rows, 2, 128), dtype=torch.bfloat16, device=DEV)
+    g = torch.full((plan.rows, 2), 0.5, dtype=torch.float32, device=DEV)
+    with pytest.raises(ValueError):
+        dpa.gdn_fwd(plan, p, q, q, q, g, g)
+    small = torch.empty(f0, dtype=torch.uint8, device=DEV)
+    with pytest.raises(dpa.DagError):
+        dpa.gdn_fwd(plan, p, q, q, q, g, g, ws=small)
+
+
+def test_kept_states_on_the_sixteen_tree_workload(dpa):
+    """The benchmark's configuration (16 heads, bf16 gradients): keeping the states gives
+    bitwise the recomputing path's outputs and gradients at full size."""
+    spec = synth.dags.config3()
+    H = 16
+    ins = _inputs(spec, H, 1005, 1.0)
+    plan = dpa.Plan(spec, gdn_chunk=64)
+    rows = lambda x: dpa.to_rows(plan, x.to(DEV), fill=float("nan"))
+    qr, kr, vr, br, ar, dr = (rows(x) for x in ins)
+    del ins
+    p = dpa.GdnParams(H, grad_dtype="bf16")
+    o = dpa.gdn_fwd(plan, p, qr, kr, vr, br, ar)
+    ref = dpa.gdn_bwd(plan, p, qr, kr, vr, br, ar, dr)
+    pk = dpa.GdnParams(H, grad_dtype="bf16", keep_states=True)
+    _, bw = dpa.gdn_workspace_bytes(plan, pk)
+    ws = torch.empty(bw, dtype=torch.uint8, device=DEV)
+    ok = dpa.gdn_fwd(plan, pk, qr, kr, vr, br, ar, ws=ws)
+    assert torch.equal(o, ok)
+    del o, ok
+    got = dpa.gdn_bwd(plan, pk, qr, kr, vr, br, ar, dr, ws=ws)
+    for n, x, y in zip(("dq", "dk", "dv", "dbeta", "dalpha"), got, ref):
+        assert torch.equal(x, y), n
+    del ws, got, ref
+    torch.cuda.empty_cache()

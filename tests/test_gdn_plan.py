@@ -110,3 +110,16 @@ def test_schedule_bounds():
         dpa.Plan(D.config1(), gdn_chunk=-1)
     with pytest.raises(dpa.DagError):
         dpa.Plan(D.config1()).gdn_seqs()
+
+
+def test_kept_states_workspace_and_flag():
+    plan = dpa.Plan(D.config1(), gdn_chunk=64)
+    f0, b0 = dpa.gdn_workspace_bytes(plan, dpa.GdnParams(2))
+    fk, bk = dpa.gdn_workspace_bytes(plan, dpa.GdnParams(2, keep_states=True))
+    assert f0 < b0 and fk == bk == b0          # the forward fills the backward's state region
+    p = dpa.GdnParams(2)
+    cp = p.c()
+    cp.keep_states = 2
+    import ctypes
+    f, b = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert dpa._lib.dag_gdn_workspace(plan._h, ctypes.byref(cp), ctypes.byref(f), ctypes.byref(b)) != 0
