@@ -5,6 +5,7 @@
 #include <cstdio>
 #include <cstring>
 #include <new>
+#include <stdexcept>
 #include <type_traits>
 #include <string>
 #include <vector>
@@ -382,6 +383,12 @@ dag_status dag_build(const dag_node* nodes, int32_t n_nodes, const dag_mount* mo
   } catch (const std::bad_alloc&) {
     st = DAG_E_OVERFLOW;
     err = "out of host memory while building the plan";
+  } catch (const std::length_error&) {
+    st = DAG_E_OVERFLOW;
+    err = "a table of the plan exceeds the host's size limits";
+  } catch (const std::exception& e) {
+    st = DAG_E_INVALID;
+    err = std::string("building the plan failed: ") + e.what();
   }
   if (st != DAG_OK) {
     delete plan;
@@ -748,6 +755,10 @@ dag_status dag_plan_logprob_map(const dag_plan* plan, const int32_t* labels, int
     st = build_logprob_map(P, labels, &rows, &targets, &err);
   } catch (const std::bad_alloc&) {
     return set_err(DAG_E_OVERFLOW, "out of host memory building the position map");
+  } catch (const std::length_error&) {
+    return set_err(DAG_E_OVERFLOW, "sizes beyond the host's limits building the position map");
+  } catch (const std::exception& e) {
+    return set_err(DAG_E_INVALID, std::string("building the position map failed: ") + e.what());
   }
   if (st != DAG_OK) return set_err(st, err);
   const int64_t n = (int64_t)rows.size();
@@ -921,6 +932,10 @@ dag_status dag_trie_build(const int32_t* tokens, const int64_t* traj_off, int32_
     st = trie_build(tokens, traj_off, n_traj, &t, &err);
   } catch (const std::bad_alloc&) {
     return set_err(DAG_E_OVERFLOW, "out of host memory building the trie");
+  } catch (const std::length_error&) {
+    return set_err(DAG_E_OVERFLOW, "sizes beyond the host's limits building the trie");
+  } catch (const std::exception& e) {
+    return set_err(DAG_E_INVALID, std::string("building the trie failed: ") + e.what());
   }
   if (st != DAG_OK) return set_err(st, err);
   *n_nodes = (int32_t)t.nodes.size();
@@ -947,6 +962,10 @@ dag_status dag_microbatch_plan(const int32_t* tokens, const int64_t* traj_off, i
     st = microbatch_plan(tokens, traj_off, n_traj, opts, &m, &err);
   } catch (const std::bad_alloc&) {
     return set_err(DAG_E_OVERFLOW, "out of host memory planning microbatches");
+  } catch (const std::length_error&) {
+    return set_err(DAG_E_OVERFLOW, "sizes beyond the host's limits planning microbatches");
+  } catch (const std::exception& e) {
+    return set_err(DAG_E_INVALID, std::string("planning microbatches failed: ") + e.what());
   }
   if (st != DAG_OK) return set_err(st, err);
   *info = m.info;

@@ -209,7 +209,7 @@ dag_status build_gdn_schedule(Plan* P, int32_t B, std::string* err) {
     g.init_slot = -1;
     g.cgrad = -1;
     g.chunk_off = (int32_t)chunks;
-    chunks += (g.n_tok + B - 1) / B;
+    chunks += ((int64_t)g.n_tok + B - 1) / B;
     if (chunks > INT32_MAX) return gfail(err, "schedule chunks %lld overflow int32", chunks);
     replay_total += g.n_replay;
     rounds = std::max(rounds, s.round);
@@ -238,7 +238,7 @@ dag_status build_gdn_schedule(Plan* P, int32_t B, std::string* err) {
       it = slot_of.emplace(key, slot).first;
       const GSeq& pr = P->gseqs[key.first];
       const int64_t c = (key.second - pr.start) / B;
-      if (c < 1 || c > (pr.n_tok + B - 1) / B) {
+      if (c < 1 || c > ((int64_t)pr.n_tok + B - 1) / B) {
         *err = "internal: exported boundary outside its producer";
         return DAG_E_INVALID;
       }

@@ -231,7 +231,7 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
   int64_t slots = 0, tokens = 0;
   for (int32_t u = 0; u < n; ++u) {
     P->slot0[u] = (int32_t)std::min<int64_t>(slots, INT32_MAX);
-    P->npages[u] = (P->length[u] + kPage - 1) / kPage;
+    P->npages[u] = (int32_t)(((int64_t)P->length[u] + kPage - 1) / kPage);  // int64: lengths reach 2^31 - 1
     P->tok_off[u] = tokens;
     slots += P->npages[u];
     tokens += P->length[u];

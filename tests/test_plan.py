@@ -188,3 +188,28 @@ def test_host_compactor_under_sanitizers(tmp_path):
     r = subprocess.run([str(exe), "300"], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "ok" in r.stdout
+
+
+def test_positions_and_rows_beyond_int32_are_rejected():
+    # positions: a 2^30-token child of a 2^30-token root ends at position 2^31
+    b = synth.DagBuilder()
+    r = b.node(-1, 1 << 30)
+    b.node(r, 1 << 30)
+    with pytest.raises(dpa.DagError) as e:
+        dpa.Plan(b.build())
+    assert e.value.code == "OVERFLOW"
+    # a mount moves the reader's start past int32 even though its own chain is short
+    b = synth.DagBuilder()
+    a = b.node(-1, (1 << 31) - 2)
+    c = b.node(-1, 1)
+    b.mount(c, a, (1 << 31) - 3, (1 << 31) - 2)
+    with pytest.raises(dpa.DagError) as e:
+        dpa.Plan(b.build())
+    assert e.value.code == "OVERFLOW"
+    # compact rows: 40 roots of 2^26 tokens need 40 * 2^26 > 2^31 - 1 rows
+    b = synth.DagBuilder()
+    for _ in range(40):
+        b.node(-1, 1 << 26)
+    with pytest.raises(dpa.DagError) as e:
+        dpa.Plan(b.build())
+    assert e.value.code == "OVERFLOW"
