@@ -343,16 +343,22 @@ __device__ __forceinline__ void bwd_commit(const BwdRegs& nx, f16_t* Kr, f16_t* 
 }
 
 // Triangular solves with the unit-lower matrix I + A (A strictly lower), for
-// the 128 columns of an [64][.] tile; thread c (< 128) owns column c.  A is
-// kept transposed in LDS (At[i][t] = A[t][i], row stride LDA).  Rows go in four
-// blocks of 16: a block first takes the contributions of the solved blocks
-// (a runtime loop over their rows), then solves its own 16 rows in registers.
+// the 128 columns of an [64][.] tile, by all 256 threads: lanes l and l ^ 32 of
+// wave w share column c = 32 w + (l & 31), and lane half h = l >> 5 takes target
+// rows 8 h .. 8 h + 7 of each 16-row block in the updates from the solved blocks
+// (a runtime loop over their rows).  The two halves then swap their partial sums
+// and both run the block's own 16-row substitution in registers and store all 16
+// solved rows (the same values to the same addresses), so every lane later reads
+// only rows it wrote itself.  Each element sees its additions in the same order as
+// with one thread per column.  A is kept transposed in LDS (At[i][t] = A[t][i], row
+// stride LDA).
 
-// 16 consecutive entries At[row][col0 .. col0 + 15] (broadcast LDS reads).
-__device__ __forceinline__ void at_row16(const float* At, int row, int col0, float (&a)[16]) {
+// n consecutive entries At[row][col0 .. col0 + n - 1] (broadcast LDS reads).
+template <int n>
+__device__ __forceinline__ void at_row(const float* At, int row, int col0, float (&a)[n]) {
   const float4* p = reinterpret_cast<const float4*>(At + row * LDA + col0);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < n / 4; ++q) {
     const float4 v = p[q];
     a[4 * q] = v.x;
     a[4 * q + 1] = v.y;
@@ -361,37 +367,50 @@ __device__ __forceinline__ void at_row16(const float* At, int row, int col0, flo
   }
 }
 
+// Both halves' 8 partial sums as the block's 16 (lane half h holds rows 8 h ..).
+__device__ __forceinline__ void join_halves(const float (&part)[8], int h, float (&full)[16]) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float o = __shfl_xor(part[j], 32, 64);
+    full[j] = h ? o : part[j];
+    full[8 + j] = h ? part[j] : o;
+  }
+}
+
 // (I + A) X = R, right-looking: once x_i is final, every later row t takes
 // -A[t][i] x_i, and A[t][i] for t in a block is a contiguous run of row i of At.
 // X overwrites R in `x` (row stride ldx); the solved rows also go to `out` as
 // fp16 if kOut.  The solved rows' contributions are taken four rows at a time
 // with all their LDS reads issued first, and row m + 1's coefficients are read
-// while row m is finished, so the loop waits on LDS once per group instead of
-// once per read.  The order of the additions is fixed (row by row, ascending).
+// while row m is finished.  The order of the additions is fixed (row by row,
+// ascending).
 template <typename TX, bool kOut>
 __device__ __forceinline__ void solve_lower(const float* __restrict__ At, TX* __restrict__ x, int ldx,
-                                            f16_t* __restrict__ out, int c) {
+                                            f16_t* __restrict__ out, int tid) {
+  const int c = 32 * (tid >> 6) + (tid & 31), h = (tid >> 5) & 1;
   for (int b = 0; b < 4; ++b) {
-    float acc[16];
+    float part[8];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = (float)x[(16 * b + j) * ldx + c];
+    for (int j = 0; j < 8; ++j) part[j] = (float)x[(16 * b + 8 * h + j) * ldx + c];
     for (int i = 0; i < 16 * b; i += 4) {
-      float xi[4], a[4][16];
+      float xi[4], a[4][8];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         xi[u] = (float)x[(i + u) * ldx + c];
-        at_row16(At, i + u, 16 * b, a[u]);
+        at_row<8>(At, i + u, 16 * b + 8 * h, a[u]);
       }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int j = 0; j < 16; ++j) acc[j] = fmaf(-a[u][j], xi[u], acc[j]);
+        for (int j = 0; j < 8; ++j) part[j] = fmaf(-a[u][j], xi[u], part[j]);
     }
+    float acc[16];
+    join_halves(part, h, acc);
     float a[2][16];
-    at_row16(At, 16 * b, 16 * b, a[0]);
+    at_row<16>(At, 16 * b, 16 * b, a[0]);
 #pragma unroll
     for (int m = 0; m < 16; ++m) {
-      if (m < 15) at_row16(At, 16 * b + m + 1, 16 * b, a[(m + 1) & 1]);
+      if (m < 15) at_row<16>(At, 16 * b + m + 1, 16 * b, a[(m + 1) & 1]);
 #pragma unroll
       for (int j = m + 1; j < 16; ++j) acc[j] = fmaf(-a[m & 1][j], acc[m], acc[j]);
       x[(16 * b + m) * ldx + c] = (TX)acc[m];
@@ -402,41 +421,44 @@ __device__ __forceinline__ void solve_lower(const float* __restrict__ At, TX* __
 
 // (I + A)^T Y = D, left-looking: y_t = d_t - sum_{i > t} A[i][t] y_i, a dot
 // product with a contiguous run of row t of At.  Y overwrites D in `x`;
-// `emit(t, y_t)` sees every solved value (a block's 16 values after the block's
-// substitution, off its dependent chain).  Reads are grouped as in solve_lower;
-// the additions keep their fixed order.
+// `emit(t, c, y_t)` sees every solved value once (the lane half that owns row t,
+// after the block's substitution, off its dependent chain).  Reads are grouped as
+// in solve_lower; the additions keep their fixed order.
 template <typename TX, typename Emit>
-__device__ __forceinline__ void solve_upper_t(const float* __restrict__ At, TX* __restrict__ x, int ldx, int c,
+__device__ __forceinline__ void solve_upper_t(const float* __restrict__ At, TX* __restrict__ x, int ldx, int tid,
                                               Emit emit) {
+  const int c = 32 * (tid >> 6) + (tid & 31), h = (tid >> 5) & 1;
   for (int b = 3; b >= 0; --b) {
-    float acc[16], y[16];
+    float part[8], y[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc[j] = (float)x[(16 * b + j) * ldx + c];
+    for (int j = 0; j < 8; ++j) part[j] = (float)x[(16 * b + 8 * h + j) * ldx + c];
     for (int ib = b + 1; ib < 4; ++ib) {
 #pragma unroll
       for (int m = 0; m < 16; ++m) y[m] = (float)x[(16 * ib + m) * ldx + c];
 #pragma unroll
-      for (int j0 = 0; j0 < 16; j0 += 4) {
+      for (int j0 = 0; j0 < 8; j0 += 4) {
         float a[4][16];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) at_row16(At, 16 * b + j0 + u, 16 * ib, a[u]);
+        for (int u = 0; u < 4; ++u) at_row<16>(At, 16 * b + 8 * h + j0 + u, 16 * ib, a[u]);
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-          for (int m = 0; m < 16; ++m) acc[j0 + u] = fmaf(-a[u][m], y[m], acc[j0 + u]);
+          for (int m = 0; m < 16; ++m) part[j0 + u] = fmaf(-a[u][m], y[m], part[j0 + u]);
       }
     }
+    float acc[16];
+    join_halves(part, h, acc);
     float a[2][16];
-    at_row16(At, 16 * b + 15, 16 * b, a[1]);
+    at_row<16>(At, 16 * b + 15, 16 * b, a[1]);
 #pragma unroll
     for (int j = 15; j >= 0; --j) {
-      if (j > 0) at_row16(At, 16 * b + j - 1, 16 * b, a[(j - 1) & 1]);
+      if (j > 0) at_row<16>(At, 16 * b + j - 1, 16 * b, a[(j - 1) & 1]);
 #pragma unroll
       for (int m = j + 1; m < 16; ++m) acc[j] = fmaf(-a[j & 1][m], acc[m], acc[j]);
       x[(16 * b + j) * ldx + c] = (TX)acc[j];
     }
 #pragma unroll
-    for (int j = 0; j < 16; ++j) emit(16 * b + j, acc[j]);
+    for (int j = 0; j < 8; ++j) emit(16 * b + 8 * h + j, c, h ? acc[8 + j] : acc[j]);
   }
 }
 
@@ -546,7 +568,7 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
     if (has_next) fetch_kqv(rwn, k, q, v, H, head, tid, nx);
 
     // -- U = (I + A)^{-1} R  (only the state is live across the solve) ------------------
-    if (tid < kD) solve_lower<float, true>(Ar, Rr, LDR, Ur, tid);
+    solve_lower<float, true>(Ar, Rr, LDR, Ur, tid);
     __syncthreads();
 
     // -- outputs: O = scale diag(gamma) Q S0^T + (scale E o QK) U -------------------------
@@ -760,7 +782,7 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
     }
     if (c > 0) bwd_fetch_data(ci, j0 - kB, k, q, dO, v, beta, alpha, H, head, tid, nx);
     __syncthreads();
-    if (tid < kD) solve_lower<f16_t, false>(Ar, Ur, LDK, nullptr, tid);
+    solve_lower<f16_t, false>(Ar, Ur, LDK, nullptr, tid);
     __syncthreads();
 
     // -- dU = scale P^T dO + diag(E_63,.) K dS^T --------------------------------------------
@@ -792,17 +814,14 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
     __syncthreads();
 
     // -- dR = (I + A)^{-T} dU; dV = diag(beta) dR -------------------------------------------
-    if (tid < kD) {
-      const int col = tid;
-      solve_upper_t<f16_t>(Ar, dRr, LDK, col, [&](int t, float y) {
-        const int kind = dst_kind[t];
-        const int64_t off = dst_off[t];
-        const float g = bs[t] * y;
-        if (kind == 1) rbuf[off + kD + col] = g;
-        else if (kind == 2) rside[off + kD + col] = g;
-        else if (kind == 3) st_g<TG>(dv + off + col, g);
-      });
-    }
+    solve_upper_t<f16_t>(Ar, dRr, LDK, tid, [&](int t, int col, float y) {
+      const int kind = dst_kind[t];
+      const int64_t off = dst_off[t];
+      const float g = bs[t] * y;
+      if (kind == 1) rbuf[off + kD + col] = g;
+      else if (kind == 2) rside[off + kD + col] = g;
+      else if (kind == 3) st_g<TG>(dv + off + col, g);
+    });
     __syncthreads();
 
     // V rows for sum_c dR[t][c] V[t][c] (beta's derivative through R): thread (t, part)
