@@ -458,7 +458,8 @@ __device__ __forceinline__ void solve_upper_t(const float* __restrict__ At, TX* 
       x[(16 * b + j) * ldx + c] = (TX)acc[j];
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) emit(16 * b + 8 * h + j, c, h ? acc[8 + j] : acc[j]);
+    for (int j = 0; j < 16; ++j)
+      if ((j >> 3) == h) emit(16 * b + j, c, acc[j]);
   }
 }
 
