@@ -451,8 +451,9 @@ def planner_time(spec):
             "trie_work": info["trie_work"]}
 
 
-def cpu_baseline(spec, plan, budget_s=15.0):
-    """The oracle (float32) on one causal trajectory of the workload, sized to ~budget_s."""
+def cpu_baseline(spec, plan, budget_s=20.0):
+    """The oracle (float32) on the workload's longest trajectories, each as one causal
+    chain, as many as fit about budget_s of CPU work (at least 0.7 budget_s)."""
     import numpy as np
 
     import synth
