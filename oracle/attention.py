@@ -268,6 +268,102 @@ class RowSampler:
                 lse[a, h] = l
         return o, lse
 
+    def row_grads(self, tokens: Sequence[int], q, k, v, do):
+        """(o [n,Hq,d], lse [n,Hq], dq [n,Hq,d]) for the given compact tokens.
+
+        Each row from its own visible set V(t) alone: P_tj = softmax_j(s_tj),
+        D_t = dO_t . O_t, dS_tj = P_tj (dO_t . v_j - D_t) and
+        dq_t = R(pos_t)^T scale sum_j dS_tj R(pos_j) k_j, the textbook softmax
+        backward for one query row (the row's dO is its compact upstream gradient).
+        """
+        q, k, v, do = _np(q), _np(k), _np(v), _np(do)
+        d = k.shape[-1]
+        scale = self.p.scale_for(d)
+        o = np.zeros((len(tokens), self.p.hq, d))
+        lse = np.zeros((len(tokens), self.p.hq))
+        dq = np.zeros((len(tokens), self.p.hq, d))
+        for a, t in enumerate(tokens):
+            t = int(t)
+            for h, (kt, P, l, oh, kk, _) in enumerate(self._fwd_one(t, q, k, v)):
+                gg = self.p.group(h)
+                g_o = np.asarray(do[t, h], np.float64)
+                dp = np.asarray(v[kt, gg], np.float64) @ g_o
+                ds = P * (dp - float(g_o @ oh))
+                o[a, h], lse[a, h] = oh, l
+                dq[a, h] = scale * (ds @ kk)
+            dq[a] = rotate_transpose(dq[a][None], self.pos[t:t + 1], self.p.rope_base)[0]
+        return o, lse, dq
+
+    def reader_nodes(self, j: int) -> List[int]:
+        """Nodes with at least one query token whose visible set contains key token j."""
+        g = self.g
+        u, jo = int(self.node_of[j]), int(self.off[j])
+        out = [u]
+        for w in range(g.n):
+            if w != u and g.length[w] > 0 and any(b <= jo < e for b, e in g.visible_ranges(w).get(u, [])):
+                out.append(w)
+        return out
+
+    def key_grads_by_node(self, keys: Sequence[int], q, k, v, do, groups: Sequence[int] = None,
+                          block: int = 256):
+        """(dk, dv) [n, Hkv, d] for the given key tokens, summed over every reader row;
+        only the KV groups in ``groups`` (default all) are filled, the rest stay zero.
+
+        Same sums as :meth:`key_grads`, organised by reader node: the query rows of one
+        node w share w's non-self visible set, so they are evaluated together as one
+        dense block of rows against [w's non-self keys, w's own keys] with the own part
+        causal (key offset <= row offset), each row normalised over its own visible set.
+        ``q`` and ``do`` need the rows of every reader node, ``k`` and ``v`` every key.
+        """
+        g, p = self.g, self.p
+        d = k.shape[-1]
+        scale = p.scale_for(d)
+        groups = list(range(p.hkv)) if groups is None else [int(x) for x in groups]
+        heads = [h for h in range(p.hq) if p.group(h) in groups]
+        keys = [int(j) for j in keys]
+        dk = np.zeros((len(keys), p.hkv, d))
+        dv = np.zeros((len(keys), p.hkv, d))
+        by_node: Dict[int, List[int]] = {}
+        for a, j in enumerate(keys):
+            for w in self.reader_nodes(j):
+                by_node.setdefault(w, []).append(a)
+        for w, idx in sorted(by_node.items()):
+            o0, L = g.offset[w], g.length[w]
+            nonself = [np.arange(g.offset[s] + b, g.offset[s] + e)
+                       for s, rs in sorted(g.visible_ranges(w).items()) for b, e in rs]
+            ns = np.concatenate(nonself).astype(np.int64) if nonself else np.zeros(0, np.int64)
+            vis = np.concatenate([ns, np.arange(o0, o0 + L)])
+            col = {int(t): c for c, t in enumerate(vis)}
+            # rows of w that see one of the keys: all of them, unless every key is w's own
+            own_min = [int(self.off[keys[a]]) for a in idx if int(self.node_of[keys[a]]) == w]
+            r_first = min(own_min) if len(own_min) == len(idx) else 0
+            kr = rotate(np.asarray(k[vis], np.float64), self.pos[vis], p.rope_base)
+            vv = np.asarray(v[vis], np.float64)
+            cols = np.array([col[keys[a]] for a in idx])
+            for r0 in range(r_first, L, block):
+                r1 = min(L, r0 + block)
+                rows = np.arange(o0 + r0, o0 + r1)
+                qr = rotate(np.asarray(q[rows], np.float64), self.pos[rows], p.rope_base)
+                g_o_all = np.asarray(do[rows], np.float64)
+                # own key offset i is visible to own row offset r iff i <= r
+                hidden = np.zeros((r1 - r0, len(vis)), bool)
+                hidden[:, len(ns):] = np.arange(L)[None, :] > np.arange(r0, r1)[:, None]
+                for h in heads:
+                    gg = p.group(h)
+                    s = np.where(hidden, -np.inf, scale * (qr[:, h] @ kr[:, gg].T))
+                    P, _ = _softmax_rows(s)
+                    O = P @ vv[:, gg]
+                    g_o = g_o_all[:, h]
+                    D = (g_o * O).sum(axis=1)
+                    Pc = P[:, cols]                                   # [rows, n keys of w]
+                    dSc = Pc * (g_o @ vv[cols, gg].T - D[:, None])
+                    for c, a in enumerate(idx):
+                        dk[a, gg] += scale * (dSc[:, c] @ qr[:, h])
+                        dv[a, gg] += Pc[:, c] @ g_o
+        for a, j in enumerate(keys):
+            dk[a] = rotate_transpose(dk[a][None], self.pos[j:j + 1], p.rope_base)[0]
+        return dk, dv
+
     def readers(self, j: int) -> np.ndarray:
         """Every compact query token whose visible set contains key token j."""
         g = self.g

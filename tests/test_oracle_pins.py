@@ -306,6 +306,53 @@ def test_row_sampler_matches_flat():
     assert np.abs(rk - dk[toks]).max() < 1e-11 and np.abs(rv - dv[toks]).max() < 1e-11
 
 
+@pytest.mark.parametrize("seed", [4, 9, 21])
+@pytest.mark.parametrize("transitive", [True, False])
+def test_row_grads_match_flat_and_brute(seed, transitive):
+    """Per-row o, lse and dq from V(t) alone equal the flat reference and brute force."""
+    rng = np.random.default_rng(seed)
+    spec = synth.random_tiny_dag(rng, n_nodes=10, max_len=9, p_mount=0.9, max_mounts=2)
+    q, k, v, do = _inputs(spec, 4, 2, 8, seed=seed)
+    p = AttnParams(4, 2)
+    o, lse, dq, _, _ = attn_flat(spec, q, k, v, do, p, transitive=transitive)
+    bo, bl, bdq, _, _ = attn_brute(spec, q, k, v, do, p, transitive=transitive)
+    rs = RowSampler(spec, p, transitive=transitive)
+    toks = list(range(spec.n_tokens))
+    ro, rl, rdq = rs.row_grads(toks, q, k, v, do)
+    for got, a, b in ((ro, o, bo), (rl, lse, bl), (rdq, dq, bdq)):
+        assert np.abs(got - a).max() < 1e-11 and np.abs(got - b).max() < 1e-11
+
+
+@pytest.mark.parametrize("seed", [4, 9, 21])
+@pytest.mark.parametrize("transitive", [True, False])
+def test_key_grads_by_node_match_flat(seed, transitive):
+    """Reader-node blocks give every key's dK/dV exactly as the flat reference does, for any
+    block size (blocks cut nodes), and fill only the requested KV groups."""
+    rng = np.random.default_rng(seed)
+    spec = synth.random_tiny_dag(rng, n_nodes=10, max_len=9, p_mount=0.9, max_mounts=2)
+    q, k, v, do = _inputs(spec, 4, 2, 8, seed=seed + 1)
+    p = AttnParams(4, 2)
+    _, _, _, dk, dv = attn_flat(spec, q, k, v, do, p, transitive=transitive)
+    rs = RowSampler(spec, p, transitive=transitive)
+    toks = list(range(spec.n_tokens))
+    for block in (3, 256):
+        rk, rv = rs.key_grads_by_node(toks, q, k, v, do, block=block)
+        assert np.abs(rk - dk).max() < 1e-11 and np.abs(rv - dv).max() < 1e-11
+    sel = toks[::2]
+    rk, rv = rs.key_grads_by_node(sel, q, k, v, do, groups=[1])
+    assert np.abs(rk[:, 1] - dk[sel, 1]).max() < 1e-11 and np.abs(rv[:, 1] - dv[sel, 1]).max() < 1e-11
+    assert not rk[:, 0].any() and not rv[:, 0].any()
+
+
+def test_reader_nodes_cover_every_reader_token():
+    rng = np.random.default_rng(17)
+    spec = synth.random_tiny_dag(rng, n_nodes=12, max_len=6, p_mount=0.9, max_mounts=2)
+    rs = RowSampler(spec, AttnParams(2, 1))
+    node_of, _ = rs.g.token_node()
+    for j in range(spec.n_tokens):
+        assert sorted(set(int(node_of[t]) for t in rs.readers(j))) == sorted(rs.reader_nodes(j))
+
+
 def test_workload3_seed_record():
     """The recorded structure seed satisfies its selection rule (checked with the oracle)."""
     rec = gold("workload3_seed.json")
