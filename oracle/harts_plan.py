@@ -318,9 +318,10 @@ class Planner:
             groups.append([x])
         return [sorted(g) for g in groups]
 
-    def sparse_repair(self, groups: List[List[int]]) -> List[List[int]]:
+    def sparse_repair(self, groups: List[List[int]], iterations: int = 4) -> List[List[int]]:
+        """At most ``iterations`` (the page's four) best strictly improving moves or swaps."""
         groups = [sorted(g) for g in groups]
-        for _ in range(4):
+        for _ in range(iterations):
             where = {x: gi for gi, g in enumerate(groups) for x in g}
             best = None
             for x in range(self.N):
