@@ -42,7 +42,7 @@ class DagMount(ctypes.Structure):
 class DagBuildOpts(ctypes.Structure):
     _fields_ = [("page_size", ctypes.c_int32), ("q_block", ctypes.c_int32),
                 ("transitive", ctypes.c_int32), ("page_shuffle", ctypes.c_int32),
-                ("gdn_chunk", ctypes.c_int32), ("view", ctypes.c_int32)]
+                ("gdn_chunk", ctypes.c_int32), ("view", ctypes.c_int32), ("pack_pages", ctypes.c_int32)]
 
 
 class DagPlanInfo(ctypes.Structure):
@@ -52,7 +52,9 @@ class DagPlanInfo(ctypes.Structure):
                [("max_position", ctypes.c_int32), ("transitive", ctypes.c_int32),
                 ("gdn_chunk", ctypes.c_int32), ("gdn_rounds", ctypes.c_int32)] + \
                [(n, ctypes.c_int64) for n in ("gdn_sequences", "gdn_replay", "gdn_slots", "gdn_chunks",
-                                             "gdn_segments")] + [("view", ctypes.c_int32)]
+                                             "gdn_segments")] + [("view", ctypes.c_int32),
+                                                                 ("semantic_tokens", ctypes.c_int64),
+                                                                 ("pack_pages", ctypes.c_int32)]
 
 VIEWS = {"mounted": 0, "mount_free": 1, "unshifted": 2}
 
@@ -117,6 +119,9 @@ def _load() -> ctypes.CDLL:
         "dag_plan_info_get": ([P, ctypes.POINTER(DagPlanInfo)], I32),
         "dag_plan_rows": ([P, P, P], I32),
         "dag_plan_starts": ([P, P], I32),
+        "dag_plan_multiplicity": ([P, P], I32),
+        "dag_plan_visibility": ([P, I32, P, I32, ctypes.POINTER(I32)], I32),
+        "dag_plan_readers": ([P, I32, P, I32, ctypes.POINTER(I32)], I32),
         "dag_plan_node_ranges": ([P, I32, P, I32, ctypes.POINTER(I32)], I32),
         "dag_plan_upload": ([P, P], I32),
         "dag_plan_gdn_seqs": ([P, P, I32, ctypes.POINTER(I32)], I32),
@@ -169,7 +174,7 @@ class Plan:
     mount_begin, mount_end``."""
 
     def __init__(self, spec, transitive: Optional[bool] = None, page_shuffle: int = 0, gdn_chunk: int = 0,
-                 view: str = "mounted"):
+                 view: str = "mounted", pack: bool = False):
         if transitive is None:
             transitive = bool(getattr(spec, "meta", {}).get("transitive", True))
         n = len(spec.parent)
@@ -181,7 +186,8 @@ class Plan:
         mounts = (DagMount * max(m, 1))()
         for i in range(m):
             mounts[i] = DagMount(int(spec.mount_src[i]), int(spec.mount_begin[i]), int(spec.mount_end[i]))
-        opts = DagBuildOpts(64, 64, 1 if transitive else 0, int(page_shuffle), int(gdn_chunk), VIEWS[view])
+        opts = DagBuildOpts(64, 64, 1 if transitive else 0, int(page_shuffle), int(gdn_chunk), VIEWS[view],
+                            1 if pack else 0)
         self._h = ctypes.c_void_p()
         _check(_lib.dag_build(nodes, n, mounts, m, ctypes.byref(opts), ctypes.byref(self._h)))
         info = DagPlanInfo()
@@ -212,6 +218,27 @@ class Plan:
             _check(_lib.dag_plan_rows(self._h, rot.ctypes.data, por.ctypes.data))
             self._rows = (rot[: self.tokens], por[: self.rows])
         return self._rows
+
+    def multiplicity(self) -> np.ndarray:
+        """``dag_plan_multiplicity``: trajectories holding each token (node-major order), int32 [U]."""
+        out = np.zeros(max(self.tokens, 1), np.int32)
+        _check(_lib.dag_plan_multiplicity(self._h, out.ctypes.data))
+        return out[: self.tokens]
+
+    def _rows_query(self, fn, row: int) -> np.ndarray:
+        n = ctypes.c_int32(0)
+        _check(fn(self._h, int(row), None, 0, ctypes.byref(n)))
+        out = np.zeros(max(n.value, 1), np.int32)
+        _check(fn(self._h, int(row), out.ctypes.data, n.value, ctypes.byref(n)))
+        return out[: n.value]
+
+    def visibility(self, row: int) -> np.ndarray:
+        """``dag_plan_visibility``: rows that query row ``row`` sees, as the forward reads the plan."""
+        return self._rows_query(_lib.dag_plan_visibility, row)
+
+    def readers(self, row: int) -> np.ndarray:
+        """``dag_plan_readers``: query rows the dK/dV kernel sums into key row ``row``."""
+        return self._rows_query(_lib.dag_plan_readers, row)
 
     def starts(self) -> np.ndarray:
         out = np.zeros(self.n_nodes, np.int32)
@@ -355,7 +382,8 @@ def attn_fwd(plan: Plan, p: AttnParams, q, k, v, o=None, lse=None, ws=None, stre
 
 def attn_bwd(plan: Plan, p: AttnParams, q, k, v, o, lse, dO, dq=None, dk=None, dv=None, ws=None,
              stream=None, o_lo=None):
-    """``dag_attn_bwd``: returns (dq [C,Hq,D], dk [C,Hkv,D], dv [C,Hkv,D])."""
+    """``dag_attn_bwd``: returns (dq [C,Hq,D], dk [C,Hkv,D], dv [C,Hkv,D]).  For bf16, ``o_lo``
+    (the forward's rounding residual of o) is required."""
     import torch
     C, dt, dev = plan.rows, p.torch_dtype, q.device
     for name, t, h in (("q", q, p.n_q_heads), ("k", k, p.n_kv_heads), ("v", v, p.n_kv_heads),

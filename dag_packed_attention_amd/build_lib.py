@@ -34,7 +34,7 @@ def _run(cmd):
     return r
 
 
-OBJS = ("plan.o", "gdn_plan.o", "logprob_map.o", "conv_plan.o", "harts_plan.o", "abi.o", "kernels.o", "gdn.o", "logprob.o",
+OBJS = ("plan.o", "pack_plan.o", "gdn_plan.o", "logprob_map.o", "conv_plan.o", "harts_plan.o", "abi.o", "kernels.o", "gdn.o", "logprob.o",
         "conv.o")
 
 
@@ -43,6 +43,7 @@ def build(verbose: bool = False) -> str:
     os.makedirs(obj_dir, exist_ok=True)
     steps = [
         ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "plan.cpp"), "-o", os.path.join(obj_dir, "plan.o")],
+        ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "pack_plan.cpp"), "-o", os.path.join(obj_dir, "pack_plan.o")],
         ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "gdn_plan.cpp"), "-o", os.path.join(obj_dir, "gdn_plan.o")],
         ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "logprob_map.cpp"),
          "-o", os.path.join(obj_dir, "logprob_map.o")],

@@ -1,6 +1,7 @@
 // C ABI of libdag_attn: plan management, workspace sizing and kernel launches.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -10,16 +11,13 @@
 #include <string>
 #include <vector>
 
+#include "abi_internal.hpp"
 #include "conv.hpp"
 #include "gdn.hpp"
 #include "harts_plan.hpp"
 #include "launch.hpp"
 #include "logprob.hpp"
 #include "plan.hpp"
-
-struct dag_plan {
-  dagattn::Plan p;
-};
 
 namespace dagattn {
 
@@ -129,6 +127,7 @@ struct FwdWs {
   void* qn;
   void* kn;
   void* vt;
+  uint32_t* amax;  // max |q|, |k|, |v| (float bits; MFMA path)
 };
 struct BwdWs {
   float2* cs;
@@ -138,7 +137,7 @@ struct BwdWs {
   void* vn;
   void* dOn;
   float2* ld;
-  uint32_t* dmax;
+  uint32_t* amax;  // max |q|, |k|, |v|, |dO| (float bits)
 };
 
 size_t carve_fwd(const LaunchShape& s, bool mfma, void* base, FwdWs* w) {
@@ -149,10 +148,12 @@ size_t carve_fwd(const LaunchShape& s, bool mfma, void* base, FwdWs* w) {
     w->qn = c.take<f16_t>(C * s.Hq * s.D);
     w->kn = c.take<f16_t>(C * s.Hkv * s.D);
     w->vt = c.take<f16_t>(C * s.Hkv * s.D);
+    w->amax = c.take<uint32_t>(3);
   } else {
     w->qn = c.take<float>(C * s.Hq * s.D);
     w->kn = c.take<float>(C * s.Hkv * s.D);
     w->vt = nullptr;
+    w->amax = nullptr;
   }
   return c.off;
 }
@@ -162,7 +163,7 @@ size_t carve_bwd(const LaunchShape& s, bool mfma, void* base, BwdWs* w) {
   const size_t C = (size_t)s.C;
   w->cs = s.log2_base > 0 ? c.take<float2>(C * (s.D / 2)) : nullptr;
   w->ld = c.take<float2>(C * s.Hq);
-  w->dmax = c.take<uint32_t>(1);
+  w->amax = c.take<uint32_t>(4);
   if (mfma) {
     w->qn = c.take<f16_t>(C * s.Hq * s.D);
     w->dOn = c.take<f16_t>(C * s.Hq * s.D);
@@ -366,6 +367,75 @@ GdnShape gdn_shape(const Plan& P, const dag_gdn_params* p) {
 
 }  // namespace
 
+dag_status dagattn::set_error(dag_status code, const std::string& msg) { return set_err(code, msg); }
+
+dag_status dagattn::attn_fwd_impl(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k,
+                                  const void* v, void* o, float* lse, void* o_lo, void* ws, size_t ws_bytes,
+                                  void* hip_stream, bool allow_upload) {
+  if (!plan) return set_err(DAG_E_INVALID, "null plan");
+  dag_status st = check_params(p);
+  if (st != DAG_OK) return st;
+  Plan& P = plan->p;
+  if (P.info.rows == 0) return DAG_OK;
+  if (!q || !k || !v || !o || !lse) return set_err(DAG_E_INVALID, "null tensor pointer");
+  if (o_lo && p->dtype != DAG_DTYPE_BF16) return set_err(DAG_E_INVALID, "o_lo is for bf16 tensors only");
+  const LaunchShape s = shape_of(P, p);
+  const bool mfma = mfma_path(p);
+  if (P.packed) return set_err(DAG_E_UNSUPPORTED, "packed page layouts are not supported by the attention kernels");
+  FwdWs w;
+  const size_t need = carve_fwd(s, mfma, nullptr, &w);
+  if (!ws || ws_bytes < need)
+    return set_err(DAG_E_WORKSPACE, "forward workspace needs " + std::to_string(need) + " bytes");
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if (allow_upload) {
+    if ((st = ensure_uploaded(P, stream)) != DAG_OK) return st;
+  } else {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return set_err(DAG_E_DEVICE, "hipGetDevice failed");
+    if (!P.dev) return set_err(DAG_E_INVALID, "the plan is not on the device yet: call dag_plan_upload first");
+    if (P.dev->device != dev)
+      return set_err(DAG_E_DEVICE, "plan was uploaded to device " + std::to_string(P.dev->device) +
+                                       ", current device is " + std::to_string(dev));
+  }
+  carve_fwd(s, mfma, ws, &w);
+  const DeviceTables& D = *P.dev;
+  const int64_t n_qp = (int64_t)P.qpages.size();
+  {
+    Span sp(P, DAG_K_PROLOGUE_FWD, stream);
+    if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
+    const int32_t* nr = D.page_nrows;
+    if (mfma) {
+      // each fp16 copy is scaled by the power of two that maps its tensor's maximum into
+      // [1, 2), so no finite bf16 input overflows fp16; the kernels undo the scales exactly
+      const bf16_t *q16 = (const bf16_t*)q, *k16 = (const bf16_t*)k, *v16 = (const bf16_t*)v;
+      launch_zero_u32(w.amax, 3, stream);
+      launch_absmax(s, q16, k16, v16, nullptr, nr, w.amax, stream);
+      launch_prep16(s, q16, w.cs, nr, w.amax + 0, (f16_t*)w.qn, nullptr, s.Hq, stream);
+      launch_prep16(s, k16, w.cs, nr, w.amax + 1, (f16_t*)w.kn, nullptr, s.Hkv, stream);
+      launch_prep16(s, v16, nullptr, nr, w.amax + 2, nullptr, (f16_t*)w.vt, s.Hkv, stream);
+    } else if (p->dtype == DAG_DTYPE_BF16) {
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, nr, nullptr, (float*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, nr, nullptr, (float*)w.kn, nullptr, s.Hkv, stream);
+    } else {
+      launch_relayout<float, float>(s, (const float*)q, w.cs, nr, nullptr, (float*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<float, float>(s, (const float*)k, w.cs, nr, nullptr, (float*)w.kn, nullptr, s.Hkv, stream);
+    }
+  }
+  {
+    Span sp(P, DAG_K_FWD, stream);
+    if (mfma)
+      launch_fwd_mfma(s, n_qp, (const f16_t*)w.qn, (const f16_t*)w.kn, (const f16_t*)w.vt, D.qpages, D.fwd_order,
+                      D.tiles, (bf16_t*)o, lse, (bf16_t*)o_lo, w.amax, stream);
+    else if (p->dtype == DAG_DTYPE_BF16)
+      launch_fwd_simple<bf16_t>(s, n_qp, (const float*)w.qn, (const float*)w.kn, (const bf16_t*)v, D.qpages,
+                                D.fwd_order, D.tiles, (bf16_t*)o, lse, (bf16_t*)o_lo, stream);
+    else
+      launch_fwd_simple<float>(s, n_qp, (const float*)w.qn, (const float*)w.kn, (const float*)v, D.qpages,
+                               D.fwd_order, D.tiles, (float*)o, lse, nullptr, stream);
+  }
+  return launched("dag_attn_fwd");
+}
+
 extern "C" {
 
 const char* dag_last_error(void) { return g_err.c_str(); }
@@ -425,6 +495,79 @@ dag_status dag_plan_rows(const dag_plan* plan, int32_t* row_of_token, int32_t* p
     std::memcpy(row_of_token, plan->p.row_of_token.data(), plan->p.row_of_token.size() * 4);
   if (pos_of_row && !plan->p.pos_of_row.empty())
     std::memcpy(pos_of_row, plan->p.pos_of_row.data(), plan->p.pos_of_row.size() * 4);
+  return DAG_OK;
+}
+
+namespace {
+// Write the sorted values into out (up to cap) and their count into *n.
+dag_status emit_rows(std::vector<int32_t>& v, int32_t* out, int32_t cap, int32_t* n) {
+  std::sort(v.begin(), v.end());
+  if (n) *n = (int32_t)v.size();
+  if (out)
+    for (int32_t i = 0; i < (int32_t)v.size() && i < cap; ++i) out[i] = v[i];
+  return DAG_OK;
+}
+}  // namespace
+
+dag_status dag_plan_visibility(const dag_plan* plan, int32_t row, int32_t* key_rows, int32_t cap, int32_t* n) {
+  if (!plan || !n || cap < 0) return set_err(DAG_E_INVALID, "null argument");
+  const Plan& P = plan->p;
+  if (row < 0 || row >= P.info.rows) return set_err(DAG_E_INVALID, "row out of range");
+  const int32_t Q = row / kPage, r = row % kPage;
+  std::vector<int32_t> v;
+  if (r < P.page_nrows[Q]) {
+    for (const QPage& qp : P.qpages) {
+      if (qp.phys != Q) continue;
+      for (int32_t t = 0; t < qp.tile_count; ++t) {
+        const Tile& tl = P.tiles[qp.tile_begin + t];
+        const int32_t lo = tl.lohi & 0xff, hi = (tl.lohi >> 8) & 0xff;
+        const int32_t mi = P.packed ? P.tile_mask[qp.tile_begin + t] : -1;
+        const bool diag = t == qp.tile_count - 1;
+        for (int32_t c = lo; c < hi; ++c) {
+          if (mi < 0 && diag && c > r) continue;  // a masked tile's mask is exact by itself
+          if (mi >= 0 && !((P.masks[(size_t)mi * 2 * kPage + r] >> c) & 1ull)) continue;
+          v.push_back(tl.page * kPage + c);
+        }
+      }
+    }
+  }
+  return emit_rows(v, key_rows, cap, n);
+}
+
+dag_status dag_plan_readers(const dag_plan* plan, int32_t row, int32_t* query_rows, int32_t cap, int32_t* n) {
+  if (!plan || !n || cap < 0) return set_err(DAG_E_INVALID, "null argument");
+  const Plan& P = plan->p;
+  if (row < 0 || row >= P.info.rows) return set_err(DAG_E_INVALID, "row out of range");
+  const int32_t K = row / kPage, c = row % kPage;
+  std::vector<int32_t> v;
+  const int64_t npairs = (int64_t)P.kpairs.size() / 2;
+  for (int64_t pr = 0; pr < npairs && c < P.page_nrows[K]; ++pr) {
+    for (int side = 0; side < 2; ++side) {
+      if (P.kpairs[2 * pr + side] != K) continue;
+      for (int64_t i = P.kpair_off[pr]; i < P.kpair_off[pr + 1]; ++i) {
+        const KStep& st = P.kpsteps[i];
+        const uint32_t inf = ((uint32_t)st.info >> (16 * side)) & 0xffffu;
+        const int32_t rb = st.info & 1, lo = (inf >> 1) & 0x7f, hi = (inf >> 8) & 0x7f;
+        const bool diag = (inf >> 15) & 1;
+        if (c < lo || c >= hi) continue;
+        const int32_t mi = P.packed ? (side ? P.kstep_mask[i].b : P.kstep_mask[i].a) : -1;
+        for (int32_t rr = 0; rr < 32; ++rr) {
+          const int32_t r = rb * 32 + rr;
+          if (r >= P.page_nrows[st.qph] || (diag && c > r)) continue;
+          if (mi >= 0 && !((P.masks[(size_t)mi * 2 * kPage + kPage + c] >> r) & 1ull)) continue;
+          v.push_back(st.qph * kPage + r);
+        }
+      }
+    }
+  }
+  return emit_rows(v, query_rows, cap, n);
+}
+
+dag_status dag_plan_multiplicity(const dag_plan* plan, int32_t* mult) {
+  if (!plan || !mult) return set_err(DAG_E_INVALID, "null argument");
+  const Plan& P = plan->p;
+  for (int32_t u = 0; u < P.n_nodes; ++u)
+    for (int32_t i = 0; i < P.length[u]; ++i) mult[P.tok_off[u] + i] = P.leaves_below[u];
   return DAG_OK;
 }
 
@@ -513,53 +656,7 @@ dag_status dag_attn_workspace(const dag_plan* plan, const dag_attn_params* p, si
 
 dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k, const void* v,
                         void* o, float* lse, void* o_lo, void* ws, size_t ws_bytes, void* hip_stream) {
-  if (!plan) return set_err(DAG_E_INVALID, "null plan");
-  dag_status st = check_params(p);
-  if (st != DAG_OK) return st;
-  Plan& P = plan->p;
-  if (P.info.rows == 0) return DAG_OK;
-  if (!q || !k || !v || !o || !lse) return set_err(DAG_E_INVALID, "null tensor pointer");
-  if (o_lo && p->dtype != DAG_DTYPE_BF16) return set_err(DAG_E_INVALID, "o_lo is for bf16 tensors only");
-  const LaunchShape s = shape_of(P, p);
-  const bool mfma = mfma_path(p);
-  FwdWs w;
-  const size_t need = carve_fwd(s, mfma, nullptr, &w);
-  if (!ws || ws_bytes < need)
-    return set_err(DAG_E_WORKSPACE, "forward workspace needs " + std::to_string(need) + " bytes");
-  hipStream_t stream = (hipStream_t)hip_stream;
-  if ((st = ensure_uploaded(P, stream)) != DAG_OK) return st;
-  carve_fwd(s, mfma, ws, &w);
-  const DeviceTables& D = *P.dev;
-  const int64_t n_qp = (int64_t)P.qpages.size();
-  {
-    Span sp(P, DAG_K_PROLOGUE_FWD, stream);
-    if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
-    const int32_t* nr = D.page_nrows;
-    if (mfma) {
-      launch_prep16(s, (const bf16_t*)q, w.cs, nr, nullptr, (f16_t*)w.qn, nullptr, nullptr, s.Hq, stream);
-      launch_prep16(s, (const bf16_t*)k, w.cs, nr, nullptr, (f16_t*)w.kn, nullptr, nullptr, s.Hkv, stream);
-      launch_prep16(s, (const bf16_t*)v, nullptr, nr, nullptr, nullptr, (f16_t*)w.vt, nullptr, s.Hkv, stream);
-    } else if (p->dtype == DAG_DTYPE_BF16) {
-      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, nr, nullptr, (float*)w.qn, nullptr, s.Hq, stream);
-      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, nr, nullptr, (float*)w.kn, nullptr, s.Hkv, stream);
-    } else {
-      launch_relayout<float, float>(s, (const float*)q, w.cs, nr, nullptr, (float*)w.qn, nullptr, s.Hq, stream);
-      launch_relayout<float, float>(s, (const float*)k, w.cs, nr, nullptr, (float*)w.kn, nullptr, s.Hkv, stream);
-    }
-  }
-  {
-    Span sp(P, DAG_K_FWD, stream);
-    if (mfma)
-      launch_fwd_mfma(s, n_qp, (const f16_t*)w.qn, (const f16_t*)w.kn, (const f16_t*)w.vt, D.qpages, D.fwd_order,
-                      D.tiles, (bf16_t*)o, lse, (bf16_t*)o_lo, stream);
-    else if (p->dtype == DAG_DTYPE_BF16)
-      launch_fwd_simple<bf16_t>(s, n_qp, (const float*)w.qn, (const float*)w.kn, (const bf16_t*)v, D.qpages,
-                                D.fwd_order, D.tiles, (bf16_t*)o, lse, (bf16_t*)o_lo, stream);
-    else
-      launch_fwd_simple<float>(s, n_qp, (const float*)w.qn, (const float*)w.kn, (const float*)v, D.qpages,
-                               D.fwd_order, D.tiles, (float*)o, lse, nullptr, stream);
-  }
-  return launched("dag_attn_fwd");
+  return attn_fwd_impl(plan, p, q, k, v, o, lse, o_lo, ws, ws_bytes, hip_stream, /*allow_upload=*/true);
 }
 
 dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k, const void* v,
@@ -573,8 +670,11 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
   if (!q || !k || !v || !o || !lse || !dO || !dq || !dk || !dv)
     return set_err(DAG_E_INVALID, "null tensor pointer");
   if (o_lo && p->dtype != DAG_DTYPE_BF16) return set_err(DAG_E_INVALID, "o_lo is for bf16 tensors only");
+  if (!o_lo && p->dtype == DAG_DTYPE_BF16)
+    return set_err(DAG_E_INVALID, "the bf16 backward needs o_lo, the forward's rounding residual of o");
   const LaunchShape s = shape_of(P, p);
   const bool mfma = mfma_path(p);
+  if (P.packed) return set_err(DAG_E_UNSUPPORTED, "packed page layouts are not supported by the attention kernels");
   BwdWs w;
   const size_t need = carve_bwd(s, mfma, nullptr, &w);
   if (!ws || ws_bytes < need)
@@ -591,25 +691,29 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       const int32_t* nr = D.page_nrows;
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
       if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
-      launch_rowdot16(s, o16, (const bf16_t*)o_lo, d16, lse, nr, w.ld, w.dmax, stream);
-      launch_prep16(s, q16, w.cs, nr, nullptr, (f16_t*)w.qn, nullptr, nullptr, s.Hq, stream);
-      launch_prep16(s, k16, w.cs, nr, nullptr, (f16_t*)w.kn, (f16_t*)w.kt, nullptr, s.Hkv, stream);
-      launch_prep16(s, v16, nullptr, nr, nullptr, (f16_t*)w.vn, nullptr, nullptr, s.Hkv, stream);
-      launch_prep16(s, d16, nullptr, nr, w.dmax, (f16_t*)w.dOn, nullptr, w.ld, s.Hq, stream);
+      // power-of-two scales for the fp16 copies of q, k, v (amax[0..2]) and dO (amax[3]); the
+      // S and dP offsets in ld are formed in the scaled units
+      launch_zero_u32(w.amax, 4, stream);
+      launch_absmax(s, q16, k16, v16, d16, nr, w.amax, stream);
+      launch_rowdot16(s, o16, (const bf16_t*)o_lo, d16, lse, nr, w.ld, w.amax, stream);
+      launch_prep16(s, q16, w.cs, nr, w.amax + 0, (f16_t*)w.qn, nullptr, s.Hq, stream);
+      launch_prep16(s, k16, w.cs, nr, w.amax + 1, (f16_t*)w.kn, (f16_t*)w.kt, s.Hkv, stream);
+      launch_prep16(s, v16, nullptr, nr, w.amax + 2, (f16_t*)w.vn, nullptr, s.Hkv, stream);
+      launch_prep16(s, d16, nullptr, nr, w.amax + 3, (f16_t*)w.dOn, nullptr, s.Hq, stream);
     }
     auto grads = [&](auto* tag) {
       using TG = std::remove_pointer_t<decltype(tag)>;
       {
         Span sp(P, DAG_K_DKDV, stream);
         launch_dkdv_mfma<TG>(s, (int64_t)P.pair_order.size(), (const f16_t*)w.qn, (const f16_t*)w.kn,
-                             (const f16_t*)w.vn, (const f16_t*)w.dOn, w.ld, w.cs, w.dmax, D.pair_order, D.kpairs,
-                             D.kpair_off, D.kpsteps, D.page_nrows, (TG*)dk, (TG*)dv, stream);
+                             (const f16_t*)w.vn, (const f16_t*)w.dOn, w.ld, w.cs, w.amax + 3, D.pair_order,
+                             D.kpairs, D.kpair_off, D.kpsteps, D.page_nrows, (TG*)dk, (TG*)dv, w.amax, stream);
       }
       {
         Span sp(P, DAG_K_DQ, stream);
         launch_dq_mfma<TG>(s, n_qp, (const f16_t*)w.qn, (const f16_t*)w.kn, (const f16_t*)w.kt,
-                           (const f16_t*)w.vn, (const f16_t*)w.dOn, w.ld, w.cs, w.dmax, D.qpages, D.fwd_order,
-                           D.tiles, (TG*)dq, stream);
+                           (const f16_t*)w.vn, (const f16_t*)w.dOn, w.ld, w.cs, w.amax + 3, D.qpages,
+                           D.fwd_order, D.tiles, (TG*)dq, w.amax, stream);
       }
     };
     if (p->grad_dtype == DAG_DTYPE_FP32)
@@ -867,6 +971,7 @@ dag_status dag_conv_workspace(const dag_plan* plan, const dag_conv_params* p, si
   if (!plan || !bwd_bytes) return set_err(DAG_E_INVALID, "null argument");
   dag_status st = check_conv(p);
   if (st != DAG_OK) return st;
+  if (plan->p.packed) return set_err(DAG_E_UNSUPPORTED, "the convolution needs a plan with one node per page");
   *bwd_bytes = conv_ws_bytes(plan->p, p);
   return DAG_OK;
 }
@@ -877,6 +982,7 @@ dag_status dag_conv_fwd(dag_plan* plan, const dag_conv_params* p, const void* x,
   Plan& P = plan->p;
   dag_status st = check_conv(p);
   if (st != DAG_OK) return st;
+  if (plan->p.packed) return set_err(DAG_E_UNSUPPORTED, "the convolution needs a plan with one node per page");
   if (P.info.rows == 0) return DAG_OK;
   if (!x || !weight || !y) return set_err(DAG_E_INVALID, "null tensor pointer");
   if (!aligned16(x) || !aligned16(y)) return set_err(DAG_E_INVALID, "x and y must be 16-byte aligned");
@@ -896,6 +1002,7 @@ dag_status dag_conv_bwd(dag_plan* plan, const dag_conv_params* p, const void* x,
   Plan& P = plan->p;
   dag_status st = check_conv(p);
   if (st != DAG_OK) return st;
+  if (plan->p.packed) return set_err(DAG_E_UNSUPPORTED, "the convolution needs a plan with one node per page");
   if (P.info.rows == 0) return DAG_OK;
   if (!x || !weight || !dy || !dx || !dweight) return set_err(DAG_E_INVALID, "null tensor pointer");
   if (!aligned16(x) || !aligned16(dy) || !aligned16(dx) || !aligned16(ws))

@@ -9,14 +9,15 @@
 //                                               are stored with bits 2 and 3 of the row index
 //                                               swapped (the order in which an MFMA accumulator
 //                                               lane holds them, see below)
-//                  ld  [page][Hq][64] float2    (lse * log2 e, s * rowsum(dO * O)) for the backward
-//                  dmax                         largest |dO| (float bits); s = 2^-floor(log2 dmax)
+//                  ld  [page][Hq][64] float2    the S and dP offsets of every row for the backward
+//                  amax[4]                      largest |q|, |k|, |v|, |dO| (float bits)
 //
-// MFMA path (D = 128, Hq = 4 Hkv).  Operands are fp16: bf16 inputs convert
-// exactly, the rotated q/k and the probabilities P and dS keep three more
-// mantissa bits than bf16, and dO is scaled by the power of two s so that
-// small gradients do not fall below fp16's normal range (undone exactly on
-// dq, dk, dv).  A work-group serves one 64-row block and one KV head; its four
+// MFMA path (D = 128, Hq = 4 Hkv).  Operands are fp16: each of q, k, v, dO is scaled by
+// the power of two that puts its largest |x| in [1, 2) (amax), so no finite bf16 input
+// overflows fp16 and small values keep fp16's range below that maximum; the scales are
+// folded into the softmax's exponent factor and the output multipliers, exactly.  The
+// rotated q/k and the probabilities P and dS keep three more mantissa bits than bf16.
+// A work-group serves one 64-row block and one KV head; its four
 // waves are the four query heads of that GQA group, so every K/V tile staged
 // in LDS is read by four heads.  Products are taken in the transposed
 // orientation S^T = K Q^T and O^T = V^T P^T with v_mfma_f32_32x32x16_f16: a
@@ -174,8 +175,10 @@ __global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ o_l
   }
 }
 
-// *out = 0 (before a kernel that takes an integer maximum into it)
-__global__ void zero_u32_kernel(uint32_t* out) { *out = 0u; }
+// out[0 .. n) = 0 (before kernels that take integer maxima into them)
+__global__ void zero_u32_kernel(uint32_t* out, int n) {
+  if ((int)threadIdx.x < n) out[threadIdx.x] = 0u;
+}
 
 // ---------------------------------------------------------------------------
 // MFMA kernels: D = 128, four query heads per KV head, fp16 operands
@@ -185,21 +188,49 @@ constexpr int kD = 128;
 
 constexpr int kRun = 8;  // consecutive units of one head that go to one XCD
 
+typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
+
+// amax[t] = max |x| over the valid rows of tensor t (t = blockIdx.y: q and dO
+// [C][Hq][128], k and v [C][Hkv][128], bf16; order q, k, v, dO), as float bits: an integer
+// maximum of non-negative floats is exact and order-free, so the result does not depend on
+// the schedule.  Padding rows are skipped (callers may leave anything there).  16-byte
+// loads, grid-stride over 16-byte pieces; amax must be 0 first.
+__global__ __launch_bounds__(256) void absmax_kernel(const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                     const bf16_t* __restrict__ v, const bf16_t* __restrict__ dO,
+                                                     const int32_t* __restrict__ page_nrows, int64_t C, int Hq, int Hkv,
+                                                     uint32_t* __restrict__ amax) {
+  __shared__ float red[4];
+  const int t = blockIdx.y;
+  const bf16_t* x = t == 0 ? q : (t == 1 ? k : (t == 2 ? v : dO));
+  const int64_t per_row = (int64_t)((t == 0 || t == 3) ? Hq : Hkv) * (kD / 8);
+  const int64_t n = C * per_row;
+  float m = 0.f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / per_row;
+    if ((int)(row & 63) >= page_nrows[row >> 6]) continue;
+    const u16x8 u = *reinterpret_cast<const u16x8*>(x + i * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(bf2f(u[e])));
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) atomicMax(amax + t, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
+}
+
 // Prologue of the MFMA path (D = 128, bf16 in, fp16 out).  One block of 512
 // threads per 64-row page walks the page's heads; thread (r, j) owns row r's
 // columns 8 j .. 8 j + 7 and 64 + 8 j .. 64 + 8 j + 7 (rotation pairs), read and
 // written as 16-byte pieces, so every global access is a full 128-byte run per
 // eight threads.  Optional: rotation by R(pos) (kRot), the page-major natural
 // copy [page][H][64][128] (kNat), the transposed copy [page][H][128][64] with
-// rows in MFMA order (kTrans, through LDS), a power-of-two scale from smax, and
-// the same scale applied to the -D offsets in ld (the dO copy).  Padding rows
-// become zeros.
-typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
+// rows in MFMA order (kTrans, through LDS) and a power-of-two scale from smax.
+// Padding rows become zeros.
 template <bool kRot, bool kNat, bool kTrans>
 __global__ __launch_bounds__(512) void prep16_kernel(const bf16_t* __restrict__ x, const float2* __restrict__ cs,
                                                      const int32_t* __restrict__ page_nrows,
                                                      const uint32_t* __restrict__ smax, f16_t* __restrict__ out_n,
-                                                     f16_t* __restrict__ out_t, float2* __restrict__ ld_fix, int H) {
+                                                     f16_t* __restrict__ out_t, int H) {
   constexpr int kTs = 72;  // padded row of the transposed tile (elements)
   __shared__ __attribute__((aligned(16))) f16_t tt[kTrans ? 128 * kTs : 8];
   const int page = blockIdx.x, t = threadIdx.x, r = t >> 3, j = t & 7;
@@ -255,23 +286,26 @@ __global__ __launch_bounds__(512) void prep16_kernel(const bf16_t* __restrict__ 
       }
       __syncthreads();
     }
-    if (ld_fix && j == 0) ld_fix[((int64_t)page * H + h) * 64 + r].y *= sc;
   }
 }
 
-// ld[page][h][r] = (-lse / scale, -sum_d dO O) with O = o (+ o_lo), zero on padding
-// rows, and *dmax = max |dO| over valid rows (float bits; an integer maximum is exact
-// and order-free).  Sixteen lanes per (row, head), eight elements each (16-byte loads),
-// summed in a fixed order; grid-stride over (row, head).  *dmax must be 0 first.
+// ld[page][h][r] = (-sq sk lse / scale, -sv sum_d dO' O) with O = o (+ o_lo), zero on
+// padding rows: the offsets that S and dP take in the backward, in the units of the scaled
+// fp16 operands (sq, sk, sv, sdo: the power-of-two scales of q, k, v, dO from amax[0..3]).
+// dO' = fp16(sdo dO) is exactly the value the dP products read, so D cancels against dP
+// wherever the exact values do (a dO element below fp16's range is zero in both), which
+// matters where a row's attention sits on one key and |k| is large.  Sixteen lanes per
+// (row, head), eight elements each (16-byte loads), summed in a fixed order; grid-stride
+// over (row, head).
 __global__ __launch_bounds__(256) void rowdot16_kernel(const bf16_t* __restrict__ o, const bf16_t* __restrict__ o_lo,
                                                        const bf16_t* __restrict__ dO, const float* __restrict__ lse,
                                                        const int32_t* __restrict__ page_nrows,
-                                                       float2* __restrict__ ldout, uint32_t* __restrict__ dmax,
+                                                       float2* __restrict__ ldout, const uint32_t* __restrict__ amax,
                                                        int64_t n_pages, int Hq, float inv_scale) {
-  __shared__ float red[4];
   const int sub = threadIdx.x & 15;
+  const float sqk = pow2_scale(amax[0]) * pow2_scale(amax[1]);
+  const float sv = pow2_scale(amax[2]), sdo = pow2_scale(amax[3]);
   const int64_t total = n_pages * 64 * Hq;
-  float m = 0.f;
   for (int64_t it = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); it < total; it += (int64_t)gridDim.x * 16) {
     const int64_t row = it / Hq;
     const int h = (int)(it % Hq);
@@ -286,21 +320,14 @@ __global__ __launch_bounds__(256) void rowdot16_kernel(const bf16_t* __restrict_
       u16x8 ul = {};
       if (o_lo) ul = *reinterpret_cast<const u16x8*>(o_lo + e);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float dv = bf2f(ud[k]);
-        acc += (bf2f(uo[k]) + bf2f(ul[k])) * dv;
-        m = fmaxf(m, fabsf(dv));
-      }
+      for (int k = 0; k < 8; ++k) acc += (bf2f(uo[k]) + bf2f(ul[k])) * (float)(f16_t)(bf2f(ud[k]) * sdo);
     }
 #pragma unroll
     for (int off = 8; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
     if (sub == 0)
-      ldout[(page * Hq + h) * 64 + r] = valid ? make_float2(-lse[row * Hq + h] * inv_scale, -acc) : make_float2(0.f, 0.f);
+      ldout[(page * Hq + h) * 64 + r] =
+          valid ? make_float2(-lse[row * Hq + h] * inv_scale * sqk, -acc * sv) : make_float2(0.f, 0.f);
   }
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) atomicMax(dmax, __float_as_uint(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]))));
 }
 
 
@@ -453,12 +480,16 @@ constexpr int kTile = 64 * kD;  // elements of a page's 64 x 128 (or 128 x 64) b
 __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vt,
     const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
-    bf16_t* __restrict__ o, float* __restrict__ lse, bf16_t* __restrict__ o_lo, int n_qp, int Hq, int Hkv,
-    float sl2) {
+    bf16_t* __restrict__ o, float* __restrict__ lse, bf16_t* __restrict__ o_lo, const uint32_t* __restrict__ amax,
+    int n_qp, int Hq, int Hkv, float sl2_raw) {
   __shared__ __attribute__((aligned(1024))) f16_t lk[2][kPageB];
   __shared__ __attribute__((aligned(1024))) f16_t lv[2][kPageC];
   int unit, g;
   if (!map_item(n_qp, Hkv, unit, g)) return;
+  // the fp16 copies hold sq q, sk k, sv v (powers of two): the scores come out as
+  // sq sk q.k and the output as sv O, so the exponent factor and 1 / l absorb them exactly
+  const float sl2 = sl2_raw / pow2_scale(amax[0]) / pow2_scale(amax[1]);
+  const float inv_sv = 1.f / pow2_scale(amax[2]);
   const QPage qp = qpages[order[unit]];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
@@ -550,11 +581,18 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
       // span starting past key 32); then m is still -inf and every score is -inf
       const float mneg = mrow == -INFINITY ? 0.f : -mrow;
       float sum = 0.f;
+      {
+        // each score is rounded to the log2 domain first and the running max subtracted
+        // after: m is the rounded product of the largest score, so the exponent is <= kLazy
+        // whatever the logits' size (a fused s * sl2 - m would leave m's rounding error,
+        // which exceeds 1 once logits pass 2^20)
+#pragma clang fp contract(off)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, mneg));
-        s[r] = p;
-        sum += p;
+        for (int r = 0; r < 16; ++r) {
+          const float p = __builtin_amdgcn_exp2f(s[r] * sl2 + mneg);
+          s[r] = p;
+          sum += p;
+        }
       }
       lrow += sum;
       const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8);
@@ -570,7 +608,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
 
   const float l = lrow + __shfl_xor(lrow, 32);
   const bool valid = row < qp.nrows;
-  const float inv = valid ? 1.f / l : 0.f;
+  const float inv = valid ? inv_sv / l : 0.f;
   const int64_t grow = (int64_t)qp.phys * 64 + row;
   bf16_t* orow = o + (grow * Hq + h) * kD;
 #pragma unroll
@@ -606,13 +644,18 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ kt,
     const f16_t* __restrict__ vn, const f16_t* __restrict__ dOn, const float2* __restrict__ ldd,
     const float2* __restrict__ cs, const uint32_t* __restrict__ dmax, const QPage* __restrict__ qpages,
-    const int32_t* __restrict__ order, const Tile* __restrict__ tiles, TG* __restrict__ dq, int n_qp, int Hq,
-    int Hkv, float sl2, float scale) {
+    const int32_t* __restrict__ order, const Tile* __restrict__ tiles, TG* __restrict__ dq,
+    const uint32_t* __restrict__ amax, int n_qp, int Hq, int Hkv, float sl2_raw, float scale) {
   __shared__ __attribute__((aligned(1024))) f16_t lk[2][kPageB];
   __shared__ __attribute__((aligned(1024))) f16_t lvv[2][kPageB];
   __shared__ __attribute__((aligned(1024))) f16_t lkt[2][kPageC];
   int unit, g;
   if (!map_item(n_qp, Hkv, unit, g)) return;
+  // fp16 copies: sq q, sk k, sv v, sdo dO (powers of two); the S and dP offsets in ldd are
+  // in the same scaled units, so dS comes out as sdo sv dS and the sum over keys of dS k
+  // as sdo sv sk dQ / scale
+  const float sq = pow2_scale(amax[0]), sk = pow2_scale(amax[1]), sv = pow2_scale(amax[2]);
+  const float sl2 = sl2_raw / sq / sk;
   const QPage qp = qpages[order[unit]];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
@@ -693,7 +736,7 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
     __syncthreads();
   }
 
-  const float gscale = scale / pow2_scale(*dmax);  // undo the dO scaling
+  const float gscale = scale / pow2_scale(*dmax) / sv / sk;  // undo the operand scalings
   const bool valid = row < qp.nrows;
   const int64_t grow = (int64_t)qp.phys * 64 + row;
   TG* out = dq + (grow * Hq + h) * kD;
@@ -809,7 +852,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const f16_t* __restrict__ dOn, const float2* __restrict__ ldd, const float2* __restrict__ cs,
     const uint32_t* __restrict__ dmax, const int32_t* __restrict__ pair_order, const int32_t* __restrict__ pairs,
     const int64_t* __restrict__ pair_off, const KStep* __restrict__ psteps, const int32_t* __restrict__ page_nrows,
-    TG* __restrict__ dk, TG* __restrict__ dv, int n_pairs, int Hq, int Hkv, float sl2, float scale) {
+    TG* __restrict__ dk, TG* __restrict__ dv, const uint32_t* __restrict__ amax, int n_pairs, int Hq, int Hkv,
+    float sl2_raw, float scale) {
   // [buffer][head of the half-step][Q, dO][32 x 128] f16 (the first 65 KiB are reused
   // for the head-parity sum at the end), the V tiles of pages A and B, and
   // [buffer][head] the 32 rows' offsets: -lse / scale for S, then -D for dP
@@ -818,6 +862,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
   __shared__ __attribute__((aligned(16))) float lds_ld[2][2][64];
   int unit, g;
   if (!map_item(n_pairs, Hkv, unit, g)) return;
+  // fp16 copies: sq q, sk k, sv v, sdo dO (powers of two), offsets in ldd in the same
+  // units: P is exact, dS comes out as sdo sv dS, the sums as sdo dV and sdo sv sq dK / scale
+  const float sq = pow2_scale(amax[0]), sk = pow2_scale(amax[1]), sv = pow2_scale(amax[2]);
+  const float sl2 = sl2_raw / sq / sk;
   const int pr = pair_order[unit];
   const int physA = pairs[2 * pr], physB = pairs[2 * pr + 1];
   const int tid = threadIdx.x;
@@ -1037,13 +1085,13 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     }
   }
 
-  const float inv_sdo = 1.f / pow2_scale(*dmax);  // undo the dO scaling
+  const float inv_sdo = 1.f / pow2_scale(*dmax);  // undo the operand scalings
   float* red = reinterpret_cast<float*>(&qd[0][0][0][0]);  // [128][129] fp32
   const int rowsA = page_nrows[physA], rowsB = physB >= 0 ? page_nrows[physB] : 0;
   // sum the two head parities in order 0, 1 through LDS, then write dk (scaled,
   // un-rotated) and dv for both pages
   dkdv_reduce_store<true>(adk, red, kt, j, active, hi, l32, tid, physA, physB, rowsA, rowsB, g, Hkv,
-                          inv_sdo * scale, cs, dk);
+                          inv_sdo * scale / sv / sq, cs, dk);
   dkdv_reduce_store<false>(adv, red, kt, j, active, hi, l32, tid, physA, physB, rowsA, rowsB, g, Hkv, inv_sdo,
                            cs, dv);
 }
@@ -1246,30 +1294,39 @@ void launch_rowdot(const LaunchShape& s, const T* o, const T* o_lo, const T* dO,
                                                                        s.pages, s.Hq, s.D, 1.f / s.scale);
 }
 
+void launch_absmax(const LaunchShape& s, const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* dO,
+                   const int32_t* page_nrows, uint32_t* amax, hipStream_t st) {
+  const int64_t pieces = s.C * s.Hq * (kD / 8);
+  const int64_t blocks = (pieces + 255) / 256;
+  const dim3 grid((unsigned)(blocks < 2048 ? (blocks > 0 ? blocks : 1) : 2048), dO ? 4 : 3);
+  absmax_kernel<<<grid, 256, 0, st>>>(q, k, v, dO, page_nrows, s.C, s.Hq, s.Hkv, amax);
+}
+
+void launch_zero_u32(uint32_t* out, int n, hipStream_t st) { zero_u32_kernel<<<1, 64, 0, st>>>(out, n); }
+
 void launch_prep16(const LaunchShape& s, const bf16_t* x, const float2* cs, const int32_t* page_nrows,
-                   const uint32_t* smax, f16_t* out_n, f16_t* out_t, float2* ld_fix, int H, hipStream_t st) {
+                   const uint32_t* smax, f16_t* out_n, f16_t* out_t, int H, hipStream_t st) {
   const unsigned grid = (unsigned)s.pages;
   if (cs) {
     if (out_n && out_t)
-      prep16_kernel<true, true, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, ld_fix, H);
+      prep16_kernel<true, true, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, H);
     else
-      prep16_kernel<true, true, false><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, ld_fix, H);
+      prep16_kernel<true, true, false><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, H);
   } else if (out_n && out_t) {
-    prep16_kernel<false, true, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, ld_fix, H);
+    prep16_kernel<false, true, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, H);
   } else if (out_t) {
-    prep16_kernel<false, false, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, ld_fix, H);
+    prep16_kernel<false, false, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, H);
   } else {
-    prep16_kernel<false, true, false><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, ld_fix, H);
+    prep16_kernel<false, true, false><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, H);
   }
 }
 
 void launch_rowdot16(const LaunchShape& s, const bf16_t* o, const bf16_t* o_lo, const bf16_t* dO, const float* lse,
-                     const int32_t* page_nrows, float2* ld, uint32_t* dmax, hipStream_t st) {
-  zero_u32_kernel<<<1, 1, 0, st>>>(dmax);
+                     const int32_t* page_nrows, float2* ld, const uint32_t* amax, hipStream_t st) {
   const int64_t items = s.pages * 64 * s.Hq;
   const int64_t blocks = (items + 15) / 16;
   rowdot16_kernel<<<(unsigned)(blocks < 8192 ? (blocks > 0 ? blocks : 1) : 8192), 256, 0, st>>>(
-      o, o_lo, dO, lse, page_nrows, ld, dmax, s.pages, s.Hq, 1.f / s.scale);
+      o, o_lo, dO, lse, page_nrows, ld, amax, s.pages, s.Hq, 1.f / s.scale);
 }
 
 template void launch_relayout<bf16_t, f16_t>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, const uint32_t*, f16_t*, f16_t*, int, hipStream_t);
@@ -1287,38 +1344,41 @@ static unsigned run_grid(int64_t n_units, int H) {
 
 void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vt,
                      const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
-                     bf16_t* o_lo, hipStream_t st) {
-  fwd_mfma_kernel<<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, vt, qpages, order, tiles, o, lse, o_lo, (int)n_qp,
-                                                         s.Hq, s.Hkv, s.scale * kLog2e);
+                     bf16_t* o_lo, const uint32_t* amax, hipStream_t st) {
+  fwd_mfma_kernel<<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, vt, qpages, order, tiles, o, lse, o_lo, amax,
+                                                         (int)n_qp, s.Hq, s.Hkv, s.scale * kLog2e);
 }
 
 template <typename TG>
 void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* kt,
                     const f16_t* vn, const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
-                    const QPage* qpages, const int32_t* order, const Tile* tiles, TG* dq, hipStream_t st) {
+                    const QPage* qpages, const int32_t* order, const Tile* tiles, TG* dq, const uint32_t* amax,
+                    hipStream_t st) {
   dq_mfma_kernel<TG><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, kt, vn, dOn, ld, cs, dmax, qpages, order,
-                                                            tiles, dq, (int)n_qp, s.Hq, s.Hkv, s.scale * kLog2e,
-                                                            s.scale);
+                                                            tiles, dq, amax, (int)n_qp, s.Hq, s.Hkv,
+                                                            s.scale * kLog2e, s.scale);
 }
 
 template <typename TG>
 void launch_dkdv_mfma(const LaunchShape& s, int64_t n_pairs, const f16_t* qn, const f16_t* kn, const f16_t* vn,
                       const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
                       const int32_t* pair_order, const int32_t* pairs, const int64_t* pair_off, const KStep* psteps,
-                      const int32_t* page_nrows, TG* dk, TG* dv, hipStream_t st) {
+                      const int32_t* page_nrows, TG* dk, TG* dv, const uint32_t* amax, hipStream_t st) {
   dkdv_mfma_kernel<TG><<<run_grid(n_pairs, s.Hkv), 512, 0, st>>>(qn, kn, vn, dOn, ld, cs, dmax, pair_order, pairs,
-                                                                 pair_off, psteps, page_nrows, dk, dv, (int)n_pairs,
-                                                                 s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
+                                                                 pair_off, psteps, page_nrows, dk, dv, amax,
+                                                                 (int)n_pairs, s.Hq, s.Hkv, s.scale * kLog2e,
+                                                                 s.scale);
 }
 
 #define INST_MFMA_BWD(TG)                                                                                      \
   template void launch_dq_mfma<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,      \
                                    const f16_t*, const f16_t*, const float2*, const float2*, const uint32_t*,  \
-                                   const QPage*, const int32_t*, const Tile*, TG*, hipStream_t);               \
+                                   const QPage*, const int32_t*, const Tile*, TG*, const uint32_t*,            \
+                                   hipStream_t);                                                               \
   template void launch_dkdv_mfma<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,    \
                                      const f16_t*, const float2*, const float2*, const uint32_t*,              \
                                      const int32_t*, const int32_t*, const int64_t*, const KStep*,             \
-                                     const int32_t*, TG*, TG*, hipStream_t);
+                                     const int32_t*, TG*, TG*, const uint32_t*, hipStream_t);
 INST_MFMA_BWD(bf16_t)
 INST_MFMA_BWD(float)
 

@@ -62,7 +62,7 @@ uint64_t splitmix64(uint64_t& s) {
 dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts, int32_t nm,
                       const dag_build_opts* opts_in, Plan* P, std::string* err) {
   // ---- options ----------------------------------------------------------
-  dag_build_opts opts{64, 64, 1, 0, 0, DAG_VIEW_MOUNTED};
+  dag_build_opts opts{64, 64, 1, 0, 0, DAG_VIEW_MOUNTED, 0};
   if (opts_in) opts = *opts_in;
   if (opts.page_size == 0) opts.page_size = kPage;
   if (opts.q_block == 0) opts.q_block = kPage;
@@ -75,6 +75,8 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
     return fail(err, DAG_E_INVALID, "view must be 0, 1 or 2 (got %lld)", opts.view);
   if (opts.gdn_chunk < 0 || opts.gdn_chunk > 4096)
     return fail(err, DAG_E_INVALID, "gdn_chunk must be in [0, 4096] (got %lld)", opts.gdn_chunk);
+  if (opts.pack_pages != 0 && opts.pack_pages != 1)
+    return fail(err, DAG_E_INVALID, "pack_pages must be 0 or 1 (got %lld)", opts.pack_pages);
   P->opts = opts;
 
   // ---- 1. validation ------------------------------------------------------
@@ -224,230 +226,242 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
   }
   P->range_off[n] = (int64_t)P->ranges.size() / 3;
 
-  // ---- 6. pages ------------------------------------------------------------------
-  P->slot0.assign(n, 0);
-  P->npages.assign(n, 0);
-  P->tok_off.assign(n, 0);
-  int64_t slots = 0, tokens = 0;
-  for (int32_t u = 0; u < n; ++u) {
-    P->slot0[u] = (int32_t)std::min<int64_t>(slots, INT32_MAX);
-    P->npages[u] = (int32_t)(((int64_t)P->length[u] + kPage - 1) / kPage);  // int64: lengths reach 2^31 - 1
-    P->tok_off[u] = tokens;
-    slots += P->npages[u];
-    tokens += P->length[u];
-  }
-  if (slots * kPage > INT32_MAX) return fail(err, DAG_E_OVERFLOW, "compact rows exceed int32");
-  const int32_t n_pages = (int32_t)slots;
-  P->page_table.resize(n_pages);
-  std::iota(P->page_table.begin(), P->page_table.end(), 0);
-  if (opts.page_shuffle) {
-    uint64_t st = (uint64_t)(uint32_t)opts.page_shuffle;
-    for (int32_t i = n_pages - 1; i > 0; --i) {
-      const int32_t j = (int32_t)(splitmix64(st) % (uint64_t)(i + 1));
-      std::swap(P->page_table[i], P->page_table[j]);
-    }
-  }
-  const int64_t C = (int64_t)n_pages * kPage;
-  P->page_nrows.assign(n_pages, 0);
-  P->pos_of_row.assign(C, -1);
-  P->row_of_token.assign(tokens, 0);
-  for (int32_t u = 0; u < n; ++u) {
-    for (int32_t lp = 0; lp < P->npages[u]; ++lp) {
-      const int32_t ph = P->page_table[P->slot0[u] + lp];
-      const int32_t nr = std::min(kPage, P->length[u] - lp * kPage);
-      P->page_nrows[ph] = nr;
-      for (int32_t r = 0; r < nr; ++r) {
-        const int64_t row = (int64_t)ph * kPage + r;
-        P->pos_of_row[row] = P->start[u] + lp * kPage + r;
-        P->row_of_token[P->tok_off[u] + lp * kPage + r] = (int32_t)row;
-      }
-    }
-  }
-
-  // ---- 7. tile lists and query pages -----------------------------------------------
-  P->tile_off.assign(n + 1, 0);
-  P->tile_nonself.assign(n, 0);
-  P->tiles.clear();
-  P->qpages.clear();
-  auto pack = [](int32_t lo, int32_t hi) { return lo | (hi << 8); };
-  for (int32_t u = 0; u < n; ++u) {
-    if ((int64_t)P->tiles.size() > INT32_MAX / 2) return fail(err, DAG_E_OVERFLOW, "tile lists too long");
-    P->tile_off[u] = (int32_t)P->tiles.size();
-    if (P->length[u] == 0) continue;
-    for (int64_t r = P->range_off[u]; r < P->range_off[u + 1]; ++r) {
-      const int32_t src = P->ranges[3 * r], lo = P->ranges[3 * r + 1], hi = P->ranges[3 * r + 2];
-      for (int32_t lp = lo / kPage; lp <= (hi - 1) / kPage; ++lp) {
-        const int32_t tlo = std::max(lo - lp * kPage, 0), thi = std::min(hi - lp * kPage, kPage);
-        P->tiles.push_back({P->page_table[P->slot0[src] + lp], pack(tlo, thi)});
-      }
-    }
-    P->tile_nonself[u] = (int32_t)P->tiles.size() - P->tile_off[u];
-    for (int32_t lp = 0; lp < P->npages[u]; ++lp) {
-      const int32_t ph = P->page_table[P->slot0[u] + lp];
-      P->tiles.push_back({ph, pack(0, P->page_nrows[ph])});
-    }
-    for (int32_t lp = 0; lp < P->npages[u]; ++lp) {
-      const int32_t ph = P->page_table[P->slot0[u] + lp];
-      P->qpages.push_back({ph, P->page_nrows[ph], P->tile_off[u], P->tile_nonself[u] + lp + 1});
-    }
-  }
-  P->tile_off[n] = (int32_t)P->tiles.size();
-
-  // ---- 8. reader lists per KV page (fixed order: reader node, then tile order) -------
-  std::vector<int64_t> cnt(n_pages + 1, 0);
-  auto for_each_entry = [&](auto&& emit) {
-    for (int32_t w = 0; w < n; ++w) {
-      if (P->length[w] == 0) continue;
-      for (int32_t t = P->tile_off[w]; t < P->tile_off[w] + P->tile_nonself[w]; ++t)
-        emit(P->tiles[t].page, KEntry{P->slot0[w], 0, P->npages[w], P->tiles[t].lohi});
-      for (int32_t lp = 0; lp < P->npages[w]; ++lp) {
-        const int32_t ph = P->page_table[P->slot0[w] + lp];
-        const int32_t nr = P->page_nrows[ph];
-        emit(ph, KEntry{P->slot0[w], lp, lp + 1, pack(0, nr) | (1 << 16)});
-        if (lp + 1 < P->npages[w]) emit(ph, KEntry{P->slot0[w], lp + 1, P->npages[w], pack(0, nr)});
-      }
-    }
-  };
-  for_each_entry([&](int32_t ph, const KEntry&) { cnt[ph + 1]++; });
-  for (int32_t i = 0; i < n_pages; ++i) cnt[i + 1] += cnt[i];
-  if (cnt[n_pages] > INT32_MAX) return fail(err, DAG_E_OVERFLOW, "reader lists too long");
-  P->kv_off.assign(n_pages + 1, 0);
-  for (int32_t i = 0; i <= n_pages; ++i) P->kv_off[i] = (int32_t)cnt[i];
-  P->kentries.assign(cnt[n_pages], KEntry{0, 0, 0, 0});
-  {
-    std::vector<int64_t> fill(cnt.begin(), cnt.end() - 1);
-    for_each_entry([&](int32_t ph, const KEntry& e) { P->kentries[fill[ph]++] = e; });
-  }
-
-  // KV page pairs for the dK/dV kernel: pages (0, 1), (2, 3), ... of each node; an odd
-  // last page goes alone (B = -1).  A pair's reader steps are its two pages' reader lists
-  // unrolled into 32-row steps and merged by (reader node, query page, occurrence of that
-  // query page in the page's list): a step that both pages see carries both visible
-  // ranges, a step that one page sees has an empty range for the other.  Every key is
-  // logical, so the merged order does not depend on the physical page placement.
-  {
-    std::vector<int32_t> node_of_slot(n_pages, -1);
-    for (int32_t w = 0; w < n; ++w)
-      if (P->length[w] > 0) node_of_slot[P->slot0[w]] = w;
-    struct Item {
-      int32_t w, lq, k, qph, info;  // info: lo << 1 | hi << 8 | diag << 15
-    };
-    auto items_of = [&](int32_t ph, std::vector<Item>& out) {
-      out.clear();
-      for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
-        const KEntry& k = P->kentries[e];
-        const int32_t w = node_of_slot[k.slot_base];
-        const int32_t vis = k.lohi_diag;
-        const int32_t info = ((vis & 0xff) << 1) | (((vis >> 8) & 0xff) << 8) | (((vis >> 16) & 1) << 15);
-        for (int32_t lq = k.lq0; lq < k.lq1; ++lq)
-          out.push_back(Item{w, lq, 0, P->page_table[k.slot_base + lq], info});
-      }
-      std::stable_sort(out.begin(), out.end(),
-                       [](const Item& a, const Item& b) { return a.w != b.w ? a.w < b.w : a.lq < b.lq; });
-      for (size_t i = 1; i < out.size(); ++i)
-        if (out[i].w == out[i - 1].w && out[i].lq == out[i - 1].lq) out[i].k = out[i - 1].k + 1;
-    };
-    auto key_less = [](const Item& a, const Item& b) {
-      if (a.w != b.w) return a.w < b.w;
-      if (a.lq != b.lq) return a.lq < b.lq;
-      return a.k < b.k;
-    };
-    P->kpairs.clear();
-    P->kpair_off.assign(1, 0);
-    P->kpsteps.clear();
-    std::vector<Item> la, lb;
+  if (opts.pack_pages) {
+    // steps 6-9 for the packed layout (pack_plan.cpp)
+    const dag_status pst = build_packed_tables(P, err);
+    if (pst != DAG_OK) return pst;
+  } else {
+    // ---- 6. pages ------------------------------------------------------------------
+    P->slot0.assign(n, 0);
+    P->npages.assign(n, 0);
+    P->tok_off.assign(n, 0);
+    int64_t slots = 0, tokens = 0;
     for (int32_t u = 0; u < n; ++u) {
-      if (P->length[u] == 0) continue;
-      for (int32_t lp = 0; lp < P->npages[u]; lp += 2) {
-        const int32_t pa = P->page_table[P->slot0[u] + lp];
-        const int32_t pb = lp + 1 < P->npages[u] ? P->page_table[P->slot0[u] + lp + 1] : -1;
-        items_of(pa, la);
-        if (pb >= 0) items_of(pb, lb); else lb.clear();
-        size_t ia = 0, ib = 0;
-        while (ia < la.size() || ib < lb.size()) {
-          int32_t qph, infa = 0, infb = 0;
-          if (ib == lb.size() || (ia < la.size() && key_less(la[ia], lb[ib]))) {
-            qph = la[ia].qph, infa = la[ia++].info;
-          } else if (ia == la.size() || key_less(lb[ib], la[ia])) {
-            qph = lb[ib].qph, infb = lb[ib++].info;
-          } else {
-            qph = la[ia].qph, infa = la[ia++].info, infb = lb[ib++].info;
-          }
-          const int32_t nr = P->page_nrows[qph];
-          for (int32_t rb = 0; rb < (nr > 32 ? 2 : 1); ++rb)
-            P->kpsteps.push_back(KStep{qph, (int32_t)((uint32_t)(rb | infa) | ((uint32_t)infb << 16))});
+      P->slot0[u] = (int32_t)std::min<int64_t>(slots, INT32_MAX);
+      P->npages[u] = (int32_t)(((int64_t)P->length[u] + kPage - 1) / kPage);  // int64: lengths reach 2^31 - 1
+      P->tok_off[u] = tokens;
+      slots += P->npages[u];
+      tokens += P->length[u];
+    }
+    if (slots * kPage > INT32_MAX) return fail(err, DAG_E_OVERFLOW, "compact rows exceed int32");
+    const int32_t n_pages = (int32_t)slots;
+    P->page_table.resize(n_pages);
+    std::iota(P->page_table.begin(), P->page_table.end(), 0);
+    if (opts.page_shuffle) {
+      uint64_t st = (uint64_t)(uint32_t)opts.page_shuffle;
+      for (int32_t i = n_pages - 1; i > 0; --i) {
+        const int32_t j = (int32_t)(splitmix64(st) % (uint64_t)(i + 1));
+        std::swap(P->page_table[i], P->page_table[j]);
+      }
+    }
+    const int64_t C = (int64_t)n_pages * kPage;
+    P->page_nrows.assign(n_pages, 0);
+    P->pos_of_row.assign(C, -1);
+    P->row_of_token.assign(tokens, 0);
+    for (int32_t u = 0; u < n; ++u) {
+      for (int32_t lp = 0; lp < P->npages[u]; ++lp) {
+        const int32_t ph = P->page_table[P->slot0[u] + lp];
+        const int32_t nr = std::min(kPage, P->length[u] - lp * kPage);
+        P->page_nrows[ph] = nr;
+        for (int32_t r = 0; r < nr; ++r) {
+          const int64_t row = (int64_t)ph * kPage + r;
+          P->pos_of_row[row] = P->start[u] + lp * kPage + r;
+          P->row_of_token[P->tok_off[u] + lp * kPage + r] = (int32_t)row;
         }
-        P->kpairs.push_back(pa);
-        P->kpairs.push_back(pb);
-        P->kpair_off.push_back((int64_t)P->kpsteps.size());
       }
     }
-  }
 
-  // ---- 9. launch orders -------------------------------------------------------------
-  // Node-grouped, heaviest first: nodes sorted by their heaviest page's work, each
-  // node's pages listed together (heaviest first).  Neighbouring work-groups then
-  // share K/V tiles (forward, dQ: one node's query pages see the same tiles) or
-  // reader lists (dK/dV: one node's KV pages are read by the same query pages).
-  {
-    std::vector<int64_t> wq(P->qpages.size(), 0);
-    for (size_t i = 0; i < P->qpages.size(); ++i) {
-      const QPage& q = P->qpages[i];
-      int64_t keys = 0;
-      for (int32_t t = q.tile_begin; t < q.tile_begin + q.tile_count; ++t)
-        keys += ((P->tiles[t].lohi >> 8) & 0xff) - (P->tiles[t].lohi & 0xff);
-      wq[i] = keys;
-    }
-    // query pages of node u are contiguous in qpages, lp ascending (heaviest last)
-    std::vector<int32_t> qp_first(n + 1, 0);
-    for (int32_t u = 0, c = 0; u < n; ++u) {
-      qp_first[u] = c;
-      c += P->length[u] > 0 ? P->npages[u] : 0;
-      qp_first[u + 1] = c;
-    }
-    std::vector<int32_t> nodes_by(n);
-    std::iota(nodes_by.begin(), nodes_by.end(), 0);
-    auto node_wq = [&](int32_t u) { return qp_first[u + 1] > qp_first[u] ? wq[qp_first[u + 1] - 1] : -1; };
-    std::stable_sort(nodes_by.begin(), nodes_by.end(), [&](int32_t a, int32_t b) { return node_wq(a) > node_wq(b); });
-    P->fwd_order.clear();
-    for (int32_t u : nodes_by)
-      for (int32_t i = qp_first[u + 1] - 1; i >= qp_first[u]; --i) P->fwd_order.push_back(i);
-
-    std::vector<int64_t> wk(n_pages, 0);
-    for (int32_t ph = 0; ph < n_pages; ++ph) {
-      int64_t w = 0;
-      for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
-        const KEntry& k = P->kentries[e];
-        w += (int64_t)(k.lq1 - k.lq0) * (((k.lohi_diag >> 8) & 0xff) - (k.lohi_diag & 0xff));
+    // ---- 7. tile lists and query pages -----------------------------------------------
+    P->tile_off.assign(n + 1, 0);
+    P->tile_nonself.assign(n, 0);
+    P->tiles.clear();
+    P->qpages.clear();
+    auto pack = [](int32_t lo, int32_t hi) { return lo | (hi << 8); };
+    for (int32_t u = 0; u < n; ++u) {
+      if ((int64_t)P->tiles.size() > INT32_MAX / 2) return fail(err, DAG_E_OVERFLOW, "tile lists too long");
+      P->tile_off[u] = (int32_t)P->tiles.size();
+      if (P->length[u] == 0) continue;
+      for (int64_t r = P->range_off[u]; r < P->range_off[u + 1]; ++r) {
+        const int32_t src = P->ranges[3 * r], lo = P->ranges[3 * r + 1], hi = P->ranges[3 * r + 2];
+        for (int32_t lp = lo / kPage; lp <= (hi - 1) / kPage; ++lp) {
+          const int32_t tlo = std::max(lo - lp * kPage, 0), thi = std::min(hi - lp * kPage, kPage);
+          P->tiles.push_back({P->page_table[P->slot0[src] + lp], pack(tlo, thi)});
+        }
       }
-      wk[ph] = w;
+      P->tile_nonself[u] = (int32_t)P->tiles.size() - P->tile_off[u];
+      for (int32_t lp = 0; lp < P->npages[u]; ++lp) {
+        const int32_t ph = P->page_table[P->slot0[u] + lp];
+        P->tiles.push_back({ph, pack(0, P->page_nrows[ph])});
+      }
+      for (int32_t lp = 0; lp < P->npages[u]; ++lp) {
+        const int32_t ph = P->page_table[P->slot0[u] + lp];
+        P->qpages.push_back({ph, P->page_nrows[ph], P->tile_off[u], P->tile_nonself[u] + lp + 1});
+      }
     }
-    auto node_wk = [&](int32_t u) {  // a node's first page has the most readers
-      return P->length[u] > 0 ? wk[P->page_table[P->slot0[u]]] : -1;
+    P->tile_off[n] = (int32_t)P->tiles.size();
+
+    // ---- 8. reader lists per KV page (fixed order: reader node, then tile order) -------
+    std::vector<int64_t> cnt(n_pages + 1, 0);
+    auto for_each_entry = [&](auto&& emit) {
+      for (int32_t w = 0; w < n; ++w) {
+        if (P->length[w] == 0) continue;
+        for (int32_t t = P->tile_off[w]; t < P->tile_off[w] + P->tile_nonself[w]; ++t)
+          emit(P->tiles[t].page, KEntry{P->slot0[w], 0, P->npages[w], P->tiles[t].lohi});
+        for (int32_t lp = 0; lp < P->npages[w]; ++lp) {
+          const int32_t ph = P->page_table[P->slot0[w] + lp];
+          const int32_t nr = P->page_nrows[ph];
+          emit(ph, KEntry{P->slot0[w], lp, lp + 1, pack(0, nr) | (1 << 16)});
+          if (lp + 1 < P->npages[w]) emit(ph, KEntry{P->slot0[w], lp + 1, P->npages[w], pack(0, nr)});
+        }
+      }
     };
-    std::stable_sort(nodes_by.begin(), nodes_by.end(), [&](int32_t a, int32_t b) { return node_wk(a) > node_wk(b); });
-    P->bwd_order.clear();
-    for (int32_t u : nodes_by)
-      if (P->length[u] > 0)
-        for (int32_t lp = 0; lp < P->npages[u]; ++lp) P->bwd_order.push_back(P->page_table[P->slot0[u] + lp]);
-    // pairs in the same node order (a node's pairs are consecutive in kpairs)
-    std::vector<int32_t> pair0(n + 1, 0);
-    for (int32_t u = 0, c = 0; u < n; ++u) {
-      pair0[u] = c;
-      if (P->length[u] > 0) c += (P->npages[u] + 1) / 2;
-      pair0[u + 1] = c;
+    for_each_entry([&](int32_t ph, const KEntry&) { cnt[ph + 1]++; });
+    for (int32_t i = 0; i < n_pages; ++i) cnt[i + 1] += cnt[i];
+    if (cnt[n_pages] > INT32_MAX) return fail(err, DAG_E_OVERFLOW, "reader lists too long");
+    P->kv_off.assign(n_pages + 1, 0);
+    for (int32_t i = 0; i <= n_pages; ++i) P->kv_off[i] = (int32_t)cnt[i];
+    P->kentries.assign(cnt[n_pages], KEntry{0, 0, 0, 0});
+    {
+      std::vector<int64_t> fill(cnt.begin(), cnt.end() - 1);
+      for_each_entry([&](int32_t ph, const KEntry& e) { P->kentries[fill[ph]++] = e; });
     }
-    P->pair_order.clear();
-    for (int32_t u : nodes_by)
-      for (int32_t i = pair0[u]; i < pair0[u + 1]; ++i) P->pair_order.push_back(i);
+
+    // KV page pairs for the dK/dV kernel: pages (0, 1), (2, 3), ... of each node; an odd
+    // last page goes alone (B = -1).  A pair's reader steps are its two pages' reader lists
+    // unrolled into 32-row steps and merged by one logical key: the other nodes' query pages
+    // first, by (reader node, query page, occurrence of that query page in the page's
+    // list), then the pages' own node's query pages, last page first.  A step that both
+    // pages see carries both visible ranges, a step that one page sees has an empty range
+    // for the other.  Every key is logical, so the merged order does not depend on the
+    // physical page placement.  Every page of a node has the same descendants and (per
+    // span) the same mount readers, and the node's own pages come last, latest first, so
+    // the pairs of one node, which run side by side, walk the shared reader steps in step
+    // with each other: each staged Q / dO tile is fetched from HBM once and served to the
+    // other pairs from L2.
+    {
+      std::vector<int32_t> node_of_slot(n_pages, -1);
+      for (int32_t w = 0; w < n; ++w)
+        if (P->length[w] > 0) node_of_slot[P->slot0[w]] = w;
+      struct Item {
+        int32_t own, w, lq, k, qph, info;  // own: the page's own node (sorted last, lq descending);
+      };                                   // info: lo << 1 | hi << 8 | diag << 15
+      auto key_less = [](const Item& a, const Item& b) {
+        if (a.own != b.own) return a.own < b.own;
+        if (a.w != b.w) return a.w < b.w;
+        if (a.lq != b.lq) return a.own ? a.lq > b.lq : a.lq < b.lq;
+        return a.k < b.k;
+      };
+      auto items_of = [&](int32_t ph, int32_t u, std::vector<Item>& out) {
+        out.clear();
+        for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
+          const KEntry& k = P->kentries[e];
+          const int32_t w = node_of_slot[k.slot_base];
+          const int32_t vis = k.lohi_diag;
+          const int32_t info = ((vis & 0xff) << 1) | (((vis >> 8) & 0xff) << 8) | (((vis >> 16) & 1) << 15);
+          for (int32_t lq = k.lq0; lq < k.lq1; ++lq)
+            out.push_back(Item{w == u ? 1 : 0, w, lq, 0, P->page_table[k.slot_base + lq], info});
+        }
+        std::stable_sort(out.begin(), out.end(), key_less);  // k is still 0: ties keep list order
+        for (size_t i = 1; i < out.size(); ++i)
+          if (out[i].w == out[i - 1].w && out[i].lq == out[i - 1].lq) out[i].k = out[i - 1].k + 1;
+      };
+      P->kpairs.clear();
+      P->kpair_off.assign(1, 0);
+      P->kpsteps.clear();
+      std::vector<Item> la, lb;
+      for (int32_t u = 0; u < n; ++u) {
+        if (P->length[u] == 0) continue;
+        for (int32_t lp = 0; lp < P->npages[u]; lp += 2) {
+          const int32_t pa = P->page_table[P->slot0[u] + lp];
+          const int32_t pb = lp + 1 < P->npages[u] ? P->page_table[P->slot0[u] + lp + 1] : -1;
+          items_of(pa, u, la);
+          if (pb >= 0) items_of(pb, u, lb); else lb.clear();
+          size_t ia = 0, ib = 0;
+          while (ia < la.size() || ib < lb.size()) {
+            int32_t qph, infa = 0, infb = 0;
+            if (ib == lb.size() || (ia < la.size() && key_less(la[ia], lb[ib]))) {
+              qph = la[ia].qph, infa = la[ia++].info;
+            } else if (ia == la.size() || key_less(lb[ib], la[ia])) {
+              qph = lb[ib].qph, infb = lb[ib++].info;
+            } else {
+              qph = la[ia].qph, infa = la[ia++].info, infb = lb[ib++].info;
+            }
+            const int32_t nr = P->page_nrows[qph];
+            for (int32_t rb = 0; rb < (nr > 32 ? 2 : 1); ++rb)
+              P->kpsteps.push_back(KStep{qph, (int32_t)((uint32_t)(rb | infa) | ((uint32_t)infb << 16))});
+          }
+          P->kpairs.push_back(pa);
+          P->kpairs.push_back(pb);
+          P->kpair_off.push_back((int64_t)P->kpsteps.size());
+        }
+      }
+    }
+
+    // ---- 9. launch orders -------------------------------------------------------------
+    // Node-grouped, heaviest first: nodes sorted by their heaviest page's work, each
+    // node's pages listed together (heaviest first).  Neighbouring work-groups then
+    // share K/V tiles (forward, dQ: one node's query pages see the same tiles) or
+    // reader lists (dK/dV: one node's KV pages are read by the same query pages).
+    {
+      std::vector<int64_t> wq(P->qpages.size(), 0);
+      for (size_t i = 0; i < P->qpages.size(); ++i) {
+        const QPage& q = P->qpages[i];
+        int64_t keys = 0;
+        for (int32_t t = q.tile_begin; t < q.tile_begin + q.tile_count; ++t)
+          keys += ((P->tiles[t].lohi >> 8) & 0xff) - (P->tiles[t].lohi & 0xff);
+        wq[i] = keys;
+      }
+      // query pages of node u are contiguous in qpages, lp ascending (heaviest last)
+      std::vector<int32_t> qp_first(n + 1, 0);
+      for (int32_t u = 0, c = 0; u < n; ++u) {
+        qp_first[u] = c;
+        c += P->length[u] > 0 ? P->npages[u] : 0;
+        qp_first[u + 1] = c;
+      }
+      std::vector<int32_t> nodes_by(n);
+      std::iota(nodes_by.begin(), nodes_by.end(), 0);
+      auto node_wq = [&](int32_t u) { return qp_first[u + 1] > qp_first[u] ? wq[qp_first[u + 1] - 1] : -1; };
+      std::stable_sort(nodes_by.begin(), nodes_by.end(), [&](int32_t a, int32_t b) { return node_wq(a) > node_wq(b); });
+      P->fwd_order.clear();
+      for (int32_t u : nodes_by)
+        for (int32_t i = qp_first[u + 1] - 1; i >= qp_first[u]; --i) P->fwd_order.push_back(i);
+
+      std::vector<int64_t> wk(n_pages, 0);
+      for (int32_t ph = 0; ph < n_pages; ++ph) {
+        int64_t w = 0;
+        for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
+          const KEntry& k = P->kentries[e];
+          w += (int64_t)(k.lq1 - k.lq0) * (((k.lohi_diag >> 8) & 0xff) - (k.lohi_diag & 0xff));
+        }
+        wk[ph] = w;
+      }
+      auto node_wk = [&](int32_t u) {  // a node's first page has the most readers
+        return P->length[u] > 0 ? wk[P->page_table[P->slot0[u]]] : -1;
+      };
+      std::stable_sort(nodes_by.begin(), nodes_by.end(), [&](int32_t a, int32_t b) { return node_wk(a) > node_wk(b); });
+      P->bwd_order.clear();
+      for (int32_t u : nodes_by)
+        if (P->length[u] > 0)
+          for (int32_t lp = 0; lp < P->npages[u]; ++lp) P->bwd_order.push_back(P->page_table[P->slot0[u] + lp]);
+      // pairs in the same node order (a node's pairs are consecutive in kpairs)
+      std::vector<int32_t> pair0(n + 1, 0);
+      for (int32_t u = 0, c = 0; u < n; ++u) {
+        pair0[u] = c;
+        if (P->length[u] > 0) c += (P->npages[u] + 1) / 2;
+        pair0[u + 1] = c;
+      }
+      P->pair_order.clear();
+      for (int32_t u : nodes_by)
+        for (int32_t i = pair0[u]; i < pair0[u + 1]; ++i) P->pair_order.push_back(i);
+    }
   }
 
   // ---- info ------------------------------------------------------------------------
   dag_plan_info& I = P->info;
   I = dag_plan_info{};
-  I.rows = C;
-  I.tokens = tokens;
-  I.pages = n_pages;
+  I.rows = (int64_t)P->pos_of_row.size();
+  I.tokens = (int64_t)P->row_of_token.size();
+  I.pages = (int64_t)P->page_nrows.size();
   I.query_pages = (int64_t)P->qpages.size();
   I.transitive = opts.transitive;
   I.view = opts.view;
@@ -455,6 +469,14 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
   std::vector<char> has_child(n, 0);
   for (int32_t u = 0; u < n; ++u)
     if (P->parent[u] >= 0) has_child[P->parent[u]] = 1;
+  // multiplicity (HARTS Sec. 3.5): a node's tokens belong to every trajectory through it,
+  // one per leaf below it; parents precede children, so one backward sweep sums them
+  P->leaves_below.assign(n, 0);
+  for (int32_t u = n - 1; u >= 0; --u) {
+    if (!has_child[u]) P->leaves_below[u] += 1;
+    if (P->parent[u] >= 0) P->leaves_below[P->parent[u]] += P->leaves_below[u];
+  }
+  for (int32_t u = 0; u < n; ++u) I.semantic_tokens += (int64_t)P->length[u] * P->leaves_below[u];
   for (int32_t u = 0; u < n; ++u) {
     int64_t nonself = 0;
     for (int64_t r = P->range_off[u]; r < P->range_off[u + 1]; ++r)
@@ -469,9 +491,12 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
     }
   }
   for (const QPage& q : P->qpages) I.fwd_tiles += q.tile_count;
-  I.bwd_entries = (int64_t)P->kentries.size();
-  const dag_status cst = build_conv_tables(P, err);
-  if (cst != DAG_OK) return cst;
+  I.bwd_entries = P->packed ? (int64_t)P->kpsteps.size() : (int64_t)P->kentries.size();
+  I.pack_pages = P->packed ? 1 : 0;
+  if (!P->packed) {  // the convolution walks a page's rows as one path: one node per page
+    const dag_status cst = build_conv_tables(P, err);
+    if (cst != DAG_OK) return cst;
+  }
   if (opts.gdn_chunk > 0) return build_gdn_schedule(P, opts.gdn_chunk, err);
   return DAG_OK;
 }

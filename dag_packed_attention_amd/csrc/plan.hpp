@@ -52,6 +52,12 @@ struct KStep {
   int32_t info;  // rb | loA << 1 | hiA << 8 | diagA << 15 | loB << 17 | hiB << 24 | diagB << 31
 };
 
+// Mask ids of one merged reader step's two pages (packed plans): -1 = the step's range
+// [lo, hi) alone says what the step's rows see of that page.
+struct KMask {
+  int32_t a, b;
+};
+
 // A token within 3 steps after a page's last token on some path, with the rows
 // 1, 2 and 3 steps before it on its own path (-1: none); the short convolution's
 // backward reads these successors.
@@ -111,6 +117,15 @@ struct Plan {
   std::vector<int32_t> conv_prev;              // 4 per physical page: rows 1..3 steps before its first token
   std::vector<int64_t> conv_ext_off;           // physical page -> first successor entry (size pages+1)
   std::vector<ConvExt> conv_ext;
+  std::vector<int32_t> leaves_below;           // per node: leaves in its subtree (itself if a leaf)
+  // packed page layout (opts.pack_pages): several short nodes share a page, so what a
+  // query row sees of a KV page can differ from row to row; such a tile carries a mask
+  bool packed = false;
+  std::vector<int64_t> node_row0;              // first compact row of every node (-1: no tokens)
+  std::vector<int32_t> tile_mask;              // per tile: mask id, -1 = [lo, hi) for every row
+  std::vector<uint64_t> masks;                 // per mask id: 64 row masks (bit c: key row c), then
+                                               // 64 key masks (bit r: query row r)
+  std::vector<KMask> kstep_mask;               // per merged reader step
   std::vector<int32_t> pos_of_row;             // C
   std::vector<int32_t> row_of_token;           // U
   // gated-delta-rule schedule (empty when opts.gdn_chunk == 0)
@@ -132,6 +147,9 @@ struct Plan {
 // Compile; returns DAG_OK or an error code with a message in `err`.
 dag_status build_plan(const dag_node* nodes, int32_t n_nodes, const dag_mount* mounts,
                       int32_t n_mounts, const dag_build_opts* opts, Plan* out, std::string* err);
+
+// Packed page layout and its attention tables (steps 6-9 of build_plan for opts.pack_pages).
+dag_status build_packed_tables(Plan* P, std::string* err);
 
 // Short-convolution tables (HARTS Sec. 4.2) over the plan's parent tree and rows.
 dag_status build_conv_tables(Plan* P, std::string* err);

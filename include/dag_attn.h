@@ -78,7 +78,14 @@ typedef struct {
 
 typedef struct {
   int32_t page_size;    /* must be 64 (0 selects 64)                                    */
-  int32_t q_block;      /* must be 64 (0 selects 64): one query block per KV page        */
+  int32_t q_block;      /* must be 64 (0 selects 64): one query block per KV page.  The    */
+                        /*    MFMA kernels take a 64-row query page and all four query     */
+                        /*    heads of a GQA group per work-group, so every staged K/V     */
+                        /*    tile already feeds 256 query rows (256 flop per byte from    */
+                        /*    LDS), and the pages of one node, launched side by side, share */
+                        /*    their tiles in L2; a 128-row block would halve the number of  */
+                        /*    work-groups without raising the intensity HBM sees.  Other    */
+                        /*    values return DAG_E_UNSUPPORTED.                              */
   int32_t transitive;   /* 1: a reader also sees what its mounted sources see (Octopus   */
                         /*    Sec. 3.3 item 1, "including transitive mounts"); 0: direct */
   int32_t page_shuffle; /* 0: pages in node order; otherwise a seed for a random physical */
@@ -95,6 +102,17 @@ typedef struct {
                         /*    continuing from its parent without the jump (Octopus Table 5's */
                         /*    unshifted regime).  Row layout and page table are the same in  */
                         /*    every view, so one set of tensors serves plans of all views.   */
+  int32_t pack_pages;   /* 0: every node starts on a fresh page (pages hold one node);       */
+                        /* 1: nodes in depth-first order share pages: a node that fits in    */
+                        /*    the rest of the open page goes there, a longer one starts a     */
+                        /*    page (its last page stays open).  For trees of short segments   */
+                        /*    (HARTS App. A's 1-15-token turns) this removes most padding     */
+                        /*    rows; a (query page, KV page) tile whose rows see the page      */
+                        /*    differently carries a 64 x 64 visibility mask.  Packed plans    */
+                        /*    run attention on the MFMA path (bf16, head_dim 128, Hq = 4 Hkv), */
+                        /*    the gated delta rule and log-probabilities; the generic          */
+                        /*    attention kernels and the convolution return DAG_E_UNSUPPORTED. */
+                        /*    Not combinable with page_shuffle.                                */
 } dag_build_opts;
 
 enum { DAG_VIEW_MOUNTED = 0, DAG_VIEW_MOUNT_FREE = 1, DAG_VIEW_UNSHIFTED = 2 };
@@ -123,6 +141,9 @@ typedef struct {
   int64_t gdn_chunks;      /* execution chunks over all sequences, replay included    */
   int64_t gdn_segments;    /* fork-free segments of the (mount-free) tree             */
   int32_t view;            /* the build option                                        */
+  int64_t semantic_tokens; /* S = sum over tokens of their multiplicity (HARTS Sec. 3.5): */
+                           /* own-token rows of the flat per-trajectory batch           */
+  int32_t pack_pages;      /* the build option                                        */
 } dag_plan_info;
 
 /* Validate the node/mount tables and compile them into a plan.  Host only;
@@ -143,6 +164,23 @@ dag_status dag_plan_info_get(const dag_plan* plan, dag_plan_info* out);
  * sum_{w<u} length(w) + i) -> row_of_token[U]; Eq. 2 position of every row
  * -> pos_of_row[C] (-1 on padding rows).  Either pointer may be NULL. */
 dag_status dag_plan_rows(const dag_plan* plan, int32_t* row_of_token, int32_t* pos_of_row);
+
+/* The compact rows that query row `row` sees, decoded from the plan's forward tables the
+ * way the forward and dQ kernels read them (tile ranges, masks, the causal rule on a query
+ * page's last unmasked tile), sorted -> key_rows[min(n, cap)], count -> *n (padding rows see
+ * nothing).  And the query rows whose contributions the dK/dV kernel sums into key row
+ * `row`, decoded from its reader steps.  Both equal Octopus Eq. 4's visible sets mapped to
+ * rows; they exist to check the tables on the host.  (The causal rule applies to a query
+ * page's last tile only when that tile carries no mask.) */
+dag_status dag_plan_visibility(const dag_plan* plan, int32_t row, int32_t* key_rows, int32_t cap, int32_t* n);
+dag_status dag_plan_readers(const dag_plan* plan, int32_t row, int32_t* query_rows, int32_t cap, int32_t* n);
+
+/* Multiplicity of every token in node-major order -> mult[U] (HARTS Sec. 3.5: the
+ * number of root-to-leaf trajectories that hold the token as one of their own tokens,
+ * i.e. the leaves below its node, the node itself if it has no children; mounted spans
+ * do not count, since a spliced copy carries no training target).  The multiplicities
+ * sum to dag_plan_info.semantic_tokens. */
+dag_status dag_plan_multiplicity(const dag_plan* plan, int32_t* mult);
 
 /* Start position s(u) of every node (Octopus Sec. 3.2 Eq. 2) -> start[n_nodes]. */
 dag_status dag_plan_starts(const dag_plan* plan, int32_t* start);
@@ -169,8 +207,11 @@ typedef struct {
   int32_t head_dim;    /* even, 2..128                                                  */
   int32_t dtype;       /* DAG_DTYPE_BF16: bf16 tensors, fp32 accumulation.  When           */
                        /* head_dim == 128 and Hq == 4 Hkv the products run on MFMA with     */
-                       /* fp16 operands (bf16 -> fp16 is exact for 2^-14 <= |x| < 2^15; dO  */
-                       /* is first scaled by a power of two so its largest |x| is in [1,2)) */
+                       /* fp16 operands: q, k, v and dO are each first scaled by the power  */
+                       /* of two that puts their tensor's largest |x| (over valid rows) in  */
+                       /* [1, 2), undone exactly in the outputs, so no finite bf16 input     */
+                       /* overflows; an element below 2^-14 of its tensor's maximum keeps   */
+                       /* fp16's subnormal spacing (2^-24 of that maximum)                   */
                        /* DAG_DTYPE_FP32: fp32 throughout                                   */
   int32_t grad_dtype;  /* element type of dq, dk, dv: DAG_DTYPE_BF16 or DAG_DTYPE_FP32;    */
                        /* must be FP32 when dtype is FP32.  Large shared-row gradients     */
@@ -188,10 +229,11 @@ dag_status dag_attn_workspace(const dag_plan* plan, const dag_attn_params* p, si
  *   o[t,h]   = sum_{j in V(t)} softmax_j(scale <R(pos_t) q[t,h], R(pos_j) k[j,g]>) v[j,g]
  *   lse[t,h] = log sum_{j in V(t)} exp(scale <R(pos_t) q[t,h], R(pos_j) k[j,g]>)
  * q, o: [C, Hq, D]; k, v: [C, Hkv, D] (dtype); lse: [C, Hq] fp32.
- * o_lo (optional, bf16 only, may be NULL): [C, Hq, D] bf16 receiving the rounding
- * residual o_exact - o; passing it to dag_attn_bwd lets the backward form
- * rowsum(dO * O) from an O accurate to ~2^-17 instead of bf16's 2^-9, which matters
- * where attention is concentrated on few keys.
+ * o_lo (bf16 only; NULL for a forward that no backward follows): [C, Hq, D] bf16
+ * receiving the rounding residual o_exact - o.  The bf16 backward needs it: it forms
+ * rowsum(dO * O) from O = o + o_lo, accurate to ~2^-17 instead of bf16's 2^-9; with O
+ * rounded to bf16 alone, attention concentrated on few keys moves dq and dk by more than
+ * 2e-2 (measured on logits of standard deviation 16).
  * ws: device workspace of at least fwd_bytes. */
 dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k,
                         const void* v, void* o, float* lse, void* o_lo, void* ws, size_t ws_bytes,
@@ -201,8 +243,9 @@ dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q,
  * dq [C, Hq, D]; dk, dv [C, Hkv, D] (grad_dtype), where every key row's gradient is the sum
  * over all readers (own branch, descendants, mount readers) taken in a fixed
  * order, so results are bitwise reproducible (Octopus Sec. 3.4 Eq. 8, HARTS
- * Sec. 3.4).  o, lse and o_lo (NULL if the forward wrote none) are the forward's
- * outputs.  ws: at least bwd_bytes. */
+ * Sec. 3.4).  o, lse and o_lo are the forward's outputs; o_lo is required for
+ * DAG_DTYPE_BF16 (DAG_E_INVALID when NULL) and must be NULL for DAG_DTYPE_FP32.
+ * ws: at least bwd_bytes. */
 dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k,
                         const void* v, const void* o, const float* lse, const void* o_lo,
                         const void* dO, void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,

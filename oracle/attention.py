@@ -268,13 +268,18 @@ class RowSampler:
                 lse[a, h] = l
         return o, lse
 
-    def row_grads(self, tokens: Sequence[int], q, k, v, do):
+    def row_grads(self, tokens: Sequence[int], q, k, v, do, term_size: bool = False):
         """(o [n,Hq,d], lse [n,Hq], dq [n,Hq,d]) for the given compact tokens.
 
         Each row from its own visible set V(t) alone: P_tj = softmax_j(s_tj),
         D_t = dO_t . O_t, dS_tj = P_tj (dO_t . v_j - D_t) and
         dq_t = R(pos_t)^T scale sum_j dS_tj R(pos_j) k_j, the textbook softmax
         backward for one query row (the row's dO is its compact upstream gradient).
+        With ``term_size`` a fourth array [n,Hq,d] bounds the terms behind each dq element:
+        scale sum_j P_tj (sum_d |dO_td v_jd| + sum_d |dO_td O_td|) |R(pos_j) k_j| (with
+        rotation, the two elements of each rotated pair added, which bounds any rotation of
+        them).  dS_tj = P_tj (dP_tj - D_t) cancels two dot products, so summing each of them
+        with a relative rounding error e per term moves dq by at most e times this.
         """
         q, k, v, do = _np(q), _np(k), _np(v), _np(do)
         d = k.shape[-1]
@@ -282,6 +287,7 @@ class RowSampler:
         o = np.zeros((len(tokens), self.p.hq, d))
         lse = np.zeros((len(tokens), self.p.hq))
         dq = np.zeros((len(tokens), self.p.hq, d))
+        size = np.zeros((len(tokens), self.p.hq, d))
         for a, t in enumerate(tokens):
             t = int(t)
             for h, (kt, P, l, oh, kk, _) in enumerate(self._fwd_one(t, q, k, v)):
@@ -291,8 +297,16 @@ class RowSampler:
                 ds = P * (dp - float(g_o @ oh))
                 o[a, h], lse[a, h] = oh, l
                 dq[a, h] = scale * (ds @ kk)
+                if term_size:
+                    dp_abs = np.abs(np.asarray(v[kt, gg], np.float64)) @ np.abs(g_o)
+                    size[a, h] = scale * ((P * (dp_abs + float(np.abs(g_o) @ np.abs(oh)))) @ np.abs(kk))
             dq[a] = rotate_transpose(dq[a][None], self.pos[t:t + 1], self.p.rope_base)[0]
-        return o, lse, dq
+        if not term_size:
+            return o, lse, dq
+        if self.p.rope_base != 0:
+            half = d // 2
+            size = np.concatenate([size[..., :half] + size[..., half:]] * 2, axis=-1)
+        return o, lse, dq, size
 
     def reader_nodes(self, j: int) -> List[int]:
         """Nodes with at least one query token whose visible set contains key token j."""

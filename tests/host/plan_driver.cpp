@@ -47,6 +47,12 @@ static int check(const Plan& P) {
   if ((int64_t)P.kpair_off.size() != npairs + 1 || P.kpair_off[0] != 0) return 8;
   if ((int64_t)P.kpsteps.size() != P.kpair_off[npairs]) return 13;
   std::vector<int> seen(pages, 0);
+  std::vector<int> node_of_page(pages, -1), slot_of_page(pages, -1);
+  for (int u = 0; u < P.n_nodes; ++u)
+    for (int lp = 0; lp < P.npages[u]; ++lp) {
+      node_of_page[P.page_table[P.slot0[u] + lp]] = u;
+      slot_of_page[P.page_table[P.slot0[u] + lp]] = lp;
+    }
   for (int64_t pr = 0; pr < npairs; ++pr) {
     for (int side = 0; side < 2; ++side) {
       const int ph = P.kpairs[2 * pr + side];
@@ -57,6 +63,7 @@ static int check(const Plan& P) {
         continue;
       }
       if (ph >= pages || seen[ph]++) return 9;
+      if (P.packed) continue;  // packed: checked against the tile lists below
       std::vector<std::array<int, 5>> want, got;  // qph, rb, lo, hi, diag
       for (int e = P.kv_off[ph]; e < P.kv_off[ph + 1]; ++e) {
         const KEntry& k = P.kentries[e];
@@ -78,10 +85,76 @@ static int check(const Plan& P) {
       if (want != got) return 11;
     }
     if (P.kpair_off[pr + 1] <= P.kpair_off[pr]) return 14;  // a launched pair has steps
+    // the pair's own node's query pages come after every other reader's, latest page first
+    if (P.packed) continue;
+    const int u = node_of_page[P.kpairs[2 * pr]];
+    bool in_own = false;
+    int prev_slot = 1 << 30;
+    for (int64_t i = P.kpair_off[pr]; i < P.kpair_off[pr + 1]; ++i) {
+      const int qph = P.kpsteps[i].qph;
+      if (node_of_page[qph] == u) {
+        in_own = true;
+        if (slot_of_page[qph] > prev_slot) return 16;
+        prev_slot = slot_of_page[qph];
+      } else if (in_own) {
+        return 16;
+      }
+    }
   }
   for (int64_t ph = 0; ph < pages; ++ph)
     if (!seen[ph] && P.page_nrows[ph] > 0) return 12;  // every page with rows is in a pair
   if ((int64_t)P.pair_order.size() != npairs) return 15;
+  if (P.packed) {
+    // masks: one id per tile / step side, in range; the key-major half is the transpose of
+    // the row-major half; a tile's [lo, hi) spans its mask's keys; padding rows see nothing
+    const int64_t nmask = (int64_t)P.masks.size() / 128;
+    if ((int64_t)P.masks.size() != nmask * 128 || P.tile_mask.size() != P.tiles.size()) return 50;
+    if (P.kstep_mask.size() != P.kpsteps.size()) return 51;
+    for (const QPage& q : P.qpages) {
+      if (P.tile_mask[q.tile_begin + q.tile_count - 1] < 0) return 52;  // own page last, masked
+      for (int t = q.tile_begin; t < q.tile_begin + q.tile_count; ++t) {
+        const int mi = P.tile_mask[t];
+        if (mi < -1 || mi >= nmask) return 53;
+        if (mi < 0) continue;
+        const uint64_t* m = &P.masks[(size_t)mi * 128];
+        uint64_t any = 0;
+        for (int r = 0; r < 64; ++r) {
+          if (r >= q.nrows && m[r]) return 54;
+          any |= m[r];
+          for (int c = 0; c < 64; ++c)
+            if (((m[r] >> c) & 1) != ((m[64 + c] >> r) & 1)) return 55;
+        }
+        const int lo = P.tiles[t].lohi & 0xff, hi = (P.tiles[t].lohi >> 8) & 0xff;
+        if (!any || __builtin_ctzll(any) != lo || 64 - __builtin_clzll(any) != hi) return 56;
+      }
+    }
+    for (const KMask& km : P.kstep_mask)
+      if (km.a < -1 || km.a >= nmask || km.b < -1 || km.b >= nmask) return 57;
+    // every (query page, KV page) tile appears as the pair's steps for that page, with the same
+    // range and mask, for each 32-row half of the query page whose rows see it
+    std::vector<std::array<int, 5>> want, got;  // kv page, qph, rb, lohi, mask
+    for (const QPage& q : P.qpages)
+      for (int t = q.tile_begin; t < q.tile_begin + q.tile_count; ++t)
+        for (int rb = 0; rb * 32 < q.nrows; ++rb) {
+          const int mi = P.tile_mask[t];
+          bool sees = mi < 0;
+          for (int r = 32 * rb; r < 32 * rb + 32 && !sees; ++r) sees = P.masks[(size_t)mi * 128 + r] != 0;
+          if (sees) want.push_back({P.tiles[t].page, q.phys, rb, P.tiles[t].lohi, mi});
+        }
+    for (int64_t pr = 0; pr < npairs; ++pr)
+      for (int64_t i = P.kpair_off[pr]; i < P.kpair_off[pr + 1]; ++i)
+        for (int side = 0; side < 2; ++side) {
+          const uint32_t inf = ((uint32_t)P.kpsteps[i].info >> (16 * side)) & 0xffffu;
+          const int lo = (inf >> 1) & 0x7f, hi = (inf >> 8) & 0x7f;
+          if (lo == hi) continue;
+          if ((inf >> 15) & 1) return 58;  // packed steps carry no causal rule
+          got.push_back({P.kpairs[2 * pr + side], P.kpsteps[i].qph, (int)(P.kpsteps[i].info & 1), lo | (hi << 8),
+                         side ? P.kstep_mask[i].b : P.kstep_mask[i].a});
+        }
+    std::sort(want.begin(), want.end());
+    std::sort(got.begin(), got.end());
+    if (want != got) return 59;
+  }
   {
     std::vector<int> cnt(npairs, 0);
     for (int32_t pr : P.pair_order)
@@ -162,7 +235,8 @@ int main(int argc, char** argv) {
       }
       nodes[u].mount_count = (int)mounts.size() - nodes[u].mount_first;
     }
-    dag_build_opts o{64, 64, (int)rnd(2), (int)rnd(3), rnd(3) ? 1 + (int)rnd(70) : 0, (int)rnd(3)};
+    dag_build_opts o{64, 64, (int)rnd(2), (int)rnd(3), rnd(3) ? 1 + (int)rnd(70) : 0, (int)rnd(3), 0};
+    if (o.page_shuffle == 0) o.pack_pages = (int)rnd(2);
     Plan P;
     std::string err;
     const dag_status st = build_plan(nodes.data(), n, mounts.data(), (int)mounts.size(), &o, &P, &err);

@@ -182,8 +182,16 @@ def test_sixteen_tree_workload_sampled(dpa):
     dag = Dag(spec)
     leaves = dag.leaves_dfs()
     # the longest trajectory and three more spread over the trees
-    pick = sorted({leaves[0], leaves[len(leaves) // 2], leaves[-1],
-                   max(leaves, key=lambda u: len(gdn.path_ids(dag, u)))})
+    sampled = sorted({leaves[0], leaves[len(leaves) // 2], leaves[-1],
+                      max(leaves, key=lambda u: len(gdn.path_ids(dag, u)))})
+    # and the three cheapest forks whose branches are chains: every row of such a node is
+    # shared by its branches' trajectories, and its gradient is their sum (HARTS Sec. 3.4
+    # Eq. 16: the boundary state's gradient flows back from every consumer)
+    forks = _chain_forks(dag)[:3]
+    assert any(end % 64 for _, _, end in forks), "no fork off the chunk grid"
+    for u, branch_leaves, end in forks:
+        print(f"  fork node {u}: {len(branch_leaves)} branches, fork at recurrent index {end}", flush=True)
+    pick = sorted(set(sampled) | {leaf for _, bl, _ in forks for leaf in bl})
     rot = torch.as_tensor(plan.row_maps()[0], dtype=torch.long, device=DEV)
     paths = {leaf: gdn.path_ids(dag, leaf) for leaf in pick}
     rows_of = {leaf: rot[torch.as_tensor(ids, device=DEV)] for leaf, ids in paths.items()}
@@ -204,7 +212,8 @@ def test_sixteen_tree_workload_sampled(dpa):
             assert torch.equal(t[r].cpu(), want), n
     del g16
     torch.cuda.synchronize()
-    for leaf, ids in paths.items():
+    for leaf in sampled:
+        ids = paths[leaf]
         L = len(ids)
         tail = np.arange(_last_fork(dag, leaf), L)   # rows no other trajectory reaches
         sub = [x[torch.as_tensor(ids)].double().numpy() for x in ins]
@@ -216,6 +225,54 @@ def test_sixteen_tree_workload_sampled(dpa):
                 err = np.abs(got[leaf][n][tail][:, h].double().numpy() - g[n][tail][:, 0])
                 assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, \
                     f"{n} leaf {leaf} head {h}: max {err.max():.3e} mean {err.mean():.3e}"
+    # fork rows: the sum over the fork's branch trajectories, each with dO on the rows it owns
+    # (Octopus Sec. 3.4 Eq. 6), one head per fork
+    owner = dag.owner()
+    for i, (u, branch_leaves, end) in enumerate(forks):
+        h = (5 * i + 3) % H
+        ln = dag.length[u]
+        ref = {n: 0.0 for n in names}
+        o_ref = None
+        for leaf in branch_leaves:
+            ids = paths[leaf]
+            at = end - ln                            # u's rows along this trajectory: [at, end)
+            sub = [x[torch.as_tensor(ids)].double().numpy() for x in ins]
+            node = np.concatenate([np.full(dag.length[a], a) for a in dag.chain(leaf)])
+            mine = np.array([owner[a] == leaf for a in node], bool)
+            dseq = np.where(mine[:, None], sub[5][:, h], 0.0)[:, None]
+            o_seq, g = gdn.recur(np.arange(len(ids)), *sub[:5], dseq, heads=[h])
+            o_ref = o_seq[at:end, 0]
+            for n in names:
+                ref[n] = ref[n] + g[n][at:end, 0]
+            got_rows = {n: got[leaf][n][at:end, h].double().numpy() for n in names}
+            got_o_rows = got_o[leaf][at:end, h].double().numpy()
+        err = np.abs(got_o_rows - o_ref)
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, f"o fork {u} head {h}: {err.max():.3e}"
+        for n in names:
+            err = np.abs(got_rows[n] - ref[n])
+            assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, \
+                f"{n} fork {u} head {h}: max {err.max():.3e} mean {err.mean():.3e}"
+
+
+def _chain_forks(dag):
+    """(node, branch leaves, recurrent index after the node) for every node with two or more
+    children whose subtrees are chains, cheapest first (fewest trajectory tokens to replay)."""
+    out = []
+    for u in range(dag.n):
+        ch = dag.children[u]
+        if not dag.length[u] or len(ch) < 2:
+            continue
+        ends = []
+        for c in ch:
+            while len(dag.children[c]) == 1:
+                c = dag.children[c][0]
+            ends.append(c if not dag.children[c] else None)
+        if None in ends:
+            continue
+        cost = sum(len(gdn.path_ids(dag, leaf)) for leaf in ends)
+        out.append((cost, u, ends, sum(dag.length[a] for a in dag.chain(u))))
+    out.sort()
+    return [(u, ends, end) for _, u, ends, end in out]
 
 
 def _last_fork(dag, leaf):

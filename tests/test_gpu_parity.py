@@ -168,6 +168,23 @@ def test_small_bf16_mfma_path(dpa, name):
     _assert_close(got, ref, "bf16", tag=name)
 
 
+def test_forward_without_residual_and_backward_that_needs_it(dpa):
+    """The bf16 forward writes the same o and lse with or without o_lo; the bf16 backward
+    refuses to run without it (rowsum(dO * O) from bf16 O alone is off by more than the
+    tolerance where attention is peaked)."""
+    spec = _mini4()
+    plan = dpa.Plan(spec)
+    p = dpa.AttnParams(16, 4, 128, "bf16")
+    q, k, v, do = (dpa.to_rows(plan, x.to(DEV)) for x in _inputs(spec, 16, 4, 128, 17, "bf16"))
+    o1, l1, lo = dpa.attn_fwd(plan, p, q, k, v, o_lo=True)
+    o2, l2 = dpa.attn_fwd(plan, p, q, k, v)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    with pytest.raises(dpa.DagError) as e:
+        dpa.attn_bwd(plan, p, q, k, v, o1, l1, do)
+    assert e.value.code == "INVALID"
+
+
 @pytest.mark.parametrize("view", ["mount_free", "unshifted"])
 @pytest.mark.parametrize("name", ["mini3", "mini4"])
 def test_layer_group_views_on_device(dpa, name, view):
@@ -238,6 +255,91 @@ def test_peaky_logits_without_rotation(dpa):
     _assert_close(got, ref, "bf16", tag="peaky")
 
 
+def _outlier_rows(x, rng, n, lo_exp, hi_exp):
+    """x with n random token rows rescaled so that each one's largest |element| is 2^e,
+    e uniform in [lo_exp, hi_exp) (bf16-exact powers of two times bf16 values)."""
+    x = x.float().clone()
+    rows = rng.choice(x.shape[0], n, replace=False)
+    peak = x[rows].abs().amax(dim=(1, 2), keepdim=True)
+    target = torch.tensor(2.0 ** rng.uniform(lo_exp, hi_exp, n), dtype=torch.float32)[:, None, None]
+    x[rows] = x[rows] / peak * target
+    return x.bfloat16()
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "qv"])
+def test_wide_range_operands(dpa, which):
+    """bf16 inputs far outside fp16's range: outlier rows of q, k or v (or q and v) whose largest
+    element is 2^16..2^17, and dO rows scaled by 2^-u, u uniform in [0, 30].  The MFMA path's
+    fp16 operand copies carry per-tensor power-of-two scales, so every output is finite and
+    within the bf16 tolerance scaled by max(1, max|ref|) per tensor (the scaling of R13).
+
+    Outlier q or k rows run without rotation: then their fp16 copies are exact, and logits of
+    ~3e4 come out to fp32 accumulation accuracy.  With rotation the rotated row is rounded to
+    fp16 (2^-12 of its size, ~7 per element here), which puts ~4 of absolute error on such
+    logits and can flip near-tied top keys; that is the precision of a half-precision operand,
+    not its range.  Outliers in q and k together are left out: their logits reach ~1e9, where
+    the fp32 lse that the interface stores is itself only accurate to about +-32."""
+    spec = _mini3(seed=21)
+    tr = bool(spec.meta.get("transitive", True))
+    rope = 0.0 if ("q" in which or "k" in which) else 10000.0
+    print(f"wide-range operands: outliers in {which}, rope base {rope}", flush=True)
+    q, k, v, do = _inputs(spec, 16, 4, 128, 808, "bf16")
+    rng = np.random.default_rng(808)
+    if "q" in which:
+        q = _outlier_rows(q, rng, 6, 16.0, 17.0)
+    if "k" in which:
+        k = _outlier_rows(k, rng, 6, 16.0, 17.0)
+    if "v" in which:
+        v = _outlier_rows(v, rng, 6, 16.0, 17.0)
+    do = (do.float() * torch.tensor(2.0 ** -rng.uniform(0.0, 30.0, spec.n_tokens),
+                                    dtype=torch.float32)[:, None, None]).bfloat16()
+    got, _ = _run(dpa, spec, q, k, v, do, 16, 4, 128, "bf16", transitive=tr, rope=rope)
+    ref = _ref(spec, q, k, v, do, 16, 4, transitive=tr, rope=rope)
+    # A row whose softmax sits on one key has dS = P (dP - D) = 0 exactly, and the GPU's dP
+    # (summed on the matrix cores) and D (summed on the vector units) then agree only to fp32
+    # summation accuracy: a 128-term fp32 sum is typically off by about sqrt(128) 2^-24 (about
+    # 2^-20.5) of its absolute terms, and with keys of |k| ~ 1e5 that difference, times k, is
+    # visible in dq (0.038 at most here, where the exact dq is 0).  The oracle sizes those terms
+    # per element (RowSampler.row_grads term_size) and dq may carry 2^-20 of them on top.
+    rs = RowSampler(spec, OParams(16, 4, rope_base=rope), transitive=tr)
+    *_, dq_terms = rs.row_grads(np.arange(spec.n_tokens), q.double().numpy(), k.double().numpy(),
+                                v.double().numpy(), do.double().numpy(), term_size=True)
+    for n in ("o", "lse", "dq", "dk", "dv"):
+        assert np.isfinite(got[n]).all(), f"{which} {n}: non-finite"
+        bar = max(1.0, float(np.abs(ref[n]).max()))
+        err = np.abs(got[n] - ref[n])
+        if n == "dq":
+            err = np.maximum(err - 2.0 ** -20 * dq_terms, 0.0)
+        assert err.max() <= BF16_MAX * bar and err.mean() <= BF16_MEAN * bar, \
+            f"{which} {n}: max {err.max():.3g} mean {err.mean():.3g} (max|ref| {bar:.3g})"
+
+
+def _mid_commander_workers():
+    # one commander-worker episode small enough for the flat oracle: a 1,024-token
+    # commander, 8 workers of 4,096 own tokens, worker w reading at 1,536 + 256 w the
+    # last 1,024 pre-read tokens of workers w +- 1 (33,792 tokens).  A commander page is
+    # read by 8 x 4,096 worker rows (about 1,000 reader steps of 32 rows), and every
+    # mounted span's dK/dV sums its producer's own rows and two readers' post-read rows.
+    return synth.config4(n_episodes=1, commander=1024, workers=8, budget=4096, span=1024, first_read=1536,
+                         read_step=256)
+
+
+def test_mid_commander_workers_elementwise(dpa):
+    """All five tensors element by element against the flat oracle on a DAG whose KV pages
+    have long reader lists and whose mounted spans route dK/dV to their producers
+    (Octopus Sec. 3.4 Eq. 8), in fp32 gradients; bf16 gradients are the same values rounded."""
+    spec = _mid_commander_workers()
+    print("mid commander-workers: 33,792 tokens, 8/2 heads", flush=True)
+    q, k, v, do = _inputs(spec, 8, 2, 128, 4242, "bf16")
+    got, _ = _run(dpa, spec, q, k, v, do, 8, 2, 128, "bf16", grad="fp32")
+    got16, _ = _run(dpa, spec, q, k, v, do, 8, 2, 128, "bf16", grad="bf16")
+    for n in ("dq", "dk", "dv"):
+        r = torch.tensor(got[n]).float().bfloat16().double().numpy()
+        assert np.array_equal(r, got16[n]), n
+    ref = _ref(spec, q, k, v, do, 8, 2)
+    _assert_close(got, ref, "bf16", tag="mid-cw")
+
+
 def test_marker_span_mass(dpa):
     """v = 1 on one mounted span and 0 elsewhere: o equals the attention mass on that span."""
     spec = _mini4()
@@ -269,33 +371,83 @@ def test_backward_is_deterministic_and_page_order_free(dpa):
 
 
 class _TokenView:
-    """Read-only view of selected token rows of a row-layout device tensor, indexed by token id."""
+    """Read-only view of selected token rows of a row-layout device tensor, indexed by token id
+    (an int, an int array or a slice of token ids)."""
 
     def __init__(self, x_rows, rot_t, tokens):
-        self.idx = {int(t): i for i, t in enumerate(tokens)}
-        sel = torch.as_tensor(np.asarray(tokens, np.int64), device=x_rows.device)
+        tokens = np.asarray(sorted(set(int(t) for t in tokens)), np.int64)
+        self.pos = np.full(int(tokens.max()) + 1 if len(tokens) else 1, -1, np.int64)
+        self.pos[tokens] = np.arange(len(tokens))
+        sel = torch.as_tensor(tokens, device=x_rows.device)
         self.data = x_rows[rot_t[sel]].double().cpu().numpy()
+
+    def _idx(self, ids):
+        i = self.pos[ids]
+        assert (i >= 0).all(), "token row not fetched"
+        return i
 
     def __getitem__(self, key):
         if isinstance(key, tuple):
-            return self.data[self.idx[int(key[0])]][key[1:]]
+            return self.data[self._idx(int(key[0]))][key[1:]]
         if isinstance(key, slice):
-            return self.data[[self.idx[t] for t in range(key.start, key.stop)]]
-        return self.data[self.idx[int(key)]]
+            return self.data[self._idx(np.arange(key.start, key.stop))]
+        if isinstance(key, np.ndarray):
+            return self.data[self._idx(key.astype(np.int64))]
+        return self.data[self._idx(int(key))]
 
 
-def _full_case(dpa, spec, seed, bwd, n_rows=24, n_keys=6, max_readers=96, view="mounted"):
-    tr = bool(spec.meta.get("transitive", True))
+def _n_reader_rows(rs, dag, j):
+    """Query rows whose visible set holds key token j (its own node's rows from j on, and
+    every row of each other reader node)."""
+    u, jo = int(rs.node_of[j]), int(rs.off[j])
+    return sum(dag.length[w] for w in rs.reader_nodes(j) if w != u) + dag.length[u] - jo
+
+
+def _heavy_keys(rs, dag, rng, hi, n_cand=150):
+    """Two keys whose dK/dV sums over many readers, each the most-read of a random sample
+    of candidates with at most ``hi`` reader rows: one in an inner node whose children are
+    all leaves (its later own rows and every child read it), one inside a directly mounted
+    span (its producer's later rows and descendants plus the reader's subtree read it)."""
+    out = []
+    inner = [u for u in range(dag.n)
+             if dag.length[u] and dag.children[u] and all(not dag.children[c] for c in dag.children[u])]
+    spans = [(s, b, e) for r in range(dag.n) for (s, b, e) in dag.nonempty_direct(r)]
+    for kind, pool in (("inner", inner), ("mounted", spans)):
+        best = None
+        for i in rng.permutation(len(pool))[:n_cand]:
+            if kind == "inner":
+                u = pool[i]
+                j = dag.offset[u] + int(rng.integers(0, dag.length[u]))
+            else:
+                s_, b_, e_ = pool[i]
+                j = dag.offset[s_] + int(rng.integers(b_, e_))
+            n = _n_reader_rows(rs, dag, j)
+            if n <= hi and (best is None or n > best[0]):
+                best = (n, j)
+        if best is not None:
+            out.append((kind, best[1], best[0]))
+    return out
+
+
+def _full_case(dpa, spec, seed, bwd, n_rows=24, n_keys=6, max_readers=96, view="mounted", heavy_hi=16000,
+               transitive=None):
+    """The workload at full size, in the benchmark's launch configuration (bf16 tensors and
+    gradients).  Compared with the oracle: o, lse and dq on sampled query rows (random tokens
+    plus the first and last token of a few nodes), and dK/dV on sampled keys -- a few
+    lightly read leaf-tail keys (all four KV heads) and, unless ``heavy_hi`` is 0, two
+    heavily read keys (an inner node's and a mounted span's, one KV head each) whose
+    gradient sums up to ``heavy_hi`` reader rows."""
+    tr = bool(spec.meta.get("transitive", True)) if transitive is None else transitive
     plan = dpa.Plan(spec, transitive=tr, view=view)
     p = dpa.AttnParams(16, 4, 128, "bf16")          # the benchmark's configuration (bf16 gradients)
     C = plan.rows
     q = synth.normal((C, 16, 128), seed, 1, DEV, torch.bfloat16)
     k = synth.normal((C, 4, 128), seed, 2, DEV, torch.bfloat16)
     v = synth.normal((C, 4, 128), seed, 3, DEV, torch.bfloat16)
+    do = synth.normal((C, 16, 128), seed, 4, DEV, torch.bfloat16)
     o, lse, o_lo = dpa.attn_fwd(plan, p, q, k, v, o_lo=True)
     res = {"o": o, "lse": lse}
     if bwd:
-        do = synth.normal((C, 16, 128), seed, 4, DEV, torch.bfloat16)
         res["dq"], res["dk"], res["dv"] = dpa.attn_bwd(plan, p, q, k, v, o, lse, do, o_lo=o_lo)
     torch.cuda.synchronize()
     for n, t in res.items():
@@ -306,39 +458,47 @@ def _full_case(dpa, spec, seed, bwd, n_rows=24, n_keys=6, max_readers=96, view="
     kh = k[rot_t].float().cpu().numpy()
     vh = v[rot_t].float().cpu().numpy()
     rng = np.random.default_rng(seed)
-    # rows: random tokens plus the first and last token of a few nodes (page edges, readers)
     picks = list(rng.choice(dag.n_tokens, n_rows, replace=False))
     for u in rng.choice(dag.n, 6, replace=False):
         if dag.length[u]:
             picks += [dag.offset[u], dag.offset[u] + dag.length[u] - 1]
     picks = np.array(sorted(set(int(x) for x in picks)))
     rs = RowSampler(spec, OParams(16, 4), transitive=tr, view=view)
-    o_ref, l_ref = rs.rows(picks, _TokenView(q, rot_t, picks), kh, vh)
-    _assert_close({"o": res["o"][rot_t[picks]].double().cpu().numpy(),
-                   "lse": res["lse"][rot_t[picks]].double().cpu().numpy()},
-                  {"o": o_ref, "lse": l_ref}, "bf16", names=("o", "lse"), tag="sampled rows")
-    if bwd:
-        # keys with few readers: tail tokens of leaf nodes that no read reaches
-        cands = []
-        for u in dag.leaves_dfs():
-            for j in range(max(0, dag.length[u] - 6), dag.length[u]):
-                cands.append(dag.offset[u] + j)
-        rng.shuffle(cands)
-        keys, readers = [], set()
-        for j in cands:
-            r = rs.readers(j)
-            if len(r) <= max_readers:
-                keys.append(j)
-                readers.update(int(t) for t in r)
-            if len(keys) == n_keys:
-                break
-        assert keys, "no lightly-read key found"
-        keys = np.array(sorted(keys))
-        need = np.array(sorted(readers))
-        dk_ref, dv_ref = rs.key_grads(keys, _TokenView(q, rot_t, need), kh, vh, _TokenView(do, rot_t, need))
-        _assert_close({"dk": res["dk"][rot_t[keys]].double().cpu().numpy(),
-                       "dv": res["dv"][rot_t[keys]].double().cpu().numpy()},
-                      {"dk": dk_ref, "dv": dv_ref}, "bf16", names=("dk", "dv"), tag="sampled keys")
+    got = lambda name, toks: res[name][rot_t[torch.as_tensor(toks, device=DEV)]].double().cpu().numpy()
+    if not bwd:
+        o_ref, l_ref = rs.rows(picks, _TokenView(q, rot_t, picks), kh, vh)
+        _assert_close({"o": got("o", picks), "lse": got("lse", picks)}, {"o": o_ref, "lse": l_ref}, "bf16",
+                      names=("o", "lse"), tag="sampled rows")
+        return plan, res
+    o_ref, l_ref, dq_ref = rs.row_grads(picks, _TokenView(q, rot_t, picks), kh, vh, _TokenView(do, rot_t, picks))
+    _assert_close({"o": got("o", picks), "lse": got("lse", picks), "dq": got("dq", picks)},
+                  {"o": o_ref, "lse": l_ref, "dq": dq_ref}, "bf16", names=("o", "lse", "dq"), tag="sampled rows")
+    # keys with few readers: tail tokens of leaf nodes that no read reaches
+    cands = []
+    for u in dag.leaves_dfs():
+        for j in range(max(0, dag.length[u] - 6), dag.length[u]):
+            cands.append(dag.offset[u] + j)
+    rng.shuffle(cands)
+    keys = []
+    for j in cands:
+        if _n_reader_rows(rs, dag, j) <= max_readers:
+            keys.append(j)
+        if len(keys) == n_keys:
+            break
+    assert keys, "no lightly-read key found"
+    sets = [("light", sorted(keys), None)]
+    if heavy_hi:
+        for i, (kind, j, n) in enumerate(_heavy_keys(rs, dag, rng, heavy_hi)):
+            print(f"  heavy key ({kind}): token {j}, {n} reader rows", flush=True)
+            sets.append((kind, [j], [i % 4]))
+    for kind, ks, groups in sets:
+        need = np.unique(np.concatenate([rs.readers(j) for j in ks]))
+        dk_ref, dv_ref = rs.key_grads_by_node(ks, _TokenView(q, rot_t, need), kh, vh, _TokenView(do, rot_t, need),
+                                              groups=groups)
+        sel = slice(None) if groups is None else groups
+        _assert_close({"dk": got("dk", ks)[:, sel], "dv": got("dv", ks)[:, sel]},
+                      {"dk": dk_ref[:, sel], "dv": dv_ref[:, sel]}, "bf16", names=("dk", "dv"),
+                      tag=f"sampled keys ({kind})")
     return plan, res
 
 
@@ -350,10 +510,17 @@ def test_full_size_views_sampled(dpa, view):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("which", ["w2", "w4", "w3", "short"])
+@pytest.mark.parametrize("which", ["w2", "w4", "w3", "w3t", "short"])
 def test_full_size_sampled(dpa, which):
-    spec = {"w2": synth.config2, "w4": synth.config4, "w3": synth.config3,
+    # w3t: the 16-tree workload with transitive reads (Octopus Sec. 3.3 item 1), the
+    # benchmark's "transitive" record
+    spec = {"w2": synth.config2, "w4": synth.config4, "w3": synth.config3, "w3t": synth.config3,
             "short": synth.dags.config3_short_segments}[which]()
-    seed = {"w2": 1002, "w4": 1004, "w3": 1003, "short": 1013}[which]
-    _full_case(dpa, spec, seed=seed, bwd=(which != "w2"))
+    seed = {"w2": 1002, "w4": 1004, "w3": 1003, "w3t": 1023, "short": 1013}[which]
+    print(f"full size: {which}", flush=True)
+    # the commander-worker episodes' inner keys have 30K-260K reader rows each, beyond what the
+    # oracle evaluates in seconds; their reductions are compared element by element on the
+    # mid-size episode instead
+    _full_case(dpa, spec, seed=seed, bwd=(which != "w2"), heavy_hi=0 if which == "w4" else 16000,
+               transitive=True if which == "w3t" else None)
     torch.cuda.empty_cache()

@@ -55,3 +55,19 @@ def test_microbatch_plan_rejects_malformed_requests(args, kw):
 def test_microbatch_plan_accepts_a_plain_request():
     assert _mb(1, 0, 10) == 0
     assert _mb(2, 0, 10) == 0
+
+
+def test_bf16_backward_refuses_a_missing_residual():
+    # decided on the host before any device call: the pointers are never dereferenced
+    import synth
+    plan = dpa.Plan(synth.config1())
+    cp = dpa.AttnParams(16, 4, 128, "bf16").c()
+    fake = ctypes.c_void_p(0x1000)
+    ws = ctypes.c_void_p(0x2000)
+    st = L.dag_attn_bwd(plan._h, ctypes.byref(cp), fake, fake, fake, fake, fake, None, fake, fake, fake, fake, ws,
+                        1 << 40, None)
+    assert st == 1 and "o_lo" in L.dag_last_error().decode()
+    cp32 = dpa.AttnParams(2, 2, 64, "fp32").c()
+    st = L.dag_attn_bwd(plan._h, ctypes.byref(cp32), fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, ws,
+                        1 << 40, None)
+    assert st == 1 and "o_lo" in L.dag_last_error().decode()

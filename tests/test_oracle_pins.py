@@ -321,6 +321,9 @@ def test_row_grads_match_flat_and_brute(seed, transitive):
     ro, rl, rdq = rs.row_grads(toks, q, k, v, do)
     for got, a, b in ((ro, o, bo), (rl, lse, bl), (rdq, dq, bdq)):
         assert np.abs(got - a).max() < 1e-11 and np.abs(got - b).max() < 1e-11
+    # the term-size bound: |dq| never exceeds the summed size of its terms
+    *_, size = rs.row_grads(toks, q, k, v, do, term_size=True)
+    assert (np.abs(rdq) <= size + 1e-12).all()
 
 
 @pytest.mark.parametrize("seed", [4, 9, 21])

@@ -48,6 +48,10 @@ def _compare(spec, transitive=True, shuffle=0, view="mounted"):
     assert info["visible_pairs"] == dag.visible_pairs()
     assert info["flat_rows"] == dag.flat_rows()
     assert info["n_trajectories"] == len(dag.leaves_dfs())
+    # HARTS Sec. 3.5: per-token multiplicity and S = its sum (own tokens of the flat batch)
+    mult = dag.multiplicity()
+    assert np.array_equal(plan.multiplicity(), mult)
+    assert info["semantic_tokens"] == int(mult.sum())
     assert info["rows"] % 64 == 0 and info["rows"] >= dag.n_tokens
     rot, por = plan.row_maps()
     pos = dag.token_positions()
@@ -179,11 +183,12 @@ def test_host_compactor_under_sanitizers(tmp_path):
     """Build plan.cpp with a small driver under ASan/UBSan (g++, host only) and run it."""
     exe = tmp_path / "plan_san"
     src = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "plan.cpp")
+    psrc = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "pack_plan.cpp")
     gsrc = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "gdn_plan.cpp")
     csrc = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "conv_plan.cpp")
     drv = os.path.join(ROOT, "tests", "host", "plan_driver.cpp")
     cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
-           f"-I{os.path.join(ROOT, 'include')}", src, gsrc, csrc, drv, "-o", str(exe)]
+           f"-I{os.path.join(ROOT, 'include')}", src, psrc, gsrc, csrc, drv, "-o", str(exe)]
     subprocess.run(cmd, check=True, capture_output=True)
     r = subprocess.run([str(exe), "300"], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
@@ -213,3 +218,69 @@ def test_positions_and_rows_beyond_int32_are_rejected():
     with pytest.raises(dpa.DagError) as e:
         dpa.Plan(b.build())
     assert e.value.code == "OVERFLOW"
+
+
+def _decode_matches_oracle(spec, transitive, view="mounted", pack=False):
+    """Every query row's visible rows and every key row's reader rows, decoded from the plan's
+    kernel tables (tile ranges, masks, causal rule; dK/dV reader steps), equal Octopus Eq. 4's
+    visible sets from the oracle, mapped to rows."""
+    from oracle.attention import AttnParams, RowSampler
+    plan = dpa.Plan(spec, transitive=transitive, view=view, pack=pack)
+    rs = RowSampler(spec, AttnParams(1, 1), transitive=transitive, view=view)
+    rot, _ = plan.row_maps()
+    dag = rs.g
+    node_of, off = dag.token_node()
+    for t in range(dag.n_tokens):
+        want = np.sort(rot[dag.visible_tokens(int(node_of[t]), int(off[t]))])
+        assert np.array_equal(plan.visibility(int(rot[t])), want), ("visibility", t)
+        assert np.array_equal(plan.readers(int(rot[t])), np.sort(rot[rs.readers(t)])), ("readers", t)
+    pad = np.setdiff1d(np.arange(plan.rows), rot)
+    for r in pad[:50]:
+        assert len(plan.visibility(int(r))) == 0 and len(plan.readers(int(r))) == 0
+    return plan
+
+
+@pytest.mark.parametrize("pack", [False, True])
+@pytest.mark.parametrize("seed", range(16))
+def test_kernel_tables_decode_to_visible_sets(seed, pack):
+    rng = np.random.default_rng(5000 + seed)
+    spec = synth.random_tiny_dag(rng, n_nodes=int(rng.integers(2, 16)), max_len=int(rng.integers(1, 90)),
+                                 p_mount=0.7, max_mounts=3, n_roots=int(rng.integers(1, 3)))
+    for transitive in (True, False):
+        for view in ("mounted", "mount_free", "unshifted"):
+            _decode_matches_oracle(spec, transitive, view, pack)
+
+
+@pytest.mark.parametrize("pack", [False, True])
+def test_kernel_tables_decode_on_short_segment_trees(pack):
+    # the page-gather diagnostic's shape in small (segments of 1-64 tokens, most pages shared
+    # when packed) and a mini commander-worker episode
+    spec = synth.dags.config3_structure(7, n_trees=2, seg=(1, 64), depth_hi=3, fan=(2, 4))
+    plan = _decode_matches_oracle(spec, bool(spec.meta.get("transitive", True)), pack=pack)
+    if pack:
+        assert plan.info["pack_pages"] == 1
+        assert plan.rows < 0.5 * dpa.Plan(spec).rows          # most padding gone
+    spec = synth.config4(n_episodes=1, commander=150, workers=4, budget=520, span=100, first_read=200,
+                         read_step=70)
+    _decode_matches_oracle(spec, True, pack=pack)
+
+
+def test_packed_layout_keeps_rows_and_padding_rules():
+    """Packed: every node's rows contiguous, every page's valid rows a prefix, padding only at
+    the ends of pages that a longer node could not join; positions and multiplicities as
+    unpacked."""
+    spec = synth.dags.config3_structure(7, n_trees=2, seg=(1, 64), depth_hi=3, fan=(2, 4))
+    a, b = dpa.Plan(spec), dpa.Plan(spec, pack=True)
+    ra, pa = a.row_maps()
+    rb, pb = b.row_maps()
+    assert np.array_equal(pa[ra], pb[rb])                     # same position per token
+    assert np.array_equal(a.multiplicity(), b.multiplicity())
+    dag = Dag(spec, transitive=bool(spec.meta.get("transitive", True)))
+    for u in range(dag.n):
+        rows = rb[dag.offset[u]: dag.offset[u] + dag.length[u]]
+        assert np.array_equal(rows, rows[0] + np.arange(len(rows))) if len(rows) else True
+    valid = (pb >= 0).reshape(-1, 64)
+    for pg in valid:                                          # a prefix of each page
+        k = int(pg.sum())
+        assert pg[:k].all() and not pg[k:].any()
+    assert b.info["visible_pairs"] == a.info["visible_pairs"]
