@@ -129,6 +129,7 @@ def _load() -> ctypes.CDLL:
                                 ctypes.POINTER(SZ)], I32),
         "dag_attn_fwd": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, P, SZ, P], I32),
         "dag_attn_bwd": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "dag_attn_fwd_noalloc": ([P, ctypes.POINTER(DagAttnParams), P, P, P, P, P, P, P], I32),
         "dag_gdn_workspace": ([P, ctypes.POINTER(DagGdnParams), ctypes.POINTER(SZ), ctypes.POINTER(SZ)], I32),
         "dag_gdn_fwd": ([P, ctypes.POINTER(DagGdnParams), P, P, P, P, P, P, P, SZ, P], I32),
         "dag_gdn_bwd": ([P, ctypes.POINTER(DagGdnParams), P, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
@@ -378,6 +379,22 @@ def attn_fwd(plan: Plan, p: AttnParams, q, k, v, o=None, lse=None, ws=None, stre
     _check(_lib.dag_attn_fwd(plan._h, ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), lo_ptr,
                              _ptr(ws), ws.numel(), _stream_ptr(stream)))
     return (o, lse, o_lo) if want_lo else (o, lse)
+
+
+def attn_fwd_noalloc(plan: Plan, p: AttnParams, q, k, v, o, lse, o_lo=None, stream=None):
+    """``dag_attn_fwd_noalloc``: the forward into caller-allocated ``o`` / ``lse`` (and ``o_lo``
+    for bf16, or None) with the library's static device workspace; the plan must be uploaded."""
+    C, dt, dev = plan.rows, p.torch_dtype, q.device
+    _check_tensor("q", q, C, p.n_q_heads, p.head_dim, dt, dev)
+    _check_tensor("k", k, C, p.n_kv_heads, p.head_dim, dt, dev)
+    _check_tensor("v", v, C, p.n_kv_heads, p.head_dim, dt, dev)
+    _check_tensor("o", o, C, p.n_q_heads, p.head_dim, dt, dev)
+    if o_lo is not None:
+        _check_tensor("o_lo", o_lo, C, p.n_q_heads, p.head_dim, dt, dev)
+    cp = p.c()
+    _check(_lib.dag_attn_fwd_noalloc(plan._h, ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                                     _ptr(o_lo) if o_lo is not None else None, _stream_ptr(stream)))
+    return o, lse
 
 
 def attn_bwd(plan: Plan, p: AttnParams, q, k, v, o, lse, dO, dq=None, dk=None, dv=None, ws=None,
@@ -712,7 +729,7 @@ def from_rows(plan: Plan, x_rows):
     return x_rows[torch.as_tensor(rot, dtype=torch.long, device=x_rows.device)]
 
 
-__all__ = ["Plan", "AttnParams", "GdnParams", "DagError", "attn_fwd", "attn_bwd", "workspace_bytes", "gdn_fwd",
+__all__ = ["Plan", "AttnParams", "GdnParams", "DagError", "attn_fwd", "attn_fwd_noalloc", "attn_bwd", "workspace_bytes", "gdn_fwd",
            "gdn_bwd", "gdn_workspace_bytes", "ConvParams", "conv_fwd", "conv_bwd", "conv_workspace_bytes",
            "logprob_fwd", "logprob_bwd", "trie_build", "microbatch_plan", "to_rows", "from_rows", "last_error",
            "LIB_PATH"]

@@ -35,7 +35,7 @@ def _run(cmd):
 
 
 OBJS = ("plan.o", "pack_plan.o", "gdn_plan.o", "logprob_map.o", "conv_plan.o", "harts_plan.o", "abi.o", "kernels.o", "gdn.o", "logprob.o",
-        "conv.o")
+        "conv.o", "noalloc.o")
 
 
 def build(verbose: bool = False) -> str:
@@ -54,6 +54,7 @@ def build(verbose: bool = False) -> str:
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "abi.cpp"), "-o", os.path.join(obj_dir, "abi.o")],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "kernels.hip"), "-o", os.path.join(obj_dir, "kernels.o")],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "gdn.hip"), "-o", os.path.join(obj_dir, "gdn.o")],
+        [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "noalloc.hip"), "-o", os.path.join(obj_dir, "noalloc.o")],
     ]
     with ThreadPoolExecutor(len(steps)) as ex:
         for r in ex.map(_run, steps):

@@ -239,6 +239,19 @@ dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q,
                         const void* v, void* o, float* lse, void* o_lo, void* ws, size_t ws_bytes,
                         void* hip_stream);
 
+/* dag_attn_fwd without allocation, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Same arguments and results as dag_attn_fwd, minus the workspace: it runs in a static
+ * 64 MiB device array that the library holds on every device it runs on until the
+ * process ends (forward workspace: about 6.6 KB per compact row at Hq = 16, Hkv = 4,
+ * D = 128, i.e. plans up to roughly 10,000 rows).  A plan needing more returns
+ * DAG_E_WORKSPACE.  The plan must already be on the current device (dag_plan_upload,
+ * which allocates); otherwise DAG_E_INVALID.  Calls on one device share the array:
+ * calls that overlap on one device (other streams or threads) race; calls in order on
+ * one stream do not. */
+dag_status dag_attn_fwd_noalloc(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k,
+                                const void* v, void* o, float* lse, void* o_lo, void* hip_stream);
+
 /* Backward of dag_attn_fwd given the upstream gradient dO [C, Hq, D] (dtype):
  * dq [C, Hq, D]; dk, dv [C, Hkv, D] (grad_dtype), where every key row's gradient is the sum
  * over all readers (own branch, descendants, mount readers) taken in a fixed
