@@ -351,17 +351,18 @@ def attn_alg_bytes(C: int) -> dict:
             "dq": C * (2 * HQ + 3 * HKV) * D * 2 + C * HQ * 8 + C * HQ * D * 2}
 
 
-def gather_time(dpa, dev, steps, warmup):
+def gather_time(dpa, dev, steps, warmup, pack=False):
     """Page-gather diagnostic: the 16-tree topology with segments of 1-64 tokens.  Pages
     hold few tokens and query blocks few rows, so every K/V or Q/dO tile a work-group
     stages feeds few products and the attention kernels stream tiles from HBM.  Per
     kernel: ms per launch, counted TFLOP/s, and GB/s on the algorithmic bytes and (when
     the committed counter summary was taken on the current source) on the measured HBM
-    bytes, both against 8 TB/s."""
+    bytes, both against 8 TB/s.  ``pack``: the packed page layout (nodes share pages,
+    per-tile masks), whose algorithmic bytes are those of its own, fewer rows."""
     import torch
     import synth
     spec = synth.dags.config3_short_segments()
-    plan = dpa.Plan(spec)
+    plan = dpa.Plan(spec, pack=pack)
     info = plan.info
     p = dpa.AttnParams(HQ, HKV, D, "bf16")
     tensors, ws = alloc(dpa, plan, p, 1013, dev)
@@ -379,7 +380,8 @@ def gather_time(dpa, dev, steps, warmup):
     f_fwd = 4.0 * D * HQ * P
     flops = {"fwd": f_fwd, "dkdv": 2.0 * f_fwd, "dq": 0.5 * f_fwd}
     alg = attn_alg_bytes(C)
-    traffic = step_traffic_record("hbm_traffic_gather.json", "kernels.hip", "kernels_hip_sha256_16")
+    traffic = step_traffic_record("hbm_traffic_gather_packed.json" if pack else "hbm_traffic_gather.json",
+                                  "kernels.hip", "kernels_hip_sha256_16")
     kern = {}
     for k in ("fwd", "dkdv", "dq"):
         ms = kt[k][0] / max(kt[k][1], 1)
@@ -398,7 +400,9 @@ def gather_time(dpa, dev, steps, warmup):
     del tensors, ws
     torch.cuda.empty_cache()
     return {"workload": "16-tree topology (seed %d) with segments of 1-64 tokens" % int(spec.meta["seed"]),
+            "layout": "packed pages (per-tile masks)" if pack else "one node per page",
             "unique_tokens": info["tokens"], "rows": C, "pages": info["pages"], "visible_pairs": P,
+            "padding_rows_frac": round(1.0 - info["tokens"] / C, 4),
             "ms_per_step": round(dt * 1e3, 3), "tflops": round(3.5 * f_fwd / dt / 1e12, 2),
             "hbm_peak_gbps": HBM_PEAK_GBPS, "kernels": kern}
 
@@ -607,6 +611,7 @@ def main() -> int:
     ap.add_argument("--no-gather", action="store_true")
     ap.add_argument("--gather-only", action="store_true",
                     help="only time the page-gather diagnostic (for profiling); prints its record")
+    ap.add_argument("--pack", action="store_true", help="with --gather-only: the packed page layout")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB -> 1 GiB device copy kernel 3 times (scales HBM counters)")
     args = ap.parse_args()
@@ -632,7 +637,7 @@ def main() -> int:
                                                "launches": 3}}))
         return 0
     if args.gather_only:
-        print(json.dumps({"gather": gather_time(dpa, dev, args.steps, args.warmup)}), flush=True)
+        print(json.dumps({"gather": gather_time(dpa, dev, args.steps, args.warmup, pack=args.pack)}), flush=True)
         return 0
     t0 = time.perf_counter()
     spec = synth.config3()
@@ -728,11 +733,12 @@ def main() -> int:
         log(f"logprob: fwd {lp['fwd_ms']:.3f} ms ({lp['roofline']['fwd']['achieved']:.0f} GB/s), "
             f"bwd {lp['bwd_ms']:.3f} ms ({lp['roofline']['bwd']['achieved']:.0f} GB/s)")
     if not args.no_gather:
-        ga = gather_time(dpa, dev, max(1, min(args.steps, 5)), 1)
-        out["gather"] = ga
-        log("gather diagnostic: " + ", ".join(f"{k} {v['ms']} ms" + (f" ({v['alg_gbps']:.0f} GB/s alg)"
-                                                                    if "alg_gbps" in v else "")
-                                              for k, v in ga["kernels"].items()))
+        for pack, key in ((False, "gather"), (True, "gather_packed")):
+            ga = gather_time(dpa, dev, max(1, min(args.steps, 5)), 1, pack=pack)
+            out[key] = ga
+            log(f"{key} diagnostic: " + ", ".join(f"{k} {v['ms']} ms" + (f" ({v['alg_gbps']:.0f} GB/s alg)"
+                                                                        if "alg_gbps" in v else "")
+                                                  for k, v in ga["kernels"].items()))
     if not args.no_flat:
         t_flat, fpairs, frows, ntraj = flat_time(dpa, spec, plan, p, dev, args.flat_steps)
         out["x_vs_flat"] = round(t_flat / dt, 3)

@@ -35,6 +35,9 @@ struct DeviceTables {
   int64_t* kpair_off = nullptr;
   KStep* kpsteps = nullptr;
   int32_t* pair_order = nullptr;
+  int32_t* tile_mask = nullptr;   // packed plans only
+  uint64_t* masks = nullptr;
+  KMask* kstep_mask = nullptr;
   int32_t* page_table = nullptr;
   int32_t* page_nrows = nullptr;
   // linear-attention schedule
@@ -199,6 +202,8 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
            align256(P.kentries.size() * sizeof(KEntry)) + align256(P.kv_off.size() * 4) +
            align256(P.bwd_order.size() * 4) + align256(P.kpairs.size() * 4) + align256(P.kpair_off.size() * 8) +
            align256(P.kpsteps.size() * sizeof(KStep)) + align256(P.pair_order.size() * 4) +
+           align256(P.tile_mask.size() * 4) + align256(P.masks.size() * 8) +
+           align256(P.kstep_mask.size() * sizeof(KMask)) +
            align256(P.page_table.size() * 4) +
            align256(P.page_nrows.size() * 4) + align256(P.gseqs.size() * sizeof(GSeq)) +
            align256(P.grows.size() * 4) + align256(P.gexports.size() * sizeof(GExport)) +
@@ -227,6 +232,9 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
   D->kpair_off = dev_take<int64_t>(b, off, P.kpair_off.size());
   D->kpsteps = dev_take<KStep>(b, off, P.kpsteps.size());
   D->pair_order = dev_take<int32_t>(b, off, P.pair_order.size());
+  D->tile_mask = P.packed ? dev_take<int32_t>(b, off, P.tile_mask.size()) : nullptr;
+  D->masks = P.packed ? dev_take<uint64_t>(b, off, P.masks.size()) : nullptr;
+  D->kstep_mask = P.packed ? dev_take<KMask>(b, off, P.kstep_mask.size()) : nullptr;
   D->page_table = dev_take<int32_t>(b, off, P.page_table.size());
   D->page_nrows = dev_take<int32_t>(b, off, P.page_nrows.size());
   D->gseqs = dev_take<GSeq>(b, off, P.gseqs.size());
@@ -256,6 +264,9 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
             put(D->kpair_off, P.kpair_off.data(), P.kpair_off.size() * 8) &&
             put(D->kpsteps, P.kpsteps.data(), P.kpsteps.size() * sizeof(KStep)) &&
             put(D->pair_order, P.pair_order.data(), P.pair_order.size() * 4) &&
+            (!P.packed || (put(D->tile_mask, P.tile_mask.data(), P.tile_mask.size() * 4) &&
+                           put(D->masks, P.masks.data(), P.masks.size() * 8) &&
+                           put(D->kstep_mask, P.kstep_mask.data(), P.kstep_mask.size() * sizeof(KMask)))) &&
             put(D->page_table, P.page_table.data(), P.page_table.size() * 4) &&
             put(D->page_nrows, P.page_nrows.data(), P.page_nrows.size() * 4) &&
             put(D->gseqs, P.gseqs.data(), P.gseqs.size() * sizeof(GSeq)) &&
@@ -381,7 +392,8 @@ dag_status dagattn::attn_fwd_impl(dag_plan* plan, const dag_attn_params* p, cons
   if (o_lo && p->dtype != DAG_DTYPE_BF16) return set_err(DAG_E_INVALID, "o_lo is for bf16 tensors only");
   const LaunchShape s = shape_of(P, p);
   const bool mfma = mfma_path(p);
-  if (P.packed) return set_err(DAG_E_UNSUPPORTED, "packed page layouts are not supported by the attention kernels");
+  if (P.packed && !mfma)
+    return set_err(DAG_E_UNSUPPORTED, "packed page layouts run on the MFMA path only (bf16, head_dim 128, Hq = 4 Hkv)");
   FwdWs w;
   const size_t need = carve_fwd(s, mfma, nullptr, &w);
   if (!ws || ws_bytes < need)
@@ -406,26 +418,27 @@ dag_status dagattn::attn_fwd_impl(dag_plan* plan, const dag_attn_params* p, cons
     const int32_t* nr = D.page_nrows;
     if (mfma) {
       // each fp16 copy is scaled by the power of two that maps its tensor's maximum into
-      // [1, 2), so no finite bf16 input overflows fp16; the kernels undo the scales exactly
+      // [2^14, 2^15) (q, k) or [1, 2) (v), so no finite bf16 input overflows fp16; the
+      // kernels undo the scales exactly
       const bf16_t *q16 = (const bf16_t*)q, *k16 = (const bf16_t*)k, *v16 = (const bf16_t*)v;
       launch_zero_u32(w.amax, 3, stream);
       launch_absmax(s, q16, k16, v16, nullptr, nr, w.amax, stream);
-      launch_prep16(s, q16, w.cs, nr, w.amax + 0, (f16_t*)w.qn, nullptr, s.Hq, stream);
-      launch_prep16(s, k16, w.cs, nr, w.amax + 1, (f16_t*)w.kn, nullptr, s.Hkv, stream);
-      launch_prep16(s, v16, nullptr, nr, w.amax + 2, nullptr, (f16_t*)w.vt, s.Hkv, stream);
+      launch_prep16(s, q16, w.cs, nr, w.amax + 0, true, (f16_t*)w.qn, nullptr, s.Hq, stream);
+      launch_prep16(s, k16, w.cs, nr, w.amax + 1, true, (f16_t*)w.kn, nullptr, s.Hkv, stream);
+      launch_prep16(s, v16, nullptr, nr, w.amax + 2, false, nullptr, (f16_t*)w.vt, s.Hkv, stream);
     } else if (p->dtype == DAG_DTYPE_BF16) {
-      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, nr, nullptr, (float*)w.qn, nullptr, s.Hq, stream);
-      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, nr, nullptr, (float*)w.kn, nullptr, s.Hkv, stream);
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, nr, (float*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, nr, (float*)w.kn, nullptr, s.Hkv, stream);
     } else {
-      launch_relayout<float, float>(s, (const float*)q, w.cs, nr, nullptr, (float*)w.qn, nullptr, s.Hq, stream);
-      launch_relayout<float, float>(s, (const float*)k, w.cs, nr, nullptr, (float*)w.kn, nullptr, s.Hkv, stream);
+      launch_relayout<float, float>(s, (const float*)q, w.cs, nr, (float*)w.qn, nullptr, s.Hq, stream);
+      launch_relayout<float, float>(s, (const float*)k, w.cs, nr, (float*)w.kn, nullptr, s.Hkv, stream);
     }
   }
   {
     Span sp(P, DAG_K_FWD, stream);
     if (mfma)
       launch_fwd_mfma(s, n_qp, (const f16_t*)w.qn, (const f16_t*)w.kn, (const f16_t*)w.vt, D.qpages, D.fwd_order,
-                      D.tiles, (bf16_t*)o, lse, (bf16_t*)o_lo, w.amax, stream);
+                      D.tiles, D.tile_mask, D.masks, (bf16_t*)o, lse, (bf16_t*)o_lo, w.amax, stream);
     else if (p->dtype == DAG_DTYPE_BF16)
       launch_fwd_simple<bf16_t>(s, n_qp, (const float*)w.qn, (const float*)w.kn, (const bf16_t*)v, D.qpages,
                                 D.fwd_order, D.tiles, (bf16_t*)o, lse, (bf16_t*)o_lo, stream);
@@ -674,7 +687,8 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
     return set_err(DAG_E_INVALID, "the bf16 backward needs o_lo, the forward's rounding residual of o");
   const LaunchShape s = shape_of(P, p);
   const bool mfma = mfma_path(p);
-  if (P.packed) return set_err(DAG_E_UNSUPPORTED, "packed page layouts are not supported by the attention kernels");
+  if (P.packed && !mfma)
+    return set_err(DAG_E_UNSUPPORTED, "packed page layouts run on the MFMA path only (bf16, head_dim 128, Hq = 4 Hkv)");
   BwdWs w;
   const size_t need = carve_bwd(s, mfma, nullptr, &w);
   if (!ws || ws_bytes < need)
@@ -696,10 +710,10 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       launch_zero_u32(w.amax, 4, stream);
       launch_absmax(s, q16, k16, v16, d16, nr, w.amax, stream);
       launch_rowdot16(s, o16, (const bf16_t*)o_lo, d16, lse, nr, w.ld, w.amax, stream);
-      launch_prep16(s, q16, w.cs, nr, w.amax + 0, (f16_t*)w.qn, nullptr, s.Hq, stream);
-      launch_prep16(s, k16, w.cs, nr, w.amax + 1, (f16_t*)w.kn, (f16_t*)w.kt, s.Hkv, stream);
-      launch_prep16(s, v16, nullptr, nr, w.amax + 2, (f16_t*)w.vn, nullptr, s.Hkv, stream);
-      launch_prep16(s, d16, nullptr, nr, w.amax + 3, (f16_t*)w.dOn, nullptr, s.Hq, stream);
+      launch_prep16(s, q16, w.cs, nr, w.amax + 0, true, (f16_t*)w.qn, nullptr, s.Hq, stream);
+      launch_prep16(s, k16, w.cs, nr, w.amax + 1, true, (f16_t*)w.kn, (f16_t*)w.kt, s.Hkv, stream);
+      launch_prep16(s, v16, nullptr, nr, w.amax + 2, false, (f16_t*)w.vn, nullptr, s.Hkv, stream);
+      launch_prep16(s, d16, nullptr, nr, w.amax + 3, false, (f16_t*)w.dOn, nullptr, s.Hq, stream);
     }
     auto grads = [&](auto* tag) {
       using TG = std::remove_pointer_t<decltype(tag)>;
@@ -707,13 +721,14 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
         Span sp(P, DAG_K_DKDV, stream);
         launch_dkdv_mfma<TG>(s, (int64_t)P.pair_order.size(), (const f16_t*)w.qn, (const f16_t*)w.kn,
                              (const f16_t*)w.vn, (const f16_t*)w.dOn, w.ld, w.cs, w.amax + 3, D.pair_order,
-                             D.kpairs, D.kpair_off, D.kpsteps, D.page_nrows, (TG*)dk, (TG*)dv, w.amax, stream);
+                             D.kpairs, D.kpair_off, D.kpsteps, D.kstep_mask, D.masks, D.page_nrows, (TG*)dk,
+                             (TG*)dv, w.amax, stream);
       }
       {
         Span sp(P, DAG_K_DQ, stream);
         launch_dq_mfma<TG>(s, n_qp, (const f16_t*)w.qn, (const f16_t*)w.kn, (const f16_t*)w.kt,
                            (const f16_t*)w.vn, (const f16_t*)w.dOn, w.ld, w.cs, w.amax + 3, D.qpages,
-                           D.fwd_order, D.tiles, (TG*)dq, w.amax, stream);
+                           D.fwd_order, D.tiles, D.tile_mask, D.masks, (TG*)dq, w.amax, stream);
       }
     };
     if (p->grad_dtype == DAG_DTYPE_FP32)
@@ -724,11 +739,11 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
     {
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
       if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
-      launch_rowdot<bf16_t>(s, (const bf16_t*)o, (const bf16_t*)o_lo, (const bf16_t*)dO, lse, D.page_nrows, nullptr,
-                            w.ld, stream);
-      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, D.page_nrows, nullptr, (float*)w.qn, nullptr, s.Hq,
+      launch_rowdot<bf16_t>(s, (const bf16_t*)o, (const bf16_t*)o_lo, (const bf16_t*)dO, lse, D.page_nrows, w.ld,
+                            stream);
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)q, w.cs, D.page_nrows, (float*)w.qn, nullptr, s.Hq,
                                      stream);
-      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, D.page_nrows, nullptr, (float*)w.kn, nullptr, s.Hkv,
+      launch_relayout<bf16_t, float>(s, (const bf16_t*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv,
                                      stream);
     }
     Span sp(P, DAG_K_DKDV, stream);
@@ -746,10 +761,10 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
     {
       Span sp(P, DAG_K_PROLOGUE_BWD, stream);
       if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
-      launch_rowdot<float>(s, (const float*)o, nullptr, (const float*)dO, lse, D.page_nrows, nullptr, w.ld, stream);
-      launch_relayout<float, float>(s, (const float*)q, w.cs, D.page_nrows, nullptr, (float*)w.qn, nullptr, s.Hq,
+      launch_rowdot<float>(s, (const float*)o, nullptr, (const float*)dO, lse, D.page_nrows, w.ld, stream);
+      launch_relayout<float, float>(s, (const float*)q, w.cs, D.page_nrows, (float*)w.qn, nullptr, s.Hq,
                                     stream);
-      launch_relayout<float, float>(s, (const float*)k, w.cs, D.page_nrows, nullptr, (float*)w.kn, nullptr, s.Hkv,
+      launch_relayout<float, float>(s, (const float*)k, w.cs, D.page_nrows, (float*)w.kn, nullptr, s.Hkv,
                                     stream);
     }
     Span sp(P, DAG_K_DKDV, stream);

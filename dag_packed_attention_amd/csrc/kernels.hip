@@ -12,10 +12,11 @@
 //                  ld  [page][Hq][64] float2    the S and dP offsets of every row for the backward
 //                  amax[4]                      largest |q|, |k|, |v|, |dO| (float bits)
 //
-// MFMA path (D = 128, Hq = 4 Hkv).  Operands are fp16: each of q, k, v, dO is scaled by
-// the power of two that puts its largest |x| in [1, 2) (amax), so no finite bf16 input
-// overflows fp16 and small values keep fp16's range below that maximum; the scales are
-// folded into the softmax's exponent factor and the output multipliers, exactly.  The
+// MFMA path (D = 128, Hq = 4 Hkv).  Operands are fp16: each of q, k, v, dO is scaled by a
+// power of two from its largest |x| (amax), so no finite bf16 input overflows fp16; q and
+// k land in [2^14, 2^15), which leaves 28 binades of normal fp16 range below the largest
+// element, v and dO in [1, 2), which keeps the backward's fp16 dS operand in range.  The
+// scales are folded into the softmax's exponent factor and the output multipliers, exactly.  The
 // rotated q/k and the probabilities P and dS keep three more mantissa bits than bf16.
 // A work-group serves one 64-row block and one KV head; its four
 // waves are the four query heads of that GQA group, so every K/V tile staged
@@ -62,12 +63,20 @@ template <> __device__ __forceinline__ void st_f<float>(float* p, float x) { *p 
 template <> __device__ __forceinline__ void st_f<bf16_t>(bf16_t* p, float x) { *p = f2bf(x); }
 template <> __device__ __forceinline__ void st_f<f16_t>(f16_t* p, float x) { *p = (f16_t)x; }
 
-// 2^-e for the largest |x| = m 2^e (m in [1, 2)), from the float bits of that maximum: a
-// power-of-two factor that maps a tensor's largest magnitude into [1, 2), exactly reversible.
-__device__ __forceinline__ float pow2_scale(uint32_t maxbits) {
+// Where the operand copies put their tensor's largest magnitude: q and k in [2^14, 2^15)
+// (a rotated pair then stays below 2^15.5, inside fp16), v and dO in [1, 2): with P <= 1
+// the backward's dS in those units is bounded by |dO.v| + |D| <= 4 D, far inside fp16.
+constexpr int kTopQK = 14, kTopVO = 0;
+
+// 2^(top - e) for the largest |x| = m 2^e (m in [1, 2)), from the float bits of that
+// maximum: a power-of-two factor that maps a tensor's largest magnitude into
+// [2^top, 2^(top+1)), exactly reversible.  e is taken as at least -24, so a tensor of
+// tiny values is scaled up by at most 2^(top+24) and the products of factors the kernels
+// form stay well inside fp32's normal range.
+__device__ __forceinline__ float pow2_scale(uint32_t maxbits, int top) {
   const float m = __uint_as_float(maxbits);
   if (!(m > 0.f) || !isfinite(m)) return 1.f;
-  return ldexpf(1.f, -ilogbf(m));
+  return ldexpf(1.f, top - max(ilogbf(m), -24));
 }
 
 // position of row r inside its transposed 16-group (bits 2 and 3 swapped)
@@ -104,12 +113,11 @@ __global__ void cs_kernel(const int32_t* __restrict__ pos_of_row, float2* __rest
 template <typename Tin, typename Tout>
 __global__ __launch_bounds__(256) void relayout_kernel(
     const Tin* __restrict__ x, const float2* __restrict__ cs, const int32_t* __restrict__ page_nrows,
-    const uint32_t* __restrict__ smax, Tout* __restrict__ out_n, Tout* __restrict__ out_t, int H, int D) {
+    Tout* __restrict__ out_n, Tout* __restrict__ out_t, int H, int D) {
   extern __shared__ float tile[];  // [64][D + 1]
   const int page = blockIdx.x / H, h = blockIdx.x % H;
   const int nrows = page_nrows[page];
   const int half = D / 2, ld = D + 1;
-  const float sc = smax ? pow2_scale(*smax) : 1.f;
   for (int idx = threadIdx.x; idx < 64 * half; idx += blockDim.x) {
     const int r = idx / half, i = idx % half;
     float a = 0.f, b = 0.f;
@@ -125,8 +133,8 @@ __global__ __launch_bounds__(256) void relayout_kernel(
         a = a2;
       }
     }
-    tile[r * ld + i] = a * sc;
-    tile[r * ld + i + half] = b * sc;
+    tile[r * ld + i] = a;
+    tile[r * ld + i + half] = b;
   }
   __syncthreads();
   const int64_t base = ((int64_t)page * H + h) * 64 * D;
@@ -150,8 +158,7 @@ __global__ __launch_bounds__(256) void relayout_kernel(
 template <typename T>
 __global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ o_lo, const T* __restrict__ dO,
                               const float* __restrict__ lse, const int32_t* __restrict__ page_nrows,
-                              const uint32_t* __restrict__ dmax, float2* __restrict__ ldout, int64_t n_pages,
-                              int Hq, int D, float inv_scale) {
+                              float2* __restrict__ ldout, int64_t n_pages, int Hq, int D, float inv_scale) {
   const int64_t idx = (int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64;  // one wave per (row, h)
   const int lane = threadIdx.x % 64;
   if (idx >= n_pages * 64 * Hq) return;
@@ -170,7 +177,7 @@ __global__ void rowdot_kernel(const T* __restrict__ o, const T* __restrict__ o_l
   for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (lane == 0) {
     float2 v = make_float2(0.f, 0.f);
-    if (valid) v = make_float2(-lse[row * Hq + h] * inv_scale, -acc * (dmax ? pow2_scale(*dmax) : 1.f));
+    if (valid) v = make_float2(-lse[row * Hq + h] * inv_scale, -acc);
     ldout[(page * Hq + h) * 64 + r] = v;
   }
 }
@@ -229,8 +236,8 @@ __global__ __launch_bounds__(256) void absmax_kernel(const bf16_t* __restrict__ 
 template <bool kRot, bool kNat, bool kTrans>
 __global__ __launch_bounds__(512) void prep16_kernel(const bf16_t* __restrict__ x, const float2* __restrict__ cs,
                                                      const int32_t* __restrict__ page_nrows,
-                                                     const uint32_t* __restrict__ smax, f16_t* __restrict__ out_n,
-                                                     f16_t* __restrict__ out_t, int H) {
+                                                     const uint32_t* __restrict__ smax, int top,
+                                                     f16_t* __restrict__ out_n, f16_t* __restrict__ out_t, int H) {
   constexpr int kTs = 72;  // padded row of the transposed tile (elements)
   __shared__ __attribute__((aligned(16))) f16_t tt[kTrans ? 128 * kTs : 8];
   const int page = blockIdx.x, t = threadIdx.x, r = t >> 3, j = t & 7;
@@ -245,7 +252,7 @@ __global__ __launch_bounds__(512) void prep16_kernel(const bf16_t* __restrict__ 
       c[2 * e] = v.x, sn[2 * e] = v.y, c[2 * e + 1] = v.z, sn[2 * e + 1] = v.w;
     }
   }
-  const float sc = smax ? pow2_scale(*smax) : 1.f;
+  const float sc = smax ? pow2_scale(*smax, top) : 1.f;
   for (int h = 0; h < H; ++h) {
     const bf16_t* src = x + (row * H + h) * kD + 8 * j;
     u16x8 ua = {}, ub = {};
@@ -303,8 +310,8 @@ __global__ __launch_bounds__(256) void rowdot16_kernel(const bf16_t* __restrict_
                                                        float2* __restrict__ ldout, const uint32_t* __restrict__ amax,
                                                        int64_t n_pages, int Hq, float inv_scale) {
   const int sub = threadIdx.x & 15;
-  const float sqk = pow2_scale(amax[0]) * pow2_scale(amax[1]);
-  const float sv = pow2_scale(amax[2]), sdo = pow2_scale(amax[3]);
+  const float sqk = pow2_scale(amax[0], kTopQK) * pow2_scale(amax[1], kTopQK);
+  const float sv = pow2_scale(amax[2], kTopVO), sdo = pow2_scale(amax[3], kTopVO);
   const int64_t total = n_pages * 64 * Hq;
   for (int64_t it = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4); it < total; it += (int64_t)gridDim.x * 16) {
     const int64_t row = it / Hq;
@@ -477,9 +484,16 @@ constexpr int kTile = 64 * kD;  // elements of a page's 64 x 128 (or 128 x 64) b
 // so one wave's softmax overlaps the other's products).  K/V tiles are
 // double-buffered in LDS and fetched straight from global memory while the
 // previous tile is multiplied; each 64-key tile is taken as two 32-key halves.
+//
+// kMasked (packed page layouts): a tile may carry a mask id; the lane then reads its query
+// row's 64-bit key mask and the mask alone decides which keys it sees (the causal rule of
+// a page's last tile applies to unmasked tiles only).  Rows of one wave may then have seen
+// no key yet when another row raises the running max; their rescale factor is 1.
+template <bool kMasked>
 __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vt,
     const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
+    const int32_t* __restrict__ tile_mask, const uint64_t* __restrict__ masks,
     bf16_t* __restrict__ o, float* __restrict__ lse, bf16_t* __restrict__ o_lo, const uint32_t* __restrict__ amax,
     int n_qp, int Hq, int Hkv, float sl2_raw) {
   __shared__ __attribute__((aligned(1024))) f16_t lk[2][kPageB];
@@ -488,8 +502,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
   if (!map_item(n_qp, Hkv, unit, g)) return;
   // the fp16 copies hold sq q, sk k, sv v (powers of two): the scores come out as
   // sq sk q.k and the output as sv O, so the exponent factor and 1 / l absorb them exactly
-  const float sl2 = sl2_raw / pow2_scale(amax[0]) / pow2_scale(amax[1]);
-  const float inv_sv = 1.f / pow2_scale(amax[2]);
+  const float sl2 = sl2_raw / pow2_scale(amax[0], kTopQK) / pow2_scale(amax[1], kTopQK);
+  const float inv_sv = 1.f / pow2_scale(amax[2], kTopVO);
   const QPage qp = qpages[order[unit]];
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
@@ -528,8 +542,14 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
     }
     const int lohi = tiles[qp.tile_begin + t].lohi;
     const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
-    const bool diag = (t == T - 1);
-    const bool full = lo == 0 && hi_t == 64 && !diag;
+    int mi = -1;
+    uint64_t rmask = 0;
+    if constexpr (kMasked) {
+      mi = tile_mask[qp.tile_begin + t];
+      if (mi >= 0) rmask = masks[(int64_t)mi * 128 + row];
+    }
+    const bool diag = (t == T - 1) && mi < 0;
+    const bool full = lo == 0 && hi_t == 64 && !diag && mi < 0;
     const f16_t* K = lk[buf];
     const f16_t* V = lv[buf];
 
@@ -559,7 +579,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = mb * 32 + acc_row(r, hi);
-          const bool ok = key >= lo && key < hi_t && (!diag || key <= row);
+          bool ok = key >= lo && key < hi_t && (!diag || key <= row);
+          if constexpr (kMasked) ok = ok && (mi < 0 || ((rmask >> key) & 1ull));
           s[r] = ok ? s[r] : -INFINITY;
         }
       }
@@ -569,7 +590,8 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
       if (__any(mx > mrow + kLazy)) {
         const float mnew = fmaxf(mrow, mx);
-        const float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+        float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
+        if constexpr (kMasked) alpha = mnew == -INFINITY ? 1.f : alpha;
         mrow = mnew;
         lrow *= alpha;
 #pragma unroll
@@ -580,22 +602,34 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
       // a half-tile can be fully masked before a row has seen any key (a mounted
       // span starting past key 32); then m is still -inf and every score is -inf
       const float mneg = mrow == -INFINITY ? 0.f : -mrow;
-      float sum = 0.f;
-      {
-        // each score is rounded to the log2 domain first and the running max subtracted
-        // after: m is the rounded product of the largest score, so the exponent is <= kLazy
-        // whatever the logits' size (a fused s * sl2 - m would leave m's rounding error,
-        // which exceeds 1 once logits pass 2^20)
+      if (!__any(fabsf(mrow) > 0x1p20f)) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, mneg));
+      } else {
+        // logits beyond 2^20 in the log2 domain: the fused s * sl2 - m keeps m's rounding
+        // error (over 2^-4 there, over 8 beyond 2^27), so each score is rounded to the log2
+        // domain first and the max subtracted after; m is the rounded product of the largest
+        // score, so the exponent stays <= kLazy whatever the logits' size
 #pragma clang fp contract(off)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(s[r] * sl2 + mneg);
-          s[r] = p;
-          sum += p;
-        }
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(s[r] * sl2 + mneg);
       }
-      lrow += sum;
+      // The row sum adds the fp16-rounded weights that the PV product multiplies, so the
+      // weights O is formed with sum to 1 exactly (a row on one key reproduces that key's
+      // value exactly, and rowsum(dO O) in the backward cancels against its dP); summed as
+      // fp16 pairs with fp32 accumulation.
       const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8);
+      {
+        typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+        const f16x2 one2 = {(f16_t)1.f, (f16_t)1.f};
+        float sum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sum = __builtin_amdgcn_fdot2(f16x2{pf0[2 * i], pf0[2 * i + 1]}, one2, sum, false);
+          sum = __builtin_amdgcn_fdot2(f16x2{pf1[2 * i], pf1[2 * i + 1]}, one2, sum, false);
+        }
+        lrow += sum;
+      }
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         oacc[a] = mfma(vfr[a * 2], pf0, oacc[a]);
@@ -639,12 +673,14 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
 // dQ for one query block (64 rows) x one KV head.  Eight waves, wave (hh, nb) =
 // query head 4 g + hh and rows 32 nb ..; the K, V and K^T tiles are
 // double-buffered in LDS like the forward's.
-template <typename TG>
+// kMasked: the forward's tile masks, read the same way.
+template <typename TG, bool kMasked>
 __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ kt,
     const f16_t* __restrict__ vn, const f16_t* __restrict__ dOn, const float2* __restrict__ ldd,
     const float2* __restrict__ cs, const uint32_t* __restrict__ dmax, const QPage* __restrict__ qpages,
-    const int32_t* __restrict__ order, const Tile* __restrict__ tiles, TG* __restrict__ dq,
+    const int32_t* __restrict__ order, const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_mask,
+    const uint64_t* __restrict__ masks, TG* __restrict__ dq,
     const uint32_t* __restrict__ amax, int n_qp, int Hq, int Hkv, float sl2_raw, float scale) {
   __shared__ __attribute__((aligned(1024))) f16_t lk[2][kPageB];
   __shared__ __attribute__((aligned(1024))) f16_t lvv[2][kPageB];
@@ -654,7 +690,7 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
   // fp16 copies: sq q, sk k, sv v, sdo dO (powers of two); the S and dP offsets in ldd are
   // in the same scaled units, so dS comes out as sdo sv dS and the sum over keys of dS k
   // as sdo sv sk dQ / scale
-  const float sq = pow2_scale(amax[0]), sk = pow2_scale(amax[1]), sv = pow2_scale(amax[2]);
+  const float sq = pow2_scale(amax[0], kTopQK), sk = pow2_scale(amax[1], kTopQK), sv = pow2_scale(amax[2], kTopVO);
   const float sl2 = sl2_raw / sq / sk;
   const QPage qp = qpages[order[unit]];
   const int tid = threadIdx.x;
@@ -700,8 +736,14 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
     }
     const int lohi = tiles[qp.tile_begin + t].lohi;
     const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
-    const bool diag = (t == T - 1);
-    const bool full = lo == 0 && hi_t == 64 && !diag && qp.nrows == 64;
+    int mi = -1;
+    uint64_t rmask = 0;
+    if constexpr (kMasked) {
+      mi = tile_mask[qp.tile_begin + t];
+      if (mi >= 0) rmask = masks[(int64_t)mi * 128 + row];
+    }
+    const bool diag = (t == T - 1) && mi < 0;
+    const bool full = lo == 0 && hi_t == 64 && !diag && qp.nrows == 64 && mi < 0;
     const f16_t* K = lk[buf];
     const f16_t* V = lvv[buf];
     const f16_t* KT = lkt[buf];
@@ -720,7 +762,8 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = mb * 32 + acc_row(r, hi);
-          const bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < qp.nrows;
+          bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < qp.nrows;
+          if constexpr (kMasked) ok = ok && (mi < 0 || ((rmask >> key) & 1ull));
           const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl));
           s[r] = ok ? p * (dp[r] + nD) : 0.f;  // padding may hold NaN
         }
@@ -736,7 +779,7 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
     __syncthreads();
   }
 
-  const float gscale = scale / pow2_scale(*dmax) / sv / sk;  // undo the operand scalings
+  const float gscale = scale / pow2_scale(*dmax, kTopVO) / sv / sk;  // undo the operand scalings
   const bool valid = row < qp.nrows;
   const int64_t grow = (int64_t)qp.phys * 64 + row;
   TG* out = dq + (grow * Hq + h) * kD;
@@ -846,12 +889,17 @@ __device__ __forceinline__ void dkdv_reduce_store(const f32x16 (&acc)[4], float*
 // between the dP products, dS between the dV products); hidden keys get a
 // per-lane -inf offset.  At the end the two head parities are summed through LDS in
 // a fixed order and each page is written once: deterministic, no atomics.
-template <typename TG>
+//
+// kMasked (packed page layouts): each step carries the two pages' mask ids (fetched with the
+// step descriptors); a lane of a masked side reads its key's 64-bit query-row mask and
+// zeroes P for the rows it hides (packed steps carry no causal rule).
+template <typename TG, bool kMasked>
 __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vn,
     const f16_t* __restrict__ dOn, const float2* __restrict__ ldd, const float2* __restrict__ cs,
     const uint32_t* __restrict__ dmax, const int32_t* __restrict__ pair_order, const int32_t* __restrict__ pairs,
-    const int64_t* __restrict__ pair_off, const KStep* __restrict__ psteps, const int32_t* __restrict__ page_nrows,
+    const int64_t* __restrict__ pair_off, const KStep* __restrict__ psteps, const KMask* __restrict__ pmasks,
+    const uint64_t* __restrict__ masks, const int32_t* __restrict__ page_nrows,
     TG* __restrict__ dk, TG* __restrict__ dv, const uint32_t* __restrict__ amax, int n_pairs, int Hq, int Hkv,
     float sl2_raw, float scale) {
   // [buffer][head of the half-step][Q, dO][32 x 128] f16 (the first 65 KiB are reused
@@ -864,7 +912,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
   if (!map_item(n_pairs, Hkv, unit, g)) return;
   // fp16 copies: sq q, sk k, sv v, sdo dO (powers of two), offsets in ldd in the same
   // units: P is exact, dS comes out as sdo sv dS, the sums as sdo dV and sdo sv sq dK / scale
-  const float sq = pow2_scale(amax[0]), sk = pow2_scale(amax[1]), sv = pow2_scale(amax[2]);
+  const float sq = pow2_scale(amax[0], kTopQK), sk = pow2_scale(amax[1], kTopQK), sv = pow2_scale(amax[2], kTopVO);
   const float sl2 = sl2_raw / sq / sk;
   const int pr = pair_order[unit];
   const int physA = pairs[2 * pr], physB = pairs[2 * pr + 1];
@@ -902,6 +950,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
   KStep cur = kst[0];
   KStep nxt = kst[min(1, n_steps - 1)];
   KStep n2 = kst[min(2, n_steps - 1)];
+  KMask cur_m{-1, -1}, nxt_m{-1, -1}, n2_m{-1, -1};
+  if constexpr (kMasked) {
+    cur_m = pmasks[s_begin];
+    nxt_m = pmasks[s_begin + min(1, n_steps - 1)];
+    n2_m = pmasks[s_begin + min(2, n_steps - 1)];
+  }
   // staging role: head sj of the half-step, tensor ts (0: Q, 1: dO), bricks sb0 .. sb0 + 3
   const int sj = wave & 1, ts = (wave >> 1) & 1, sb0 = 4 * (wave >> 2);
   const uint32_t rlo = brick_lane_off(lane);
@@ -931,6 +985,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const bool offs = ts == 0 && sb0 == 0;
 
     const uint32_t inf = ((uint32_t)cur.info >> (16 * side)) & 0xffffu;
+    uint64_t kmask = 0;
+    int mi = -1;
+    if constexpr (kMasked) {
+      mi = side ? cur_m.b : cur_m.a;
+      if (mi >= 0 && active) kmask = masks[(int64_t)mi * 128 + 64 + kb * 32 + l32];
+    }
     const int rb = cur.info & 1, lo = (inf >> 1) & 0x7f, hi_t = (inf >> 8) & 0x7f;
     const bool diag = (inf >> 15) & 1;
     if (!active || lo >= hi_t) {
@@ -1013,6 +1073,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = key <= rb * 32 + acc_row(r, hi) ? s[r] : 0.f;
       }
+      if constexpr (kMasked) {
+        // packed: the rows of the step that see this lane's key
+        if (mi >= 0) {
+          const uint32_t rows = (uint32_t)(kmask >> (32 * (cur.info & 1)));
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = ((rows >> acc_row(r, hi)) & 1u) ? s[r] : 0.f;
+        }
+      }
       // Padding rows need no mask: their Q and dO rows and offsets are zero, so they add
       // exact zeros to dV and dK.
       const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8);
@@ -1076,16 +1144,23 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     // the descriptor three steps ahead: issued here, where the closing wait covers it
     __builtin_amdgcn_sched_barrier(0);
     const KStep n3 = kst[min((u >> 1) + 3, n_steps - 1)];
+    KMask n3_m{-1, -1};
+    if constexpr (kMasked) n3_m = pmasks[s_begin + min((u >> 1) + 3, n_steps - 1)];
     wait_all_loads();
     __syncthreads();
     if (hp) {
       cur = nxt;
       nxt = n2;
       n2 = n3;
+      if constexpr (kMasked) {
+        cur_m = nxt_m;
+        nxt_m = n2_m;
+        n2_m = n3_m;
+      }
     }
   }
 
-  const float inv_sdo = 1.f / pow2_scale(*dmax);  // undo the operand scalings
+  const float inv_sdo = 1.f / pow2_scale(*dmax, kTopVO);  // undo the operand scalings
   float* red = reinterpret_cast<float*>(&qd[0][0][0][0]);  // [128][129] fp32
   const int rowsA = page_nrows[physA], rowsB = physB >= 0 ? page_nrows[physB] : 0;
   // sum the two head parities in order 0, 1 through LDS, then write dk (scaled,
@@ -1281,17 +1356,16 @@ void launch_cs(const LaunchShape& s, const int32_t* pos_of_row, float2* cs, hipS
 
 template <typename Tin, typename Tout>
 void launch_relayout(const LaunchShape& s, const Tin* x, const float2* cs, const int32_t* page_nrows,
-                     const uint32_t* smax, Tout* out_n, Tout* out_t, int H, hipStream_t st) {
+                     Tout* out_n, Tout* out_t, int H, hipStream_t st) {
   const size_t lds = (size_t)64 * (s.D + 1) * sizeof(float);
-  relayout_kernel<Tin, Tout><<<(unsigned)(s.pages * H), 256, lds, st>>>(x, cs, page_nrows, smax, out_n, out_t, H,
-                                                                         s.D);
+  relayout_kernel<Tin, Tout><<<(unsigned)(s.pages * H), 256, lds, st>>>(x, cs, page_nrows, out_n, out_t, H, s.D);
 }
 
 template <typename T>
 void launch_rowdot(const LaunchShape& s, const T* o, const T* o_lo, const T* dO, const float* lse,
-                   const int32_t* page_nrows, const uint32_t* dmax, float2* ld, hipStream_t st) {
-  rowdot_kernel<T><<<blocks_for(s.pages * 64 * s.Hq, 4), 256, 0, st>>>(o, o_lo, dO, lse, page_nrows, dmax, ld,
-                                                                       s.pages, s.Hq, s.D, 1.f / s.scale);
+                   const int32_t* page_nrows, float2* ld, hipStream_t st) {
+  rowdot_kernel<T><<<blocks_for(s.pages * 64 * s.Hq, 4), 256, 0, st>>>(o, o_lo, dO, lse, page_nrows, ld, s.pages,
+                                                                       s.Hq, s.D, 1.f / s.scale);
 }
 
 void launch_absmax(const LaunchShape& s, const bf16_t* q, const bf16_t* k, const bf16_t* v, const bf16_t* dO,
@@ -1305,19 +1379,20 @@ void launch_absmax(const LaunchShape& s, const bf16_t* q, const bf16_t* k, const
 void launch_zero_u32(uint32_t* out, int n, hipStream_t st) { zero_u32_kernel<<<1, 64, 0, st>>>(out, n); }
 
 void launch_prep16(const LaunchShape& s, const bf16_t* x, const float2* cs, const int32_t* page_nrows,
-                   const uint32_t* smax, f16_t* out_n, f16_t* out_t, int H, hipStream_t st) {
+                   const uint32_t* smax, bool qk, f16_t* out_n, f16_t* out_t, int H, hipStream_t st) {
+  const int top = qk ? kTopQK : kTopVO;
   const unsigned grid = (unsigned)s.pages;
   if (cs) {
     if (out_n && out_t)
-      prep16_kernel<true, true, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, H);
+      prep16_kernel<true, true, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, top, out_n, out_t, H);
     else
-      prep16_kernel<true, true, false><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, H);
+      prep16_kernel<true, true, false><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, top, out_n, out_t, H);
   } else if (out_n && out_t) {
-    prep16_kernel<false, true, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, H);
+    prep16_kernel<false, true, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, top, out_n, out_t, H);
   } else if (out_t) {
-    prep16_kernel<false, false, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, H);
+    prep16_kernel<false, false, true><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, top, out_n, out_t, H);
   } else {
-    prep16_kernel<false, true, false><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, out_n, out_t, H);
+    prep16_kernel<false, true, false><<<grid, 512, 0, st>>>(x, cs, page_nrows, smax, top, out_n, out_t, H);
   }
 }
 
@@ -1329,11 +1404,11 @@ void launch_rowdot16(const LaunchShape& s, const bf16_t* o, const bf16_t* o_lo, 
       o, o_lo, dO, lse, page_nrows, ld, amax, s.pages, s.Hq, 1.f / s.scale);
 }
 
-template void launch_relayout<bf16_t, f16_t>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, const uint32_t*, f16_t*, f16_t*, int, hipStream_t);
-template void launch_relayout<bf16_t, float>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, const uint32_t*, float*, float*, int, hipStream_t);
-template void launch_relayout<float, float>(const LaunchShape&, const float*, const float2*, const int32_t*, const uint32_t*, float*, float*, int, hipStream_t);
-template void launch_rowdot<bf16_t>(const LaunchShape&, const bf16_t*, const bf16_t*, const bf16_t*, const float*, const int32_t*, const uint32_t*, float2*, hipStream_t);
-template void launch_rowdot<float>(const LaunchShape&, const float*, const float*, const float*, const float*, const int32_t*, const uint32_t*, float2*, hipStream_t);
+template void launch_relayout<bf16_t, f16_t>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, f16_t*, f16_t*, int, hipStream_t);
+template void launch_relayout<bf16_t, float>(const LaunchShape&, const bf16_t*, const float2*, const int32_t*, float*, float*, int, hipStream_t);
+template void launch_relayout<float, float>(const LaunchShape&, const float*, const float2*, const int32_t*, float*, float*, int, hipStream_t);
+template void launch_rowdot<bf16_t>(const LaunchShape&, const bf16_t*, const bf16_t*, const bf16_t*, const float*, const int32_t*, float2*, hipStream_t);
+template void launch_rowdot<float>(const LaunchShape&, const float*, const float*, const float*, const float*, const int32_t*, float2*, hipStream_t);
 
 // Grid for map_item: whole runs of kRun units per head, padded to a multiple of 8 runs.
 static unsigned run_grid(int64_t n_units, int H) {
@@ -1343,42 +1418,61 @@ static unsigned run_grid(int64_t n_units, int H) {
 }
 
 void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vt,
-                     const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
-                     bf16_t* o_lo, const uint32_t* amax, hipStream_t st) {
-  fwd_mfma_kernel<<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, vt, qpages, order, tiles, o, lse, o_lo, amax,
-                                                         (int)n_qp, s.Hq, s.Hkv, s.scale * kLog2e);
+                     const QPage* qpages, const int32_t* order, const Tile* tiles, const int32_t* tile_mask,
+                     const uint64_t* masks, bf16_t* o, float* lse, bf16_t* o_lo, const uint32_t* amax,
+                     hipStream_t st) {
+  if (tile_mask)
+    fwd_mfma_kernel<true><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, vt, qpages, order, tiles, tile_mask, masks, o,
+                                                                 lse, o_lo, amax, (int)n_qp, s.Hq, s.Hkv,
+                                                                 s.scale * kLog2e);
+  else
+    fwd_mfma_kernel<false><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, vt, qpages, order, tiles, nullptr, nullptr,
+                                                                  o, lse, o_lo, amax, (int)n_qp, s.Hq, s.Hkv,
+                                                                  s.scale * kLog2e);
 }
 
 template <typename TG>
 void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* kt,
                     const f16_t* vn, const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
-                    const QPage* qpages, const int32_t* order, const Tile* tiles, TG* dq, const uint32_t* amax,
-                    hipStream_t st) {
-  dq_mfma_kernel<TG><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, kt, vn, dOn, ld, cs, dmax, qpages, order,
-                                                            tiles, dq, amax, (int)n_qp, s.Hq, s.Hkv,
-                                                            s.scale * kLog2e, s.scale);
+                    const QPage* qpages, const int32_t* order, const Tile* tiles, const int32_t* tile_mask,
+                    const uint64_t* masks, TG* dq, const uint32_t* amax, hipStream_t st) {
+  if (tile_mask)
+    dq_mfma_kernel<TG, true><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, kt, vn, dOn, ld, cs, dmax, qpages, order,
+                                                                    tiles, tile_mask, masks, dq, amax, (int)n_qp,
+                                                                    s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
+  else
+    dq_mfma_kernel<TG, false><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, kt, vn, dOn, ld, cs, dmax, qpages,
+                                                                     order, tiles, nullptr, nullptr, dq, amax,
+                                                                     (int)n_qp, s.Hq, s.Hkv, s.scale * kLog2e,
+                                                                     s.scale);
 }
 
 template <typename TG>
 void launch_dkdv_mfma(const LaunchShape& s, int64_t n_pairs, const f16_t* qn, const f16_t* kn, const f16_t* vn,
                       const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
                       const int32_t* pair_order, const int32_t* pairs, const int64_t* pair_off, const KStep* psteps,
-                      const int32_t* page_nrows, TG* dk, TG* dv, const uint32_t* amax, hipStream_t st) {
-  dkdv_mfma_kernel<TG><<<run_grid(n_pairs, s.Hkv), 512, 0, st>>>(qn, kn, vn, dOn, ld, cs, dmax, pair_order, pairs,
-                                                                 pair_off, psteps, page_nrows, dk, dv, amax,
-                                                                 (int)n_pairs, s.Hq, s.Hkv, s.scale * kLog2e,
-                                                                 s.scale);
+                      const KMask* pmasks, const uint64_t* masks, const int32_t* page_nrows, TG* dk, TG* dv,
+                      const uint32_t* amax, hipStream_t st) {
+  if (pmasks)
+    dkdv_mfma_kernel<TG, true><<<run_grid(n_pairs, s.Hkv), 512, 0, st>>>(
+        qn, kn, vn, dOn, ld, cs, dmax, pair_order, pairs, pair_off, psteps, pmasks, masks, page_nrows, dk, dv, amax,
+        (int)n_pairs, s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
+  else
+    dkdv_mfma_kernel<TG, false><<<run_grid(n_pairs, s.Hkv), 512, 0, st>>>(
+        qn, kn, vn, dOn, ld, cs, dmax, pair_order, pairs, pair_off, psteps, nullptr, nullptr, page_nrows, dk, dv,
+        amax, (int)n_pairs, s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
 }
 
 #define INST_MFMA_BWD(TG)                                                                                      \
   template void launch_dq_mfma<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,      \
                                    const f16_t*, const f16_t*, const float2*, const float2*, const uint32_t*,  \
-                                   const QPage*, const int32_t*, const Tile*, TG*, const uint32_t*,            \
-                                   hipStream_t);                                                               \
+                                   const QPage*, const int32_t*, const Tile*, const int32_t*,                  \
+                                   const uint64_t*, TG*, const uint32_t*, hipStream_t);                        \
   template void launch_dkdv_mfma<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,    \
                                      const f16_t*, const float2*, const float2*, const uint32_t*,              \
                                      const int32_t*, const int32_t*, const int64_t*, const KStep*,             \
-                                     const int32_t*, TG*, TG*, const uint32_t*, hipStream_t);
+                                     const KMask*, const uint64_t*, const int32_t*, TG*, TG*,                  \
+                                     const uint32_t*, hipStream_t);
 INST_MFMA_BWD(bf16_t)
 INST_MFMA_BWD(float)
 

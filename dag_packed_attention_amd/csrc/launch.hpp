@@ -20,10 +20,10 @@ struct LaunchShape {
 void launch_cs(const LaunchShape& s, const int32_t* pos_of_row, float2* cs, hipStream_t st);
 template <typename Tin, typename Tout>
 void launch_relayout(const LaunchShape& s, const Tin* x, const float2* cs, const int32_t* page_nrows,
-                     const uint32_t* smax, Tout* out_n, Tout* out_t, int H, hipStream_t st);
+                     Tout* out_n, Tout* out_t, int H, hipStream_t st);
 template <typename T>
 void launch_rowdot(const LaunchShape& s, const T* o, const T* o_lo, const T* dO, const float* lse,
-                   const int32_t* page_nrows, const uint32_t* dmax, float2* ld, hipStream_t st);
+                   const int32_t* page_nrows, float2* ld, hipStream_t st);
 // out[0 .. n) = 0, n <= 64 (integer maxima start from it)
 void launch_zero_u32(uint32_t* out, int n, hipStream_t st);
 // amax[0..3) = max |q|, |k|, |v| (and amax[3] = max |dO| when dO is given) over valid
@@ -32,27 +32,30 @@ void launch_absmax(const LaunchShape& s, const bf16_t* q, const bf16_t* k, const
                    const int32_t* page_nrows, uint32_t* amax, hipStream_t st);
 // MFMA-path prologue (D = 128, bf16 in): rotate / scale / relayout one tensor into its fp16
 // page-major copy (out_n) and/or transposed copy (out_t), scaled by the power of two that
-// maps the maximum *smax into [1, 2).
+// maps the maximum *smax into [2^14, 2^15) for q and k (qk), into [1, 2) for v and dO.
 void launch_prep16(const LaunchShape& s, const bf16_t* x, const float2* cs, const int32_t* page_nrows,
-                   const uint32_t* smax, f16_t* out_n, f16_t* out_t, int H, hipStream_t st);
+                   const uint32_t* smax, bool qk, f16_t* out_n, f16_t* out_t, int H, hipStream_t st);
 // ld = (-sq sk lse / scale, -sv rowsum(fp16(sdo dO) (o + o_lo))) per (page, head, row), the
 // scales from amax[0..3].
 void launch_rowdot16(const LaunchShape& s, const bf16_t* o, const bf16_t* o_lo, const bf16_t* dO, const float* lse,
                      const int32_t* page_nrows, float2* ld, const uint32_t* amax, hipStream_t st);
-// amax: the q, k, v maxima whose power-of-two scales the fp16 copies carry.
+// amax: the q, k, v maxima whose power-of-two scales the fp16 copies carry.  tile_mask /
+// masks (packed plans; nullptr otherwise) select the kernels that read per-tile masks.
 void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vt,
-                     const QPage* qpages, const int32_t* order, const Tile* tiles, bf16_t* o, float* lse,
-                     bf16_t* o_lo, const uint32_t* amax, hipStream_t st);
+                     const QPage* qpages, const int32_t* order, const Tile* tiles, const int32_t* tile_mask,
+                     const uint64_t* masks, bf16_t* o, float* lse, bf16_t* o_lo, const uint32_t* amax,
+                     hipStream_t st);
 template <typename TG>
 void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* kt,
                     const f16_t* vn, const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
-                    const QPage* qpages, const int32_t* order, const Tile* tiles, TG* dq, const uint32_t* amax,
-                    hipStream_t st);
+                    const QPage* qpages, const int32_t* order, const Tile* tiles, const int32_t* tile_mask,
+                    const uint64_t* masks, TG* dq, const uint32_t* amax, hipStream_t st);
 template <typename TG>
 void launch_dkdv_mfma(const LaunchShape& s, int64_t n_pairs, const f16_t* qn, const f16_t* kn, const f16_t* vn,
                       const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
                       const int32_t* pair_order, const int32_t* pairs, const int64_t* pair_off, const KStep* psteps,
-                      const int32_t* page_nrows, TG* dk, TG* dv, const uint32_t* amax, hipStream_t st);
+                      const KMask* pmasks, const uint64_t* masks, const int32_t* page_nrows, TG* dk, TG* dv,
+                      const uint32_t* amax, hipStream_t st);
 template <typename T>
 void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,
                        const QPage* qpages, const int32_t* order, const Tile* tiles, T* o, float* lse, T* o_lo,

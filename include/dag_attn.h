@@ -209,9 +209,10 @@ typedef struct {
                        /* head_dim == 128 and Hq == 4 Hkv the products run on MFMA with     */
                        /* fp16 operands: q, k, v and dO are each first scaled by the power  */
                        /* of two that puts their tensor's largest |x| (over valid rows) in  */
-                       /* [1, 2), undone exactly in the outputs, so no finite bf16 input     */
-                       /* overflows; an element below 2^-14 of its tensor's maximum keeps   */
-                       /* fp16's subnormal spacing (2^-24 of that maximum)                   */
+                       /* [2^14, 2^15) for q and k, [1, 2) for v and dO, undone exactly in  */
+                       /* the outputs, so no finite bf16 input overflows.  An element       */
+                       /* below 2^-28 (q, k) or 2^-14 (v, dO) of its tensor's maximum keeps */
+                       /* fp16's subnormal spacing (2^-38 or 2^-24 of that maximum)          */
                        /* DAG_DTYPE_FP32: fp32 throughout                                   */
   int32_t grad_dtype;  /* element type of dq, dk, dv: DAG_DTYPE_BF16 or DAG_DTYPE_FP32;    */
                        /* must be FP32 when dtype is FP32.  Large shared-row gradients     */

@@ -34,13 +34,13 @@ def dpa():
 
 
 def _run(dpa, spec, q, k, v, do, hq, hkv, d, dtype, rope=10000.0, transitive=None, shuffle=0, bwd=True,
-         scale=0.0, grad="fp32", view="mounted"):
+         scale=0.0, grad="fp32", view="mounted", pack=False):
     """Token-major CPU tensors in, token-major CPU float64 results out (via the row layout).
 
     Gradients come back in fp32 by default: in these small DAGs a shared row's dK/dV reaches
     magnitudes (~11) where bf16 storage alone is 0.03 away from the exact value.
     """
-    plan = dpa.Plan(spec, transitive=transitive, page_shuffle=shuffle, view=view)
+    plan = dpa.Plan(spec, transitive=transitive, page_shuffle=shuffle, view=view, pack=pack)
     p = dpa.AttnParams(hq, hkv, d, dtype, scale=scale, rope_base=rope, grad_dtype=grad)
     tdt = p.torch_dtype
     rows = lambda x: dpa.to_rows(plan, x.to(DEV, tdt), fill=float("nan"))
@@ -314,6 +314,28 @@ def test_wide_range_operands(dpa, which):
             f"{which} {n}: max {err.max():.3g} mean {err.mean():.3g} (max|ref| {bar:.3g})"
 
 
+def test_forward_with_huge_logits(dpa):
+    """Outlier rows in q and k together (2^16..2^17, no rotation): logits reach ~1e9, past
+    where the forward's fused exponent form would overflow; the forward switches to the exact
+    form there, and o and lse come out finite and within the scaled bar.  (The backward is
+    not compared: the fp32 lse of the interface resolves such logits only to about +-32.)"""
+    spec = _mini3(seed=21)
+    tr = bool(spec.meta.get("transitive", True))
+    q, k, v, do = _inputs(spec, 16, 4, 128, 909, "bf16")
+    rng = np.random.default_rng(909)
+    q = _outlier_rows(q, rng, 6, 16.0, 17.0)
+    k = _outlier_rows(k, rng, 6, 16.0, 17.0)
+    got, _ = _run(dpa, spec, q, k, v, do, 16, 4, 128, "bf16", transitive=tr, rope=0.0, bwd=False)
+    ref = _ref(spec, q, k, v, do, 16, 4, transitive=tr, rope=0.0, bwd=False)
+    assert np.abs(ref["lse"]).max() > 1e8
+    for n in ("o", "lse"):
+        assert np.isfinite(got[n]).all(), n
+        bar = max(1.0, float(np.abs(ref[n]).max()))
+        err = np.abs(got[n] - ref[n])
+        assert err.max() <= BF16_MAX * bar and err.mean() <= BF16_MEAN * bar, \
+            f"{n}: max {err.max():.3g} mean {err.mean():.3g} (max|ref| {bar:.3g})"
+
+
 def _mid_commander_workers():
     # one commander-worker episode small enough for the flat oracle: a 1,024-token
     # commander, 8 workers of 4,096 own tokens, worker w reading at 1,536 + 256 w the
@@ -430,7 +452,7 @@ def _heavy_keys(rs, dag, rng, hi, n_cand=150):
 
 
 def _full_case(dpa, spec, seed, bwd, n_rows=24, n_keys=6, max_readers=96, view="mounted", heavy_hi=16000,
-               transitive=None):
+               transitive=None, pack=False):
     """The workload at full size, in the benchmark's launch configuration (bf16 tensors and
     gradients).  Compared with the oracle: o, lse and dq on sampled query rows (random tokens
     plus the first and last token of a few nodes), and dK/dV on sampled keys -- a few
@@ -438,7 +460,7 @@ def _full_case(dpa, spec, seed, bwd, n_rows=24, n_keys=6, max_readers=96, view="
     heavily read keys (an inner node's and a mounted span's, one KV head each) whose
     gradient sums up to ``heavy_hi`` reader rows."""
     tr = bool(spec.meta.get("transitive", True)) if transitive is None else transitive
-    plan = dpa.Plan(spec, transitive=tr, view=view)
+    plan = dpa.Plan(spec, transitive=tr, view=view, pack=pack)
     p = dpa.AttnParams(16, 4, 128, "bf16")          # the benchmark's configuration (bf16 gradients)
     C = plan.rows
     q = synth.normal((C, 16, 128), seed, 1, DEV, torch.bfloat16)
@@ -510,6 +532,64 @@ def test_full_size_views_sampled(dpa, view):
     torch.cuda.empty_cache()
 
 
+# ---------------------------------------------------------------- packed page layouts
+
+
+@pytest.mark.parametrize("name", ["mini_short", "mini3", "mini4", "tiny"])
+def test_packed_pages_small(dpa, name):
+    """Nodes sharing pages (per-tile visibility masks): all five tensors against the flat oracle."""
+    spec = SMALL[name]()
+    tr = bool(spec.meta.get("transitive", True))
+    print(f"packed {name}", flush=True)
+    q, k, v, do = _inputs(spec, 16, 4, 128, 6000 + len(name), "bf16")
+    got, plan = _run(dpa, spec, q, k, v, do, 16, 4, 128, "bf16", transitive=tr, pack=True)
+    assert plan.info["pack_pages"] == 1
+    ref = _ref(spec, q, k, v, do, 16, 4, transitive=tr)
+    _assert_close(got, ref, "bf16", tag=f"packed {name}")
+
+
+@pytest.mark.parametrize("seed", [3, 4])
+def test_packed_pages_random_reads(dpa, seed):
+    """Random DAGs whose reads reach nodes later in depth-first order (a mounted key can then sit
+    above its reader in the same page), transitive closure on and off."""
+    rng = np.random.default_rng(seed)
+    spec = synth.random_tiny_dag(rng, n_nodes=14, max_len=40, p_mount=0.9, max_mounts=2)
+    q, k, v, do = _inputs(spec, 16, 4, 128, 70 + seed, "bf16")
+    for tr in (True, False):
+        got, _ = _run(dpa, spec, q, k, v, do, 16, 4, 128, "bf16", transitive=tr, pack=True)
+        ref = _ref(spec, q, k, v, do, 16, 4, transitive=tr)
+        _assert_close(got, ref, "bf16", tag=f"packed random {seed} transitive={tr}")
+
+
+def test_packed_pages_gdn_and_refusals(dpa):
+    """The gated delta rule reads rows through the plan's maps: on a packed plan its outputs and
+    gradients are bitwise those of the unpacked plan.  The generic attention path and the
+    convolution refuse packed plans."""
+    spec = SMALL["mini_short"]()
+    H = 2
+    ins = synth.tensors.gdn_inputs(spec.n_tokens, H, 128, 128, 31, dtype=torch.bfloat16, decay_scale=0.2)
+    outs = []
+    for pack in (False, True):
+        plan = dpa.Plan(spec, gdn_chunk=64, pack=pack)
+        p = dpa.GdnParams(H, grad_dtype="fp32")
+        rows = lambda x: dpa.to_rows(plan, x.to(DEV), fill=float("nan"))
+        qr, kr, vr, br, ar, dr = (rows(x) for x in ins)
+        o = dpa.gdn_fwd(plan, p, qr, kr, vr, br, ar)
+        g = dpa.gdn_bwd(plan, p, qr, kr, vr, br, ar, dr)
+        torch.cuda.synchronize()
+        outs.append([dpa.from_rows(plan, t).cpu() for t in (o, *g)])
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    plan = dpa.Plan(spec, pack=True)
+    q, k, v, _ = (dpa.to_rows(plan, x.to(DEV)) for x in _inputs(spec, 4, 2, 64, 5, "bf16"))
+    with pytest.raises(dpa.DagError) as e:
+        dpa.attn_fwd(plan, dpa.AttnParams(4, 2, 64, "bf16"), q, k, v)
+    assert e.value.code == "UNSUPPORTED"
+    with pytest.raises(dpa.DagError) as e:
+        dpa.conv_workspace_bytes(plan, dpa.ConvParams(64))
+    assert e.value.code == "UNSUPPORTED"
+
+
 @pytest.mark.parametrize("which", ["w2", "w4", "w3", "w3t", "short"])
 def test_full_size_sampled(dpa, which):
     # w3t: the 16-tree workload with transitive reads (Octopus Sec. 3.3 item 1), the
@@ -523,4 +603,12 @@ def test_full_size_sampled(dpa, which):
     # mid-size episode instead
     _full_case(dpa, spec, seed=seed, bwd=(which != "w2"), heavy_hi=0 if which == "w4" else 16000,
                transitive=True if which == "w3t" else None)
+    torch.cuda.empty_cache()
+
+
+def test_full_size_short_segments_packed(dpa):
+    # the page-gather diagnostic in the packed layout, as the benchmark's gather record runs it
+    print("full size: short segments, packed pages", flush=True)
+    plan, _ = _full_case(dpa, synth.dags.config3_short_segments(), seed=1017, bwd=True, pack=True)
+    assert plan.info["pack_pages"] == 1
     torch.cuda.empty_cache()
