@@ -47,6 +47,7 @@ struct DeviceTables {
   int32_t* gslot_off = nullptr;
   int32_t* gslot_cons = nullptr;
   int32_t* ground_seq = nullptr;
+  int32_t* gitems = nullptr;
   int32_t* grep_rows = nullptr;
   int32_t* grep_off = nullptr;
   int32_t* grep_tok = nullptr;
@@ -208,7 +209,7 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
            align256(P.page_nrows.size() * 4) + align256(P.gseqs.size() * sizeof(GSeq)) +
            align256(P.grows.size() * 4) + align256(P.gexports.size() * sizeof(GExport)) +
            align256(P.gslot_off.size() * 4) + align256(P.gslot_cons.size() * 4) + align256(P.ground_seq.size() * 4) +
-           align256(P.grep_rows.size() * 4) + align256(P.grep_off.size() * 4) + align256(P.grep_tok.size() * 4) +
+           align256(P.gitems.size() * 4) + align256(P.grep_rows.size() * 4) + align256(P.grep_off.size() * 4) + align256(P.grep_tok.size() * 4) +
            align256(P.grep_slot.size() * 4) + align256(P.conv_prev.size() * 4) +
            align256(P.conv_ext_off.size() * 8) + align256(P.conv_ext.size() * sizeof(ConvExt)) + 256;
   DeviceTables* D = new (std::nothrow) DeviceTables();
@@ -243,6 +244,7 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
   D->gslot_off = dev_take<int32_t>(b, off, P.gslot_off.size());
   D->gslot_cons = dev_take<int32_t>(b, off, P.gslot_cons.size());
   D->ground_seq = dev_take<int32_t>(b, off, P.ground_seq.size());
+  D->gitems = dev_take<int32_t>(b, off, P.gitems.size());
   D->grep_rows = dev_take<int32_t>(b, off, P.grep_rows.size());
   D->grep_off = dev_take<int32_t>(b, off, P.grep_off.size());
   D->grep_tok = dev_take<int32_t>(b, off, P.grep_tok.size());
@@ -275,6 +277,7 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
             put(D->gslot_off, P.gslot_off.data(), P.gslot_off.size() * 4) &&
             put(D->gslot_cons, P.gslot_cons.data(), P.gslot_cons.size() * 4) &&
             put(D->ground_seq, P.ground_seq.data(), P.ground_seq.size() * 4) &&
+            put(D->gitems, P.gitems.data(), P.gitems.size() * 4) &&
             put(D->grep_rows, P.grep_rows.data(), P.grep_rows.size() * 4) &&
             put(D->grep_off, P.grep_off.data(), P.grep_off.size() * 4) &&
             put(D->grep_tok, P.grep_tok.data(), P.grep_tok.size() * 4) &&
@@ -346,13 +349,18 @@ struct GdnWs {
   float* cgrad;
   float* rside;
   float* rbuf;
+  f16_t* tinv;   // per chunk item: (I + A)^{-1} as fp16 high and low parts, and P
+  f16_t* dsend;  // backward, per chunk item of one round: the state gradient at the chunk's end
 };
 
 size_t carve_gdn(const Plan& P, int H, bool bwd, void* base, GdnWs* w) {
   Carve c(base);
   const size_t st = (size_t)H * 128 * 128;
+  const size_t items = (size_t)P.gdn_round_chunks_max * H;
   w->slots = c.take<float>((size_t)P.info.gdn_slots * st);
+  w->tinv = c.take<f16_t>((size_t)P.info.gdn_chunks * H * kGdnTinvHalfs);
   w->states = bwd ? c.take<f16_t>((size_t)P.info.gdn_chunks * 2 * st) : nullptr;
+  w->dsend = bwd ? c.take<f16_t>(items * 128 * 128) : nullptr;
   w->cgrad = bwd ? c.take<float>((size_t)P.gdn_ncgrad * st) : nullptr;
   w->rside = bwd ? c.take<float>(P.grep_rows.size() * H * 256) : nullptr;
   w->rbuf = bwd ? c.take<float>((size_t)P.info.gdn_replay * H * 258) : nullptr;
@@ -371,6 +379,7 @@ GdnShape gdn_shape(const Plan& P, const dag_gdn_params* p) {
   g.rep_rows = D.grep_rows;
   g.rep_off = D.grep_off;
   g.rep_tok = D.grep_tok;
+  g.items = D.gitems;
   g.H = p->n_heads;
   g.scale = p->scale != 0.f ? p->scale : 1.f;
   return g;
@@ -805,10 +814,13 @@ dag_status dag_gdn_fwd(dag_plan* plan, const dag_gdn_params* p, const void* q, c
   const DeviceTables& D = *P.dev;
   {
     Span sp(P, DAG_K_GDN_FWD, stream);
+    // every chunk's T and P at once (a forward that keeps its states keeps these too)
+    launch_gdn_tinv(g, (int)P.info.gdn_chunks, D.gitems, (const bf16_t*)q, (const bf16_t*)k, beta, alpha, w.tinv,
+                    stream);
     for (int r = 0; r < P.info.gdn_rounds; ++r)
       launch_gdn_fwd(g, P.ground_off[r + 1] - P.ground_off[r], D.ground_seq + P.ground_off[r], (const bf16_t*)q,
-                     (const bf16_t*)k, (const bf16_t*)v, beta, alpha, (bf16_t*)o, w.slots, keep ? w.states : nullptr,
-                     stream);
+                     (const bf16_t*)k, (const bf16_t*)v, beta, alpha, w.tinv, (bf16_t*)o, w.slots,
+                     keep ? w.states : nullptr, stream);
     launch_gdn_pad<bf16_t>(P.info.pages, D.page_nrows, (bf16_t*)o, p->n_heads, 128, stream);
   }
   return launched("dag_gdn_fwd");
@@ -835,19 +847,23 @@ dag_status dag_gdn_bwd(dag_plan* plan, const dag_gdn_params* p, const void* q, c
   const DeviceTables& D = *P.dev;
   const int H = p->n_heads;
   const bf16_t *q16 = (const bf16_t*)q, *k16 = (const bf16_t*)k, *v16 = (const bf16_t*)v, *d16 = (const bf16_t*)dO;
-  if (!p->keep_states) {  // otherwise the forward left every chunk's state in ws
+  if (!p->keep_states) {  // otherwise the forward left every chunk's state, T and P in ws
     Span sp(P, DAG_K_GDN_STATES, stream);
+    launch_gdn_tinv(g, (int)P.info.gdn_chunks, D.gitems, q16, k16, beta, alpha, w.tinv, stream);
     for (int r = 0; r < P.info.gdn_rounds; ++r)
       launch_gdn_fwd(g, P.ground_off[r + 1] - P.ground_off[r], D.ground_seq + P.ground_off[r], q16, k16, v16, beta,
-                     alpha, nullptr, w.slots, w.states, stream);
+                     alpha, w.tinv, nullptr, w.slots, w.states, stream);
   }
   auto run = [&](auto* tag) {
     using TG = std::remove_pointer_t<decltype(tag)>;
     Span sp(P, DAG_K_GDN_BWD, stream);
-    for (int r = P.info.gdn_rounds - 1; r >= 0; --r)
-      launch_gdn_bwd<TG>(g, P.ground_off[r + 1] - P.ground_off[r], D.ground_seq + P.ground_off[r], q16, k16, v16,
-                         beta, alpha, d16, w.states, w.cgrad, (TG*)dq, (TG*)dk, (TG*)dv, dbeta, dalpha, w.rside,
-                         w.rbuf, stream);
+    for (int r = P.info.gdn_rounds - 1; r >= 0; --r) {
+      const int item0 = P.gitem_off[r], n_items = P.gitem_off[r + 1] - item0;
+      launch_gdn_bscan(g, P.ground_off[r + 1] - P.ground_off[r], D.ground_seq + P.ground_off[r], item0, q16, k16,
+                       beta, alpha, d16, w.tinv, w.cgrad, w.dsend, stream);
+      launch_gdn_bpar<TG>(g, item0, n_items, q16, k16, v16, beta, alpha, d16, w.states, w.tinv, w.dsend, (TG*)dq,
+                          (TG*)dk, (TG*)dv, dbeta, dalpha, w.rside, w.rbuf, stream);
+    }
     launch_gdn_fixup<TG>(g, (int)P.grep_rows.size(), w.rside, w.rbuf, (TG*)dk, (TG*)dv, dbeta, dalpha, stream);
     launch_gdn_pad<TG>(P.info.pages, D.page_nrows, (TG*)dq, H, 128, stream);
     launch_gdn_pad<TG>(P.info.pages, D.page_nrows, (TG*)dk, H, 128, stream);

@@ -25,11 +25,18 @@
 //         S64 = gamma_63 S0 + (diag(E_63,.) U)^T K
 //     and the backward is the exact derivative of these lines.
 //
-// One work-group (256 threads, 4 waves) owns one (sequence, head) and walks
-// its chunks in order (backward: in reverse).  Dense products run on
-// v_mfma_f32_32x32x16_f16 with fp16 operands staged in LDS (transposed
-// operands through ds_read_b64_tr_b16) and fp32 accumulation; the triangular
-// solves are forward / backward substitution in registers.
+// Only the state carry is serial.  Per round, every chunk of every sequence is an
+// independent work item for the state-independent part: A, P = scale lower(E o QK^T)
+// and T = (I + A)^{-1} (gdn_tinv_kernel, one work-group per chunk and head: forward
+// substitution on the identity).  The serial kernels, one work-group (256 threads,
+// 4 waves) per (sequence, head), then walk the chunks with products only: the
+// solves become U = T R and dR = T^T dU on the matrix cores, with T as an fp16
+// high part plus an fp16 low part (T - high), so the product keeps about 22 bits of
+// T.  The backward's serial kernel carries only the state gradient and leaves each
+// chunk's end-state gradient behind; the rest of the backward (every input gradient)
+// is again one work-group per chunk and head (gdn_bpar_kernel).  Dense products run
+// on v_mfma_f32_32x32x16_f16 with fp16 operands staged in LDS (transposed operands
+// through ds_read_b64_tr_b16) and fp32 accumulation.
 #include <hip/hip_runtime.h>
 
 #include "gdn.hpp"
@@ -288,6 +295,7 @@ __device__ __forceinline__ void bwd_fetch_rows(const ChunkIn& ci, int j0, int ti
   if (tid < kB) nx.row = j0 + tid < ci.n_tok ? ci.rows[j0 + tid] : -1;
 }
 
+template <bool kV>
 __device__ __forceinline__ void bwd_fetch_data(const ChunkIn& ci, int j0, const bf16_t* __restrict__ k,
                                                const bf16_t* __restrict__ q, const bf16_t* __restrict__ dO,
                                                const bf16_t* __restrict__ v, const float* __restrict__ beta,
@@ -301,7 +309,7 @@ __device__ __forceinline__ void bwd_fetch_data(const ChunkIn& ci, int j0, const 
       const int64_t base = ((int64_t)nx.r4[m] * H + head) * kD + (tid & 15) * 8;
       nx.k4[m] = *reinterpret_cast<const uint4*>(k + base);
       nx.q4[m] = *reinterpret_cast<const uint4*>(q + base);
-      nx.v4[m] = *reinterpret_cast<const uint4*>(v + base);
+      if (kV) nx.v4[m] = *reinterpret_cast<const uint4*>(v + base);
       if (j >= ci.n_replay) nx.d4[m] = *reinterpret_cast<const uint4*>(dO + base);
     }
   }
@@ -315,9 +323,10 @@ __device__ __forceinline__ void bwd_fetch_data(const ChunkIn& ci, int j0, const 
   }
 }
 
-// Make the fetched chunk current: K, Q, dO, V rows as fp16 in LDS, row numbers, beta,
-// alpha and the cumulative log decay.  Tokens past the sequence's end are zero (beta
-// = 0, log alpha = 0), which makes them inert in every product.
+// Make the fetched chunk current: K, Q, dO (and V if kV) rows as fp16 in LDS, row
+// numbers, beta, alpha and the cumulative log decay.  Tokens past the sequence's end are
+// zero (beta = 0, log alpha = 0), which makes them inert in every product.
+template <bool kV>
 __device__ __forceinline__ void bwd_commit(const BwdRegs& nx, f16_t* Kr, f16_t* Qr, f16_t* dOr, f16_t* Vr, int* rw,
                                            float* gs, float* bs, float* al, int tid) {
 #pragma unroll
@@ -326,7 +335,7 @@ __device__ __forceinline__ void bwd_commit(const BwdRegs& nx, f16_t* Kr, f16_t* 
     *reinterpret_cast<f16x8*>(Kr + t * LDK + c8) = bf8_to_h8(nx.k4[m]);
     *reinterpret_cast<f16x8*>(Qr + t * LDK + c8) = bf8_to_h8(nx.q4[m]);
     *reinterpret_cast<f16x8*>(dOr + t * LDK + c8) = bf8_to_h8(nx.d4[m]);
-    *reinterpret_cast<f16x8*>(Vr + t * LDK + c8) = bf8_to_h8(nx.v4[m]);
+    if (kV) *reinterpret_cast<f16x8*>(Vr + t * LDK + c8) = bf8_to_h8(nx.v4[m]);
   }
   if (tid < kB) {
     rw[tid] = nx.row;
@@ -342,8 +351,9 @@ __device__ __forceinline__ void bwd_commit(const BwdRegs& nx, f16_t* Kr, f16_t* 
   }
 }
 
-// Triangular solves with the unit-lower matrix I + A (A strictly lower), for
-// the 128 columns of an [64][.] tile, by all 256 threads: lanes l and l ^ 32 of
+// Triangular solve with the unit-lower matrix I + A (A strictly lower), for
+// the 128 columns of an [64][.] tile, by all 256 threads (or its first 64 columns by
+// the first 128): lanes l and l ^ 32 of
 // wave w share column c = 32 w + (l & 31), and lane half h = l >> 5 takes target
 // rows 8 h .. 8 h + 7 of each 16-row block in the updates from the solved blocks
 // (a runtime loop over their rows).  The two halves then swap their partial sums
@@ -419,48 +429,125 @@ __device__ __forceinline__ void solve_lower(const float* __restrict__ At, TX* __
   }
 }
 
-// (I + A)^T Y = D, left-looking: y_t = d_t - sum_{i > t} A[i][t] y_i, a dot
-// product with a contiguous run of row t of At.  Y overwrites D in `x`;
-// `emit(t, c, y_t)` sees every solved value once (the lane half that owns row t,
-// after the block's substitution, off its dependent chain).  Reads are grouped as
-// in solve_lower; the additions keep their fixed order.
-template <typename TX, typename Emit>
-__device__ __forceinline__ void solve_upper_t(const float* __restrict__ At, TX* __restrict__ x, int ldx, int tid,
-                                              Emit emit) {
-  const int c = 32 * (tid >> 6) + (tid & 31), h = (tid >> 5) & 1;
-  for (int b = 3; b >= 0; --b) {
-    float part[8], y[16];
+// ---------------------------------------------------------------------------------
+// (I + A)^{-1} and P of every chunk of one round.  Grid: (round's chunk items) x H.
+// Per (item, head), kGdnTinvHalfs fp16 values: T's high part, T's low part (T minus the
+// high part, rounded) and P, each [64][64] row-major ([t][i]).
+// ---------------------------------------------------------------------------------
+constexpr int kTinv = 3 * kB * kB;  // halfs per (item, head)
+
+__global__ __launch_bounds__(256) void gdn_tinv_kernel(const GSeq* __restrict__ seqs,
+                                                       const int32_t* __restrict__ items,
+                                                       const int32_t* __restrict__ grows,
+                                                       const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
+                                                       const float* __restrict__ beta,
+                                                       const float* __restrict__ alpha, f16_t* __restrict__ tinv,
+                                                       int H, float scale) {
+  __shared__ __attribute__((aligned(16))) f16_t Kr[kB * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t Qr[kB * LDK];
+  __shared__ __attribute__((aligned(16))) float Ar[kB * LDA];  // A^T
+  __shared__ float gs[kB], bs[kB];
+  float* Xr = reinterpret_cast<float*>(Kr);  // after the products: the identity, then T ([t][j])
+  static_assert(kB * LDA * 4 <= kB * LDK * 2, "the solve tile fits the K tile");
+  __shared__ int rw[kB];
+  const int head = blockIdx.x % H;
+  const int item = blockIdx.x / H;
+  const GSeq sq = seqs[items[2 * item]];
+  const int j0 = items[2 * item + 1] * kB;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  if (tid < kB) {
+    const int j = j0 + tid;
+    int row = -1;
+    float b = 0.f, a = 1.f;
+    if (j < sq.n_tok) {
+      row = grows[sq.tok_off + j];
+      b = beta[(int64_t)row * H + head];
+      a = alpha[(int64_t)row * H + head];
+    }
+    rw[tid] = row;
+    bs[tid] = b;
+    float la = logf(a);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) part[j] = (float)x[(16 * b + 8 * h + j) * ldx + c];
-    for (int ib = b + 1; ib < 4; ++ib) {
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(la, off, 64);
+      if (tid >= off) la += y;
+    }
+    gs[tid] = la;
+  }
+  __syncthreads();
 #pragma unroll
-      for (int m = 0; m < 16; ++m) y[m] = (float)x[(16 * ib + m) * ldx + c];
+  for (int m = 0; m < 4; ++m) {
+    const int t = (tid >> 4) + 16 * m, c8 = (tid & 15) * 8;
+    const int row = rw[t];
+    uint4 k4 = make_uint4(0, 0, 0, 0), q4 = make_uint4(0, 0, 0, 0);
+    if (row >= 0) {
+      const int64_t base = ((int64_t)row * H + head) * kD + c8;
+      k4 = *reinterpret_cast<const uint4*>(k + base);
+      q4 = *reinterpret_cast<const uint4*>(q + base);
+    }
+    *reinterpret_cast<f16x8*>(Kr + t * LDK + c8) = bf8_to_h8(k4);
+    *reinterpret_cast<f16x8*>(Qr + t * LDK + c8) = bf8_to_h8(q4);
+  }
+  __syncthreads();
+  f16_t* dst = tinv + ((int64_t)item * H + head) * kTinv;
+  {
+    // A = strict_lower(diag(beta) E o KK^T) (kept transposed) and P = scale lower(E o QK^T)
+    const int bm = wave >> 1, bn = wave & 1;
+    f32x16 kk = zero16(), qk = zero16();
+    if (bm >= bn) {
 #pragma unroll
-      for (int j0 = 0; j0 < 8; j0 += 4) {
-        float a[4][16];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) at_row<16>(At, 16 * b + 8 * h + j0 + u, 16 * ib, a[u]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-#pragma unroll
-          for (int m = 0; m < 16; ++m) part[j0 + u] = fmaf(-a[u][m], y[m], part[j0 + u]);
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 b = frag_n(Kr, LDK, 32 * bn, 16 * s, lane);
+        kk = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), b, kk);
+        qk = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), b, qk);
       }
     }
-    float acc[16];
-    join_halves(part, h, acc);
-    float a[2][16];
-    at_row<16>(At, 16 * b + 15, 16 * b, a[1]);
+    const int i = 32 * bn + l32;
 #pragma unroll
-    for (int j = 15; j >= 0; --j) {
-      if (j > 0) at_row<16>(At, 16 * b + j - 1, 16 * b, a[(j - 1) & 1]);
-#pragma unroll
-      for (int m = j + 1; m < 16; ++m) acc[j] = fmaf(-a[j & 1][m], acc[m], acc[j]);
-      x[(16 * b + j) * ldx + c] = (TX)acc[j];
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * bm + acc_row(r, hi);
+      const float e = i <= t ? __expf(gs[t] - gs[i]) : 0.f;
+      Ar[i * LDA + t] = i < t ? bs[t] * e * kk[r] : 0.f;
+      dst[2 * kB * kB + t * kB + i] = (f16_t)(scale * e * qk[r]);
     }
-#pragma unroll
-    for (int j = 0; j < 16; ++j)
-      if ((j >> 3) == h) emit(16 * b + j, c, acc[j]);
   }
+  __syncthreads();
+  for (int idx = tid; idx < kB * kB; idx += 256) Xr[(idx >> 6) * LDA + (idx & 63)] = (idx >> 6) == (idx & 63) ? 1.f : 0.f;
+  __syncthreads();
+  // T = (I + A)^{-1}: the solve on the identity, 64 columns (two waves, two lanes a column)
+  if (tid < 128) solve_lower<float, false>(Ar, Xr, LDA, nullptr, tid);
+  __syncthreads();
+  for (int idx = tid; idx < kB * kB; idx += 256) {
+    const float x = Xr[(idx >> 6) * LDA + (idx & 63)];
+    const f16_t h = (f16_t)x;
+    dst[idx] = h;
+    dst[kB * kB + idx] = (f16_t)(x - (float)h);
+  }
+}
+
+// The chunk's T high / low parts and P, fetched into registers one chunk ahead
+// (two 16-byte pieces of each tile a thread) and committed to LDS tiles [64][LDP].
+struct TinvRegs {
+  uint4 h0, h1, l0, l1, p0, p1;
+};
+__device__ __forceinline__ void fetch_tinv(const f16_t* __restrict__ src, int tid, TinvRegs& nx) {
+  const uint4* s4 = reinterpret_cast<const uint4*>(src);
+  nx.h0 = s4[tid];
+  nx.h1 = s4[tid + 256];
+  nx.l0 = s4[512 + tid];
+  nx.l1 = s4[512 + tid + 256];
+  nx.p0 = s4[1024 + tid];
+  nx.p1 = s4[1024 + tid + 256];
+}
+__device__ __forceinline__ void commit_tinv(const TinvRegs& nx, f16_t* Th, f16_t* Tl, f16_t* Pr, int tid) {
+  // piece tid (+ 256) of a [64][64] tile: row (tid >> 3) (+ 32), columns 8 (tid & 7) ..
+  const int o0 = (tid >> 3) * LDP + 8 * (tid & 7), o1 = o0 + 32 * LDP;
+  *reinterpret_cast<uint4*>(Th + o0) = nx.h0;
+  *reinterpret_cast<uint4*>(Th + o1) = nx.h1;
+  *reinterpret_cast<uint4*>(Tl + o0) = nx.l0;
+  *reinterpret_cast<uint4*>(Tl + o1) = nx.l1;
+  *reinterpret_cast<uint4*>(Pr + o0) = nx.p0;
+  *reinterpret_cast<uint4*>(Pr + o1) = nx.p1;
 }
 
 // ---------------------------------------------------------------------------------
@@ -473,22 +560,30 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
     const GSeq* __restrict__ seqs, const int32_t* __restrict__ order, const int32_t* __restrict__ grows,
     const GExport* __restrict__ exports, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ alpha,
-    bf16_t* __restrict__ o, float* __restrict__ slots, f16_t* __restrict__ states, int H, float scale) {
+    const f16_t* __restrict__ tinv, bf16_t* __restrict__ o, float* __restrict__ slots, f16_t* __restrict__ states,
+    int H, float scale) {
   __shared__ __attribute__((aligned(16))) f16_t Kr[kB * LDK];
   __shared__ __attribute__((aligned(16))) f16_t Qr[kB * LDK];
   __shared__ __attribute__((aligned(16))) f16_t Sh[kD * LDK];
   __shared__ __attribute__((aligned(16))) f16_t Pr[kB * LDP];
   __shared__ __attribute__((aligned(16))) f16_t Ur[kB * LDK];
-  __shared__ __attribute__((aligned(16))) float Ar[kB * LDA];  // A^T
-  __shared__ __attribute__((aligned(16))) float Rr[kB * LDR];
+  __shared__ __attribute__((aligned(16))) f16_t Th[kB * LDP];
+  __shared__ __attribute__((aligned(16))) f16_t Tl[kB * LDP];
+  // V rows (fp32, exact) in; then R as fp16 high and low parts, two [64][LDK] tiles
+  __shared__ __attribute__((aligned(16))) float Rr[(2 * kB * LDK) / 2];
   __shared__ float gs[kB], bs[kB];
   __shared__ int rw[kB], rwn[kB];
+  static_assert(kB * LDR <= 2 * kB * LDK / 2, "the V rows fit the R tiles");
+  f16_t* Rh = reinterpret_cast<f16_t*>(Rr);
+  f16_t* Rl = Rh + kB * LDK;
 
   const int head = blockIdx.x % H;
   const GSeq sq = seqs[order[blockIdx.x / H]];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
   const int nch = (sq.n_tok + kB - 1) / kB;
   const ChunkIn ci{grows + sq.tok_off, sq.n_tok, sq.n_replay};
+  const f16_t* tinv_seq = tinv + (int64_t)sq.item0 * H * kTinv + (int64_t)head * kTinv;
+  const int64_t tinv_step = (int64_t)H * kTinv;
 
   f32x16 S[4];
   if (sq.init_slot >= 0) {
@@ -508,6 +603,11 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
 
   // chunk 0 is fetched up front; chunk c + 1's inputs are fetched during chunk c
   ChunkRegs nx;
+  if (nch > 0) {
+    TinvRegs t0;
+    fetch_tinv(tinv_seq, tid, t0);
+    commit_tinv(t0, Th, Tl, Pr, tid);
+  }
   fetch_rows(ci, 0, beta, alpha, H, head, tid, nx);
   if (tid < kB) rwn[tid] = nx.row;
   __syncthreads();
@@ -516,35 +616,17 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
-    // opaque thread indices inside the chunk loop (see the backward kernel)
+    // opaque thread indices inside the chunk loop (see the backward kernels)
     int tid_o = threadIdx.x;
     asm volatile("" : "+v"(tid_o));
     const int tid = tid_o, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
     const int j0 = c * kB;
     const bool has_next = c + 1 < nch;
     if (has_next) fetch_rows(ci, j0 + kB, beta, alpha, H, head, tid, nx);
+    const int cc = 32 * wave + l32;
+    TinvRegs tx;
 
-    // -- products with K, Q and the chunk's starting state --------------------------
-    {
-      const int bm = wave >> 1, bn = wave & 1;
-      f32x16 kk = zero16(), qk = zero16();
-      if (bm >= bn) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const f16x8 b = frag_n(Kr, LDK, 32 * bn, 16 * s, lane);
-          kk = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), b, kk);
-          if (kOut) qk = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), b, qk);
-        }
-      }
-      const int i = 32 * bn + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * bm + acc_row(r, hi);
-        const float e = i <= t ? __expf(gs[t] - gs[i]) : 0.f;
-        Ar[i * LDA + t] = i < t ? bs[t] * e * kk[r] : 0.f;
-        if (kOut) Pr[t * LDP + i] = (f16_t)(scale * e * qk[r]);
-      }
-    }
+    // -- R = diag(beta) (V - diag(gamma) K S0^T), split into fp16 high and low parts ------
     {
       f32x16 ks[2];
 #pragma unroll
@@ -555,21 +637,52 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
 #pragma unroll
         for (int bm = 0; bm < 2; ++bm) ks[bm] = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), b, ks[bm]);
       }
-      const int cc = 32 * wave + l32;
 #pragma unroll
       for (int bm = 0; bm < 2; ++bm)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int t = 32 * bm + acc_row(r, hi);
-          Rr[t * LDR + cc] = bs[t] * (Rr[t * LDR + cc] - __expf(gs[t]) * ks[bm][r]);  // V in, R out
+          ks[bm][r] = bs[t] * (Rr[t * LDR + cc] - __expf(gs[t]) * ks[bm][r]);  // V in, R out
+        }
+      if (tid < kB) rwn[tid] = has_next ? nx.row : -1;
+      __syncthreads();  // every V row read: the R tiles overwrite them
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int t = 32 * bm + acc_row(r, hi);
+          const f16_t h = (f16_t)ks[bm][r];
+          Rh[t * LDK + cc] = h;
+          Rl[t * LDK + cc] = (f16_t)(ks[bm][r] - (float)h);
         }
     }
-    if (tid < kB) rwn[tid] = has_next ? nx.row : -1;
-    __syncthreads();
     if (has_next) fetch_kqv(rwn, k, q, v, H, head, tid, nx);
+    __syncthreads();
 
-    // -- U = (I + A)^{-1} R  (only the state is live across the solve) ------------------
-    solve_lower<float, true>(Ar, Rr, LDR, Ur, tid);
+    // -- U = (I + A)^{-1} R = T R: T_hi R_hi + T_hi R_lo + T_lo R_hi ---------------------------
+    {
+      f32x16 u[2];
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm) u[bm] = zero16();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 bh = frag_t(Rh, LDK, 16 * s, 32 * wave, lane);
+        const f16x8 bl = frag_t(Rl, LDK, 16 * s, 32 * wave, lane);
+#pragma unroll
+        for (int bm = 0; bm < 2; ++bm) {
+          const f16x8 ah = frag_n(Th, LDP, 32 * bm, 16 * s, lane);
+          u[bm] = mfma(ah, bh, u[bm]);
+          u[bm] = mfma(ah, bl, u[bm]);
+          u[bm] = mfma(frag_n(Tl, LDP, 32 * bm, 16 * s, lane), bh, u[bm]);
+        }
+      }
+#pragma unroll
+      for (int bm = 0; bm < 2; ++bm)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) Ur[(32 * bm + acc_row(r, hi)) * LDK + cc] = (f16_t)u[bm][r];
+    }
+    // the next chunk's T and P (issued here, where the R and U registers are free)
+    if (has_next) fetch_tinv(tinv_seq + (c + 1) * tinv_step, tid, tx);
     __syncthreads();
 
     // -- outputs: O = scale diag(gamma) Q S0^T + (scale E o QK) U -------------------------
@@ -602,6 +715,10 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
           if (j >= sq.n_replay && j < sq.n_tok)
             o[((int64_t)rw[t] * H + head) * kD + 32 * wave + l32] = f2bf(acc_o[bm][r]);
         }
+    }
+    if (has_next) {  // T and P of this chunk are read: the next chunk's replace them
+      __syncthreads();
+      commit_tinv(tx, Th, Tl, Pr, tid);
     }
 
     // -- state update: S <- gamma_63 S + (diag(E_63,.) U)^T K ------------------------------
@@ -641,60 +758,55 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
 }
 
 // ---------------------------------------------------------------------------------
-// Backward: one round, sequences in any order; chunks in reverse.
+// Backward, serial part: one round, sequences in any order, chunks in reverse.  Carries
+// only the state gradient dS (fp32, registers): at chunk c it is the gradient of the
+// chunk's end state (consumers' initial-state gradients added at exported boundaries),
+// saved as fp16 [dv][dk] for the per-chunk kernel; then
+//   dU = diag(E_63,.) K dS^T + P^T dO,   dR = T^T dU,
+//   dS <- gamma_63 dS + scale (diag(gamma) dO)^T Q - (diag(beta gamma) dR)^T K.
+// At the sequence's start dS is its initial-state gradient.
 // ---------------------------------------------------------------------------------
-template <typename TG>
-__global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
+__global__ __launch_bounds__(256, 1) void gdn_bscan_kernel(
     const GSeq* __restrict__ seqs, const int32_t* __restrict__ order, const int32_t* __restrict__ grows,
     const GExport* __restrict__ exports, const int32_t* __restrict__ slot_off, const int32_t* __restrict__ slot_cons,
-    const int32_t* __restrict__ rep_slot, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
-    const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ alpha,
-    const bf16_t* __restrict__ dO, const f16_t* __restrict__ states, float* __restrict__ cgrad,
-    TG* __restrict__ dq, TG* __restrict__ dk, TG* __restrict__ dv, float* __restrict__ dbeta,
-    float* __restrict__ dalpha, float* __restrict__ rside, float* __restrict__ rbuf, int H, float scale) {
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ beta,
+    const float* __restrict__ alpha, const bf16_t* __restrict__ dO, const f16_t* __restrict__ tinv,
+    float* __restrict__ cgrad, f16_t* __restrict__ dsend, int round_item0, int H, float scale) {
   __shared__ __attribute__((aligned(16))) f16_t dSh[kD * LDK];
   __shared__ __attribute__((aligned(16))) f16_t Kr[kB * LDK];
   __shared__ __attribute__((aligned(16))) f16_t Qr[kB * LDK];
   __shared__ __attribute__((aligned(16))) f16_t dOr[kB * LDK];
-  __shared__ __attribute__((aligned(16))) f16_t Ur[kB * LDK];   // R, then U
   __shared__ __attribute__((aligned(16))) f16_t dRr[kB * LDK];  // dU, then dR
-  __shared__ __attribute__((aligned(16))) f16_t Pr[kB * LDP];   // scale E o QK, then dP~
-  __shared__ __attribute__((aligned(16))) float Ar[kB * LDA];   // A^T, then dKk (fp16 [64][LDP])
+  __shared__ __attribute__((aligned(16))) f16_t Pr[kB * LDP];
+  __shared__ __attribute__((aligned(16))) f16_t Th[kB * LDP];
+  __shared__ __attribute__((aligned(16))) f16_t Tl[kB * LDP];
   __shared__ float gs[kB], bs[kB], al[kB];
   __shared__ int rw[kB];
-  // where row t's gradients go: 0 nowhere (past the sequence), 1 the replay buffer,
-  // 2 the side buffer of a replayed row, 3 its own dk / dv row; with the base offset
-  __shared__ int dst_kind[kB];
-  __shared__ int64_t dst_off[kB];
-  __shared__ float red_dg[4][kB], red_g[4][kB], red_b[4][kB], red_e[4][kB], red_s[4], red_v[kB];
 
   const int head = blockIdx.x % H;
   const GSeq sq = seqs[order[blockIdx.x / H]];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
   const int nch = (sq.n_tok + kB - 1) / kB;
   const ChunkIn ci{grows + sq.tok_off, sq.n_tok, sq.n_replay};
-  f16_t* Kk = reinterpret_cast<f16_t*>(Ar);
-  const int bm = wave >> 1, bn = wave & 1;  // this wave's 32x32 block of a 64x64 matrix
+  const f16_t* tinv_seq = tinv + (int64_t)sq.item0 * H * kTinv + (int64_t)head * kTinv;
+  const int64_t tinv_step = (int64_t)H * kTinv;
 
   f32x16 D[4];  // dS: dv rows 32 wave .., four dk blocks
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) D[nb] = zero16();
   int ex = sq.exp_off + sq.exp_cnt - 1;
   BwdRegs nx;
+  TinvRegs tx;
   if (nch > 0) {
     bwd_fetch_rows(ci, (nch - 1) * kB, tid, nx);
-    bwd_fetch_data(ci, (nch - 1) * kB, k, q, dO, v, beta, alpha, H, head, tid, nx);
+    bwd_fetch_data<false>(ci, (nch - 1) * kB, k, q, dO, nullptr, beta, alpha, H, head, tid, nx);
+    fetch_tinv(tinv_seq + (nch - 1) * tinv_step, tid, tx);
   }
 
   for (int c = nch - 1; c >= 0; --c) {
-    // The thread's indices, opaque to the compiler inside the chunk loop: otherwise it
-    // hoists hundreds of LDS fragment addresses out of the loop and spills them to
-    // scratch (or parks them in AGPRs), reloading them every chunk; recomputing them
-    // costs a few VALU ops.
     int tid_o = threadIdx.x;
     asm volatile("" : "+v"(tid_o));
     const int tid = tid_o, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
-    const int bm = wave >> 1, bn = wave & 1;
     const int j0 = c * kB;
     // -- consumers' initial-state gradients enter at exported boundaries ----------------
     if (ex >= sq.exp_off && exports[ex].chunk == c + 1) {
@@ -708,85 +820,26 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
       }
       --ex;
     }
+    {
+      f16_t* dst = dsend + ((int64_t)(sq.item0 - round_item0 + c) * H + head) * kD * kD;
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32] = (f16_t)D[nb][r];
+    }
     state_to_lds(D, dSh, wave, lane);
-    bwd_commit(nx, Kr, Qr, dOr, dRr, rw, gs, bs, al, tid);
-    if (c > 0) bwd_fetch_rows(ci, j0 - kB, tid, nx);
-    if (tid < kB) {  // each row's destination, looked up once per chunk, not per element
-      const int t = tid, row = rw[t], j = j0 + t;
-      const int rs = row >= 0 ? rep_slot[row] : -1;
-      int kind;
-      int64_t off;
-      if (j >= sq.n_tok) {
-        kind = 0;
-        off = 0;
-      } else if (j < sq.n_replay) {
-        kind = 1;
-        off = ((int64_t)(sq.rep_off + j) * H + head) * kRep;
-      } else if (rs >= 0) {
-        kind = 2;
-        off = ((int64_t)rs * H + head) * 2 * kD;
-      } else {
-        kind = 3;
-        off = ((int64_t)row * H + head) * kD;
-      }
-      dst_kind[t] = kind;
-      dst_off[t] = off;
+    bwd_commit<false>(nx, Kr, Qr, dOr, nullptr, rw, gs, bs, al, tid);
+    commit_tinv(tx, Th, Tl, Pr, tid);
+    if (c > 0) {
+      bwd_fetch_rows(ci, j0 - kB, tid, nx);
+      fetch_tinv(tinv_seq + (c - 1) * tinv_step, tid, tx);
     }
-    red_dg[wave][lane] = 0.f;
-    red_g[wave][lane] = 0.f;
-    red_b[wave][lane] = 0.f;
-    red_e[wave][lane] = 0.f;
     __syncthreads();
-    const f16_t* S0n = states + ((int64_t)(sq.chunk_off + c) * H + head) * 2 * kD * kD;
-    const f16_t* S0t = S0n + kD * kD;
+    if (c > 0) bwd_fetch_data<false>(ci, j0 - kB, k, q, dO, nullptr, beta, alpha, H, head, tid, nx);
     const float g63 = gs[kB - 1];
-
-    // -- recompute A, P = scale E o QK and R ---------------------------------------------------
-    {
-      f32x16 kk = zero16(), qk = zero16();
-      if (bm >= bn) {
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const f16x8 b = frag_n(Kr, LDK, 32 * bn, 16 * s, lane);
-          kk = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), b, kk);
-          qk = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), b, qk);
-        }
-      }
-      const int i = 32 * bn + l32;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * bm + acc_row(r, hi);
-        const float e = i <= t ? __expf(gs[t] - gs[i]) : 0.f;
-        Ar[i * LDA + t] = i < t ? bs[t] * e * kk[r] : 0.f;
-        Pr[t * LDP + i] = (f16_t)(scale * e * qk[r]);
-      }
-    }
     const int cc = 32 * wave + l32;
-    f32x16 ks[2];  // K S0^T: used for R here and for R's beta/gamma derivatives below
-    {
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) ks[b2] = zero16();
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 b = frag_g(S0n, 32 * wave, 16 * s, lane);
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) ks[b2] = mfma(frag_n(Kr, LDK, 32 * b2, 16 * s, lane), b, ks[b2]);
-      }
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * b2 + acc_row(r, hi);
-          const float vv = (float)dRr[t * LDK + cc];  // V rows, staged by bwd_commit
-          Ur[t * LDK + cc] = (f16_t)(bs[t] * (vv - __expf(gs[t]) * ks[b2][r]));
-        }
-    }
-    if (c > 0) bwd_fetch_data(ci, j0 - kB, k, q, dO, v, beta, alpha, H, head, tid, nx);
-    __syncthreads();
-    solve_lower<f16_t, false>(Ar, Ur, LDK, nullptr, tid);
-    __syncthreads();
 
-    // -- dU = scale P^T dO + diag(E_63,.) K dS^T --------------------------------------------
+    // -- dU = diag(E_63,.) K dS^T + P^T dO ----------------------------------------------------
     {
       f32x16 du[2];
 #pragma unroll
@@ -813,121 +866,27 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
         for (int r = 0; r < 16; ++r) dRr[(32 * b2 + acc_row(r, hi)) * LDK + cc] = (f16_t)du[b2][r];
     }
     __syncthreads();
-
-    // -- dR = (I + A)^{-T} dU; dV = diag(beta) dR -------------------------------------------
-    solve_upper_t<f16_t>(Ar, dRr, LDK, tid, [&](int t, int col, float y) {
-      const int kind = dst_kind[t];
-      const int64_t off = dst_off[t];
-      const float g = bs[t] * y;
-      if (kind == 1) rbuf[off + kD + col] = g;
-      else if (kind == 2) rside[off + kD + col] = g;
-      else if (kind == 3) st_g<TG>(dv + off + col, g);
-    });
+    // -- dR = (I + A)^{-T} dU = T^T dU: T_hi^T dU + T_lo^T dU -----------------------------------
+    {
+      f32x16 dr[2];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) dr[b2] = zero16();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const f16x8 b = frag_t(dRr, LDK, 16 * s, 32 * wave, lane);
+#pragma unroll
+        for (int b2 = 0; b2 < 2; ++b2) {
+          dr[b2] = mfma(frag_t(Th, LDP, 16 * s, 32 * b2, lane), b, dr[b2]);
+          dr[b2] = mfma(frag_t(Tl, LDP, 16 * s, 32 * b2, lane), b, dr[b2]);
+        }
+      }
+      __syncthreads();  // every wave has read dU
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dRr[(32 * b2 + acc_row(r, hi)) * LDK + cc] = (f16_t)dr[b2][r];
+    }
     __syncthreads();
-
-    // V rows for sum_c dR[t][c] V[t][c] (beta's derivative through R): thread (t, part)
-    // takes row t's columns 32 part .. 32 part + 31 as four 16-byte pieces, read here and
-    // used after the products below
-    uint4 vrow[4];
-    {
-      const int t = tid >> 2, part = tid & 3;
-      const int row = rw[t];
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-        vrow[m] = row >= 0 ? *reinterpret_cast<const uint4*>(v + ((int64_t)row * H + head) * kD + 32 * part + 8 * m)
-                           : make_uint4(0, 0, 0, 0);
-    }
-    // -- <dS, S0> for the decay of the whole chunk ------------------------------------------
-    {
-      // S0 from its transposed copy: a lane's four consecutive rows are one 8-byte read
-      typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
-      float s = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f16x4 w = *reinterpret_cast<const f16x4*>(S0t + (32 * nb + l32) * kD + 32 * wave + 8 * r4 + 4 * hi);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) s += D[nb][4 * r4 + j] * (float)w[j];
-        }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
-      if (lane == 0) red_s[wave] = s;
-    }
-    // -- dP = dO U^T, dA = -dR U^T on this wave's block -----------------------------------------
-    {
-      f32x16 dp = zero16(), da = zero16(), kk = zero16(), qk = zero16();
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 b = frag_n(Ur, LDK, 32 * bn, 16 * s, lane);
-        dp = mfma(frag_n(dOr, LDK, 32 * bm, 16 * s, lane), b, dp);
-        if (bm >= bn) {
-          const f16x8 bk = frag_n(Kr, LDK, 32 * bn, 16 * s, lane);
-          da = mfma(frag_n(dRr, LDK, 32 * bm, 16 * s, lane), b, da);
-          kk = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), bk, kk);
-          qk = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), bk, qk);
-        }
-      }
-      const int i = 32 * bn + l32;
-      float xy[16], z[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * bm + acc_row(r, hi);
-        const float e = i <= t ? __expf(gs[t] - gs[i]) : 0.f;
-        const float dpt = scale * e * dp[r];          // dP~ = d(QK) (scale and decay folded)
-        const float dat = i < t ? -da[r] : 0.f;       // dA
-        const float dkk = dat * bs[t] * e;            // d(KK)
-        Pr[t * LDP + i] = (f16_t)dpt;
-        Kk[t * LDP + i] = (f16_t)dkk;
-        xy[r] = dpt * qk[r] + dkk * kk[r];            // dg from E_ti inside P and A
-        z[r] = dat * e * kk[r];                       // dbeta through A
-      }
-      const float rs = rowsum16(xy, lane);
-      const float rz = rowsum16(z, lane);
-      const float cs = colsum16(xy);
-      if (!(lane & 1)) {
-        const int t = 32 * bm + acc_row(rowsum16_elem(lane), hi);
-        red_dg[wave][t] += rs;
-        red_b[wave][t] += rz;
-      }
-      if (hi == 0) red_dg[wave][i] -= cs;
-    }
-    // -- R's dependence on beta and gamma ------------------------------------------------------
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
-      float xb[16], xg[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * b2 + acc_row(r, hi);
-        const float dr = (float)dRr[t * LDK + cc];
-        xb[r] = -dr * __expf(gs[t]) * ks[b2][r];  // the dR V part is red_v
-        xg[r] = -bs[t] * dr * ks[b2][r];
-      }
-      const float sb = rowsum16(xb, lane);
-      const float sg = rowsum16(xg, lane);
-      if (!(lane & 1)) {
-        const int t = 32 * b2 + acc_row(rowsum16_elem(lane), hi);
-        red_b[wave][t] += sb;
-        red_g[wave][t] += sg;
-      }
-    }
-    {
-      const int t = tid >> 2, part = tid & 3;
-      float acc = 0.f;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const f16x8 d8 = *reinterpret_cast<const f16x8*>(dRr + t * LDK + 32 * part + 8 * m);
-        const uint32_t w[4] = {vrow[m].x, vrow[m].y, vrow[m].z, vrow[m].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc = fmaf((float)d8[2 * e], __uint_as_float(w[e] << 16), acc);
-          acc = fmaf((float)d8[2 * e + 1], __uint_as_float(w[e] & 0xffff0000u), acc);
-        }
-      }
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (part == 0) red_v[t] = acc;
-    }
     // -- dS_prev = gamma_63 dS + scale (diag(gamma) dO)^T Q - (diag(beta gamma) dR)^T K -----------
     {
       const float gn = __expf(g63);
@@ -955,141 +914,6 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
       }
     }
     __syncthreads();
-
-    // -- dQ = scale diag(gamma) dO S0 + dP~ K ----------------------------------------------------
-    {
-      f32x16 aq[2];
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) aq[b2] = zero16();
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 b = frag_g(S0t, 32 * wave, 16 * s, lane);
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) aq[b2] = mfma(frag_n(dOr, LDK, 32 * b2, 16 * s, lane), b, aq[b2]);
-      }
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        float xg[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * b2 + acc_row(r, hi);
-          xg[r] = scale * aq[b2][r] * (float)Qr[t * LDK + cc];
-          aq[b2][r] *= scale * __expf(gs[t]);
-        }
-        const float sg = rowsum16(xg, lane);
-        if (!(lane & 1)) red_g[wave][32 * b2 + acc_row(rowsum16_elem(lane), hi)] += sg;
-      }
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const f16x8 b = frag_t(Kr, LDK, 16 * s, 32 * wave, lane);
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) aq[b2] = mfma(frag_n(Pr, LDP, 32 * b2, 16 * s, lane), b, aq[b2]);
-      }
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * b2 + acc_row(r, hi);
-          const int j = j0 + t;
-          if (j >= sq.n_replay && j < sq.n_tok) st_g<TG>(dq + ((int64_t)rw[t] * H + head) * kD + cc, aq[b2][r]);
-        }
-    }
-    // -- dK = dP~^T Q + dKk K + dKk^T K + diag(E_63,.) U dS - diag(beta gamma) dR S0 -----------
-    {
-      f32x16 ak[2];
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) ak[b2] = zero16();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const f16x8 bq = frag_t(Qr, LDK, 16 * s, 32 * wave, lane);
-        const f16x8 bk = frag_t(Kr, LDK, 16 * s, 32 * wave, lane);
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-          ak[b2] = mfma(frag_t(Pr, LDP, 16 * s, 32 * b2, lane), bq, ak[b2]);
-          ak[b2] = mfma(frag_n(Kk, LDP, 32 * b2, 16 * s, lane), bk, ak[b2]);
-          ak[b2] = mfma(frag_t(Kk, LDP, 16 * s, 32 * b2, lane), bk, ak[b2]);
-        }
-      }
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        f32x16 ud = zero16();
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          ud = mfma(frag_n(Ur, LDK, 32 * b2, 16 * s, lane), frag_t(dSh, LDK, 16 * s, 32 * wave, lane), ud);
-        float xe[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * b2 + acc_row(r, hi);
-          xe[r] = ud[r] * (float)Kr[t * LDK + cc];
-          ak[b2][r] = fmaf(__expf(g63 - gs[t]), ud[r], ak[b2][r]);
-        }
-        const float se = rowsum16(xe, lane);
-        if (!(lane & 1)) red_e[wave][32 * b2 + acc_row(rowsum16_elem(lane), hi)] += se;
-      }
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        f32x16 rs0 = zero16();
-#pragma unroll
-        for (int s = 0; s < 8; ++s)
-          rs0 = mfma(frag_n(dRr, LDK, 32 * b2, 16 * s, lane), frag_g(S0t, 32 * wave, 16 * s, lane), rs0);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * b2 + acc_row(r, hi);
-          ak[b2][r] = fmaf(-bs[t] * __expf(gs[t]), rs0[r], ak[b2][r]);
-        }
-      }
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * b2 + acc_row(r, hi);
-          const int kind = dst_kind[t];
-          const int64_t off = dst_off[t];
-          if (kind == 1) rbuf[off + cc] = ak[b2][r];
-          else if (kind == 2) rside[off + cc] = ak[b2][r];
-          else if (kind == 3) st_g<TG>(dk + off + cc, ak[b2][r]);
-        }
-    }
-    __syncthreads();
-
-    // -- per-token dbeta, dalpha (reverse cumulative sum of dg) --------------------------------
-    if (tid < kB) {
-      const int t = tid;
-      const float en = __expf(g63 - gs[t]);
-      float e_t = 0.f, dgp = 0.f, dgam = 0.f, db = 0.f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        dgp += red_dg[w][t];
-        dgam += red_g[w][t];
-        db += red_b[w][t];
-        e_t += red_e[w][t];
-      }
-      db += red_v[t];
-      float dg = dgp + __expf(gs[t]) * dgam - e_t * en;
-      float tot = e_t * en;  // sum over the chunk of dEn_i E_63,i goes to g_63
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off);
-      if (t == kB - 1) dg += tot + __expf(g63) * (red_s[0] + red_s[1] + red_s[2] + red_s[3]);
-      // reverse inclusive scan: dlogalpha_t = sum_{s >= t} dg_s
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_down(dg, off, 64);
-        if (t + off < 64) dg += y;
-      }
-      const int j = j0 + t;
-      if (j < sq.n_tok) {
-        const float da = dg / al[t];
-        if (j < sq.n_replay) {
-          float* rb = rbuf + ((int64_t)(sq.rep_off + j) * H + head) * kRep;
-          rb[2 * kD] = db;
-          rb[2 * kD + 1] = da;
-        } else {
-          dbeta[(int64_t)rw[t] * H + head] = db;
-          dalpha[(int64_t)rw[t] * H + head] = da;
-        }
-      }
-    }
-    __syncthreads();
   }
   if (sq.cgrad >= 0) {
     float* dst = cgrad + ((int64_t)sq.cgrad * H + head) * kD * kD;
@@ -1098,6 +922,435 @@ __global__ __launch_bounds__(256, 1) void gdn_bwd_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) dst[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32] = D[nb][r];
   }
+}
+
+// ---------------------------------------------------------------------------------
+// Backward, parallel part: every input gradient of one chunk and head, given the
+// chunk's start state S0 (saved by the forward's state pass), its end-state gradient
+// dS (saved by the serial scan), T and P.  Grid: (round's chunk items) x H.
+// ---------------------------------------------------------------------------------
+template <typename TG>
+__global__ __launch_bounds__(256, 1) void gdn_bpar_kernel(
+    const GSeq* __restrict__ seqs, const int32_t* __restrict__ items, int round_item0,
+    const int32_t* __restrict__ grows, const int32_t* __restrict__ rep_slot, const bf16_t* __restrict__ q,
+    const bf16_t* __restrict__ k,
+    const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ alpha,
+    const bf16_t* __restrict__ dO, const f16_t* __restrict__ states, const f16_t* __restrict__ tinv,
+    const f16_t* __restrict__ dsend, TG* __restrict__ dq, TG* __restrict__ dk, TG* __restrict__ dv,
+    float* __restrict__ dbeta, float* __restrict__ dalpha, float* __restrict__ rside, float* __restrict__ rbuf, int H,
+    float scale) {
+  __shared__ __attribute__((aligned(16))) f16_t dSh[kD * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t Kr[kB * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t Qr[kB * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t dOr[kB * LDK];
+  __shared__ __attribute__((aligned(16))) f16_t Ur[kB * LDK];   // R, then U
+  __shared__ __attribute__((aligned(16))) f16_t dRr[kB * LDK];  // V rows, then dU, then dR
+  __shared__ __attribute__((aligned(16))) f16_t Pr[kB * LDP];   // P, then dP~
+  __shared__ __attribute__((aligned(16))) f16_t Th[kB * LDP];   // T high part, then dKk
+  __shared__ __attribute__((aligned(16))) f16_t Tl[kB * LDP];
+  __shared__ float gs[kB], bs[kB], al[kB];
+  __shared__ int rw[kB];
+  // where row t's gradients go: 0 nowhere (past the sequence), 1 the replay buffer,
+  // 2 the side buffer of a replayed row, 3 its own dk / dv row; with the base offset
+  __shared__ int dst_kind[kB];
+  __shared__ int64_t dst_off[kB];
+  __shared__ float red_dg[4][kB], red_g[4][kB], red_b[4][kB], red_e[4][kB], red_s[4], red_v[kB];
+
+  const int head = blockIdx.x % H;
+  const int ritem = blockIdx.x / H;      // within the round (its end-state gradient)
+  const int item = round_item0 + ritem;  // among all items (its T and P)
+  const GSeq sq = seqs[items[2 * item]];
+  const int c = items[2 * item + 1];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int bm = wave >> 1, bn = wave & 1;  // this wave's 32x32 block of a 64x64 matrix
+  const int j0 = c * kB;
+  const ChunkIn ci{grows + sq.tok_off, sq.n_tok, sq.n_replay};
+  f16_t* Kk = Th;
+
+  {
+    BwdRegs nx;
+    TinvRegs tx;
+    fetch_tinv(tinv + ((int64_t)item * H + head) * kTinv, tid, tx);
+    bwd_fetch_rows(ci, j0, tid, nx);
+    bwd_fetch_data<true>(ci, j0, k, q, dO, v, beta, alpha, H, head, tid, nx);
+    // the end-state gradient: thread tid takes dv rows tid / 2, columns 64 (tid & 1) ..
+    const f16_t* src = dsend + ((int64_t)ritem * H + head) * kD * kD + (tid >> 1) * kD + 64 * (tid & 1);
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      *reinterpret_cast<uint4*>(dSh + (tid >> 1) * LDK + 64 * (tid & 1) + 8 * m) =
+          reinterpret_cast<const uint4*>(src)[m];
+    bwd_commit<true>(nx, Kr, Qr, dOr, dRr, rw, gs, bs, al, tid);
+    commit_tinv(tx, Th, Tl, Pr, tid);
+  }
+  if (tid < kB) {  // each row's destination, looked up once
+    const int t = tid, row = rw[t], j = j0 + t;
+    const int rs = row >= 0 ? rep_slot[row] : -1;
+    int kind;
+    int64_t off;
+    if (j >= sq.n_tok) {
+      kind = 0;
+      off = 0;
+    } else if (j < sq.n_replay) {
+      kind = 1;
+      off = ((int64_t)(sq.rep_off + j) * H + head) * kRep;
+    } else if (rs >= 0) {
+      kind = 2;
+      off = ((int64_t)rs * H + head) * 2 * kD;
+    } else {
+      kind = 3;
+      off = ((int64_t)row * H + head) * kD;
+    }
+    dst_kind[t] = kind;
+    dst_off[t] = off;
+  }
+  red_dg[wave][lane] = 0.f;
+  red_g[wave][lane] = 0.f;
+  red_b[wave][lane] = 0.f;
+  red_e[wave][lane] = 0.f;
+  __syncthreads();
+  const f16_t* S0n = states + ((int64_t)(sq.chunk_off + c) * H + head) * 2 * kD * kD;
+  const f16_t* S0t = S0n + kD * kD;
+  const float g63 = gs[kB - 1];
+  const int cc = 32 * wave + l32;
+  // S0 fragments with the contraction over dv: this wave's dk rows 32 wave .. of the
+  // transposed copy, read once for <dS, S0>, dQ and dK
+  f16x8 s0f[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) s0f[s] = frag_g(S0t, 32 * wave, 16 * s, lane);
+
+  // -- R = diag(beta) (V - diag(gamma) K S0^T) (fp16), then U = T R --------------------------
+  f32x16 ks[2];  // K S0^T: used for R here and for R's beta/gamma derivatives below
+  {
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) ks[b2] = zero16();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const f16x8 b = frag_g(S0n, 32 * wave, 16 * s, lane);
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) ks[b2] = mfma(frag_n(Kr, LDK, 32 * b2, 16 * s, lane), b, ks[b2]);
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * b2 + acc_row(r, hi);
+        const float vv = (float)dRr[t * LDK + cc];  // V rows, staged by bwd_commit
+        Ur[t * LDK + cc] = (f16_t)(bs[t] * (vv - __expf(gs[t]) * ks[b2][r]));
+      }
+  }
+  __syncthreads();
+  {
+    f32x16 u[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) u[b2] = zero16();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 b = frag_t(Ur, LDK, 16 * s, 32 * wave, lane);
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        u[b2] = mfma(frag_n(Th, LDP, 32 * b2, 16 * s, lane), b, u[b2]);
+        u[b2] = mfma(frag_n(Tl, LDP, 32 * b2, 16 * s, lane), b, u[b2]);
+      }
+    }
+    __syncthreads();  // every wave has read R
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Ur[(32 * b2 + acc_row(r, hi)) * LDK + cc] = (f16_t)u[b2][r];
+  }
+
+  // -- dU = scale P^T dO + diag(E_63,.) K dS^T --------------------------------------------
+  {
+    f32x16 du[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) du[b2] = zero16();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const f16x8 b = frag_n(dSh, LDK, 32 * wave, 16 * s, lane);
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) du[b2] = mfma(frag_n(Kr, LDK, 32 * b2, 16 * s, lane), b, du[b2]);
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) du[b2][r] *= __expf(g63 - gs[32 * b2 + acc_row(r, hi)]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 b = frag_t(dOr, LDK, 16 * s, 32 * wave, lane);
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) du[b2] = mfma(frag_t(Pr, LDP, 16 * s, 32 * b2, lane), b, du[b2]);
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dRr[(32 * b2 + acc_row(r, hi)) * LDK + cc] = (f16_t)du[b2][r];
+  }
+  __syncthreads();
+
+  // -- dR = (I + A)^{-T} dU = T^T dU; dV = diag(beta) dR ---------------------------------------
+  {
+    f32x16 dr[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) dr[b2] = zero16();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 b = frag_t(dRr, LDK, 16 * s, 32 * wave, lane);
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        dr[b2] = mfma(frag_t(Th, LDP, 16 * s, 32 * b2, lane), b, dr[b2]);
+        dr[b2] = mfma(frag_t(Tl, LDP, 16 * s, 32 * b2, lane), b, dr[b2]);
+      }
+    }
+    __syncthreads();  // every wave has read dU and T
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * b2 + acc_row(r, hi);
+        dRr[t * LDK + cc] = (f16_t)dr[b2][r];
+        const int kind = dst_kind[t];
+        const int64_t off = dst_off[t];
+        const float g = bs[t] * dr[b2][r];
+        if (kind == 1) rbuf[off + kD + cc] = g;
+        else if (kind == 2) rside[off + kD + cc] = g;
+        else if (kind == 3) st_g<TG>(dv + off + cc, g);
+      }
+  }
+  __syncthreads();
+
+  // V rows for sum_c dR[t][c] V[t][c] (beta's derivative through R): thread (t, part)
+  // takes row t's columns 32 part .. 32 part + 31 as four 16-byte pieces, read here and
+  // used after the products below
+  uint4 vrow[4];
+  {
+    const int t = tid >> 2, part = tid & 3;
+    const int row = rw[t];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+      vrow[m] = row >= 0 ? *reinterpret_cast<const uint4*>(v + ((int64_t)row * H + head) * kD + 32 * part + 8 * m)
+                         : make_uint4(0, 0, 0, 0);
+  }
+  // -- <dS, S0> for the decay of the whole chunk ------------------------------------------
+  {
+    // lane holds S0[16 s + 8 hi + j][32 wave + l32] in s0f[s][j]
+    float s = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 8; ++sb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        s += (float)dSh[(16 * sb + 8 * hi + j) * LDK + 32 * wave + l32] * (float)s0f[sb][j];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) red_s[wave] = s;
+  }
+  // -- dP = dO U^T, dA = -dR U^T on this wave's block -----------------------------------------
+  {
+    f32x16 dp = zero16(), da = zero16(), kk = zero16(), qk = zero16();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const f16x8 b = frag_n(Ur, LDK, 32 * bn, 16 * s, lane);
+      dp = mfma(frag_n(dOr, LDK, 32 * bm, 16 * s, lane), b, dp);
+      if (bm >= bn) {
+        const f16x8 bk = frag_n(Kr, LDK, 32 * bn, 16 * s, lane);
+        da = mfma(frag_n(dRr, LDK, 32 * bm, 16 * s, lane), b, da);
+        kk = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), bk, kk);
+        qk = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), bk, qk);
+      }
+    }
+    const int i = 32 * bn + l32;
+    float xy[16], z[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * bm + acc_row(r, hi);
+      const float e = i <= t ? __expf(gs[t] - gs[i]) : 0.f;
+      const float dpt = scale * e * dp[r];          // dP~ = d(QK) (scale and decay folded)
+      const float dat = i < t ? -da[r] : 0.f;       // dA
+      const float dkk = dat * bs[t] * e;            // d(KK)
+      Pr[t * LDP + i] = (f16_t)dpt;
+      Kk[t * LDP + i] = (f16_t)dkk;
+      xy[r] = dpt * qk[r] + dkk * kk[r];            // dg from E_ti inside P and A
+      z[r] = dat * e * kk[r];                       // dbeta through A
+    }
+    const float rs = rowsum16(xy, lane);
+    const float rz = rowsum16(z, lane);
+    const float cs = colsum16(xy);
+    if (!(lane & 1)) {
+      const int t = 32 * bm + acc_row(rowsum16_elem(lane), hi);
+      red_dg[wave][t] += rs;
+      red_b[wave][t] += rz;
+    }
+    if (hi == 0) red_dg[wave][i] -= cs;
+  }
+  // -- R's dependence on beta and gamma ------------------------------------------------------
+#pragma unroll
+  for (int b2 = 0; b2 < 2; ++b2) {
+    float xb[16], xg[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * b2 + acc_row(r, hi);
+      const float dr = (float)dRr[t * LDK + cc];
+      xb[r] = -dr * __expf(gs[t]) * ks[b2][r];  // the dR V part is red_v
+      xg[r] = -bs[t] * dr * ks[b2][r];
+    }
+    const float sb = rowsum16(xb, lane);
+    const float sg = rowsum16(xg, lane);
+    if (!(lane & 1)) {
+      const int t = 32 * b2 + acc_row(rowsum16_elem(lane), hi);
+      red_b[wave][t] += sb;
+      red_g[wave][t] += sg;
+    }
+  }
+  {
+    const int t = tid >> 2, part = tid & 3;
+    float acc = 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f16x8 d8 = *reinterpret_cast<const f16x8*>(dRr + t * LDK + 32 * part + 8 * m);
+      const uint32_t w[4] = {vrow[m].x, vrow[m].y, vrow[m].z, vrow[m].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc = fmaf((float)d8[2 * e], __uint_as_float(w[e] << 16), acc);
+        acc = fmaf((float)d8[2 * e + 1], __uint_as_float(w[e] & 0xffff0000u), acc);
+      }
+    }
+    acc += __shfl_xor(acc, 1);
+    acc += __shfl_xor(acc, 2);
+    if (part == 0) red_v[t] = acc;
+  }
+  // -- dQ = scale diag(gamma) dO S0 + dP~ K ----------------------------------------------------
+  {
+    f32x16 aq[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) aq[b2] = zero16();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const f16x8 b = s0f[s];
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) aq[b2] = mfma(frag_n(dOr, LDK, 32 * b2, 16 * s, lane), b, aq[b2]);
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      float xg[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * b2 + acc_row(r, hi);
+        xg[r] = scale * aq[b2][r] * (float)Qr[t * LDK + cc];
+        aq[b2][r] *= scale * __expf(gs[t]);
+      }
+      const float sg = rowsum16(xg, lane);
+      if (!(lane & 1)) red_g[wave][32 * b2 + acc_row(rowsum16_elem(lane), hi)] += sg;
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 b = frag_t(Kr, LDK, 16 * s, 32 * wave, lane);
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) aq[b2] = mfma(frag_n(Pr, LDP, 32 * b2, 16 * s, lane), b, aq[b2]);
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * b2 + acc_row(r, hi);
+        const int j = j0 + t;
+        if (j >= sq.n_replay && j < sq.n_tok) st_g<TG>(dq + ((int64_t)rw[t] * H + head) * kD + cc, aq[b2][r]);
+      }
+  }
+  // -- dK = dP~^T Q + dKk K + dKk^T K + diag(E_63,.) U dS - diag(beta gamma) dR S0 -----------
+  {
+    f32x16 ak[2];
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) ak[b2] = zero16();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 bq = frag_t(Qr, LDK, 16 * s, 32 * wave, lane);
+      const f16x8 bk = frag_t(Kr, LDK, 16 * s, 32 * wave, lane);
+#pragma unroll
+      for (int b2 = 0; b2 < 2; ++b2) {
+        ak[b2] = mfma(frag_t(Pr, LDP, 16 * s, 32 * b2, lane), bq, ak[b2]);
+        ak[b2] = mfma(frag_n(Kk, LDP, 32 * b2, 16 * s, lane), bk, ak[b2]);
+        ak[b2] = mfma(frag_t(Kk, LDP, 16 * s, 32 * b2, lane), bk, ak[b2]);
+      }
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      f32x16 ud = zero16();
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        ud = mfma(frag_n(Ur, LDK, 32 * b2, 16 * s, lane), frag_t(dSh, LDK, 16 * s, 32 * wave, lane), ud);
+      float xe[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * b2 + acc_row(r, hi);
+        xe[r] = ud[r] * (float)Kr[t * LDK + cc];
+        ak[b2][r] = fmaf(__expf(g63 - gs[t]), ud[r], ak[b2][r]);
+      }
+      const float se = rowsum16(xe, lane);
+      if (!(lane & 1)) red_e[wave][32 * b2 + acc_row(rowsum16_elem(lane), hi)] += se;
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2) {
+      f32x16 rs0 = zero16();
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        rs0 = mfma(frag_n(dRr, LDK, 32 * b2, 16 * s, lane), s0f[s], rs0);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * b2 + acc_row(r, hi);
+        ak[b2][r] = fmaf(-bs[t] * __expf(gs[t]), rs0[r], ak[b2][r]);
+      }
+    }
+#pragma unroll
+    for (int b2 = 0; b2 < 2; ++b2)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * b2 + acc_row(r, hi);
+        const int kind = dst_kind[t];
+        const int64_t off = dst_off[t];
+        if (kind == 1) rbuf[off + cc] = ak[b2][r];
+        else if (kind == 2) rside[off + cc] = ak[b2][r];
+        else if (kind == 3) st_g<TG>(dk + off + cc, ak[b2][r]);
+      }
+  }
+  __syncthreads();
+
+  // -- per-token dbeta, dalpha (reverse cumulative sum of dg) --------------------------------
+  if (tid < kB) {
+    const int t = tid;
+    const float en = __expf(g63 - gs[t]);
+    float e_t = 0.f, dgp = 0.f, dgam = 0.f, db = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      dgp += red_dg[w][t];
+      dgam += red_g[w][t];
+      db += red_b[w][t];
+      e_t += red_e[w][t];
+    }
+    db += red_v[t];
+    float dg = dgp + __expf(gs[t]) * dgam - e_t * en;
+    float tot = e_t * en;  // sum over the chunk of dEn_i E_63,i goes to g_63
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off);
+    if (t == kB - 1) dg += tot + __expf(g63) * (red_s[0] + red_s[1] + red_s[2] + red_s[3]);
+    // reverse inclusive scan: dlogalpha_t = sum_{s >= t} dg_s
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(dg, off, 64);
+      if (t + off < 64) dg += y;
+    }
+    const int j = j0 + t;
+    if (j < sq.n_tok) {
+      const float da = dg / al[t];
+      if (j < sq.n_replay) {
+        float* rb = rbuf + ((int64_t)(sq.rep_off + j) * H + head) * kRep;
+        rb[2 * kD] = db;
+        rb[2 * kD + 1] = da;
+      } else {
+        dbeta[(int64_t)rw[t] * H + head] = db;
+        dalpha[(int64_t)rw[t] * H + head] = da;
+      }
+    }
+  }
+  __syncthreads();
 }
 
 // Rows that are replayed somewhere: own contribution (kept in fp32) plus every
@@ -1146,31 +1399,48 @@ __global__ __launch_bounds__(256) void gdn_pad_kernel(T* __restrict__ x, const i
 // ---------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------
+void launch_gdn_tinv(const GdnShape& s, int n_items, const int32_t* items, const bf16_t* q, const bf16_t* k,
+                     const float* beta, const float* alpha, f16_t* tinv, hipStream_t st) {
+  if (n_items <= 0) return;
+  static_assert(gdn::kTinv == kGdnTinvHalfs, "chunk-inverse record size");
+  gdn::gdn_tinv_kernel<<<dim3((unsigned)(n_items * s.H)), 256, 0, st>>>(s.seqs, items, s.rows, q, k, beta, alpha,
+                                                                        tinv, s.H, s.scale);
+}
+
 void launch_gdn_fwd(const GdnShape& s, int n_seq, const int32_t* order, const bf16_t* q,
-                    const bf16_t* k, const bf16_t* v, const float* beta, const float* alpha, bf16_t* o,
-                    float* slots, f16_t* states, hipStream_t st) {
+                    const bf16_t* k, const bf16_t* v, const float* beta, const float* alpha, const f16_t* tinv,
+                    bf16_t* o, float* slots, f16_t* states, hipStream_t st) {
   if (n_seq <= 0) return;
   const dim3 grid((unsigned)(n_seq * s.H));
   if (o && states)
-    gdn::gdn_fwd_kernel<true, true><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha, o,
-                                                          slots, states, s.H, s.scale);
+    gdn::gdn_fwd_kernel<true, true><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha,
+                                                          tinv, o, slots, states, s.H, s.scale);
   else if (states)
     gdn::gdn_fwd_kernel<false, true><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha,
-                                                           o, slots, states, s.H, s.scale);
+                                                           tinv, o, slots, states, s.H, s.scale);
   else
     gdn::gdn_fwd_kernel<true, false><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha,
-                                                           o, slots, states, s.H, s.scale);
+                                                           tinv, o, slots, states, s.H, s.scale);
+}
+
+void launch_gdn_bscan(const GdnShape& s, int n_seq, const int32_t* order, int item0, const bf16_t* q,
+                      const bf16_t* k, const float* beta, const float* alpha, const bf16_t* dO, const f16_t* tinv,
+                      float* cgrad, f16_t* dsend, hipStream_t st) {
+  if (n_seq <= 0) return;
+  gdn::gdn_bscan_kernel<<<dim3((unsigned)(n_seq * s.H)), 256, 0, st>>>(
+      s.seqs, order, s.rows, s.exports, s.slot_off, s.slot_cons, q, k, beta, alpha, dO, tinv, cgrad, dsend, item0,
+      s.H, s.scale);
 }
 
 template <typename TG>
-void launch_gdn_bwd(const GdnShape& s, int n_seq, const int32_t* order, const bf16_t* q, const bf16_t* k,
-                    const bf16_t* v, const float* beta, const float* alpha, const bf16_t* dO, const f16_t* states,
-                    float* cgrad, TG* dq, TG* dk, TG* dv, float* dbeta, float* dalpha, float* rside, float* rbuf,
-                    hipStream_t st) {
-  if (n_seq <= 0) return;
-  gdn::gdn_bwd_kernel<TG><<<dim3((unsigned)(n_seq * s.H)), 256, 0, st>>>(
-      s.seqs, order, s.rows, s.exports, s.slot_off, s.slot_cons, s.rep_slot, q, k, v, beta, alpha, dO, states, cgrad,
-      dq, dk, dv, dbeta, dalpha, rside, rbuf, s.H, s.scale);
+void launch_gdn_bpar(const GdnShape& s, int item0, int n_items, const bf16_t* q, const bf16_t* k,
+                     const bf16_t* v, const float* beta, const float* alpha, const bf16_t* dO, const f16_t* states,
+                     const f16_t* tinv, const f16_t* dsend, TG* dq, TG* dk, TG* dv, float* dbeta, float* dalpha,
+                     float* rside, float* rbuf, hipStream_t st) {
+  if (n_items <= 0) return;
+  gdn::gdn_bpar_kernel<TG><<<dim3((unsigned)(n_items * s.H)), 256, 0, st>>>(
+      s.seqs, s.items, item0, s.rows, s.rep_slot, q, k, v, beta, alpha, dO, states, tinv, dsend, dq, dk, dv, dbeta,
+      dalpha, rside, rbuf, s.H, s.scale);
 }
 
 template <typename TG>
@@ -1188,12 +1458,14 @@ void launch_gdn_pad(int64_t pages, const int32_t* page_nrows, T* x, int H, int W
   gdn::gdn_pad_kernel<T><<<dim3((unsigned)(pages * H)), 256, 0, st>>>(x, page_nrows, H, W);
 }
 
-template void launch_gdn_bwd<bf16_t>(const GdnShape&, int, const int32_t*, const bf16_t*, const bf16_t*,
-                                     const bf16_t*, const float*, const float*, const bf16_t*, const f16_t*, float*,
-                                     bf16_t*, bf16_t*, bf16_t*, float*, float*, float*, float*, hipStream_t);
-template void launch_gdn_bwd<float>(const GdnShape&, int, const int32_t*, const bf16_t*, const bf16_t*,
-                                    const bf16_t*, const float*, const float*, const bf16_t*, const f16_t*, float*,
-                                    float*, float*, float*, float*, float*, float*, float*, hipStream_t);
+template void launch_gdn_bpar<bf16_t>(const GdnShape&, int, int, const bf16_t*, const bf16_t*,
+                                      const bf16_t*, const float*, const float*, const bf16_t*, const f16_t*,
+                                      const f16_t*, const f16_t*, bf16_t*, bf16_t*, bf16_t*, float*, float*, float*,
+                                      float*, hipStream_t);
+template void launch_gdn_bpar<float>(const GdnShape&, int, int, const bf16_t*, const bf16_t*,
+                                     const bf16_t*, const float*, const float*, const bf16_t*, const f16_t*,
+                                     const f16_t*, const f16_t*, float*, float*, float*, float*, float*, float*,
+                                     float*, hipStream_t);
 template void launch_gdn_fixup<bf16_t>(const GdnShape&, int, const float*, const float*, bf16_t*, bf16_t*, float*,
                                        float*, hipStream_t);
 template void launch_gdn_fixup<float>(const GdnShape&, int, const float*, const float*, float*, float*, float*,

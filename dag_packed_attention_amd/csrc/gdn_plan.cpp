@@ -275,6 +275,26 @@ dag_status build_gdn_schedule(Plan* P, int32_t B, std::string* err) {
     P->ground_seq.insert(P->ground_seq.end(), ids.begin(), ids.end());
     P->ground_off[r] = (int32_t)P->ground_seq.size();
   }
+  // each round's chunks as independent work items (the chunk-parallel kernels)
+  P->gitem_off.assign(rounds + 1, 0);
+  P->gitems.clear();
+  P->gdn_round_chunks_max = 0;
+  for (int32_t r = 0; r < rounds; ++r) {
+    const int64_t first = (int64_t)P->gitems.size() / 2;
+    for (int32_t i = P->ground_off[r]; i < P->ground_off[r + 1]; ++i) {
+      GSeq& g = P->gseqs[P->ground_seq[i]];
+      g.item0 = (int32_t)((int64_t)P->gitems.size() / 2);
+      const int32_t nch = (int32_t)(((int64_t)g.n_tok + B - 1) / B);
+      for (int32_t c = 0; c < nch; ++c) {
+        P->gitems.push_back(P->ground_seq[i]);
+        P->gitems.push_back(c);
+      }
+    }
+    const int64_t n = (int64_t)P->gitems.size() / 2 - first;
+    if (n > INT32_MAX) return gfail(err, "round chunks %lld overflow int32", (long long)n);
+    P->gitem_off[r + 1] = (int32_t)((int64_t)P->gitems.size() / 2);
+    P->gdn_round_chunks_max = std::max(P->gdn_round_chunks_max, n);
+  }
 
   // -- 8. replay fix-up lists: per row, its replayed occurrences in schedule order ------
   // (replay index = position of the token among all replayed tokens, sequence order)

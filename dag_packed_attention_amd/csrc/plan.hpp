@@ -78,7 +78,7 @@ struct GSeq {
   int32_t chunk_off;  // first entry of its per-chunk saved states
   int32_t round;
   int32_t rep_off;    // replay index of its first replayed token (replay gradients)
-  int32_t pad0;
+  int32_t item0;      // index of its chunk 0 among all chunk items (rounds in order)
 };
 // An exported boundary: the state after `chunk` chunks of the sequence goes to `slot`.
 struct GExport {
@@ -135,6 +135,10 @@ struct Plan {
   std::vector<GExport> gexports;
   std::vector<int32_t> gslot_off, gslot_cons;  // slot -> consumers' cgrad ids, sequence order
   std::vector<int32_t> ground_off, ground_seq; // round r (0-based) -> sequences, most tokens first
+  // round r's chunks, gitems[2 i] = sequence, gitems[2 i + 1] = chunk, for i in
+  // [gitem_off[r], gitem_off[r + 1]): the round's sequences in ground_seq order, chunks ascending
+  std::vector<int32_t> gitem_off, gitems;
+  int64_t gdn_round_chunks_max = 0;            // most chunk items in one round
   // replay fix-up: rows that are replayed somewhere, each with its replay indices
   // (in schedule order); grep_slot maps every row to its position in grep_rows or -1
   std::vector<int32_t> grep_rows, grep_off, grep_tok, grep_slot;

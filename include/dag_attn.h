@@ -308,17 +308,21 @@ typedef struct {
   int32_t grad_dtype;  /* dq, dk, dv: DAG_DTYPE_BF16 or DAG_DTYPE_FP32           */
   float scale;         /* output scale; 0 selects 1                              */
   int32_t keep_states; /* 0: the backward recomputes every chunk's starting state
-                          from the inputs; 1: the forward saves them (fp16) into
-                          its workspace and the backward reads them there: pass
-                          the same ws to both calls and leave it untouched in
-                          between.  Trades a recomputation pass for keeping
-                          2 * H * 128 * 128 * 2 bytes per execution chunk alive
-                          from the forward to the backward                      */
+                          (and its chunk inverse) from the inputs; 1: the
+                          forward saves them (fp16) into its workspace and the
+                          backward reads them there: pass the same ws to both
+                          calls and leave it untouched in between.  Trades a
+                          recomputation pass for keeping (2 * 128 * 128 + 3 * 64
+                          * 64) * 2 bytes per head and execution chunk alive from
+                          the forward to the backward                           */
 } dag_gdn_params;
 
 /* Workspace bytes for dag_gdn_fwd and dag_gdn_bwd (with keep_states the two are
  * equal: the forward fills the part of the backward's workspace that holds the
- * states). */
+ * states).  Both hold every execution chunk's (I + A)^{-1} and P (3 * 64 * 64
+ * fp16 per head and chunk, computed for all chunks at once); the backward adds the
+ * chunk states and one round's end-state gradients (128 * 128 fp16 per head and
+ * chunk of the largest round). */
 dag_status dag_gdn_workspace(const dag_plan* plan, const dag_gdn_params* p, size_t* fwd_bytes,
                              size_t* bwd_bytes);
 
