@@ -927,18 +927,20 @@ __global__ __launch_bounds__(256, 1) void gdn_bscan_kernel(
 // ---------------------------------------------------------------------------------
 // Backward, parallel part: every input gradient of one chunk and head, given the
 // chunk's start state S0 (saved by the forward's state pass), its end-state gradient
-// dS (saved by the serial scan), T and P.  Grid: (round's chunk items) x H.
+// dS (saved by the serial scan), T and P.  Grid: (round's chunk items) x H.  Eight
+// waves, two per SIMD: wave (rb, cb) owns rows 32 rb .. and columns 32 cb .. of every
+// [64][128] product; the [64][64] products run on waves 0..3 (block (bm, bn)).
 // ---------------------------------------------------------------------------------
 template <typename TG>
-__global__ __launch_bounds__(256, 1) void gdn_bpar_kernel(
+__global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     const GSeq* __restrict__ seqs, const int32_t* __restrict__ items, int round_item0,
     const int32_t* __restrict__ grows, const int32_t* __restrict__ rep_slot, const bf16_t* __restrict__ q,
-    const bf16_t* __restrict__ k,
-    const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ alpha,
-    const bf16_t* __restrict__ dO, const f16_t* __restrict__ states, const f16_t* __restrict__ tinv,
-    const f16_t* __restrict__ dsend, TG* __restrict__ dq, TG* __restrict__ dk, TG* __restrict__ dv,
-    float* __restrict__ dbeta, float* __restrict__ dalpha, float* __restrict__ rside, float* __restrict__ rbuf, int H,
-    float scale) {
+    const bf16_t* __restrict__ k, const bf16_t* __restrict__ v, const float* __restrict__ beta,
+    const float* __restrict__ alpha, const bf16_t* __restrict__ dO, const f16_t* __restrict__ states,
+    const f16_t* __restrict__ tinv, const f16_t* __restrict__ dsend, TG* __restrict__ dq, TG* __restrict__ dk,
+    TG* __restrict__ dv, float* __restrict__ dbeta, float* __restrict__ dalpha, float* __restrict__ rside,
+    float* __restrict__ rbuf, int H, float scale) {
+  constexpr int kW = 8;
   __shared__ __attribute__((aligned(16))) f16_t dSh[kD * LDK];
   __shared__ __attribute__((aligned(16))) f16_t Kr[kB * LDK];
   __shared__ __attribute__((aligned(16))) f16_t Qr[kB * LDK];
@@ -948,13 +950,13 @@ __global__ __launch_bounds__(256, 1) void gdn_bpar_kernel(
   __shared__ __attribute__((aligned(16))) f16_t Pr[kB * LDP];   // P, then dP~
   __shared__ __attribute__((aligned(16))) f16_t Th[kB * LDP];   // T high part, then dKk
   __shared__ __attribute__((aligned(16))) f16_t Tl[kB * LDP];
-  __shared__ float gs[kB], bs[kB], al[kB];
+  __shared__ float gs[kB], bs[kB], al[kB], gam[kB], egam[kB];
   __shared__ int rw[kB];
   // where row t's gradients go: 0 nowhere (past the sequence), 1 the replay buffer,
   // 2 the side buffer of a replayed row, 3 its own dk / dv row; with the base offset
   __shared__ int dst_kind[kB];
   __shared__ int64_t dst_off[kB];
-  __shared__ float red_dg[4][kB], red_g[4][kB], red_b[4][kB], red_e[4][kB], red_s[4], red_v[kB];
+  __shared__ float red_dg[kW][kB], red_g[kW][kB], red_b[kW][kB], red_e[kW][kB], red_s[kW], red_v[kB];
 
   const int head = blockIdx.x % H;
   const int ritem = blockIdx.x / H;      // within the round (its end-state gradient)
@@ -962,12 +964,12 @@ __global__ __launch_bounds__(256, 1) void gdn_bpar_kernel(
   const GSeq sq = seqs[items[2 * item]];
   const int c = items[2 * item + 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
-  const int bm = wave >> 1, bn = wave & 1;  // this wave's 32x32 block of a 64x64 matrix
+  const int rb = wave >> 2, cb = wave & 3;  // this wave's 32-row, 32-column block
   const int j0 = c * kB;
   const ChunkIn ci{grows + sq.tok_off, sq.n_tok, sq.n_replay};
   f16_t* Kk = Th;
 
-  {
+  if (tid < 256) {
     BwdRegs nx;
     TinvRegs tx;
     fetch_tinv(tinv + ((int64_t)item * H + head) * kTinv, tid, tx);
@@ -981,170 +983,133 @@ __global__ __launch_bounds__(256, 1) void gdn_bpar_kernel(
           reinterpret_cast<const uint4*>(src)[m];
     bwd_commit<true>(nx, Kr, Qr, dOr, dRr, rw, gs, bs, al, tid);
     commit_tinv(tx, Th, Tl, Pr, tid);
-  }
-  if (tid < kB) {  // each row's destination, looked up once
-    const int t = tid, row = rw[t], j = j0 + t;
-    const int rs = row >= 0 ? rep_slot[row] : -1;
-    int kind;
-    int64_t off;
-    if (j >= sq.n_tok) {
-      kind = 0;
-      off = 0;
-    } else if (j < sq.n_replay) {
-      kind = 1;
-      off = ((int64_t)(sq.rep_off + j) * H + head) * kRep;
-    } else if (rs >= 0) {
-      kind = 2;
-      off = ((int64_t)rs * H + head) * 2 * kD;
-    } else {
-      kind = 3;
-      off = ((int64_t)row * H + head) * kD;
+    if (tid < kB) {  // each row's destination, looked up once; the decay factors
+      const int t = tid, row = rw[t], j = j0 + t;
+      const int rs = row >= 0 ? rep_slot[row] : -1;
+      int kind;
+      int64_t off;
+      if (j >= sq.n_tok) {
+        kind = 0;
+        off = 0;
+      } else if (j < sq.n_replay) {
+        kind = 1;
+        off = ((int64_t)(sq.rep_off + j) * H + head) * kRep;
+      } else if (rs >= 0) {
+        kind = 2;
+        off = ((int64_t)rs * H + head) * 2 * kD;
+      } else {
+        kind = 3;
+        off = ((int64_t)row * H + head) * kD;
+      }
+      dst_kind[t] = kind;
+      dst_off[t] = off;
     }
-    dst_kind[t] = kind;
-    dst_off[t] = off;
   }
   red_dg[wave][lane] = 0.f;
   red_g[wave][lane] = 0.f;
   red_b[wave][lane] = 0.f;
   red_e[wave][lane] = 0.f;
   __syncthreads();
+  if (tid < kB) {
+    gam[tid] = __expf(gs[tid]);
+    egam[tid] = __expf(gs[kB - 1] - gs[tid]);
+  }
   const f16_t* S0n = states + ((int64_t)(sq.chunk_off + c) * H + head) * 2 * kD * kD;
   const f16_t* S0t = S0n + kD * kD;
   const float g63 = gs[kB - 1];
-  const int cc = 32 * wave + l32;
-  // S0 fragments with the contraction over dv: this wave's dk rows 32 wave .. of the
-  // transposed copy, read once for <dS, S0>, dQ and dK
+  const int cc = 32 * cb + l32;
+  // S0 fragments with the contraction over dv: dk rows 32 cb .. of the transposed copy,
+  // read once for <dS, S0>, dQ and dK
   f16x8 s0f[8];
 #pragma unroll
-  for (int s = 0; s < 8; ++s) s0f[s] = frag_g(S0t, 32 * wave, 16 * s, lane);
+  for (int s = 0; s < 8; ++s) s0f[s] = frag_g(S0t, 32 * cb, 16 * s, lane);
+  __syncthreads();
 
   // -- R = diag(beta) (V - diag(gamma) K S0^T) (fp16), then U = T R --------------------------
-  f32x16 ks[2];  // K S0^T: used for R here and for R's beta/gamma derivatives below
+  f32x16 ks = zero16();  // K S0^T: used for R here and for R's beta/gamma derivatives below
   {
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) ks[b2] = zero16();
+    for (int s = 0; s < 8; ++s)
+      ks = mfma(frag_n(Kr, LDK, 32 * rb, 16 * s, lane), frag_g(S0n, 32 * cb, 16 * s, lane), ks);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const f16x8 b = frag_g(S0n, 32 * wave, 16 * s, lane);
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) ks[b2] = mfma(frag_n(Kr, LDK, 32 * b2, 16 * s, lane), b, ks[b2]);
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * rb + acc_row(r, hi);
+      const float vv = (float)dRr[t * LDK + cc];  // V rows, staged by bwd_commit
+      Ur[t * LDK + cc] = (f16_t)(bs[t] * (vv - gam[t] * ks[r]));
     }
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * b2 + acc_row(r, hi);
-        const float vv = (float)dRr[t * LDK + cc];  // V rows, staged by bwd_commit
-        Ur[t * LDK + cc] = (f16_t)(bs[t] * (vv - __expf(gs[t]) * ks[b2][r]));
-      }
   }
   __syncthreads();
   {
-    f32x16 u[2];
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) u[b2] = zero16();
+    f32x16 u = zero16();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const f16x8 b = frag_t(Ur, LDK, 16 * s, 32 * wave, lane);
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        u[b2] = mfma(frag_n(Th, LDP, 32 * b2, 16 * s, lane), b, u[b2]);
-        u[b2] = mfma(frag_n(Tl, LDP, 32 * b2, 16 * s, lane), b, u[b2]);
-      }
+      const f16x8 b = frag_t(Ur, LDK, 16 * s, 32 * cb, lane);
+      u = mfma(frag_n(Th, LDP, 32 * rb, 16 * s, lane), b, u);
+      u = mfma(frag_n(Tl, LDP, 32 * rb, 16 * s, lane), b, u);
     }
     __syncthreads();  // every wave has read R
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Ur[(32 * b2 + acc_row(r, hi)) * LDK + cc] = (f16_t)u[b2][r];
+    for (int r = 0; r < 16; ++r) Ur[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)u[r];
   }
 
   // -- dU = scale P^T dO + diag(E_63,.) K dS^T --------------------------------------------
   {
-    f32x16 du[2];
+    f32x16 du = zero16();
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) du[b2] = zero16();
+    for (int s = 0; s < 8; ++s)
+      du = mfma(frag_n(Kr, LDK, 32 * rb, 16 * s, lane), frag_n(dSh, LDK, 32 * cb, 16 * s, lane), du);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const f16x8 b = frag_n(dSh, LDK, 32 * wave, 16 * s, lane);
+    for (int r = 0; r < 16; ++r) du[r] *= egam[32 * rb + acc_row(r, hi)];
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) du[b2] = mfma(frag_n(Kr, LDK, 32 * b2, 16 * s, lane), b, du[b2]);
-    }
+    for (int s = 0; s < 4; ++s)
+      du = mfma(frag_t(Pr, LDP, 16 * s, 32 * rb, lane), frag_t(dOr, LDK, 16 * s, 32 * cb, lane), du);
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) du[b2][r] *= __expf(g63 - gs[32 * b2 + acc_row(r, hi)]);
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8 b = frag_t(dOr, LDK, 16 * s, 32 * wave, lane);
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) du[b2] = mfma(frag_t(Pr, LDP, 16 * s, 32 * b2, lane), b, du[b2]);
-    }
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dRr[(32 * b2 + acc_row(r, hi)) * LDK + cc] = (f16_t)du[b2][r];
+    for (int r = 0; r < 16; ++r) dRr[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)du[r];
   }
   __syncthreads();
 
   // -- dR = (I + A)^{-T} dU = T^T dU; dV = diag(beta) dR ---------------------------------------
   {
-    f32x16 dr[2];
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) dr[b2] = zero16();
+    f32x16 dr = zero16();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const f16x8 b = frag_t(dRr, LDK, 16 * s, 32 * wave, lane);
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        dr[b2] = mfma(frag_t(Th, LDP, 16 * s, 32 * b2, lane), b, dr[b2]);
-        dr[b2] = mfma(frag_t(Tl, LDP, 16 * s, 32 * b2, lane), b, dr[b2]);
-      }
+      const f16x8 b = frag_t(dRr, LDK, 16 * s, 32 * cb, lane);
+      dr = mfma(frag_t(Th, LDP, 16 * s, 32 * rb, lane), b, dr);
+      dr = mfma(frag_t(Tl, LDP, 16 * s, 32 * rb, lane), b, dr);
     }
     __syncthreads();  // every wave has read dU and T
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * b2 + acc_row(r, hi);
-        dRr[t * LDK + cc] = (f16_t)dr[b2][r];
-        const int kind = dst_kind[t];
-        const int64_t off = dst_off[t];
-        const float g = bs[t] * dr[b2][r];
-        if (kind == 1) rbuf[off + kD + cc] = g;
-        else if (kind == 2) rside[off + kD + cc] = g;
-        else if (kind == 3) st_g<TG>(dv + off + cc, g);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * rb + acc_row(r, hi);
+      dRr[t * LDK + cc] = (f16_t)dr[r];
+      const int kind = dst_kind[t];
+      const int64_t off = dst_off[t];
+      const float g = bs[t] * dr[r];
+      if (kind == 1) rbuf[off + kD + cc] = g;
+      else if (kind == 2) rside[off + kD + cc] = g;
+      else if (kind == 3) st_g<TG>(dv + off + cc, g);
+    }
   }
   __syncthreads();
 
-  // V rows for sum_c dR[t][c] V[t][c] (beta's derivative through R): thread (t, part)
-  // takes row t's columns 32 part .. 32 part + 31 as four 16-byte pieces, read here and
-  // used after the products below
-  uint4 vrow[4];
+  // -- <dS, S0> for the decay of the whole chunk: this wave's dk columns, dv rows 64 rb .. --
   {
-    const int t = tid >> 2, part = tid & 3;
-    const int row = rw[t];
-#pragma unroll
-    for (int m = 0; m < 4; ++m)
-      vrow[m] = row >= 0 ? *reinterpret_cast<const uint4*>(v + ((int64_t)row * H + head) * kD + 32 * part + 8 * m)
-                         : make_uint4(0, 0, 0, 0);
-  }
-  // -- <dS, S0> for the decay of the whole chunk ------------------------------------------
-  {
-    // lane holds S0[16 s + 8 hi + j][32 wave + l32] in s0f[s][j]
+    // lane holds S0[16 s + 8 hi + j][32 cb + l32] in s0f[s][j]
     float s = 0.f;
 #pragma unroll
-    for (int sb = 0; sb < 8; ++sb)
+    for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        s += (float)dSh[(16 * sb + 8 * hi + j) * LDK + 32 * wave + l32] * (float)s0f[sb][j];
+      for (int j = 0; j < 8; ++j) {
+        const int d = 16 * (4 * rb + sb) + 8 * hi + j;
+        s += (float)dSh[d * LDK + cc] * (float)(rb ? s0f[4 + sb][j] : s0f[sb][j]);
+      }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
     if (lane == 0) red_s[wave] = s;
   }
-  // -- dP = dO U^T, dA = -dR U^T on this wave's block -----------------------------------------
-  {
+  // -- dP = dO U^T, dA = -dR U^T on block (bm, bn), waves 0..3 ---------------------------------
+  if (wave < 4) {
+    const int bm = wave >> 1, bn = wave & 1;
     f32x16 dp = zero16(), da = zero16(), kk = zero16(), qk = zero16();
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
@@ -1180,28 +1145,16 @@ __global__ __launch_bounds__(256, 1) void gdn_bpar_kernel(
       red_b[wave][t] += rz;
     }
     if (hi == 0) red_dg[wave][i] -= cs;
-  }
-  // -- R's dependence on beta and gamma ------------------------------------------------------
+  } else {
+    // sum_c dR[t][c] V[t][c] (beta's derivative through R), on the waves the block above
+    // leaves idle: thread (t, part) takes row t's columns 32 part .. 32 part + 31
+    const int t = (tid - 256) >> 2, part = tid & 3;
+    const int row = rw[t];
+    uint4 vrow[4];
 #pragma unroll
-  for (int b2 = 0; b2 < 2; ++b2) {
-    float xb[16], xg[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * b2 + acc_row(r, hi);
-      const float dr = (float)dRr[t * LDK + cc];
-      xb[r] = -dr * __expf(gs[t]) * ks[b2][r];  // the dR V part is red_v
-      xg[r] = -bs[t] * dr * ks[b2][r];
-    }
-    const float sb = rowsum16(xb, lane);
-    const float sg = rowsum16(xg, lane);
-    if (!(lane & 1)) {
-      const int t = 32 * b2 + acc_row(rowsum16_elem(lane), hi);
-      red_b[wave][t] += sb;
-      red_g[wave][t] += sg;
-    }
-  }
-  {
-    const int t = tid >> 2, part = tid & 3;
+    for (int m = 0; m < 4; ++m)
+      vrow[m] = row >= 0 ? *reinterpret_cast<const uint4*>(v + ((int64_t)row * H + head) * kD + 32 * part + 8 * m)
+                         : make_uint4(0, 0, 0, 0);
     float acc = 0.f;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -1217,120 +1170,119 @@ __global__ __launch_bounds__(256, 1) void gdn_bpar_kernel(
     acc += __shfl_xor(acc, 2);
     if (part == 0) red_v[t] = acc;
   }
+  // -- R's dependence on beta and gamma ------------------------------------------------------
+  {
+    float xb[16], xg[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * rb + acc_row(r, hi);
+      const float dr = (float)dRr[t * LDK + cc];
+      xb[r] = -dr * gam[t] * ks[r];  // the dR V part is red_v
+      xg[r] = -bs[t] * dr * ks[r];
+    }
+    const float sb = rowsum16(xb, lane);
+    const float sg = rowsum16(xg, lane);
+    if (!(lane & 1)) {
+      const int t = 32 * rb + acc_row(rowsum16_elem(lane), hi);
+      red_b[wave][t] += sb;
+      red_g[wave][t] += sg;
+    }
+  }
+  __syncthreads();  // dP~ and dKk (waves 0..3) are read by every wave below
+
   // -- dQ = scale diag(gamma) dO S0 + dP~ K ----------------------------------------------------
   {
-    f32x16 aq[2];
+    f32x16 aq = zero16();
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) aq[b2] = zero16();
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const f16x8 b = s0f[s];
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) aq[b2] = mfma(frag_n(dOr, LDK, 32 * b2, 16 * s, lane), b, aq[b2]);
-    }
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
+    for (int s = 0; s < 8; ++s) aq = mfma(frag_n(dOr, LDK, 32 * rb, 16 * s, lane), s0f[s], aq);
+    {
       float xg[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = 32 * b2 + acc_row(r, hi);
-        xg[r] = scale * aq[b2][r] * (float)Qr[t * LDK + cc];
-        aq[b2][r] *= scale * __expf(gs[t]);
+        const int t = 32 * rb + acc_row(r, hi);
+        xg[r] = scale * aq[r] * (float)Qr[t * LDK + cc];
+        aq[r] *= scale * gam[t];
       }
       const float sg = rowsum16(xg, lane);
-      if (!(lane & 1)) red_g[wave][32 * b2 + acc_row(rowsum16_elem(lane), hi)] += sg;
+      if (!(lane & 1)) red_g[wave][32 * rb + acc_row(rowsum16_elem(lane), hi)] += sg;
     }
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8 b = frag_t(Kr, LDK, 16 * s, 32 * wave, lane);
+    for (int s = 0; s < 4; ++s)
+      aq = mfma(frag_n(Pr, LDP, 32 * rb, 16 * s, lane), frag_t(Kr, LDK, 16 * s, 32 * cb, lane), aq);
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) aq[b2] = mfma(frag_n(Pr, LDP, 32 * b2, 16 * s, lane), b, aq[b2]);
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * rb + acc_row(r, hi);
+      const int j = j0 + t;
+      if (j >= sq.n_replay && j < sq.n_tok) st_g<TG>(dq + ((int64_t)rw[t] * H + head) * kD + cc, aq[r]);
     }
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * b2 + acc_row(r, hi);
-        const int j = j0 + t;
-        if (j >= sq.n_replay && j < sq.n_tok) st_g<TG>(dq + ((int64_t)rw[t] * H + head) * kD + cc, aq[b2][r]);
-      }
   }
   // -- dK = dP~^T Q + dKk K + dKk^T K + diag(E_63,.) U dS - diag(beta gamma) dR S0 -----------
   {
-    f32x16 ak[2];
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) ak[b2] = zero16();
+    f32x16 ak = zero16();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const f16x8 bq = frag_t(Qr, LDK, 16 * s, 32 * wave, lane);
-      const f16x8 bk = frag_t(Kr, LDK, 16 * s, 32 * wave, lane);
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) {
-        ak[b2] = mfma(frag_t(Pr, LDP, 16 * s, 32 * b2, lane), bq, ak[b2]);
-        ak[b2] = mfma(frag_n(Kk, LDP, 32 * b2, 16 * s, lane), bk, ak[b2]);
-        ak[b2] = mfma(frag_t(Kk, LDP, 16 * s, 32 * b2, lane), bk, ak[b2]);
-      }
+      const f16x8 bq = frag_t(Qr, LDK, 16 * s, 32 * cb, lane);
+      const f16x8 bk = frag_t(Kr, LDK, 16 * s, 32 * cb, lane);
+      ak = mfma(frag_t(Pr, LDP, 16 * s, 32 * rb, lane), bq, ak);
+      ak = mfma(frag_n(Kk, LDP, 32 * rb, 16 * s, lane), bk, ak);
+      ak = mfma(frag_t(Kk, LDP, 16 * s, 32 * rb, lane), bk, ak);
     }
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
+    {
       f32x16 ud = zero16();
 #pragma unroll
       for (int s = 0; s < 8; ++s)
-        ud = mfma(frag_n(Ur, LDK, 32 * b2, 16 * s, lane), frag_t(dSh, LDK, 16 * s, 32 * wave, lane), ud);
+        ud = mfma(frag_n(Ur, LDK, 32 * rb, 16 * s, lane), frag_t(dSh, LDK, 16 * s, 32 * cb, lane), ud);
       float xe[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = 32 * b2 + acc_row(r, hi);
+        const int t = 32 * rb + acc_row(r, hi);
         xe[r] = ud[r] * (float)Kr[t * LDK + cc];
-        ak[b2][r] = fmaf(__expf(g63 - gs[t]), ud[r], ak[b2][r]);
+        ak[r] = fmaf(egam[t], ud[r], ak[r]);
       }
       const float se = rowsum16(xe, lane);
-      if (!(lane & 1)) red_e[wave][32 * b2 + acc_row(rowsum16_elem(lane), hi)] += se;
+      if (!(lane & 1)) red_e[wave][32 * rb + acc_row(rowsum16_elem(lane), hi)] += se;
     }
-#pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2) {
+    {
       f32x16 rs0 = zero16();
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
-        rs0 = mfma(frag_n(dRr, LDK, 32 * b2, 16 * s, lane), s0f[s], rs0);
+      for (int s = 0; s < 8; ++s) rs0 = mfma(frag_n(dRr, LDK, 32 * rb, 16 * s, lane), s0f[s], rs0);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = 32 * b2 + acc_row(r, hi);
-        ak[b2][r] = fmaf(-bs[t] * __expf(gs[t]), rs0[r], ak[b2][r]);
+        const int t = 32 * rb + acc_row(r, hi);
+        ak[r] = fmaf(-bs[t] * gam[t], rs0[r], ak[r]);
       }
     }
 #pragma unroll
-    for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * b2 + acc_row(r, hi);
-        const int kind = dst_kind[t];
-        const int64_t off = dst_off[t];
-        if (kind == 1) rbuf[off + cc] = ak[b2][r];
-        else if (kind == 2) rside[off + cc] = ak[b2][r];
-        else if (kind == 3) st_g<TG>(dk + off + cc, ak[b2][r]);
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int t = 32 * rb + acc_row(r, hi);
+      const int kind = dst_kind[t];
+      const int64_t off = dst_off[t];
+      if (kind == 1) rbuf[off + cc] = ak[r];
+      else if (kind == 2) rside[off + cc] = ak[r];
+      else if (kind == 3) st_g<TG>(dk + off + cc, ak[r]);
+    }
   }
   __syncthreads();
 
   // -- per-token dbeta, dalpha (reverse cumulative sum of dg) --------------------------------
   if (tid < kB) {
     const int t = tid;
-    const float en = __expf(g63 - gs[t]);
-    float e_t = 0.f, dgp = 0.f, dgam = 0.f, db = 0.f;
+    const float en = egam[t];
+    float e_t = 0.f, dgp = 0.f, dgam = 0.f, db = 0.f, ss = 0.f;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kW; ++w) {
       dgp += red_dg[w][t];
       dgam += red_g[w][t];
       db += red_b[w][t];
       e_t += red_e[w][t];
+      ss += red_s[w];
     }
     db += red_v[t];
-    float dg = dgp + __expf(gs[t]) * dgam - e_t * en;
+    float dg = dgp + gam[t] * dgam - e_t * en;
     float tot = e_t * en;  // sum over the chunk of dEn_i E_63,i goes to g_63
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off);
-    if (t == kB - 1) dg += tot + __expf(g63) * (red_s[0] + red_s[1] + red_s[2] + red_s[3]);
+    if (t == kB - 1) dg += tot + gam[kB - 1] * ss;
     // reverse inclusive scan: dlogalpha_t = sum_{s >= t} dg_s
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -1341,16 +1293,15 @@ __global__ __launch_bounds__(256, 1) void gdn_bpar_kernel(
     if (j < sq.n_tok) {
       const float da = dg / al[t];
       if (j < sq.n_replay) {
-        float* rb = rbuf + ((int64_t)(sq.rep_off + j) * H + head) * kRep;
-        rb[2 * kD] = db;
-        rb[2 * kD + 1] = da;
+        float* rb_ = rbuf + ((int64_t)(sq.rep_off + j) * H + head) * kRep;
+        rb_[2 * kD] = db;
+        rb_[2 * kD + 1] = da;
       } else {
         dbeta[(int64_t)rw[t] * H + head] = db;
         dalpha[(int64_t)rw[t] * H + head] = da;
       }
     }
   }
-  __syncthreads();
 }
 
 // Rows that are replayed somewhere: own contribution (kept in fp32) plus every
@@ -1438,7 +1389,7 @@ void launch_gdn_bpar(const GdnShape& s, int item0, int n_items, const bf16_t* q,
                      const f16_t* tinv, const f16_t* dsend, TG* dq, TG* dk, TG* dv, float* dbeta, float* dalpha,
                      float* rside, float* rbuf, hipStream_t st) {
   if (n_items <= 0) return;
-  gdn::gdn_bpar_kernel<TG><<<dim3((unsigned)(n_items * s.H)), 256, 0, st>>>(
+  gdn::gdn_bpar_kernel<TG><<<dim3((unsigned)(n_items * s.H)), 512, 0, st>>>(
       s.seqs, s.items, item0, s.rows, s.rep_slot, q, k, v, beta, alpha, dO, states, tinv, dsend, dq, dk, dv, dbeta,
       dalpha, rside, rbuf, s.H, s.scale);
 }
