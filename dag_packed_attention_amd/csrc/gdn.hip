@@ -174,34 +174,49 @@ struct ChunkIn {
   int n_tok, n_replay;
 };
 
-// Write the state accumulators (wave w: dv rows 32 w .., four dk blocks) as fp16 into
-// an LDS tile [dv][LDK].
-__device__ __forceinline__ void state_to_lds(const f32x16 (&S)[4], f16_t* Sh, int wave, int lane) {
+// Eight-wave state layout: wave (rb, cb) holds dv rows 32 cb .. and dk blocks 2 rb and
+// 2 rb + 1 (accumulator element r of S[b] is row 32 cb + acc_row(r, hi), column
+// 32 (2 rb + b) + lane % 32).
+__device__ __forceinline__ void state_to_lds8(const f32x16 (&S)[2], f16_t* Sh, int cb, int rb, int lane) {
   const int hi = lane >> 5, l32 = lane & 31;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb)
+  for (int b = 0; b < 2; ++b)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Sh[(32 * wave + acc_row(r, hi)) * LDK + 32 * nb + l32] = (f16_t)S[nb][r];
+    for (int r = 0; r < 16; ++r) Sh[(32 * cb + acc_row(r, hi)) * LDK + 32 * (2 * rb + b) + l32] = (f16_t)S[b][r];
 }
-
-// Save the state as fp16 in both layouts: [dv][dk] then [dk][dv].
-__device__ __forceinline__ void state_save(const f32x16 (&S)[4], f16_t* __restrict__ dst, int wave, int lane) {
+__device__ __forceinline__ void state_save8(const f32x16 (&S)[2], f16_t* __restrict__ dst, int cb, int rb, int lane) {
   const int hi = lane >> 5, l32 = lane & 31;
   f16_t* nat = dst;
   f16_t* tr = dst + kD * kD;
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
+  for (int b = 0; b < 2; ++b) {
+    const int nb = 2 * rb + b;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) nat[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32] = (f16_t)S[nb][r];
+    for (int r = 0; r < 16; ++r) nat[(32 * cb + acc_row(r, hi)) * kD + 32 * nb + l32] = (f16_t)S[b][r];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       typedef __attribute__((ext_vector_type(4))) _Float16 f16x4;
       f16x4 w;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) w[j] = (f16_t)S[nb][4 * r4 + j];
-      *reinterpret_cast<f16x4*>(tr + (32 * nb + l32) * kD + 32 * wave + 8 * r4 + 4 * hi) = w;
+      for (int j = 0; j < 4; ++j) w[j] = (f16_t)S[b][4 * r4 + j];
+      *reinterpret_cast<f16x4*>(tr + (32 * nb + l32) * kD + 32 * cb + 8 * r4 + 4 * hi) = w;
     }
   }
+}
+// fp32 [dv][dk] state in global memory <-> the eight-wave accumulators
+__device__ __forceinline__ void state_load8(f32x16 (&S)[2], const float* __restrict__ src, int cb, int rb, int lane) {
+  const int hi = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) S[b][r] = src[(32 * cb + acc_row(r, hi)) * kD + 32 * (2 * rb + b) + l32];
+}
+__device__ __forceinline__ void state_store8(const f32x16 (&S)[2], float* __restrict__ dst, int cb, int rb, int lane) {
+  const int hi = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[(32 * cb + acc_row(r, hi)) * kD + 32 * (2 * rb + b) + l32] = S[b][r];
 }
 
 // The next chunk's inputs, fetched into registers while the current chunk
@@ -550,13 +565,32 @@ __device__ __forceinline__ void commit_tinv(const TinvRegs& nx, f16_t* Th, f16_t
   *reinterpret_cast<uint4*>(Pr + o1) = nx.p1;
 }
 
+// The same with 512 threads: one 16-byte piece of each tile a thread (plain vector
+// types, which the compiler keeps in registers).
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+struct TinvRegs8 {
+  u32x4 h, l, p;
+};
+__device__ __forceinline__ void fetch_tinv8(const f16_t* __restrict__ src, int tid, TinvRegs8& nx) {
+  const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+  nx.h = s4[tid];
+  nx.l = s4[512 + tid];
+  nx.p = s4[1024 + tid];
+}
+__device__ __forceinline__ void commit_tinv8(const TinvRegs8& nx, f16_t* Th, f16_t* Tl, f16_t* Pr, int tid) {
+  const int o = (tid >> 3) * LDP + 8 * (tid & 7);  // row tid / 8, columns 8 (tid % 8) ..
+  *reinterpret_cast<u32x4*>(Th + o) = nx.h;
+  *reinterpret_cast<u32x4*>(Tl + o) = nx.l;
+  *reinterpret_cast<u32x4*>(Pr + o) = nx.p;
+}
+
 // ---------------------------------------------------------------------------------
 // Forward.  kOut: the outputs; kSave: every chunk's starting state, saved for the
 // backward.  Outputs alone are the plain forward, states alone the backward's
 // recomputation, both a forward that keeps its states.  All export boundary states.
 // ---------------------------------------------------------------------------------
 template <bool kOut, bool kSave>
-__global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
+__global__ __launch_bounds__(512, 1) void gdn_fwd_kernel(
     const GSeq* __restrict__ seqs, const int32_t* __restrict__ order, const int32_t* __restrict__ grows,
     const GExport* __restrict__ exports, const bf16_t* __restrict__ q, const bf16_t* __restrict__ k,
     const bf16_t* __restrict__ v, const float* __restrict__ beta, const float* __restrict__ alpha,
@@ -571,7 +605,7 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
   __shared__ __attribute__((aligned(16))) f16_t Tl[kB * LDP];
   // V rows (fp32, exact) in; then R as fp16 high and low parts, two [64][LDK] tiles
   __shared__ __attribute__((aligned(16))) float Rr[(2 * kB * LDK) / 2];
-  __shared__ float gs[kB], bs[kB];
+  __shared__ float gs[kB], bs[kB], gam[kB], egam[kB];
   __shared__ int rw[kB], rwn[kB];
   static_assert(kB * LDR <= 2 * kB * LDK / 2, "the V rows fit the R tiles");
   f16_t* Rh = reinterpret_cast<f16_t*>(Rr);
@@ -580,39 +614,41 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
   const int head = blockIdx.x % H;
   const GSeq sq = seqs[order[blockIdx.x / H]];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int rb = wave >> 2, cb = wave & 3;
+  const bool stager = tid < 256;  // the first four waves fetch and commit the chunk inputs
   const int nch = (sq.n_tok + kB - 1) / kB;
   const ChunkIn ci{grows + sq.tok_off, sq.n_tok, sq.n_replay};
   const f16_t* tinv_seq = tinv + (int64_t)sq.item0 * H * kTinv + (int64_t)head * kTinv;
   const int64_t tinv_step = (int64_t)H * kTinv;
 
-  f32x16 S[4];
+  f32x16 S[2];
   if (sq.init_slot >= 0) {
-    const float* src = slots + ((int64_t)sq.init_slot * H + head) * kD * kD;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) S[nb][r] = src[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32];
+    state_load8(S, slots + ((int64_t)sq.init_slot * H + head) * kD * kD, cb, rb, lane);
   } else {
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) S[nb] = zero16();
+    for (int b2 = 0; b2 < 2; ++b2) S[b2] = zero16();
   }
-  state_to_lds(S, Sh, wave, lane);
-  if (kSave) state_save(S, states + ((int64_t)sq.chunk_off * H + head) * 2 * kD * kD, wave, lane);
+  state_to_lds8(S, Sh, cb, rb, lane);
+  if (kSave) state_save8(S, states + ((int64_t)sq.chunk_off * H + head) * 2 * kD * kD, cb, rb, lane);
   int ex = sq.exp_off;
   const int ex_end = sq.exp_off + sq.exp_cnt;
 
   // chunk 0 is fetched up front; chunk c + 1's inputs are fetched during chunk c
   ChunkRegs nx;
   if (nch > 0) {
-    TinvRegs t0;
-    fetch_tinv(tinv_seq, tid, t0);
-    commit_tinv(t0, Th, Tl, Pr, tid);
+    TinvRegs8 t0;
+    fetch_tinv8(tinv_seq, tid, t0);
+    commit_tinv8(t0, Th, Tl, Pr, tid);
   }
-  fetch_rows(ci, 0, beta, alpha, H, head, tid, nx);
-  if (tid < kB) rwn[tid] = nx.row;
+  if (stager) {
+    fetch_rows(ci, 0, beta, alpha, H, head, tid, nx);
+    if (tid < kB) rwn[tid] = nx.row;
+  }
   __syncthreads();
-  fetch_kqv(rwn, k, q, v, H, head, tid, nx);
-  commit_chunk(nx, Kr, Qr, Rr, rw, gs, bs, tid);
+  if (stager) {
+    fetch_kqv(rwn, k, q, v, H, head, tid, nx);
+    commit_chunk(nx, Kr, Qr, Rr, rw, gs, bs, tid);
+  }
   __syncthreads();
 
   for (int c = 0; c < nch; ++c) {
@@ -620,138 +656,109 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
     int tid_o = threadIdx.x;
     asm volatile("" : "+v"(tid_o));
     const int tid = tid_o, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+    const int rb = wave >> 2, cb = wave & 3;
     const int j0 = c * kB;
     const bool has_next = c + 1 < nch;
-    if (has_next) fetch_rows(ci, j0 + kB, beta, alpha, H, head, tid, nx);
-    const int cc = 32 * wave + l32;
-    TinvRegs tx;
+    if (has_next && stager) fetch_rows(ci, j0 + kB, beta, alpha, H, head, tid, nx);
+    if (tid < kB) {
+      gam[tid] = __expf(gs[tid]);
+      egam[tid] = __expf(gs[kB - 1] - gs[tid]);
+    }
+    const int cc = 32 * cb + l32;
+    TinvRegs8 tx;
 
     // -- R = diag(beta) (V - diag(gamma) K S0^T), split into fp16 high and low parts ------
     {
-      f32x16 ks[2];
+      f32x16 ks = zero16();
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm) ks[bm] = zero16();
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 b = frag_n(Sh, LDK, 32 * wave, 16 * s, lane);
-#pragma unroll
-        for (int bm = 0; bm < 2; ++bm) ks[bm] = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), b, ks[bm]);
-      }
-#pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * bm + acc_row(r, hi);
-          ks[bm][r] = bs[t] * (Rr[t * LDR + cc] - __expf(gs[t]) * ks[bm][r]);  // V in, R out
-        }
+      for (int s = 0; s < 8; ++s)
+        ks = mfma(frag_n(Kr, LDK, 32 * rb, 16 * s, lane), frag_n(Sh, LDK, 32 * cb, 16 * s, lane), ks);
       if (tid < kB) rwn[tid] = has_next ? nx.row : -1;
+      __syncthreads();  // the decay factors are in place
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * rb + acc_row(r, hi);
+        ks[r] = bs[t] * (Rr[t * LDR + cc] - gam[t] * ks[r]);  // V in, R out
+      }
       __syncthreads();  // every V row read: the R tiles overwrite them
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * bm + acc_row(r, hi);
-          const f16_t h = (f16_t)ks[bm][r];
-          Rh[t * LDK + cc] = h;
-          Rl[t * LDK + cc] = (f16_t)(ks[bm][r] - (float)h);
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * rb + acc_row(r, hi);
+        const f16_t h = (f16_t)ks[r];
+        Rh[t * LDK + cc] = h;
+        Rl[t * LDK + cc] = (f16_t)(ks[r] - (float)h);
+      }
     }
-    if (has_next) fetch_kqv(rwn, k, q, v, H, head, tid, nx);
+    if (has_next && stager) fetch_kqv(rwn, k, q, v, H, head, tid, nx);
     __syncthreads();
 
     // -- U = (I + A)^{-1} R = T R: T_hi R_hi + T_hi R_lo + T_lo R_hi ---------------------------
     {
-      f32x16 u[2];
-#pragma unroll
-      for (int bm = 0; bm < 2; ++bm) u[bm] = zero16();
+      f32x16 u = zero16();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const f16x8 bh = frag_t(Rh, LDK, 16 * s, 32 * wave, lane);
-        const f16x8 bl = frag_t(Rl, LDK, 16 * s, 32 * wave, lane);
-#pragma unroll
-        for (int bm = 0; bm < 2; ++bm) {
-          const f16x8 ah = frag_n(Th, LDP, 32 * bm, 16 * s, lane);
-          u[bm] = mfma(ah, bh, u[bm]);
-          u[bm] = mfma(ah, bl, u[bm]);
-          u[bm] = mfma(frag_n(Tl, LDP, 32 * bm, 16 * s, lane), bh, u[bm]);
-        }
+        const f16x8 bh = frag_t(Rh, LDK, 16 * s, 32 * cb, lane);
+        const f16x8 bl = frag_t(Rl, LDK, 16 * s, 32 * cb, lane);
+        const f16x8 ah = frag_n(Th, LDP, 32 * rb, 16 * s, lane);
+        u = mfma(ah, bh, u);
+        u = mfma(ah, bl, u);
+        u = mfma(frag_n(Tl, LDP, 32 * rb, 16 * s, lane), bh, u);
       }
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Ur[(32 * bm + acc_row(r, hi)) * LDK + cc] = (f16_t)u[bm][r];
+      for (int r = 0; r < 16; ++r) Ur[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)u[r];
     }
-    // the next chunk's T and P (issued here, where the R and U registers are free)
-    if (has_next) fetch_tinv(tinv_seq + (c + 1) * tinv_step, tid, tx);
+    // the next chunk's T and P (issued here, where the R and U registers are free; the
+    // last chunk fetches its own again)
+    fetch_tinv8(tinv_seq + (has_next ? c + 1 : c) * tinv_step, tid, tx);
     __syncthreads();
 
     // -- outputs: O = scale diag(gamma) Q S0^T + (scale E o QK) U -------------------------
     if (kOut) {
-      f32x16 acc_o[2];
+      f32x16 acc_o = zero16();
 #pragma unroll
-      for (int bm = 0; bm < 2; ++bm) acc_o[bm] = zero16();
+      for (int s = 0; s < 8; ++s)
+        acc_o = mfma(frag_n(Qr, LDK, 32 * rb, 16 * s, lane), frag_n(Sh, LDK, 32 * cb, 16 * s, lane), acc_o);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 b = frag_n(Sh, LDK, 32 * wave, 16 * s, lane);
+      for (int r = 0; r < 16; ++r) acc_o[r] *= scale * gam[32 * rb + acc_row(r, hi)];
 #pragma unroll
-        for (int bm = 0; bm < 2; ++bm) acc_o[bm] = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), b, acc_o[bm]);
+      for (int s = 0; s < 4; ++s)
+        acc_o = mfma(frag_n(Pr, LDP, 32 * rb, 16 * s, lane), frag_t(Ur, LDK, 16 * s, 32 * cb, lane), acc_o);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * rb + acc_row(r, hi);
+        const int j = j0 + t;
+        if (j >= sq.n_replay && j < sq.n_tok) o[((int64_t)rw[t] * H + head) * kD + cc] = f2bf(acc_o[r]);
       }
-#pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[bm][r] *= scale * __expf(gs[32 * bm + acc_row(r, hi)]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const f16x8 b = frag_t(Ur, LDK, 16 * s, 32 * wave, lane);
-#pragma unroll
-        for (int bm = 0; bm < 2; ++bm) acc_o[bm] = mfma(frag_n(Pr, LDP, 32 * bm, 16 * s, lane), b, acc_o[bm]);
-      }
-#pragma unroll
-      for (int bm = 0; bm < 2; ++bm)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int t = 32 * bm + acc_row(r, hi);
-          const int j = j0 + t;
-          if (j >= sq.n_replay && j < sq.n_tok)
-            o[((int64_t)rw[t] * H + head) * kD + 32 * wave + l32] = f2bf(acc_o[bm][r]);
-        }
     }
-    if (has_next) {  // T and P of this chunk are read: the next chunk's replace them
-      __syncthreads();
-      commit_tinv(tx, Th, Tl, Pr, tid);
-    }
+    __syncthreads();  // T and P of this chunk are read: the next chunk's replace them
+    commit_tinv8(tx, Th, Tl, Pr, tid);
 
     // -- state update: S <- gamma_63 S + (diag(E_63,.) U)^T K ------------------------------
     {
-      const float g63 = gs[kB - 1];
-      const float gn = __expf(g63);
+      const float gn = gam[kB - 1];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[nb][r] *= gn;
+        for (int r = 0; r < 16; ++r) S[b2][r] *= gn;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float e[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = __expf(g63 - gs[16 * s + 8 * hi + j]);
-        const f16x8 a = scale8(frag_t(Ur, LDK, 16 * s, 32 * wave, lane), e);
+        for (int j = 0; j < 8; ++j) e[j] = egam[16 * s + 8 * hi + j];
+        const f16x8 a = scale8(frag_t(Ur, LDK, 16 * s, 32 * cb, lane), e);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) S[nb] = mfma(a, frag_t(Kr, LDK, 16 * s, 32 * nb, lane), S[nb]);
+        for (int b2 = 0; b2 < 2; ++b2) S[b2] = mfma(a, frag_t(Kr, LDK, 16 * s, 32 * (2 * rb + b2), lane), S[b2]);
       }
     }
     if (ex < ex_end && exports[ex].chunk == c + 1) {
-      float* dst = slots + ((int64_t)exports[ex].slot * H + head) * kD * kD;
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dst[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32] = S[nb][r];
+      state_store8(S, slots + ((int64_t)exports[ex].slot * H + head) * kD * kD, cb, rb, lane);
       ++ex;
     }
     __syncthreads();
     if (has_next) {
-      commit_chunk(nx, Kr, Qr, Rr, rw, gs, bs, tid);
-      state_to_lds(S, Sh, wave, lane);
-      if (kSave) state_save(S, states + ((int64_t)(sq.chunk_off + c + 1) * H + head) * 2 * kD * kD, wave, lane);
+      if (stager) commit_chunk(nx, Kr, Qr, Rr, rw, gs, bs, tid);
+      state_to_lds8(S, Sh, cb, rb, lane);
+      if (kSave) state_save8(S, states + ((int64_t)(sq.chunk_off + c + 1) * H + head) * 2 * kD * kD, cb, rb, lane);
       __syncthreads();
     }
   }
@@ -766,7 +773,7 @@ __global__ __launch_bounds__(256, 1) void gdn_fwd_kernel(
 //   dS <- gamma_63 dS + scale (diag(gamma) dO)^T Q - (diag(beta gamma) dR)^T K.
 // At the sequence's start dS is its initial-state gradient.
 // ---------------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 1) void gdn_bscan_kernel(
+__global__ __launch_bounds__(512, 1) void gdn_bscan_kernel(
     const GSeq* __restrict__ seqs, const int32_t* __restrict__ order, const int32_t* __restrict__ grows,
     const GExport* __restrict__ exports, const int32_t* __restrict__ slot_off, const int32_t* __restrict__ slot_cons,
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ beta,
@@ -780,148 +787,131 @@ __global__ __launch_bounds__(256, 1) void gdn_bscan_kernel(
   __shared__ __attribute__((aligned(16))) f16_t Pr[kB * LDP];
   __shared__ __attribute__((aligned(16))) f16_t Th[kB * LDP];
   __shared__ __attribute__((aligned(16))) f16_t Tl[kB * LDP];
-  __shared__ float gs[kB], bs[kB], al[kB];
+  __shared__ float gs[kB], bs[kB], al[kB], gam[kB], egam[kB];
   __shared__ int rw[kB];
 
   const int head = blockIdx.x % H;
   const GSeq sq = seqs[order[blockIdx.x / H]];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rb = wave >> 2, cb = wave & 3;
+  const bool stager = tid < 256;  // the first four waves fetch and commit the chunk inputs
   const int nch = (sq.n_tok + kB - 1) / kB;
   const ChunkIn ci{grows + sq.tok_off, sq.n_tok, sq.n_replay};
   const f16_t* tinv_seq = tinv + (int64_t)sq.item0 * H * kTinv + (int64_t)head * kTinv;
   const int64_t tinv_step = (int64_t)H * kTinv;
 
-  f32x16 D[4];  // dS: dv rows 32 wave .., four dk blocks
+  f32x16 D[2];  // dS, eight-wave state layout
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) D[nb] = zero16();
+  for (int b2 = 0; b2 < 2; ++b2) D[b2] = zero16();
   int ex = sq.exp_off + sq.exp_cnt - 1;
   BwdRegs nx;
-  TinvRegs tx;
+  TinvRegs8 tx;
   if (nch > 0) {
-    bwd_fetch_rows(ci, (nch - 1) * kB, tid, nx);
-    bwd_fetch_data<false>(ci, (nch - 1) * kB, k, q, dO, nullptr, beta, alpha, H, head, tid, nx);
-    fetch_tinv(tinv_seq + (nch - 1) * tinv_step, tid, tx);
+    if (stager) {
+      bwd_fetch_rows(ci, (nch - 1) * kB, tid, nx);
+      bwd_fetch_data<false>(ci, (nch - 1) * kB, k, q, dO, nullptr, beta, alpha, H, head, tid, nx);
+    }
+    fetch_tinv8(tinv_seq + (nch - 1) * tinv_step, tid, tx);
   }
 
   for (int c = nch - 1; c >= 0; --c) {
     int tid_o = threadIdx.x;
     asm volatile("" : "+v"(tid_o));
     const int tid = tid_o, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+    const int rb = wave >> 2, cb = wave & 3;
     const int j0 = c * kB;
     // -- consumers' initial-state gradients enter at exported boundaries ----------------
     if (ex >= sq.exp_off && exports[ex].chunk == c + 1) {
       const int slot = exports[ex].slot;
       for (int e = slot_off[slot]; e < slot_off[slot + 1]; ++e) {
-        const float* src = cgrad + ((int64_t)slot_cons[e] * H + head) * kD * kD;
+        f32x16 G[2];
+        state_load8(G, cgrad + ((int64_t)slot_cons[e] * H + head) * kD * kD, cb, rb, lane);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) D[nb][r] += src[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32];
+          for (int r = 0; r < 16; ++r) D[b2][r] += G[b2][r];
       }
       --ex;
     }
     {
       f16_t* dst = dsend + ((int64_t)(sq.item0 - round_item0 + c) * H + head) * kD * kD;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dst[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32] = (f16_t)D[nb][r];
+        for (int r = 0; r < 16; ++r)
+          dst[(32 * cb + acc_row(r, hi)) * kD + 32 * (2 * rb + b2) + l32] = (f16_t)D[b2][r];
     }
-    state_to_lds(D, dSh, wave, lane);
-    bwd_commit<false>(nx, Kr, Qr, dOr, nullptr, rw, gs, bs, al, tid);
-    commit_tinv(tx, Th, Tl, Pr, tid);
-    if (c > 0) {
-      bwd_fetch_rows(ci, j0 - kB, tid, nx);
-      fetch_tinv(tinv_seq + (c - 1) * tinv_step, tid, tx);
-    }
+    state_to_lds8(D, dSh, cb, rb, lane);
+    if (stager) bwd_commit<false>(nx, Kr, Qr, dOr, nullptr, rw, gs, bs, al, tid);
+    commit_tinv8(tx, Th, Tl, Pr, tid);
+    if (c > 0 && stager) bwd_fetch_rows(ci, j0 - kB, tid, nx);
+    fetch_tinv8(tinv_seq + (c > 0 ? c - 1 : c) * tinv_step, tid, tx);
     __syncthreads();
-    if (c > 0) bwd_fetch_data<false>(ci, j0 - kB, k, q, dO, nullptr, beta, alpha, H, head, tid, nx);
-    const float g63 = gs[kB - 1];
-    const int cc = 32 * wave + l32;
+    if (c > 0 && stager) bwd_fetch_data<false>(ci, j0 - kB, k, q, dO, nullptr, beta, alpha, H, head, tid, nx);
+    if (tid < kB) {
+      gam[tid] = __expf(gs[tid]);
+      egam[tid] = __expf(gs[kB - 1] - gs[tid]);
+    }
+    const int cc = 32 * cb + l32;
+    __syncthreads();
 
     // -- dU = diag(E_63,.) K dS^T + P^T dO ----------------------------------------------------
     {
-      f32x16 du[2];
+      f32x16 du = zero16();
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) du[b2] = zero16();
+      for (int s = 0; s < 8; ++s)
+        du = mfma(frag_n(Kr, LDK, 32 * rb, 16 * s, lane), frag_n(dSh, LDK, 32 * cb, 16 * s, lane), du);
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const f16x8 b = frag_n(dSh, LDK, 32 * wave, 16 * s, lane);
+      for (int r = 0; r < 16; ++r) du[r] *= egam[32 * rb + acc_row(r, hi)];
 #pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) du[b2] = mfma(frag_n(Kr, LDK, 32 * b2, 16 * s, lane), b, du[b2]);
-      }
+      for (int s = 0; s < 4; ++s)
+        du = mfma(frag_t(Pr, LDP, 16 * s, 32 * rb, lane), frag_t(dOr, LDK, 16 * s, 32 * cb, lane), du);
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) du[b2][r] *= __expf(g63 - gs[32 * b2 + acc_row(r, hi)]);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const f16x8 b = frag_t(dOr, LDK, 16 * s, 32 * wave, lane);
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) du[b2] = mfma(frag_t(Pr, LDP, 16 * s, 32 * b2, lane), b, du[b2]);
-      }
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dRr[(32 * b2 + acc_row(r, hi)) * LDK + cc] = (f16_t)du[b2][r];
+      for (int r = 0; r < 16; ++r) dRr[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)du[r];
     }
     __syncthreads();
     // -- dR = (I + A)^{-T} dU = T^T dU: T_hi^T dU + T_lo^T dU -----------------------------------
     {
-      f32x16 dr[2];
-#pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2) dr[b2] = zero16();
+      f32x16 dr = zero16();
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const f16x8 b = frag_t(dRr, LDK, 16 * s, 32 * wave, lane);
-#pragma unroll
-        for (int b2 = 0; b2 < 2; ++b2) {
-          dr[b2] = mfma(frag_t(Th, LDP, 16 * s, 32 * b2, lane), b, dr[b2]);
-          dr[b2] = mfma(frag_t(Tl, LDP, 16 * s, 32 * b2, lane), b, dr[b2]);
-        }
+        const f16x8 b = frag_t(dRr, LDK, 16 * s, 32 * cb, lane);
+        dr = mfma(frag_t(Th, LDP, 16 * s, 32 * rb, lane), b, dr);
+        dr = mfma(frag_t(Tl, LDP, 16 * s, 32 * rb, lane), b, dr);
       }
       __syncthreads();  // every wave has read dU
 #pragma unroll
-      for (int b2 = 0; b2 < 2; ++b2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) dRr[(32 * b2 + acc_row(r, hi)) * LDK + cc] = (f16_t)dr[b2][r];
+      for (int r = 0; r < 16; ++r) dRr[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)dr[r];
     }
     __syncthreads();
     // -- dS_prev = gamma_63 dS + scale (diag(gamma) dO)^T Q - (diag(beta gamma) dR)^T K -----------
     {
-      const float gn = __expf(g63);
+      const float gn = gam[kB - 1];
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
+      for (int b2 = 0; b2 < 2; ++b2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) D[nb][r] *= gn;
+        for (int r = 0; r < 16; ++r) D[b2][r] *= gn;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         float e1[8], e2[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int t = 16 * s + 8 * hi + j;
-          const float gam = __expf(gs[t]);
-          e1[j] = scale * gam;
-          e2[j] = -bs[t] * gam;
+          e1[j] = scale * gam[t];
+          e2[j] = -bs[t] * gam[t];
         }
-        const f16x8 a1 = scale8(frag_t(dOr, LDK, 16 * s, 32 * wave, lane), e1);
-        const f16x8 a2 = scale8(frag_t(dRr, LDK, 16 * s, 32 * wave, lane), e2);
+        const f16x8 a1 = scale8(frag_t(dOr, LDK, 16 * s, 32 * cb, lane), e1);
+        const f16x8 a2 = scale8(frag_t(dRr, LDK, 16 * s, 32 * cb, lane), e2);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          D[nb] = mfma(a1, frag_t(Qr, LDK, 16 * s, 32 * nb, lane), D[nb]);
-          D[nb] = mfma(a2, frag_t(Kr, LDK, 16 * s, 32 * nb, lane), D[nb]);
+        for (int b2 = 0; b2 < 2; ++b2) {
+          D[b2] = mfma(a1, frag_t(Qr, LDK, 16 * s, 32 * (2 * rb + b2), lane), D[b2]);
+          D[b2] = mfma(a2, frag_t(Kr, LDK, 16 * s, 32 * (2 * rb + b2), lane), D[b2]);
         }
       }
     }
     __syncthreads();
   }
-  if (sq.cgrad >= 0) {
-    float* dst = cgrad + ((int64_t)sq.cgrad * H + head) * kD * kD;
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dst[(32 * wave + acc_row(r, hi)) * kD + 32 * nb + l32] = D[nb][r];
-  }
+  if (sq.cgrad >= 0) state_store8(D, cgrad + ((int64_t)sq.cgrad * H + head) * kD * kD, cb, rb, lane);
 }
 
 // ---------------------------------------------------------------------------------
@@ -1364,13 +1354,13 @@ void launch_gdn_fwd(const GdnShape& s, int n_seq, const int32_t* order, const bf
   if (n_seq <= 0) return;
   const dim3 grid((unsigned)(n_seq * s.H));
   if (o && states)
-    gdn::gdn_fwd_kernel<true, true><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha,
+    gdn::gdn_fwd_kernel<true, true><<<grid, 512, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha,
                                                           tinv, o, slots, states, s.H, s.scale);
   else if (states)
-    gdn::gdn_fwd_kernel<false, true><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha,
+    gdn::gdn_fwd_kernel<false, true><<<grid, 512, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha,
                                                            tinv, o, slots, states, s.H, s.scale);
   else
-    gdn::gdn_fwd_kernel<true, false><<<grid, 256, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha,
+    gdn::gdn_fwd_kernel<true, false><<<grid, 512, 0, st>>>(s.seqs, order, s.rows, s.exports, q, k, v, beta, alpha,
                                                            tinv, o, slots, states, s.H, s.scale);
 }
 
@@ -1378,7 +1368,7 @@ void launch_gdn_bscan(const GdnShape& s, int n_seq, const int32_t* order, int it
                       const bf16_t* k, const float* beta, const float* alpha, const bf16_t* dO, const f16_t* tinv,
                       float* cgrad, f16_t* dsend, hipStream_t st) {
   if (n_seq <= 0) return;
-  gdn::gdn_bscan_kernel<<<dim3((unsigned)(n_seq * s.H)), 256, 0, st>>>(
+  gdn::gdn_bscan_kernel<<<dim3((unsigned)(n_seq * s.H)), 512, 0, st>>>(
       s.seqs, order, s.rows, s.exports, s.slot_off, s.slot_cons, q, k, beta, alpha, dO, tinv, cgrad, dsend, item0,
       s.H, s.scale);
 }
