@@ -152,10 +152,18 @@ def flat_time(dpa, spec, plan, p, dev, steps, max_rows=3_000_000):
     return total, pairs, sum(lengths), len(lengths)
 
 
-# Executed MFMA FLOPs of the gated-delta-rule kernels per (chunk, head): products of
-# 64x64x128 (mmd) and 64x128x128 (mdd) shapes, two FLOPs per multiply-add.
+# Gated-delta-rule FLOPs per (chunk, head), in products of 64x64x128 (mmd) and
+# 64x128x128 (mdd) shapes, two FLOPs per multiply-add.
+# Algorithmic: the blockwise recurrence's products, the forward's KK^T, QK^T, K S0^T,
+# (I + A)^{-1} R, Q S0^T, P U and U^T K (triangular ones counted dense), the backward
+# twice the forward.  Executed by the kernels of each timed span: the chunk inverse (the
+# lower three quarters of KK^T and QK^T) in gdn_fwd and gdn_states, T R as three fp16
+# products and T^T dU as two (high and low parts of T), the backward's recomputed R, U
+# and block products.
 _MMD, _MDD = 2 * 64 * 64 * 128, 2 * 64 * 128 * 128
-GDN_FLOPS = {"gdn_fwd": 3 * _MMD + 3 * _MDD, "gdn_states": _MMD + 2 * _MDD, "gdn_bwd": 11 * _MMD + 8 * _MDD}
+GDN_ALG = {"fwd": 4 * _MMD + 3 * _MDD, "bwd": 8 * _MMD + 6 * _MDD}
+GDN_FLOPS = {"gdn_fwd": 5.5 * _MMD + 3 * _MDD, "gdn_states": 4.5 * _MMD + 2 * _MDD,
+             "gdn_bwd": 15.25 * _MMD + 8 * _MDD}
 GDN_H = 16
 
 
@@ -214,7 +222,15 @@ def gdn_time(dpa, spec, dev, steps, warmup):
            "mfma_tflops": {n: round(GDN_FLOPS[n] * ch / (ms[n] * 1e-3) / 1e12, 2) for n in GDN_FLOPS},
            "keep_states": {"fwd_ms": round(msk["gdn_fwd"], 3), "bwd_ms": round(msk["gdn_bwd"], 3),
                            "fwd_bwd_ms_wall": round(wall_k * 1e3, 3),
-                           "state_bytes": int(info["gdn_chunks"]) * GDN_H * 2 * 128 * 128 * 2}}
+                           "state_bytes": int(info["gdn_chunks"]) * GDN_H * (2 * 128 * 128 + 3 * 64 * 64) * 2}}
+    # algorithmic rate of the layer (forward + backward, states recomputed) against the
+    # dense fp16/bf16 MFMA peak
+    alg = (GDN_ALG["fwd"] + GDN_ALG["bwd"]) * ch
+    t_layer = (ms["gdn_fwd"] + ms["gdn_states"] + ms["gdn_bwd"]) * 1e-3
+    out["roofline"] = {"bound": "mfma", "algorithmic_flop": alg,
+                       "algorithmic_flop_per_chunk_head": GDN_ALG,
+                       "achieved": round(alg / t_layer / 1e12, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(alg / t_layer / 1e12 / PEAK_BF16_TFLOPS, 4)}
     del q, k, v, b, a, do, o, grads, ws
     torch.cuda.empty_cache()
     return out

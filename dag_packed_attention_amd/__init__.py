@@ -22,7 +22,9 @@ from typing import Optional, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libdag_attn.so")
+# DAG_ATTN_DEBUG=1 selects the device debug build (plan-table checks in the kernels)
+DEBUG = os.environ.get("DAG_ATTN_DEBUG", "0") == "1"
+LIB_PATH = os.path.join(_HERE, "libdag_attn_debug.so" if DEBUG else "libdag_attn.so")
 
 DAG_OK = 0
 STATUS = {0: "OK", 1: "INVALID", 2: "NOT_TOPO", 3: "MOUNT_CYCLE", 4: "MOUNT_RANGE",
@@ -109,7 +111,7 @@ def _load() -> ctypes.CDLL:
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         from . import build_lib
-        build_lib.build()
+        build_lib.build(debug=DEBUG)
     lib = ctypes.CDLL(LIB_PATH)
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     sig = {
@@ -145,6 +147,8 @@ def _load() -> ctypes.CDLL:
         "dag_attn_timing_enable": ([P, I32, I32], I32),
         "dag_attn_timing_read": ([P, P, P], I32),
         "dag_last_error": ([], ctypes.c_char_p),
+        "dag_debug_build": ([], I32),
+        "dag_debug_limit_pages": ([I32], I32),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

@@ -18,13 +18,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libdag_attn.so")
+LIB_DEBUG = os.path.join(HERE, "libdag_attn_debug.so")  # DAG_DEBUG: device checks of the plan tables
 ARCH = os.environ.get("DAG_ATTN_ARCH", "gfx950")
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
+_HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              f"-I{os.path.join(ROOT, 'include')}"]
-CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{os.path.join(ROOT, 'include')}"]
+_CXX_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{os.path.join(ROOT, 'include')}"]
 
 
 def _run(cmd):
@@ -38,9 +39,14 @@ OBJS = ("plan.o", "pack_plan.o", "gdn_plan.o", "logprob_map.o", "conv_plan.o", "
         "conv.o", "noalloc.o")
 
 
-def build(verbose: bool = False) -> str:
-    obj_dir = os.path.join(HERE, "_build")
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile every source and link libdag_attn.so (debug: libdag_attn_debug.so, every
+    file compiled with DAG_DEBUG, objects in their own folder)."""
+    obj_dir = os.path.join(HERE, "_build_debug" if debug else "_build")
     os.makedirs(obj_dir, exist_ok=True)
+    HIP_FLAGS = _HIP_FLAGS + (["-DDAG_DEBUG"] if debug else [])
+    CXX_FLAGS = _CXX_FLAGS + (["-DDAG_DEBUG"] if debug else [])
+    lib = LIB_DEBUG if debug else LIB
     steps = [
         ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "plan.cpp"), "-o", os.path.join(obj_dir, "plan.o")],
         ["g++", *CXX_FLAGS, "-c", os.path.join(CSRC, "pack_plan.cpp"), "-o", os.path.join(obj_dir, "pack_plan.o")],
@@ -60,12 +66,12 @@ def build(verbose: bool = False) -> str:
         for r in ex.map(_run, steps):
             if verbose and r.stderr:
                 sys.stderr.write(r.stderr)
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-o", tmp,
           *(os.path.join(obj_dir, f) for f in OBJS)])
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, debug="--debug" in sys.argv[1:]))

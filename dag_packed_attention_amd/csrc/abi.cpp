@@ -327,6 +327,33 @@ dag_status launched(const char* what) {
   return DAG_OK;
 }
 
+// Device debug builds: the plan's table sizes for the kernels' checks before an attention
+// call, and the first recorded failure after it (which waits for the stream).
+int32_t g_dbg_page_limit = 0;  // test override: page ids from this one on fail the checks
+dag_status dbg_begin(const Plan& P, hipStream_t st) {
+  if (!dbg_enabled()) return DAG_OK;
+  DbgLimits lim;
+  lim.pages = (int32_t)P.info.pages;
+  if (g_dbg_page_limit > 0 && g_dbg_page_limit < lim.pages) lim.pages = g_dbg_page_limit;
+  lim.masks = (int32_t)(P.masks.size() / 128);
+  lim.tiles = (int64_t)P.tiles.size();
+  lim.steps = (int64_t)P.kpsteps.size();
+  lim.qpages = (int64_t)P.qpages.size();
+  lim.pairs = (int64_t)P.kpairs.size() / 2;
+  if (!dbg_set_limits(lim, st)) return set_err(DAG_E_DEVICE, "upload of the debug check limits failed");
+  return DAG_OK;
+}
+dag_status dbg_end(dag_status st, const char* what, hipStream_t stream) {
+  if (st != DAG_OK || !dbg_enabled()) return st;
+  uint32_t e[3];
+  if (!dbg_take(e, stream)) return set_err(DAG_E_DEVICE, std::string(what) + ": reading the debug check record failed");
+  if (e[0])
+    return set_err(DAG_E_INVALID, std::string(what) + ": device check of the plan tables failed (code " +
+                                      std::to_string(e[0]) + ", value " + std::to_string((int32_t)e[1]) + ", " +
+                                      std::to_string(e[2]) + " failures)");
+  return DAG_OK;
+}
+
 
 // ---- gated delta rule -------------------------------------------------------------
 dag_status check_gdn(const Plan& P, const dag_gdn_params* p) {
@@ -421,6 +448,7 @@ dag_status dagattn::attn_fwd_impl(dag_plan* plan, const dag_attn_params* p, cons
   carve_fwd(s, mfma, ws, &w);
   const DeviceTables& D = *P.dev;
   const int64_t n_qp = (int64_t)P.qpages.size();
+  if ((st = dbg_begin(P, stream)) != DAG_OK) return st;
   {
     Span sp(P, DAG_K_PROLOGUE_FWD, stream);
     if (w.cs) launch_cs(s, D.pos_of_row, w.cs, stream);
@@ -455,7 +483,7 @@ dag_status dagattn::attn_fwd_impl(dag_plan* plan, const dag_attn_params* p, cons
       launch_fwd_simple<float>(s, n_qp, (const float*)w.qn, (const float*)w.kn, (const float*)v, D.qpages,
                                D.fwd_order, D.tiles, (float*)o, lse, nullptr, stream);
   }
-  return launched("dag_attn_fwd");
+  return dbg_end(launched("dag_attn_fwd"), "dag_attn_fwd", stream);
 }
 
 extern "C" {
@@ -593,6 +621,15 @@ dag_status dag_plan_multiplicity(const dag_plan* plan, int32_t* mult) {
   return DAG_OK;
 }
 
+int32_t dag_debug_build(void) { return dbg_enabled() ? 1 : 0; }
+
+dag_status dag_debug_limit_pages(int32_t max_pages) {
+  if (!dbg_enabled()) return set_err(DAG_E_UNSUPPORTED, "dag_debug_limit_pages needs a device debug build");
+  if (max_pages < 0) return set_err(DAG_E_INVALID, "max_pages must be >= 0");
+  g_dbg_page_limit = max_pages;
+  return DAG_OK;
+}
+
 dag_status dag_plan_starts(const dag_plan* plan, int32_t* start) {
   if (!plan || !start) return set_err(DAG_E_INVALID, "null argument");
   std::memcpy(start, plan->p.start.data(), plan->p.start.size() * 4);
@@ -705,6 +742,7 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
   hipStream_t stream = (hipStream_t)hip_stream;
   if ((st = ensure_uploaded(P, stream)) != DAG_OK) return st;
   carve_bwd(s, mfma, ws, &w);
+  if ((st = dbg_begin(P, stream)) != DAG_OK) return st;
   const DeviceTables& D = *P.dev;
   const int64_t n_qp = (int64_t)P.qpages.size(), n_kvp = (int64_t)P.bwd_order.size();
   if (mfma) {
@@ -781,7 +819,7 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
                              (const float*)dO, w.ld, w.cs, D.qpages, D.fwd_order, D.tiles, D.bwd_order, D.kv_off,
                              D.kentries, D.page_table, D.page_nrows, (float*)dq, (float*)dk, (float*)dv, stream);
   }
-  return launched("dag_attn_bwd");
+  return dbg_end(launched("dag_attn_bwd"), "dag_attn_bwd", stream);
 }
 
 dag_status dag_gdn_workspace(const dag_plan* plan, const dag_gdn_params* p, size_t* fwd_bytes, size_t* bwd_bytes) {

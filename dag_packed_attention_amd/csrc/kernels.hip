@@ -79,6 +79,88 @@ __device__ __forceinline__ float pow2_scale(uint32_t maxbits, int top) {
   return ldexpf(1.f, top - max(ilogbf(m), -24));
 }
 
+// ---------------------------------------------------------------------------
+// Plan-table checks (device debug builds).  Built with DAG_DEBUG, the attention
+// kernels check every query page, tile range, page id, mask id, visible interval and
+// reader step they read from the plan tables against the plan's sizes (set by the
+// host before each call).  A failed check records (code, value) once and counts
+// every failure in g_dbg_err, and the kernel goes on with a safe value (page 0, an
+// empty interval, no mask, the table's first entry), so no access leaves its buffer.
+// Without DAG_DEBUG every check compiles to nothing.
+// ---------------------------------------------------------------------------
+#ifdef DAG_DEBUG
+__device__ DbgLimits g_dbg_lim;
+__device__ uint32_t g_dbg_err[4];  // first code, its value, number of failures
+__device__ __noinline__ void dbg_fail(uint32_t code, int64_t value) {
+  atomicAdd(&g_dbg_err[2], 1u);
+  if (atomicCAS(&g_dbg_err[0], 0u, code) == 0u) atomicExch(&g_dbg_err[1], (uint32_t)value);
+}
+#endif
+__device__ __forceinline__ int dbg_index(int i, int64_t n, uint32_t code) {  // 0 <= i < n
+#ifdef DAG_DEBUG
+  if (i < 0 || i >= n) {
+    dbg_fail(code, i);
+    return 0;
+  }
+#endif
+  return i;
+}
+__device__ __forceinline__ int dbg_page(int page, uint32_t code) {
+#ifdef DAG_DEBUG
+  return dbg_index(page, g_dbg_lim.pages, code);
+#else
+  return page;
+#endif
+}
+__device__ __forceinline__ int dbg_lohi(int lohi) {  // lo | hi << 8, lo <= hi <= 64
+#ifdef DAG_DEBUG
+  const int lo = lohi & 0xff, hi = (lohi >> 8) & 0xff;
+  if (lohi < 0 || lo > hi || hi > 64) {
+    dbg_fail(kDbgInterval, lohi);
+    return 0;
+  }
+#endif
+  return lohi;
+}
+__device__ __forceinline__ int dbg_mask(int mi) {  // -1 (no mask) or a mask id
+#ifdef DAG_DEBUG
+  if (mi < -1 || mi >= g_dbg_lim.masks) {
+    dbg_fail(kDbgMask, mi);
+    return -1;
+  }
+#endif
+  return mi;
+}
+// a query page: its page and a tile list inside the table (at least one tile)
+__device__ __forceinline__ QPage dbg_qpage(QPage qp) {
+#ifdef DAG_DEBUG
+  if (qp.tile_begin < 0 || qp.tile_count < 1 || (int64_t)qp.tile_begin + qp.tile_count > g_dbg_lim.tiles) {
+    dbg_fail(kDbgTileRange, qp.tile_begin);
+    qp.tile_begin = 0;
+    qp.tile_count = 1;
+  }
+  qp.phys = dbg_page(qp.phys, kDbgQPage);
+#endif
+  return qp;
+}
+// a merged reader step: its query page and the two sides' intervals
+__device__ __forceinline__ KStep dbg_step(KStep d) {
+#ifdef DAG_DEBUG
+  d.qph = dbg_page(d.qph, kDbgStepPage);
+  bool ok = true;
+  for (int side = 0; side < 2; ++side) {
+    const uint32_t inf = ((uint32_t)d.info >> (16 * side)) & 0xffffu;
+    const int lo = (inf >> 1) & 0x7f, hi = (inf >> 8) & 0x7f;
+    ok = ok && lo <= hi && hi <= 64;
+  }
+  if (!ok) {
+    dbg_fail(kDbgInterval, d.info);
+    d.info &= 1;  // both sides empty
+  }
+#endif
+  return d;
+}
+
 // position of row r inside its transposed 16-group (bits 2 and 3 swapped)
 __device__ __forceinline__ int tperm(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -504,7 +586,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
   // sq sk q.k and the output as sv O, so the exponent factor and 1 / l absorb them exactly
   const float sl2 = sl2_raw / pow2_scale(amax[0], kTopQK) / pow2_scale(amax[1], kTopQK);
   const float inv_sv = 1.f / pow2_scale(amax[2], kTopVO);
-  const QPage qp = qpages[order[unit]];
+  const QPage qp = dbg_qpage(qpages[dbg_index(order[unit], n_qp, kDbgQPage)]);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
   const int l32 = lane & 31, hi = lane >> 5;
@@ -526,7 +608,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
 
   const int T = qp.tile_count;
   if (wave < 4) {
-    const int64_t base = ((int64_t)tiles[qp.tile_begin].page * Hkv + g) * kTile;
+    const int64_t base = ((int64_t)dbg_page(tiles[qp.tile_begin].page, kDbgTilePage) * Hkv + g) * kTile;
     stage_bricks<4>(lk[0], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
     stage_cbricks<4>(lv[0], tile_rsrc(vt + base, kTile * 2), 4 * wave, clo);
   }
@@ -536,16 +618,16 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
   for (int t = 0; t < T; ++t) {
     const int buf = t & 1;
     if (t + 1 < T && wave < 4) {
-      const int64_t base = ((int64_t)tiles[qp.tile_begin + t + 1].page * Hkv + g) * kTile;
+      const int64_t base = ((int64_t)dbg_page(tiles[qp.tile_begin + t + 1].page, kDbgTilePage) * Hkv + g) * kTile;
       stage_bricks<4>(lk[buf ^ 1], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
       stage_cbricks<4>(lv[buf ^ 1], tile_rsrc(vt + base, kTile * 2), 4 * wave, clo);
     }
-    const int lohi = tiles[qp.tile_begin + t].lohi;
+    const int lohi = dbg_lohi(tiles[qp.tile_begin + t].lohi);
     const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
     int mi = -1;
     uint64_t rmask = 0;
     if constexpr (kMasked) {
-      mi = tile_mask[qp.tile_begin + t];
+      mi = dbg_mask(tile_mask[qp.tile_begin + t]);
       if (mi >= 0) rmask = masks[(int64_t)mi * 128 + row];
     }
     const bool diag = (t == T - 1) && mi < 0;
@@ -692,7 +774,7 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
   // as sdo sv sk dQ / scale
   const float sq = pow2_scale(amax[0], kTopQK), sk = pow2_scale(amax[1], kTopQK), sv = pow2_scale(amax[2], kTopVO);
   const float sl2 = sl2_raw / sq / sk;
-  const QPage qp = qpages[order[unit]];
+  const QPage qp = dbg_qpage(qpages[dbg_index(order[unit], n_qp, kDbgQPage)]);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
   const int l32 = lane & 31, hi = lane >> 5;
@@ -718,7 +800,7 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
 
   const int T = qp.tile_count;
   if (wave < 4) {
-    const int64_t base = ((int64_t)tiles[qp.tile_begin].page * Hkv + g) * kTile;
+    const int64_t base = ((int64_t)dbg_page(tiles[qp.tile_begin].page, kDbgTilePage) * Hkv + g) * kTile;
     stage_bricks<4>(lk[0], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
     stage_bricks<4>(lvv[0], tile_rsrc(vn + base, kTile * 2), 4 * wave, rlo);
     stage_cbricks<4>(lkt[0], tile_rsrc(kt + base, kTile * 2), 4 * wave, clo);
@@ -729,17 +811,17 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
   for (int t = 0; t < T; ++t) {
     const int buf = t & 1;
     if (t + 1 < T && wave < 4) {
-      const int64_t base = ((int64_t)tiles[qp.tile_begin + t + 1].page * Hkv + g) * kTile;
+      const int64_t base = ((int64_t)dbg_page(tiles[qp.tile_begin + t + 1].page, kDbgTilePage) * Hkv + g) * kTile;
       stage_bricks<4>(lk[buf ^ 1], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
       stage_bricks<4>(lvv[buf ^ 1], tile_rsrc(vn + base, kTile * 2), 4 * wave, rlo);
       stage_cbricks<4>(lkt[buf ^ 1], tile_rsrc(kt + base, kTile * 2), 4 * wave, clo);
     }
-    const int lohi = tiles[qp.tile_begin + t].lohi;
+    const int lohi = dbg_lohi(tiles[qp.tile_begin + t].lohi);
     const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
     int mi = -1;
     uint64_t rmask = 0;
     if constexpr (kMasked) {
-      mi = tile_mask[qp.tile_begin + t];
+      mi = dbg_mask(tile_mask[qp.tile_begin + t]);
       if (mi >= 0) rmask = masks[(int64_t)mi * 128 + row];
     }
     const bool diag = (t == T - 1) && mi < 0;
@@ -914,8 +996,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
   // units: P is exact, dS comes out as sdo sv dS, the sums as sdo dV and sdo sv sq dK / scale
   const float sq = pow2_scale(amax[0], kTopQK), sk = pow2_scale(amax[1], kTopQK), sv = pow2_scale(amax[2], kTopVO);
   const float sl2 = sl2_raw / sq / sk;
-  const int pr = pair_order[unit];
-  const int physA = pairs[2 * pr], physB = pairs[2 * pr + 1];
+  const int pr = dbg_index(pair_order[unit], n_pairs, kDbgPair);
+  const int physA = dbg_page(pairs[2 * pr], kDbgPair);
+  int physB = pairs[2 * pr + 1];
+  if (physB != -1) physB = dbg_page(physB, kDbgPair);
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
   const int l32 = lane & 31, hi = lane >> 5;
@@ -943,18 +1027,28 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
 
   // Step descriptors are uniform and come through the scalar cache ahead of their
   // use (no vector-memory wait for them, which would also wait for the staging loads).
-  const int64_t s_begin = pair_off[pr];
-  const int n_steps = (int)(pair_off[pr + 1] - s_begin);
+  int64_t s_begin = pair_off[pr];
+  int n_steps = (int)(pair_off[pr + 1] - s_begin);
+#ifdef DAG_DEBUG
+  if (s_begin < 0 || n_steps < 1 || s_begin + n_steps > g_dbg_lim.steps) {
+    dbg_fail(kDbgStepRange, s_begin);
+    s_begin = 0;
+    n_steps = 1;
+  }
+#endif
   const int n_units = 2 * n_steps;
   const KStep* kst = psteps + s_begin;
-  KStep cur = kst[0];
-  KStep nxt = kst[min(1, n_steps - 1)];
-  KStep n2 = kst[min(2, n_steps - 1)];
+  KStep cur = dbg_step(kst[0]);
+  KStep nxt = dbg_step(kst[min(1, n_steps - 1)]);
+  KStep n2 = dbg_step(kst[min(2, n_steps - 1)]);
   KMask cur_m{-1, -1}, nxt_m{-1, -1}, n2_m{-1, -1};
   if constexpr (kMasked) {
     cur_m = pmasks[s_begin];
     nxt_m = pmasks[s_begin + min(1, n_steps - 1)];
     n2_m = pmasks[s_begin + min(2, n_steps - 1)];
+    cur_m.a = dbg_mask(cur_m.a), cur_m.b = dbg_mask(cur_m.b);
+    nxt_m.a = dbg_mask(nxt_m.a), nxt_m.b = dbg_mask(nxt_m.b);
+    n2_m.a = dbg_mask(n2_m.a), n2_m.b = dbg_mask(n2_m.b);
   }
   // staging role: head sj of the half-step, tensor ts (0: Q, 1: dO), bricks sb0 .. sb0 + 3
   const int sj = wave & 1, ts = (wave >> 1) & 1, sb0 = 4 * (wave >> 2);
@@ -1143,9 +1237,12 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     }
     // the descriptor three steps ahead: issued here, where the closing wait covers it
     __builtin_amdgcn_sched_barrier(0);
-    const KStep n3 = kst[min((u >> 1) + 3, n_steps - 1)];
+    const KStep n3 = dbg_step(kst[min((u >> 1) + 3, n_steps - 1)]);
     KMask n3_m{-1, -1};
-    if constexpr (kMasked) n3_m = pmasks[s_begin + min((u >> 1) + 3, n_steps - 1)];
+    if constexpr (kMasked) {
+      n3_m = pmasks[s_begin + min((u >> 1) + 3, n_steps - 1)];
+      n3_m.a = dbg_mask(n3_m.a), n3_m.b = dbg_mask(n3_m.b);
+    }
     wait_all_loads();
     __syncthreads();
     if (hp) {
@@ -1377,6 +1474,30 @@ void launch_absmax(const LaunchShape& s, const bf16_t* q, const bf16_t* k, const
 }
 
 void launch_zero_u32(uint32_t* out, int n, hipStream_t st) { zero_u32_kernel<<<1, 64, 0, st>>>(out, n); }
+
+#ifdef DAG_DEBUG
+bool dbg_enabled() { return true; }
+bool dbg_set_limits(const DbgLimits& lim, hipStream_t st) {
+  return hipMemcpyToSymbolAsync(HIP_SYMBOL(g_dbg_lim), &lim, sizeof(lim), 0, hipMemcpyHostToDevice, st) == hipSuccess;
+}
+bool dbg_take(uint32_t out[3], hipStream_t st) {
+  uint32_t e[4] = {0, 0, 0, 0};
+  const uint32_t zero[4] = {0, 0, 0, 0};
+  if (hipMemcpyFromSymbolAsync(e, HIP_SYMBOL(g_dbg_err), sizeof(e), 0, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipMemcpyToSymbolAsync(HIP_SYMBOL(g_dbg_err), zero, sizeof(zero), 0, hipMemcpyHostToDevice, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return false;
+  out[0] = e[0], out[1] = e[1], out[2] = e[2];
+  return true;
+}
+#else
+bool dbg_enabled() { return false; }
+bool dbg_set_limits(const DbgLimits&, hipStream_t) { return true; }
+bool dbg_take(uint32_t out[3], hipStream_t) {
+  out[0] = out[1] = out[2] = 0;
+  return true;
+}
+#endif
 
 void launch_prep16(const LaunchShape& s, const bf16_t* x, const float2* cs, const int32_t* page_nrows,
                    const uint32_t* smax, bool qk, f16_t* out_n, f16_t* out_t, int H, hipStream_t st) {

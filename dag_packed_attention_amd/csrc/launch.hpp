@@ -8,6 +8,28 @@
 namespace dagattn {
 
 typedef uint16_t bf16_t;  // bf16 bits
+
+// Plan-table checks of device debug builds (compiled with DAG_DEBUG): the sizes the
+// kernels check table entries against, the failure codes they record, and the host
+// side.  In other builds dbg_enabled() is false and the other two do nothing.
+struct DbgLimits {
+  int32_t pages, masks;
+  int64_t tiles, steps, qpages, pairs;
+};
+enum : uint32_t {
+  kDbgQPage = 1,      // query page id or its launch-order index
+  kDbgTileRange = 2,  // a query page's tile list outside the tile table
+  kDbgTilePage = 3,   // a tile's KV page
+  kDbgInterval = 4,   // a visible interval [lo, hi) not within [0, 64]
+  kDbgMask = 5,       // a mask id outside the mask table
+  kDbgPair = 6,       // a KV page pair (index or page)
+  kDbgStepRange = 7,  // a pair's reader steps outside the step table
+  kDbgStepPage = 8,   // a reader step's query page
+};
+bool dbg_enabled();
+bool dbg_set_limits(const DbgLimits& lim, hipStream_t st);
+// the first recorded failure (code, value) and the failure count, cleared; waits for st
+bool dbg_take(uint32_t out[3], hipStream_t st);
 typedef _Float16 f16_t;
 
 struct LaunchShape {

@@ -182,6 +182,21 @@ dag_status dag_plan_readers(const dag_plan* plan, int32_t row, int32_t* query_ro
  * sum to dag_plan_info.semantic_tokens. */
 dag_status dag_plan_multiplicity(const dag_plan* plan, int32_t* mult);
 
+/* Device debug build.  libdag_attn_debug.so is this library compiled with DAG_DEBUG (the
+ * Python binding loads it when DAG_ATTN_DEBUG=1): its attention kernels check every
+ * query page, tile range, page id, mask id, visible interval and reader step they read
+ * from the plan tables against the plan's sizes, record the first failure and go on
+ * with a safe in-bounds value, and dag_attn_fwd / dag_attn_bwd then wait for the stream
+ * and return DAG_E_INVALID naming the check (codes: 1 query page, 2 tile range, 3 tile
+ * page, 4 interval, 5 mask id, 6 page pair, 7 step range, 8 step page).  Results of a
+ * passing call are bitwise those of the release build.
+ * dag_debug_build: 1 in the debug build, 0 otherwise. */
+int32_t dag_debug_build(void);
+/* Debug build only (DAG_E_UNSUPPORTED otherwise): page ids >= max_pages fail the checks
+ * from the next call on (0: the plan's page count), so the checks can be exercised on
+ * valid tables without any access leaving its buffer.  Process-wide, not thread-safe. */
+dag_status dag_debug_limit_pages(int32_t max_pages);
+
 /* Start position s(u) of every node (Octopus Sec. 3.2 Eq. 2) -> start[n_nodes]. */
 dag_status dag_plan_starts(const dag_plan* plan, int32_t* start);
 
