@@ -571,7 +571,14 @@ constexpr int kTile = 64 * kD;  // elements of a page's 64 x 128 (or 128 x 64) b
 // row's 64-bit key mask and the mask alone decides which keys it sees (the causal rule of
 // a page's last tile applies to unmasked tiles only).  Rows of one wave may then have seen
 // no key yet when another row raises the running max; their rescale factor is 1.
-template <bool kMasked>
+//
+// kForm, the exponent's form: |s sl2| <= D max|q| max|k| |scale log2 e| (rotation keeps
+// norms), and only beyond 2^20 does the fused s sl2 - m lose m's rounding.  Unmasked
+// plans launch two kernels, kForm 0 (fused) and 1 (unfused), each returning at once
+// unless the bound is on its side, so neither carries the other's code in its loop;
+// the masked variant (more registers) takes kForm 2, a check of the running max per
+// half-tile.
+template <bool kMasked, int kForm>
 __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
     const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vt,
     const QPage* __restrict__ qpages, const int32_t* __restrict__ order, const Tile* __restrict__ tiles,
@@ -582,6 +589,10 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
   __shared__ __attribute__((aligned(1024))) f16_t lv[2][kPageC];
   int unit, g;
   if (!map_item(n_qp, Hkv, unit, g)) return;
+  if constexpr (kForm != 2) {  // the exponent's form (see above): one of the two kernels works
+    const float bound = (float)kD * __uint_as_float(amax[0]) * __uint_as_float(amax[1]) * fabsf(sl2_raw);
+    if ((kForm == 1) == (bound <= 0x1p20f)) return;
+  }
   // the fp16 copies hold sq q, sk k, sv v (powers of two): the scores come out as
   // sq sk q.k and the output as sv O, so the exponent factor and 1 / l absorb them exactly
   const float sl2 = sl2_raw / pow2_scale(amax[0], kTopQK) / pow2_scale(amax[1], kTopQK);
@@ -684,7 +695,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
       // a half-tile can be fully masked before a row has seen any key (a mounted
       // span starting past key 32); then m is still -inf and every score is -inf
       const float mneg = mrow == -INFINITY ? 0.f : -mrow;
-      if (!__any(fabsf(mrow) > 0x1p20f)) {
+      if (kForm == 0 || (kForm == 2 && !__any(fabsf(mrow) > 0x1p20f))) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, mneg));
       } else {
@@ -1542,14 +1553,19 @@ void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const 
                      const QPage* qpages, const int32_t* order, const Tile* tiles, const int32_t* tile_mask,
                      const uint64_t* masks, bf16_t* o, float* lse, bf16_t* o_lo, const uint32_t* amax,
                      hipStream_t st) {
-  if (tile_mask)
-    fwd_mfma_kernel<true><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, vt, qpages, order, tiles, tile_mask, masks, o,
-                                                                 lse, o_lo, amax, (int)n_qp, s.Hq, s.Hkv,
-                                                                 s.scale * kLog2e);
-  else
-    fwd_mfma_kernel<false><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, vt, qpages, order, tiles, nullptr, nullptr,
-                                                                  o, lse, o_lo, amax, (int)n_qp, s.Hq, s.Hkv,
-                                                                  s.scale * kLog2e);
+  if (tile_mask) {
+    fwd_mfma_kernel<true, 2><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(
+        qn, kn, vt, qpages, order, tiles, tile_mask, masks, o, lse, o_lo, amax, (int)n_qp, s.Hq, s.Hkv,
+        s.scale * kLog2e);
+  } else {
+    // both forms; the one the operand maxima do not select returns at once
+    fwd_mfma_kernel<false, 0><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(
+        qn, kn, vt, qpages, order, tiles, nullptr, nullptr, o, lse, o_lo, amax, (int)n_qp, s.Hq, s.Hkv,
+        s.scale * kLog2e);
+    fwd_mfma_kernel<false, 1><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(
+        qn, kn, vt, qpages, order, tiles, nullptr, nullptr, o, lse, o_lo, amax, (int)n_qp, s.Hq, s.Hkv,
+        s.scale * kLog2e);
+  }
 }
 
 template <typename TG>
