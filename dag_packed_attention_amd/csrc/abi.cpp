@@ -109,7 +109,10 @@ dag_status check_params(const dag_attn_params* p) {
     return set_err(DAG_E_UNSUPPORTED, "fp32 inputs need fp32 gradients");
   if (!(p->rope_base >= 0.f) || std::isinf(p->rope_base) || (p->rope_base > 0.f && p->rope_base <= 1.f))
     return set_err(DAG_E_INVALID, "rope_base must be 0 (off) or > 1");
-  if (!std::isfinite(p->scale)) return set_err(DAG_E_INVALID, "scale must be finite");
+  // the kernels hide a score by sending it to -inf before the scale multiplies it, so
+  // the scale must be positive (a negative one is the positive one with k negated)
+  if (!std::isfinite(p->scale) || p->scale < 0.f)
+    return set_err(DAG_E_INVALID, "scale must be finite and >= 0 (0 selects 1/sqrt(head_dim))");
   return DAG_OK;
 }
 

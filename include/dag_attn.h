@@ -232,7 +232,7 @@ typedef struct {
   int32_t grad_dtype;  /* element type of dq, dk, dv: DAG_DTYPE_BF16 or DAG_DTYPE_FP32;    */
                        /* must be FP32 when dtype is FP32.  Large shared-row gradients     */
                        /* keep their precision in FP32                                      */
-  float scale;         /* softmax scale; 0 selects 1/sqrt(head_dim)                      */
+  float scale;         /* softmax scale, finite and >= 0; 0 selects 1/sqrt(head_dim)     */
   float rope_base;     /* rotary base (Octopus Eq. 1, pairs (i, i + D/2),                */
                        /* theta_i = base^(-2i/D), angles in fp64); 0 disables rotation    */
 } dag_attn_params;

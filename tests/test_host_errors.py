@@ -71,3 +71,14 @@ def test_bf16_backward_refuses_a_missing_residual():
     st = L.dag_attn_bwd(plan._h, ctypes.byref(cp32), fake, fake, fake, fake, fake, fake, fake, fake, fake, fake, ws,
                         1 << 40, None)
     assert st == 1 and "o_lo" in L.dag_last_error().decode()
+
+
+@pytest.mark.parametrize("scale", [-0.5, float("inf"), float("nan")])
+def test_attention_refuses_a_negative_or_non_finite_scale(scale):
+    # decided on the host before any device call: the pointers are never dereferenced
+    import synth
+    plan = dpa.Plan(synth.config1())
+    cp = dpa.AttnParams(16, 4, 128, "bf16", scale=scale).c()
+    fake = ctypes.c_void_p(0x1000)
+    st = L.dag_attn_fwd(plan._h, ctypes.byref(cp), fake, fake, fake, fake, fake, fake, fake, 1 << 40, None)
+    assert st == 1 and "scale" in L.dag_last_error().decode()
