@@ -565,7 +565,9 @@ constexpr int kTile = 64 * kD;  // elements of a page's 64 x 128 (or 128 x 64) b
 // serves query head 4 g + hh and rows 32 nb .. 32 nb + 31 (two waves per SIMD,
 // so one wave's softmax overlaps the other's products).  K/V tiles are
 // double-buffered in LDS and fetched straight from global memory while the
-// previous tile is multiplied; each 64-key tile is taken as two 32-key halves.
+// previous tile is multiplied, all by waves 0 and 1 (measured faster than four or
+// eight issuing waves: the others' products run without load issue in between);
+// each 64-key tile is taken as two 32-key halves.
 //
 // kMasked (packed page layouts): a tile may carry a mask id; the lane then reads its query
 // row's 64-bit key mask and the mask alone decides which keys it sees (the causal rule of
@@ -618,20 +620,20 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
   float mrow = -INFINITY, lrow = 0.f;
 
   const int T = qp.tile_count;
-  if (wave < 4) {
+  if (wave < 2) {
     const int64_t base = ((int64_t)dbg_page(tiles[qp.tile_begin].page, kDbgTilePage) * Hkv + g) * kTile;
-    stage_bricks<4>(lk[0], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
-    stage_cbricks<4>(lv[0], tile_rsrc(vt + base, kTile * 2), 4 * wave, clo);
+    stage_bricks<8>(lk[0], tile_rsrc(kn + base, kTile * 2), 8 * wave, rlo);
+    stage_cbricks<8>(lv[0], tile_rsrc(vt + base, kTile * 2), 8 * wave, clo);
   }
   wait_all_loads();
   __syncthreads();
 
   for (int t = 0; t < T; ++t) {
     const int buf = t & 1;
-    if (t + 1 < T && wave < 4) {
+    if (t + 1 < T && wave < 2) {
       const int64_t base = ((int64_t)dbg_page(tiles[qp.tile_begin + t + 1].page, kDbgTilePage) * Hkv + g) * kTile;
-      stage_bricks<4>(lk[buf ^ 1], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
-      stage_cbricks<4>(lv[buf ^ 1], tile_rsrc(vt + base, kTile * 2), 4 * wave, clo);
+      stage_bricks<8>(lk[buf ^ 1], tile_rsrc(kn + base, kTile * 2), 8 * wave, rlo);
+      stage_cbricks<8>(lv[buf ^ 1], tile_rsrc(vt + base, kTile * 2), 8 * wave, clo);
     }
     const int lohi = dbg_lohi(tiles[qp.tile_begin + t].lohi);
     const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
