@@ -140,7 +140,6 @@ struct BwdWs {
   float2* cs;
   void* qn;
   void* kn;
-  void* kt;
   void* vn;
   void* dOn;
   float2* ld;
@@ -175,12 +174,11 @@ size_t carve_bwd(const LaunchShape& s, bool mfma, void* base, BwdWs* w) {
     w->qn = c.take<f16_t>(C * s.Hq * s.D);
     w->dOn = c.take<f16_t>(C * s.Hq * s.D);
     w->kn = c.take<f16_t>(C * s.Hkv * s.D);
-    w->kt = c.take<f16_t>(C * s.Hkv * s.D);
     w->vn = c.take<f16_t>(C * s.Hkv * s.D);
   } else {
     w->qn = c.take<float>(C * s.Hq * s.D);
     w->kn = c.take<float>(C * s.Hkv * s.D);
-    w->kt = w->vn = w->dOn = nullptr;
+    w->vn = w->dOn = nullptr;
   }
   return c.off;
 }
@@ -761,7 +759,7 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       launch_absmax(s, q16, k16, v16, d16, nr, w.amax, stream);
       launch_rowdot16(s, o16, (const bf16_t*)o_lo, d16, lse, nr, w.ld, w.amax, stream);
       launch_prep16(s, q16, w.cs, nr, w.amax + 0, true, (f16_t*)w.qn, nullptr, s.Hq, stream);
-      launch_prep16(s, k16, w.cs, nr, w.amax + 1, true, (f16_t*)w.kn, (f16_t*)w.kt, s.Hkv, stream);
+      launch_prep16(s, k16, w.cs, nr, w.amax + 1, true, (f16_t*)w.kn, nullptr, s.Hkv, stream);
       launch_prep16(s, v16, nullptr, nr, w.amax + 2, false, (f16_t*)w.vn, nullptr, s.Hkv, stream);
       launch_prep16(s, d16, nullptr, nr, w.amax + 3, false, (f16_t*)w.dOn, nullptr, s.Hq, stream);
     }
@@ -776,7 +774,7 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       }
       {
         Span sp(P, DAG_K_DQ, stream);
-        launch_dq_mfma<TG>(s, n_qp, (const f16_t*)w.qn, (const f16_t*)w.kn, (const f16_t*)w.kt,
+        launch_dq_mfma<TG>(s, n_qp, (const f16_t*)w.qn, (const f16_t*)w.kn,
                            (const f16_t*)w.vn, (const f16_t*)w.dOn, w.ld, w.cs, w.amax + 3, D.qpages,
                            D.fwd_order, D.tiles, D.tile_mask, D.masks, (TG*)dq, w.amax, stream);
       }

@@ -765,138 +765,6 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
   if (hi == 0) lse[grow * Hq + h] = valid ? (mrow + __log2f(l)) * kLn2 : 0.f;
 }
 
-// dQ for one query block (64 rows) x one KV head.  Eight waves, wave (hh, nb) =
-// query head 4 g + hh and rows 32 nb ..; the K, V and K^T tiles are
-// double-buffered in LDS like the forward's.
-// kMasked: the forward's tile masks, read the same way.
-template <typename TG, bool kMasked>
-__global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
-    const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ kt,
-    const f16_t* __restrict__ vn, const f16_t* __restrict__ dOn, const float2* __restrict__ ldd,
-    const float2* __restrict__ cs, const uint32_t* __restrict__ dmax, const QPage* __restrict__ qpages,
-    const int32_t* __restrict__ order, const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_mask,
-    const uint64_t* __restrict__ masks, TG* __restrict__ dq,
-    const uint32_t* __restrict__ amax, int n_qp, int Hq, int Hkv, float sl2_raw, float scale) {
-  __shared__ __attribute__((aligned(1024))) f16_t lk[2][kPageB];
-  __shared__ __attribute__((aligned(1024))) f16_t lvv[2][kPageB];
-  __shared__ __attribute__((aligned(1024))) f16_t lkt[2][kPageC];
-  int unit, g;
-  if (!map_item(n_qp, Hkv, unit, g)) return;
-  // fp16 copies: sq q, sk k, sv v, sdo dO (powers of two); the S and dP offsets in ldd are
-  // in the same scaled units, so dS comes out as sdo sv dS and the sum over keys of dS k
-  // as sdo sv sk dQ / scale
-  const float sq = pow2_scale(amax[0], kTopQK), sk = pow2_scale(amax[1], kTopQK), sv = pow2_scale(amax[2], kTopVO);
-  const float sl2 = sl2_raw / sq / sk;
-  const QPage qp = dbg_qpage(qpages[dbg_index(order[unit], n_qp, kDbgQPage)]);
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
-  const int l32 = lane & 31, hi = lane >> 5;
-  const int hh = wave & 3, nb = wave >> 2;
-  const int h = g * 4 + hh;
-  const int row = nb * 32 + l32;
-  const int kb0 = frag_base(l32, hi), tb0 = cfrag_base(l32, hi);
-  const uint32_t rlo = brick_lane_off(lane), clo = cbrick_lane_off(lane);
-
-  f16x8 qf[8], df[8];
-  const f16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
-  const f16_t* db = dOn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    qf[ks] = ld8(qb + row * kD + ks * 16 + hi * 8);
-    df[ks] = ld8(db + row * kD + ks * 16 + hi * 8);
-  }
-  const float2 lt = ldd[((int64_t)qp.phys * Hq + h) * 64 + row];
-  const float nl = lt.x * sl2, nD = lt.y;  // exponent offset (log2 domain) and -D
-  f32x16 acc[4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a) acc[a] = zero16();
-
-  const int T = qp.tile_count;
-  if (wave < 4) {
-    const int64_t base = ((int64_t)dbg_page(tiles[qp.tile_begin].page, kDbgTilePage) * Hkv + g) * kTile;
-    stage_bricks<4>(lk[0], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
-    stage_bricks<4>(lvv[0], tile_rsrc(vn + base, kTile * 2), 4 * wave, rlo);
-    stage_cbricks<4>(lkt[0], tile_rsrc(kt + base, kTile * 2), 4 * wave, clo);
-  }
-  wait_all_loads();
-  __syncthreads();
-
-  for (int t = 0; t < T; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < T && wave < 4) {
-      const int64_t base = ((int64_t)dbg_page(tiles[qp.tile_begin + t + 1].page, kDbgTilePage) * Hkv + g) * kTile;
-      stage_bricks<4>(lk[buf ^ 1], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
-      stage_bricks<4>(lvv[buf ^ 1], tile_rsrc(vn + base, kTile * 2), 4 * wave, rlo);
-      stage_cbricks<4>(lkt[buf ^ 1], tile_rsrc(kt + base, kTile * 2), 4 * wave, clo);
-    }
-    const int lohi = dbg_lohi(tiles[qp.tile_begin + t].lohi);
-    const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
-    int mi = -1;
-    uint64_t rmask = 0;
-    if constexpr (kMasked) {
-      mi = dbg_mask(tile_mask[qp.tile_begin + t]);
-      if (mi >= 0) rmask = masks[(int64_t)mi * 128 + row];
-    }
-    const bool diag = (t == T - 1) && mi < 0;
-    const bool full = lo == 0 && hi_t == 64 && !diag && qp.nrows == 64 && mi < 0;
-    const f16_t* K = lk[buf];
-    const f16_t* V = lvv[buf];
-    const f16_t* KT = lkt[buf];
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      f32x16 s = zero16(), dp = zero16();
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        s = mfma(ld8(K + kb0 + mb * 8 * kBrick + kstep(ks)), qf[ks], s);
-        dp = mfma(ld8(V + kb0 + mb * 8 * kBrick + kstep(ks)), df[ks], dp);
-      }
-      if (full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl)) * (dp[r] + nD);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = mb * 32 + acc_row(r, hi);
-          bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < qp.nrows;
-          if constexpr (kMasked) ok = ok && (mi < 0 || ((rmask >> key) & 1ull));
-          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl));
-          s[r] = ok ? p * (dp[r] + nD) : 0.f;  // padding may hold NaN
-        }
-      }
-      const f16x8 d0 = pack8(s, 0), d1 = pack8(s, 8);
-#pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        acc[a] = mfma(ld8(KT + tb0 + a * 4 * kCBrick + (mb * 2 + 0) * 128), d0, acc[a]);
-        acc[a] = mfma(ld8(KT + tb0 + a * 4 * kCBrick + (mb * 2 + 1) * 128), d1, acc[a]);
-      }
-    }
-    wait_all_loads();
-    __syncthreads();
-  }
-
-  const float gscale = scale / pow2_scale(*dmax, kTopVO) / sv / sk;  // undo the operand scalings
-  const bool valid = row < qp.nrows;
-  const int64_t grow = (int64_t)qp.phys * 64 + row;
-  TG* out = dq + (grow * Hq + h) * kD;
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = a * 32 + 8 * j + 4 * hi + i;  // d < 64 pairs with d + 64 (block a + 2)
-        const float g1 = acc[a][4 * j + i] * gscale, g2 = acc[a + 2][4 * j + i] * gscale;
-        float r1 = 0.f, r2 = 0.f;
-        if (valid) {
-          const float2 c = cs ? cs[grow * (kD / 2) + d] : make_float2(1.f, 0.f);
-          r1 = g1 * c.x + g2 * c.y;
-          r2 = g2 * c.x - g1 * c.y;
-        }
-        st_f(out + d, r1);
-        st_f(out + d + 64, r2);
-      }
-}
-
 // LDS transpose read (gfx950 ds_read_b64_tr_b16).  Within each group of 16
 // lanes, lane i receives element i % 4 of the 8-byte pieces fetched by lanes
 // 4 j + i / 4 (j = 0..3).  So if source lane 4 j + q reads row (r0 + j) at
@@ -926,6 +794,134 @@ __device__ __forceinline__ f16x8 frag_tr(const f16_t* tb, int kk, int dblk) {
     for (int j = 0; j < 4; ++j) out[half * 4 + j] = (f16_t)v[j];
   }
   return out;
+}
+
+// dQ for one query block (64 rows) x one KV head.  Eight waves, wave (hh, nb) =
+// query head 4 g + hh and rows 32 nb ..; the K and V tiles are double-buffered in
+// LDS like the forward's, and the dQ products read K's columns with transpose reads
+// (no transposed copy of K is staged).
+// kMasked: the forward's tile masks, read the same way.
+template <typename TG, bool kMasked>
+__global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
+    const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vn, const f16_t* __restrict__ dOn, const float2* __restrict__ ldd,
+    const float2* __restrict__ cs, const uint32_t* __restrict__ dmax, const QPage* __restrict__ qpages,
+    const int32_t* __restrict__ order, const Tile* __restrict__ tiles, const int32_t* __restrict__ tile_mask,
+    const uint64_t* __restrict__ masks, TG* __restrict__ dq,
+    const uint32_t* __restrict__ amax, int n_qp, int Hq, int Hkv, float sl2_raw, float scale) {
+  __shared__ __attribute__((aligned(1024))) f16_t lk[2][kPageB];
+  __shared__ __attribute__((aligned(1024))) f16_t lvv[2][kPageB];
+  int unit, g;
+  if (!map_item(n_qp, Hkv, unit, g)) return;
+  // fp16 copies: sq q, sk k, sv v, sdo dO (powers of two); the S and dP offsets in ldd are
+  // in the same scaled units, so dS comes out as sdo sv dS and the sum over keys of dS k
+  // as sdo sv sk dQ / scale
+  const float sq = pow2_scale(amax[0], kTopQK), sk = pow2_scale(amax[1], kTopQK), sv = pow2_scale(amax[2], kTopVO);
+  const float sl2 = sl2_raw / sq / sk;
+  const QPage qp = dbg_qpage(qpages[dbg_index(order[unit], n_qp, kDbgQPage)]);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int hh = wave & 3, nb = wave >> 2;
+  const int h = g * 4 + hh;
+  const int row = nb * 32 + l32;
+  const int kb0 = frag_base(l32, hi), tb = tr_base(lane);
+  const uint32_t rlo = brick_lane_off(lane);
+
+  f16x8 qf[8], df[8];
+  const f16_t* qb = qn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
+  const f16_t* db = dOn + ((int64_t)qp.phys * Hq + h) * 64 * kD;
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    qf[ks] = ld8(qb + row * kD + ks * 16 + hi * 8);
+    df[ks] = ld8(db + row * kD + ks * 16 + hi * 8);
+  }
+  const float2 lt = ldd[((int64_t)qp.phys * Hq + h) * 64 + row];
+  const float nl = lt.x * sl2, nD = lt.y;  // exponent offset (log2 domain) and -D
+  f32x16 acc[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) acc[a] = zero16();
+
+  const int T = qp.tile_count;
+  if (wave < 4) {
+    const int64_t base = ((int64_t)dbg_page(tiles[qp.tile_begin].page, kDbgTilePage) * Hkv + g) * kTile;
+    stage_bricks<4>(lk[0], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
+    stage_bricks<4>(lvv[0], tile_rsrc(vn + base, kTile * 2), 4 * wave, rlo);
+  }
+  wait_all_loads();
+  __syncthreads();
+
+  for (int t = 0; t < T; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < T && wave < 4) {
+      const int64_t base = ((int64_t)dbg_page(tiles[qp.tile_begin + t + 1].page, kDbgTilePage) * Hkv + g) * kTile;
+      stage_bricks<4>(lk[buf ^ 1], tile_rsrc(kn + base, kTile * 2), 4 * wave, rlo);
+      stage_bricks<4>(lvv[buf ^ 1], tile_rsrc(vn + base, kTile * 2), 4 * wave, rlo);
+    }
+    const int lohi = dbg_lohi(tiles[qp.tile_begin + t].lohi);
+    const int lo = lohi & 0xff, hi_t = (lohi >> 8) & 0xff;
+    int mi = -1;
+    uint64_t rmask = 0;
+    if constexpr (kMasked) {
+      mi = dbg_mask(tile_mask[qp.tile_begin + t]);
+      if (mi >= 0) rmask = masks[(int64_t)mi * 128 + row];
+    }
+    const bool diag = (t == T - 1) && mi < 0;
+    const bool full = lo == 0 && hi_t == 64 && !diag && qp.nrows == 64 && mi < 0;
+    const f16_t* K = lk[buf];
+    const f16_t* V = lvv[buf];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      f32x16 s = zero16(), dp = zero16();
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        s = mfma(ld8(K + kb0 + mb * 8 * kBrick + kstep(ks)), qf[ks], s);
+        dp = mfma(ld8(V + kb0 + mb * 8 * kBrick + kstep(ks)), df[ks], dp);
+      }
+      if (full) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl)) * (dp[r] + nD);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = mb * 32 + acc_row(r, hi);
+          bool ok = key >= lo && key < hi_t && (!diag || key <= row) && row < qp.nrows;
+          if constexpr (kMasked) ok = ok && (mi < 0 || ((rmask >> key) & 1ull));
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, nl));
+          s[r] = ok ? p * (dp[r] + nD) : 0.f;  // padding may hold NaN
+        }
+      }
+      const f16x8 d0 = pack8(s, 0), d1 = pack8(s, 8);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        acc[a] = mfma(frag_tr(K + tb, mb * 2 + 0, a), d0, acc[a]);
+        acc[a] = mfma(frag_tr(K + tb, mb * 2 + 1, a), d1, acc[a]);
+      }
+    }
+    wait_all_loads();
+    __syncthreads();
+  }
+
+  const float gscale = scale / pow2_scale(*dmax, kTopVO) / sv / sk;  // undo the operand scalings
+  const bool valid = row < qp.nrows;
+  const int64_t grow = (int64_t)qp.phys * 64 + row;
+  TG* out = dq + (grow * Hq + h) * kD;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = a * 32 + 8 * j + 4 * hi + i;  // d < 64 pairs with d + 64 (block a + 2)
+        const float g1 = acc[a][4 * j + i] * gscale, g2 = acc[a + 2][4 * j + i] * gscale;
+        float r1 = 0.f, r2 = 0.f;
+        if (valid) {
+          const float2 c = cs ? cs[grow * (kD / 2) + d] : make_float2(1.f, 0.f);
+          r1 = g1 * c.x + g2 * c.y;
+          r2 = g2 * c.x - g1 * c.y;
+        }
+        st_f(out + d, r1);
+        st_f(out + d + 64, r2);
+      }
 }
 
 // Sum the two head-parity waves' dK (or dV) accumulators of every 32-key tile
@@ -1571,16 +1567,16 @@ void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const 
 }
 
 template <typename TG>
-void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* kt,
-                    const f16_t* vn, const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
+void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vn,
+                    const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
                     const QPage* qpages, const int32_t* order, const Tile* tiles, const int32_t* tile_mask,
                     const uint64_t* masks, TG* dq, const uint32_t* amax, hipStream_t st) {
   if (tile_mask)
-    dq_mfma_kernel<TG, true><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, kt, vn, dOn, ld, cs, dmax, qpages, order,
+    dq_mfma_kernel<TG, true><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, vn, dOn, ld, cs, dmax, qpages, order,
                                                                     tiles, tile_mask, masks, dq, amax, (int)n_qp,
                                                                     s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
   else
-    dq_mfma_kernel<TG, false><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, kt, vn, dOn, ld, cs, dmax, qpages,
+    dq_mfma_kernel<TG, false><<<run_grid(n_qp, s.Hkv), 512, 0, st>>>(qn, kn, vn, dOn, ld, cs, dmax, qpages,
                                                                      order, tiles, nullptr, nullptr, dq, amax,
                                                                      (int)n_qp, s.Hq, s.Hkv, s.scale * kLog2e,
                                                                      s.scale);
@@ -1604,7 +1600,7 @@ void launch_dkdv_mfma(const LaunchShape& s, int64_t n_pairs, const f16_t* qn, co
 
 #define INST_MFMA_BWD(TG)                                                                                      \
   template void launch_dq_mfma<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,      \
-                                   const f16_t*, const f16_t*, const float2*, const float2*, const uint32_t*,  \
+                                   const f16_t*, const float2*, const float2*, const uint32_t*,                \
                                    const QPage*, const int32_t*, const Tile*, const int32_t*,                  \
                                    const uint64_t*, TG*, const uint32_t*, hipStream_t);                        \
   template void launch_dkdv_mfma<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,    \

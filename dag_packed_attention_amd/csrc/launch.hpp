@@ -68,8 +68,8 @@ void launch_fwd_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const 
                      const uint64_t* masks, bf16_t* o, float* lse, bf16_t* o_lo, const uint32_t* amax,
                      hipStream_t st);
 template <typename TG>
-void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* kt,
-                    const f16_t* vn, const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
+void launch_dq_mfma(const LaunchShape& s, int64_t n_qp, const f16_t* qn, const f16_t* kn, const f16_t* vn,
+                    const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
                     const QPage* qpages, const int32_t* order, const Tile* tiles, const int32_t* tile_mask,
                     const uint64_t* masks, TG* dq, const uint32_t* amax, hipStream_t st);
 template <typename TG>
