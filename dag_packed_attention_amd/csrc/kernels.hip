@@ -974,7 +974,7 @@ __device__ __forceinline__ void dkdv_reduce_store(const f32x16 (&acc)[4], float*
 // 4 g + j and 4 g + 2 + j, keeping its dK and dV (32 x 128 each) in accumulation
 // registers and its K fragments in registers; the two waves of a SIMD share the
 // key tile.  A half-step stages two heads' Q and dO rows (32 KiB) in LDS with
-// direct loads, double buffered: every staged byte now feeds 128 keys, so a pair
+// direct loads issued by waves 0..3, double buffered: every staged byte now feeds 128 keys, so a pair
 // moves half the staging bytes per product that one page would.  Within a
 // half-step the products run as four MFMA chains S, dP, dV, dK (exponentials
 // between the dP products, dS between the dV products); hidden keys get a
@@ -1059,8 +1059,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     nxt_m.a = dbg_mask(nxt_m.a), nxt_m.b = dbg_mask(nxt_m.b);
     n2_m.a = dbg_mask(n2_m.a), n2_m.b = dbg_mask(n2_m.b);
   }
-  // staging role: head sj of the half-step, tensor ts (0: Q, 1: dO), bricks sb0 .. sb0 + 3
-  const int sj = wave & 1, ts = (wave >> 1) & 1, sb0 = 4 * (wave >> 2);
+  // staging by waves 0..3 (one per SIMD; measured faster than all eight): head sj of the
+  // half-step, tensor ts (0: Q, 1: dO), all eight bricks
+  const bool stager = wave < 4;
+  const int sj = wave & 1, ts = (wave >> 1) & 1;
   const uint32_t rlo = brick_lane_off(lane);
   const uint32_t llo = (uint32_t)((2 * (lane & 31) + (lane >> 5)) * 4);
   const f16_t* stsrc = ts == 0 ? qn : dOn;
@@ -1069,8 +1071,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
   };
   {
     const int64_t r0 = head_row0(cur, 0, sj);
-    stage_bricks<4>(qd[0][sj][ts], tile_rsrc(stsrc + r0 * kD, 32 * kD * 2), sb0, rlo);
-    if (ts == 0 && sb0 == 0) dma4(&lds_ld[0][sj][0], llo, tile_rsrc(ldd + r0, 256), 0);
+    if (stager) {
+      stage_bricks<8>(qd[0][sj][ts], tile_rsrc(stsrc + r0 * kD, 32 * kD * 2), 0, rlo);
+      if (ts == 0) dma4(&lds_ld[0][sj][0], llo, tile_rsrc(ldd + r0, 256), 0);
+    }
   }
   wait_all_loads();
   __syncthreads();
@@ -1085,7 +1089,7 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const int64_t nr0 = head_row0(sd, hp ^ 1, sj);
     const i32x4 nrs = tile_rsrc(stsrc + nr0 * kD, 32 * kD * 2);
     f16_t* ndst = qd[buf ^ 1][sj][ts];
-    const bool offs = ts == 0 && sb0 == 0;
+    const bool offs = stager && ts == 0;
 
     const uint32_t inf = ((uint32_t)cur.info >> (16 * side)) & 0xffffu;
     uint64_t kmask = 0;
@@ -1098,8 +1102,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
     const bool diag = (inf >> 15) & 1;
     if (!active || lo >= hi_t) {
       // this wave's page is not read by this step: stage only
+      if (stager) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dma16(ndst + (sb0 + i) * kBrick, rlo, nrs, (sb0 + i) * 4 * kD * 2);
+        for (int i = 0; i < 8; ++i) dma16(ndst + i * kBrick, rlo, nrs, i * 4 * kD * 2);
+      }
       if (offs) dma4(&lds_ld[buf ^ 1][sj][0], llo, tile_rsrc(ldd + nr0, 256), 0);
     } else {
       const f16_t* Qt = qd[buf][j][0];
@@ -1127,15 +1133,14 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
       const float koff = (key >= lo && key < hi_t) ? 0.f : -INFINITY;
       {
         // S: Q fragments read one k-step ahead; the next unit's staging goes out one
-        // load per two k-steps
+        // load per k-step (waves 0..3)
         f16x8 qa[2];
         qa[0] = ld8(Qt + qb);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
           if (ks < 7) qa[(ks + 1) & 1] = ld8(Qt + qb + kstep(ks + 1));
           s = mfma(qa[ks & 1], kf[ks], s);
-          if ((ks & 1) == 0)
-            dma16(ndst + (sb0 + ks / 2) * kBrick, rlo, nrs, (sb0 + ks / 2) * 4 * kD * 2);
+          if (stager) dma16(ndst + ks * kBrick, rlo, nrs, ks * 4 * kD * 2);
         }
         if (offs) dma4(&lds_ld[buf ^ 1][sj][0], llo, tile_rsrc(ldd + nr0, 256), 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
