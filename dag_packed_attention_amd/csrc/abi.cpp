@@ -31,6 +31,10 @@ struct DeviceTables {
   KEntry* kentries = nullptr;
   int32_t* kv_off = nullptr;
   int32_t* bwd_order = nullptr;
+  int32_t* kgroups = nullptr;
+  int64_t* kgroup_off = nullptr;
+  GStep* kgsteps = nullptr;
+  int32_t* group_order = nullptr;
   int32_t* kpairs = nullptr;
   int64_t* kpair_off = nullptr;
   KStep* kpsteps = nullptr;
@@ -202,7 +206,9 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
   bytes += align256(P.pos_of_row.size() * 4) + align256(P.tiles.size() * sizeof(Tile)) +
            align256(P.qpages.size() * sizeof(QPage)) + align256(P.fwd_order.size() * 4) +
            align256(P.kentries.size() * sizeof(KEntry)) + align256(P.kv_off.size() * 4) +
-           align256(P.bwd_order.size() * 4) + align256(P.kpairs.size() * 4) + align256(P.kpair_off.size() * 8) +
+           align256(P.bwd_order.size() * 4) + align256(P.kgroups.size() * 4) +
+           align256(P.kgroup_off.size() * 8) + align256(P.kgsteps.size() * sizeof(GStep)) +
+           align256(P.group_order.size() * 4) + align256(P.kpairs.size() * 4) + align256(P.kpair_off.size() * 8) +
            align256(P.kpsteps.size() * sizeof(KStep)) + align256(P.pair_order.size() * 4) +
            align256(P.tile_mask.size() * 4) + align256(P.masks.size() * 8) +
            align256(P.kstep_mask.size() * sizeof(KMask)) +
@@ -230,6 +236,10 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
   D->kentries = dev_take<KEntry>(b, off, P.kentries.size());
   D->kv_off = dev_take<int32_t>(b, off, P.kv_off.size());
   D->bwd_order = dev_take<int32_t>(b, off, P.bwd_order.size());
+  D->kgroups = dev_take<int32_t>(b, off, P.kgroups.size());
+  D->kgroup_off = dev_take<int64_t>(b, off, P.kgroup_off.size());
+  D->kgsteps = dev_take<GStep>(b, off, P.kgsteps.size());
+  D->group_order = dev_take<int32_t>(b, off, P.group_order.size());
   D->kpairs = dev_take<int32_t>(b, off, P.kpairs.size());
   D->kpair_off = dev_take<int64_t>(b, off, P.kpair_off.size());
   D->kpsteps = dev_take<KStep>(b, off, P.kpsteps.size());
@@ -263,6 +273,10 @@ dag_status ensure_uploaded(Plan& P, hipStream_t st) {
             put(D->kentries, P.kentries.data(), P.kentries.size() * sizeof(KEntry)) &&
             put(D->kv_off, P.kv_off.data(), P.kv_off.size() * 4) &&
             put(D->bwd_order, P.bwd_order.data(), P.bwd_order.size() * 4) &&
+            put(D->kgroups, P.kgroups.data(), P.kgroups.size() * 4) &&
+            put(D->kgroup_off, P.kgroup_off.data(), P.kgroup_off.size() * 8) &&
+            put(D->kgsteps, P.kgsteps.data(), P.kgsteps.size() * sizeof(GStep)) &&
+            put(D->group_order, P.group_order.data(), P.group_order.size() * 4) &&
             put(D->kpairs, P.kpairs.data(), P.kpairs.size() * 4) &&
             put(D->kpair_off, P.kpair_off.data(), P.kpair_off.size() * 8) &&
             put(D->kpsteps, P.kpsteps.data(), P.kpsteps.size() * sizeof(KStep)) &&
@@ -341,6 +355,8 @@ dag_status dbg_begin(const Plan& P, hipStream_t st) {
   lim.steps = (int64_t)P.kpsteps.size();
   lim.qpages = (int64_t)P.qpages.size();
   lim.pairs = (int64_t)P.kpairs.size() / 2;
+  lim.groups = (int64_t)P.kgroups.size() / kGroup;
+  lim.gsteps = (int64_t)P.kgsteps.size();
   if (!dbg_set_limits(lim, st)) return set_err(DAG_E_DEVICE, "upload of the debug check limits failed");
   return DAG_OK;
 }
@@ -591,6 +607,24 @@ dag_status dag_plan_readers(const dag_plan* plan, int32_t row, int32_t* query_ro
   if (row < 0 || row >= P.info.rows) return set_err(DAG_E_INVALID, "row out of range");
   const int32_t K = row / kPage, c = row % kPage;
   std::vector<int32_t> v;
+  const int64_t ngroups = (int64_t)P.kgroups.size() / kGroup;
+  for (int64_t gr = 0; gr < ngroups && c < P.page_nrows[K]; ++gr) {
+    for (int side = 0; side < kGroup; ++side) {
+      if (P.kgroups[kGroup * gr + side] != K) continue;
+      for (int64_t i = P.kgroup_off[gr]; i < P.kgroup_off[gr + 1]; ++i) {
+        const GStep& st = P.kgsteps[i];
+        const uint32_t inf = gvis_of(st, side);
+        const int32_t lo = gvis_lo(inf), hi = gvis_hi(inf);
+        const bool diag = gvis_diag(inf);
+        if (c < lo || c >= hi) continue;
+        for (int32_t rr = 0; rr < 32; ++rr) {
+          const int32_t r = st.rb * 32 + rr;
+          if (r >= P.page_nrows[st.qph] || (diag && c > r)) continue;
+          v.push_back(st.qph * kPage + r);
+        }
+      }
+    }
+  }
   const int64_t npairs = (int64_t)P.kpairs.size() / 2;
   for (int64_t pr = 0; pr < npairs && c < P.page_nrows[K]; ++pr) {
     for (int side = 0; side < 2; ++side) {
@@ -767,6 +801,9 @@ dag_status dag_attn_bwd(dag_plan* plan, const dag_attn_params* p, const void* q,
       using TG = std::remove_pointer_t<decltype(tag)>;
       {
         Span sp(P, DAG_K_DKDV, stream);
+        launch_dkdv_group<TG>(s, (int64_t)P.group_order.size(), (const f16_t*)w.qn, (const f16_t*)w.kn,
+                              (const f16_t*)w.vn, (const f16_t*)w.dOn, w.ld, w.cs, w.amax + 3, D.group_order,
+                              D.kgroups, D.kgroup_off, D.kgsteps, D.page_nrows, (TG*)dk, (TG*)dv, w.amax, stream);
         launch_dkdv_mfma<TG>(s, (int64_t)P.pair_order.size(), (const f16_t*)w.qn, (const f16_t*)w.kn,
                              (const f16_t*)w.vn, (const f16_t*)w.dOn, w.ld, w.cs, w.amax + 3, D.pair_order,
                              D.kpairs, D.kpair_off, D.kpsteps, D.kstep_mask, D.masks, D.page_nrows, (TG*)dk,

@@ -161,6 +161,24 @@ __device__ __forceinline__ KStep dbg_step(KStep d) {
   return d;
 }
 
+// a four-page group's reader step: its query page, its 32-row half and the pages' intervals
+__device__ __forceinline__ GStep dbg_gstep(GStep d) {
+#ifdef DAG_DEBUG
+  d.qph = dbg_page(d.qph, kDbgStepPage);
+  bool ok = d.rb == 0 || d.rb == 1;
+  for (int i = 0; i < kGroup; ++i) {
+    const uint32_t v = gvis_of(d, i);
+    ok = ok && gvis_lo(v) <= gvis_hi(v) && gvis_hi(v) <= 64;
+  }
+  if (!ok) {
+    dbg_fail(kDbgInterval, (int64_t)d.vis[0]);
+    d.rb = 0;
+    d.vis[0] = d.vis[1] = 0;  // no page read
+  }
+#endif
+  return d;
+}
+
 // position of row r inside its transposed 16-group (bits 2 and 3 swapped)
 __device__ __forceinline__ int tperm(int r) {
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
@@ -967,8 +985,9 @@ __device__ __forceinline__ void dkdv_reduce_store(const f32x16 (&acc)[4], float*
   }
 }
 
-// dK, dV for a pair of KV pages (pages 2 i and 2 i + 1 of one node, or a lone last
-// page) and one KV head.  Each 32-row reader step of the pair's merged reader list
+// dK, dV for a pair of KV pages (a node of one or two pages, or consecutive pages of a
+// packed plan; or a lone page) and one KV head; nodes of three pages or more run in
+// four-page groups (dkdv_group_kernel below).  Each 32-row reader step of the pair's merged reader list
 // is taken as two half-steps, query heads 4 g + 2 hp + {0, 1} (hp = 0, 1).  Eight
 // waves: wave (kt, j) serves keys 32 (kt % 2) .. of page kt / 2 and the query heads
 // 4 g + j and 4 g + 2 + j, keeping its dK and dV (32 x 128 each) in accumulation
@@ -1282,6 +1301,327 @@ __global__ __launch_bounds__(512, 1) void dkdv_mfma_kernel(
                            cs, dv);
 }
 
+// Write the accumulated dK (or dV) of two of the group's pages (slots 2 hf, 2 hf + 1)
+// through LDS, so that every row goes out as whole 256-byte runs: the four waves of
+// those pages park their 32 x 128 blocks, then all threads scale, rotate dK back by
+// R(pos)^T and store.  Each key has one accumulating wave: no sums, no atomics.
+template <bool kRotate, typename TG>
+__device__ __forceinline__ void dkdv_store_half(const f32x16 (&acc)[4], float* red, int hf, int ps, int kb,
+                                                bool active, int hi, int l32, int tid, const int (&phys)[kGroup],
+                                                const int (&nrows)[kGroup], int g, int Hkv, float mul,
+                                                const float2* __restrict__ cs, TG* __restrict__ out) {
+  __syncthreads();
+  if ((ps >> 1) == hf && active) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((ps & 1) * 64 + kb * 32 + acc_row(r, hi)) * (kD + 1) + b * 32 + l32] = acc[b][r];
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 128 * 64; idx += 512) {
+    const int k2 = idx / 64, i = idx % 64;  // key of the two pages, column pair (i, i + 64)
+    const int slot = 2 * hf + (k2 >> 6), row = k2 & 63;
+    const int page = phys[slot];
+    if (page < 0) continue;
+    const int64_t grow = (int64_t)page * 64 + row;
+    float a = red[k2 * (kD + 1) + i] * mul, b = red[k2 * (kD + 1) + i + 64] * mul;
+    if (row >= nrows[slot]) {
+      a = b = 0.f;
+    } else if (kRotate && cs) {
+      const float2 c = cs[grow * (kD / 2) + i];
+      const float a2 = a * c.x + b * c.y;
+      b = b * c.x - a * c.y;
+      a = a2;
+    }
+    TG* o = out + (grow * Hkv + g) * kD;
+    st_f(o + i, a);
+    st_f(o + i + 64, b);
+  }
+}
+
+// dK, dV for a group of up to four KV pages (consecutive pages of one node, or of the
+// packed page sequence) and one KV head.  Eight waves: wave (ps, kb) owns keys
+// 32 kb .. 32 kb + 31 of the group's page ps and keeps their dK and dV (32 x 128 each)
+// in accumulation registers and their K fragments in registers; the V tiles of the
+// four pages sit in LDS.  Each 32-row reader step of the group's merged reader list is
+// taken as two half-steps of two query heads (4 g + 2 hp + {0, 1}): a half-step stages
+// those heads' Q and dO rows (32 KiB) in LDS with direct loads, double buffered, and
+// every wave runs both heads through it, so each staged byte feeds 256 keys.  Per head
+// the products run as four MFMA chains S, dP, dV, dK (exponentials between the dP
+// products, dS between the dV products); hidden keys get a per-lane -inf offset.  A
+// wave whose page the step does not read only stages.  Every key has one owner wave,
+// so the pages are written once at the end: deterministic, no atomics.  Plans with one
+// node per page only (packed plans run every page in pairs).
+template <typename TG>
+__global__ __launch_bounds__(512, 1) void dkdv_group_kernel(
+    const f16_t* __restrict__ qn, const f16_t* __restrict__ kn, const f16_t* __restrict__ vn,
+    const f16_t* __restrict__ dOn, const float2* __restrict__ ldd, const float2* __restrict__ cs,
+    const uint32_t* __restrict__ dmax, const int32_t* __restrict__ group_order, const int32_t* __restrict__ groups,
+    const int64_t* __restrict__ group_off, const GStep* __restrict__ gsteps, const int32_t* __restrict__ page_nrows,
+    TG* __restrict__ dk, TG* __restrict__ dv, const uint32_t* __restrict__ amax, int n_groups, int Hq, int Hkv,
+    float sl2_raw, float scale) {
+  // [buffer][head of the half-step][Q, dO][32 x 128] f16 (the first 65 KiB are reused
+  // for the output staging at the end), the V tiles of the four pages, and
+  // [buffer][head] the 32 rows' offsets: -lse / scale for S, then -D for dP
+  __shared__ __attribute__((aligned(1024))) f16_t qd[2][2][2][kStepB];
+  __shared__ __attribute__((aligned(1024))) f16_t lvp[kGroup][kPageB];
+  __shared__ __attribute__((aligned(16))) float lds_ld[2][2][64];
+  int unit, g;
+  if (!map_item(n_groups, Hkv, unit, g)) return;
+  // fp16 copies: sq q, sk k, sv v, sdo dO (powers of two), offsets in ldd in the same
+  // units: P is exact, dS comes out as sdo sv dS, the sums as sdo dV and sdo sv sq dK / scale
+  const float sq = pow2_scale(amax[0], kTopQK), sk = pow2_scale(amax[1], kTopQK), sv = pow2_scale(amax[2], kTopVO);
+  const float sl2 = sl2_raw / sq / sk;
+  const int gr = dbg_index(group_order[unit], n_groups, kDbgGroup);
+  int phys[kGroup];
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) {
+    phys[i] = groups[kGroup * gr + i];
+    if (phys[i] != -1) phys[i] = dbg_page(phys[i], kDbgGroup);
+  }
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int ps = wave >> 1, kb = wave & 1;  // page slot of the group, key half of the page
+  const int page = phys[ps];
+  const bool active = page >= 0;  // a group with fewer pages: this wave only stages
+
+  f16x8 kf[8];
+  {
+    const int64_t base = ((int64_t)(active ? page : phys[0]) * Hkv + g) * 64 * kD;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kf[ks] = ld8(kn + base + (kb * 32 + l32) * kD + ks * 16 + hi * 8);
+    // the two waves of page ps stage its V tile, eight bricks each
+    if (active)
+      stage_bricks<8>(lvp[ps], tile_rsrc(vn + ((int64_t)page * Hkv + g) * kTile, kTile * 2), 8 * kb,
+                      brick_lane_off(lane));
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) pin(kf[ks]);
+  }
+  f32x16 adk[4], adv[4];  // [d block]
+#pragma unroll
+  for (int b = 0; b < 4; ++b) adk[b] = adv[b] = zero16();
+
+  // Step descriptors are uniform and come through the scalar cache ahead of their
+  // use (no vector-memory wait for them, which would also wait for the staging loads).
+  int64_t s_begin = group_off[gr];
+  int n_steps = (int)(group_off[gr + 1] - s_begin);
+#ifdef DAG_DEBUG
+  if (s_begin < 0 || n_steps < 1 || s_begin + n_steps > g_dbg_lim.gsteps) {
+    dbg_fail(kDbgStepRange, s_begin);
+    s_begin = 0;
+    n_steps = 1;
+  }
+#endif
+  const int n_units = 2 * n_steps;
+  const GStep* kst = gsteps + s_begin;
+  GStep cur = dbg_gstep(kst[0]);
+  GStep nxt = dbg_gstep(kst[min(1, n_steps - 1)]);
+  // staging by waves 0..3 (one per SIMD): head sj of the half-step, tensor ts (0: Q,
+  // 1: dO), all eight bricks
+  const bool stager = wave < 4;
+  const int sj = wave & 1, ts = (wave >> 1) & 1;
+  const uint32_t rlo = brick_lane_off(lane);
+  const uint32_t llo = (uint32_t)((2 * (lane & 31) + (lane >> 5)) * 4);
+  const f16_t* stsrc = ts == 0 ? qn : dOn;
+  auto head_row0 = [&](const GStep& d, int hp, int jj) -> int64_t {  // first staged row of head jj
+    return ((int64_t)d.qph * Hq + g * 4 + 2 * hp + jj) * 64 + d.rb * 32;
+  };
+  {
+    const int64_t r0 = head_row0(cur, 0, sj);
+    if (stager) {
+      stage_bricks<8>(qd[0][sj][ts], tile_rsrc(stsrc + r0 * kD, 32 * kD * 2), 0, rlo);
+      if (ts == 0) dma4(&lds_ld[0][sj][0], llo, tile_rsrc(ldd + r0, 256), 0);
+    }
+  }
+  wait_all_loads();
+  __syncthreads();
+
+  const int key = kb * 32 + l32;
+  const int qb = frag_base(l32, hi), vb = frag_base(key, hi), tb = tr_base(lane);
+  const f16_t* Vp = lvp[ps];
+  for (int u = 0; u < n_units; ++u) {
+    const int buf = u & 1, hp = u & 1;
+    // staging of unit u + 1 (the same step's second half, or the next step's first);
+    // on the last unit it repeats this one into the idle buffer (harmless)
+    const GStep& sd = hp ? nxt : cur;
+    const int64_t nr0 = head_row0(sd, hp ^ 1, sj);
+    const i32x4 nrs = tile_rsrc(stsrc + nr0 * kD, 32 * kD * 2);
+    f16_t* ndst = qd[buf ^ 1][sj][ts];
+    const bool offs = stager && ts == 0;
+
+    const uint32_t inf = gvis_of(cur, ps);
+    const int lo = gvis_lo(inf), hi_t = gvis_hi(inf);
+    const bool diag = gvis_diag(inf);
+    if (!active || lo >= hi_t) {
+      // this wave's page is not read by this step: stage only
+      if (stager) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma16(ndst + i * kBrick, rlo, nrs, i * 4 * kD * 2);
+      }
+      if (offs) dma4(&lds_ld[buf ^ 1][sj][0], llo, tile_rsrc(ldd + nr0, 256), 0);
+    } else {
+      // A key outside the step's visible range gets -inf added before the exponential.
+      const float koff = (key >= lo && key < hi_t) ? 0.f : -INFINITY;
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const f16_t* Qt = qd[buf][jj][0];
+        const f16_t* Dt = qd[buf][jj][1];
+        // S = Q K^T - lse / scale, dP = dO V^T - D: 32 rows (M) x this wave's 32 keys (N);
+        // lane holds key kb*32 + l32 and rows rb*32 + acc_row(r, hi), so the offsets of
+        // its rows come as four runs of four consecutive floats straight into the
+        // accumulators
+        f32x16 s, dp;
+        {
+          const float* L = lds_ld[buf][jj];
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const float4 a = *reinterpret_cast<const float4*>(L + 8 * q4 + 4 * hi);
+            const float4 b = *reinterpret_cast<const float4*>(L + 32 + 8 * q4 + 4 * hi);
+            s[4 * q4] = a.x, s[4 * q4 + 1] = a.y, s[4 * q4 + 2] = a.z, s[4 * q4 + 3] = a.w;
+            dp[4 * q4] = b.x, dp[4 * q4 + 1] = b.y, dp[4 * q4 + 2] = b.z, dp[4 * q4 + 3] = b.w;
+          }
+        }
+        // The four products run as four chains of eight MFMAs, S, dP, dV, dK, and each
+        // chain carries the vector work of the previous one: the exponentials of S run
+        // between the dP products, dS = P (dP - D) between the dV products.
+        {
+          // S: Q fragments read one k-step ahead; with the first head, the next unit's
+          // staging goes out one load per k-step (waves 0..3)
+          f16x8 qa[2];
+          qa[0] = ld8(Qt + qb);
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            if (ks < 7) qa[(ks + 1) & 1] = ld8(Qt + qb + kstep(ks + 1));
+            s = mfma(qa[ks & 1], kf[ks], s);
+            if (jj == 0 && stager) dma16(ndst + ks * kBrick, rlo, nrs, ks * 4 * kD * 2);
+          }
+          if (jj == 0 && offs) dma4(&lds_ld[buf ^ 1][sj][0], llo, tile_rsrc(ldd + nr0, 256), 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+#pragma unroll
+          for (int ks = 0; ks < 7; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          // dP, with P = 2^(S scale log2 e) computed in between
+          f16x8 da[2], va[2];
+          da[0] = ld8(Dt + qb);
+          va[0] = ld8(Vp + vb);
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            if (ks < 7) {
+              da[(ks + 1) & 1] = ld8(Dt + qb + kstep(ks + 1));
+              va[(ks + 1) & 1] = ld8(Vp + vb + kstep(ks + 1));
+            }
+            dp = mfma(da[ks & 1], va[ks & 1], dp);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, koff));
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            if (ks < 7) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (diag) {
+          // the reader's own page: key <= row (a hidden score may have overflowed: select)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = key <= cur.rb * 32 + acc_row(r, hi) ? s[r] : 0.f;
+        }
+        // Padding rows need no mask: their Q and dO rows and offsets are zero, so they add
+        // exact zeros to dV and dK.
+        const f16x8 pf0 = pack8(s, 0), pf1 = pack8(s, 8);
+        // dV += P^T dO, then dK += dS^T Q: keys (M) x d (N), the 32 rows contracted; d
+        // block b + 1's fragments (transpose reads) are read while block b's products run
+        const f16_t* Dtb = Dt + tb;
+        const f16_t* Qtb = Qt + tb;
+        f16x8 sf0, sf1;
+        f16x8 frq[2];
+        {
+          f16x8 fr[2][2];
+          fr[0][0] = frag_tr(Dtb, 0, 0);
+          fr[0][1] = frag_tr(Dtb, 1, 0);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            if (b < 3) {
+              fr[(b + 1) & 1][0] = frag_tr(Dtb, 0, b + 1);
+              fr[(b + 1) & 1][1] = frag_tr(Dtb, 1, b + 1);
+            }
+            adv[b] = mfma(pf0, fr[b & 1][0], adv[b]);
+            adv[b] = mfma(pf1, fr[b & 1][1], adv[b]);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) dp[r] *= s[r];
+          sf0 = pack8(dp, 0);
+          sf1 = pack8(dp, 8);
+          frq[0] = frag_tr(Qtb, 0, 0);
+          frq[1] = frag_tr(Qtb, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        {
+          f16x8 fr[2][2];
+          fr[0][0] = frq[0];
+          fr[0][1] = frq[1];
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            if (b < 3) {
+              fr[(b + 1) & 1][0] = frag_tr(Qtb, 0, b + 1);
+              fr[(b + 1) & 1][1] = frag_tr(Qtb, 1, b + 1);
+            }
+            adk[b] = mfma(sf0, fr[b & 1][0], adk[b]);
+            adk[b] = mfma(sf1, fr[b & 1][1], adk[b]);
+          }
+#pragma unroll
+          for (int b = 0; b < 3; ++b) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // after a step's second half, the descriptor two steps ahead: first needed by the
+    // staging one unit later, so a whole unit covers the scalar load
+    __builtin_amdgcn_sched_barrier(0);
+    if (hp) {
+      cur = nxt;
+      nxt = dbg_gstep(kst[min((u >> 1) + 2, n_steps - 1)]);
+    }
+    wait_all_loads();
+    __syncthreads();
+  }
+
+  const float inv_sdo = 1.f / pow2_scale(*dmax, kTopVO);  // undo the operand scalings
+  float* red = reinterpret_cast<float*>(&qd[0][0][0][0]);  // [128][129] fp32
+  int nrows[kGroup];
+#pragma unroll
+  for (int i = 0; i < kGroup; ++i) nrows[i] = phys[i] >= 0 ? page_nrows[phys[i]] : 0;
+  // dk (scaled, un-rotated) and dv, two pages at a time
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    dkdv_store_half<true>(adk, red, hf, ps, kb, active, hi, l32, tid, phys, nrows, g, Hkv, inv_sdo * scale / sv / sq,
+                          cs, dk);
+    dkdv_store_half<false>(adv, red, hf, ps, kb, active, hi, l32, tid, phys, nrows, g, Hkv, inv_sdo, cs, dv);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Generic kernels (any even head dim <= 128, any GQA ratio, bf16 or fp32 tensors).
 // One thread per query row (forward, dQ) or key row (dK/dV); fp32 throughout.
@@ -1593,6 +1933,7 @@ void launch_dkdv_mfma(const LaunchShape& s, int64_t n_pairs, const f16_t* qn, co
                       const int32_t* pair_order, const int32_t* pairs, const int64_t* pair_off, const KStep* psteps,
                       const KMask* pmasks, const uint64_t* masks, const int32_t* page_nrows, TG* dk, TG* dv,
                       const uint32_t* amax, hipStream_t st) {
+  if (n_pairs <= 0) return;  // every page in a four-page group
   if (pmasks)
     dkdv_mfma_kernel<TG, true><<<run_grid(n_pairs, s.Hkv), 512, 0, st>>>(
         qn, kn, vn, dOn, ld, cs, dmax, pair_order, pairs, pair_off, psteps, pmasks, masks, page_nrows, dk, dv, amax,
@@ -1601,6 +1942,18 @@ void launch_dkdv_mfma(const LaunchShape& s, int64_t n_pairs, const f16_t* qn, co
     dkdv_mfma_kernel<TG, false><<<run_grid(n_pairs, s.Hkv), 512, 0, st>>>(
         qn, kn, vn, dOn, ld, cs, dmax, pair_order, pairs, pair_off, psteps, nullptr, nullptr, page_nrows, dk, dv,
         amax, (int)n_pairs, s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
+}
+
+template <typename TG>
+void launch_dkdv_group(const LaunchShape& s, int64_t n_groups, const f16_t* qn, const f16_t* kn, const f16_t* vn,
+                       const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
+                       const int32_t* group_order, const int32_t* groups, const int64_t* group_off,
+                       const GStep* gsteps, const int32_t* page_nrows, TG* dk, TG* dv, const uint32_t* amax,
+                       hipStream_t st) {
+  if (n_groups <= 0) return;
+  dkdv_group_kernel<TG><<<run_grid(n_groups, s.Hkv), 512, 0, st>>>(
+      qn, kn, vn, dOn, ld, cs, dmax, group_order, groups, group_off, gsteps, page_nrows, dk, dv, amax, (int)n_groups,
+      s.Hq, s.Hkv, s.scale * kLog2e, s.scale);
 }
 
 #define INST_MFMA_BWD(TG)                                                                                      \
@@ -1612,7 +1965,11 @@ void launch_dkdv_mfma(const LaunchShape& s, int64_t n_pairs, const f16_t* qn, co
                                      const f16_t*, const float2*, const float2*, const uint32_t*,              \
                                      const int32_t*, const int32_t*, const int64_t*, const KStep*,             \
                                      const KMask*, const uint64_t*, const int32_t*, TG*, TG*,                  \
-                                     const uint32_t*, hipStream_t);
+                                     const uint32_t*, hipStream_t);                                            \
+  template void launch_dkdv_group<TG>(const LaunchShape&, int64_t, const f16_t*, const f16_t*, const f16_t*,   \
+                                      const f16_t*, const float2*, const float2*, const uint32_t*,             \
+                                      const int32_t*, const int32_t*, const int64_t*, const GStep*,            \
+                                      const int32_t*, TG*, TG*, const uint32_t*, hipStream_t);
 INST_MFMA_BWD(bf16_t)
 INST_MFMA_BWD(float)
 

@@ -14,7 +14,7 @@ typedef uint16_t bf16_t;  // bf16 bits
 // side.  In other builds dbg_enabled() is false and the other two do nothing.
 struct DbgLimits {
   int32_t pages, masks;
-  int64_t tiles, steps, qpages, pairs;
+  int64_t tiles, steps, qpages, pairs, groups, gsteps;
 };
 enum : uint32_t {
   kDbgQPage = 1,      // query page id or its launch-order index
@@ -25,6 +25,7 @@ enum : uint32_t {
   kDbgPair = 6,       // a KV page pair (index or page)
   kDbgStepRange = 7,  // a pair's reader steps outside the step table
   kDbgStepPage = 8,   // a reader step's query page
+  kDbgGroup = 9,      // a KV page group (index or page)
 };
 bool dbg_enabled();
 bool dbg_set_limits(const DbgLimits& lim, hipStream_t st);
@@ -78,6 +79,12 @@ void launch_dkdv_mfma(const LaunchShape& s, int64_t n_pairs, const f16_t* qn, co
                       const int32_t* pair_order, const int32_t* pairs, const int64_t* pair_off, const KStep* psteps,
                       const KMask* pmasks, const uint64_t* masks, const int32_t* page_nrows, TG* dk, TG* dv,
                       const uint32_t* amax, hipStream_t st);
+template <typename TG>
+void launch_dkdv_group(const LaunchShape& s, int64_t n_groups, const f16_t* qn, const f16_t* kn, const f16_t* vn,
+                       const f16_t* dOn, const float2* ld, const float2* cs, const uint32_t* dmax,
+                       const int32_t* group_order, const int32_t* groups, const int64_t* group_off,
+                       const GStep* gsteps, const int32_t* page_nrows, TG* dk, TG* dv, const uint32_t* amax,
+                       hipStream_t st);
 template <typename T>
 void launch_fwd_simple(const LaunchShape& s, int64_t n_qp, const float* qn, const float* kn, const T* v,
                        const QPage* qpages, const int32_t* order, const Tile* tiles, T* o, float* lse, T* o_lo,

@@ -242,6 +242,10 @@ dag_status build_packed_tables(Plan* P, std::string* err) {
   P->kentries.clear();
   P->kv_off.assign(n_pages + 1, 0);
   P->bwd_order.clear();
+  P->kgroups.clear();  // packed plans run every page in pairs
+  P->kgroup_off.assign(1, 0);
+  P->kgsteps.clear();
+  P->group_order.clear();
   P->kpairs.clear();
   P->kpair_off.assign(1, 0);
   P->kpsteps.clear();

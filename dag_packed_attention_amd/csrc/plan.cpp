@@ -326,25 +326,34 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
       for_each_entry([&](int32_t ph, const KEntry& e) { P->kentries[fill[ph]++] = e; });
     }
 
-    // KV page pairs for the dK/dV kernel: pages (0, 1), (2, 3), ... of each node; an odd
-    // last page goes alone (B = -1).  A pair's reader steps are its two pages' reader lists
-    // unrolled into 32-row steps and merged by one logical key: the other nodes' query pages
-    // first, by (reader node, query page, occurrence of that query page in the page's
-    // list), then the pages' own node's query pages, last page first.  A step that both
-    // pages see carries both visible ranges, a step that one page sees has an empty range
-    // for the other.  Every key is logical, so the merged order does not depend on the
-    // physical page placement.  Every page of a node has the same descendants and (per
-    // span) the same mount readers, and the node's own pages come last, latest first, so
-    // the pairs of one node, which run side by side, walk the shared reader steps in step
-    // with each other: each staged Q / dO tile is fetched from HBM once and served to the
-    // other pairs from L2.
+    int64_t small_pages = 0;
+    for (int32_t u = 0; u < n; ++u)
+      if (P->length[u] > 0 && P->npages[u] <= 2) small_pages += P->npages[u];
+    const bool small_in_pairs = 2 * small_pages > n_pages;
+    auto in_pair = [&](int32_t u) { return small_in_pairs && P->npages[u] <= 2; };
+    // KV pages for the dK/dV kernels: a node's pages in groups of four, 4 i .. 4 i + 3 (its
+    // last group may hold fewer).  When nodes of one or two pages hold most of the plan's
+    // pages (short segments), those go as pairs (or lone pages) instead, where the pair
+    // kernel leaves fewer waves idle; otherwise they stay in groups, so that the one launch
+    // takes every unit heaviest first (a second launch would start a long pair only after
+    // the last group).  A group's reader steps are its
+    // pages' reader lists unrolled into 32-row steps and merged by one logical key: the
+    // other nodes' query pages first, by (reader node, query page, occurrence of that
+    // query page in the page's list), then the pages' own node's query pages, last page
+    // first.  A step carries every page's visible range (empty for a page its rows do not
+    // read); a pair's the same, merged over its two pages.  Every key is logical, so the merged order does not depend on the physical
+    // page placement.  Every page of a node has the same descendants and (per span) the
+    // same mount readers, and the node's own pages come last, latest first, so the groups
+    // of one node, which run side by side, walk the shared reader steps in step with each
+    // other: a staged Q / dO tile fetched from HBM by one is served to the others from L2.
     {
       std::vector<int32_t> node_of_slot(n_pages, -1);
       for (int32_t w = 0; w < n; ++w)
         if (P->length[w] > 0) node_of_slot[P->slot0[w]] = w;
       struct Item {
-        int32_t own, w, lq, k, qph, info;  // own: the page's own node (sorted last, lq descending);
-      };                                   // info: lo << 1 | hi << 8 | diag << 15
+        int32_t own, w, lq, k, qph;  // own: the page's own node (sorted last, lq descending)
+        int32_t lo, hi, diag;
+      };
       auto key_less = [](const Item& a, const Item& b) {
         if (a.own != b.own) return a.own < b.own;
         if (a.w != b.w) return a.w < b.w;
@@ -356,43 +365,72 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
         for (int32_t e = P->kv_off[ph]; e < P->kv_off[ph + 1]; ++e) {
           const KEntry& k = P->kentries[e];
           const int32_t w = node_of_slot[k.slot_base];
-          const int32_t vis = k.lohi_diag;
-          const int32_t info = ((vis & 0xff) << 1) | (((vis >> 8) & 0xff) << 8) | (((vis >> 16) & 1) << 15);
+          const int32_t lh = k.lohi_diag;
           for (int32_t lq = k.lq0; lq < k.lq1; ++lq)
-            out.push_back(Item{w == u ? 1 : 0, w, lq, 0, P->page_table[k.slot_base + lq], info});
+            out.push_back(Item{w == u ? 1 : 0, w, lq, 0, P->page_table[k.slot_base + lq], lh & 0xff, (lh >> 8) & 0xff,
+                               (lh >> 16) & 1});
         }
         std::stable_sort(out.begin(), out.end(), key_less);  // k is still 0: ties keep list order
         for (size_t i = 1; i < out.size(); ++i)
           if (out[i].w == out[i - 1].w && out[i].lq == out[i - 1].lq) out[i].k = out[i - 1].k + 1;
       };
+      // merge the m lists li[0 .. m) by key; emit(qph, rb, item or nullptr per list)
+      std::vector<Item> li[kGroup];
+      auto merge = [&](int m, auto&& emit) {
+        size_t at[kGroup] = {};
+        for (;;) {
+          int first = -1;
+          for (int i = 0; i < m; ++i)
+            if (at[i] < li[i].size() && (first < 0 || key_less(li[i][at[i]], li[first][at[first]]))) first = i;
+          if (first < 0) break;
+          const Item head = li[first][at[first]];
+          const Item* x[kGroup] = {};
+          for (int i = 0; i < m; ++i)
+            if (at[i] < li[i].size() && !key_less(head, li[i][at[i]])) x[i] = &li[i][at[i]++];
+          const int32_t nr = P->page_nrows[head.qph];
+          for (int32_t rb = 0; rb < (nr > 32 ? 2 : 1); ++rb) emit(head.qph, rb, x);
+        }
+      };
+      P->kgroups.clear();
+      P->kgroup_off.assign(1, 0);
+      P->kgsteps.clear();
       P->kpairs.clear();
       P->kpair_off.assign(1, 0);
       P->kpsteps.clear();
-      std::vector<Item> la, lb;
       for (int32_t u = 0; u < n; ++u) {
         if (P->length[u] == 0) continue;
-        for (int32_t lp = 0; lp < P->npages[u]; lp += 2) {
-          const int32_t pa = P->page_table[P->slot0[u] + lp];
-          const int32_t pb = lp + 1 < P->npages[u] ? P->page_table[P->slot0[u] + lp + 1] : -1;
-          items_of(pa, u, la);
-          if (pb >= 0) items_of(pb, u, lb); else lb.clear();
-          size_t ia = 0, ib = 0;
-          while (ia < la.size() || ib < lb.size()) {
-            int32_t qph, infa = 0, infb = 0;
-            if (ib == lb.size() || (ia < la.size() && key_less(la[ia], lb[ib]))) {
-              qph = la[ia].qph, infa = la[ia++].info;
-            } else if (ia == la.size() || key_less(lb[ib], la[ia])) {
-              qph = lb[ib].qph, infb = lb[ib++].info;
-            } else {
-              qph = la[ia].qph, infa = la[ia++].info, infb = lb[ib++].info;
-            }
-            const int32_t nr = P->page_nrows[qph];
-            for (int32_t rb = 0; rb < (nr > 32 ? 2 : 1); ++rb)
-              P->kpsteps.push_back(KStep{qph, (int32_t)((uint32_t)(rb | infa) | ((uint32_t)infb << 16))});
-          }
+        const int32_t np = P->npages[u];
+        if (in_pair(u)) {
+          const int32_t pa = P->page_table[P->slot0[u]];
+          const int32_t pb = np == 2 ? P->page_table[P->slot0[u] + 1] : -1;
+          items_of(pa, u, li[0]);
+          if (pb >= 0) items_of(pb, u, li[1]); else li[1].clear();
+          merge(2, [&](int32_t qph, int32_t rb, const Item* const* x) {
+            uint32_t info = (uint32_t)rb;
+            for (int i = 0; i < 2; ++i)
+              if (x[i])
+                info |= ((uint32_t)(x[i]->lo << 1) | (uint32_t)(x[i]->hi << 8) | (uint32_t)(x[i]->diag << 15))
+                        << (16 * i);
+            P->kpsteps.push_back(KStep{qph, (int32_t)info});
+          });
           P->kpairs.push_back(pa);
           P->kpairs.push_back(pb);
           P->kpair_off.push_back((int64_t)P->kpsteps.size());
+          continue;
+        }
+        for (int32_t lp = 0; lp < np; lp += kGroup) {
+          for (int i = 0; i < kGroup; ++i) {
+            const int32_t ph = lp + i < np ? P->page_table[P->slot0[u] + lp + i] : -1;
+            P->kgroups.push_back(ph);
+            if (ph >= 0) items_of(ph, u, li[i]); else li[i].clear();
+          }
+          merge(kGroup, [&](int32_t qph, int32_t rb, const Item* const* x) {
+            GStep st{qph, rb, {0u, 0u}};
+            for (int i = 0; i < kGroup; ++i)
+              if (x[i]) st.vis[i >> 1] |= gvis(x[i]->lo, x[i]->hi, x[i]->diag) << (16 * (i & 1));
+            P->kgsteps.push_back(st);
+          });
+          P->kgroup_off.push_back((int64_t)P->kgsteps.size());
         }
       }
     }
@@ -443,16 +481,27 @@ dag_status build_plan(const dag_node* nodes, int32_t n, const dag_mount* mounts,
       for (int32_t u : nodes_by)
         if (P->length[u] > 0)
           for (int32_t lp = 0; lp < P->npages[u]; ++lp) P->bwd_order.push_back(P->page_table[P->slot0[u] + lp]);
-      // pairs in the same node order (a node's pairs are consecutive in kpairs)
-      std::vector<int32_t> pair0(n + 1, 0);
-      for (int32_t u = 0, c = 0; u < n; ++u) {
-        pair0[u] = c;
-        if (P->length[u] > 0) c += (P->npages[u] + 1) / 2;
-        pair0[u + 1] = c;
+      // groups and pairs in the same node order (a node's groups are consecutive in
+      // kgroups; a node of one or two pages has one pair instead)
+      std::vector<int32_t> group0(n + 1, 0), pair0(n + 1, 0);
+      for (int32_t u = 0, cg = 0, cp = 0; u < n; ++u) {
+        group0[u] = cg;
+        pair0[u] = cp;
+        if (P->length[u] > 0) {
+          if (in_pair(u))
+            ++cp;
+          else
+            cg += (P->npages[u] + kGroup - 1) / kGroup;
+        }
+        group0[u + 1] = cg;
+        pair0[u + 1] = cp;
       }
+      P->group_order.clear();
       P->pair_order.clear();
-      for (int32_t u : nodes_by)
+      for (int32_t u : nodes_by) {
+        for (int32_t i = group0[u]; i < group0[u + 1]; ++i) P->group_order.push_back(i);
         for (int32_t i = pair0[u]; i < pair0[u + 1]; ++i) P->pair_order.push_back(i);
+      }
     }
   }
 

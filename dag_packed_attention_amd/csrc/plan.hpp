@@ -42,8 +42,8 @@ struct KEntry {
   int32_t lohi_diag;  // lo | (hi << 8) | (diag << 16)
 };
 
-// One 32-row step of a KV page pair's merged reader list, as the dK/dV kernel walks
-// it: rows 32 rb .. 32 rb + 31 of physical query page qph see rows [loA, hiA) of
+// One 32-row step of a KV page pair's merged reader list (a node of one or two pages, or
+// consecutive pages of a packed plan), as the pair dK/dV kernel walks it: rows 32 rb .. 32 rb + 31 of physical query page qph see rows [loA, hiA) of
 // page A and [loB, hiB) of page B (an empty range: that page is not read by this
 // step; diag: the page's own query block, masked causally).  Packed so a kernel
 // fetches a step with one 8-byte load.
@@ -57,6 +57,25 @@ struct KStep {
 struct KMask {
   int32_t a, b;
 };
+
+// One 32-row step of a group of up to four KV pages (pages 4 i .. 4 i + 3 of one node),
+// as the four-page dK/dV kernel walks it: rows 32 rb .. 32 rb + 31
+// of physical query page qph see rows [lo, hi) of each page of the group (empty: not
+// read by this step; diag: the page's own query block, masked causally).  Page i's 16
+// bits sit in vis[i / 2] >> (16 (i % 2)) as lo | hi << 7 | diag << 14; 16 bytes, one load.
+constexpr int kGroup = 4;
+struct GStep {
+  int32_t qph;
+  int32_t rb;
+  uint32_t vis[2];
+};
+inline constexpr uint32_t gvis(int lo, int hi, int diag) {
+  return (uint32_t)lo | ((uint32_t)hi << 7) | ((uint32_t)diag << 14);
+}
+inline constexpr uint32_t gvis_of(const GStep& s, int i) { return (s.vis[i >> 1] >> (16 * (i & 1))) & 0xffffu; }
+inline constexpr int gvis_lo(uint32_t v) { return (int)(v & 0x7f); }
+inline constexpr int gvis_hi(uint32_t v) { return (int)((v >> 7) & 0x7f); }
+inline constexpr int gvis_diag(uint32_t v) { return (int)((v >> 14) & 1); }
 
 // A token within 3 steps after a page's last token on some path, with the rows
 // 1, 2 and 3 steps before it on its own path (-1: none); the short convolution's
@@ -109,6 +128,13 @@ struct Plan {
   std::vector<int32_t> kv_off;                 // physical page -> first reader entry (size pages+1)
   std::vector<KEntry> kentries;
   std::vector<int32_t> bwd_order;              // physical pages with rows, heaviest first
+  // dK/dV work: with one node per page, each node's pages in groups of four (its last
+  // group may hold fewer), or, when nodes of one or two pages hold most pages, those as
+  // pairs; a packed plan's pages in pairs of consecutive pages
+  std::vector<int32_t> kgroups;                // kGroup pages per group (-1: none)
+  std::vector<int64_t> kgroup_off;             // group -> its first merged reader step (size groups+1)
+  std::vector<GStep> kgsteps;                  // merged reader steps of every group
+  std::vector<int32_t> group_order;            // group ids, node-grouped, heaviest first
   std::vector<int32_t> kpairs;                 // KV page pairs (A, B; B = -1 for a lone page)
   std::vector<int64_t> kpair_off;              // pair -> its first merged reader step (size pairs+1)
   std::vector<KStep> kpsteps;                  // merged reader steps of every pair

@@ -188,8 +188,8 @@ dag_status dag_plan_multiplicity(const dag_plan* plan, int32_t* mult);
  * from the plan tables against the plan's sizes, record the first failure and go on
  * with a safe in-bounds value, and dag_attn_fwd / dag_attn_bwd then wait for the stream
  * and return DAG_E_INVALID naming the check (codes: 1 query page, 2 tile range, 3 tile
- * page, 4 interval, 5 mask id, 6 page pair, 7 step range, 8 step page).  Results of a
- * passing call are bitwise those of the release build.
+ * page, 4 interval, 5 mask id, 6 page pair, 7 step range, 8 step page, 9 page group).
+ * Results of a passing call are bitwise those of the release build.
  * dag_debug_build: 1 in the debug build, 0 otherwise. */
 int32_t dag_debug_build(void);
 /* Debug build only (DAG_E_UNSUPPORTED otherwise): page ids >= max_pages fail the checks

@@ -40,12 +40,6 @@ static int check(const Plan& P) {
       const int lo = k.lohi_diag & 0xff, hi = (k.lohi_diag >> 8) & 0xff;
       if (lo >= hi || hi > P.page_nrows[ph]) return 7;
     }
-  // KV page pairs: two consecutive pages of one node (or one lone last page); each
-  // pair's merged steps, projected on each of its pages (steps with a non-empty range
-  // for it), are exactly that page's reader entries unrolled into 32-row steps
-  const int64_t npairs = (int64_t)P.kpairs.size() / 2;
-  if ((int64_t)P.kpair_off.size() != npairs + 1 || P.kpair_off[0] != 0) return 8;
-  if ((int64_t)P.kpsteps.size() != P.kpair_off[npairs]) return 13;
   std::vector<int> seen(pages, 0);
   std::vector<int> node_of_page(pages, -1), slot_of_page(pages, -1);
   for (int u = 0; u < P.n_nodes; ++u)
@@ -53,6 +47,91 @@ static int check(const Plan& P) {
       node_of_page[P.page_table[P.slot0[u] + lp]] = u;
       slot_of_page[P.page_table[P.slot0[u] + lp]] = lp;
     }
+  // one node per page: groups of a node's pages 4 i .. 4 i + 3 (the last may hold fewer);
+  // each group's merged steps, projected on each of its pages, are exactly that page's
+  // reader entries unrolled into 32-row steps, and the node's own query pages come last,
+  // latest first.  Packed plans have no groups.
+  const int64_t ngroups = (int64_t)P.kgroups.size() / kGroup;
+  if ((int64_t)P.kgroups.size() != ngroups * kGroup) return 70;
+  if ((int64_t)P.kgroup_off.size() != ngroups + 1 || P.kgroup_off[0] != 0) return 70;
+  if ((int64_t)P.kgsteps.size() != P.kgroup_off[ngroups]) return 71;
+  if ((int64_t)P.group_order.size() != ngroups) return 72;
+  if (P.packed && ngroups) return 73;
+  {
+    std::vector<int> cnt(ngroups, 0);
+    for (int32_t gr : P.group_order)
+      if (gr < 0 || gr >= ngroups || cnt[gr]++) return 72;
+  }
+  for (int64_t gr = 0; gr < ngroups; ++gr) {
+    if (P.kgroup_off[gr + 1] <= P.kgroup_off[gr]) return 74;
+    const int ph0 = P.kgroups[kGroup * gr];
+    if (ph0 < 0 || ph0 >= pages || slot_of_page[ph0] % kGroup) return 75;
+    const int u = node_of_page[ph0];
+    int npg = 0;
+    for (int side = 0; side < kGroup; ++side) {
+      const int ph = P.kgroups[kGroup * gr + side];
+      if (ph < 0) {
+        for (int64_t i = P.kgroup_off[gr]; i < P.kgroup_off[gr + 1]; ++i)
+          if (gvis_of(P.kgsteps[i], side)) return 76;  // a missing page is never read
+        continue;
+      }
+      ++npg;
+      if (ph >= pages || seen[ph]++ || npg != side + 1) return 75;  // missing pages last
+      if (node_of_page[ph] != u || slot_of_page[ph] != slot_of_page[ph0] + side) return 75;
+      std::vector<std::array<int, 5>> want, got;  // qph, rb, lo, hi, diag
+      for (int e = P.kv_off[ph]; e < P.kv_off[ph + 1]; ++e) {
+        const KEntry& k = P.kentries[e];
+        for (int lq = k.lq0; lq < k.lq1; ++lq) {
+          const int qph = P.page_table[k.slot_base + lq];
+          for (int rb = 0; rb * 32 < P.page_nrows[qph]; ++rb)
+            want.push_back({qph, rb, k.lohi_diag & 0xff, (k.lohi_diag >> 8) & 0xff, (k.lohi_diag >> 16) & 1});
+        }
+      }
+      for (int64_t i = P.kgroup_off[gr]; i < P.kgroup_off[gr + 1]; ++i) {
+        const GStep& st = P.kgsteps[i];
+        if (st.qph < 0 || st.qph >= pages || (st.rb != 0 && st.rb != 1) || st.rb * 32 >= P.page_nrows[st.qph])
+          return 77;
+        const uint32_t v = gvis_of(st, side);
+        if (gvis_lo(v) == gvis_hi(v)) {
+          if (v) return 78;  // an empty range carries no other bits
+          continue;
+        }
+        got.push_back({st.qph, st.rb, gvis_lo(v), gvis_hi(v), gvis_diag(v)});
+      }
+      std::sort(want.begin(), want.end());
+      std::sort(got.begin(), got.end());
+      if (want != got) return 79;
+    }
+    // four pages, or the node's last ones
+    if (npg != kGroup && slot_of_page[ph0] + npg != P.npages[u]) return 80;
+    for (int64_t i = P.kgroup_off[gr]; i < P.kgroup_off[gr + 1]; ++i)
+      if (!P.kgsteps[i].vis[0] && !P.kgsteps[i].vis[1]) return 81;  // every step reads a page
+    bool in_own = false;
+    int prev_slot = 1 << 30;
+    for (int64_t i = P.kgroup_off[gr]; i < P.kgroup_off[gr + 1]; ++i) {
+      const int qph = P.kgsteps[i].qph;
+      if (node_of_page[qph] == u) {
+        in_own = true;
+        if (slot_of_page[qph] > prev_slot) return 82;
+        prev_slot = slot_of_page[qph];
+      } else if (in_own) {
+        return 82;
+      }
+    }
+  }
+  // KV page pairs: a node of one or two pages (packed plans: consecutive pages), or one
+  // lone page; each pair's merged steps, projected on each of its pages, are exactly that
+  // page's reader entries unrolled into 32-row steps
+  const int64_t npairs = (int64_t)P.kpairs.size() / 2;
+  if ((int64_t)P.kpair_off.size() != npairs + 1 || P.kpair_off[0] != 0) return 8;
+  if ((int64_t)P.kpsteps.size() != P.kpair_off[npairs]) return 13;
+  for (int64_t pr = 0; pr < npairs && !P.packed; ++pr) {
+    const int pa = P.kpairs[2 * pr];
+    if (pa < 0 || pa >= pages || slot_of_page[pa] != 0 || P.npages[node_of_page[pa]] > 2) return 83;
+  }
+  if (npairs && !P.packed)  // pairs only when small nodes hold most pages, and then all of them
+    for (int64_t gr = 0; gr < ngroups; ++gr)
+      if (P.npages[node_of_page[P.kgroups[kGroup * gr]]] < 3) return 84;
   for (int64_t pr = 0; pr < npairs; ++pr) {
     for (int side = 0; side < 2; ++side) {
       const int ph = P.kpairs[2 * pr + side];
@@ -102,7 +181,7 @@ static int check(const Plan& P) {
     }
   }
   for (int64_t ph = 0; ph < pages; ++ph)
-    if (!seen[ph] && P.page_nrows[ph] > 0) return 12;  // every page with rows is in a pair
+    if (!seen[ph] && P.page_nrows[ph] > 0) return 12;  // every page with rows is in a group or a pair
   if ((int64_t)P.pair_order.size() != npairs) return 15;
   if (P.packed) {
     // masks: one id per tile / step side, in range; the key-major half is the transpose of
