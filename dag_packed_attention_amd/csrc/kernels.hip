@@ -1417,10 +1417,10 @@ __global__ __launch_bounds__(512, 1) void dkdv_group_kernel(
   const GStep* kst = gsteps + s_begin;
   GStep cur = dbg_gstep(kst[0]);
   GStep nxt = dbg_gstep(kst[min(1, n_steps - 1)]);
-  // staging by waves 0..3 (one per SIMD): head sj of the half-step, tensor ts (0: Q,
-  // 1: dO), all eight bricks
-  const bool stager = wave < 4;
-  const int sj = wave & 1, ts = (wave >> 1) & 1;
+  // staging by all eight waves (measured faster than by four or two here, where every
+  // wave runs two heads per half-step): head sj of the half-step, tensor ts (0: Q,
+  // 1: dO), bricks sb0 .. sb0 + 3
+  const int sj = wave & 1, ts = (wave >> 1) & 1, sb0 = 4 * (wave >> 2);
   const uint32_t rlo = brick_lane_off(lane);
   const uint32_t llo = (uint32_t)((2 * (lane & 31) + (lane >> 5)) * 4);
   const f16_t* stsrc = ts == 0 ? qn : dOn;
@@ -1429,10 +1429,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_group_kernel(
   };
   {
     const int64_t r0 = head_row0(cur, 0, sj);
-    if (stager) {
-      stage_bricks<8>(qd[0][sj][ts], tile_rsrc(stsrc + r0 * kD, 32 * kD * 2), 0, rlo);
-      if (ts == 0) dma4(&lds_ld[0][sj][0], llo, tile_rsrc(ldd + r0, 256), 0);
-    }
+    stage_bricks<4>(qd[0][sj][ts], tile_rsrc(stsrc + r0 * kD, 32 * kD * 2), sb0, rlo);
+    if (ts == 0 && sb0 == 0) dma4(&lds_ld[0][sj][0], llo, tile_rsrc(ldd + r0, 256), 0);
   }
   wait_all_loads();
   __syncthreads();
@@ -1448,17 +1446,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_group_kernel(
     const int64_t nr0 = head_row0(sd, hp ^ 1, sj);
     const i32x4 nrs = tile_rsrc(stsrc + nr0 * kD, 32 * kD * 2);
     f16_t* ndst = qd[buf ^ 1][sj][ts];
-    const bool offs = stager && ts == 0;
+    const bool offs = ts == 0 && sb0 == 0;
 
     const uint32_t inf = gvis_of(cur, ps);
     const int lo = gvis_lo(inf), hi_t = gvis_hi(inf);
     const bool diag = gvis_diag(inf);
     if (!active || lo >= hi_t) {
       // this wave's page is not read by this step: stage only
-      if (stager) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) dma16(ndst + i * kBrick, rlo, nrs, i * 4 * kD * 2);
-      }
+      for (int i = 0; i < 4; ++i) dma16(ndst + (sb0 + i) * kBrick, rlo, nrs, (sb0 + i) * 4 * kD * 2);
       if (offs) dma4(&lds_ld[buf ^ 1][sj][0], llo, tile_rsrc(ldd + nr0, 256), 0);
     } else {
       // A key outside the step's visible range gets -inf added before the exponential.
@@ -1487,14 +1483,15 @@ __global__ __launch_bounds__(512, 1) void dkdv_group_kernel(
         // between the dP products, dS = P (dP - D) between the dV products.
         {
           // S: Q fragments read one k-step ahead; with the first head, the next unit's
-          // staging goes out one load per k-step (waves 0..3)
+          // staging goes out one load per two k-steps
           f16x8 qa[2];
           qa[0] = ld8(Qt + qb);
 #pragma unroll
           for (int ks = 0; ks < 8; ++ks) {
             if (ks < 7) qa[(ks + 1) & 1] = ld8(Qt + qb + kstep(ks + 1));
             s = mfma(qa[ks & 1], kf[ks], s);
-            if (jj == 0 && stager) dma16(ndst + ks * kBrick, rlo, nrs, ks * 4 * kD * 2);
+            if (jj == 0 && (ks & 1) == 0)
+              dma16(ndst + (sb0 + ks / 2) * kBrick, rlo, nrs, (sb0 + ks / 2) * 4 * kD * 2);
           }
           if (jj == 0 && offs) dma4(&lds_ld[buf ^ 1][sj][0], llo, tile_rsrc(ldd + nr0, 256), 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
