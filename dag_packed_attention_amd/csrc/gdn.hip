@@ -65,6 +65,14 @@ __device__ __forceinline__ bf16_t f2bf(float x) {
 template <typename T> __device__ __forceinline__ void st_g(T* p, float x);
 template <> __device__ __forceinline__ void st_g<float>(float* p, float x) { *p = x; }
 template <> __device__ __forceinline__ void st_g<bf16_t>(bf16_t* p, float x) { *p = f2bf(x); }
+// Two consecutive elements (p even-aligned).
+template <typename T> __device__ __forceinline__ void st2_g(T* p, float x0, float x1);
+template <> __device__ __forceinline__ void st2_g<float>(float* p, float x0, float x1) {
+  *reinterpret_cast<float2*>(p) = make_float2(x0, x1);
+}
+template <> __device__ __forceinline__ void st2_g<bf16_t>(bf16_t* p, float x0, float x1) {
+  *reinterpret_cast<uint32_t*>(p) = (uint32_t)f2bf(x0) | ((uint32_t)f2bf(x1) << 16);
+}
 
 __device__ __forceinline__ f32x16 mfma(const f16x8& a, const f16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
@@ -77,6 +85,25 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 // Row of element r of a 32x32 accumulator in lane half `hi` (column = lane % 32).
 __device__ __forceinline__ int acc_row(int r, int hi) { return 8 * (r >> 2) + 4 * hi + (r & 3); }
+
+// Global stores of a 32 x 32 accumulator block two columns per lane: the lanes of each
+// even/odd pair (columns c, c + 1) trade one value of every row pair (2 i, 2 i + 1) with a
+// DPP swap, so the even lane holds row 2 i and the odd lane row 2 i + 1, each at both
+// columns; put(t, x0, x1) stores row t's pair at the pair's even column.  Half the store
+// instructions of one element per lane.
+__device__ __forceinline__ float swap_adjacent_lanes(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+}
+template <typename F>
+__device__ __forceinline__ void put_pairs(const f32x16& a, int row0, int lane, F&& put) {
+  const int odd = lane & 1, hi = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float got = swap_adjacent_lanes(odd ? a[2 * i] : a[2 * i + 1]);
+    const float x0 = odd ? got : a[2 * i], x1 = odd ? a[2 * i + 1] : got;
+    put(row0 + 8 * (i >> 1) + 4 * hi + 2 * (i & 1) + odd, x0, x1);  // acc_row(2 i + odd, hi)
+  }
+}
 
 // MFMA operand with the contraction index contiguous: rows mn0 + lane % 32 of
 // X[.][ld], elements k0 + 8 (lane / 32) .. + 7.
@@ -723,12 +750,10 @@ __global__ __launch_bounds__(512, 1) void gdn_fwd_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         acc_o = mfma(frag_n(Pr, LDP, 32 * rb, 16 * s, lane), frag_t(Ur, LDK, 16 * s, 32 * cb, lane), acc_o);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * rb + acc_row(r, hi);
+      put_pairs(acc_o, 32 * rb, lane, [&](int t, float x0, float x1) {
         const int j = j0 + t;
-        if (j >= sq.n_replay && j < sq.n_tok) o[((int64_t)rw[t] * H + head) * kD + cc] = f2bf(acc_o[r]);
-      }
+        if (j >= sq.n_replay && j < sq.n_tok) st2_g<bf16_t>(o + ((int64_t)rw[t] * H + head) * kD + (cc & ~1), x0, x1);
+      });
     }
     __syncthreads();  // T and P of this chunk are read: the next chunk's replace them
     commit_tinv8(tx, Th, Tl, Pr, tid);
@@ -958,6 +983,18 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
   const int j0 = c * kB;
   const ChunkIn ci{grows + sq.tok_off, sq.n_tok, sq.n_replay};
   f16_t* Kk = Th;
+  const int cc = 32 * cb + l32;
+  // The start state's fragments go out first, beside the chunk's rows: S0 (for K S0^T)
+  // and its transposed copy (contraction over dv: dk rows 32 cb .., read once for
+  // <dS, S0>, dQ and dK).  Neither depends on the rows, so their latency overlaps.
+  const f16_t* S0n = states + ((int64_t)(sq.chunk_off + c) * H + head) * 2 * kD * kD;
+  const f16_t* S0t = S0n + kD * kD;
+  f16x8 s0f[8], s0n[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    s0n[s] = frag_g(S0n, 32 * cb, 16 * s, lane);
+    s0f[s] = frag_g(S0t, 32 * cb, 16 * s, lane);
+  }
 
   if (tid < 256) {
     BwdRegs nx;
@@ -1004,15 +1041,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     gam[tid] = __expf(gs[tid]);
     egam[tid] = __expf(gs[kB - 1] - gs[tid]);
   }
-  const f16_t* S0n = states + ((int64_t)(sq.chunk_off + c) * H + head) * 2 * kD * kD;
-  const f16_t* S0t = S0n + kD * kD;
   const float g63 = gs[kB - 1];
-  const int cc = 32 * cb + l32;
-  // S0 fragments with the contraction over dv: dk rows 32 cb .. of the transposed copy,
-  // read once for <dS, S0>, dQ and dK
-  f16x8 s0f[8];
-#pragma unroll
-  for (int s = 0; s < 8; ++s) s0f[s] = frag_g(S0t, 32 * cb, 16 * s, lane);
   __syncthreads();
 
   // -- R = diag(beta) (V - diag(gamma) K S0^T) (fp16), then U = T R --------------------------
@@ -1020,7 +1049,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
   {
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      ks = mfma(frag_n(Kr, LDK, 32 * rb, 16 * s, lane), frag_g(S0n, 32 * cb, 16 * s, lane), ks);
+      ks = mfma(frag_n(Kr, LDK, 32 * rb, 16 * s, lane), s0n[s], ks);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * rb + acc_row(r, hi);
@@ -1069,16 +1098,15 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     }
     __syncthreads();  // every wave has read dU and T
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * rb + acc_row(r, hi);
-      dRr[t * LDK + cc] = (f16_t)dr[r];
+    for (int r = 0; r < 16; ++r) dRr[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)dr[r];
+    put_pairs(dr, 32 * rb, lane, [&](int t, float x0, float x1) {
       const int kind = dst_kind[t];
-      const int64_t off = dst_off[t];
-      const float g = bs[t] * dr[r];
-      if (kind == 1) rbuf[off + kD + cc] = g;
-      else if (kind == 2) rside[off + kD + cc] = g;
-      else if (kind == 3) st_g<TG>(dv + off + cc, g);
-    }
+      const int64_t off = dst_off[t] + kD + (cc & ~1);
+      const float b = bs[t];
+      if (kind == 1) st2_g<float>(rbuf + off, b * x0, b * x1);
+      else if (kind == 2) st2_g<float>(rside + off, b * x0, b * x1);
+      else if (kind == 3) st2_g<TG>(dv + off - kD, b * x0, b * x1);
+    });
   }
   __syncthreads();
 
@@ -1199,12 +1227,10 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       aq = mfma(frag_n(Pr, LDP, 32 * rb, 16 * s, lane), frag_t(Kr, LDK, 16 * s, 32 * cb, lane), aq);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * rb + acc_row(r, hi);
+    put_pairs(aq, 32 * rb, lane, [&](int t, float x0, float x1) {
       const int j = j0 + t;
-      if (j >= sq.n_replay && j < sq.n_tok) st_g<TG>(dq + ((int64_t)rw[t] * H + head) * kD + cc, aq[r]);
-    }
+      if (j >= sq.n_replay && j < sq.n_tok) st2_g<TG>(dq + ((int64_t)rw[t] * H + head) * kD + (cc & ~1), x0, x1);
+    });
   }
   // -- dK = dP~^T Q + dKk K + dKk^T K + diag(E_63,.) U dS - diag(beta gamma) dR S0 -----------
   {
@@ -1242,15 +1268,13 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
         ak[r] = fmaf(-bs[t] * gam[t], rs0[r], ak[r]);
       }
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * rb + acc_row(r, hi);
+    put_pairs(ak, 32 * rb, lane, [&](int t, float x0, float x1) {
       const int kind = dst_kind[t];
-      const int64_t off = dst_off[t];
-      if (kind == 1) rbuf[off + cc] = ak[r];
-      else if (kind == 2) rside[off + cc] = ak[r];
-      else if (kind == 3) st_g<TG>(dk + off + cc, ak[r]);
-    }
+      const int64_t off = dst_off[t] + (cc & ~1);
+      if (kind == 1) st2_g<float>(rbuf + off, x0, x1);
+      else if (kind == 2) st2_g<float>(rside + off, x0, x1);
+      else if (kind == 3) st2_g<TG>(dk + off, x0, x1);
+    });
   }
   __syncthreads();
 

@@ -1320,12 +1320,14 @@ __device__ __forceinline__ void dkdv_store_half(const f32x16 (&acc)[4], float* r
   __syncthreads();
   for (int idx = tid; idx < 128 * 64; idx += 512) {
     const int k2 = idx / 64, i = idx % 64;  // key of the two pages, column pair (i, i + 64)
-    const int slot = 2 * hf + (k2 >> 6), row = k2 & 63;
-    const int page = phys[slot];
+    const bool second = k2 >= 64;
+    const int row = k2 & 63;
+    // selects rather than an index: an indexed private array would live in LDS
+    const int page = second ? phys[2 * hf + 1] : phys[2 * hf];
     if (page < 0) continue;
     const int64_t grow = (int64_t)page * 64 + row;
     float a = red[k2 * (kD + 1) + i] * mul, b = red[k2 * (kD + 1) + i + 64] * mul;
-    if (row >= nrows[slot]) {
+    if (row >= (second ? nrows[2 * hf + 1] : nrows[2 * hf])) {
       a = b = 0.f;
     } else if (kRotate && cs) {
       const float2 c = cs[grow * (kD / 2) + i];
@@ -1383,7 +1385,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_group_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;  // wave index: uniform
   const int l32 = lane & 31, hi = lane >> 5;
   const int ps = wave >> 1, kb = wave & 1;  // page slot of the group, key half of the page
-  const int page = phys[ps];
+  // uniform selects rather than an index (an indexed private array would live in LDS)
+  const int page = ps == 0 ? phys[0] : ps == 1 ? phys[1] : ps == 2 ? phys[2] : phys[3];
   const bool active = page >= 0;  // a group with fewer pages: this wave only stages
 
   f16x8 kf[8];
@@ -1448,7 +1451,8 @@ __global__ __launch_bounds__(512, 1) void dkdv_group_kernel(
     f16_t* ndst = qd[buf ^ 1][sj][ts];
     const bool offs = ts == 0 && sb0 == 0;
 
-    const uint32_t inf = gvis_of(cur, ps);
+    const uint32_t vw = (ps & 2) ? cur.vis[1] : cur.vis[0];  // uniform select, see above
+    const uint32_t inf = ((ps & 1) ? vw >> 16 : vw) & 0xffffu;
     const int lo = gvis_lo(inf), hi_t = gvis_hi(inf);
     const bool diag = gvis_diag(inf);
     if (!active || lo >= hi_t) {
@@ -1528,9 +1532,11 @@ __global__ __launch_bounds__(512, 1) void dkdv_group_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
         if (diag) {
-          // the reader's own page: key <= row (a hidden score may have overflowed: select)
+          // the reader's own page: key <= row (a hidden score may have overflowed: select);
+          // compared as key - row0 <= acc_row(r, 0), a constant per element
+          const int t = key - cur.rb * 32 - 4 * hi;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[r] = key <= cur.rb * 32 + acc_row(r, hi) ? s[r] : 0.f;
+          for (int r = 0; r < 16; ++r) s[r] = t <= acc_row(r, 0) ? s[r] : 0.f;
         }
         // Padding rows need no mask: their Q and dO rows and offsets are zero, so they add
         // exact zeros to dV and dK.
