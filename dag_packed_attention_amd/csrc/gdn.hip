@@ -150,41 +150,57 @@ __device__ __forceinline__ f16x8 bf8_to_h8(uint4 u) {
   return o;
 }
 
-// Sum of the 16 accumulator values of each row over the 32 lanes of one lane
-// half, in a fixed butterfly order: afterwards lane 2 r (and 2 r + 1) of the
-// half holds the sum for element r (row acc_row(r, hi)).
+// Lane exchanges inside rows of 16 lanes (DPP): the value of lane i ^ 1, of lane i ^ 2,
+// and of the lanes 4 and 8 places away in the lane's row.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float from_xor1(float x) { return dpp_mov<0xB1>(x); }  // quad_perm 1,0,3,2
+__device__ __forceinline__ float from_xor2(float x) { return dpp_mov<0x4E>(x); }  // quad_perm 2,3,0,1
+__device__ __forceinline__ float from_ror4(float x) { return dpp_mov<0x124>(x); }  // row_ror 4
+__device__ __forceinline__ float from_ror8(float x) { return dpp_mov<0x128>(x); }  // row_ror 8 (lane i ^ 8)
+
+// Sum of the 16 accumulator values of each row over the 32 lanes of one lane half, in a
+// fixed order: four halving steps inside each row of 16 lanes, the lane keeping the half
+// of its values that one bit of its index selects and adding the partner's partial sums
+// of that half (partners: lane ^ 1, lane ^ 2, then the lanes 4 and 8 places away in the
+// row, which differ in bits 2 and 3 and agree in the bits already used), then the sum of
+// the half's two rows.  Afterwards lanes l and l ^ 16 hold the sum for element
+// rowsum16_elem(l) (row acc_row(., hi)); rowsum16_writer(l) picks one of the two.
 __device__ __forceinline__ float rowsum16(const float (&x)[16], int lane) {
   float a8[8], a4[4], a2[2], a1;
-  const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+  const bool b0 = lane & 1, b1 = lane & 2, b2 = lane & 4, b3 = lane & 8;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float send = b4 ? x[j] : x[8 + j];
-    const float keep = b4 ? x[8 + j] : x[j];
-    a8[j] = keep + __shfl_xor(send, 16);
+    const float send = b0 ? x[j] : x[8 + j];
+    const float keep = b0 ? x[8 + j] : x[j];
+    a8[j] = keep + from_xor1(send);
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float send = b3 ? a8[j] : a8[4 + j];
-    const float keep = b3 ? a8[4 + j] : a8[j];
-    a4[j] = keep + __shfl_xor(send, 8);
+    const float send = b1 ? a8[j] : a8[4 + j];
+    const float keep = b1 ? a8[4 + j] : a8[j];
+    a4[j] = keep + from_xor2(send);
   }
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const float send = b2 ? a4[j] : a4[2 + j];
     const float keep = b2 ? a4[2 + j] : a4[j];
-    a2[j] = keep + __shfl_xor(send, 4);
+    a2[j] = keep + from_ror4(send);
   }
   {
-    const float send = b1 ? a2[0] : a2[1];
-    const float keep = b1 ? a2[1] : a2[0];
-    a1 = keep + __shfl_xor(send, 2);
+    const float send = b3 ? a2[0] : a2[1];
+    const float keep = b3 ? a2[1] : a2[0];
+    a1 = keep + from_ror8(send);
   }
-  return a1 + __shfl_xor(a1, 1);
+  return a1 + __shfl_xor(a1, 16);
 }
 // Element index of the row whose sum rowsum16 leaves in this lane.
 __device__ __forceinline__ int rowsum16_elem(int lane) {
-  return 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 1) & 1);
+  return 8 * (lane & 1) + 4 * ((lane >> 1) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 3) & 1);
 }
+__device__ __forceinline__ bool rowsum16_writer(int lane) { return !(lane & 16); }
 // Sum over the 32 rows of one accumulator column (both lane halves).
 __device__ __forceinline__ float colsum16(const float (&x)[16]) {
   float s = 0.f;
@@ -1122,7 +1138,11 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
         s += (float)dSh[d * LDK + cc] * (float)(rb ? s0f[4 + sb][j] : s0f[sb][j]);
       }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) s += __shfl_xor(s, off);
+    for (int off = 32; off >= 16; off >>= 1) s += __shfl_xor(s, off);
+    s += from_xor1(s);
+    s += from_xor2(s);
+    s += from_ror4(s);
+    s += from_ror8(s);  // every lane: the sum over the row's 16 lanes of the cross-row sums
     if (lane == 0) red_s[wave] = s;
   }
   // -- dP = dO U^T, dA = -dR U^T on block (bm, bn), waves 0..3 ---------------------------------
@@ -1157,7 +1177,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     const float rs = rowsum16(xy, lane);
     const float rz = rowsum16(z, lane);
     const float cs = colsum16(xy);
-    if (!(lane & 1)) {
+    if (rowsum16_writer(lane)) {
       const int t = 32 * bm + acc_row(rowsum16_elem(lane), hi);
       red_dg[wave][t] += rs;
       red_b[wave][t] += rz;
@@ -1200,7 +1220,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     }
     const float sb = rowsum16(xb, lane);
     const float sg = rowsum16(xg, lane);
-    if (!(lane & 1)) {
+    if (rowsum16_writer(lane)) {
       const int t = 32 * rb + acc_row(rowsum16_elem(lane), hi);
       red_b[wave][t] += sb;
       red_g[wave][t] += sg;
@@ -1222,7 +1242,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
         aq[r] *= scale * gam[t];
       }
       const float sg = rowsum16(xg, lane);
-      if (!(lane & 1)) red_g[wave][32 * rb + acc_row(rowsum16_elem(lane), hi)] += sg;
+      if (rowsum16_writer(lane)) red_g[wave][32 * rb + acc_row(rowsum16_elem(lane), hi)] += sg;
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -1256,7 +1276,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
         ak[r] = fmaf(egam[t], ud[r], ak[r]);
       }
       const float se = rowsum16(xe, lane);
-      if (!(lane & 1)) red_e[wave][32 * rb + acc_row(rowsum16_elem(lane), hi)] += se;
+      if (rowsum16_writer(lane)) red_e[wave][32 * rb + acc_row(rowsum16_elem(lane), hi)] += se;
     }
     {
       f32x16 rs0 = zero16();
