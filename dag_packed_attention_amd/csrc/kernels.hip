@@ -668,6 +668,10 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
 
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {  // 32-key halves
+      // a half with no key visible to this wave's rows (outside the range, above the
+      // diagonal, or rows that are all padding) would add exact zeros: skipped
+      if (hi_t <= mb * 32 || lo >= mb * 32 + 32 || (diag && mb * 32 > nb * 32 + 31) || nb * 32 >= qp.nrows)
+        continue;
       // all eight K fragments are read first, so the products wait only for the first;
       // the V fragments of this half go out before the softmax and arrive under it
       f16x8 kfr[8], vfr[8];
@@ -889,6 +893,9 @@ __global__ __launch_bounds__(512, 1) void dq_mfma_kernel(
     const f16_t* V = lvv[buf];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
+      // a half with no key visible to this wave's rows adds exact zeros: skipped
+      if (hi_t <= mb * 32 || lo >= mb * 32 + 32 || (diag && mb * 32 > nb * 32 + 31) || nb * 32 >= qp.nrows)
+        continue;
       f32x16 s = zero16(), dp = zero16();
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
