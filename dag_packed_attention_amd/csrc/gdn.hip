@@ -201,6 +201,16 @@ __device__ __forceinline__ int rowsum16_elem(int lane) {
   return 8 * (lane & 1) + 4 * ((lane >> 1) & 1) + 2 * ((lane >> 2) & 1) + ((lane >> 3) & 1);
 }
 __device__ __forceinline__ bool rowsum16_writer(int lane) { return !(lane & 16); }
+
+// The per-row values v[r] = a[32 rb + acc_row(r, hi)] of an accumulator lane's 16 rows:
+// four runs of four consecutive floats (a 16-byte aligned), one 16-byte LDS read each.
+__device__ __forceinline__ void rows16(const float* a, int rb, int hi, float (&v)[16]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float4 x = *reinterpret_cast<const float4*>(a + 32 * rb + 8 * q + 4 * hi);
+    v[4 * q] = x.x, v[4 * q + 1] = x.y, v[4 * q + 2] = x.z, v[4 * q + 3] = x.w;
+  }
+}
 // Sum over the 32 rows of one accumulator column (both lane halves).
 __device__ __forceinline__ float colsum16(const float (&x)[16]) {
   float s = 0.f;
@@ -981,7 +991,12 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
   __shared__ __attribute__((aligned(16))) f16_t Pr[kB * LDP];   // P, then dP~
   __shared__ __attribute__((aligned(16))) f16_t Th[kB * LDP];   // T high part, then dKk
   __shared__ __attribute__((aligned(16))) f16_t Tl[kB * LDP];
-  __shared__ float gs[kB], bs[kB], al[kB], gam[kB], egam[kB];
+  // per-row values; 16-byte aligned for the accumulator lanes' float4 reads (rows16)
+  __shared__ __attribute__((aligned(16))) float gs[kB];
+  __shared__ __attribute__((aligned(16))) float bs[kB];
+  __shared__ __attribute__((aligned(16))) float al[kB];
+  __shared__ __attribute__((aligned(16))) float gam[kB];
+  __shared__ __attribute__((aligned(16))) float egam[kB];
   __shared__ int rw[kB];
   // where row t's gradients go: 0 nowhere (past the sequence), 1 the replay buffer,
   // 2 the side buffer of a replayed row, 3 its own dk / dv row; with the base offset
@@ -994,7 +1009,8 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
   const int item = round_item0 + ritem;  // among all items (its T and P)
   const GSeq sq = seqs[items[2 * item]];
   const int c = items[2 * item + 1];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: wave-level branches stay scalar
   const int rb = wave >> 2, cb = wave & 3;  // this wave's 32-row, 32-column block
   const int j0 = c * kB;
   const ChunkIn ci{grows + sq.tok_off, sq.n_tok, sq.n_replay};
@@ -1057,7 +1073,6 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     gam[tid] = __expf(gs[tid]);
     egam[tid] = __expf(gs[kB - 1] - gs[tid]);
   }
-  const float g63 = gs[kB - 1];
   __syncthreads();
 
   // -- R = diag(beta) (V - diag(gamma) K S0^T) (fp16), then U = T R --------------------------
@@ -1066,11 +1081,14 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       ks = mfma(frag_n(Kr, LDK, 32 * rb, 16 * s, lane), s0n[s], ks);
+    float b16[16], g16[16];
+    rows16(bs, rb, hi, b16);
+    rows16(gam, rb, hi, g16);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * rb + acc_row(r, hi);
       const float vv = (float)dRr[t * LDK + cc];  // V rows, staged by bwd_commit
-      Ur[t * LDK + cc] = (f16_t)(bs[t] * (vv - gam[t] * ks[r]));
+      Ur[t * LDK + cc] = (f16_t)(b16[r] * (vv - g16[r] * ks[r]));
     }
   }
   __syncthreads();
@@ -1093,8 +1111,12 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
 #pragma unroll
     for (int s = 0; s < 8; ++s)
       du = mfma(frag_n(Kr, LDK, 32 * rb, 16 * s, lane), frag_n(dSh, LDK, 32 * cb, 16 * s, lane), du);
+    {
+      float e16[16];
+      rows16(egam, rb, hi, e16);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) du[r] *= egam[32 * rb + acc_row(r, hi)];
+      for (int r = 0; r < 16; ++r) du[r] *= e16[r];
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       du = mfma(frag_t(Pr, LDP, 16 * s, 32 * rb, lane), frag_t(dOr, LDK, 16 * s, 32 * cb, lane), du);
@@ -1104,6 +1126,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
   __syncthreads();
 
   // -- dR = (I + A)^{-T} dU = T^T dU; dV = diag(beta) dR ---------------------------------------
+  f16_t drh[16];  // this lane's dR elements as stored (fp16), reused below
   {
     f32x16 dr = zero16();
 #pragma unroll
@@ -1114,7 +1137,10 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     }
     __syncthreads();  // every wave has read dU and T
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dRr[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)dr[r];
+    for (int r = 0; r < 16; ++r) {
+      drh[r] = (f16_t)dr[r];
+      dRr[(32 * rb + acc_row(r, hi)) * LDK + cc] = drh[r];
+    }
     put_pairs(dr, 32 * rb, lane, [&](int t, float x0, float x1) {
       const int kind = dst_kind[t];
       const int64_t off = dst_off[t] + kD + (cc & ~1);
@@ -1149,26 +1175,35 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
   if (wave < 4) {
     const int bm = wave >> 1, bn = wave & 1;
     f32x16 dp = zero16(), da = zero16(), kk = zero16(), qk = zero16();
+    if (bm >= bn) {  // blocks on or below the diagonal: dA, KK and QK as well
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const f16x8 b = frag_n(Ur, LDK, 32 * bn, 16 * s, lane);
-      dp = mfma(frag_n(dOr, LDK, 32 * bm, 16 * s, lane), b, dp);
-      if (bm >= bn) {
+      for (int s = 0; s < 8; ++s) {
+        const f16x8 b = frag_n(Ur, LDK, 32 * bn, 16 * s, lane);
         const f16x8 bk = frag_n(Kr, LDK, 32 * bn, 16 * s, lane);
+        dp = mfma(frag_n(dOr, LDK, 32 * bm, 16 * s, lane), b, dp);
         da = mfma(frag_n(dRr, LDK, 32 * bm, 16 * s, lane), b, da);
         kk = mfma(frag_n(Kr, LDK, 32 * bm, 16 * s, lane), bk, kk);
         qk = mfma(frag_n(Qr, LDK, 32 * bm, 16 * s, lane), bk, qk);
       }
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s)
+        dp = mfma(frag_n(dOr, LDK, 32 * bm, 16 * s, lane), frag_n(Ur, LDK, 32 * bn, 16 * s, lane), dp);
     }
     const int i = 32 * bn + l32;
+    const float gi = gs[i];
+    float gt[16], b16[16];
+    rows16(gs, bm, hi, gt);
+    rows16(bs, bm, hi, b16);
     float xy[16], z[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * bm + acc_row(r, hi);
-      const float e = i <= t ? __expf(gs[t] - gs[i]) : 0.f;
+      // E_ti = exp(g_t - g_i) on and below the diagonal; exp(-inf) = 0 above it (no branch)
+      const float e = __expf(i <= t ? gt[r] - gi : -INFINITY);
       const float dpt = scale * e * dp[r];          // dP~ = d(QK) (scale and decay folded)
       const float dat = i < t ? -da[r] : 0.f;       // dA
-      const float dkk = dat * bs[t] * e;            // d(KK)
+      const float dkk = dat * b16[r] * e;           // d(KK)
       Pr[t * LDP + i] = (f16_t)dpt;
       Kk[t * LDP + i] = (f16_t)dkk;
       xy[r] = dpt * qk[r] + dkk * kk[r];            // dg from E_ti inside P and A
@@ -1210,13 +1245,14 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
   }
   // -- R's dependence on beta and gamma ------------------------------------------------------
   {
-    float xb[16], xg[16];
+    float xb[16], xg[16], b16[16], g16[16];
+    rows16(bs, rb, hi, b16);
+    rows16(gam, rb, hi, g16);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int t = 32 * rb + acc_row(r, hi);
-      const float dr = (float)dRr[t * LDK + cc];
-      xb[r] = -dr * gam[t] * ks[r];  // the dR V part is red_v
-      xg[r] = -bs[t] * dr * ks[r];
+      const float dr = (float)drh[r];
+      xb[r] = -dr * g16[r] * ks[r];  // the dR V part is red_v
+      xg[r] = -b16[r] * dr * ks[r];
     }
     const float sb = rowsum16(xb, lane);
     const float sg = rowsum16(xg, lane);
@@ -1234,12 +1270,13 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
 #pragma unroll
     for (int s = 0; s < 8; ++s) aq = mfma(frag_n(dOr, LDK, 32 * rb, 16 * s, lane), s0f[s], aq);
     {
-      float xg[16];
+      float xg[16], g16[16];
+      rows16(gam, rb, hi, g16);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 32 * rb + acc_row(r, hi);
         xg[r] = scale * aq[r] * (float)Qr[t * LDK + cc];
-        aq[r] *= scale * gam[t];
+        aq[r] *= scale * g16[r];
       }
       const float sg = rowsum16(xg, lane);
       if (rowsum16_writer(lane)) red_g[wave][32 * rb + acc_row(rowsum16_elem(lane), hi)] += sg;
@@ -1268,12 +1305,13 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
 #pragma unroll
       for (int s = 0; s < 8; ++s)
         ud = mfma(frag_n(Ur, LDK, 32 * rb, 16 * s, lane), frag_t(dSh, LDK, 16 * s, 32 * cb, lane), ud);
-      float xe[16];
+      float xe[16], e16[16];
+      rows16(egam, rb, hi, e16);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = 32 * rb + acc_row(r, hi);
         xe[r] = ud[r] * (float)Kr[t * LDK + cc];
-        ak[r] = fmaf(egam[t], ud[r], ak[r]);
+        ak[r] = fmaf(e16[r], ud[r], ak[r]);
       }
       const float se = rowsum16(xe, lane);
       if (rowsum16_writer(lane)) red_e[wave][32 * rb + acc_row(rowsum16_elem(lane), hi)] += se;
@@ -1282,11 +1320,11 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
       f32x16 rs0 = zero16();
 #pragma unroll
       for (int s = 0; s < 8; ++s) rs0 = mfma(frag_n(dRr, LDK, 32 * rb, 16 * s, lane), s0f[s], rs0);
+      float b16[16], g16[16];
+      rows16(bs, rb, hi, b16);
+      rows16(gam, rb, hi, g16);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * rb + acc_row(r, hi);
-        ak[r] = fmaf(-bs[t] * gam[t], rs0[r], ak[r]);
-      }
+      for (int r = 0; r < 16; ++r) ak[r] = fmaf(-b16[r] * g16[r], rs0[r], ak[r]);
     }
     put_pairs(ak, 32 * rb, lane, [&](int t, float x0, float x1) {
       const int kind = dst_kind[t];
