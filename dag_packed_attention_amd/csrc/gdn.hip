@@ -104,6 +104,14 @@ __device__ __forceinline__ void put_pairs(const f32x16& a, int row0, int lane, F
     put(row0 + 8 * (i >> 1) + 4 * hi + 2 * (i & 1) + odd, x0, x1);  // acc_row(2 i + odd, hi)
   }
 }
+typedef __attribute__((ext_vector_type(2))) f16_t f16x2_t;
+// fp16 copy of a 32 x 32 accumulator block (column col = col0 + lane % 32) into an LDS tile
+// of row stride ld halfs, two columns per lane: one 4-byte write per element pair.
+__device__ __forceinline__ void lds_put_f16(const f32x16& a, f16_t* tile, int ld, int row0, int col, int lane) {
+  put_pairs(a, row0, lane, [&](int t, float x0, float x1) {
+    *reinterpret_cast<f16x2_t*>(tile + t * ld + (col & ~1)) = f16x2_t{(f16_t)x0, (f16_t)x1};
+  });
+}
 
 // MFMA operand with the contraction index contiguous: rows mn0 + lane % 32 of
 // X[.][ld], elements k0 + 8 (lane / 32) .. + 7.
@@ -734,13 +742,12 @@ __global__ __launch_bounds__(512, 1) void gdn_fwd_kernel(
         ks[r] = bs[t] * (Rr[t * LDR + cc] - gam[t] * ks[r]);  // V in, R out
       }
       __syncthreads();  // every V row read: the R tiles overwrite them
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = 32 * rb + acc_row(r, hi);
-        const f16_t h = (f16_t)ks[r];
-        Rh[t * LDK + cc] = h;
-        Rl[t * LDK + cc] = (f16_t)(ks[r] - (float)h);
-      }
+      // R as an fp16 high part and the fp16 rounding of the rest, two columns per lane
+      put_pairs(ks, 32 * rb, lane, [&](int t, float x0, float x1) {
+        const f16_t h0 = (f16_t)x0, h1 = (f16_t)x1;
+        *reinterpret_cast<f16x2_t*>(Rh + t * LDK + (cc & ~1)) = f16x2_t{h0, h1};
+        *reinterpret_cast<f16x2_t*>(Rl + t * LDK + (cc & ~1)) = f16x2_t{(f16_t)(x0 - (float)h0), (f16_t)(x1 - (float)h1)};
+      });
     }
     if (has_next && stager) fetch_kqv(rwn, k, q, v, H, head, tid, nx);
     __syncthreads();
@@ -757,8 +764,7 @@ __global__ __launch_bounds__(512, 1) void gdn_fwd_kernel(
         u = mfma(ah, bl, u);
         u = mfma(frag_n(Tl, LDP, 32 * rb, 16 * s, lane), bh, u);
       }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Ur[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)u[r];
+      lds_put_f16(u, Ur, LDK, 32 * rb, cc, lane);
     }
     // the next chunk's T and P (issued here, where the R and U registers are free; the
     // last chunk fetches its own again)
@@ -917,8 +923,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bscan_kernel(
 #pragma unroll
       for (int s = 0; s < 4; ++s)
         du = mfma(frag_t(Pr, LDP, 16 * s, 32 * rb, lane), frag_t(dOr, LDK, 16 * s, 32 * cb, lane), du);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dRr[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)du[r];
+      lds_put_f16(du, dRr, LDK, 32 * rb, cc, lane);
     }
     __syncthreads();
     // -- dR = (I + A)^{-T} dU = T^T dU: T_hi^T dU + T_lo^T dU -----------------------------------
@@ -931,8 +936,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bscan_kernel(
         dr = mfma(frag_t(Tl, LDP, 16 * s, 32 * rb, lane), b, dr);
       }
       __syncthreads();  // every wave has read dU
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dRr[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)dr[r];
+      lds_put_f16(dr, dRr, LDK, 32 * rb, cc, lane);
     }
     __syncthreads();
     // -- dS_prev = gamma_63 dS + scale (diag(gamma) dO)^T Q - (diag(beta gamma) dR)^T K -----------
@@ -1084,12 +1088,14 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     float b16[16], g16[16];
     rows16(bs, rb, hi, b16);
     rows16(gam, rb, hi, g16);
+    f32x16 rr;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * rb + acc_row(r, hi);
       const float vv = (float)dRr[t * LDK + cc];  // V rows, staged by bwd_commit
-      Ur[t * LDK + cc] = (f16_t)(b16[r] * (vv - g16[r] * ks[r]));
+      rr[r] = b16[r] * (vv - g16[r] * ks[r]);
     }
+    lds_put_f16(rr, Ur, LDK, 32 * rb, cc, lane);
   }
   __syncthreads();
   {
@@ -1101,8 +1107,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
       u = mfma(frag_n(Tl, LDP, 32 * rb, 16 * s, lane), b, u);
     }
     __syncthreads();  // every wave has read R
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Ur[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)u[r];
+    lds_put_f16(u, Ur, LDK, 32 * rb, cc, lane);
   }
 
   // -- dU = scale P^T dO + diag(E_63,.) K dS^T --------------------------------------------
@@ -1120,8 +1125,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       du = mfma(frag_t(Pr, LDP, 16 * s, 32 * rb, lane), frag_t(dOr, LDK, 16 * s, 32 * cb, lane), du);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) dRr[(32 * rb + acc_row(r, hi)) * LDK + cc] = (f16_t)du[r];
+    lds_put_f16(du, dRr, LDK, 32 * rb, cc, lane);
   }
   __syncthreads();
 
@@ -1137,10 +1141,8 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     }
     __syncthreads();  // every wave has read dU and T
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      drh[r] = (f16_t)dr[r];
-      dRr[(32 * rb + acc_row(r, hi)) * LDK + cc] = drh[r];
-    }
+    for (int r = 0; r < 16; ++r) drh[r] = (f16_t)dr[r];
+    lds_put_f16(dr, dRr, LDK, 32 * rb, cc, lane);
     put_pairs(dr, 32 * rb, lane, [&](int t, float x0, float x1) {
       const int kind = dst_kind[t];
       const int64_t off = dst_off[t] + kD + (cc & ~1);
@@ -1196,6 +1198,7 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     rows16(gs, bm, hi, gt);
     rows16(bs, bm, hi, b16);
     float xy[16], z[16];
+    f32x16 dpt16, dkk16;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * bm + acc_row(r, hi);
@@ -1204,11 +1207,13 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
       const float dpt = scale * e * dp[r];          // dP~ = d(QK) (scale and decay folded)
       const float dat = i < t ? -da[r] : 0.f;       // dA
       const float dkk = dat * b16[r] * e;           // d(KK)
-      Pr[t * LDP + i] = (f16_t)dpt;
-      Kk[t * LDP + i] = (f16_t)dkk;
+      dpt16[r] = dpt;
+      dkk16[r] = dkk;
       xy[r] = dpt * qk[r] + dkk * kk[r];            // dg from E_ti inside P and A
       z[r] = dat * e * kk[r];                       // dbeta through A
     }
+    lds_put_f16(dpt16, Pr, LDP, 32 * bm, i, lane);
+    lds_put_f16(dkk16, Kk, LDP, 32 * bm, i, lane);
     const float rs = rowsum16(xy, lane);
     const float rz = rowsum16(z, lane);
     const float cs = colsum16(xy);
