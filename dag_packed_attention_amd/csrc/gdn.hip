@@ -136,6 +136,19 @@ __device__ __forceinline__ f16x8 frag_t(const f16_t* X, int ld, int k0, int mn0,
   }
   return o;
 }
+// The values of an LDS tile X[.][ld] at an accumulator lane's 16 rows row0 + acc_row(r, hi)
+// and its column col0 + lane % 32, as fp32: four transpose reads of four rows each (in each
+// group of 16 lanes, lane s fetches row s / 4 of the group's four at columns 4 (s % 4) ..).
+__device__ __forceinline__ void acc_col_f16(const f16_t* X, int ld, int row0, int col0, int lane, float (&v)[16]) {
+  const int G = lane >> 4, a = lane & 15;
+  const f16_t* p = X + (row0 + 4 * (G >> 1) + (a >> 2)) * ld + col0 + 16 * (G & 1) + 4 * (a & 3);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const v4fp16 w = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4fp16*)(p + 8 * q * ld));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[4 * q + j] = (float)(f16_t)w[j];
+  }
+}
 // Same operand layout as frag_n, read from global memory.
 __device__ __forceinline__ f16x8 frag_g(const f16_t* __restrict__ X, int mn0, int k0, int lane) {
   return *reinterpret_cast<const f16x8*>(X + (mn0 + (lane & 31)) * kD + k0 + 8 * (lane >> 5));
@@ -1088,13 +1101,11 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     float b16[16], g16[16];
     rows16(bs, rb, hi, b16);
     rows16(gam, rb, hi, g16);
+    float v16[16];
+    acc_col_f16(dRr, LDK, 32 * rb, 32 * cb, lane, v16);  // V rows, staged by bwd_commit
     f32x16 rr;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * rb + acc_row(r, hi);
-      const float vv = (float)dRr[t * LDK + cc];  // V rows, staged by bwd_commit
-      rr[r] = b16[r] * (vv - g16[r] * ks[r]);
-    }
+    for (int r = 0; r < 16; ++r) rr[r] = b16[r] * (v16[r] - g16[r] * ks[r]);
     lds_put_f16(rr, Ur, LDK, 32 * rb, cc, lane);
   }
   __syncthreads();
@@ -1157,14 +1168,14 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
   // -- <dS, S0> for the decay of the whole chunk: this wave's dk columns, dv rows 64 rb .. --
   {
     // lane holds S0[16 s + 8 hi + j][32 cb + l32] in s0f[s][j]
+    // and dS[16 (4 rb + sb) + 8 hi + j][32 cb + l32] in frag_t(dSh, ..)[j]
     float s = 0.f;
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb)
+    for (int sb = 0; sb < 4; ++sb) {
+      const f16x8 ds8 = frag_t(dSh, LDK, 16 * (4 * rb + sb), 32 * cb, lane);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int d = 16 * (4 * rb + sb) + 8 * hi + j;
-        s += (float)dSh[d * LDK + cc] * (float)(rb ? s0f[4 + sb][j] : s0f[sb][j]);
-      }
+      for (int j = 0; j < 8; ++j) s += (float)ds8[j] * (float)(rb ? s0f[4 + sb][j] : s0f[sb][j]);
+    }
 #pragma unroll
     for (int off = 32; off >= 16; off >>= 1) s += __shfl_xor(s, off);
     s += from_xor1(s);
@@ -1275,12 +1286,12 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
 #pragma unroll
     for (int s = 0; s < 8; ++s) aq = mfma(frag_n(dOr, LDK, 32 * rb, 16 * s, lane), s0f[s], aq);
     {
-      float xg[16], g16[16];
+      float xg[16], g16[16], q16[16];
       rows16(gam, rb, hi, g16);
+      acc_col_f16(Qr, LDK, 32 * rb, 32 * cb, lane, q16);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = 32 * rb + acc_row(r, hi);
-        xg[r] = scale * aq[r] * (float)Qr[t * LDK + cc];
+        xg[r] = scale * aq[r] * q16[r];
         aq[r] *= scale * g16[r];
       }
       const float sg = rowsum16(xg, lane);
@@ -1310,12 +1321,12 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
 #pragma unroll
       for (int s = 0; s < 8; ++s)
         ud = mfma(frag_n(Ur, LDK, 32 * rb, 16 * s, lane), frag_t(dSh, LDK, 16 * s, 32 * cb, lane), ud);
-      float xe[16], e16[16];
+      float xe[16], e16[16], k16[16];
       rows16(egam, rb, hi, e16);
+      acc_col_f16(Kr, LDK, 32 * rb, 32 * cb, lane, k16);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int t = 32 * rb + acc_row(r, hi);
-        xe[r] = ud[r] * (float)Kr[t * LDK + cc];
+        xe[r] = ud[r] * k16[r];
         ak[r] = fmaf(e16[r], ud[r], ak[r]);
       }
       const float se = rowsum16(xe, lane);
