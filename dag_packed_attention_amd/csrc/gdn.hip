@@ -535,7 +535,8 @@ __global__ __launch_bounds__(256) void gdn_tinv_kernel(const GSeq* __restrict__ 
   __shared__ __attribute__((aligned(16))) f16_t Kr[kB * LDK];
   __shared__ __attribute__((aligned(16))) f16_t Qr[kB * LDK];
   __shared__ __attribute__((aligned(16))) float Ar[kB * LDA];  // A^T
-  __shared__ float gs[kB], bs[kB];
+  __shared__ __attribute__((aligned(16))) float gs[kB];
+  __shared__ __attribute__((aligned(16))) float bs[kB];
   float* Xr = reinterpret_cast<float*>(Kr);  // after the products: the identity, then T ([t][j])
   static_assert(kB * LDA * 4 <= kB * LDK * 2, "the solve tile fits the K tile");
   __shared__ int rw[kB];
@@ -543,7 +544,8 @@ __global__ __launch_bounds__(256) void gdn_tinv_kernel(const GSeq* __restrict__ 
   const int item = blockIdx.x / H;
   const GSeq sq = seqs[items[2 * item]];
   const int j0 = items[2 * item + 1] * kB;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, hi = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   if (tid < kB) {
     const int j = j0 + tid;
     int row = -1;
@@ -592,13 +594,22 @@ __global__ __launch_bounds__(256) void gdn_tinv_kernel(const GSeq* __restrict__ 
       }
     }
     const int i = 32 * bn + l32;
+    const float gi = gs[i];
+    float gt[16], b16[16];
+    rows16(gs, bm, hi, gt);
+    rows16(bs, bm, hi, b16);
+    f32x16 pq;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int t = 32 * bm + acc_row(r, hi);
-      const float e = i <= t ? __expf(gs[t] - gs[i]) : 0.f;
-      Ar[i * LDA + t] = i < t ? bs[t] * e * kk[r] : 0.f;
-      dst[2 * kB * kB + t * kB + i] = (f16_t)(scale * e * qk[r]);
+      // E_ti = exp(g_t - g_i) on and below the diagonal; exp(-inf) = 0 above it (no branch)
+      const float e = __expf(i <= t ? gt[r] - gi : -INFINITY);
+      Ar[i * LDA + t] = i < t ? b16[r] * e * kk[r] : 0.f;
+      pq[r] = scale * e * qk[r];
     }
+    put_pairs(pq, 32 * bm, lane, [&](int t, float x0, float x1) {
+      *reinterpret_cast<f16x2_t*>(dst + 2 * kB * kB + t * kB + (i & ~1)) = f16x2_t{(f16_t)x0, (f16_t)x1};
+    });
   }
   __syncthreads();
   for (int idx = tid; idx < kB * kB; idx += 256) Xr[(idx >> 6) * LDA + (idx & 63)] = (idx >> 6) == (idx & 63) ? 1.f : 0.f;
@@ -606,11 +617,11 @@ __global__ __launch_bounds__(256) void gdn_tinv_kernel(const GSeq* __restrict__ 
   // T = (I + A)^{-1}: the solve on the identity, 64 columns (two waves, two lanes a column)
   if (tid < 128) solve_lower<float, false>(Ar, Xr, LDA, nullptr, tid);
   __syncthreads();
-  for (int idx = tid; idx < kB * kB; idx += 256) {
-    const float x = Xr[(idx >> 6) * LDA + (idx & 63)];
-    const f16_t h = (f16_t)x;
-    dst[idx] = h;
-    dst[kB * kB + idx] = (f16_t)(x - (float)h);
+  for (int idx = 2 * tid; idx < kB * kB; idx += 512) {  // two consecutive elements per thread
+    const float2 x = *reinterpret_cast<const float2*>(Xr + (idx >> 6) * LDA + (idx & 63));
+    const f16_t h0 = (f16_t)x.x, h1 = (f16_t)x.y;
+    *reinterpret_cast<f16x2_t*>(dst + idx) = f16x2_t{h0, h1};
+    *reinterpret_cast<f16x2_t*>(dst + kB * kB + idx) = f16x2_t{(f16_t)(x.x - (float)h0), (f16_t)(x.y - (float)h1)};
   }
 }
 
@@ -1369,7 +1380,11 @@ __global__ __launch_bounds__(512, 1) void gdn_bpar_kernel(
     float dg = dgp + gam[t] * dgam - e_t * en;
     float tot = e_t * en;  // sum over the chunk of dEn_i E_63,i goes to g_63
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) tot += __shfl_xor(tot, off);
+    for (int off = 32; off >= 16; off >>= 1) tot += __shfl_xor(tot, off);
+    tot += from_xor1(tot);
+    tot += from_xor2(tot);
+    tot += from_ror4(tot);
+    tot += from_ror8(tot);  // every lane: the wave's sum
     if (t == kB - 1) dg += tot + gam[kB - 1] * ss;
     // reverse inclusive scan: dlogalpha_t = sum_{s >= t} dg_s
 #pragma unroll
