@@ -579,6 +579,17 @@ __device__ __forceinline__ void pin(const f16x8& x) { asm volatile("" : : "v"(x)
 
 constexpr int kTile = 64 * kD;  // elements of a page's 64 x 128 (or 128 x 64) block in global memory
 
+// Lane pair l, l ^ 32: v_permlane32_swap with both operands one value leaves {value of the
+// pair's lower lane, of its upper lane} in both lanes (no LDS crossbar, unlike a shuffle).
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Forward for one 64-row query block x one KV head.  Eight waves: wave (hh, nb)
 // serves query head 4 g + hh and rows 32 nb .. 32 nb + 31 (two waves per SIMD,
 // so one wave's softmax overlaps the other's products).  K/V tiles are
@@ -704,7 +715,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
       float mx = s[0];
 #pragma unroll
       for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      mx = max_xor32(mx) * sl2;
       if (__any(mx > mrow + kLazy)) {
         const float mnew = fmaxf(mrow, mx);
         float alpha = __builtin_amdgcn_exp2f(mrow - mnew);
@@ -757,7 +768,7 @@ __global__ __launch_bounds__(512, 1) void fwd_mfma_kernel(
     __syncthreads();
   }
 
-  const float l = lrow + __shfl_xor(lrow, 32);
+  const float l = sum_xor32(lrow);
   const bool valid = row < qp.nrows;
   const float inv = valid ? inv_sv / l : 0.f;
   const int64_t grow = (int64_t)qp.phys * 64 + row;
