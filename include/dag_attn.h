@@ -250,7 +250,9 @@ dag_status dag_attn_workspace(const dag_plan* plan, const dag_attn_params* p, si
  * rowsum(dO * O) from O = o + o_lo, accurate to ~2^-17 instead of bf16's 2^-9; with O
  * rounded to bf16 alone, attention concentrated on few keys moves dq and dk by more than
  * 2e-2 (measured on logits of standard deviation 16).
- * ws: device workspace of at least fwd_bytes. */
+ * ws: device workspace of at least fwd_bytes.
+ * A plan without rows (every node of length 0) returns DAG_OK after checking p, reading
+ * no pointer; the backward and the gated-delta-rule calls do the same. */
 dag_status dag_attn_fwd(dag_plan* plan, const dag_attn_params* p, const void* q, const void* k,
                         const void* v, void* o, float* lse, void* o_lo, void* ws, size_t ws_bytes,
                         void* hip_stream);

@@ -170,3 +170,21 @@ def test_logprob_parameters_are_checked(fields, code):
     p = dpa.DagLogprobParams(*fields)
     st = L.dag_logprob_fwd(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert st == code and _err()
+
+
+def test_a_plan_without_rows_returns_at_once():
+    # every node of length 0: nothing to compute, so no pointer is read (all NULL here)
+    b = synth.dags.DagBuilder()
+    r = b.node(-1, 0)
+    b.node(r, 0)
+    for gc in (0, 64):
+        empty = dpa.Plan(b.build(), gdn_chunk=gc)
+        assert empty.rows == 0
+        cp = _attn()
+        assert L.dag_attn_fwd(empty._h, ctypes.byref(cp), None, None, None, None, None, None, None, 0, None) == OK
+        assert L.dag_attn_bwd(empty._h, ctypes.byref(cp), *([None] * 10), None, 0, None) == OK
+        assert _fwd(empty, _attn(n_q=0)) == UNSUPPORTED  # the parameters are still checked
+        if gc:
+            gp = _gdn()
+            assert L.dag_gdn_fwd(empty._h, ctypes.byref(gp), *([None] * 7), 0, None) == OK
+            assert L.dag_gdn_bwd(empty._h, ctypes.byref(gp), *([None] * 12), 0, None) == OK
