@@ -605,6 +605,41 @@ def traffic_record(kernel: str):
     return ent.get("bytes_per_launch")
 
 
+def staging_record(plan, hkv: int) -> dict:
+    """Bytes each attention kernel stages from global memory per launch before any cache reuse
+    (the plan's tile and reader-step counts, `dag_plan_stats_get`), and, where the committed
+    counter summary matches the kernels, the share of them that the caches absorbed.  The HBM
+    reads also count each kernel's other loads (its own query rows), so `absorbed` is a lower
+    bound for the staged tiles and rows."""
+    st = plan.stats()
+    rec = {"fwd_tiles": st["fwd_tiles"], "dkdv_groups": st["dkdv_groups"], "dkdv_pairs": st["dkdv_pairs"],
+           "dkdv_reader_steps": st["dkdv_group_steps"] + st["dkdv_pair_steps"]}
+    reads = traffic_reads()
+    for k in ("fwd", "dkdv", "dq"):
+        staged = st[f"{k}_staged_bytes"] * hkv
+        ent = {"staged_bytes": staged}
+        if reads.get(k) and staged:
+            ent["hbm_read_bytes"] = reads[k]
+            ent["absorbed"] = round(1.0 - reads[k] / staged, 4)
+        rec[k] = ent
+    return rec
+
+
+def traffic_reads() -> dict:
+    """HBM read bytes per launch of the attention kernels from the committed counter summary,
+    if it matches the source (else empty)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "kernels.hip")
+    if rec.get("kernels_hip_sha256_16") != hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]:
+        return {}
+    return {k: v.get("read_bytes") for k, v in rec.get("kernels", {}).items()}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -710,7 +745,8 @@ def main() -> int:
                       "seed": int(spec.meta["seed"]), "unique_tokens": info["tokens"], "rows": info["rows"],
                       "visible_pairs": P, "flat_rows": info["flat_rows"], "flat_pairs": info["flat_pairs"],
                       "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "page": 64},
-           "roofline": roof}
+           "roofline": roof,
+           "staging": staging_record(plan, HKV)}
 
     if not args.no_views:
         out["views"] = views_time(dpa, spec, p, tensors, ws, dev)

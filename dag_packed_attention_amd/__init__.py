@@ -58,6 +58,12 @@ class DagPlanInfo(ctypes.Structure):
                                                                  ("semantic_tokens", ctypes.c_int64),
                                                                  ("pack_pages", ctypes.c_int32)]
 
+class DagPlanStats(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("fwd_tiles", "dkdv_groups", "dkdv_group_steps", "dkdv_pairs",
+                                             "dkdv_pair_steps", "fwd_staged_bytes", "dq_staged_bytes",
+                                             "dkdv_staged_bytes")]
+
+
 VIEWS = {"mounted": 0, "mount_free": 1, "unshifted": 2}
 
 
@@ -119,6 +125,7 @@ def _load() -> ctypes.CDLL:
                        ctypes.POINTER(DagBuildOpts), ctypes.POINTER(P)], I32),
         "dag_plan_destroy": ([P], None),
         "dag_plan_info_get": ([P, ctypes.POINTER(DagPlanInfo)], I32),
+        "dag_plan_stats_get": ([P, ctypes.POINTER(DagPlanStats)], I32),
         "dag_plan_rows": ([P, P, P], I32),
         "dag_plan_starts": ([P, P], I32),
         "dag_plan_multiplicity": ([P, P], I32),
@@ -223,6 +230,13 @@ class Plan:
             _check(_lib.dag_plan_rows(self._h, rot.ctypes.data, por.ctypes.data))
             self._rows = (rot[: self.tokens], por[: self.rows])
         return self._rows
+
+    def stats(self) -> dict:
+        """``dag_plan_stats_get``: tiles, dK/dV groups and pairs with their reader steps, and the
+        bytes each attention kernel stages per KV head before any cache reuse."""
+        st = DagPlanStats()
+        _check(_lib.dag_plan_stats_get(self._h, ctypes.byref(st)))
+        return {f: int(getattr(st, f)) for f, _ in DagPlanStats._fields_}
 
     def multiplicity(self) -> np.ndarray:
         """``dag_plan_multiplicity``: trajectories holding each token (node-major order), int32 [U]."""

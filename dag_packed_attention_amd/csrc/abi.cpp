@@ -556,6 +556,27 @@ dag_status dag_plan_info_get(const dag_plan* plan, dag_plan_info* out) {
   return DAG_OK;
 }
 
+dag_status dag_plan_stats_get(const dag_plan* plan, dag_plan_stats* out) {
+  if (!plan || !out) return set_err(DAG_E_INVALID, "null argument");
+  const Plan& P = plan->p;
+  constexpr int64_t kTileBytes = 64 * 128 * 2;        // one fp16 64 x 128 tile
+  constexpr int64_t kUnitBytes = 2 * 2 * 32 * 128 * 2 + 2 * 256;  // two heads' Q, dO rows + offsets
+  dag_plan_stats st{};
+  for (const QPage& q : P.qpages) st.fwd_tiles += q.tile_count;  // visits: a node's pages share its list
+  st.dkdv_groups = (int64_t)P.kgroups.size() / kGroup;
+  st.dkdv_group_steps = (int64_t)P.kgsteps.size();
+  st.dkdv_pairs = (int64_t)P.kpairs.size() / 2;
+  st.dkdv_pair_steps = (int64_t)P.kpsteps.size();
+  st.fwd_staged_bytes = st.fwd_tiles * 2 * kTileBytes;
+  st.dq_staged_bytes = st.fwd_staged_bytes;
+  int64_t own_pages = 0;  // pages whose K and V tiles a group or pair loads once
+  for (int32_t ph : P.kgroups) own_pages += ph >= 0;
+  for (int32_t ph : P.kpairs) own_pages += ph >= 0;
+  st.dkdv_staged_bytes = (st.dkdv_group_steps + st.dkdv_pair_steps) * 2 * kUnitBytes + own_pages * 2 * kTileBytes;
+  *out = st;
+  return DAG_OK;
+}
+
 dag_status dag_plan_rows(const dag_plan* plan, int32_t* row_of_token, int32_t* pos_of_row) {
   if (!plan) return set_err(DAG_E_INVALID, "null plan");
   if (row_of_token && !plan->p.row_of_token.empty())

@@ -160,6 +160,27 @@ void dag_plan_destroy(dag_plan* plan);
 
 dag_status dag_plan_info_get(const dag_plan* plan, dag_plan_info* out);
 
+/* What the attention kernels walk for this plan, and the bytes they stage from global
+ * memory per KV head on the matrix-core path (head_dim 128, fp16 operand copies) before
+ * any cache reuse: a launch stages n_kv_heads times these.  Host only.
+ *   forward and dQ: one 64 x 128 K tile and one V tile (32 KiB) per visited tile;
+ *   dK/dV: per 32-row reader step two half-steps, each the Q and dO rows of two query
+ *   heads (32 KiB) and their two 256-byte row-offset runs, plus each group's or pair's
+ *   own K and V tiles once.
+ * Comparing these with the kernels' measured HBM reads gives the share the caches absorb
+ * (the merged reader lists order steps so that side-by-side groups share rows). */
+typedef struct {
+  int64_t fwd_tiles;         /* (query page, KV page) tiles of the forward and of dQ  */
+  int64_t dkdv_groups;       /* four-page groups                                       */
+  int64_t dkdv_group_steps;  /* their 32-row reader steps                              */
+  int64_t dkdv_pairs;        /* page pairs (packed plans, small nodes)                 */
+  int64_t dkdv_pair_steps;   /* their 32-row reader steps                              */
+  int64_t fwd_staged_bytes;  /* per KV head                                            */
+  int64_t dq_staged_bytes;   /* per KV head                                            */
+  int64_t dkdv_staged_bytes; /* per KV head                                            */
+} dag_plan_stats;
+dag_status dag_plan_stats_get(const dag_plan* plan, dag_plan_stats* out);
+
 /* Row of every token in node-major order (token (u, i) has index
  * sum_{w<u} length(w) + i) -> row_of_token[U]; Eq. 2 position of every row
  * -> pos_of_row[C] (-1 on padding rows).  Either pointer may be NULL. */
