@@ -420,7 +420,9 @@ def gather_time(dpa, dev, steps, warmup, pack=False):
             "unique_tokens": info["tokens"], "rows": C, "pages": info["pages"], "visible_pairs": P,
             "padding_rows_frac": round(1.0 - info["tokens"] / C, 4),
             "ms_per_step": round(dt * 1e3, 3), "tflops": round(3.5 * f_fwd / dt / 1e12, 2),
-            "hbm_peak_gbps": HBM_PEAK_GBPS, "kernels": kern}
+            "hbm_peak_gbps": HBM_PEAK_GBPS, "kernels": kern,
+            "staging": staging_record(plan, HKV, "hbm_traffic_gather_packed.json" if pack
+                                      else "hbm_traffic_gather.json")}
 
 
 def step_traffic_record(json_name: str, src_name: str, sha_key: str):
@@ -605,7 +607,7 @@ def traffic_record(kernel: str):
     return ent.get("bytes_per_launch")
 
 
-def staging_record(plan, hkv: int) -> dict:
+def staging_record(plan, hkv: int, json_name: str = "hbm_traffic.json") -> dict:
     """Bytes each attention kernel stages from global memory per launch before any cache reuse
     (the plan's tile and reader-step counts, `dag_plan_stats_get`), and, where the committed
     counter summary matches the kernels, the share of them that the caches absorbed.  The HBM
@@ -614,7 +616,7 @@ def staging_record(plan, hkv: int) -> dict:
     st = plan.stats()
     rec = {"fwd_tiles": st["fwd_tiles"], "dkdv_groups": st["dkdv_groups"], "dkdv_pairs": st["dkdv_pairs"],
            "dkdv_reader_steps": st["dkdv_group_steps"] + st["dkdv_pair_steps"]}
-    reads = traffic_reads()
+    reads = traffic_reads(json_name)
     for k in ("fwd", "dkdv", "dq"):
         staged = st[f"{k}_staged_bytes"] * hkv
         ent = {"staged_bytes": staged}
@@ -625,11 +627,11 @@ def staging_record(plan, hkv: int) -> dict:
     return rec
 
 
-def traffic_reads() -> dict:
-    """HBM read bytes per launch of the attention kernels from the committed counter summary,
+def traffic_reads(json_name: str = "hbm_traffic.json") -> dict:
+    """HBM read bytes per launch of the attention kernels from a committed counter summary,
     if it matches the source (else empty)."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    path = os.path.join(ROOT, "profiles", json_name)
     if not os.path.exists(path):
         return {}
     with open(path) as f:
