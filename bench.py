@@ -425,9 +425,9 @@ def gather_time(dpa, dev, steps, warmup, pack=False):
                                       else "hbm_traffic_gather.json")}
 
 
-def step_traffic_record(json_name: str, src_name: str, sha_key: str):
-    """HBM bytes per launch of a step's kernels from its committed counter summary,
-    if it was taken on the current source; {} otherwise."""
+def counter_summary(json_name: str, src_name: str = "kernels.hip", sha_key: str = "kernels_hip_sha256_16"):
+    """Per-kernel entries of a committed counter summary under profiles/, if it was taken on
+    the current source file (its sha256 prefix matches); {} otherwise."""
     import hashlib
     path = os.path.join(ROOT, "profiles", json_name)
     if not os.path.exists(path):
@@ -437,7 +437,13 @@ def step_traffic_record(json_name: str, src_name: str, sha_key: str):
     src = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", src_name)
     if rec.get(sha_key) != hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]:
         return {}
-    return {k: v.get("bytes_per_launch") for k, v in rec.get("kernels", {}).items()}
+    return rec.get("kernels", {})
+
+
+def step_traffic_record(json_name: str, src_name: str, sha_key: str):
+    """HBM bytes per launch of a step's kernels from its committed counter summary,
+    if it was taken on the current source; {} otherwise."""
+    return {k: v.get("bytes_per_launch") for k, v in counter_summary(json_name, src_name, sha_key).items()}
 
 
 def lp_traffic_record():
@@ -593,18 +599,7 @@ def cpu_model() -> str:
 
 def traffic_record(kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, if it matches the source."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    src = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "kernels.hip")
-    h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-    ent = rec.get("kernels", {}).get(kernel)
-    if not ent or rec.get("kernels_hip_sha256_16") != h:
-        return None
-    return ent.get("bytes_per_launch")
+    return counter_summary("hbm_traffic.json").get(kernel, {}).get("bytes_per_launch")
 
 
 def staging_record(plan, hkv: int, json_name: str = "hbm_traffic.json") -> dict:
@@ -630,16 +625,7 @@ def staging_record(plan, hkv: int, json_name: str = "hbm_traffic.json") -> dict:
 def traffic_reads(json_name: str = "hbm_traffic.json") -> dict:
     """HBM read bytes per launch of the attention kernels from a committed counter summary,
     if it matches the source (else empty)."""
-    import hashlib
-    path = os.path.join(ROOT, "profiles", json_name)
-    if not os.path.exists(path):
-        return {}
-    with open(path) as f:
-        rec = json.load(f)
-    src = os.path.join(ROOT, "dag_packed_attention_amd", "csrc", "kernels.hip")
-    if rec.get("kernels_hip_sha256_16") != hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]:
-        return {}
-    return {k: v.get("read_bytes") for k, v in rec.get("kernels", {}).items()}
+    return {k: v.get("read_bytes") for k, v in counter_summary(json_name).items()}
 
 
 def main() -> int:
